@@ -1,0 +1,330 @@
+#!/usr/bin/env python3
+"""CSA + HCA decode at 1M-token context on one MI355X.
+
+One step = one new token for each of B = 8 sequences through one CSA layer and one HCA
+layer, every stage in the library's HIP kernels:
+  CSA: compress the newest 4-token block (K, V and the indexer key, the key quantised to
+       MXFP4) into the caches; indexer over all 262,144 MXFP4 keys + top-1024 selection;
+       attention over the 1024 selected entries + the 128-token window.
+  HCA: compress the newest 128-token block (K, V); dense attention over all 8,192
+       entries + the 128-token window; split-K partials merged by log-sum-exp.
+A new block completes only every 4 (CSA) or 128 (HCA) tokens; compressing one of each in
+every step is the worst case.  value = queries/s, one query = one token of one sequence
+through both layers (all 64 heads).  Inputs are seeded synthetic tensors resident in HBM;
+three replicas of the streamed inputs rotate so that the 256 MB Infinity Cache does not
+serve a step from the previous one.
+
+python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+B, CTX, H, D = 8, 1 << 20, 64, 512
+M_CSA, M_HCA = 4, 128
+N_CSA, N_HCA = CTX // M_CSA, CTX // M_HCA
+HI, DI, TOPK, W, LWIN = 8, 128, 1024, 128, 128
+CFG_HCA, CFG_CSA = 3, 4            # config numbers used in the seeds
+HBM_PEAK_GBS = 8000.0
+
+
+def seed(cfg, tid, rep, b=0):
+    return 1000 * cfg + tid + 50 * rep + 100000 * (b + 1)
+
+
+def algorithmic_bytes():
+    """Bytes the method must move once per step (inputs read once + outputs written once)."""
+    keys = B * N_CSA * (DI // 2 + DI // 32)                       # MXFP4 codes + E8M0 scales
+    q_idx = B * HI * DI * 2 + B * HI * 4                          # indexer query + head weights
+    csa_rows = B * (TOPK + W) * 2 * D * 2                         # selected K/V rows + window rows
+    hca_rows = B * (N_HCA + W) * 2 * D * 2                        # every entry + window rows
+    q_o = 2 * (2 * B * H * D * 2 + B * H * 4)                     # q, o, lse for both layers
+    compress = B * (M_CSA * (2 * D + DI) * 2 + M_CSA * 4 + 2 * D * 2 + (DI // 2 + DI // 32)) \
+        + B * (M_HCA * 4 + 2 * D * 2)                             # HCA block rows are the window rows
+    parts = dict(csa_index_keys=keys, csa_index_q=q_idx, csa_attend_rows=csa_rows, hca_attend_rows=hca_rows,
+                 q_o_lse=q_o, compress=compress)
+    return sum(parts.values()), parts
+
+
+INDEX_KERNEL_BYTES = B * N_CSA * (DI // 2 + DI // 32) + B * HI * DI * 2 + B * HI * 4
+
+
+class Workload:
+    """Device tensors of the 1M-context decode step (three replicas of the streamed inputs)."""
+
+    def __init__(self, L, torch, synth, replicas):
+        dev = "cuda"
+        bf = torch.bfloat16
+        self.replicas = replicas
+        self.q_pos = torch.full((B, 1), CTX - 1, dtype=torch.int32, device=dev)
+        self.win_pos0 = torch.full((B,), CTX - LWIN, dtype=torch.int32, device=dev)
+        # CSA compressed K/V cache (gathered rows only; one copy)
+        self.kc = torch.empty((B, N_CSA, D), dtype=bf, device=dev)
+        self.vc = torch.empty((B, N_CSA, D), dtype=bf, device=dev)
+        for b in range(B):
+            self.kc[b] = synth.device_normal((N_CSA, D), seed(CFG_CSA, synth.KC, 0, b), bf)
+            self.vc[b] = synth.device_normal((N_CSA, D), seed(CFG_CSA, synth.VC, 0, b), bf)
+        self.r = []
+        zeros1 = torch.zeros(1, dtype=torch.float32, device=dev)
+        for rep in range(replicas):
+            t = {}
+            t["q"] = synth.device_normal((B, 1, H, D), seed(CFG_CSA, synth.Q, rep), bf)
+            t["qi"] = synth.device_normal((B, 1, HI, DI), seed(CFG_CSA, synth.QI, rep), bf)
+            t["wi"] = synth.device_uniform((B, 1, HI), seed(CFG_CSA, synth.WI, rep))
+            t["ki"] = torch.empty((B, N_CSA, DI // 2), dtype=torch.uint8, device=dev)
+            t["ks"] = torch.empty((B, N_CSA, DI // 32), dtype=torch.uint8, device=dev)
+            for b in range(B):
+                k32 = synth.device_normal((1, N_CSA, DI), seed(CFG_CSA, synth.KI, rep, b), torch.float32)
+                gz = torch.zeros((1, N_CSA), dtype=torch.float32, device=dev)
+                L.csa_compress(k32, gz, zeros1, 1, L.MXFP4_DTYPE, out=t["ki"][b:b + 1], out_scale=t["ks"][b:b + 1])
+                del k32, gz
+            t["kw"] = synth.device_normal((B, LWIN, D), seed(CFG_CSA, synth.KW, rep), bf)
+            t["vw"] = synth.device_normal((B, LWIN, D), seed(CFG_CSA, synth.VW, rep), bf)
+            t["kiw"] = synth.device_normal((B, LWIN, DI), seed(CFG_CSA, synth.RAW_KI, rep), bf)
+            t["gate"] = synth.device_normal((B, LWIN), seed(CFG_CSA, synth.GATE, rep), torch.float32)
+            t["bias"] = synth.device_normal((M_CSA,), seed(CFG_CSA, synth.BIAS, rep), torch.float32, std=0.1)
+            # HCA layer
+            t["hq"] = synth.device_normal((B, 1, H, D), seed(CFG_HCA, synth.Q, rep), bf)
+            t["hkc"] = synth.device_normal((B, N_HCA, D), seed(CFG_HCA, synth.KC, rep), bf)
+            t["hvc"] = synth.device_normal((B, N_HCA, D), seed(CFG_HCA, synth.VC, rep), bf)
+            t["hkw"] = synth.device_normal((B, LWIN, D), seed(CFG_HCA, synth.KW, rep), bf)
+            t["hvw"] = synth.device_normal((B, LWIN, D), seed(CFG_HCA, synth.VW, rep), bf)
+            t["hgate"] = synth.device_normal((B, LWIN), seed(CFG_HCA, synth.GATE, rep), torch.float32)
+            t["hbias"] = synth.device_normal((M_HCA,), seed(CFG_HCA, synth.BIAS, rep), torch.float32, std=0.1)
+            # outputs
+            t["idx"] = torch.empty((B, 1, TOPK), dtype=torch.int32, device=dev)
+            t["o"] = torch.empty((B, 1, H, D), dtype=bf, device=dev)
+            t["lse"] = torch.empty((B, 1, H), dtype=torch.float32, device=dev)
+            t["ho"] = torch.empty((B, 1, H, D), dtype=bf, device=dev)
+            t["hlse"] = torch.empty((B, 1, H), dtype=torch.float32, device=dev)
+            self.r.append(t)
+        torch.cuda.synchronize()
+
+
+def marshal_step(L, torch, wl, rep):
+    """The step as a list of (C function, argument tuple) with every pointer resolved."""
+    lib = L.lib()
+    t = wl.r[rep]
+    P = lambda x: ctypes.c_void_p(x.data_ptr()) if x is not None else None
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    scale = 1.0 / math.sqrt(D)
+    calls = []
+    g4 = t["gate"][:, LWIN - M_CSA:].contiguous()
+    t["g4"] = g4
+    # CSA: the newest 4-token block -> entry N_CSA-1 of K, V (bf16) and indexer key (MXFP4)
+    for src, dst in ((t["kw"], wl.kc), (t["vw"], wl.vc)):
+        calls.append((lib.csa_compress, (P(src[:, LWIN - M_CSA:]), L.BF16, P(g4), P(t["bias"]), B, M_CSA, D, M_CSA,
+                                         LWIN, P(dst[:, N_CSA - 1:]), None, L.BF16, N_CSA, st)))
+    calls.append((lib.csa_compress, (P(t["kiw"][:, LWIN - M_CSA:]), L.BF16, P(g4), P(t["bias"]), B, M_CSA, DI, M_CSA,
+                                     LWIN, P(t["ki"][:, N_CSA - 1:]), P(t["ks"][:, N_CSA - 1:]), L.MXFP4, N_CSA, st)))
+    # CSA: indexer + top-k
+    n = ctypes.c_size_t(0)
+    idx_args = (P(t["qi"]), L.BF16, P(t["wi"]), P(t["ki"]), P(t["ks"]), L.MXFP4, P(wl.q_pos), B, 1, HI, DI, N_CSA, 0,
+                M_CSA, TOPK, P(t["idx"]), None)
+    assert lib.csa_index_topk(*idx_args, None, ctypes.byref(n), st) == 0
+    t["ws_idx"] = torch.empty(n.value, dtype=torch.uint8, device="cuda")
+    t["ws_idx_n"] = ctypes.c_size_t(n.value)
+    calls.append((lib.csa_index_topk, idx_args + (P(t["ws_idx"]), ctypes.byref(t["ws_idx_n"]), st)))
+    index_call = len(calls) - 1
+    # CSA attention
+    att = (P(t["q"]), P(wl.kc), P(wl.vc), L.BF16, P(t["idx"]), TOPK, P(t["kw"]), P(t["vw"]), P(wl.win_pos0), LWIN, W,
+           P(wl.q_pos), B, 1, H, D, N_CSA, 0, ctypes.c_float(scale), P(t["o"]), P(t["lse"]))
+    assert lib.csa_attend(*att, None, ctypes.byref(n), st) == 0
+    t["ws_csa"] = torch.empty(max(n.value, 1), dtype=torch.uint8, device="cuda")
+    t["ws_csa_n"] = ctypes.c_size_t(n.value)
+    calls.append((lib.csa_attend, att + (P(t["ws_csa"]), ctypes.byref(t["ws_csa_n"]), st)))
+    # HCA: the newest 128-token block (the whole window) -> entry N_HCA-1
+    for src, dst in ((t["hkw"], t["hkc"]), (t["hvw"], t["hvc"])):
+        calls.append((lib.csa_compress, (P(src), L.BF16, P(t["hgate"]), P(t["hbias"]), B, M_HCA, D, M_HCA, LWIN,
+                                         P(dst[:, N_HCA - 1:]), None, L.BF16, N_HCA, st)))
+    hatt = (P(t["hq"]), P(t["hkc"]), P(t["hvc"]), L.BF16, M_HCA, P(t["hkw"]), P(t["hvw"]), P(wl.win_pos0), LWIN, W,
+            P(wl.q_pos), B, 1, H, D, N_HCA, 0, ctypes.c_float(scale), P(t["ho"]), P(t["hlse"]))
+    assert lib.hca_attend(*hatt, None, ctypes.byref(n), st) == 0
+    t["ws_hca"] = torch.empty(max(n.value, 1), dtype=torch.uint8, device="cuda")
+    t["ws_hca_n"] = ctypes.c_size_t(n.value)
+    calls.append((lib.hca_attend, hatt + (P(t["ws_hca"]), ctypes.byref(t["ws_hca_n"]), st)))
+    return calls, index_call
+
+
+class HipEvents:
+    """Raw hipEvent_t pairs from the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+
+def run_step(lib, calls, arm=None, index_call=-1):
+    for i, (fn, args) in enumerate(calls):
+        if arm is not None and i == index_call:
+            lib.dsv4_time_next_kernel(*arm)
+        st = fn(*args)
+        if st != 0:
+            raise RuntimeError(f"{fn.__name__}: {lib.dsv4_last_error().decode()}")
+
+
+# ------------------------------------------------------------------------------------ oracle leg
+def cpu_baseline(L, torch, synth, wl, budget_s):
+    """The float64 oracle on host cores, on whole sequences of replica 0 until ~budget_s."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import codecs, method
+
+    t = wl.r[0]
+
+    def bits(x):
+        return x.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    done, elapsed = 0, 0.0
+    scale = 1.0 / math.sqrt(D)
+    with threadpool_limits(limits=1):
+        for b in range(B):
+            # ---- inputs of sequence b (generated by torch's RNG; nothing from the library)
+            k32 = synth.device_normal((1, N_CSA, DI), seed(CFG_CSA, synth.KI, 0, b), torch.float32)[0].cpu().numpy()
+            packed, scales = codecs.encode_mxfp4(k32)            # the stored MXFP4 cache (untimed)
+            del k32
+            q = codecs.decode_bf16(bits(t["q"][b:b + 1]))
+            qi = codecs.decode_bf16(bits(t["qi"][b:b + 1]))
+            wi = t["wi"][b:b + 1].cpu().numpy()
+            kw, vw = codecs.decode_bf16(bits(t["kw"][b:b + 1])), codecs.decode_bf16(bits(t["vw"][b:b + 1]))
+            kiw = codecs.decode_bf16(bits(t["kiw"][b:b + 1]))
+            gate = t["gate"][b:b + 1].cpu().numpy()
+            bias = t["bias"].cpu().numpy()
+            hq = codecs.decode_bf16(bits(t["hq"][b:b + 1]))
+            hkc_bits, hvc_bits = bits(t["hkc"][b:b + 1]), bits(t["hvc"][b:b + 1])
+            hkw, hvw = codecs.decode_bf16(bits(t["hkw"][b:b + 1])), codecs.decode_bf16(bits(t["hvw"][b:b + 1]))
+            hgate, hbias = t["hgate"][b:b + 1].cpu().numpy(), t["hbias"].cpu().numpy()
+            kcb, vcb = wl.kc[b], wl.vc[b]
+            t0 = time.perf_counter()
+            # ---- CSA: compress the newest block (K, V, indexer key -> MXFP4)
+            g4 = gate[:, LWIN - M_CSA:]
+            new_k = method.compress(kw[:, LWIN - M_CSA:], g4, bias, M_CSA)
+            new_v = method.compress(vw[:, LWIN - M_CSA:], g4, bias, M_CSA)
+            new_ki = method.compress(kiw[:, LWIN - M_CSA:], g4, bias, M_CSA)
+            p_new, s_new = codecs.encode_mxfp4(new_ki[0].astype(np.float32))
+            packed[-1], scales[-1] = p_new[0], s_new[0]
+            ki = codecs.Stored(packed[None], codecs.MXFP4, scales[None])
+            pos = np.array([[CTX - 1]])
+            s = method.index_scores(qi, wi, ki, pos, M_CSA)
+            idx = method.topk(s, pos, M_CSA, TOPK)
+            sel = idx[0, 0][idx[0, 0] >= 0]
+            old = sel[sel < N_CSA - 1]
+            kg = codecs.decode_bf16(bits(kcb[torch.from_numpy(old).cuda()]))
+            vg = codecs.decode_bf16(bits(vcb[torch.from_numpy(old).cuda()]))
+            if len(old) < len(sel):
+                kg = np.concatenate([kg, new_k[0]])
+                vg = np.concatenate([vg, new_v[0]])
+            # attention over the gathered selection (listed 0..n-1) and the window
+            n_sel = len(sel)
+            o_c, _ = method.csa_attend(q, kg[None], vg[None], np.arange(n_sel)[None, None], kw, vw,
+                                       np.array([CTX - LWIN]), W, pos, scale)
+            # ---- HCA: compress the newest block, dense attention
+            hk = codecs.decode_bf16(hkc_bits)
+            hv = codecs.decode_bf16(hvc_bits)
+            hk[0, -1] = method.compress(hkw, hgate, hbias, M_HCA)[0, 0]
+            hv[0, -1] = method.compress(hvw, hgate, hbias, M_HCA)[0, 0]
+            o_h, _ = method.hca_attend(hq, hk, hv, M_HCA, hkw, hvw, np.array([CTX - LWIN]), W, pos, scale)
+            elapsed += time.perf_counter() - t0
+            done += 1
+            if elapsed >= budget_s:
+                break
+    return done, elapsed
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--replicas", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        sys.stderr.write("bench.py measures one GPU only: this build runs the path on a single MI355X "
+                         "(the multi-GPU sharding is described, not built). Use --gpus 1.\n")
+        sys.exit(2)
+
+    import torch
+
+    import long_context_attention_25_amd as L
+    import synth
+
+    lib = L.lib()
+    torch.cuda.set_device(0)
+    wl = Workload(L, torch, synth, args.replicas)
+    steps = [marshal_step(L, torch, wl, r) for r in range(args.replicas)]
+    index_call = steps[0][1]
+    ev = HipEvents()
+    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+
+    for i in range(args.warmup):
+        run_step(lib, steps[i % args.replicas][0])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        run_step(lib, steps[i % args.replicas][0], arm=pairs[i], index_call=index_call)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    k_ms = sum(ev.elapsed_ms(a, b) for a, b in pairs) / args.steps
+
+    total_bytes, parts = algorithmic_bytes()
+    qps = B / (ms / 1e3)
+    achieved = INDEX_KERNEL_BYTES / (k_ms / 1e3) / 1e9
+    out = {
+        "metric": "CSA+HCA decode queries/s at 1M ctx + achieved HBM GB/s vs peak",
+        "value": round(qps, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) / U(0,1); MXFP4 indexer keys, bf16 KV)",
+        "config": {"workload": "CSA decode (MXFP4 indexer, top-1024 of 262144 + 128 window) + HCA decode "
+                               "(8192 entries at 128x + 128 window) at 1M context, new block compressed each step",
+                   "batch": B, "context": CTX, "heads": H, "head_dim": D, "csa_entries": N_CSA,
+                   "hca_entries": N_HCA, "topk": TOPK, "window": W, "indexer_heads": HI, "indexer_dim": DI,
+                   "replicas": args.replicas},
+        "step_hbm_gbs": round(total_bytes / (ms / 1e3) / 1e9, 1),
+        "step_hbm_frac": round(total_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "bytes_per_step": total_bytes,
+        "roofline": {"bound": "hbm", "kernel": "index_mfma_kernel (MXFP4 keys)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": INDEX_KERNEL_BYTES, "avg_launch_ms": round(k_ms, 5)},
+    }
+    if not args.no_cpu_baseline:
+        done, el = cpu_baseline(L, torch, synth, wl, args.cpu_seconds)
+        out["cpu_baseline"] = {"value": round(done / el, 3), "unit": "queries/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{done} of {B} sequences of replica 0, one decode step each "
+                                         f"(both layers), {el:.1f} s on 1 host thread (float64 NumPy)"}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

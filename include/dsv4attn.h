@@ -1,0 +1,195 @@
+/*
+ * dsv4attn — CSA / HCA long-context attention for MI355X (gfx950), C ABI.
+ *
+ * The operations follow the method described on:
+ *   [CSA] honbul.tistory.com/221, section "CSA: 압축한 뒤, 필요한 기억만 골라서 보기"
+ *         (bundle several tokens into one compressed KV entry, let a small indexer
+ *         pick the relevant entries for the current token, attend only to those,
+ *         and keep recent tokens in a separate sliding window used together with
+ *         the compressed memory);
+ *   [HCA] same page, section "HCA: 더 강하게 압축하고, 압축된 전체를 보기"
+ *         (stronger compression, no sparse selection, attention over every
+ *         compressed entry);
+ *   [KVC] same page, section "KV cache를 줄이는 방식: 저장 구조까지 바꾼다"
+ *         (compressed-entry cache, sliding-window cache and not-yet-compressed tail
+ *         kept separately);
+ *   [P2]  pogovet.com "DeepSeek-V4: a million-token context that agents can actually
+ *         use", 상세 정리 §4 (4x compression by softmax-gated pooling with a learned
+ *         positional bias, FP4 lightning indexer choosing top-k compressed blocks per
+ *         query, sliding-window branch, 128x compression attended densely) and §5
+ *         (KV mostly FP8 with RoPE dims in BF16, indexer in FP4).
+ *
+ * Conventions for every call
+ *   - Tensor pointers are DEVICE pointers, row-major, last dimension contiguous.
+ *     q_pos and win_pos0 are device arrays too (so calls can be captured in a graph).
+ *   - Every call is asynchronous on `stream`; the library never synchronises,
+ *     allocates or frees.  Scratch memory comes from the caller's `workspace`.
+ *   - Workspace protocol: with workspace == NULL and ws_bytes != NULL the call only
+ *     writes the required byte count to *ws_bytes and launches nothing; with a
+ *     workspace of at least that size and *ws_bytes set to its size the call runs.
+ *     A call whose required size is 0 runs with workspace == NULL and ws_bytes == NULL.
+ *     A workspace may be reused by later calls on the same stream; calls that share
+ *     one workspace must not run concurrently.
+ *   - The caller owns every buffer.  Inputs are read-only; outputs are fully
+ *     overwritten; inputs, outputs and workspace must not overlap.
+ *   - All arguments are validated on the host before anything is launched; a bad
+ *     argument returns DSV4_ERR_INVALID_ARG, an unsupported combination
+ *     DSV4_ERR_UNSUPPORTED, a too-small workspace DSV4_ERR_WORKSPACE, a failed launch
+ *     DSV4_ERR_LAUNCH.  dsv4_last_error() then holds a message (per thread).
+ *     Device-side faults surface at the caller's next synchronisation.
+ *   - Softmax: lse is the natural-log log-sum-exp of scale * q.k and includes
+ *     `scale`.  An empty key set gives o = 0 and lse = -inf.
+ *   - MXFP4: two E2M1 codes per byte, the even element in the low nibble; one E8M0
+ *     scale byte (exponent + 127) per 32 consecutive elements, in a separate array.
+ *     fp8 is OCP E4M3 (bias 7, largest finite 448).  bf16 is IEEE binary32's top half.
+ */
+#ifndef DSV4ATTN_H
+#define DSV4ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSV4_OK = 0,
+  DSV4_ERR_INVALID_ARG = 1,
+  DSV4_ERR_UNSUPPORTED = 2,
+  DSV4_ERR_WORKSPACE = 3,
+  DSV4_ERR_LAUNCH = 4
+} dsv4_status;
+
+typedef enum {
+  DSV4_F32 = 0,
+  DSV4_BF16 = 1,
+  DSV4_FP8_E4M3 = 2,
+  DSV4_MXFP4 = 3
+} dsv4_dtype;
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int dsv4_version(void);
+/* Static name of a status code. */
+const char* dsv4_status_string(int status);
+/* Message of the last failing call on this thread ("" if none). */
+const char* dsv4_last_error(void);
+
+/*
+ * Instrumentation: arm two events that the NEXT library call made on this thread records
+ * immediately before and after its main kernel (the indexer kernel of csa_index_topk, the
+ * attention kernel of csa_attend / hca_attend, the pooling kernel of csa_compress, the
+ * merge kernel of lse_merge), on that call's stream.  Helper kernels of the same call are
+ * outside the pair.  Passing two NULLs disarms.  The events are owned by the caller and
+ * must have been created for the device of the call's stream.
+ */
+dsv4_status dsv4_time_next_kernel(hipEvent_t start, hipEvent_t stop);
+
+/*
+ * csa_compress — softmax-gated pooling of disjoint blocks of m raw tokens  [CSA], [HCA], [P2 §4].
+ *
+ *   y[b,i,:] = sum_{j<m} a_j * x[b, i*m + j, :],
+ *   a = softmax_j( gate[b, i*m + j] + pos_bias[j] )          (one gate logit per raw
+ *   token, one learned bias per slot; m = 4 for CSA, 128 for HCA; m = 1 is a plain
+ *   format conversion, e.g. to quantise indexer keys to MXFP4).
+ *
+ *   x        [B, x_bstride rows, C] of x_dt (F32 | BF16); batch b starts at row b*x_bstride.
+ *            Rows 0..T-1 of each batch are pooled.  x_bstride == 0 means T.
+ *   gate     [B, T] f32;  pos_bias [m] f32.
+ *   y        [B, y_bstride rows, C] of y_dt (F32 | BF16 | FP8_E4M3), or for MXFP4
+ *            [B, y_bstride rows, C/2] bytes plus y_scale [B, y_bstride rows, C/32].
+ *            Rows 0..T/m-1 are written.  y_bstride == 0 means T/m.
+ *   Requires T % m == 0, 1 <= m <= 1024, C % 8 == 0, C <= 1024 (F32 x) or 2048 (BF16 x),
+ *   C % 32 == 0 for MXFP4.
+ *   Arithmetic: softmax and sums in fp32; rounding to y_dt is nearest-even (fp8 and
+ *   MXFP4 saturate; MXFP4 scale = floor(log2 max|y|) - 2 per 32 channels, 0 for an
+ *   all-zero group).
+ */
+dsv4_status csa_compress(const void* x, int x_dt, const float* gate, const float* pos_bias,
+                         int64_t B, int64_t T, int64_t C, int32_t m, int64_t x_bstride,
+                         void* y, uint8_t* y_scale, int y_dt, int64_t y_bstride,
+                         hipStream_t stream);
+
+/*
+ * csa_index_topk — lightning-indexer scores and per-query top-k block selection  [CSA], [P2 §4].
+ *
+ *   n(p)      = min(N, floor((p + 1) / m))        blocks complete at or before position p
+ *   s[b,q,j]  = sum_{h<HI} wi[b,q,h] * max(0, qi[b,q,h,:] . ki[b,j,:])   for j < n(q_pos[b,q])
+ *   out_idx[b,q,:] = the min(k, n) indices with the largest s (equal scores: lower index
+ *   first), in ascending order, then -1 padding up to k.
+ *
+ *   qi        [B, Q, HI, DI] of qi_dt;  wi [B, Q, HI] f32;  q_pos [B, Q] int32 (device).
+ *   ki        [B, ki_bstride rows, DI] of ki_dt, or MXFP4 bytes [B, ki_bstride, DI/2] plus
+ *             ki_scale [B, ki_bstride, DI/32]; ki_bstride == 0 means N.
+ *   (qi_dt, ki_dt) in {(F32,F32), (BF16,BF16), (BF16,MXFP4), (FP8_E4M3,FP8_E4M3)};
+ *   HI in {4,8,16} and DI in {32,64,128,256} (F32 pair: 1 <= HI <= 16, 1 <= DI <= 256);
+ *   1 <= k <= 4096; N < 2^31; B*Q <= 65535.
+ *   out_idx   [B, Q, k] int32.   out_score [B, Q, k] f32 (score of each selected index,
+ *             -inf on padding) or NULL.
+ *   Scores are accumulated in fp32 (bf16 / fp8 / MXFP4 inputs are exact in bf16 / fp8
+ *   arithmetic); selection is exact on the fp32 scores.
+ */
+dsv4_status csa_index_topk(const void* qi, int qi_dt, const float* wi,
+                           const void* ki, const uint8_t* ki_scale, int ki_dt,
+                           const int32_t* q_pos, int64_t B, int64_t Q, int32_t HI, int32_t DI,
+                           int64_t N, int64_t ki_bstride, int32_t m, int32_t k,
+                           int32_t* out_idx, float* out_score,
+                           void* workspace, size_t* ws_bytes, hipStream_t stream);
+
+/*
+ * csa_attend — attention over the selected compressed entries plus the sliding
+ * window, as ONE softmax over the union  [CSA], [P2 §4].
+ *
+ *   S(b,q) = { kc/vc rows idx[b,q,t] : 0 <= idx < N }  U
+ *            { kw/vw rows r < L : q_pos - W < win_pos0[b] + r <= q_pos }
+ *   o[b,q,h,:] = sum_{s in S} softmax_s(scale * q[b,q,h,:] . K_s) V_s
+ *   lse[b,q,h] = log sum_{s in S} exp(scale * q[b,q,h,:] . K_s)
+ *   (multi-query: the H heads share one K/V; a recent token may contribute both through
+ *   its compressed entry and through its window row.)
+ *
+ *   q    [B, Q, H, D];  kc, vc [B, kv_bstride rows, D] (kv_bstride == 0 means N);
+ *   idx  [B, Q, k] int32 (entries outside [0, N) are skipped);
+ *   kw, vw [B, L, D]: row r holds position win_pos0[b] + r;  win_pos0 [B], q_pos [B, Q].
+ *   dt = F32 or BF16 for q, kc, vc, kw, vw and out.  BF16: D in {128, 256, 512} and
+ *   H in {16, 32, 48, 64}; F32: D <= 512.  B*Q <= 65535.  out [B, Q, H, D] of dt;  lse [B, Q, H] f32 or NULL.
+ *   fp32 accumulation; partial results are merged by log-sum-exp in fp32.
+ */
+dsv4_status csa_attend(const void* q, const void* kc, const void* vc, int dt,
+                       const int32_t* idx, int32_t k,
+                       const void* kw, const void* vw, const int32_t* win_pos0, int64_t L, int32_t W,
+                       const int32_t* q_pos, int64_t B, int64_t Q, int32_t H, int32_t D,
+                       int64_t N, int64_t kv_bstride, float scale,
+                       void* out, float* lse, void* workspace, size_t* ws_bytes, hipStream_t stream);
+
+/*
+ * hca_attend — dense attention over every visible compressed entry plus the sliding
+ * window, as ONE softmax  [HCA], [P2 §4].
+ *
+ *   S(b,q) = { kc/vc rows j < min(N, floor((q_pos + 1) / m)) }  U  window rows as in
+ *   csa_attend.  Arguments and layouts as csa_attend, without idx/k and with the
+ *   compression ratio m.
+ */
+dsv4_status hca_attend(const void* q, const void* kc, const void* vc, int dt, int32_t m,
+                       const void* kw, const void* vw, const int32_t* win_pos0, int64_t L, int32_t W,
+                       const int32_t* q_pos, int64_t B, int64_t Q, int32_t H, int32_t D,
+                       int64_t N, int64_t kv_bstride, float scale,
+                       void* out, float* lse, void* workspace, size_t* ws_bytes, hipStream_t stream);
+
+/*
+ * lse_merge — combine attention results over P disjoint key sets (e.g. the compressed
+ * part and the window part, or the shards of a split key range) into the result over
+ * their union:
+ *   M = max_p lse_p;  lse = M + log sum_p exp(lse_p - M);  o = sum_p exp(lse_p - lse) o_p
+ *   (a part with lse = -inf is empty; all parts empty -> o = 0, lse = -inf).
+ *
+ *   o_parts [P, R, D] f32;  lse_parts [P, R] f32;  out [R, D] of out_dt (F32 | BF16);
+ *   lse_out [R] f32 or NULL.  1 <= P <= 1024; D % 4 == 0, D <= 4096.
+ */
+dsv4_status lse_merge(const float* o_parts, const float* lse_parts, int32_t P, int64_t R, int32_t D,
+                      void* out, int out_dt, float* lse_out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSV4ATTN_H */

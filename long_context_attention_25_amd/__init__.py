@@ -1,0 +1,188 @@
+"""CSA / HCA long-context attention for MI355X — thin Python binding of libdsv4attn.so.
+
+Each function marshals torch tensors (device memory, the current HIP stream) into the
+C ABI declared in include/dsv4attn.h and returns the output tensors; every step of
+the computation runs in the library's HIP kernels.  There is no fallback: if the
+library is not built, or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["csa_compress", "csa_index_topk", "csa_attend", "hca_attend", "lse_merge", "lib", "LibError",
+           "F32", "BF16", "FP8_E4M3", "MXFP4", "MXFP4_DTYPE"]
+
+F32, BF16, FP8_E4M3, MXFP4 = 0, 1, 2, 3
+MXFP4_DTYPE = "mxfp4"            # marker for packed MXFP4 (uint8 codes + uint8 E8M0 scales)
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsv4attn.so")
+_lib = None
+
+_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_SIGS = {
+    "dsv4_version": ([], ctypes.c_int),
+    "dsv4_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "dsv4_last_error": ([], ctypes.c_char_p),
+    "dsv4_time_next_kernel": ([_p, _p], ctypes.c_int),
+    "csa_compress": ([_p, ctypes.c_int, _p, _p, _i64, _i64, _i64, _i32, _i64, _p, _p, ctypes.c_int, _i64, _p],
+                     ctypes.c_int),
+    "csa_index_topk": ([_p, ctypes.c_int, _p, _p, _p, ctypes.c_int, _p, _i64, _i64, _i32, _i32, _i64, _i64, _i32,
+                        _i32, _p, _p, _p, ctypes.POINTER(ctypes.c_size_t), _p], ctypes.c_int),
+    "csa_attend": ([_p, _p, _p, ctypes.c_int, _p, _i32, _p, _p, _p, _i64, _i32, _p, _i64, _i64, _i32, _i32, _i64,
+                    _i64, ctypes.c_float, _p, _p, _p, ctypes.POINTER(ctypes.c_size_t), _p], ctypes.c_int),
+    "hca_attend": ([_p, _p, _p, ctypes.c_int, _i32, _p, _p, _p, _i64, _i32, _p, _i64, _i64, _i32, _i32, _i64, _i64,
+                    ctypes.c_float, _p, _p, _p, ctypes.POINTER(ctypes.c_size_t), _p], ctypes.c_int),
+    "lse_merge": ([_p, _p, _i32, _i64, _i32, _p, ctypes.c_int, _p, _p], ctypes.c_int),
+}
+
+
+class LibError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (torch is imported first so that one HIP runtime is shared)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m long_context_attention_25_amd.build`")
+        _lib = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(_lib, name)
+            fn.argtypes = args
+            fn.restype = res
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise LibError(status, lib().dsv4_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dt(t) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float8_e4m3fn:
+        return FP8_E4M3
+    if t.dtype == torch.uint8:
+        return MXFP4
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _workspace(query, workspace):
+    """Run the size query; return (device buffer or None, size argument for the real call)."""
+    n = ctypes.c_size_t(0)
+    _check(query(n))
+    if n.value == 0:
+        return None, None
+    if workspace is None or workspace.numel() < n.value:
+        workspace = torch.empty(n.value, dtype=torch.uint8, device="cuda")
+    n.value = workspace.numel()
+    return workspace, ctypes.byref(n)
+
+
+def csa_compress(x, gate, pos_bias, m: int, y_dtype=torch.bfloat16, out=None, out_scale=None):
+    """Softmax-gated pooling of disjoint blocks of m tokens: x [B,T,C] -> y [B,T/m,C].
+
+    y_dtype: torch.float32 / torch.bfloat16 / torch.float8_e4m3fn, or MXFP4_DTYPE (returns
+    (codes [B,T/m,C/2] uint8, scales [B,T/m,C/32] uint8)).  `out` may be a [B, rows, ...] view
+    with rows >= T/m (e.g. the tail of a cache); its batch stride is passed through.
+    """
+    B, T, C = x.shape
+    nb = T // m
+    if y_dtype == MXFP4_DTYPE:
+        ydt = MXFP4
+        if out is None:
+            out = torch.empty((B, nb, C // 2), dtype=torch.uint8, device=x.device)
+            out_scale = torch.empty((B, nb, C // 32), dtype=torch.uint8, device=x.device)
+    else:
+        ydt = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3}[y_dtype]
+        if out is None:
+            out = torch.empty((B, nb, C), dtype=y_dtype, device=x.device)
+    y_bs = out.stride(0) // out.stride(1) if out.dim() == 3 and B > 0 else 0
+    x_bs = x.stride(0) // x.stride(1) if B > 0 else 0
+    _check(lib().csa_compress(_ptr(x), _dt(x), _ptr(gate), _ptr(pos_bias), B, T, C, m, x_bs, _ptr(out),
+                              _ptr(out_scale), ydt, y_bs, _stream()))
+    return (out, out_scale) if ydt == MXFP4 else out
+
+
+def csa_index_topk(qi, wi, ki, q_pos, m: int, k: int, ki_scale=None, N=None, with_scores=False, workspace=None,
+                   out_idx=None, out_score=None):
+    """Indexer scores + per-query top-k.  qi [B,Q,HI,DI], wi [B,Q,HI] f32, ki [B,rows,DI]
+    (or MXFP4 codes [B,rows,DI/2] uint8 with ki_scale [B,rows,DI/32]), q_pos [B,Q] int32.
+    Returns idx [B,Q,k] int32 (and scores [B,Q,k] f32 with with_scores)."""
+    B, Q, HI, DI = qi.shape
+    rows = ki.shape[1]
+    N = rows if N is None else N
+    kdt = _dt(ki)
+    k_bs = ki.stride(0) // ki.stride(1) if B > 0 else 0
+    if out_idx is None:
+        out_idx = torch.empty((B, Q, k), dtype=torch.int32, device=qi.device)
+    if with_scores and out_score is None:
+        out_score = torch.empty((B, Q, k), dtype=torch.float32, device=qi.device)
+    args = (_ptr(qi), _dt(qi), _ptr(wi), _ptr(ki), _ptr(ki_scale), kdt, _ptr(q_pos), B, Q, HI, DI, N, k_bs, m, k,
+            _ptr(out_idx), _ptr(out_score))
+    ws, n = _workspace(lambda n: lib().csa_index_topk(*args, None, ctypes.byref(n), _stream()), workspace)
+    _check(lib().csa_index_topk(*args, _ptr(ws), n, _stream()))
+    return (out_idx, out_score) if with_scores else out_idx
+
+
+def _attend_common(q, kc, kw, win_pos0, q_pos, N):
+    B, Q, H, D = q.shape
+    N = kc.shape[1] if N is None else N
+    kv_bs = kc.stride(0) // kc.stride(1) if B > 0 else 0
+    L = kw.shape[1]
+    return B, Q, H, D, N, kv_bs, L
+
+
+def csa_attend(q, kc, vc, idx, kw, vw, win_pos0, W: int, q_pos, scale: float, N=None, workspace=None, out=None,
+               lse=None):
+    """One softmax over the listed compressed entries and the window rows.
+    Returns (o [B,Q,H,D] in q's dtype, lse [B,Q,H] f32)."""
+    B, Q, H, D, N, kv_bs, L = _attend_common(q, kc, kw, win_pos0, q_pos, N)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Q, H), dtype=torch.float32, device=q.device) if lse is None else lse
+    args = (_ptr(q), _ptr(kc), _ptr(vc), _dt(q), _ptr(idx), idx.shape[2], _ptr(kw), _ptr(vw), _ptr(win_pos0), L, W,
+            _ptr(q_pos), B, Q, H, D, N, kv_bs, float(scale), _ptr(out), _ptr(lse))
+    ws, n = _workspace(lambda n: lib().csa_attend(*args, None, ctypes.byref(n), _stream()), workspace)
+    _check(lib().csa_attend(*args, _ptr(ws), n, _stream()))
+    return out, lse
+
+
+def hca_attend(q, kc, vc, m: int, kw, vw, win_pos0, W: int, q_pos, scale: float, N=None, workspace=None, out=None,
+               lse=None):
+    """One softmax over every visible compressed entry and the window rows."""
+    B, Q, H, D, N, kv_bs, L = _attend_common(q, kc, kw, win_pos0, q_pos, N)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Q, H), dtype=torch.float32, device=q.device) if lse is None else lse
+    args = (_ptr(q), _ptr(kc), _ptr(vc), _dt(q), m, _ptr(kw), _ptr(vw), _ptr(win_pos0), L, W, _ptr(q_pos), B, Q, H,
+            D, N, kv_bs, float(scale), _ptr(out), _ptr(lse))
+    ws, n = _workspace(lambda n: lib().hca_attend(*args, None, ctypes.byref(n), _stream()), workspace)
+    _check(lib().hca_attend(*args, _ptr(ws), n, _stream()))
+    return out, lse
+
+
+def lse_merge(o_parts, lse_parts, out_dtype=torch.float32, out=None, lse_out=None):
+    """Merge partial attentions over disjoint key sets: o_parts [P,R,D] f32, lse_parts [P,R] f32."""
+    P, R, D = o_parts.shape
+    out = torch.empty((R, D), dtype=out_dtype, device=o_parts.device) if out is None else out
+    lse_out = torch.empty((R,), dtype=torch.float32, device=o_parts.device) if lse_out is None else lse_out
+    _check(lib().lse_merge(_ptr(o_parts), _ptr(lse_parts), P, R, D, _ptr(out), _dt(out), _ptr(lse_out), _stream()))
+    return out, lse_out

@@ -1,0 +1,268 @@
+// C ABI of the library: host-side validation, workspace sizing and dispatch.
+// Every argument is checked before any HIP call; no call allocates or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/dsv4attn.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+thread_local hipEvent_t g_time_start = nullptr, g_time_stop = nullptr;
+
+dsv4_status fail(dsv4_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+dsv4_status ok() {
+  g_err[0] = '\0';
+  return DSV4_OK;
+}
+
+dsv4_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(DSV4_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+#define REQUIRE(cond, ...)                                  \
+  do {                                                      \
+    if (!(cond)) return fail(DSV4_ERR_INVALID_ARG, __VA_ARGS__); \
+  } while (0)
+#define SUPPORT(cond, ...)                                  \
+  do {                                                      \
+    if (!(cond)) return fail(DSV4_ERR_UNSUPPORTED, __VA_ARGS__); \
+  } while (0)
+
+// Workspace protocol shared by the calls that need scratch memory:
+//   workspace == NULL, ws_bytes != NULL : size query (writes *ws_bytes, launches nothing);
+//   workspace == NULL, ws_bytes == NULL : run a call whose required size is 0;
+//   workspace != NULL                   : run with *ws_bytes bytes of scratch.
+dsv4_status workspace_check(const char* what, void* ws, size_t* ws_bytes, size_t need, bool* query) {
+  *query = false;
+  if (ws == nullptr && ws_bytes != nullptr) {
+    *ws_bytes = need;
+    *query = true;
+    return ok();
+  }
+  if (ws == nullptr) {
+    if (need > 0) return fail(DSV4_ERR_WORKSPACE, "%s: requires a workspace of %zu bytes", what, need);
+    return ok();
+  }
+  REQUIRE(ws_bytes != nullptr, "%s: ws_bytes must not be NULL when a workspace is given", what);
+  if (*ws_bytes < need)
+    return fail(DSV4_ERR_WORKSPACE, "%s: workspace of %zu bytes is smaller than the %zu bytes required", what,
+                *ws_bytes, need);
+  return ok();
+}
+
+struct AttendCommon {
+  const void *q, *kc, *vc, *kw, *vw;
+  int dt;
+  const int32_t *win_pos0, *q_pos;
+  int64_t L;
+  int32_t W;
+  int64_t B, Q;
+  int32_t H, D;
+  int64_t N, kv_bstride;
+  float scale;
+  void* out;
+};
+
+dsv4_status check_attend(const char* what, const AttendCommon& c) {
+  REQUIRE(c.B >= 0 && c.Q >= 0 && c.N >= 0 && c.L >= 0 && c.W >= 0, "%s: sizes must be non-negative", what);
+  REQUIRE(c.H > 0 && c.D > 0, "%s: H and D must be positive", what);
+  SUPPORT(c.dt == DSV4_F32 || c.dt == DSV4_BF16, "%s: dt must be DSV4_F32 or DSV4_BF16", what);
+  if (c.dt == DSV4_BF16) {
+    SUPPORT(c.D == 128 || c.D == 256 || c.D == 512, "%s: bf16 path supports D in {128, 256, 512}, got %d", what, c.D);
+    SUPPORT(c.H % 16 == 0 && c.H <= 64, "%s: bf16 path supports H in {16, 32, 48, 64}, got %d", what, c.H);
+  } else {
+    SUPPORT(c.D <= 512, "%s: f32 path supports D <= 512, got %d", what, c.D);
+    SUPPORT(c.H <= 65535, "%s: H too large", what);
+  }
+  REQUIRE(c.kv_bstride == 0 || c.kv_bstride >= c.N, "%s: kv_bstride (%lld) must be 0 or >= N (%lld)", what,
+          (long long)c.kv_bstride, (long long)c.N);
+  REQUIRE(c.B * c.Q <= 65535, "%s: B*Q must be <= 65535", what);
+  if (c.B * c.Q > 0) {
+    REQUIRE(c.q && c.out && c.q_pos && c.win_pos0, "%s: q, out, q_pos and win_pos0 must not be NULL", what);
+    REQUIRE(c.N == 0 || (c.kc && c.vc), "%s: kc and vc must not be NULL when N > 0", what);
+    REQUIRE(c.L == 0 || (c.kw && c.vw), "%s: kw and vw must not be NULL when L > 0", what);
+  }
+  REQUIRE(c.scale == c.scale, "%s: scale is NaN", what);
+  return ok();
+}
+
+dsv4::AttendArgs to_args(const AttendCommon& c, bool csa, const int32_t* idx, int k, int m, float* lse) {
+  dsv4::AttendArgs a;
+  a.csa = csa;
+  a.q = c.q; a.kc = c.kc; a.vc = c.vc; a.f32 = c.dt == DSV4_F32;
+  a.idx = idx; a.k = k; a.m = m;
+  a.kw = c.kw; a.vw = c.vw; a.win_pos0 = c.win_pos0; a.L = c.L; a.W = c.W;
+  a.q_pos = c.q_pos; a.B = c.B; a.Q = c.Q; a.H = c.H; a.D = c.D;
+  a.N = c.N; a.kv_bs = c.kv_bstride ? c.kv_bstride : c.N;
+  a.scale = c.scale; a.out = c.out; a.lse = lse;
+  return a;
+}
+
+dsv4_status run_attend(const char* what, const dsv4::AttendArgs& a, void* ws, size_t* ws_bytes, hipStream_t st) {
+  dsv4::AttendPlan p = dsv4::plan_attend(a);
+  bool query;
+  dsv4_status s = workspace_check(what, ws, ws_bytes, p.ws_bytes, &query);
+  if (s != DSV4_OK || query) return s;
+  return launched(dsv4::launch_attend(a, p, ws, st), what);
+}
+
+}  // namespace
+
+namespace dsv4 {
+bool take_kernel_timing(hipEvent_t* start, hipEvent_t* stop) {
+  if (!g_time_start) return false;
+  *start = g_time_start;
+  *stop = g_time_stop;
+  g_time_start = g_time_stop = nullptr;
+  return true;
+}
+}  // namespace dsv4
+
+extern "C" {
+
+dsv4_status dsv4_time_next_kernel(hipEvent_t start, hipEvent_t stop) {
+  REQUIRE((start == nullptr) == (stop == nullptr), "dsv4_time_next_kernel: give both events or neither");
+  g_time_start = start;
+  g_time_stop = stop;
+  return ok();
+}
+
+int dsv4_version(void) { return 100; }
+
+const char* dsv4_status_string(int s) {
+  switch (s) {
+    case DSV4_OK: return "DSV4_OK";
+    case DSV4_ERR_INVALID_ARG: return "DSV4_ERR_INVALID_ARG";
+    case DSV4_ERR_UNSUPPORTED: return "DSV4_ERR_UNSUPPORTED";
+    case DSV4_ERR_WORKSPACE: return "DSV4_ERR_WORKSPACE";
+    case DSV4_ERR_LAUNCH: return "DSV4_ERR_LAUNCH";
+    default: return "DSV4_ERR_UNKNOWN";
+  }
+}
+
+const char* dsv4_last_error(void) { return g_err; }
+
+dsv4_status csa_compress(const void* x, int x_dt, const float* gate, const float* pos_bias, int64_t B, int64_t T,
+                         int64_t C, int32_t m, int64_t x_bstride, void* y, uint8_t* y_scale, int y_dt,
+                         int64_t y_bstride, hipStream_t stream) {
+  const char* what = "csa_compress";
+  REQUIRE(B >= 0 && T >= 0 && C > 0, "%s: need B >= 0, T >= 0, C > 0", what);
+  REQUIRE(m >= 1 && m <= 1024, "%s: m must be in [1, 1024], got %d", what, m);
+  REQUIRE(T % m == 0, "%s: T (%lld) must be a multiple of m (%d)", what, (long long)T, m);
+  SUPPORT(x_dt == DSV4_F32 || x_dt == DSV4_BF16, "%s: x_dt must be F32 or BF16", what);
+  SUPPORT(y_dt >= DSV4_F32 && y_dt <= DSV4_MXFP4, "%s: unknown y_dt %d", what, y_dt);
+  SUPPORT(C % 8 == 0, "%s: C must be a multiple of 8, got %lld", what, (long long)C);
+  SUPPORT(C <= (x_dt == DSV4_F32 ? 1024 : 2048), "%s: C too large (f32: <= 1024, bf16: <= 2048)", what);
+  if (y_dt == DSV4_MXFP4) SUPPORT(C % 32 == 0, "%s: MXFP4 output needs C %% 32 == 0", what);
+  REQUIRE(x_bstride == 0 || x_bstride >= T, "%s: x_bstride must be 0 or >= T", what);
+  REQUIRE(y_bstride == 0 || y_bstride >= T / m, "%s: y_bstride must be 0 or >= T/m", what);
+  if (B * T > 0) {
+    REQUIRE(x && gate && pos_bias && y, "%s: x, gate, pos_bias and y must not be NULL", what);
+    if (y_dt == DSV4_MXFP4) REQUIRE(y_scale, "%s: y_scale must not be NULL for MXFP4 output", what);
+  }
+  dsv4::CompressArgs a;
+  a.x = x; a.x_f32 = x_dt == DSV4_F32; a.gate = gate; a.bias = pos_bias;
+  a.B = B; a.T = T; a.C = C; a.m = m;
+  a.x_bs = x_bstride ? x_bstride : T;
+  a.y_bs = y_bstride ? y_bstride : T / m;
+  a.y = y; a.y_scale = y_scale; a.y_dt = y_dt;
+  if (a.total_blocks() == 0) return ok();
+  return launched(dsv4::launch_compress(a, stream), what);
+}
+
+dsv4_status csa_index_topk(const void* qi, int qi_dt, const float* wi, const void* ki, const uint8_t* ki_scale,
+                           int ki_dt, const int32_t* q_pos, int64_t B, int64_t Q, int32_t HI, int32_t DI, int64_t N,
+                           int64_t ki_bstride, int32_t m, int32_t k, int32_t* out_idx, float* out_score,
+                           void* workspace, size_t* ws_bytes, hipStream_t stream) {
+  const char* what = "csa_index_topk";
+  REQUIRE(B >= 0 && Q >= 0 && N >= 0, "%s: sizes must be non-negative", what);
+  REQUIRE(m >= 1, "%s: m must be >= 1", what);
+  REQUIRE(k >= 1 && k <= 4096, "%s: k must be in [1, 4096], got %d", what, k);
+  REQUIRE(N < (int64_t)1 << 31, "%s: N must be < 2^31", what);
+  REQUIRE(ki_bstride == 0 || ki_bstride >= N, "%s: ki_bstride must be 0 or >= N", what);
+  REQUIRE(B * Q <= 65535, "%s: B*Q must be <= 65535", what);
+  int kind;
+  if (qi_dt == DSV4_F32 && ki_dt == DSV4_F32) kind = dsv4::KEY_F32;
+  else if (qi_dt == DSV4_BF16 && ki_dt == DSV4_BF16) kind = dsv4::KEY_BF16;
+  else if (qi_dt == DSV4_BF16 && ki_dt == DSV4_MXFP4) kind = dsv4::KEY_MXFP4;
+  else if (qi_dt == DSV4_FP8_E4M3 && ki_dt == DSV4_FP8_E4M3) kind = dsv4::KEY_FP8;
+  else return fail(DSV4_ERR_UNSUPPORTED, "%s: unsupported (qi_dt, ki_dt) = (%d, %d)", what, qi_dt, ki_dt);
+  if (kind == dsv4::KEY_F32) {
+    SUPPORT(HI >= 1 && HI <= 16, "%s: f32 path supports HI in [1, 16], got %d", what, HI);
+    SUPPORT(DI >= 1 && DI <= 256, "%s: f32 path supports DI in [1, 256], got %d", what, DI);
+  } else {
+    SUPPORT(HI == 4 || HI == 8 || HI == 16, "%s: HI must be 4, 8 or 16, got %d", what, HI);
+    SUPPORT(DI == 32 || DI == 64 || DI == 128 || DI == 256, "%s: DI must be 32, 64, 128 or 256, got %d", what, DI);
+  }
+  const int64_t R = B * Q;
+  if (R > 0) {
+    REQUIRE(qi && wi && q_pos && out_idx, "%s: qi, wi, q_pos and out_idx must not be NULL", what);
+    REQUIRE(N == 0 || ki, "%s: ki must not be NULL when N > 0", what);
+    if (kind == dsv4::KEY_MXFP4) REQUIRE(N == 0 || ki_scale, "%s: ki_scale must not be NULL for MXFP4", what);
+  }
+  bool query;
+  dsv4_status s = workspace_check(what, workspace, ws_bytes, R > 0 ? dsv4::topk_workspace_bytes(R, N) : 0, &query);
+  if (s != DSV4_OK || query || R == 0) return s;
+  dsv4::IndexArgs a;
+  a.qi = qi; a.wi = wi; a.ki = ki; a.ki_scale = ki_scale; a.kind = kind; a.q_pos = q_pos;
+  a.B = B; a.Q = Q; a.HI = HI; a.DI = DI; a.N = N; a.k_bs = ki_bstride ? ki_bstride : N;
+  a.m = m; a.k = k; a.out_idx = out_idx; a.out_score = out_score;
+  return launched(dsv4::launch_index_topk(a, dsv4::topk_workspace_carve(workspace, R, N), stream), what);
+}
+
+dsv4_status csa_attend(const void* q, const void* kc, const void* vc, int dt, const int32_t* idx, int32_t k,
+                       const void* kw, const void* vw, const int32_t* win_pos0, int64_t L, int32_t W,
+                       const int32_t* q_pos, int64_t B, int64_t Q, int32_t H, int32_t D, int64_t N,
+                       int64_t kv_bstride, float scale, void* out, float* lse, void* workspace, size_t* ws_bytes,
+                       hipStream_t stream) {
+  const char* what = "csa_attend";
+  AttendCommon c{q, kc, vc, kw, vw, dt, win_pos0, q_pos, L, W, B, Q, H, D, N, kv_bstride, scale, out};
+  dsv4_status s = check_attend(what, c);
+  if (s != DSV4_OK) return s;
+  REQUIRE(k >= 0 && k <= 65536, "%s: k must be in [0, 65536]", what);
+  if (B * Q > 0 && k > 0) REQUIRE(idx, "%s: idx must not be NULL", what);
+  return run_attend(what, to_args(c, true, idx, k, 1, lse), workspace, ws_bytes, stream);
+}
+
+dsv4_status hca_attend(const void* q, const void* kc, const void* vc, int dt, int32_t m, const void* kw,
+                       const void* vw, const int32_t* win_pos0, int64_t L, int32_t W, const int32_t* q_pos,
+                       int64_t B, int64_t Q, int32_t H, int32_t D, int64_t N, int64_t kv_bstride, float scale,
+                       void* out, float* lse, void* workspace, size_t* ws_bytes, hipStream_t stream) {
+  const char* what = "hca_attend";
+  AttendCommon c{q, kc, vc, kw, vw, dt, win_pos0, q_pos, L, W, B, Q, H, D, N, kv_bstride, scale, out};
+  dsv4_status s = check_attend(what, c);
+  if (s != DSV4_OK) return s;
+  REQUIRE(m >= 1, "%s: m must be >= 1", what);
+  return run_attend(what, to_args(c, false, nullptr, 0, m, lse), workspace, ws_bytes, stream);
+}
+
+dsv4_status lse_merge(const float* o_parts, const float* lse_parts, int32_t P, int64_t R, int32_t D, void* out,
+                      int out_dt, float* lse_out, hipStream_t stream) {
+  const char* what = "lse_merge";
+  REQUIRE(P >= 1 && P <= 1024, "%s: P must be in [1, 1024], got %d", what, P);
+  REQUIRE(R >= 0, "%s: R must be non-negative", what);
+  REQUIRE(D > 0 && D % 4 == 0 && D <= 4096, "%s: D must be a positive multiple of 4, <= 4096", what);
+  SUPPORT(out_dt == DSV4_F32 || out_dt == DSV4_BF16, "%s: out_dt must be F32 or BF16", what);
+  REQUIRE(R <= 0x7fffffff, "%s: R too large", what);
+  if (R > 0) REQUIRE(o_parts && lse_parts && out, "%s: o_parts, lse_parts and out must not be NULL", what);
+  if (R == 0) return ok();
+  return launched(dsv4::launch_lse_merge(o_parts, lse_parts, P, R, D, out, out_dt == DSV4_F32, lse_out, stream),
+                  what);
+}
+
+}  // extern "C"

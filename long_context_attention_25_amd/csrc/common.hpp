@@ -1,0 +1,121 @@
+// Device-side helpers shared by the gfx950 kernels: storage-format conversions,
+// order-preserving score keys, wave reductions and MFMA operand types.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsv4 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kHistBits = 12;                 // top bits of a score key used by the first select pass
+constexpr int kHistBins = 1 << kHistBits;
+
+// ------------------------------------------------------------------ bf16
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {   // nearest-even
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Two floats to two bf16 (nearest-even, one v_cvt_pk_bf16_f32 on gfx950), low half first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 r;
+  r[0] = (__bf16)lo;
+  r[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Loads through the global address space (the pointers come from kernel-argument structs
+// or LDS, where the compiler cannot see that they are global).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 gload_u4(const void* p) {
+  const u32x4_t v = *(const __attribute__((address_space(1))) u32x4_t*)(p);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint32_t gload_u32(const void* p) {
+  return *(const __attribute__((address_space(1))) uint32_t*)(p);
+}
+
+// ------------------------------------------------------------------ OCP fp8 e4m3
+// Nearest-even on the 3-bit mantissa, saturating to +-448 (0x7e), NaN -> 0x7f.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
+  uint32_t u = __float_as_uint(f);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu;
+  if (__uint_as_float(a) >= 448.0f) return sign | 0x7eu;
+  uint32_t code;
+  if (a >= 0x3c800000u) {                           // >= 2^-6: normal range
+    uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);   // round away the low 20 mantissa bits
+    code = ((((r >> 23) & 0xffu) - 120u) << 3) | ((r >> 20) & 7u);
+  } else {                                          // subnormal: multiples of 2^-9
+    code = (uint32_t)__float2int_rn(__uint_as_float(a) * 512.0f);
+  }
+  return sign | code;
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+  return (c & 0x80u) ? -v : v;
+}
+
+// ------------------------------------------------------------------ OCP E2M1 (MXFP4 element)
+// Nearest-even on the grid {0, .5, 1, 1.5, 2, 3, 4, 6}, saturating to 6; sign in bit 3.
+__device__ __forceinline__ uint32_t f32_to_e2m1(float v) {
+  float a = fabsf(v);
+  uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+               (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+               (uint32_t)(a > 5.0f);
+  return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// Shared MXFP4 exponent of a 32-element group: floor(log2 amax) - 2, clamped to
+// [-127, 127]; 0 for an all-zero group.
+__device__ __forceinline__ int mx_shared_exp(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  int e = (int)((__float_as_uint(amax) >> 23) & 0xffu) - 127;   // floor(log2) for normals
+  if (e < -126) e = -127;                                         // subnormal amax
+  int x = e - 2;
+  return x < -127 ? -127 : (x > 127 ? 127 : x);
+}
+
+// ------------------------------------------------------------------ score keys
+// Monotone map float -> uint32 (larger score <=> larger key); -0 and +0 map together.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = (s == 0.0f) ? 0u : __float_as_uint(s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ------------------------------------------------------------------ wave helpers
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_fp8(long a, long b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
+}
+
+template <typename T>
+__device__ __forceinline__ T bit_cast_to(const uint4& v) {
+  return __builtin_bit_cast(T, v);
+}
+
+}  // namespace dsv4

@@ -1,0 +1,104 @@
+// Internal launcher interface between the C ABI (abi.cpp) and the kernels.
+// Arguments arrive here already validated.
+#pragma once
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsv4 {
+
+// Events armed by dsv4_time_next_kernel() on this thread, consumed by the next main
+// kernel launch (false when nothing is armed).
+bool take_kernel_timing(hipEvent_t* start, hipEvent_t* stop);
+
+// Launch of a call's main kernel: recorded between the armed events when there are any.
+#define DSV4_LAUNCH_MAIN(kernel, grid, block, smem, stream, ...)                                     \
+  do {                                                                                             \
+    hipEvent_t dsv4_t0_, dsv4_t1_;                                                                 \
+    if (::dsv4::take_kernel_timing(&dsv4_t0_, &dsv4_t1_))                                          \
+      hipExtLaunchKernelGGL(kernel, grid, block, smem, stream, dsv4_t0_, dsv4_t1_, 0, __VA_ARGS__);  \
+    else                                                                                           \
+      hipLaunchKernelGGL(kernel, grid, block, smem, stream, __VA_ARGS__);                          \
+  } while (0)
+
+struct CompressArgs {
+  const void* x;
+  bool x_f32;
+  const float* gate;
+  const float* bias;
+  int64_t B, T, C;
+  int m;
+  int64_t x_bs, y_bs;   // batch strides in rows
+  void* y;
+  uint8_t* y_scale;
+  int y_dt;             // 0 f32, 1 bf16, 2 fp8 e4m3, 3 MXFP4
+  int64_t total_blocks() const { return B * (T / m); }
+};
+hipError_t launch_compress(const CompressArgs& a, hipStream_t st);
+
+// ---------------------------------------------------------------- indexer + top-k
+enum KeyKind { KEY_F32 = 0, KEY_BF16 = 1, KEY_FP8 = 2, KEY_MXFP4 = 3 };
+
+struct IndexArgs {
+  const void* qi;
+  const float* wi;
+  const void* ki;
+  const uint8_t* ki_scale;
+  int kind;
+  const int32_t* q_pos;
+  int64_t B, Q;
+  int HI, DI;
+  int64_t N, k_bs;
+  int m, k;
+  int32_t* out_idx;
+  float* out_score;
+};
+
+// Workspace layout of the decode selection path (rows R = B*Q).
+struct TopkWorkspace {
+  float* scores;        // [R][N]
+  uint32_t* hist;       // [R][kHistBins]
+  uint32_t* counters;   // [R][2]: candidate count, finished workgroups
+  uint32_t* bitmap;     // [R][words]
+  uint64_t* cand;       // [R][N]
+};
+size_t topk_workspace_bytes(int64_t R, int64_t N);
+TopkWorkspace topk_workspace_carve(void* base, int64_t R, int64_t N);
+hipError_t launch_index_topk(const IndexArgs& a, const TopkWorkspace& ws, hipStream_t st);
+
+// ---------------------------------------------------------------- attention
+struct AttendArgs {
+  const void* q;
+  const void* kc;
+  const void* vc;
+  bool f32;
+  bool csa;             // CSA (listed entries) or HCA (every visible entry)
+  const int32_t* idx;   // CSA: [B,Q,k]
+  int k;
+  int m;                // HCA compression ratio
+  const void* kw;
+  const void* vw;
+  const int32_t* win_pos0;
+  int64_t L;
+  int W;
+  const int32_t* q_pos;
+  int64_t B, Q;
+  int H, D;
+  int64_t N, kv_bs;
+  float scale;
+  void* out;
+  float* lse;
+};
+struct AttendPlan {
+  int splits;           // key-range splits per (b, q)
+  int chunk;            // keys per split (multiple of the key tile)
+  size_t ws_bytes;
+};
+AttendPlan plan_attend(const AttendArgs& a);
+hipError_t launch_attend(const AttendArgs& a, const AttendPlan& p, void* ws, hipStream_t st);
+
+hipError_t launch_lse_merge(const float* o_parts, const float* lse_parts, int P, int64_t R, int D,
+                            void* out, bool out_f32, float* lse_out, hipStream_t st);
+
+}  // namespace dsv4

@@ -1,0 +1,54 @@
+"""Shared helpers of the GPU parity tests: tolerances and comparison rules.
+
+Tolerances (floating point):
+  * fp32 path: max over rows of ||o - o_ref||_inf / ||o_ref||_inf <= 1e-4.
+  * bf16 path: the same row metric <= 1e-2; lse absolute error <= 1e-2.
+  * MXFP4-indexer end-to-end: <= 5e-2.
+Top-k (integer result decided by floating point): with s* the oracle's k-th score and
+tau = 1e-3 * max(1, |s*|), every index whose oracle score is above s* + tau must be
+chosen, every chosen index must have an oracle score >= s* - tau, and the count is
+min(k, n).  Outside that tie zone the sets are equal.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def row_rel_err(o, o_ref) -> float:
+    o = np.asarray(o, dtype=np.float64)
+    o_ref = np.asarray(o_ref, dtype=np.float64)
+    D = o.shape[-1]
+    a = np.abs(o - o_ref).reshape(-1, D).max(axis=1)
+    b = np.abs(o_ref).reshape(-1, D).max(axis=1)
+    b = np.where(b > 0, b, 1.0)
+    return float((a / b).max()) if a.size else 0.0
+
+
+def lse_abs_err(lse, lse_ref) -> float:
+    lse = np.asarray(lse, np.float64)
+    lse_ref = np.asarray(lse_ref, np.float64)
+    both_inf = np.isneginf(lse) & np.isneginf(lse_ref)
+    with np.errstate(invalid="ignore"):
+        d = np.where(both_inf, 0.0, np.abs(lse - lse_ref))
+    return float(d.max()) if d.size else 0.0
+
+
+def check_topk(idx_gpu: np.ndarray, s_ref: np.ndarray, n: int, k: int, tau_rel: float = 1e-3):
+    """Validate one row of GPU top-k indices against the oracle's float64 scores."""
+    idx_gpu = np.asarray(idx_gpu)
+    take = min(k, n)
+    assert np.all(idx_gpu[take:] == -1), "padding must be -1"
+    sel = idx_gpu[:take].astype(np.int64)
+    assert np.all(np.diff(sel) > 0), "indices must be strictly ascending"
+    assert np.all((sel >= 0) & (sel < n)), "indices must be visible blocks"
+    if take == 0:
+        return 0
+    s = s_ref[:n]
+    order = np.argsort(-s, kind="stable")
+    s_star = s[order[take - 1]]
+    tau = tau_rel * max(1.0, abs(s_star))
+    must = np.nonzero(s > s_star + tau)[0]
+    assert np.all(np.isin(must, sel)), "a block clearly above the k-th score is missing"
+    assert np.all(s[sel] >= s_star - tau), "a block clearly below the k-th score was chosen"
+    ref = np.sort(order[:take])
+    return int(np.sum(~np.isin(sel, ref)))   # tie-zone swaps (allowed)
