@@ -6,7 +6,7 @@
 #include <cstdio>
 #include <cstring>
 
-#include "../../include/dsv4attn.h"
+#include "dsv4attn.h"
 #include "launch.hpp"
 
 namespace {

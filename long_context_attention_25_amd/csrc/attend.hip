@@ -27,10 +27,13 @@ namespace dsv4 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTile = 32;            // keys per sub-tile
+constexpr int kTile = 32;            // keys per sub-tile (split granularity)
+constexpr int kMaxCsaChunk = 2048;   // index entries of one CSA split (staged in LDS)
 constexpr int kTargetWorkgroups = 256;   // gfx950: 256 CUs, one attention workgroup each
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazyRescale = 8.0f;  // log2 units: rescale O only when the max grows by > 2^8
+constexpr int kHeads = 64;            // query heads handled by one workgroup (4 waves x 16)
 
 struct KeyRange {
   int64_t n_c;      // compressed part length (CSA: k list slots, HCA: visible blocks)
@@ -75,228 +78,267 @@ __device__ __forceinline__ int64_t key_row(const AttendArgs& a, int64_t bq, cons
 }
 
 // ---------------------------------------------------------------------------- bf16 / MFMA
-// Global row pointers (K and V) of list position `pos`; an empty slot points at a real
-// row (compressed row 0, or window row 0 when there are no compressed rows) and is
-// reported invalid, so tile loads never branch.
-__device__ __forceinline__ bool key_ptrs(const AttendArgs& a, int64_t bq, const KeyRange& kr, int64_t pos,
-                                         const uint16_t** kp, const uint16_t** vp) {
-  const int64_t b = bq / a.Q;
-  const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.kc) + b * a.kv_bs * a.D;
-  const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.vc) + b * a.kv_bs * a.D;
-  const uint16_t* kw = reinterpret_cast<const uint16_t*>(a.kw) + b * a.L * a.D;
-  const uint16_t* vw = reinterpret_cast<const uint16_t*>(a.vw) + b * a.L * a.D;
-  *kp = a.N > 0 ? kc : kw;
-  *vp = a.N > 0 ? vc : vw;
-  if (pos >= kr.n_tot) return false;
-  if (pos < kr.n_c) {
-    const int64_t j = a.csa ? (int64_t)a.idx[bq * a.k + pos] : pos;
-    if (j < 0 || j >= a.N) return false;
-    *kp = kc + j * a.D;
-    *vp = vc + j * a.D;
-    return true;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// Pointer held by lane `src` (src < 64): a scalar readlane when `src` is the same for the
+// whole wave, a cross-lane shuffle otherwise.
+template <bool kUniform>
+__device__ __forceinline__ const uint16_t* lane_ptr(const uint16_t* p, int src) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  uint32_t lo, hi;
+  if constexpr (kUniform) {
+    lo = __builtin_amdgcn_readlane((uint32_t)v, src);
+    hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), src);
+  } else {
+    lo = (uint32_t)__shfl((int)(uint32_t)v, src);
+    hi = (uint32_t)__shfl((int)(uint32_t)(v >> 32), src);
   }
-  const int64_t r = kr.r_lo + (pos - kr.n_c);
-  *kp = kw + r * a.D;
-  *vp = vw + r * a.D;
-  return true;
+  return reinterpret_cast<const uint16_t*>(((uint64_t)hi << 32) | lo);
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendArgs a, int64_t chunk, int splits,
+// LDS tiles are dense (row = one K or V row) with the 16-byte chunks of row r stored at
+// position chunk ^ swz(r): swz swaps the two 2-bit halves of r % 16, which keeps both the
+// K operand reads (16 rows, one chunk each) and the transposed V reads (4 rows x 2 chunks
+// per 16 lanes) on distinct banks.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// Async copy of 16 bytes per lane from global memory into LDS at dst + lane * 16.
+__device__ __forceinline__ void copy16_to_lds(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+
+// Wait until at most n vector-memory operations of this wave are outstanding (n < 64).
+// Copies into LDS count as vector-memory operations until their data is in LDS.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+}
+
+// Workgroup barrier for the tile ring: waits for this wave's LDS instructions only.  A
+// fence-based barrier would also wait for every copy into LDS still in flight (they are
+// LDS writes), i.e. for the next tile's prefetch; the copies a tile needs are waited for
+// explicitly with wait_vmcnt before this barrier.  The empty asm statements keep the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((0xf) | (0x3 << 14) | (0x7 << 4));   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One workgroup: 4 x DS waves = 4 head groups of 16 heads x DS slices of the head dim for
+// O (each slice computes the scores of its head group over the full head dim).  The key
+// list of the split is walked in 32-key tiles; tile t+1's K and V rows are copied straight
+// into the other half of a two-stage LDS ring while tile t is used.
+template <int D, int DS>
+__global__ __launch_bounds__(256 * DS) void attend_bf16_kernel(AttendArgs a, int64_t chunk, int splits,
                                                                float* __restrict__ o_part,
                                                                float* __restrict__ lse_part) {
+  constexpr int KT = 32;                   // keys per tile
+  constexpr int NT = 256 * DS;
+  constexpr int NWV = NT / kWave;
   constexpr int KS = D / 32;               // MFMA k-steps over the head dim
-  constexpr int KSTR = D + 8;              // LDS row stride of K (elements)
-  constexpr int VSTR = kTile + 8;          // LDS row stride of V^T (elements)
-  constexpr int KCH = D / 8;               // 16-byte chunks per row
-  constexpr int KROWS = kThreads / KCH;    // K rows loaded per pass
-  constexpr int KLD = kTile / KROWS;       // K loads (16 B) per thread and tile
-  constexpr int DP = D / 2;                // dim pairs
-  constexpr int KG = kThreads / DP;        // key groups for V
-  constexpr int KPG = kTile / KG;          // V loads (4 B) per thread and tile, keys of one group
-  constexpr int NREG = KLD * 4 > KPG ? KLD * 4 : KPG;
-  constexpr int MC = 128;                  // keys per macro-chunk (softmax max taken over it)
-  constexpr int TPM = MC / kTile;          // tiles per macro-chunk
-  constexpr int LDS_ELEMS = (kTile * KSTR > D * VSTR) ? kTile * KSTR : D * VSTR;
-  static_assert(KPG % 8 == 0, "V transpose needs groups of 8 keys");
+  constexpr int DH = D / DS;               // dims of O per wave
+  constexpr int RB = D * 2;                // bytes per row
+  constexpr int LPR = RB / 16;             // lanes (16-byte chunks) per row
+  constexpr int RPI = kWave / LPR;         // rows per copy instruction
+  constexpr int IPT = KT / RPI;            // copy instructions per tile and matrix
+  constexpr int IPW = IPT / NWV;           // ... per wave
+  constexpr int NL = 2 * IPW;              // vector-memory ops per wave and tile (K + V)
+  constexpr int TB = KT * RB;              // bytes of one tile
+  static_assert(IPT % NWV == 0 && IPW >= 1, "copy instructions must split evenly over the waves");
 
-  __shared__ __attribute__((aligned(16))) uint16_t tile[LDS_ELEMS];   // K rows or V^T, in turn
-  __shared__ const uint16_t* kptr[2][MC];
-  __shared__ const uint16_t* vptr[2][MC];
-  __shared__ uint32_t valid[2][MC / 32];
+  // two stages of K and V tiles, as separate arrays so that reads of one stage are known
+  // not to alias the copies into the other
+  __shared__ __attribute__((aligned(1024))) uint8_t k0[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t v0[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t k1[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t v1[TB];
+  __shared__ int32_t list[kMaxCsaChunk];                              // the split's index entries
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
   const int64_t bq = blockIdx.y;
+  const int64_t b = bq / a.Q;
   const int split = blockIdx.x;
   const KeyRange kr = key_range(a, bq);
   const int64_t s0 = (int64_t)split * chunk;
   int64_t s1 = s0 + chunk;
   if (s1 > kr.n_tot) s1 = kr.n_tot;
-  const int nmacro = s1 > s0 ? (int)((s1 - s0 + MC - 1) / MC) : 0;
+  const int ntile = s1 > s0 ? (int)((s1 - s0 + KT - 1) / KT) : 0;
 
-  const int head = wave * 16 + col;
-  const bool wave_on = wave * 16 < a.H;
+  const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.kc) + b * a.kv_bs * D;
+  const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.vc) + b * a.kv_bs * D;
+  const uint16_t* kw = reinterpret_cast<const uint16_t*>(a.kw) + b * a.L * D;
+  const uint16_t* vw = reinterpret_cast<const uint16_t*>(a.vw) + b * a.L * D;
 
+  const int hg = wave % 4, dh = wave / 4;  // head group (16 heads) and slice of D for O
+  const int head = hg * 16 + col;
+  const bool wave_on = hg * 16 < a.H;
+
+  // CSA: the split's index entries, once, in LDS (the tile loop issues no other loads)
+  if (a.csa) {
+    int64_t e1 = s1 < kr.n_c ? s1 : kr.n_c;
+    for (int64_t p = s0 + tid; p < e1; p += NT) list[p - s0] = a.idx[bq * a.k + p];
+  }
+  // Q^T operand of this lane: head `head`, dims g*D/4 + 8c .. +7 for k-step c
   uint4 qop[KS];
   {
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + (bq * a.H + (wave_on ? head : 0)) * D + g * (D / 4);
 #pragma unroll
     for (int c = 0; c < KS; ++c) qop[c] = wave_on ? gload_u4(qp + 8 * c) : make_uint4(0, 0, 0, 0);
   }
-  f32x4 acc[D / 16];
+  __syncthreads();
+
+  // Row pointers of tile t for key (lane % 32); invalid slots point at a real row.
+  const uint16_t* my_kp;
+  const uint16_t* my_vp;
+  uint32_t vmask;                           // validity of the tile's 32 keys
+  auto tile_ptrs = [&](int t) {
+    const int64_t pos = s0 + (int64_t)t * KT + (lane & (KT - 1));
+    bool ok = false;
+    const uint16_t* kp = a.N > 0 ? kc : kw;
+    const uint16_t* vp = a.N > 0 ? vc : vw;
+    if (pos < s1) {
+      if (pos < kr.n_c) {
+        const int64_t j = a.csa ? (int64_t)list[pos - s0] : pos;
+        if (j >= 0 && j < a.N) {
+          ok = true;
+          kp = kc + j * D;
+          vp = vc + j * D;
+        }
+      } else {
+        const int64_t r = kr.r_lo + (pos - kr.n_c);
+        ok = true;
+        kp = kw + r * D;
+        vp = vw + r * D;
+      }
+    }
+    my_kp = kp;
+    my_vp = vp;
+    vmask = (uint32_t)__ballot(ok);
+  };
+  auto issue = [&](uint8_t* kdst, uint8_t* vdst) {
 #pragma unroll
-  for (int i = 0; i < D / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < IPW; ++j) {
+      const int ins = wave + j * NWV;
+      const int r = ins * RPI + lane / LPR;            // row of the tile this lane copies
+      const int p = lane % LPR;                        // its chunk position in LDS
+      const int off = ((p ^ swz(r & 15)) * 8);         // source chunk (elements)
+      copy16_to_lds(lane_ptr<(RPI == 1)>(my_kp, r) + off, kdst + ins * 1024);
+      copy16_to_lds(lane_ptr<(RPI == 1)>(my_vp, r) + off, vdst + ins * 1024);
+    }
+  };
+
+  f32x4 acc[DH / 16];                      // O^T dims dh*DH + 16dt + 4g + i, head `head`
+#pragma unroll
+  for (int i = 0; i < DH / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.scale * kLog2e;
 
-  uint32_t reg[NREG];                      // the next tile in flight (K chunks or V dwords)
-  const int kcol = (tid % KCH) * 8, krow = tid / KCH;
-  const int dp = tid % DP, kg = tid / DP;
-
-#define DSV4_FILL(mc_, buf_)                                                                   \
-  do {                                                                                         \
-    if (tid < MC) {                                                                            \
-      const uint16_t *kp_, *vp_;                                                               \
-      const bool ok_ = key_ptrs(a, bq, kr, s0 + (int64_t)(mc_) * MC + tid, &kp_, &vp_);         \
-      kptr[buf_][tid] = kp_;                                                                   \
-      vptr[buf_][tid] = vp_;                                                                   \
-      const uint64_t m_ = __ballot(ok_);                                                       \
-      if (lane == 0) {                                                                         \
-        valid[buf_][2 * wave] = (uint32_t)m_;                                                  \
-        valid[buf_][2 * wave + 1] = (uint32_t)(m_ >> 32);                                      \
-      }                                                                                        \
-    }                                                                                          \
-  } while (0)
-#define DSV4_LOAD_K(buf_, t_)                                                                  \
-  do {                                                                                         \
-    _Pragma("unroll") for (int i_ = 0; i_ < KLD; ++i_) {                                       \
-      const uint4 v_ = gload_u4(kptr[buf_][(t_) * kTile + krow + i_ * KROWS] + kcol);          \
-      reg[4 * i_] = v_.x; reg[4 * i_ + 1] = v_.y; reg[4 * i_ + 2] = v_.z; reg[4 * i_ + 3] = v_.w; \
-    }                                                                                          \
-  } while (0)
-#define DSV4_LOAD_V(buf_, t_)                                                                  \
-  do {                                                                                         \
-    _Pragma("unroll") for (int e_ = 0; e_ < KPG; ++e_)                                         \
-      reg[e_] = gload_u32(vptr[buf_][(t_) * kTile + kg * KPG + e_] + 2 * dp);                  \
-  } while (0)
-
-  if (nmacro > 0) {
-    DSV4_FILL(0, 0);
-    __syncthreads();
-    DSV4_LOAD_K(0, 0);
-  }
-  for (int mc = 0; mc < nmacro; ++mc) {
-    const int buf = mc & 1;
-    const int64_t left = s1 - s0 - (int64_t)mc * MC;
-    const int ntile = left < MC ? (int)((left + kTile - 1) / kTile) : TPM;
-    // ---- phase K: scores of every key of the macro-chunk (S^T = K . Q^T)
-    f32x4 s[TPM][2];
+  auto compute = [&](const uint8_t* kt_l, const uint8_t* vt_l, uint32_t cur_mask) {
+    if (wave_on) {
+      // ---- S^T = K . Q^T for keys 0..15 and 16..31 of the tile
+      f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int t = 0; t < TPM; ++t) {
-      s[t][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-      s[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (t < ntile) {
-        __syncthreads();                   // the previous tile's LDS reads are done
+      for (int c = 0; c < KS; ++c) {
+        const bf16x8 qv = bit_cast_to<bf16x8>(qop[c]);
 #pragma unroll
-        for (int i = 0; i < KLD; ++i)
-          *reinterpret_cast<uint4*>(&tile[(krow + i * KROWS) * KSTR + kcol]) =
-              make_uint4(reg[4 * i], reg[4 * i + 1], reg[4 * i + 2], reg[4 * i + 3]);
-        __syncthreads();
-        if (t + 1 < ntile) DSV4_LOAD_K(buf, t + 1);
-        else DSV4_LOAD_V(buf, 0);
-        if (wave_on) {
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt) {
-            const uint16_t* kr_l = &tile[(kt * 16 + col) * KSTR + g * (D / 4)];
-#pragma unroll
-            for (int c = 0; c < KS; ++c) {
-              const uint4 kv = *reinterpret_cast<const uint4*>(kr_l + 8 * c);
-              s[t][kt] = mfma_bf16(bit_cast_to<bf16x8>(kv), bit_cast_to<bf16x8>(qop[c]), s[t][kt]);
-            }
-          }
+        for (int kt = 0; kt < 2; ++kt) {
+          const int r = kt * 16 + col;
+          const int chunk_l = g * (D / 32) + c;
+          const uint4 kv = *reinterpret_cast<const uint4*>(kt_l + r * RB + ((chunk_l ^ swz(r & 15)) * 16));
+          s[kt] = mfma_bf16(bit_cast_to<bf16x8>(kv), qv, s[kt]);
         }
       }
-    }
-    if (mc + 1 < nmacro) DSV4_FILL(mc + 1, buf ^ 1);
-    // ---- softmax over the macro-chunk for head `head` (lane: keys 16kt+4g+i of each tile)
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < TPM; ++t) {
-      const uint32_t vm = t < ntile ? valid[buf][t] : 0u;
+      // ---- softmax (lane holds keys 16kt + 4g + i of head `head`), lazy rescaling
+      float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bool ok = (vm >> (kt * 16 + 4 * g + i)) & 1u;
-          s[t][kt][i] = ok ? s[t][kt][i] * sl2 : -INFINITY;
-          mx = fmaxf(mx, s[t][kt][i]);
+          const bool ok = (cur_mask >> (kt * 16 + 4 * g + i)) & 1u;
+          s[kt][i] = ok ? s[kt][i] * sl2 : -INFINITY;
+          mx = fmaxf(mx, s[kt][i]);
         }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    if (m_run != -INFINITY && m_new > m_run) {
-      const float alpha = exp2f(m_run - m_new);
-      l_run *= alpha;
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      if (m_new > m_run + kLazyRescale) {
+        if (m_run != -INFINITY) {
+          const float alpha = exp2f(m_run - m_new);
+          l_run *= alpha;
 #pragma unroll
-      for (int i = 0; i < D / 16; ++i) acc[i] *= alpha;
-    }
-    m_run = m_new;
-    uint4 pop[TPM];
-#pragma unroll
-    for (int t = 0; t < TPM; ++t) {
-      float p[8];
+          for (int i = 0; i < DH / 16; ++i) acc[i] *= alpha;
+        }
+        m_run = m_new;
+      }
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
+      float pv[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        p[i] = exp2f(s[t][0][i] - m_use);
-        p[4 + i] = exp2f(s[t][1][i] - m_use);
+        pv[i] = exp2f(s[0][i] - m_use);
+        pv[4 + i] = exp2f(s[1][i] - m_use);
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) l_run += p[i];
-      pop[t] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                          pack_bf16x2(p[6], p[7]));
-    }
-    // ---- phase V: O^T += V^T . P^T
+      for (int i = 0; i < 8; ++i) l_run += pv[i];
+      // P^T operand: slots 0-3 are keys 4g+i, slots 4-7 keys 16+4g+i
+      const bf16x8 pb = bit_cast_to<bf16x8>(make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                                                       pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])));
+      // ---- O^T += V^T . P^T; V^T operands by transposed LDS reads of the row-major tile:
+      // lane p of a 16-lane block addresses key row 4g + p/4 (then 16 + 4g + p/4) at dims
+      // base + 4(p%4) and receives its own dim (base + p) from the four key rows.
+      const int kr0 = 4 * g + (col >> 2);
 #pragma unroll
-    for (int t = 0; t < TPM; ++t) {
-      if (t < ntile) {
-        __syncthreads();
-#pragma unroll
-        for (int e8 = 0; e8 < KPG; e8 += 8) {
-          uint4 lo, hi;
-          lo.x = __builtin_amdgcn_perm(reg[e8 + 1], reg[e8 + 0], 0x05040100u);
-          lo.y = __builtin_amdgcn_perm(reg[e8 + 3], reg[e8 + 2], 0x05040100u);
-          lo.z = __builtin_amdgcn_perm(reg[e8 + 5], reg[e8 + 4], 0x05040100u);
-          lo.w = __builtin_amdgcn_perm(reg[e8 + 7], reg[e8 + 6], 0x05040100u);
-          hi.x = __builtin_amdgcn_perm(reg[e8 + 1], reg[e8 + 0], 0x07060302u);
-          hi.y = __builtin_amdgcn_perm(reg[e8 + 3], reg[e8 + 2], 0x07060302u);
-          hi.z = __builtin_amdgcn_perm(reg[e8 + 5], reg[e8 + 4], 0x07060302u);
-          hi.w = __builtin_amdgcn_perm(reg[e8 + 7], reg[e8 + 6], 0x07060302u);
-          const int key0 = kg * KPG + e8;
-          *reinterpret_cast<uint4*>(&tile[(2 * dp) * VSTR + key0]) = lo;
-          *reinterpret_cast<uint4*>(&tile[(2 * dp + 1) * VSTR + key0]) = hi;
-        }
-        __syncthreads();
-        if (t + 1 < ntile) DSV4_LOAD_V(buf, t + 1);
-        else if (mc + 1 < nmacro) DSV4_LOAD_K(buf ^ 1, 0);
-        if (wave_on) {
-          const bf16x8 pb = bit_cast_to<bf16x8>(pop[t]);
-#pragma unroll
-          for (int dt = 0; dt < D / 16; ++dt) {
-            const uint16_t* vr = &tile[(dt * 16 + col) * VSTR + 4 * g];
-            const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-            const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
-            acc[dt] = mfma_bf16(bit_cast_to<bf16x8>(make_uint4(lo.x, lo.y, hi.x, hi.y)), pb, acc[dt]);
-          }
-        }
+      for (int dt = 0; dt < DH / 16; ++dt) {
+        const int dim = dh * DH + dt * 16 + 4 * (col & 3);
+        const int chunk_l = dim >> 3, half = (dim >> 2) & 1;
+        const uint8_t* p0 = vt_l + kr0 * RB + ((chunk_l ^ swz(kr0 & 15)) * 16) + half * 8;
+        const uint8_t* p1 = vt_l + (kr0 + 16) * RB + ((chunk_l ^ swz((kr0 + 16) & 15)) * 16) + half * 8;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p0);
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p1);
+        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+        acc[dt] = mfma_bf16(bit_cast_to<bf16x8>(make_uint4(l2.x, l2.y, h2.x, h2.y)), pb, acc[dt]);
       }
     }
+  };
+
+  // Tiles alternate between stage 0 (even t) and stage 1 (odd t).  Before tile t is used,
+  // tile t+1 is issued into the other stage; the barrier after tile t lets stage t%2 be
+  // overwritten by tile t+2.
+  uint32_t mask0 = 0, mask1 = 0;
+  if (ntile > 0) {
+    tile_ptrs(0);
+    mask0 = vmask;
+    issue(k0, v0);
   }
-#undef DSV4_FILL
-#undef DSV4_LOAD_K
-#undef DSV4_LOAD_V
+  for (int t = 0; t < ntile; t += 2) {
+    if (t + 1 < ntile) {
+      tile_ptrs(t + 1);
+      mask1 = vmask;
+      issue(k1, v1);
+      wait_vmcnt<NL>();                    // tile t has landed; tile t+1 stays in flight
+    } else {
+      wait_vmcnt<0>();
+    }
+    tile_barrier();
+    compute(k0, v0, mask0);
+    tile_barrier();
+    if (t + 1 >= ntile) break;
+    if (t + 2 < ntile) {
+      tile_ptrs(t + 2);
+      mask0 = vmask;
+      issue(k0, v0);
+      wait_vmcnt<NL>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    tile_barrier();
+    compute(k1, v1, mask1);
+    tile_barrier();
+  }
 
   if (!wave_on) return;
   l_run += __shfl_xor(l_run, 16);
@@ -306,22 +348,22 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendArgs a, int
   const int64_t R = a.B * a.Q * a.H;
   const int64_t orow = bq * a.H + head;
   if (splits == 1) {
-    uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + orow * D;
+    uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + orow * D + dh * DH;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
+    for (int dt = 0; dt < DH / 16; ++dt) {
       uint2 w;
       w.x = pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv);
       w.y = pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv);
       *reinterpret_cast<uint2*>(out + dt * 16 + 4 * g) = w;
     }
-    if (g == 0 && a.lse) a.lse[orow] = lse;
+    if (g == 0 && dh == 0 && a.lse) a.lse[orow] = lse;
   } else {
-    float* op = o_part + ((int64_t)split * R + orow) * D;
+    float* op = o_part + ((int64_t)split * R + orow) * D + dh * DH;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
+    for (int dt = 0; dt < DH / 16; ++dt)
       *reinterpret_cast<float4*>(op + dt * 16 + 4 * g) =
           make_float4(acc[dt][0] * inv, acc[dt][1] * inv, acc[dt][2] * inv, acc[dt][3] * inv);
-    if (g == 0) lse_part[(int64_t)split * R + orow] = lse;
+    if (g == 0 && dh == 0) lse_part[(int64_t)split * R + orow] = lse;
   }
 }
 
@@ -498,6 +540,7 @@ AttendPlan plan_attend(const AttendArgs& a) {
   if (want < 1) want = 1;
   int64_t chunk = (n_max + want - 1) / want;
   chunk = ((chunk + kTile - 1) / kTile) * kTile;
+  if (a.csa && chunk > kMaxCsaChunk) chunk = kMaxCsaChunk;
   int64_t splits = (n_max + chunk - 1) / chunk;
   p.splits = (int)splits;
   p.chunk = (int)chunk;
@@ -525,9 +568,9 @@ hipError_t launch_attend(const AttendArgs& a, const AttendPlan& p, void* ws, hip
   }
   dim3 grid((unsigned)p.splits, (unsigned)rows);
   switch (a.D) {
-    case 128: DSV4_LAUNCH_MAIN(attend_bf16_kernel<128>, grid, dim3(kThreads), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part); break;
-    case 256: DSV4_LAUNCH_MAIN(attend_bf16_kernel<256>, grid, dim3(kThreads), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part); break;
-    default: DSV4_LAUNCH_MAIN(attend_bf16_kernel<512>, grid, dim3(kThreads), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part); break;
+    case 128: DSV4_LAUNCH_MAIN((attend_bf16_kernel<128, 1>), grid, dim3(kThreads), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part); break;
+    case 256: DSV4_LAUNCH_MAIN((attend_bf16_kernel<256, 1>), grid, dim3(kThreads), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part); break;
+    default: DSV4_LAUNCH_MAIN((attend_bf16_kernel<512, 2>), grid, dim3(kThreads * 2), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;

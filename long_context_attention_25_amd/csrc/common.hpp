@@ -94,6 +94,17 @@ __device__ __forceinline__ uint32_t score_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// ------------------------------------------------------------------ barriers
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for every
+// outstanding global access (vmcnt(0)), which would drain the next tile's prefetch at
+// each tile; this one waits for the wave's LDS operations and leaves global loads in
+// flight.  Use it only where the data exchanged through the barrier lives in LDS.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ------------------------------------------------------------------ wave helpers
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -31,6 +31,7 @@ constexpr int kThreads = 256;
 constexpr int kKeysPerIter = 256;   // 4 waves x 4 tiles x 16 keys
 constexpr int kMaxSelGroups = 64;   // select workgroups per row at most
 constexpr int kSelCounters = 1 + kMaxSelGroups;
+constexpr int kCandCap = 4096;      // candidates staged in LDS by the finishing workgroup
 
 __device__ __forceinline__ uint32_t vis_blocks(const int32_t* q_pos, int64_t row, int m, int64_t N) {
   int64_t p = q_pos[row];
@@ -69,11 +70,11 @@ __global__ void clear_kernel(uint32_t* p, int64_t n) {
 }
 
 // Writes one score and counts it in the LDS histogram of its query slot.
-__device__ __forceinline__ void emit_score(float* scores, uint32_t* hist_l, int64_t row, int64_t N,
-                                           int64_t key, uint32_t nvis, float v) {
+__device__ __forceinline__ void emit_score(float* scores, uint32_t* hist_l, int64_t row, int64_t sstride,
+                                           int64_t N, int64_t key, uint32_t nvis, float v) {
   if (key >= N) return;
   bool vis = key < (int64_t)nvis;
-  scores[row * N + key] = vis ? v : -INFINITY;
+  scores[row * sstride + key] = vis ? v : -INFINITY;
   if (vis) atomicAdd(&hist_l[score_key(v) >> (32 - kHistBits)], 1u);
 }
 
@@ -88,7 +89,7 @@ __device__ __forceinline__ void flush_hist(const uint32_t* hist_l, uint32_t* his
 __global__ __launch_bounds__(kThreads) void index_f32_kernel(
     const float* __restrict__ qi, const float* __restrict__ wi, const float* __restrict__ ki,
     const int32_t* __restrict__ q_pos, int64_t N, int64_t k_bs, int64_t Q, int HI, int DI, int m,
-    float* __restrict__ scores, uint32_t* __restrict__ hist_g) {
+    float* __restrict__ scores, int64_t sstride, uint32_t* __restrict__ hist_g) {
   extern __shared__ uint32_t sm[];
   uint32_t* hist_l = sm;
   float* qs = reinterpret_cast<float*>(sm + kHistBins);
@@ -111,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void index_f32_kernel(
         s = fmaf(ws[h], fmaxf(d, 0.f), s);
       }
     }
-    emit_score(scores, hist_l, row, N, key, nvis, s);
+    emit_score(scores, hist_l, row, sstride, N, key, nvis, s);
   }
   __syncthreads();
   flush_hist(hist_l, hist_g, row);
@@ -180,7 +181,7 @@ template <int KIND, int DI, int HI>
 __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
     const uint8_t* __restrict__ qi, const float* __restrict__ wi, const uint8_t* __restrict__ ki,
     const uint8_t* __restrict__ ksc, const int32_t* __restrict__ q_pos, int64_t N, int64_t k_bs,
-    int64_t Q, int m, int64_t chunk, float* __restrict__ scores, uint32_t* __restrict__ hist_g) {
+    int64_t Q, int m, int64_t chunk, float* __restrict__ scores, int64_t sstride, uint32_t* __restrict__ hist_g) {
   constexpr int QPT = 16 / HI;          // queries per 16-row MFMA tile
   constexpr int KS = DI / 32;
   constexpr int GPQ = HI / 4;           // lane groups per query slot
@@ -230,23 +231,38 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
     sbase = ksc + b * k_bs * (DI / 32);
   }
 
+  // Each wave takes 64 consecutive keys (4 tiles) per step; the next step's tiles are
+  // loaded before this step's are used.  Key indices past the range are clamped to its
+  // last key, so loads never branch; only the score write is guarded.
   const int64_t c0 = (int64_t)blockIdx.x * chunk;
   int64_t c1 = c0 + chunk;
   if (c1 > N) c1 = N;
-  for (int64_t base = c0 + wave * 64; base < c1; base += kKeysPerIter) {
-    KeyTile<KIND, DI> kt[4];
+  const int64_t klast = c1 - 1;
+  KeyTile<KIND, DI> cur[4], nxt[4];
+  int64_t base = c0 + wave * 64;
+  if (base < c1) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      int64_t key = base + u * 16 + col;
-      kt[u].load(kbase, sbase, key, g, key < c1);
+      const int64_t key = base + u * 16 + col;
+      cur[u].load(kbase, sbase, key < klast ? key : klast, g, true);
+    }
+  }
+  for (; base < c1; base += kKeysPerIter) {
+    const int64_t nb = base + kKeysPerIter;
+    if (nb < c1) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t key = nb + u * 16 + col;
+        nxt[u].load(kbase, sbase, key < klast ? key : klast, g, true);
+      }
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < KS; ++c) {
-        if constexpr (KIND == KEY_FP8) acc = mfma_fp8(__builtin_bit_cast(long, qa8[c]), kt[u].op(c), acc);
-        else acc = mfma_bf16(bit_cast_to<bf16x8>(qa16[c]), kt[u].op(c), acc);
+        if constexpr (KIND == KEY_FP8) acc = mfma_fp8(__builtin_bit_cast(long, qa8[c]), cur[u].op(c), acc);
+        else acc = mfma_bf16(bit_cast_to<bf16x8>(qa16[c]), cur[u].op(c), acc);
       }
       float v = wv[0] * fmaxf(acc[0], 0.f);
       v = fmaf(wv[1], fmaxf(acc[1], 0.f), v);
@@ -254,8 +270,11 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
       v = fmaf(wv[3], fmaxf(acc[3], 0.f), v);
       if constexpr (GPQ >= 2) v += __shfl_xor(v, 16);
       if constexpr (GPQ >= 4) v += __shfl_xor(v, 32);
-      if (owner) emit_score(scores, hist_l + qs_c * kHistBins, row_c, N, base + u * 16 + col, nvis, v);
+      const int64_t key = base + u * 16 + col;
+      if (owner && key < c1) emit_score(scores, hist_l + qs_c * kHistBins, row_c, sstride, N, key, nvis, v);
     }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) cur[u] = nxt[u];
   }
   __syncthreads();
   for (int s = 0; s < nq; ++s) flush_hist(hist_l + s * kHistBins, hist_g, b * Q + qt * QPT + s);
@@ -265,7 +284,7 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
 __global__ __launch_bounds__(kThreads) void select_kernel(
     const float* __restrict__ scores, const uint32_t* __restrict__ hist_g, uint32_t* __restrict__ counters,
     uint32_t* __restrict__ bitmap, uint64_t* __restrict__ cand, const int32_t* __restrict__ q_pos,
-    int64_t N, int64_t words, int m, int k, int64_t chunk, int32_t* __restrict__ out_idx,
+    int64_t N, int64_t sstride, int64_t words, int m, int k, int64_t chunk, int32_t* __restrict__ out_idx,
     float* __restrict__ out_score) {
   __shared__ uint32_t sh_misc[16];
   __shared__ uint32_t sh_h[256];
@@ -298,53 +317,50 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
   const uint32_t tbin = sh_misc[4], cnt_above = sh_misc[5];
 
   // ---- bitmap words of this range (keys strictly above the bin) + candidates (in the bin).
-  // Candidates go to this workgroup's own slice of the candidate buffer (its key range),
-  // counted with LDS atomics; only the arrival below touches a shared global counter.
+  // Thread t owns 64 consecutive keys per 16384-key group: 16 float4 loads in flight, its
+  // two bitmap words built in registers, its candidates placed by a block-wide scan into
+  // this workgroup's own slice of the candidate buffer.
   const int64_t c0 = (int64_t)blockIdx.x * chunk;
   int64_t c1 = c0 + chunk;
   if (c1 > (int64_t)n) c1 = n;
   uint32_t* bm = bitmap + row * words;
   uint64_t* cr = cand + row * N + c0;
   uint32_t* rc = counters + row * kSelCounters;     // [0] arrivals, [1 + w] candidates of workgroup w
-  if (tid == 0) sh_misc[7] = 0u;
-  __syncthreads();
-  constexpr int kBatch = 8;
-  for (int64_t base0 = c0 + wave * 64; base0 < c1; base0 += kThreads * kBatch) {
-    float sv[kBatch];
+  const float* srow_in = scores + row * sstride;
+  uint32_t cand_base = 0;
+  for (int64_t gbase = c0; gbase < c1; gbase += (int64_t)kThreads * 64) {
+    const int64_t kb = gbase + (int64_t)tid * 64;
+    float4 v[16];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      int64_t j = base0 + u * kThreads + lane;
-      sv[u] = j < c1 ? scores[row * N + j] : 0.f;
-    }
+    for (int i = 0; i < 16; ++i)
+      v[i] = kb < c1 ? reinterpret_cast<const float4*>(srow_in + kb)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    uint32_t wlo = 0, whi = 0, ncand = 0;
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int64_t base = base0 + u * kThreads;
-      if (base >= c1) break;
-      const int64_t j = base + lane;
-      const bool in = j < c1;
-      const uint32_t key = score_key(sv[u]);
-      const uint32_t bin = key >> (32 - kHistBits);
-      const bool sel = in && bin > tbin;
-      const bool cnd = in && bin == tbin;
-      const uint64_t bs = __ballot(sel);
-      const uint64_t bc = __ballot(cnd);
-      if (lane == 0) {
-        bm[base / 32] = (uint32_t)bs;
-        if (base + 32 < c1) bm[base / 32 + 1] = (uint32_t)(bs >> 32);
+    for (int e = 0; e < 64; ++e) {
+      const float sv = (e & 3) == 0 ? v[e >> 2].x : (e & 3) == 1 ? v[e >> 2].y : (e & 3) == 2 ? v[e >> 2].z : v[e >> 2].w;
+      const uint32_t bin = score_key(sv) >> (32 - kHistBits);
+      const bool in = kb + e < c1;
+      if (in && bin > tbin) {
+        if (e < 32) wlo |= 1u << e;
+        else whi |= 1u << (e - 32);
       }
-      if (bc) {
-        uint32_t pos0 = 0;
-        if (lane == 0) pos0 = atomicAdd(&sh_misc[7], (uint32_t)__popcll(bc));
-        pos0 = __shfl(pos0, 0);
-        if (cnd) {
-          const uint32_t rank = __popcll(bc & ((1ull << lane) - 1ull));
-          cr[pos0 + rank] = ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)j);
-        }
+      ncand += (in && bin == tbin) ? 1u : 0u;
+    }
+    if (kb < c1) *reinterpret_cast<uint2*>(bm + kb / 32) = make_uint2(wlo, whi);
+    uint32_t gtot;
+    uint32_t pos = cand_base + block_excl_scan(ncand, sh_misc, &gtot);
+    if (ncand) {
+#pragma unroll
+      for (int e = 0; e < 64; ++e) {
+        const float sv = (e & 3) == 0 ? v[e >> 2].x : (e & 3) == 1 ? v[e >> 2].y : (e & 3) == 2 ? v[e >> 2].z : v[e >> 2].w;
+        const uint32_t key = score_key(sv);
+        if (kb + e < c1 && (key >> (32 - kHistBits)) == tbin)
+          cr[pos++] = ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)(kb + e));
       }
     }
+    cand_base += gtot;
   }
-  __syncthreads();
-  if (tid == 0) rc[1 + blockIdx.x] = sh_misc[7];
+  if (tid == 0) rc[1 + blockIdx.x] = cand_base;
 
   // ---- the last workgroup of the row finishes the selection (every thread releases its
   // own bitmap / candidate stores before the arrival is counted)
@@ -363,15 +379,53 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
     sh_cnt[w] = __hip_atomic_load(&rc[1 + w], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const uint64_t* call = cand + row * N;
-  uint32_t c = 0;
-  for (int w = 0; w < (int)gridDim.x; ++w) c += sh_cnt[w];
-#define DSV4_FOR_CAND(body)                                             \
-  for (int w_ = 0; w_ < (int)gridDim.x; ++w_) {                         \
-    const uint64_t* cw_ = call + (int64_t)w_ * chunk;                   \
-    for (uint32_t i_ = tid; i_ < sh_cnt[w_]; i_ += kThreads) {          \
-      const uint64_t comp = cw_[i_];                                    \
-      body                                                              \
-    }                                                                   \
+  // Stage the candidates in LDS when they fit (the usual case: about one histogram bin of
+  // keys); otherwise the passes below read them from each workgroup's slice in turn.
+  __shared__ uint64_t sh_cand[kCandCap];
+  __shared__ uint32_t sh_pre[kMaxSelGroups + 1];
+  if (tid == 0) {
+    uint32_t acc_ = 0;
+    for (int w = 0; w < (int)gridDim.x; ++w) {
+      sh_pre[w] = acc_;
+      acc_ += sh_cnt[w];
+    }
+    sh_pre[gridDim.x] = acc_;
+  }
+  __syncthreads();
+  const uint32_t c = sh_pre[gridDim.x];
+  const bool in_lds = c <= (uint32_t)kCandCap;
+  if (in_lds) {
+    // kCandCap / kThreads = 16 slots per thread: all loads issued before any is stored
+    constexpr int kPer = kCandCap / kThreads;
+    uint64_t vals[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const uint32_t f = tid + u * kThreads;
+      int w = 0;
+      while (w + 1 < (int)gridDim.x && sh_pre[w + 1] <= f) ++w;
+      vals[u] = f < c ? call[(int64_t)w * chunk + (f - sh_pre[w])] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const uint32_t f = tid + u * kThreads;
+      if (f < c) sh_cand[f] = vals[u];
+    }
+    __syncthreads();
+  }
+#define DSV4_FOR_CAND(body)                                               \
+  if (in_lds) {                                                           \
+    for (uint32_t f_ = tid; f_ < c; f_ += kThreads) {                     \
+      const uint64_t comp = sh_cand[f_];                                  \
+      body                                                                \
+    }                                                                     \
+  } else {                                                                \
+    for (int w_ = 0; w_ < (int)gridDim.x; ++w_) {                         \
+      const uint64_t* cw_ = call + (int64_t)w_ * chunk;                   \
+      for (uint32_t i_ = tid; i_ < sh_cnt[w_]; i_ += kThreads) {          \
+        const uint64_t comp = cw_[i_];                                    \
+        body                                                              \
+      }                                                                   \
+    }                                                                     \
   }
   uint32_t need = kk - cnt_above;
   // threshold on the composite key (score key << 32 | ~index): select comp >= thr
@@ -446,7 +500,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(
         int64_t j = (w0 + i) * 32 + bpos;
         if (off < (uint32_t)k) {
           orow[off] = (int32_t)j;
-          if (srow) srow[off] = scores[row * N + j];
+          if (srow) srow[off] = scores[row * sstride + j];
         }
         ++off;
       }
@@ -470,7 +524,7 @@ hipError_t launch_mfma_di(const IndexArgs& a, float* scores, uint32_t* hist, int
   const uint8_t* ki = reinterpret_cast<const uint8_t*>(a.ki);
 #define DSV4_IDX_LAUNCH(HIv)                                                                                  \
   DSV4_LAUNCH_MAIN((index_mfma_kernel<KIND, DI, HIv>), grid, dim3(kThreads), smem, st, qi, a.wi, ki,        \
-                     a.ki_scale, a.q_pos, a.N, a.k_bs, a.Q, a.m, chunk, scores, hist)
+                     a.ki_scale, a.q_pos, a.N, a.k_bs, a.Q, a.m, chunk, scores, ((a.N + 63) / 64) * 64, hist)
   switch (a.HI) {
     case 4: DSV4_IDX_LAUNCH(4); break;
     case 8: DSV4_IDX_LAUNCH(8); break;
@@ -496,7 +550,8 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t topk_workspace_bytes(int64_t R, int64_t N) {
   int64_t words = ((N + 127) / 128) * 4;   // rows of 16-byte multiples
-  return align256((size_t)R * N * 4) + align256((size_t)R * kHistBins * 4 + (size_t)R * kSelCounters * 4) +
+  const int64_t sstride = ((N + 63) / 64) * 64;
+  return align256((size_t)R * sstride * 4) + align256((size_t)R * kHistBins * 4 + (size_t)R * kSelCounters * 4) +
          align256((size_t)R * words * 4) + align256((size_t)R * N * 8);
 }
 
@@ -505,7 +560,7 @@ TopkWorkspace topk_workspace_carve(void* base, int64_t R, int64_t N) {
   uint8_t* p = reinterpret_cast<uint8_t*>(base);
   TopkWorkspace w;
   w.scores = reinterpret_cast<float*>(p);
-  p += align256((size_t)R * N * 4);
+  p += align256((size_t)R * (((N + 63) / 64) * 64) * 4);
   w.hist = reinterpret_cast<uint32_t*>(p);
   w.counters = w.hist + R * kHistBins;
   p += align256((size_t)R * kHistBins * 4 + (size_t)R * kSelCounters * 4);
@@ -529,13 +584,13 @@ hipError_t launch_index_topk(const IndexArgs& a, const TopkWorkspace& ws, hipStr
       size_t smem = (kHistBins + (size_t)a.HI * a.DI + a.HI) * 4;
       DSV4_LAUNCH_MAIN(index_f32_kernel, grid, dim3(kThreads), smem, st, reinterpret_cast<const float*>(a.qi),
                          a.wi, reinterpret_cast<const float*>(a.ki), a.q_pos, a.N, a.k_bs, a.Q, a.HI, a.DI, a.m,
-                         ws.scores, ws.hist);
+                         ws.scores, ((a.N + 63) / 64) * 64, ws.hist);
       e = hipGetLastError();
     } else {
-      // about 2048 workgroups over the whole call, each a multiple of 256 keys
+      // about two workgroups per CU over the whole call, each a multiple of 256 keys
       int QPT = 16 / a.HI;
       int64_t rows = a.B * ((a.Q + QPT - 1) / QPT);
-      int64_t per = (a.N * rows + 2047) / 2048;
+      int64_t per = (a.N * rows + 511) / 512;
       int64_t chunk = ((per + kKeysPerIter - 1) / kKeysPerIter) * kKeysPerIter;
       if (chunk < kKeysPerIter) chunk = kKeysPerIter;
       if (a.kind == KEY_BF16) e = launch_mfma<KEY_BF16>(a, ws.scores, ws.hist, chunk, st);
@@ -544,16 +599,17 @@ hipError_t launch_index_topk(const IndexArgs& a, const TopkWorkspace& ws, hipStr
     }
     if (e != hipSuccess) return e;
   }
-  // selection: up to 16 ranges per row (64 at most), each a multiple of 256 keys
-  int64_t schunk = (a.N + 15) / 16;
-  if (schunk < 4096) schunk = 4096;
-  if (schunk < (a.N + kMaxSelGroups - 1) / kMaxSelGroups) schunk = (a.N + kMaxSelGroups - 1) / kMaxSelGroups;
-  schunk = ((schunk + 255) / 256) * 256;
+  // selection: ranges of 16384 keys (more per range past 64 ranges per row)
+  const int64_t kGroup = (int64_t)kThreads * 64;
+  int64_t schunk = kGroup;
+  if ((a.N + schunk - 1) / schunk > kMaxSelGroups)
+    schunk = ((a.N + kMaxSelGroups * kGroup - 1) / (kMaxSelGroups * kGroup)) * kGroup;
   int64_t nsel = (a.N + schunk - 1) / schunk;
   if (nsel < 1) nsel = 1;
   int64_t words = ((a.N + 127) / 128) * 4;
   hipLaunchKernelGGL(select_kernel, dim3((unsigned)nsel, (unsigned)R), dim3(kThreads), 0, st, ws.scores, ws.hist,
-                     ws.counters, ws.bitmap, ws.cand, a.q_pos, a.N, words, a.m, a.k, schunk, a.out_idx, a.out_score);
+                     ws.counters, ws.bitmap, ws.cand, a.q_pos, a.N, ((a.N + 63) / 64) * 64, words, a.m, a.k, schunk,
+                     a.out_idx, a.out_score);
   return hipGetLastError();
 }
 
