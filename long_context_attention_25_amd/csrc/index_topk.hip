@@ -13,11 +13,10 @@
 //      epilogue applies ReLU, the head weights and the head sum, writes the fp32
 //      scores and adds the top 12 bits of each score's order-preserving key into a
 //      per-row histogram (LDS histogram, then one global atomic per non-empty bin).
-//   2. select kernel: every workgroup finds the threshold bin of its row from the
-//      histogram, writes the bitmap words of its key range for the keys strictly
-//      above the bin, and appends the keys inside the bin as candidates.  The last
-//      workgroup of a row (atomic counter) radix-selects the remaining candidates by
-//      (score, lower index first), sets their bits, and compacts the bitmap into
+//   2. select kernel, one workgroup per row: finds the threshold bin of the row from the
+//      histogram, reads the row's scores once, marks the keys above the bin in an LDS
+//      bitmap and collects the keys inside the bin as candidates, radix-selects the
+//      remaining candidates by (score, lower index first), and compacts the bitmap into
 //      ascending indices.
 // The result is exact on the fp32 scores and independent of scheduling.
 #include "common.hpp"
@@ -29,39 +28,12 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kKeysPerIter = 256;   // 4 waves x 4 tiles x 16 keys
-constexpr int kMaxSelGroups = 64;   // select workgroups per row at most
-constexpr int kSelCounters = 1 + kMaxSelGroups;
-constexpr int kCandCap = 4096;      // candidates staged in LDS by the finishing workgroup
 
 __device__ __forceinline__ uint32_t vis_blocks(const int32_t* q_pos, int64_t row, int m, int64_t N) {
   int64_t p = q_pos[row];
   int64_t n = (p + 1) / m;
   if (p < 0) n = 0;
   return (uint32_t)(n < N ? n : N);
-}
-
-// Block-wide exclusive prefix sum of one value per thread (256 threads); returns the
-// exclusive prefix and writes the total to *total.
-__device__ uint32_t block_excl_scan(uint32_t v, uint32_t* lds4, uint32_t* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t t = __shfl_up(incl, o);
-    if (lane >= o) incl += t;
-  }
-  if (lane == 63) lds4[wave] = incl;
-  __syncthreads();
-  uint32_t base = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    uint32_t x = lds4[w];
-    base += (w < wave) ? x : 0u;
-    tot += x;
-  }
-  __syncthreads();
-  *total = tot;
-  return base + incl - v;
 }
 
 __global__ void clear_kernel(uint32_t* p, int64_t n) {
@@ -281,234 +253,311 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
 }
 
 // ------------------------------------------------------------------ selection
-__global__ __launch_bounds__(kThreads) void select_kernel(
-    const float* __restrict__ scores, const uint32_t* __restrict__ hist_g, uint32_t* __restrict__ counters,
-    uint32_t* __restrict__ bitmap, uint64_t* __restrict__ cand, const int32_t* __restrict__ q_pos,
-    int64_t N, int64_t sstride, int64_t words, int m, int k, int64_t chunk, int32_t* __restrict__ out_idx,
-    float* __restrict__ out_score) {
-  __shared__ uint32_t sh_misc[16];
-  __shared__ uint32_t sh_h[256];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t row = blockIdx.y;
-  const uint32_t n = vis_blocks(q_pos, row, m, N);
-  const uint32_t kk = (uint32_t)k < n ? (uint32_t)k : n;
+// Block-wide exclusive prefix sum for NT threads (NT / 64 waves); `tmp` holds NT / 64
+// words of LDS.  Returns the exclusive prefix and writes the total to *total.
+template <int NT>
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) tmp[wave] = incl;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t x = tmp[w];
+    base += (w < wave) ? x : 0u;
+    tot += x;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + incl - v;
+}
 
-  // ---- threshold bin: largest t with #(keys with bin >= t) >= kk
-  const uint32_t* hr = hist_g + row * kHistBins;
-  uint32_t hv[kHistBins / kThreads];
+// Threshold bin of a row: the bin b* with #(bin > b*) < kk <= #(bin >= b*).  Every thread
+// of an NT-thread workgroup takes kHistBins / NT consecutive bins; the result goes to
+// misc[0] (bin) and misc[1] (#keys above it).
+template <int NT>
+__device__ __forceinline__ void threshold_bin(const uint32_t* __restrict__ hr, uint32_t kk, uint32_t* tmp,
+                                              uint32_t* misc) {
+  constexpr int BPT = kHistBins / NT;
+  uint32_t hv[BPT];
   uint32_t tsum = 0;
 #pragma unroll
-  for (int i = 0; i < kHistBins / kThreads; ++i) {
-    hv[i] = hr[tid * (kHistBins / kThreads) + i];
-    tsum += hv[i];
+  for (int i = 0; i < BPT; i += 4) {
+    const uint4 v = *reinterpret_cast<const uint4*>(hr + threadIdx.x * BPT + i);
+    hv[i] = v.x; hv[i + 1] = v.y; hv[i + 2] = v.z; hv[i + 3] = v.w;
+    tsum += v.x + v.y + v.z + v.w;
   }
-  if (tid == 0) { sh_misc[4] = kHistBins; sh_misc[5] = 0; }
   uint32_t total;
-  uint32_t excl = block_excl_scan(tsum, sh_misc, &total);
-  uint32_t above = total - excl - tsum;         // keys in higher threads' bins
-  if (kk > 0 && above < kk && kk <= above + tsum) {
+  const uint32_t excl = block_scan<NT>(tsum, tmp, &total);
+  const uint32_t above = total - excl - tsum;                // keys in higher threads' bins
+  if (above < kk && kk <= above + tsum) {
     uint32_t acc = above;
-    for (int i = kHistBins / kThreads - 1; i >= 0; --i) {
-      if (acc + hv[i] >= kk) { sh_misc[4] = tid * (kHistBins / kThreads) + i; sh_misc[5] = acc; break; }
+    for (int i = BPT - 1; i >= 0; --i) {
+      if (acc + hv[i] >= kk) {
+        misc[0] = threadIdx.x * BPT + i;
+        misc[1] = acc;
+        break;
+      }
       acc += hv[i];
     }
   }
   __syncthreads();
-  const uint32_t tbin = sh_misc[4], cnt_above = sh_misc[5];
+}
 
-  // ---- bitmap words of this range (keys strictly above the bin) + candidates (in the bin).
-  // Thread t owns 64 consecutive keys per 16384-key group: 16 float4 loads in flight, its
-  // two bitmap words built in registers, its candidates placed by a block-wide scan into
-  // this workgroup's own slice of the candidate buffer.
-  const int64_t c0 = (int64_t)blockIdx.x * chunk;
-  int64_t c1 = c0 + chunk;
-  if (c1 > (int64_t)n) c1 = n;
-  uint32_t* bm = bitmap + row * words;
-  uint64_t* cr = cand + row * N + c0;
-  uint32_t* rc = counters + row * kSelCounters;     // [0] arrivals, [1 + w] candidates of workgroup w
-  const float* srow_in = scores + row * sstride;
-  uint32_t cand_base = 0;
-  for (int64_t gbase = c0; gbase < c1; gbase += (int64_t)kThreads * 64) {
-    const int64_t kb = gbase + (int64_t)tid * 64;
-    float4 v[16];
+// Selection, pass 1 (all rows x key ranges of kScanKeys): keys above the threshold bin
+// get their bit in the row's key bitmap (whole 32-bit words, plain stores); keys inside
+// the bin are appended to this range's own slice of the candidate buffer as composite
+// keys (score key << 32 | ~index: equal scores order the lower index first).
+constexpr int kScanThreads = 256;
+constexpr int kScanKeys = 8192;                              // 8 float4 loads per thread
+constexpr int kFinThreads = 1024;
+constexpr int kLdsBitmapKeys = 1 << 18;                      // bitmap kept in LDS by pass 2
+constexpr int kCandCap = 4096;                               // candidates staged in LDS by pass 2
+
+__global__ __launch_bounds__(kScanThreads) void select_scan_kernel(
+    const float* __restrict__ scores, const uint32_t* __restrict__ hist_g, uint32_t* __restrict__ bitmap_g,
+    uint64_t* __restrict__ cand_g, uint32_t* __restrict__ ccount, const int32_t* __restrict__ q_pos, int64_t N,
+    int64_t sstride, int64_t words, int m, int k) {
+  __shared__ uint32_t tmp[kScanThreads / kWave];
+  __shared__ uint32_t misc[4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t row = blockIdx.y;
+  const uint32_t n = vis_blocks(q_pos, row, m, N);
+  const uint32_t kk = (uint32_t)k < n ? (uint32_t)k : n;
+  const int64_t c0 = (int64_t)blockIdx.x * kScanKeys;
+  const int64_t nch = gridDim.x;
+  if (kk == 0 || c0 >= (int64_t)n) {
+    if (tid == 0) ccount[row * nch + blockIdx.x] = 0u;
+    return;
+  }
+  // issue the score loads first; the threshold is computed while they are in flight
+  const float* sc = scores + row * sstride + c0;
+  const int64_t c1 = (c0 + kScanKeys < (int64_t)n ? c0 + kScanKeys : (int64_t)n) - c0;   // keys in range
+  constexpr int IT = kScanKeys / (4 * kScanThreads);
+  float4 v[IT];
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      v[i] = kb < c1 ? reinterpret_cast<const float4*>(srow_in + kb)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-    uint32_t wlo = 0, whi = 0, ncand = 0;
+  for (int u = 0; u < IT; ++u) {
+    const int64_t kb = (int64_t)(u * kScanThreads + tid) * 4;
+    v[u] = kb < c1 ? reinterpret_cast<const float4*>(sc)[u * kScanThreads + tid]
+                   : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+  }
+  if (tid == 0) misc[2] = 0u;
+  threshold_bin<kScanThreads>(hist_g + row * kHistBins, kk, tmp, misc);
+  const uint32_t tbin = misc[0];
+
+  uint32_t* bm = bitmap_g + row * words + c0 / 32;
+  uint64_t* cs = cand_g + row * N + c0;
 #pragma unroll
-    for (int e = 0; e < 64; ++e) {
-      const float sv = (e & 3) == 0 ? v[e >> 2].x : (e & 3) == 1 ? v[e >> 2].y : (e & 3) == 2 ? v[e >> 2].z : v[e >> 2].w;
-      const uint32_t bin = score_key(sv) >> (32 - kHistBits);
+  for (int u = 0; u < IT; ++u) {
+    const int64_t kb = (int64_t)(u * kScanThreads + tid) * 4;   // this lane's 4 keys
+    const float e4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+    uint32_t nib = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t sk = score_key(e4[e]);
+      const uint32_t bin = sk >> (32 - kHistBits);
       const bool in = kb + e < c1;
-      if (in && bin > tbin) {
-        if (e < 32) wlo |= 1u << e;
-        else whi |= 1u << (e - 32);
-      }
-      ncand += (in && bin == tbin) ? 1u : 0u;
-    }
-    if (kb < c1) *reinterpret_cast<uint2*>(bm + kb / 32) = make_uint2(wlo, whi);
-    uint32_t gtot;
-    uint32_t pos = cand_base + block_excl_scan(ncand, sh_misc, &gtot);
-    if (ncand) {
-#pragma unroll
-      for (int e = 0; e < 64; ++e) {
-        const float sv = (e & 3) == 0 ? v[e >> 2].x : (e & 3) == 1 ? v[e >> 2].y : (e & 3) == 2 ? v[e >> 2].z : v[e >> 2].w;
-        const uint32_t key = score_key(sv);
-        if (kb + e < c1 && (key >> (32 - kHistBits)) == tbin)
-          cr[pos++] = ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)(kb + e));
+      if (in && bin > tbin) nib |= 1u << e;
+      const bool isc = in && bin == tbin;
+      const uint64_t mask = __ballot(isc);
+      if (mask) {
+        const int leader = __ffsll((unsigned long long)mask) - 1;
+        uint32_t base = 0;
+        if (lane == leader) base = atomicAdd(&misc[2], (uint32_t)__popcll(mask));
+        base = __shfl(base, leader);
+        if (isc) {
+          const uint32_t f = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+          cs[f] = ((uint64_t)sk << 32) | (uint64_t)(~(uint32_t)(c0 + kb + e));
+        }
       }
     }
-    cand_base += gtot;
-  }
-  if (tid == 0) rc[1 + blockIdx.x] = cand_base;
-
-  // ---- the last workgroup of the row finishes the selection (every thread releases its
-  // own bitmap / candidate stores before the arrival is counted)
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t prev = atomicAdd(&rc[0], 1u);
-    sh_misc[6] = (prev == gridDim.x - 1) ? 1u : 0u;
+    // a bitmap word is the nibbles of 8 consecutive lanes
+    uint32_t wv = nib << (4 * (lane & 7));
+    wv |= __shfl_xor(wv, 1);
+    wv |= __shfl_xor(wv, 2);
+    wv |= __shfl_xor(wv, 4);
+    if ((lane & 7) == 0 && kb < c1) bm[kb / 32] = wv;
   }
   __syncthreads();
-  if (!sh_misc[6]) return;
-  __threadfence();
+  if (tid == 0) ccount[row * nch + blockIdx.x] = misc[2];
+}
 
-  __shared__ uint32_t sh_cnt[kMaxSelGroups];
-  for (int w = tid; w < (int)gridDim.x; w += kThreads)
-    sh_cnt[w] = __hip_atomic_load(&rc[1 + w], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  const uint64_t* call = cand + row * N;
-  // Stage the candidates in LDS when they fit (the usual case: about one histogram bin of
-  // keys); otherwise the passes below read them from each workgroup's slice in turn.
-  __shared__ uint64_t sh_cand[kCandCap];
-  __shared__ uint32_t sh_pre[kMaxSelGroups + 1];
-  if (tid == 0) {
-    uint32_t acc_ = 0;
-    for (int w = 0; w < (int)gridDim.x; ++w) {
-      sh_pre[w] = acc_;
-      acc_ += sh_cnt[w];
+// Selection, pass 2 (one workgroup per row): radix-selects (8-bit digits) the
+// kk - #(bin > b*) largest composites among the candidates, adds their bits to the
+// bitmap and compacts it into ascending indices, then -1 padding.
+// kLdsBits: the row's bitmap is copied into LDS (N <= kLdsBitmapKeys).
+template <bool kLdsBits>
+__global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
+    const float* __restrict__ scores, const uint32_t* __restrict__ hist_g, uint32_t* __restrict__ bitmap_g,
+    const uint64_t* __restrict__ cand_g, const uint32_t* __restrict__ ccount, const int32_t* __restrict__ q_pos,
+    int64_t N, int64_t sstride, int64_t words, int m, int k, int nch, int32_t* __restrict__ out_idx,
+    float* __restrict__ out_score) {
+  constexpr int NT = kFinThreads;
+  __shared__ uint32_t bits_l[kLdsBits ? kLdsBitmapKeys / 32 : 1];
+  __shared__ uint64_t cand_l[kCandCap];
+  __shared__ uint32_t pre[kFinThreads + 1];                  // candidate offsets of the ranges
+  __shared__ uint32_t tmp[NT / kWave];
+  __shared__ uint32_t h256[256];
+  __shared__ uint32_t misc[8];
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const uint32_t n = vis_blocks(q_pos, row, m, N);
+  const uint32_t kk = (uint32_t)k < n ? (uint32_t)k : n;
+  const int64_t wn = ((int64_t)n + 31) / 32;                 // bitmap words in use
+  int32_t* orow = out_idx + row * k;
+  float* srow = out_score ? out_score + row * k : nullptr;
+  const float* sc = scores + row * sstride;
+  uint32_t* gbits = bitmap_g + row * words;
+  if (kk == 0) {
+    for (int p = tid; p < k; p += NT) {
+      orow[p] = -1;
+      if (srow) srow[p] = -INFINITY;
     }
-    sh_pre[gridDim.x] = acc_;
+    return;
   }
+  // bitmap copy and candidate counts first (independent loads), then the threshold
+  if constexpr (kLdsBits) {
+    for (int64_t w = (int64_t)tid * 4; w < wn; w += (int64_t)NT * 4) {
+      const uint4 x = *reinterpret_cast<const uint4*>(gbits + w);   // rows are 16-byte padded
+      *reinterpret_cast<uint4*>(bits_l + w) = x;
+    }
+  }
+  const int nrange = (int)(((int64_t)n + kScanKeys - 1) / kScanKeys);
+  threshold_bin<NT>(hist_g + row * kHistBins, kk, tmp, misc);
+  const uint32_t tbin = misc[0], cnt_above = misc[1];
+  // candidate offsets per range (ranges beyond n hold none); more than NT ranges are
+  // summed in rounds
+  uint32_t run = 0;
+  for (int r0 = 0; r0 < nrange; r0 += NT) {
+    const uint32_t cnt = r0 + tid < nrange ? ccount[row * nch + r0 + tid] : 0u;
+    uint32_t tot;
+    const uint32_t ex = block_scan<NT>(cnt, tmp, &tot);
+    if (r0 + tid < nrange && r0 + tid < NT) pre[r0 + tid] = run + ex;
+    run += tot;
+  }
+  if (tid == 0) pre[nrange < NT ? nrange : NT] = run;
   __syncthreads();
-  const uint32_t c = sh_pre[gridDim.x];
-  const bool in_lds = c <= (uint32_t)kCandCap;
-  if (in_lds) {
-    // kCandCap / kThreads = 16 slots per thread: all loads issued before any is stored
-    constexpr int kPer = kCandCap / kThreads;
+  const uint32_t c = run;
+  // candidate f -> its range (binary search over the offsets; at most NT ranges are
+  // indexed this way, beyond that the tail ranges are searched linearly from there)
+  auto cand_at = [&](uint32_t f) -> uint64_t {
+    int lo = 0, hi = (nrange < NT ? nrange : NT) - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] <= f) lo = mid;
+      else hi = mid - 1;
+    }
+    uint32_t base = pre[lo];
+    int64_t r = lo;
+    if (r == NT - 1 && nrange > NT) {                         // rare: very long rows
+      uint32_t cnt = ccount[row * nch + r];
+      while (f >= base + cnt) {
+        base += cnt;
+        ++r;
+        cnt = ccount[row * nch + r];
+      }
+    }
+    return cand_g[row * N + r * kScanKeys + (f - base)];
+  };
+  {
+    constexpr int kPer = kCandCap / NT;
     uint64_t vals[kPer];
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
-      const uint32_t f = tid + u * kThreads;
-      int w = 0;
-      while (w + 1 < (int)gridDim.x && sh_pre[w + 1] <= f) ++w;
-      vals[u] = f < c ? call[(int64_t)w * chunk + (f - sh_pre[w])] : 0ull;
+      const uint32_t f = tid + u * NT;
+      vals[u] = f < c ? cand_at(f) : 0ull;
     }
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
-      const uint32_t f = tid + u * kThreads;
-      if (f < c) sh_cand[f] = vals[u];
+      const uint32_t f = tid + u * NT;
+      if (f < c) cand_l[f] = vals[u];
     }
-    __syncthreads();
   }
-#define DSV4_FOR_CAND(body)                                               \
-  if (in_lds) {                                                           \
-    for (uint32_t f_ = tid; f_ < c; f_ += kThreads) {                     \
-      const uint64_t comp = sh_cand[f_];                                  \
-      body                                                                \
-    }                                                                     \
-  } else {                                                                \
-    for (int w_ = 0; w_ < (int)gridDim.x; ++w_) {                         \
-      const uint64_t* cw_ = call + (int64_t)w_ * chunk;                   \
-      for (uint32_t i_ = tid; i_ < sh_cnt[w_]; i_ += kThreads) {          \
-        const uint64_t comp = cw_[i_];                                    \
-        body                                                              \
-      }                                                                   \
-    }                                                                     \
+  __syncthreads();
+#define DSV4_FOR_CAND(body)                                              \
+  for (uint32_t f_ = tid; f_ < c; f_ += NT) {                            \
+    const uint64_t comp = f_ < (uint32_t)kCandCap ? cand_l[f_] : cand_at(f_); \
+    body                                                                 \
   }
   uint32_t need = kk - cnt_above;
-  // threshold on the composite key (score key << 32 | ~index): select comp >= thr
-  uint64_t prefix = (uint64_t)tbin << (64 - kHistBits);
-  uint64_t thr;
-  bool none = (need == 0);
-  if (need == c) {
-    thr = 0;
-  } else {
-    int hi = 64 - kHistBits;                    // bits [hi-1 : 0] still open
+  uint64_t thr = 0;                                          // select composites >= thr
+  if (need < c) {
+    uint64_t prefix = (uint64_t)tbin << (64 - kHistBits);
+    int hi = 64 - kHistBits;                                 // bits [hi-1 : 0] still open
     while (true) {
-      int wd = hi < 8 ? hi : 8;
-      int sh = hi - wd;
-      sh_h[tid] = 0u;
+      const int wd = hi < 8 ? hi : 8;
+      const int sh = hi - wd;
+      if (tid < 256) h256[tid] = 0u;
       __syncthreads();
-      DSV4_FOR_CAND(if ((comp >> hi) == (prefix >> hi)) atomicAdd(&sh_h[(comp >> sh) & ((1u << wd) - 1u)], 1u);)
+      DSV4_FOR_CAND(if ((comp >> hi) == (prefix >> hi)) atomicAdd(&h256[(comp >> sh) & ((1u << wd) - 1u)], 1u);)
       __syncthreads();
-      uint32_t hcount = (tid < (1 << wd)) ? sh_h[tid] : 0u;
+      const uint32_t hc = (tid < (1 << wd)) ? h256[tid] : 0u;
       uint32_t tot;
-      uint32_t ex = block_excl_scan(hcount, sh_misc, &tot);
-      uint32_t gt = tot - ex - hcount;          // candidates with a larger digit
-      if (tid < (1 << wd) && gt < need && need <= gt + hcount) {
-        sh_misc[8] = tid;
-        sh_misc[9] = gt;
-        sh_misc[10] = hcount;
+      const uint32_t ex = block_scan<NT>(hc, tmp, &tot);
+      const uint32_t gt = tot - ex - hc;                     // candidates with a larger digit
+      if (tid < (1 << wd) && gt < need && need <= gt + hc) {
+        misc[4] = tid;
+        misc[5] = gt;
+        misc[6] = hc;
       }
       __syncthreads();
-      uint32_t d = sh_misc[8];
-      need -= sh_misc[9];
-      prefix |= (uint64_t)d << sh;
-      bool done = (sh_misc[10] == need) || sh == 0;
-      __syncthreads();
+      need -= misc[5];
+      prefix |= (uint64_t)misc[4] << sh;
+      const bool done = misc[6] == need || sh == 0;
       hi = sh;
       if (done) break;
     }
     thr = prefix;
   }
-  if (!none) {
-    DSV4_FOR_CAND(if (comp >= thr) {
-      const uint32_t j = ~(uint32_t)comp;
-      atomicOr(&bm[j / 32], 1u << (j % 32));
-    })
-  }
-  __threadfence();
+  uint32_t* bits = kLdsBits ? bits_l : gbits;
+  DSV4_FOR_CAND(if (comp >= thr) {
+    const uint32_t j = ~(uint32_t)comp;
+    atomicOr(&bits[j >> 5], 1u << (j & 31));
+  })
+#undef DSV4_FOR_CAND
+  __threadfence_block();
   __syncthreads();
 
-  // ---- compact the bitmap into ascending indices: rounds of 32 words (1024 keys) per
-  // thread, loaded as 8 x 16 bytes (the fence above made the other workgroups' words and
-  // the atomics visible to plain loads)
-  const int64_t wn = ((int64_t)n + 31) / 32;
-  int32_t* orow = out_idx + row * k;
-  float* srow = out_score ? out_score + row * k : nullptr;
+  // compaction: thread t takes 8 consecutive words (256 keys) per round
   uint32_t base_off = 0;
-  for (int64_t r0 = 0; r0 < wn; r0 += 32 * kThreads) {
-    const int64_t w0 = r0 + (int64_t)tid * 32;
-    uint32_t wv[32];
+  for (int64_t r0 = 0; r0 < wn; r0 += 8 * NT) {
+    const int64_t w0 = r0 + (int64_t)tid * 8;
+    uint32_t wv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      uint4 v = (w0 + 4 * i < wn) ? *reinterpret_cast<const uint4*>(bm + w0 + 4 * i) : make_uint4(0, 0, 0, 0);
-      wv[4 * i] = v.x; wv[4 * i + 1] = v.y; wv[4 * i + 2] = v.z; wv[4 * i + 3] = v.w;
+      if constexpr (kLdsBits) wv[i] = w0 + i < wn ? bits[w0 + i] : 0u;
+      else wv[i] = w0 + i < wn ? __hip_atomic_load(&bits[w0 + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
     }
     uint32_t cnt = 0;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) cnt += __popc(w0 + i < wn ? wv[i] : 0u);
+    for (int i = 0; i < 8; ++i) cnt += __popc(wv[i]);
     uint32_t rtot;
-    uint32_t off = base_off + block_excl_scan(cnt, sh_misc, &rtot);
-    for (int i = 0; i < 32; ++i) {
-      uint32_t bits = w0 + i < wn ? wv[i] : 0u;
-      while (bits) {
-        int bpos = __ffs(bits) - 1;
-        bits &= bits - 1;
-        int64_t j = (w0 + i) * 32 + bpos;
+    uint32_t off = base_off + block_scan<NT>(cnt, tmp, &rtot);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t b_ = wv[i];
+      while (b_) {
+        const int bpos = __ffs(b_) - 1;
+        b_ &= b_ - 1;
+        const int64_t j = (w0 + i) * 32 + bpos;
         if (off < (uint32_t)k) {
           orow[off] = (int32_t)j;
-          if (srow) srow[off] = scores[row * sstride + j];
+          if (srow) srow[off] = sc[j];
         }
         ++off;
       }
     }
     base_off += rtot;
   }
-  const uint32_t tot = base_off;
-  for (int64_t p = (int64_t)tot + tid; p < k; p += kThreads) {
+  for (int64_t p = (int64_t)base_off + tid; p < k; p += NT) {
     orow[p] = -1;
     if (srow) srow[p] = -INFINITY;
   }
@@ -551,8 +600,9 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t topk_workspace_bytes(int64_t R, int64_t N) {
   int64_t words = ((N + 127) / 128) * 4;   // rows of 16-byte multiples
   const int64_t sstride = ((N + 63) / 64) * 64;
-  return align256((size_t)R * sstride * 4) + align256((size_t)R * kHistBins * 4 + (size_t)R * kSelCounters * 4) +
-         align256((size_t)R * words * 4) + align256((size_t)R * N * 8);
+  const int64_t nch = (N + kScanKeys - 1) / kScanKeys;
+  return align256((size_t)R * sstride * 4) + align256((size_t)R * kHistBins * 4) + align256((size_t)R * words * 4) +
+         align256((size_t)R * N * 8) + align256((size_t)R * nch * 4);
 }
 
 TopkWorkspace topk_workspace_carve(void* base, int64_t R, int64_t N) {
@@ -562,18 +612,19 @@ TopkWorkspace topk_workspace_carve(void* base, int64_t R, int64_t N) {
   w.scores = reinterpret_cast<float*>(p);
   p += align256((size_t)R * (((N + 63) / 64) * 64) * 4);
   w.hist = reinterpret_cast<uint32_t*>(p);
-  w.counters = w.hist + R * kHistBins;
-  p += align256((size_t)R * kHistBins * 4 + (size_t)R * kSelCounters * 4);
+  p += align256((size_t)R * kHistBins * 4);
   w.bitmap = reinterpret_cast<uint32_t*>(p);
   p += align256((size_t)R * words * 4);
   w.cand = reinterpret_cast<uint64_t*>(p);
+  p += align256((size_t)R * N * 8);
+  w.ccount = reinterpret_cast<uint32_t*>(p);
   return w;
 }
 
 hipError_t launch_index_topk(const IndexArgs& a, const TopkWorkspace& ws, hipStream_t st) {
   const int64_t R = a.B * a.Q;
   if (R == 0) return hipSuccess;
-  const int64_t nclear = R * kHistBins + R * kSelCounters;
+  const int64_t nclear = R * kHistBins;
   hipLaunchKernelGGL(clear_kernel, dim3((unsigned)((nclear + 1023) / 1024 < 256 ? (nclear + 1023) / 1024 : 256)),
                      dim3(1024), 0, st, ws.hist, nclear);
   hipError_t e = hipGetLastError();
@@ -599,17 +650,28 @@ hipError_t launch_index_topk(const IndexArgs& a, const TopkWorkspace& ws, hipStr
     }
     if (e != hipSuccess) return e;
   }
-  // selection: ranges of 16384 keys (more per range past 64 ranges per row)
-  const int64_t kGroup = (int64_t)kThreads * 64;
-  int64_t schunk = kGroup;
-  if ((a.N + schunk - 1) / schunk > kMaxSelGroups)
-    schunk = ((a.N + kMaxSelGroups * kGroup - 1) / (kMaxSelGroups * kGroup)) * kGroup;
-  int64_t nsel = (a.N + schunk - 1) / schunk;
-  if (nsel < 1) nsel = 1;
-  int64_t words = ((a.N + 127) / 128) * 4;
-  hipLaunchKernelGGL(select_kernel, dim3((unsigned)nsel, (unsigned)R), dim3(kThreads), 0, st, ws.scores, ws.hist,
-                     ws.counters, ws.bitmap, ws.cand, a.q_pos, a.N, ((a.N + 63) / 64) * 64, words, a.m, a.k, schunk,
-                     a.out_idx, a.out_score);
+  // selection: pass 1 over all rows x key ranges, pass 2 one workgroup per row
+  if (a.N == 0) {
+    hipLaunchKernelGGL(select_finish_kernel<true>, dim3((unsigned)R), dim3(kFinThreads), 0, st, ws.scores, ws.hist,
+                       ws.bitmap, ws.cand, ws.ccount, a.q_pos, a.N, (int64_t)0, (int64_t)0, a.m, a.k, 0, a.out_idx,
+                       a.out_score);
+    return hipGetLastError();
+  }
+  const int64_t words = ((a.N + 127) / 128) * 4;
+  const int64_t sstride = ((a.N + 63) / 64) * 64;
+  const int64_t nch = (a.N + kScanKeys - 1) / kScanKeys;
+  hipLaunchKernelGGL(select_scan_kernel, dim3((unsigned)nch, (unsigned)R), dim3(kScanThreads), 0, st, ws.scores,
+                     ws.hist, ws.bitmap, ws.cand, ws.ccount, a.q_pos, a.N, sstride, words, a.m, a.k);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.N <= kLdsBitmapKeys)
+    hipLaunchKernelGGL(select_finish_kernel<true>, dim3((unsigned)R), dim3(kFinThreads), 0, st, ws.scores, ws.hist,
+                       ws.bitmap, ws.cand, ws.ccount, a.q_pos, a.N, sstride, words, a.m, a.k, (int)nch, a.out_idx,
+                       a.out_score);
+  else
+    hipLaunchKernelGGL(select_finish_kernel<false>, dim3((unsigned)R), dim3(kFinThreads), 0, st, ws.scores, ws.hist,
+                       ws.bitmap, ws.cand, ws.ccount, a.q_pos, a.N, sstride, words, a.m, a.k, (int)nch, a.out_idx,
+                       a.out_score);
   return hipGetLastError();
 }
 

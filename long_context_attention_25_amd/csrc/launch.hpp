@@ -59,9 +59,9 @@ struct IndexArgs {
 struct TopkWorkspace {
   float* scores;        // [R][N]
   uint32_t* hist;       // [R][kHistBins]
-  uint32_t* counters;   // [R][2]: candidate count, finished workgroups
   uint32_t* bitmap;     // [R][words]
-  uint64_t* cand;       // [R][N]
+  uint64_t* cand;       // [R][N]: candidate slices of the key ranges
+  uint32_t* ccount;     // [R][ranges]: candidates per key range
 };
 size_t topk_workspace_bytes(int64_t R, int64_t N);
 TopkWorkspace topk_workspace_carve(void* base, int64_t R, int64_t N);

@@ -244,6 +244,24 @@ def test_index_topk_ties_and_zero_scores():
     check_topk(idx[0, 1], s_ref[0, 1], N, k)
 
 
+@pytest.mark.parametrize("N", [10000, 300000])
+def test_index_topk_many_candidates(N):
+    """All-zero scores put every key into the threshold bin: more candidates than the
+    on-chip candidate buffer holds (and, at N > 2^18, a bitmap kept in the workspace)."""
+    B, Q, HI, DI, m, k = 1, 2, 4, 64, 4, 1024
+    qi = -np.abs(synth.normal(231, synth.QI, (B, Q, HI, DI)))
+    ki = np.abs(synth.normal(231, synth.KI, (B, N, DI)))
+    w = synth.uniform(231, synth.WI, (B, Q, HI))
+    qi[0, 1] = synth.normal(232, synth.QI, (HI, DI))      # query 1: ordinary scores
+    pos = np.array([[4 * N - 1, 4 * N - 5]], dtype=np.int32)
+    qd, qbits = dev_bf16(qi)
+    kd, kbits = dev_bf16(ki)
+    idx = L.csa_index_topk(qd, dev(w), kd, dev(pos), m, k).cpu().numpy()
+    assert list(idx[0, 0]) == list(range(k))
+    s_ref = _scores_oracle(codecs.decode_bf16(qbits), w, codecs.decode_bf16(kbits), pos, m)
+    check_topk(idx[0, 1], s_ref[0, 1], int(method.visible_blocks(pos, m, N)[0, 1]), k)
+
+
 def test_index_topk_f32_is_deterministic():
     cfg = 240
     B, Q, HI, DI, N, m, k = 1, 1, 4, 64, 1024, 4, 64
