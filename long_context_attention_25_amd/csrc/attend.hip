@@ -96,12 +96,6 @@ __device__ __forceinline__ const uint16_t* lane_ptr(const uint16_t* p, int src) 
   return reinterpret_cast<const uint16_t*>(((uint64_t)hi << 32) | lo);
 }
 
-// LDS tiles are dense (row = one K or V row) with the 16-byte chunks of row r stored at
-// position chunk ^ swz(r): swz swaps the two 2-bit halves of r % 16, which keeps both the
-// K operand reads (16 rows, one chunk each) and the transposed V reads (4 rows x 2 chunks
-// per 16 lanes) on distinct banks.
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-
 // Async copy of 16 bytes per lane from global memory into LDS at dst + lane * 16.
 __device__ __forceinline__ void copy16_to_lds(const void* src, void* dst) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
@@ -128,35 +122,36 @@ __device__ __forceinline__ void tile_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// One workgroup: 4 x DS waves = 4 head groups of 16 heads x DS slices of the head dim for
-// O (each slice computes the scores of its head group over the full head dim).  The key
-// list of the split is walked in 32-key tiles; tile t+1's K and V rows are copied straight
-// into the other half of a two-stage LDS ring while tile t is used.
-template <int D, int DS>
-__global__ __launch_bounds__(256 * DS) void attend_bf16_kernel(AttendArgs a, int64_t chunk, int splits,
+// One workgroup = 4 waves, one per SIMD; wave w owns heads 16w .. 16w+15 over the full
+// head dim (scores and output).  The key list of the split is walked in 32-key tiles;
+// tile t+1's K and V rows are copied straight into the other half of a two-stage LDS
+// ring while tile t is used.  Rows are padded in LDS (K: +16 bytes, V: +32 bytes) so that
+// the K operand reads (16 rows, same column) and the transposed V reads (4 rows x 2
+// chunks per 16 lanes) hit distinct banks while every read of a lane uses one base
+// address plus immediate offsets.
+template <int D>
+__global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendArgs a, int64_t chunk, int splits,
                                                                float* __restrict__ o_part,
                                                                float* __restrict__ lse_part) {
   constexpr int KT = 32;                   // keys per tile
-  constexpr int NT = 256 * DS;
-  constexpr int NWV = NT / kWave;
+  constexpr int NWV = kThreads / kWave;    // 4
   constexpr int KS = D / 32;               // MFMA k-steps over the head dim
-  constexpr int DH = D / DS;               // dims of O per wave
+  constexpr int NDT = D / 16;              // 16-dim output tiles
   constexpr int RB = D * 2;                // bytes per row
+  constexpr int KSTR = RB + 16;            // LDS row strides
+  constexpr int VSTR = RB + 32;
   constexpr int LPR = RB / 16;             // lanes (16-byte chunks) per row
-  constexpr int RPI = kWave / LPR;         // rows per copy instruction
-  constexpr int IPT = KT / RPI;            // copy instructions per tile and matrix
-  constexpr int IPW = IPT / NWV;           // ... per wave
-  constexpr int NL = 2 * IPW;              // vector-memory ops per wave and tile (K + V)
-  constexpr int TB = KT * RB;              // bytes of one tile
-  static_assert(IPT % NWV == 0 && IPW >= 1, "copy instructions must split evenly over the waves");
+  constexpr int RPW = KT / NWV;            // rows copied per wave and matrix
+  constexpr int NL = 2 * RPW;              // copy instructions per wave and tile
+  constexpr int KTB = KT * KSTR, VTB = KT * VSTR;
+  static_assert(LPR <= kWave && kWave % LPR == 0, "a row is copied by one instruction");
+  static_assert(NL < 64, "vmcnt range");
 
-  // two stages of K and V tiles, as separate arrays so that reads of one stage are known
-  // not to alias the copies into the other
-  __shared__ __attribute__((aligned(1024))) uint8_t k0[TB];
-  __shared__ __attribute__((aligned(1024))) uint8_t v0[TB];
-  __shared__ __attribute__((aligned(1024))) uint8_t k1[TB];
-  __shared__ __attribute__((aligned(1024))) uint8_t v1[TB];
-  __shared__ int32_t list[kMaxCsaChunk];                              // the split's index entries
+  __shared__ __attribute__((aligned(1024))) uint8_t k0[KTB];
+  __shared__ __attribute__((aligned(1024))) uint8_t v0[VTB];
+  __shared__ __attribute__((aligned(1024))) uint8_t k1[KTB];
+  __shared__ __attribute__((aligned(1024))) uint8_t v1[VTB];
+  __shared__ int32_t list[kMaxCsaChunk];  // the split's index entries
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
@@ -174,21 +169,13 @@ __global__ __launch_bounds__(256 * DS) void attend_bf16_kernel(AttendArgs a, int
   const uint16_t* kw = reinterpret_cast<const uint16_t*>(a.kw) + b * a.L * D;
   const uint16_t* vw = reinterpret_cast<const uint16_t*>(a.vw) + b * a.L * D;
 
-  const int hg = wave % 4, dh = wave / 4;  // head group (16 heads) and slice of D for O
-  const int head = hg * 16 + col;
-  const bool wave_on = hg * 16 < a.H;
+  const int head = wave * 16 + col;
+  const bool wave_on = wave * 16 < a.H;
 
   // CSA: the split's index entries, once, in LDS (the tile loop issues no other loads)
   if (a.csa) {
     int64_t e1 = s1 < kr.n_c ? s1 : kr.n_c;
-    for (int64_t p = s0 + tid; p < e1; p += NT) list[p - s0] = a.idx[bq * a.k + p];
-  }
-  // Q^T operand of this lane: head `head`, dims g*D/4 + 8c .. +7 for k-step c
-  uint4 qop[KS];
-  {
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + (bq * a.H + (wave_on ? head : 0)) * D + g * (D / 4);
-#pragma unroll
-    for (int c = 0; c < KS; ++c) qop[c] = wave_on ? gload_u4(qp + 8 * c) : make_uint4(0, 0, 0, 0);
+    for (int64_t p = s0 + tid; p < e1; p += kThreads) list[p - s0] = a.idx[bq * a.k + p];
   }
   __syncthreads();
 
@@ -220,88 +207,122 @@ __global__ __launch_bounds__(256 * DS) void attend_bf16_kernel(AttendArgs a, int
     my_vp = vp;
     vmask = (uint32_t)__ballot(ok);
   };
+  // Wave w copies rows w, w+4, ... of the tile; a row is LPR lanes x 16 bytes.  When a
+  // row is shorter than a wave, the other lanes are masked off and the LDS base is moved
+  // back so that the active lanes land on the row.
   auto issue = [&](uint8_t* kdst, uint8_t* vdst) {
+    const int j = lane / LPR;              // 0 unless LPR < 64
 #pragma unroll
-    for (int j = 0; j < IPW; ++j) {
-      const int ins = wave + j * NWV;
-      const int r = ins * RPI + lane / LPR;            // row of the tile this lane copies
-      const int p = lane % LPR;                        // its chunk position in LDS
-      const int off = ((p ^ swz(r & 15)) * 8);         // source chunk (elements)
-      copy16_to_lds(lane_ptr<(RPI == 1)>(my_kp, r) + off, kdst + ins * 1024);
-      copy16_to_lds(lane_ptr<(RPI == 1)>(my_vp, r) + off, vdst + ins * 1024);
+    for (int i = 0; i < RPW; ++i) {
+      const int r = wave + i * NWV;
+      const int off = (lane % LPR) * 8;
+      if (j == 0) {
+        copy16_to_lds(lane_ptr<true>(my_kp, r) + off, kdst + r * KSTR);
+        copy16_to_lds(lane_ptr<true>(my_vp, r) + off, vdst + r * VSTR);
+      }
     }
   };
 
-  f32x4 acc[DH / 16];                      // O^T dims dh*DH + 16dt + 4g + i, head `head`
+  f32x4 acc[NDT];                          // O^T dims 16dt + 4g + i, head `head`
 #pragma unroll
-  for (int i = 0; i < DH / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < NDT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.scale * kLog2e;
+  // per-lane LDS byte offsets: K operand row `col`, chunk g*KS; V^T rows 4g + col/4 at
+  // dims 4(col%4)
+  const int k_off = col * KSTR + g * (D / 4) * 2;
+  const int v_off = (4 * g + (col >> 2)) * VSTR + (col & 3) * 8;
 
+  uint4 qop[KS];                           // Q^T operands, loaded below
   auto compute = [&](const uint8_t* kt_l, const uint8_t* vt_l, uint32_t cur_mask) {
-    if (wave_on) {
-      // ---- S^T = K . Q^T for keys 0..15 and 16..31 of the tile
-      f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    if (!wave_on) return;
+    // ---- S^T = K . Q^T for keys 0..15 and 16..31 of the tile.  K operands are read in
+    // batches of 2 x CB (two batches stay within the 15 outstanding LDS reads the counter
+    // tracks); batch i+1 is issued before the MFMAs of batch i (the scheduling
+    // barriers keep the compiler from interleaving each read with its MFMA).
+    f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    constexpr int CB = KS < 2 ? KS : 2;
+    constexpr int NB = KS / CB;
+    uint4 kv[2][2][CB];
+    auto kread = [&](int buf, int c0) {
 #pragma unroll
-      for (int c = 0; c < KS; ++c) {
-        const bf16x8 qv = bit_cast_to<bf16x8>(qop[c]);
+      for (int c = 0; c < CB; ++c)
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          const int r = kt * 16 + col;
-          const int chunk_l = g * (D / 32) + c;
-          const uint4 kv = *reinterpret_cast<const uint4*>(kt_l + r * RB + ((chunk_l ^ swz(r & 15)) * 16));
-          s[kt] = mfma_bf16(bit_cast_to<bf16x8>(kv), qv, s[kt]);
-        }
-      }
-      // ---- softmax (lane holds keys 16kt + 4g + i of head `head`), lazy rescaling
-      float mx = -INFINITY;
+        for (int kt = 0; kt < 2; ++kt)
+          kv[buf][kt][c] = *reinterpret_cast<const uint4*>(kt_l + k_off + kt * 16 * KSTR + (c0 + c) * 16);
+    };
+    kread(0, 0);
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+    for (int bi = 0; bi < NB; ++bi) {
+      if (bi + 1 < NB) kread((bi + 1) & 1, (bi + 1) * CB);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool ok = (cur_mask >> (kt * 16 + 4 * g + i)) & 1u;
-          s[kt][i] = ok ? s[kt][i] * sl2 : -INFINITY;
-          mx = fmaxf(mx, s[kt][i]);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      if (m_new > m_run + kLazyRescale) {
-        if (m_run != -INFINITY) {
-          const float alpha = exp2f(m_run - m_new);
-          l_run *= alpha;
+      for (int c = 0; c < CB; ++c)
 #pragma unroll
-          for (int i = 0; i < DH / 16; ++i) acc[i] *= alpha;
-        }
-        m_run = m_new;
-      }
-      const float m_use = m_run == -INFINITY ? 0.f : m_run;
-      float pv[8];
+        for (int kt = 0; kt < 2; ++kt)
+          s[kt] = mfma_bf16(bit_cast_to<bf16x8>(kv[bi & 1][kt][c]), bit_cast_to<bf16x8>(qop[bi * CB + c]), s[kt]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // ---- softmax (lane holds keys 16kt + 4g + i of head `head`), lazy rescaling
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        pv[i] = exp2f(s[0][i] - m_use);
-        pv[4 + i] = exp2f(s[1][i] - m_use);
+        const bool ok = (cur_mask >> (kt * 16 + 4 * g + i)) & 1u;
+        s[kt][i] = ok ? s[kt][i] * sl2 : -INFINITY;
+        mx = fmaxf(mx, s[kt][i]);
       }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    if (m_new > m_run + kLazyRescale) {
+      if (m_run != -INFINITY) {
+        const float alpha = exp2f(m_run - m_new);
+        l_run *= alpha;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) l_run += pv[i];
-      // P^T operand: slots 0-3 are keys 4g+i, slots 4-7 keys 16+4g+i
-      const bf16x8 pb = bit_cast_to<bf16x8>(make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
-                                                       pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])));
-      // ---- O^T += V^T . P^T; V^T operands by transposed LDS reads of the row-major tile:
-      // lane p of a 16-lane block addresses key row 4g + p/4 (then 16 + 4g + p/4) at dims
-      // base + 4(p%4) and receives its own dim (base + p) from the four key rows.
-      const int kr0 = 4 * g + (col >> 2);
-#pragma unroll
-      for (int dt = 0; dt < DH / 16; ++dt) {
-        const int dim = dh * DH + dt * 16 + 4 * (col & 3);
-        const int chunk_l = dim >> 3, half = (dim >> 2) & 1;
-        const uint8_t* p0 = vt_l + kr0 * RB + ((chunk_l ^ swz(kr0 & 15)) * 16) + half * 8;
-        const uint8_t* p1 = vt_l + (kr0 + 16) * RB + ((chunk_l ^ swz((kr0 + 16) & 15)) * 16) + half * 8;
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p0);
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p1);
-        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-        acc[dt] = mfma_bf16(bit_cast_to<bf16x8>(make_uint4(l2.x, l2.y, h2.x, h2.y)), pb, acc[dt]);
+        for (int i = 0; i < NDT; ++i) acc[i] *= alpha;
       }
+      m_run = m_new;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    float pv[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pv[i] = exp2f(s[0][i] - m_use);
+      pv[4 + i] = exp2f(s[1][i] - m_use);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) l_run += pv[i];
+    // P^T operand: slots 0-3 are keys 4g+i, slots 4-7 keys 16+4g+i
+    const bf16x8 pb = bit_cast_to<bf16x8>(make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                                                     pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])));
+    // ---- O^T += V^T . P^T; V^T operands by transposed LDS reads of the row-major tile:
+    // lane p of a 16-lane block addresses key row 4g + p/4 (then 16 + 4g + p/4) at dims
+    // 16dt + 4(p%4) and receives its own dim (16dt + p) from the four key rows.
+    constexpr int DB = NDT < 2 ? NDT : 2;
+    constexpr int ND = NDT / DB;
+    v4i16 vlo[2][DB], vhi[2][DB];
+    auto vread = [&](int buf, int d0) {
+#pragma unroll
+      for (int d = 0; d < DB; ++d) {
+        vlo[buf][d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16*)(vt_l + v_off + (d0 + d) * 32));
+        vhi[buf][d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16*)(vt_l + v_off + 16 * VSTR + (d0 + d) * 32));
+      }
+    };
+    vread(0, 0);
+#pragma unroll
+    for (int bi = 0; bi < ND; ++bi) {
+      if (bi + 1 < ND) vread((bi + 1) & 1, (bi + 1) * DB);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int d = 0; d < DB; ++d) {
+        const uint2 l2 = __builtin_bit_cast(uint2, vlo[bi & 1][d]), h2 = __builtin_bit_cast(uint2, vhi[bi & 1][d]);
+        acc[bi * DB + d] = mfma_bf16(bit_cast_to<bf16x8>(make_uint4(l2.x, l2.y, h2.x, h2.y)), pb, acc[bi * DB + d]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -314,6 +335,15 @@ __global__ __launch_bounds__(256 * DS) void attend_bf16_kernel(AttendArgs a, int
     mask0 = vmask;
     issue(k0, v0);
   }
+  // Q^T operand of this lane: head `head`, dims g*D/4 + 8c .. +7 for k-step c.  Loaded
+  // while tile 0 is in flight; both are waited for here, before the loop (registers
+  // still loading at loop entry would make the compiler drain every load there anyway).
+  {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + (bq * a.H + (wave_on ? head : 0)) * D + g * (D / 4);
+#pragma unroll
+    for (int c = 0; c < KS; ++c) qop[c] = gload_u4(qp + 8 * c);
+  }
+  wait_vmcnt<0>();
   for (int t = 0; t < ntile; t += 2) {
     if (t + 1 < ntile) {
       tile_ptrs(t + 1);
@@ -348,22 +378,22 @@ __global__ __launch_bounds__(256 * DS) void attend_bf16_kernel(AttendArgs a, int
   const int64_t R = a.B * a.Q * a.H;
   const int64_t orow = bq * a.H + head;
   if (splits == 1) {
-    uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + orow * D + dh * DH;
+    uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + orow * D;
 #pragma unroll
-    for (int dt = 0; dt < DH / 16; ++dt) {
+    for (int dt = 0; dt < NDT; ++dt) {
       uint2 w;
       w.x = pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv);
       w.y = pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv);
       *reinterpret_cast<uint2*>(out + dt * 16 + 4 * g) = w;
     }
-    if (g == 0 && dh == 0 && a.lse) a.lse[orow] = lse;
+    if (g == 0 && a.lse) a.lse[orow] = lse;
   } else {
-    float* op = o_part + ((int64_t)split * R + orow) * D + dh * DH;
+    float* op = o_part + ((int64_t)split * R + orow) * D;
 #pragma unroll
-    for (int dt = 0; dt < DH / 16; ++dt)
+    for (int dt = 0; dt < NDT; ++dt)
       *reinterpret_cast<float4*>(op + dt * 16 + 4 * g) =
           make_float4(acc[dt][0] * inv, acc[dt][1] * inv, acc[dt][2] * inv, acc[dt][3] * inv);
-    if (g == 0 && dh == 0) lse_part[(int64_t)split * R + orow] = lse;
+    if (g == 0) lse_part[(int64_t)split * R + orow] = lse;
   }
 }
 
@@ -568,9 +598,9 @@ hipError_t launch_attend(const AttendArgs& a, const AttendPlan& p, void* ws, hip
   }
   dim3 grid((unsigned)p.splits, (unsigned)rows);
   switch (a.D) {
-    case 128: DSV4_LAUNCH_MAIN((attend_bf16_kernel<128, 1>), grid, dim3(kThreads), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part); break;
-    case 256: DSV4_LAUNCH_MAIN((attend_bf16_kernel<256, 1>), grid, dim3(kThreads), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part); break;
-    default: DSV4_LAUNCH_MAIN((attend_bf16_kernel<512, 2>), grid, dim3(kThreads * 2), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part); break;
+    case 128: DSV4_LAUNCH_MAIN((attend_bf16_kernel<128>), grid, dim3(kThreads), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part); break;
+    case 256: DSV4_LAUNCH_MAIN((attend_bf16_kernel<256>), grid, dim3(kThreads), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part); break;
+    default: DSV4_LAUNCH_MAIN((attend_bf16_kernel<512>), grid, dim3(kThreads), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
