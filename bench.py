@@ -52,7 +52,21 @@ def algorithmic_bytes():
     return sum(parts.values()), parts
 
 
-INDEX_KERNEL_BYTES = B * N_CSA * (DI // 2 + DI // 32) + B * HI * DI * 2 + B * HI * 4
+# Algorithmic bytes per launch of the three big kernels (what each must read once; the
+# split-K partials, scores and histograms are excluded).
+KERNEL_BYTES = {
+    # MXFP4 key codes + E8M0 scales of every visible block, indexer queries, head weights
+    "index_mfma_kernel": B * N_CSA * (DI // 2 + DI // 32) + B * HI * DI * 2 + B * HI * 4,
+    # the selected K/V rows + window rows, q, the index list
+    "attend_bf16_kernel (CSA)": B * (TOPK + W) * 2 * D * 2 + B * H * D * 2 + B * TOPK * 4,
+    # every visible K/V entry + window rows, q
+    "attend_bf16_kernel (HCA)": B * (N_HCA + W) * 2 * D * 2 + B * H * D * 2,
+}
+
+# HBM traffic per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs, each scaled by
+# the counter's reading for a 256 MiB device copy (see profiles/).  An entry is used only
+# while the kernel source it was measured on is unchanged (sha256 of the file).
+MEASURED_TRAFFIC = {}
 
 
 class Workload:
@@ -131,7 +145,7 @@ def marshal_step(L, torch, wl, rep):
     t["ws_idx"] = torch.empty(n.value, dtype=torch.uint8, device="cuda")
     t["ws_idx_n"] = ctypes.c_size_t(n.value)
     calls.append((lib.csa_index_topk, idx_args + (P(t["ws_idx"]), ctypes.byref(t["ws_idx_n"]), st)))
-    index_call = len(calls) - 1
+    timed = {len(calls) - 1: "index_mfma_kernel"}
     # CSA attention
     att = (P(t["q"]), P(wl.kc), P(wl.vc), L.BF16, P(t["idx"]), TOPK, P(t["kw"]), P(t["vw"]), P(wl.win_pos0), LWIN, W,
            P(wl.q_pos), B, 1, H, D, N_CSA, 0, ctypes.c_float(scale), P(t["o"]), P(t["lse"]))
@@ -139,6 +153,7 @@ def marshal_step(L, torch, wl, rep):
     t["ws_csa"] = torch.empty(max(n.value, 1), dtype=torch.uint8, device="cuda")
     t["ws_csa_n"] = ctypes.c_size_t(n.value)
     calls.append((lib.csa_attend, att + (P(t["ws_csa"]), ctypes.byref(t["ws_csa_n"]), st)))
+    timed[len(calls) - 1] = "attend_bf16_kernel (CSA)"
     # HCA: the newest 128-token block (the whole window) -> entry N_HCA-1
     for src, dst in ((t["hkw"], t["hkc"]), (t["hvw"], t["hvc"])):
         calls.append((lib.csa_compress, (P(src), L.BF16, P(t["hgate"]), P(t["hbias"]), B, M_HCA, D, M_HCA, LWIN,
@@ -149,7 +164,8 @@ def marshal_step(L, torch, wl, rep):
     t["ws_hca"] = torch.empty(max(n.value, 1), dtype=torch.uint8, device="cuda")
     t["ws_hca_n"] = ctypes.c_size_t(n.value)
     calls.append((lib.hca_attend, hatt + (P(t["ws_hca"]), ctypes.byref(t["ws_hca_n"]), st)))
-    return calls, index_call
+    timed[len(calls) - 1] = "attend_bf16_kernel (HCA)"
+    return calls, timed
 
 
 class HipEvents:
@@ -171,10 +187,11 @@ class HipEvents:
         return ms.value
 
 
-def run_step(lib, calls, arm=None, index_call=-1):
+def run_step(lib, calls, arm=None):
+    """One step; arm maps a call index to the (start, stop) events of its main kernel."""
     for i, (fn, args) in enumerate(calls):
-        if arm is not None and i == index_call:
-            lib.dsv4_time_next_kernel(*arm)
+        if arm is not None and i in arm:
+            lib.dsv4_time_next_kernel(*arm[i])
         st = fn(*args)
         if st != 0:
             raise RuntimeError(f"{fn.__name__}: {lib.dsv4_last_error().decode()}")
@@ -182,7 +199,9 @@ def run_step(lib, calls, arm=None, index_call=-1):
 
 # ------------------------------------------------------------------------------------ oracle leg
 def cpu_baseline(L, torch, synth, wl, budget_s):
-    """The float64 oracle on host cores, on whole sequences of replica 0 until ~budget_s."""
+    """The float64 oracle on one host thread: whole decode steps of the sequences of
+    replica 0 (both layers), cycling over the 8 sequences until ~budget_s of timed work.
+    Inputs are generated and decoded beforehand (untimed); the library is not used."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -193,60 +212,68 @@ def cpu_baseline(L, torch, synth, wl, budget_s):
     def bits(x):
         return x.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
+    seqs = []
+    for b in range(B):
+        k32 = synth.device_normal((1, N_CSA, DI), seed(CFG_CSA, synth.KI, 0, b), torch.float32)[0].cpu().numpy()
+        packed, scales = codecs.encode_mxfp4(k32)                 # the stored MXFP4 cache
+        del k32
+        seqs.append(dict(
+            packed=packed, scales=scales,
+            q=codecs.decode_bf16(bits(t["q"][b:b + 1])), qi=codecs.decode_bf16(bits(t["qi"][b:b + 1])),
+            wi=t["wi"][b:b + 1].cpu().numpy(),
+            kw=codecs.decode_bf16(bits(t["kw"][b:b + 1])), vw=codecs.decode_bf16(bits(t["vw"][b:b + 1])),
+            kiw=codecs.decode_bf16(bits(t["kiw"][b:b + 1])), gate=t["gate"][b:b + 1].cpu().numpy(),
+            bias=t["bias"].cpu().numpy(), hq=codecs.decode_bf16(bits(t["hq"][b:b + 1])),
+            hk=codecs.decode_bf16(bits(t["hkc"][b:b + 1])), hv=codecs.decode_bf16(bits(t["hvc"][b:b + 1])),
+            hkw=codecs.decode_bf16(bits(t["hkw"][b:b + 1])), hvw=codecs.decode_bf16(bits(t["hvw"][b:b + 1])),
+            hgate=t["hgate"][b:b + 1].cpu().numpy(), hbias=t["hbias"].cpu().numpy(),
+            kc=wl.kc[b], vc=wl.vc[b]))
+
     done, elapsed = 0, 0.0
     scale = 1.0 / math.sqrt(D)
+    pos = np.array([[CTX - 1]])
     with threadpool_limits(limits=1):
-        for b in range(B):
-            # ---- inputs of sequence b (generated by torch's RNG; nothing from the library)
-            k32 = synth.device_normal((1, N_CSA, DI), seed(CFG_CSA, synth.KI, 0, b), torch.float32)[0].cpu().numpy()
-            packed, scales = codecs.encode_mxfp4(k32)            # the stored MXFP4 cache (untimed)
-            del k32
-            q = codecs.decode_bf16(bits(t["q"][b:b + 1]))
-            qi = codecs.decode_bf16(bits(t["qi"][b:b + 1]))
-            wi = t["wi"][b:b + 1].cpu().numpy()
-            kw, vw = codecs.decode_bf16(bits(t["kw"][b:b + 1])), codecs.decode_bf16(bits(t["vw"][b:b + 1]))
-            kiw = codecs.decode_bf16(bits(t["kiw"][b:b + 1]))
-            gate = t["gate"][b:b + 1].cpu().numpy()
-            bias = t["bias"].cpu().numpy()
-            hq = codecs.decode_bf16(bits(t["hq"][b:b + 1]))
-            hkc_bits, hvc_bits = bits(t["hkc"][b:b + 1]), bits(t["hvc"][b:b + 1])
-            hkw, hvw = codecs.decode_bf16(bits(t["hkw"][b:b + 1])), codecs.decode_bf16(bits(t["hvw"][b:b + 1]))
-            hgate, hbias = t["hgate"][b:b + 1].cpu().numpy(), t["hbias"].cpu().numpy()
-            kcb, vcb = wl.kc[b], wl.vc[b]
+        while elapsed < budget_s:
+            sq = seqs[done % B]
             t0 = time.perf_counter()
             # ---- CSA: compress the newest block (K, V, indexer key -> MXFP4)
-            g4 = gate[:, LWIN - M_CSA:]
-            new_k = method.compress(kw[:, LWIN - M_CSA:], g4, bias, M_CSA)
-            new_v = method.compress(vw[:, LWIN - M_CSA:], g4, bias, M_CSA)
-            new_ki = method.compress(kiw[:, LWIN - M_CSA:], g4, bias, M_CSA)
+            g4 = sq["gate"][:, LWIN - M_CSA:]
+            new_k = method.compress(sq["kw"][:, LWIN - M_CSA:], g4, sq["bias"], M_CSA)
+            new_v = method.compress(sq["vw"][:, LWIN - M_CSA:], g4, sq["bias"], M_CSA)
+            new_ki = method.compress(sq["kiw"][:, LWIN - M_CSA:], g4, sq["bias"], M_CSA)
             p_new, s_new = codecs.encode_mxfp4(new_ki[0].astype(np.float32))
+            packed, scales = sq["packed"].copy(), sq["scales"].copy()
             packed[-1], scales[-1] = p_new[0], s_new[0]
             ki = codecs.Stored(packed[None], codecs.MXFP4, scales[None])
-            pos = np.array([[CTX - 1]])
-            s = method.index_scores(qi, wi, ki, pos, M_CSA)
+            s = method.index_scores(sq["qi"], sq["wi"], ki, pos, M_CSA)
             idx = method.topk(s, pos, M_CSA, TOPK)
             sel = idx[0, 0][idx[0, 0] >= 0]
+            t_gather = time.perf_counter()
             old = sel[sel < N_CSA - 1]
-            kg = codecs.decode_bf16(bits(kcb[torch.from_numpy(old).cuda()]))
-            vg = codecs.decode_bf16(bits(vcb[torch.from_numpy(old).cuda()]))
+            kg = codecs.decode_bf16(bits(sq["kc"][torch.from_numpy(old).cuda()]))
+            vg = codecs.decode_bf16(bits(sq["vc"][torch.from_numpy(old).cuda()]))
+            t_gather = time.perf_counter() - t_gather               # device-to-host gather: not timed
             if len(old) < len(sel):
                 kg = np.concatenate([kg, new_k[0]])
                 vg = np.concatenate([vg, new_v[0]])
-            # attention over the gathered selection (listed 0..n-1) and the window
             n_sel = len(sel)
-            o_c, _ = method.csa_attend(q, kg[None], vg[None], np.arange(n_sel)[None, None], kw, vw,
-                                       np.array([CTX - LWIN]), W, pos, scale)
+            method.csa_attend(sq["q"], kg[None], vg[None], np.arange(n_sel)[None, None], sq["kw"], sq["vw"],
+                              np.array([CTX - LWIN]), W, pos, scale)
             # ---- HCA: compress the newest block, dense attention
-            hk = codecs.decode_bf16(hkc_bits)
-            hv = codecs.decode_bf16(hvc_bits)
-            hk[0, -1] = method.compress(hkw, hgate, hbias, M_HCA)[0, 0]
-            hv[0, -1] = method.compress(hvw, hgate, hbias, M_HCA)[0, 0]
-            o_h, _ = method.hca_attend(hq, hk, hv, M_HCA, hkw, hvw, np.array([CTX - LWIN]), W, pos, scale)
-            elapsed += time.perf_counter() - t0
+            hk, hv = sq["hk"].copy(), sq["hv"].copy()
+            hk[0, -1] = method.compress(sq["hkw"], sq["hgate"], sq["hbias"], M_HCA)[0, 0]
+            hv[0, -1] = method.compress(sq["hvw"], sq["hgate"], sq["hbias"], M_HCA)[0, 0]
+            method.hca_attend(sq["hq"], hk, hv, M_HCA, sq["hkw"], sq["hvw"], np.array([CTX - LWIN]), W, pos, scale)
+            elapsed += time.perf_counter() - t0 - t_gather
             done += 1
-            if elapsed >= budget_s:
-                break
     return done, elapsed
+
+
+def source_sha(path):
+    import hashlib
+
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
 
 
 def main():
@@ -257,11 +284,13 @@ def main():
     ap.add_argument("--replicas", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one device copy of this size after warm-up (reference for traffic counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        sys.stderr.write("bench.py measures one GPU only: this build runs the path on a single MI355X "
-                         "(the multi-GPU sharding is described, not built). Use --gpus 1.\n")
+        sys.stderr.write("bench.py measures one GPU only: the path runs on a single MI355X and multi-GPU "
+                         "sharding is not implemented. Use --gpus 1.\n")
         sys.exit(2)
 
     import torch
@@ -273,25 +302,43 @@ def main():
     torch.cuda.set_device(0)
     wl = Workload(L, torch, synth, args.replicas)
     steps = [marshal_step(L, torch, wl, r) for r in range(args.replicas)]
-    index_call = steps[0][1]
+    timed = steps[0][1]
     ev = HipEvents()
-    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    pairs = [{i: (ev.create(), ev.create()) for i in timed} for _ in range(args.steps)]
 
     for i in range(args.warmup):
         run_step(lib, steps[i % args.replicas][0])
     torch.cuda.synchronize()
+    if args.copy_calibration_mib:
+        # a plain device copy of known size: the reference reading for the traffic counters
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(args.steps):
-        run_step(lib, steps[i % args.replicas][0], arm=pairs[i], index_call=index_call)
+        run_step(lib, steps[i % args.replicas][0], arm=pairs[i])
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
-    k_ms = sum(ev.elapsed_ms(a, b) for a, b in pairs) / args.steps
 
     total_bytes, parts = algorithmic_bytes()
     qps = B / (ms / 1e3)
-    achieved = INDEX_KERNEL_BYTES / (k_ms / 1e3) / 1e9
+    kernels = {}
+    for i, name in timed.items():
+        k_ms = sum(ev.elapsed_ms(*p[i]) for p in pairs) / args.steps
+        gbs = KERNEL_BYTES[name] / (k_ms / 1e3) / 1e9
+        kernels[name] = {"avg_launch_us": round(k_ms * 1e3, 2), "bytes_per_launch": KERNEL_BYTES[name],
+                         "achieved_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    dom = max(kernels, key=lambda n: kernels[n]["avg_launch_us"])
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "long_context_attention_25_amd", "csrc",
+                       "index_topk.hip" if dom.startswith("index") else "attend.hip")
+    tr = MEASURED_TRAFFIC.get(dom)
+    traffic = tr["bytes_per_launch"] if tr and tr["source_sha256"] == source_sha(src) else None
+    k = kernels[dom]
     out = {
         "metric": "CSA+HCA decode queries/s at 1M ctx + achieved HBM GB/s vs peak",
         "value": round(qps, 1),
@@ -313,16 +360,17 @@ def main():
         "step_hbm_gbs": round(total_bytes / (ms / 1e3) / 1e9, 1),
         "step_hbm_frac": round(total_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "bytes_per_step": total_bytes,
-        "roofline": {"bound": "hbm", "kernel": "index_mfma_kernel (MXFP4 keys)",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "bytes_per_launch": INDEX_KERNEL_BYTES, "avg_launch_ms": round(k_ms, 5)},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": k["achieved_gbs"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": k["frac"], "traffic": traffic,
+                     "bytes_per_launch": k["bytes_per_launch"], "avg_launch_us": k["avg_launch_us"]},
+        "kernels": kernels,
     }
     if not args.no_cpu_baseline:
         done, el = cpu_baseline(L, torch, synth, wl, args.cpu_seconds)
         out["cpu_baseline"] = {"value": round(done / el, 3), "unit": "queries/s", "cores": 1, "kind": "oracle",
-                               "sample": f"{done} of {B} sequences of replica 0, one decode step each "
-                                         f"(both layers), {el:.1f} s on 1 host thread (float64 NumPy)"}
+                               "sample": f"{done} decode steps of single sequences (both layers; cycling over "
+                                         f"the {B} sequences of replica 0), {el:.1f} s on 1 host thread "
+                                         f"(float64 NumPy oracle)"}
     print(json.dumps(out), flush=True)
 
 

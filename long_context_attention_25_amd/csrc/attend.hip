@@ -96,10 +96,19 @@ __device__ __forceinline__ const uint16_t* lane_ptr(const uint16_t* p, int src) 
   return reinterpret_cast<const uint16_t*>(((uint64_t)hi << 32) | lo);
 }
 
-// Async copy of 16 bytes per lane from global memory into LDS at dst + lane * 16.
-__device__ __forceinline__ void copy16_to_lds(const void* src, void* dst) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                   (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+// Async copy of 16 bytes per lane from global memory (per-lane address) into LDS at byte
+// address lds + 16 * lane; lds must be the same in every lane.  Issued from asm so that
+// the compiler does not track it: it would otherwise make LDS reads wait for copies into
+// other buffers.  The copy has no register result; completion is waited for explicitly
+// with wait_vmcnt (it counts as a vector-memory operation until its data is in LDS).
+// s_nop 3 covers the m0 write before the copy reads it.
+__device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 3\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src),
+               "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p);
 }
 
 // Wait until at most n vector-memory operations of this wave are outstanding (n < 64).
@@ -122,21 +131,24 @@ __device__ __forceinline__ void tile_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// One workgroup = 4 waves, one per SIMD; wave w owns heads 16w .. 16w+15 over the full
-// head dim (scores and output).  The key list of the split is walked in 32-key tiles;
-// tile t+1's K and V rows are copied straight into the other half of a two-stage LDS
-// ring while tile t is used.  Rows are padded in LDS (K: +16 bytes, V: +32 bytes) so that
-// the K operand reads (16 rows, same column) and the transposed V reads (4 rows x 2
-// chunks per 16 lanes) hit distinct banks while every read of a lane uses one base
-// address plus immediate offsets.
-template <int D>
-__global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendArgs a, int64_t chunk, int splits,
-                                                               float* __restrict__ o_part,
+// One workgroup = 4 x DS waves: wave w owns heads 16(w%4) .. +15 and the slice w/4 of
+// the head dim for the output (each of the DS waves of a head group computes the same
+// scores over the full head dim; this keeps the accumulators in ordinary VGPRs).  The key list of the split is walked in 16-key tiles
+// through a four-stage LDS ring: while tile t is used, tiles t+1 .. t+3 are being copied
+// straight into LDS, so about 100 KB per CU stay in flight.  Rows are padded in LDS (K: +16
+// bytes, V: +32 bytes) so that the K operand reads (16 rows, same column) and the
+// transposed V reads (4 rows x 2 chunks per 16 lanes) hit distinct banks while every read
+// of a lane uses one base address plus immediate offsets.
+template <int D, int DS>
+__global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a, int64_t chunk, int splits,
+                                                               uint16_t* __restrict__ o_part,
                                                                float* __restrict__ lse_part) {
-  constexpr int KT = 32;                   // keys per tile
-  constexpr int NWV = kThreads / kWave;    // 4
+  constexpr int KT = 16;                   // keys per tile
+  constexpr int NT = kThreads * DS;
+  constexpr int NWV = NT / kWave;
   constexpr int KS = D / 32;               // MFMA k-steps over the head dim
-  constexpr int NDT = D / 16;              // 16-dim output tiles
+  constexpr int DH = D / DS;               // output dims of a wave
+  constexpr int NDT = DH / 16;             // 16-dim output tiles of a wave
   constexpr int RB = D * 2;                // bytes per row
   constexpr int KSTR = RB + 16;            // LDS row strides
   constexpr int VSTR = RB + 32;
@@ -145,12 +157,10 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendArgs a, int
   constexpr int NL = 2 * RPW;              // copy instructions per wave and tile
   constexpr int KTB = KT * KSTR, VTB = KT * VSTR;
   static_assert(LPR <= kWave && kWave % LPR == 0, "a row is copied by one instruction");
-  static_assert(NL < 64, "vmcnt range");
+  static_assert(3 * NL < 64, "vmcnt range");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t k0[KTB];
-  __shared__ __attribute__((aligned(1024))) uint8_t v0[VTB];
-  __shared__ __attribute__((aligned(1024))) uint8_t k1[KTB];
-  __shared__ __attribute__((aligned(1024))) uint8_t v1[VTB];
+  constexpr int STB = KTB + VTB;          // one stage: K tile then V tile
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[4 * STB];
   __shared__ int32_t list[kMaxCsaChunk];  // the split's index entries
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -169,20 +179,21 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendArgs a, int
   const uint16_t* kw = reinterpret_cast<const uint16_t*>(a.kw) + b * a.L * D;
   const uint16_t* vw = reinterpret_cast<const uint16_t*>(a.vw) + b * a.L * D;
 
-  const int head = wave * 16 + col;
-  const bool wave_on = wave * 16 < a.H;
+  const int hg = wave % 4, dh = wave / 4;  // head group and output slice
+  const int head = hg * 16 + col;
+  const bool wave_on = hg * 16 < a.H;
 
   // CSA: the split's index entries, once, in LDS (the tile loop issues no other loads)
   if (a.csa) {
     int64_t e1 = s1 < kr.n_c ? s1 : kr.n_c;
-    for (int64_t p = s0 + tid; p < e1; p += kThreads) list[p - s0] = a.idx[bq * a.k + p];
+    for (int64_t p = s0 + tid; p < e1; p += NT) list[p - s0] = a.idx[bq * a.k + p];
   }
   __syncthreads();
 
-  // Row pointers of tile t for key (lane % 32); invalid slots point at a real row.
+  // Row pointers of tile t for key (lane % 16); invalid slots point at a real row.
   const uint16_t* my_kp;
   const uint16_t* my_vp;
-  uint32_t vmask;                           // validity of the tile's 32 keys
+  uint32_t vmask;                           // validity of the tile's 16 keys
   auto tile_ptrs = [&](int t) {
     const int64_t pos = s0 + (int64_t)t * KT + (lane & (KT - 1));
     bool ok = false;
@@ -205,12 +216,14 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendArgs a, int
     }
     my_kp = kp;
     my_vp = vp;
-    vmask = (uint32_t)__ballot(ok);
+    vmask = (uint32_t)__ballot(ok) & 0xffffu;
   };
-  // Wave w copies rows w, w+4, ... of the tile; a row is LPR lanes x 16 bytes.  When a
-  // row is shorter than a wave, the other lanes are masked off and the LDS base is moved
-  // back so that the active lanes land on the row.
-  auto issue = [&](uint8_t* kdst, uint8_t* vdst) {
+  // Wave w copies rows w, w+4, ... of the tile; a row is LPR lanes x 16 bytes (the other
+  // lanes of a wave are masked off when a row is shorter than a wave).
+  const uint32_t ring_lds = lds_addr(ring);
+  auto issue = [&](int stage) {
+    const uint32_t kdst = ring_lds + stage * STB;
+    const uint32_t vdst = kdst + KTB;
     const int j = lane / LPR;              // 0 unless LPR < 64
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
@@ -223,33 +236,32 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendArgs a, int
     }
   };
 
-  f32x4 acc[NDT];                          // O^T dims 16dt + 4g + i, head `head`
+  f32x4 acc[NDT];                          // O^T dims dh*DH + 16dt + 4g + i, head `head`
 #pragma unroll
   for (int i = 0; i < NDT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.scale * kLog2e;
   // per-lane LDS byte offsets: K operand row `col`, chunk g*KS; V^T rows 4g + col/4 at
-  // dims 4(col%4)
+  // dims dh*DH + 4(col%4)
   const int k_off = col * KSTR + g * (D / 4) * 2;
-  const int v_off = (4 * g + (col >> 2)) * VSTR + (col & 3) * 8;
+  const int v_off = (4 * g + (col >> 2)) * VSTR + dh * DH * 2 + (col & 3) * 8;
 
   uint4 qop[KS];                           // Q^T operands, loaded below
-  auto compute = [&](const uint8_t* kt_l, const uint8_t* vt_l, uint32_t cur_mask) {
+  auto compute = [&](int stage, uint32_t cur_mask) {
     if (!wave_on) return;
-    // ---- S^T = K . Q^T for keys 0..15 and 16..31 of the tile.  K operands are read in
-    // batches of 2 x CB (two batches stay within the 15 outstanding LDS reads the counter
-    // tracks); batch i+1 is issued before the MFMAs of batch i (the scheduling
-    // barriers keep the compiler from interleaving each read with its MFMA).
-    f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    constexpr int CB = KS < 2 ? KS : 2;
+    const uint8_t* kt_l = ring + stage * STB;
+    const uint8_t* vt_l = kt_l + KTB;
+    // ---- S^T = K . Q^T (16 keys x 16 heads).  K operands are read in batches of CB;
+    // batch i+1 is issued before the MFMAs of batch i (the scheduling barriers keep the
+    // compiler from pairing each read with its MFMA; two batches stay within the 15
+    // outstanding LDS reads the counter tracks).
+    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr int CB = KS < 4 ? KS : 4;
     constexpr int NB = KS / CB;
-    uint4 kv[2][2][CB];
+    uint4 kv[2][CB];
     auto kread = [&](int buf, int c0) {
 #pragma unroll
-      for (int c = 0; c < CB; ++c)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-          kv[buf][kt][c] = *reinterpret_cast<const uint4*>(kt_l + k_off + kt * 16 * KSTR + (c0 + c) * 16);
+      for (int c = 0; c < CB; ++c) kv[buf][c] = *reinterpret_cast<const uint4*>(kt_l + k_off + (c0 + c) * 16);
     };
     kread(0, 0);
 #pragma unroll
@@ -258,21 +270,17 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendArgs a, int
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int c = 0; c < CB; ++c)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-          s[kt] = mfma_bf16(bit_cast_to<bf16x8>(kv[bi & 1][kt][c]), bit_cast_to<bf16x8>(qop[bi * CB + c]), s[kt]);
+        s = mfma_bf16(bit_cast_to<bf16x8>(kv[bi & 1][c]), bit_cast_to<bf16x8>(qop[bi * CB + c]), s);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // ---- softmax (lane holds keys 16kt + 4g + i of head `head`), lazy rescaling
+    // ---- softmax (lane holds keys 4g + i of head `head`), lazy rescaling
     float mx = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool ok = (cur_mask >> (kt * 16 + 4 * g + i)) & 1u;
-        s[kt][i] = ok ? s[kt][i] * sl2 : -INFINITY;
-        mx = fmaxf(mx, s[kt][i]);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = (cur_mask >> (4 * g + i)) & 1u;
+      s[i] = ok ? s[i] * sl2 : -INFINITY;
+      mx = fmaxf(mx, s[i]);
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);
@@ -286,31 +294,25 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendArgs a, int
       m_run = m_new;
     }
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    float pv[8];
+    float pv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      pv[i] = exp2f(s[0][i] - m_use);
-      pv[4 + i] = exp2f(s[1][i] - m_use);
+      pv[i] = exp2f(s[i] - m_use);
+      l_run += pv[i];
     }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) l_run += pv[i];
-    // P^T operand: slots 0-3 are keys 4g+i, slots 4-7 keys 16+4g+i
-    const bf16x8 pb = bit_cast_to<bf16x8>(make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
-                                                     pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])));
+    // P^T operand of the 16x16x16 MFMA: this lane's own keys 4g .. 4g+3 of head `head`
+    const v4i16 pb = __builtin_bit_cast(v4i16, make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])));
     // ---- O^T += V^T . P^T; V^T operands by transposed LDS reads of the row-major tile:
-    // lane p of a 16-lane block addresses key row 4g + p/4 (then 16 + 4g + p/4) at dims
-    // 16dt + 4(p%4) and receives its own dim (16dt + p) from the four key rows.
-    constexpr int DB = NDT < 2 ? NDT : 2;
+    // lane p of a 16-lane block addresses key row 4g + p/4 at dims 16dt + 4(p%4) and
+    // receives its own dim (16dt + p) from the four key rows.
+    constexpr int DB = NDT < 4 ? NDT : 4;
     constexpr int ND = NDT / DB;
-    v4i16 vlo[2][DB], vhi[2][DB];
+    v4i16 vt[2][DB];
     auto vread = [&](int buf, int d0) {
 #pragma unroll
-      for (int d = 0; d < DB; ++d) {
-        vlo[buf][d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      for (int d = 0; d < DB; ++d)
+        vt[buf][d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) v4i16*)(vt_l + v_off + (d0 + d) * 32));
-        vhi[buf][d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16*)(vt_l + v_off + 16 * VSTR + (d0 + d) * 32));
-      }
     };
     vread(0, 0);
 #pragma unroll
@@ -318,56 +320,42 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendArgs a, int
       if (bi + 1 < ND) vread((bi + 1) & 1, (bi + 1) * DB);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int d = 0; d < DB; ++d) {
-        const uint2 l2 = __builtin_bit_cast(uint2, vlo[bi & 1][d]), h2 = __builtin_bit_cast(uint2, vhi[bi & 1][d]);
-        acc[bi * DB + d] = mfma_bf16(bit_cast_to<bf16x8>(make_uint4(l2.x, l2.y, h2.x, h2.y)), pb, acc[bi * DB + d]);
-      }
+      for (int d = 0; d < DB; ++d)
+        acc[bi * DB + d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[bi & 1][d], pb, acc[bi * DB + d], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // Tiles alternate between stage 0 (even t) and stage 1 (odd t).  Before tile t is used,
-  // tile t+1 is issued into the other stage; the barrier after tile t lets stage t%2 be
-  // overwritten by tile t+2.
-  uint32_t mask0 = 0, mask1 = 0;
-  if (ntile > 0) {
-    tile_ptrs(0);
-    mask0 = vmask;
-    issue(k0, v0);
-  }
-  // Q^T operand of this lane: head `head`, dims g*D/4 + 8c .. +7 for k-step c.  Loaded
-  // while tile 0 is in flight; both are waited for here, before the loop (registers
-  // still loading at loop entry would make the compiler drain every load there anyway).
+  // Tile t lives in stage t % 4.  Tiles 0..2 are issued first and this lane's Q^T operands
+  // (head `head`, dims g*D/4 + 8c .. +7 for k-step c) behind them, so that the query
+  // loads overlap the first copies; one wait covers both.  Step t then waits for tile t
+  // (tiles t+1, t+2 stay in flight), passes a barrier (tile t visible to all waves; every
+  // wave is done with tile t-1), issues tile t+3 into the stage of tile t-1 and uses tile t.
+  uint32_t mq0 = 0, mq1 = 0, mq2 = 0;      // masks of tiles t, t+1, t+2
+  if (ntile > 0) { tile_ptrs(0); mq0 = vmask; issue(0); }
+  if (ntile > 1) { tile_ptrs(1); mq1 = vmask; issue(1); }
+  if (ntile > 2) { tile_ptrs(2); mq2 = vmask; issue(2); }
   {
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + (bq * a.H + (wave_on ? head : 0)) * D + g * (D / 4);
 #pragma unroll
     for (int c = 0; c < KS; ++c) qop[c] = gload_u4(qp + 8 * c);
   }
   wait_vmcnt<0>();
-  for (int t = 0; t < ntile; t += 2) {
-    if (t + 1 < ntile) {
-      tile_ptrs(t + 1);
-      mask1 = vmask;
-      issue(k1, v1);
-      wait_vmcnt<NL>();                    // tile t has landed; tile t+1 stays in flight
-    } else {
-      wait_vmcnt<0>();
+  for (int t = 0; t < ntile; ++t) {
+    if (t + 2 < ntile) wait_vmcnt<2 * NL>();
+    else if (t + 1 < ntile) wait_vmcnt<NL>();
+    else wait_vmcnt<0>();
+    tile_barrier();
+    uint32_t mq3 = 0;
+    if (t + 3 < ntile) {
+      tile_ptrs(t + 3);
+      mq3 = vmask;
+      issue((t + 3) & 3);
     }
-    tile_barrier();
-    compute(k0, v0, mask0);
-    tile_barrier();
-    if (t + 1 >= ntile) break;
-    if (t + 2 < ntile) {
-      tile_ptrs(t + 2);
-      mask0 = vmask;
-      issue(k0, v0);
-      wait_vmcnt<NL>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    tile_barrier();
-    compute(k1, v1, mask1);
-    tile_barrier();
+    compute(t & 3, mq0);
+    mq0 = mq1;
+    mq1 = mq2;
+    mq2 = mq3;
   }
 
   if (!wave_on) return;
@@ -375,25 +363,25 @@ __global__ __launch_bounds__(kThreads) void attend_bf16_kernel(AttendArgs a, int
   l_run += __shfl_xor(l_run, 32);
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
   const float lse = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+  // the output row, or with several splits this split's partial row (bf16 like the
+  // output; the merge accumulates in fp32)
   const int64_t R = a.B * a.Q * a.H;
   const int64_t orow = bq * a.H + head;
-  if (splits == 1) {
-    uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + orow * D;
+  uint16_t* out = (splits == 1 ? reinterpret_cast<uint16_t*>(a.out) + orow * D
+                               : o_part + ((int64_t)split * R + orow) * D) + dh * DH;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      uint2 w;
-      w.x = pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv);
-      w.y = pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv);
-      *reinterpret_cast<uint2*>(out + dt * 16 + 4 * g) = w;
+  for (int dt = 0; dt < NDT; ++dt) {
+    uint2 w;
+    w.x = pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv);
+    w.y = pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv);
+    *reinterpret_cast<uint2*>(out + dt * 16 + 4 * g) = w;
+  }
+  if (g == 0 && dh == 0) {
+    if (splits == 1) {
+      if (a.lse) a.lse[orow] = lse;
+    } else {
+      lse_part[(int64_t)split * R + orow] = lse;
     }
-    if (g == 0 && a.lse) a.lse[orow] = lse;
-  } else {
-    float* op = o_part + ((int64_t)split * R + orow) * D;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-      *reinterpret_cast<float4*>(op + dt * 16 + 4 * g) =
-          make_float4(acc[dt][0] * inv, acc[dt][1] * inv, acc[dt][2] * inv, acc[dt][3] * inv);
-    if (g == 0) lse_part[(int64_t)split * R + orow] = lse;
   }
 }
 
@@ -551,6 +539,83 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(const float* __rest
   if (lane == 0 && lse_out) lse_out[r] = (tot > 0.f) ? mx + logf(tot) : -INFINITY;
 }
 
+// Merge of the attention kernel's bf16 split partials (same arithmetic as lse_merge_kernel
+// with 8 dims per lane and load): one wave per output row, bf16 output.
+template <int NV>
+__global__ __launch_bounds__(kThreads) void merge_bf16_parts_kernel(const uint16_t* __restrict__ o_parts,
+                                                                    const float* __restrict__ lse_parts, int P,
+                                                                    int64_t R, int D, uint16_t* __restrict__ out,
+                                                                    float* __restrict__ lse_out) {
+  __shared__ float wsh[kThreads / kWave][1024];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t r = (int64_t)blockIdx.x * (kThreads / kWave) + wave;
+  if (r >= R) return;                    // whole wave; no workgroup barrier below
+  float* w = wsh[wave];
+  float mx = -INFINITY;
+  for (int p = lane; p < P; p += kWave) mx = fmaxf(mx, lse_parts[(int64_t)p * R + r]);
+  mx = wave_max(mx);
+  float tot = 0.f;
+  for (int p = lane; p < P; p += kWave) {
+    float e = (mx == -INFINITY) ? 0.f : expf(lse_parts[(int64_t)p * R + r] - mx);
+    w[p] = e;
+    tot += e;
+  }
+  tot = wave_sum(tot);
+  __builtin_amdgcn_s_waitcnt(0xc07f);    // lgkmcnt(0): this wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  const int nd8 = D / 8;
+  float acc[NV][8];
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
+  const uint4* base = reinterpret_cast<const uint4*>(o_parts + r * D);
+  const int64_t pstride = R * D / 8;     // uint4 stride between parts
+  auto fma8 = [&](float wu, const uint4& v, float* a8) {
+    const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a8[2 * e] = fmaf(wu, __uint_as_float(x[e] << 16), a8[2 * e]);
+      a8[2 * e + 1] = fmaf(wu, __uint_as_float(x[e] & 0xffff0000u), a8[2 * e + 1]);
+    }
+  };
+  int p = 0;
+  for (; p + 4 <= P; p += 4) {
+    uint4 v[4][NV];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int d8 = lane + i * kWave;
+        v[u][i] = d8 < nd8 ? base[(int64_t)(p + u) * pstride + d8] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < NV; ++i) fma8(w[p + u], v[u][i], acc[i]);
+  }
+  for (; p < P; ++p) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int d8 = lane + i * kWave;
+      if (d8 < nd8) fma8(w[p], base[(int64_t)p * pstride + d8], acc[i]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int d8 = lane + i * kWave;
+    if (d8 >= nd8) continue;
+    uint4 o;
+    o.x = pack_bf16x2(acc[i][0] * inv, acc[i][1] * inv);
+    o.y = pack_bf16x2(acc[i][2] * inv, acc[i][3] * inv);
+    o.z = pack_bf16x2(acc[i][4] * inv, acc[i][5] * inv);
+    o.w = pack_bf16x2(acc[i][6] * inv, acc[i][7] * inv);
+    reinterpret_cast<uint4*>(out + r * D)[d8] = o;
+  }
+  if (lane == 0 && lse_out) lse_out[r] = (tot > 0.f) ? mx + logf(tot) : -INFINITY;
+}
+
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
@@ -576,7 +641,7 @@ AttendPlan plan_attend(const AttendArgs& a) {
   p.chunk = (int)chunk;
   if (splits > 1) {
     const int64_t R = a.B * a.Q * a.H;
-    p.ws_bytes = align256((size_t)splits * R * a.D * 4) + align256((size_t)splits * R * 4);
+    p.ws_bytes = align256((size_t)splits * R * a.D * 2) + align256((size_t)splits * R * 4);   // bf16 parts
   }
   return p;
 }
@@ -589,22 +654,29 @@ hipError_t launch_attend(const AttendArgs& a, const AttendPlan& p, void* ws, hip
     DSV4_LAUNCH_MAIN(attend_f32_kernel, dim3((unsigned)a.H, (unsigned)rows), dim3(kThreads), smem, st, a);
     return hipGetLastError();
   }
-  float* o_part = nullptr;
+  uint16_t* o_part = nullptr;
   float* lse_part = nullptr;
   const int64_t R = rows * a.H;
   if (p.splits > 1) {
-    o_part = reinterpret_cast<float*>(ws);
-    lse_part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + align256((size_t)p.splits * R * a.D * 4));
+    o_part = reinterpret_cast<uint16_t*>(ws);
+    lse_part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + align256((size_t)p.splits * R * a.D * 2));
   }
   dim3 grid((unsigned)p.splits, (unsigned)rows);
   switch (a.D) {
-    case 128: DSV4_LAUNCH_MAIN((attend_bf16_kernel<128>), grid, dim3(kThreads), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part); break;
-    case 256: DSV4_LAUNCH_MAIN((attend_bf16_kernel<256>), grid, dim3(kThreads), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part); break;
-    default: DSV4_LAUNCH_MAIN((attend_bf16_kernel<512>), grid, dim3(kThreads), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part); break;
+    case 128: DSV4_LAUNCH_MAIN((attend_bf16_kernel<128, 1>), grid, dim3(kThreads), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part); break;
+    case 256: DSV4_LAUNCH_MAIN((attend_bf16_kernel<256, 1>), grid, dim3(kThreads), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part); break;
+    default: DSV4_LAUNCH_MAIN((attend_bf16_kernel<512, 2>), grid, dim3(kThreads * 2), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  return launch_lse_merge(o_part, lse_part, p.splits, R, a.D, a.out, false, a.lse, st);
+  {
+    const int rows_per_wg = kThreads / kWave;
+    dim3 mgrid((unsigned)((R + rows_per_wg - 1) / rows_per_wg));
+    uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+    hipLaunchKernelGGL(merge_bf16_parts_kernel<1>, mgrid, dim3(kThreads), 0, st, o_part, lse_part, p.splits, R, a.D,
+                       out, a.lse);   // D <= 512: one 8-dim load per lane and part
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_lse_merge(const float* o_parts, const float* lse_parts, int P, int64_t R, int D, void* out,
