@@ -539,17 +539,20 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(const float* __rest
   if (lane == 0 && lse_out) lse_out[r] = (tot > 0.f) ? mx + logf(tot) : -INFINITY;
 }
 
-// Merge of the attention kernel's bf16 split partials (same arithmetic as lse_merge_kernel
-// with 8 dims per lane and load): one wave per output row, bf16 output.
-template <int NV>
+// Merge of the attention kernel's bf16 split partials (the arithmetic of lse_merge_kernel):
+// one workgroup per output row.  Every wave computes the part weights exp(lse_p - lse)
+// into its own LDS slice; wave w then accumulates parts w, w+4, ... for 8 dims per lane
+// with up to 8 loads in flight, and the four partial sums are added through LDS.
+constexpr int kMergePPT = 8;              // parts per lane and round
 __global__ __launch_bounds__(kThreads) void merge_bf16_parts_kernel(const uint16_t* __restrict__ o_parts,
                                                                     const float* __restrict__ lse_parts, int P,
                                                                     int64_t R, int D, uint16_t* __restrict__ out,
                                                                     float* __restrict__ lse_out) {
-  __shared__ float wsh[kThreads / kWave][1024];
+  constexpr int NW = kThreads / kWave;
+  __shared__ float wsh[NW][1024];
+  __shared__ float red[NW - 1][kWave * 8];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t r = (int64_t)blockIdx.x * (kThreads / kWave) + wave;
-  if (r >= R) return;                    // whole wave; no workgroup barrier below
+  const int64_t r = blockIdx.x;
   float* w = wsh[wave];
   float mx = -INFINITY;
   for (int p = lane; p < P; p += kWave) mx = fmaxf(mx, lse_parts[(int64_t)p * R + r]);
@@ -563,57 +566,55 @@ __global__ __launch_bounds__(kThreads) void merge_bf16_parts_kernel(const uint16
   tot = wave_sum(tot);
   __builtin_amdgcn_s_waitcnt(0xc07f);    // lgkmcnt(0): this wave's LDS writes are done
   __builtin_amdgcn_wave_barrier();
-  const float inv = tot > 0.f ? 1.f / tot : 0.f;
   const int nd8 = D / 8;
-  float acc[NV][8];
+  const bool on = lane < nd8;
+  float acc[8];
 #pragma unroll
-  for (int i = 0; i < NV; ++i)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
-  const uint4* base = reinterpret_cast<const uint4*>(o_parts + r * D);
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  const uint4* base = reinterpret_cast<const uint4*>(o_parts + r * D) + lane;
   const int64_t pstride = R * D / 8;     // uint4 stride between parts
-  auto fma8 = [&](float wu, const uint4& v, float* a8) {
-    const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+  for (int p0 = wave; p0 < P; p0 += NW * kMergePPT) {
+    uint4 v[kMergePPT];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      a8[2 * e] = fmaf(wu, __uint_as_float(x[e] << 16), a8[2 * e]);
-      a8[2 * e + 1] = fmaf(wu, __uint_as_float(x[e] & 0xffff0000u), a8[2 * e + 1]);
+    for (int u = 0; u < kMergePPT; ++u) {
+      const int p = p0 + u * NW;
+      v[u] = (on && p < P) ? base[(int64_t)p * pstride] : make_uint4(0, 0, 0, 0);
     }
-  };
-  int p = 0;
-  for (; p + 4 <= P; p += 4) {
-    uint4 v[4][NV];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < kMergePPT; ++u) {
+      const int p = p0 + u * NW;
+      if (p < P) {
+        const float wu = w[p];
+        const uint32_t x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const int d8 = lane + i * kWave;
-        v[u][i] = d8 < nd8 ? base[(int64_t)(p + u) * pstride + d8] : make_uint4(0, 0, 0, 0);
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] = fmaf(wu, __uint_as_float(x[e] << 16), acc[2 * e]);
+          acc[2 * e + 1] = fmaf(wu, __uint_as_float(x[e] & 0xffff0000u), acc[2 * e + 1]);
+        }
       }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int i = 0; i < NV; ++i) fma8(w[p + u], v[u][i], acc[i]);
-  }
-  for (; p < P; ++p) {
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int d8 = lane + i * kWave;
-      if (d8 < nd8) fma8(w[p], base[(int64_t)p * pstride + d8], acc[i]);
     }
   }
+  if (wave > 0) {
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int d8 = lane + i * kWave;
-    if (d8 >= nd8) continue;
-    uint4 o;
-    o.x = pack_bf16x2(acc[i][0] * inv, acc[i][1] * inv);
-    o.y = pack_bf16x2(acc[i][2] * inv, acc[i][3] * inv);
-    o.z = pack_bf16x2(acc[i][4] * inv, acc[i][5] * inv);
-    o.w = pack_bf16x2(acc[i][6] * inv, acc[i][7] * inv);
-    reinterpret_cast<uint4*>(out + r * D)[d8] = o;
+    for (int e = 0; e < 8; ++e) red[wave - 1][lane * 8 + e] = acc[e];
   }
-  if (lane == 0 && lse_out) lse_out[r] = (tot > 0.f) ? mx + logf(tot) : -INFINITY;
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int q = 0; q < NW - 1; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += red[q][lane * 8 + e];
+    const float inv = tot > 0.f ? 1.f / tot : 0.f;
+    if (on) {
+      uint4 o;
+      o.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+      o.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+      o.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+      o.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
+      reinterpret_cast<uint4*>(out + r * D)[lane] = o;
+    }
+    if (lane == 0 && lse_out) lse_out[r] = (tot > 0.f) ? mx + logf(tot) : -INFINITY;
+  }
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -669,13 +670,8 @@ hipError_t launch_attend(const AttendArgs& a, const AttendPlan& p, void* ws, hip
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  {
-    const int rows_per_wg = kThreads / kWave;
-    dim3 mgrid((unsigned)((R + rows_per_wg - 1) / rows_per_wg));
-    uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
-    hipLaunchKernelGGL(merge_bf16_parts_kernel<1>, mgrid, dim3(kThreads), 0, st, o_part, lse_part, p.splits, R, a.D,
-                       out, a.lse);   // D <= 512: one 8-dim load per lane and part
-  }
+  hipLaunchKernelGGL(merge_bf16_parts_kernel, dim3((unsigned)R), dim3(kThreads), 0, st, o_part, lse_part, p.splits, R,
+                     a.D, reinterpret_cast<uint16_t*>(a.out), a.lse);   // D <= 512: 8 dims per lane
   return hipGetLastError();
 }
 

@@ -60,45 +60,63 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
   const int64_t blk0 = (int64_t)(blockIdx.x / cs) * bpw;   // cs workgroups share a block group,
   const int slice = blockIdx.x % cs;                         // each on lpr of its channel vectors
 
-  // ---- softmax weights of each block handled here, one wave per block
-  for (int bi = wave; bi < bpw; bi += kThreads / kWave) {
+  // ---- this thread's first rows (up to 4) are loaded before the weights are computed,
+  // so that the two memory round trips overlap
+  const int rs_total = kThreads / lpr;
+  const int slot = tid / lpr, cv = tid % lpr + slice * lpr;
+  const int bi = slot / spb, r0 = slot % spb;
+  const bool active = slot < rs_total && bi < bpw && blk0 + bi < total_blocks;
+  const TX* xb = nullptr;
+  float xf[4][V];
+  if (active) {
     int64_t blk = blk0 + bi;
+    int64_t b = blk / nb_per_b, i = blk % nb_per_b;
+    xb = x + ((b * x_bs + i * m) * (int64_t)C) + (int64_t)cv * V;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (r0 + u * spb < m) XVec<TX>::load(xb + (int64_t)(r0 + u * spb) * C, xf[u]);
+  }
+
+  // ---- softmax weights of each block handled here, one wave per block
+  for (int wi = wave; wi < bpw; wi += kThreads / kWave) {
+    int64_t blk = blk0 + wi;
     if (blk >= total_blocks) break;
     int64_t b = blk / nb_per_b, i = blk % nb_per_b;
     const float* g = gate + b * T + i * m;
     float mx = -INFINITY;
     for (int j = lane; j < m; j += kWave) {
       float z = g[j] + bias[j];
-      wts[bi * m + j] = z;
+      wts[wi * m + j] = z;
       mx = fmaxf(mx, z);
     }
     mx = wave_max(mx);
     float sum = 0.f;
     for (int j = lane; j < m; j += kWave) {
-      float e = expf(wts[bi * m + j] - mx);
-      wts[bi * m + j] = e;
+      float e = expf(wts[wi * m + j] - mx);
+      wts[wi * m + j] = e;
       sum += e;
     }
     sum = wave_sum(sum);
     float inv = 1.0f / sum;
-    for (int j = lane; j < m; j += kWave) wts[bi * m + j] *= inv;
+    for (int j = lane; j < m; j += kWave) wts[wi * m + j] *= inv;
   }
   __syncthreads();
 
   // ---- weighted row sums: thread = (row slot, channel vector)
-  const int rs_total = kThreads / lpr;
-  const int slot = tid / lpr, cv = tid % lpr + slice * lpr;
-  const int bi = slot / spb, r0 = slot % spb;
-  const bool active = slot < rs_total && bi < bpw && blk0 + bi < total_blocks;
   float acc[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) acc[v] = 0.f;
   if (active) {
-    int64_t blk = blk0 + bi;
-    int64_t b = blk / nb_per_b, i = blk % nb_per_b;
-    const TX* xb = x + ((b * x_bs + i * m) * (int64_t)C) + (int64_t)cv * V;
     const float* wb = wts + bi * m;
-    int j = r0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (r0 + u * spb < m) {
+        const float w = wb[r0 + u * spb];
+#pragma unroll
+        for (int v = 0; v < V; ++v) acc[v] = fmaf(w, xf[u][v], acc[v]);
+      }
+    }
+    int j = r0 + 4 * spb;
     for (; j + 3 * spb < m; j += 4 * spb) {
       float xv[4][V];
 #pragma unroll

@@ -27,7 +27,14 @@ namespace dsv4 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kKeysPerIter = 256;   // 4 waves x 4 tiles x 16 keys
+// 16-key tiles per wave and step: enough loads in flight per lane (the next step's tiles
+// are loaded while this step's are used) within a register budget of about 80 VGPRs.
+template <int KIND, int DI>
+constexpr int tiles_per_step() {
+  return KIND == KEY_BF16 ? (DI >= 256 ? 2 : 4) : (KIND == KEY_FP8 && DI >= 256 ? 4 : 8);
+}
+template <int KIND, int DI>
+constexpr int keys_per_step() { return tiles_per_step<KIND, DI>() * 16 * 4; }   // 4 waves
 
 __device__ __forceinline__ uint32_t vis_blocks(const int32_t* q_pos, int64_t row, int m, int64_t N) {
   int64_t p = q_pos[row];
@@ -203,33 +210,35 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
     sbase = ksc + b * k_bs * (DI / 32);
   }
 
-  // Each wave takes 64 consecutive keys (4 tiles) per step; the next step's tiles are
+  // Each wave takes TPW consecutive 16-key tiles per step; the next step's tiles are
   // loaded before this step's are used.  Key indices past the range are clamped to its
   // last key, so loads never branch; only the score write is guarded.
+  constexpr int TPW = tiles_per_step<KIND, DI>();
+  constexpr int KPS = keys_per_step<KIND, DI>();
   const int64_t c0 = (int64_t)blockIdx.x * chunk;
   int64_t c1 = c0 + chunk;
   if (c1 > N) c1 = N;
   const int64_t klast = c1 - 1;
-  KeyTile<KIND, DI> cur[4], nxt[4];
-  int64_t base = c0 + wave * 64;
+  KeyTile<KIND, DI> cur[TPW], nxt[TPW];
+  int64_t base = c0 + wave * (TPW * 16);
   if (base < c1) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < TPW; ++u) {
       const int64_t key = base + u * 16 + col;
       cur[u].load(kbase, sbase, key < klast ? key : klast, g, true);
     }
   }
-  for (; base < c1; base += kKeysPerIter) {
-    const int64_t nb = base + kKeysPerIter;
+  for (; base < c1; base += KPS) {
+    const int64_t nb = base + KPS;
     if (nb < c1) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < TPW; ++u) {
         const int64_t key = nb + u * 16 + col;
         nxt[u].load(kbase, sbase, key < klast ? key : klast, g, true);
       }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < TPW; ++u) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < KS; ++c) {
@@ -246,7 +255,7 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
       if (owner && key < c1) emit_score(scores, hist_l + qs_c * kHistBins, row_c, sstride, N, key, nvis, v);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) cur[u] = nxt[u];
+    for (int u = 0; u < TPW; ++u) cur[u] = nxt[u];
   }
   __syncthreads();
   for (int s = 0; s < nq; ++s) flush_hist(hist_l + s * kHistBins, hist_g, b * Q + qt * QPT + s);
@@ -565,6 +574,9 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
 
 template <int KIND, int DI>
 hipError_t launch_mfma_di(const IndexArgs& a, float* scores, uint32_t* hist, int64_t chunk, hipStream_t st) {
+  constexpr int KPS = keys_per_step<KIND, DI>();
+  chunk = ((chunk + KPS - 1) / KPS) * KPS;
+  if (chunk < KPS) chunk = KPS;
   int QPT = 16 / a.HI;
   int64_t QT = (a.Q + QPT - 1) / QPT;
   dim3 grid((unsigned)((a.N + chunk - 1) / chunk), (unsigned)(a.B * QT));
@@ -638,12 +650,12 @@ hipError_t launch_index_topk(const IndexArgs& a, const TopkWorkspace& ws, hipStr
                          ws.scores, ((a.N + 63) / 64) * 64, ws.hist);
       e = hipGetLastError();
     } else {
-      // about two workgroups per CU over the whole call, each a multiple of 256 keys
+      // about two workgroups per CU over the whole call
       int QPT = 16 / a.HI;
       int64_t rows = a.B * ((a.Q + QPT - 1) / QPT);
       int64_t per = (a.N * rows + 511) / 512;
-      int64_t chunk = ((per + kKeysPerIter - 1) / kKeysPerIter) * kKeysPerIter;
-      if (chunk < kKeysPerIter) chunk = kKeysPerIter;
+      // (rounded to whole steps of the kernel inside launch_mfma_di)
+      int64_t chunk = per;
       if (a.kind == KEY_BF16) e = launch_mfma<KEY_BF16>(a, ws.scores, ws.hist, chunk, st);
       else if (a.kind == KEY_FP8) e = launch_mfma<KEY_FP8>(a, ws.scores, ws.hist, chunk, st);
       else e = launch_mfma<KEY_MXFP4>(a, ws.scores, ws.hist, chunk, st);
