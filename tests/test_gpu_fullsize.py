@@ -209,3 +209,117 @@ def test_csa_decode_64k_bf16_all_rows():
                                    win_pos0, W, pos, scale)
     assert row_rel_err(host_bf16(o), o_r) <= 1e-2
     assert lse_abs_err(lse.cpu().numpy(), lse_r) <= 1e-2
+
+
+# ----------------------------------------------------------------------------------- c5
+def _fp8_valid_rounding(codes, exact):
+    """Each fp8 code is the nearest-even rounding of `exact` or one of its two neighbours
+    (the library pools in fp32, the oracle in fp64)."""
+    dec = codecs.decode_e4m3(codes)
+    a = np.abs(exact)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    ulp = np.ldexp(1.0, (e - 3).astype(np.int64))
+    return np.all(np.abs(dec - np.clip(exact, -448, 448)) <= ulp * 1.0001)
+
+
+def test_prefill_chunk_csa_and_hca_layers_sampled_queries():
+    """A 4096-token chunk against a 256K-token cache: compress the chunk (4x / 128x, fp8
+    indexer keys), fp8 indexer + top-512 for 4096 queries, CSA and HCA attention with a
+    4224-row window buffer.  Sampled query rows are checked against the oracle; the new
+    compressed entries both sides read are the oracle's (the library's compression of the
+    same chunk is checked separately)."""
+    T, H, D, HI, DI, k, W, m = 4096, 64, 512, 8, 128, 512, 128, 4
+    P0 = 262144                                   # cached raw tokens
+    N0c, N0h = P0 // 4, P0 // 128                 # cached CSA / HCA entries
+    Lw = 128 + T                                  # window buffer: positions [P0-128, P0+T)
+    wpos0 = np.array([P0 - 128], np.int32)
+    qpos = (P0 + np.arange(T, dtype=np.int32))[None]
+    sampled = np.array([0, 1, 2, 3, 127, 128, 2047, 4094, 4095])
+    scale = 1.0 / math.sqrt(D)
+    dec = codecs.decode_bf16
+    cfg = 5
+    # ---------------- inputs shared by the two layers' windows
+    gate = synth.normal(cfg, synth.GATE, (1, T))
+    bias4 = synth.normal(cfg, synth.BIAS, (m,), std=0.1)
+    bias128 = synth.normal(cfg + 10, synth.BIAS, (128,), std=0.1)
+
+    # ================ CSA layer
+    rk = synth.bf16_bits(synth.normal(cfg, synth.RAW_K, (1, T, D)))
+    rv = synth.bf16_bits(synth.normal(cfg, synth.RAW_V, (1, T, D)))
+    rki = synth.bf16_bits(synth.normal(cfg, synth.RAW_KI, (1, T, DI)))
+    new_k = method.compress(dec(rk), gate, bias4, m)[0]           # [1024, D] fp64
+    new_v = method.compress(dec(rv), gate, bias4, m)[0]
+    new_ki = method.compress(dec(rki), gate, bias4, m)[0]
+    # the library's compression of the same chunk
+    g_d, b_d = dev(gate), dev(bias4)
+    ck = L.csa_compress(dev(rk.view(np.int16)).view(torch.bfloat16), g_d, b_d, m, torch.bfloat16)
+    cki = L.csa_compress(dev(rki.view(np.int16)).view(torch.bfloat16), g_d, b_d, m, torch.float8_e4m3fn)
+    torch.cuda.synchronize()
+    amax = np.abs(dec(rk)).reshape(T // m, m * D).max(axis=1)[:, None]
+    ulp = np.ldexp(1.0, (np.floor(np.log2(np.maximum(np.abs(new_k), 2.0 ** -126))) - 7).astype(np.int64))
+    assert np.all(np.abs(host_bf16(ck)[0] - new_k) <= ulp + m * 2.0 ** -21 * amax)
+    assert _fp8_valid_rounding(cki.view(torch.uint8).cpu().numpy()[0], new_ki)
+    # caches: cached part drawn, new part = the oracle's entries
+    kc = torch.empty((1, N0c + T // m, D), dtype=torch.bfloat16, device="cuda")
+    vc = torch.empty_like(kc)
+    kc[0, :N0c] = synth.device_normal((N0c, D), 5101, torch.bfloat16)
+    vc[0, :N0c] = synth.device_normal((N0c, D), 5102, torch.bfloat16)
+    nk_bits, nv_bits = codecs.encode_bf16(new_k), codecs.encode_bf16(new_v)
+    kc[0, N0c:] = dev(nk_bits.view(np.int16)).view(torch.bfloat16)
+    vc[0, N0c:] = dev(nv_bits.view(np.int16)).view(torch.bfloat16)
+    ki_codes = np.concatenate([codecs.encode_e4m3(synth.normal(cfg, synth.KI, (N0c, DI))), codecs.encode_e4m3(new_ki)])
+    ki = dev(ki_codes[None]).view(torch.float8_e4m3fn)
+    qi_codes = codecs.encode_e4m3(synth.normal(cfg, synth.QI, (1, T, HI, DI)))
+    qi = dev(qi_codes).view(torch.float8_e4m3fn)
+    wi = synth.uniform(cfg, synth.WI, (1, T, HI))
+    idx = L.csa_index_topk(qi, dev(wi), ki, dev(qpos), m, k)
+    torch.cuda.synchronize()
+    idx_g = idx.cpu().numpy()
+    s = method.index_scores(codecs.decode_e4m3(qi_codes[:, sampled]), wi[:, sampled],
+                            codecs.decode_e4m3(ki_codes)[None], qpos[:, sampled], m)
+    idx_r = method.topk(s, qpos[:, sampled], m, k)
+    n_vis = method.visible_blocks(qpos[:, sampled], m, N0c + T // m)
+    for j, qq in enumerate(sampled):
+        assert check_topk(idx_g[0, qq], s[0, j], int(n_vis[0, j]), k) <= 2
+    # window buffer: 128 cached raw rows then the chunk's raw rows
+    kw_bits = np.concatenate([synth.bf16_bits(synth.normal(cfg, synth.KW, (1, 128, D))), rk], axis=1)
+    vw_bits = np.concatenate([synth.bf16_bits(synth.normal(cfg, synth.VW, (1, 128, D))), rv], axis=1)
+    q = synth.device_normal((1, T, H, D), 5103, torch.bfloat16)
+    idx_in = idx.clone()
+    idx_in[0, torch.from_numpy(sampled).cuda()] = torch.from_numpy(idx_r[0]).cuda()
+    o, lse = L.csa_attend(q, kc, vc, idx_in, dev(kw_bits.view(np.int16)).view(torch.bfloat16),
+                          dev(vw_bits.view(np.int16)).view(torch.bfloat16), dev(wpos0), W, dev(qpos), scale)
+    torch.cuda.synchronize()
+    kc_h = np.concatenate([host_bf16(kc[0, :N0c]), dec(nk_bits)])[None]
+    vc_h = np.concatenate([host_bf16(vc[0, :N0c]), dec(nv_bits)])[None]
+    o_r, lse_r = method.csa_attend(host_bf16(q[:, torch.from_numpy(sampled).cuda()]), kc_h, vc_h, idx_r,
+                                   dec(kw_bits), dec(vw_bits), wpos0, W, qpos[:, sampled], scale)
+    assert row_rel_err(host_bf16(o[:, torch.from_numpy(sampled).cuda()]), o_r) <= 1e-2
+    assert lse_abs_err(lse[:, torch.from_numpy(sampled).cuda()].cpu().numpy(), lse_r) <= 1e-2
+    del kc, vc, ki, qi, q, o
+
+    # ================ HCA layer
+    cfg = 6
+    rk = synth.bf16_bits(synth.normal(cfg, synth.RAW_K, (1, T, D)))
+    rv = synth.bf16_bits(synth.normal(cfg, synth.RAW_V, (1, T, D)))
+    hn_k = method.compress(dec(rk), gate, bias128, 128)[0]        # [32, D]
+    hn_v = method.compress(dec(rv), gate, bias128, 128)[0]
+    hck = L.csa_compress(dev(rk.view(np.int16)).view(torch.bfloat16), g_d, dev(bias128), 128, torch.bfloat16)
+    torch.cuda.synchronize()
+    amax = np.abs(dec(rk)).reshape(T // 128, 128 * D).max(axis=1)[:, None]
+    ulp = np.ldexp(1.0, (np.floor(np.log2(np.maximum(np.abs(hn_k), 2.0 ** -126))) - 7).astype(np.int64))
+    assert np.all(np.abs(host_bf16(hck)[0] - hn_k) <= ulp + 128 * 2.0 ** -21 * amax)
+    hkc_bits = np.concatenate([synth.bf16_bits(synth.normal(cfg, synth.KC, (N0h, D))), codecs.encode_bf16(hn_k)])[None]
+    hvc_bits = np.concatenate([synth.bf16_bits(synth.normal(cfg, synth.VC, (N0h, D))), codecs.encode_bf16(hn_v)])[None]
+    kw_bits = np.concatenate([synth.bf16_bits(synth.normal(cfg, synth.KW, (1, 128, D))), rk], axis=1)
+    vw_bits = np.concatenate([synth.bf16_bits(synth.normal(cfg, synth.VW, (1, 128, D))), rv], axis=1)
+    q = synth.device_normal((1, T, H, D), 6103, torch.bfloat16)
+    b16 = lambda x: dev(x.view(np.int16)).view(torch.bfloat16)
+    o, lse = L.hca_attend(q, b16(hkc_bits), b16(hvc_bits), 128, b16(kw_bits), b16(vw_bits), dev(wpos0), W, dev(qpos),
+                          scale)
+    torch.cuda.synchronize()
+    sel = torch.from_numpy(sampled).cuda()
+    o_r, lse_r = method.hca_attend(host_bf16(q[:, sel]), dec(hkc_bits), dec(hvc_bits), 128, dec(kw_bits),
+                                   dec(vw_bits), wpos0, W, qpos[:, sampled], scale)
+    assert row_rel_err(host_bf16(o[:, sel]), o_r) <= 1e-2
+    assert lse_abs_err(lse[:, sel].cpu().numpy(), lse_r) <= 1e-2
