@@ -26,6 +26,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 B, CTX, H, D = 8, 1 << 20, 64, 512
 M_CSA, M_HCA = 4, 128
 N_CSA, N_HCA = CTX // M_CSA, CTX // M_HCA
@@ -283,6 +285,119 @@ def source_sha(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
+# ------------------------------------------------------------------------------------ prefill
+PF_T, PF_P0, PF_K = 4096, 262144, 512           # chunk tokens, cached raw tokens, top-k
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
+
+
+def prefill_flops():
+    """Algorithmic flops of one CSA layer's indexer (fp8) and attention (bf16), and of one
+    HCA layer's attention (bf16), for a 4096-token chunk against a 256K-token cache:
+    2*HI*DI per (query, visible block) and 4*H*D per (query, key in the attended set)."""
+    pos = PF_P0 + np.arange(PF_T, dtype=np.int64)
+    n_csa = np.minimum(PF_P0 // 4 + PF_T // 4, (pos + 1) // 4)
+    n_hca = np.minimum(PF_P0 // 128 + PF_T // 128, (pos + 1) // 128)
+    idx = 2.0 * HI * DI * float(n_csa.sum())
+    csa = 4.0 * H * D * PF_T * (PF_K + W)
+    hca = 4.0 * H * D * float((n_hca + W).sum())
+    return idx, csa, hca
+
+
+def run_prefill(L, torch, synth, steps, warmup):
+    """Chunked prefill: a 4-layer stack (CSA, HCA, CSA, HCA, independent seeds) over one
+    4096-token chunk against a 256K-token cache; each layer compresses the chunk into its
+    caches and attends (CSA: fp8 indexer + top-512 + window; HCA: dense + window)."""
+    lib = L.lib()
+    bf, f8 = torch.bfloat16, torch.float8_e4m3fn
+    T, P0 = PF_T, PF_P0
+    Lw = W + T
+    qpos = (P0 + torch.arange(T, dtype=torch.int32, device="cuda")).reshape(1, T)
+    wpos0 = torch.tensor([P0 - W], dtype=torch.int32, device="cuda")
+    scale = 1.0 / math.sqrt(D)
+    layers = []
+    for li, kind in enumerate(("csa", "hca", "csa", "hca")):
+        sd = lambda tid: seed(5 if kind == "csa" else 6, tid, li)
+        t = {"kind": kind}
+        m = M_CSA if kind == "csa" else M_HCA
+        n0 = P0 // m
+        n = n0 + T // m
+        t["kc"] = synth.device_normal((1, n, D), sd(synth.KC), bf)
+        t["vc"] = synth.device_normal((1, n, D), sd(synth.VC), bf)
+        t["kw"] = synth.device_normal((1, Lw, D), sd(synth.KW), bf)       # window: 128 cached + chunk
+        t["vw"] = synth.device_normal((1, Lw, D), sd(synth.VW), bf)
+        t["gate"] = synth.device_normal((1, T), sd(synth.GATE), torch.float32)
+        t["bias"] = synth.device_normal((m,), sd(synth.BIAS), torch.float32, std=0.1)
+        t["q"] = synth.device_normal((1, T, H, D), sd(synth.Q), bf)
+        t["o"] = torch.empty_like(t["q"])
+        t["lse"] = torch.empty((1, T, H), dtype=torch.float32, device="cuda")
+        t["n0"], t["m"] = n0, m
+        if kind == "csa":
+            t["ki"] = synth.device_normal((1, n, DI), sd(synth.KI), f8)
+            t["kiw"] = synth.device_normal((1, T, DI), sd(synth.RAW_KI), bf)
+            t["qi"] = synth.device_normal((1, T, HI, DI), sd(synth.QI), f8)
+            t["wi"] = synth.device_uniform((1, T, HI), sd(synth.WI))
+            t["idx"] = torch.empty((1, T, PF_K), dtype=torch.int32, device="cuda")
+        layers.append(t)
+    torch.cuda.synchronize()
+    ws = {}
+
+    def layer(t, arm=None):
+        m, n0 = t["m"], t["n0"]
+        kwc, vwc = t["kw"][:, W:], t["vw"][:, W:]                      # the chunk's raw rows
+        L.csa_compress(kwc, t["gate"], t["bias"], m, bf, out=t["kc"][:, n0:])
+        L.csa_compress(vwc, t["gate"], t["bias"], m, bf, out=t["vc"][:, n0:])
+        if t["kind"] == "csa":
+            L.csa_compress(t["kiw"], t["gate"], t["bias"], m, f8, out=t["ki"][:, n0:])
+            if arm:
+                lib.dsv4_time_next_kernel(*arm[0])
+            L.csa_index_topk(t["qi"], t["wi"], t["ki"], qpos, m, PF_K, out_idx=t["idx"],
+                             workspace=ws.setdefault("idx", None))
+            if arm:
+                lib.dsv4_time_next_kernel(*arm[1])
+            L.csa_attend(t["q"], t["kc"], t["vc"], t["idx"], t["kw"], t["vw"], wpos0, W, qpos, scale,
+                         out=t["o"], lse=t["lse"])
+        else:
+            if arm:
+                lib.dsv4_time_next_kernel(*arm[2])
+            L.hca_attend(t["q"], t["kc"], t["vc"], m, t["kw"], t["vw"], wpos0, W, qpos, scale, out=t["o"],
+                         lse=t["lse"])
+
+    ev = HipEvents()
+    for _ in range(warmup):
+        for t in layers:
+            layer(t)
+    torch.cuda.synchronize()
+    pairs = [[(ev.create(), ev.create()) for _ in range(3)] for _ in range(steps * 4)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        for j, t in enumerate(layers):
+            layer(t, pairs[4 * i + j])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    f_idx, f_csa, f_hca = prefill_flops()
+    k_idx = sum(ev.elapsed_ms(*pairs[4 * i + j][0]) for i in range(steps) for j in (0, 2)) / (2 * steps)
+    k_csa = sum(ev.elapsed_ms(*pairs[4 * i + j][1]) for i in range(steps) for j in (0, 2)) / (2 * steps)
+    k_hca = sum(ev.elapsed_ms(*pairs[4 * i + j][2]) for i in range(steps) for j in (1, 3)) / (2 * steps)
+    ideal_ms = 2 * (f_idx / PEAK_TFLOPS["fp8"] + f_csa / PEAK_TFLOPS["bf16"] + f_hca / PEAK_TFLOPS["bf16"]) / 1e9
+    kern = lambda f, kms, pk: {"avg_launch_ms": round(kms, 4), "tflops": round(f / kms / 1e9, 1),
+                               "frac_of_peak": round(f / kms / 1e9 / PEAK_TFLOPS[pk], 4), "flops": f}
+    return {
+        "metric": "chunked prefill MFMA utilisation (4-layer CSA/HCA stack, 4096-token chunk, 256K cache)",
+        "value": round(ideal_ms / ms, 4), "unit": "fraction of dense MFMA peak", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16+fp8", "data": "synthetic (seeded N(0,1) / U(0,1))",
+        "config": {"workload": "chunked prefill: CSA, HCA, CSA, HCA layers; 4096 queries at positions "
+                               "262144..266239; 64 heads x 512; fp8 indexer 8 x 128, top-512; window 128",
+                   "chunk": T, "cache_tokens": P0},
+        "ideal_ms_at_peak": round(ideal_ms, 4),
+        "kernels": {"index_mfma_kernel (fp8)": kern(f_idx, k_idx, "fp8"),
+                    "attend_bf16_kernel (CSA)": kern(f_csa, k_csa, "bf16"),
+                    "attend_bf16_kernel (HCA)": kern(f_hca, k_hca, "bf16")},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -291,6 +406,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill", action="store_true",
+                    help="measure the chunked-prefill stack instead of decode (prints its own line)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device copy of this size after warm-up (reference for traffic counters)")
     args = ap.parse_args()
@@ -307,6 +424,9 @@ def main():
 
     lib = L.lib()
     torch.cuda.set_device(0)
+    if args.prefill:
+        print(json.dumps(run_prefill(L, torch, synth, max(1, args.steps // 10), max(1, args.warmup // 5))), flush=True)
+        return
     wl = Workload(L, torch, synth, args.replicas)
     steps = [marshal_step(L, torch, wl, r) for r in range(args.replicas)]
     timed = steps[0][1]
