@@ -48,19 +48,28 @@ __global__ void clear_kernel(uint32_t* p, int64_t n) {
   for (; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0u;
 }
 
+// LDS histograms hold two 16-bit bin counters per word (a workgroup counts fewer than
+// 2^16 keys per query: kMaxIndexChunk); the flush adds them to the 32-bit row histogram.
+constexpr int kHistWords = kHistBins / 2;
+constexpr int64_t kMaxIndexChunk = 32768;
+
 // Writes one score and counts it in the LDS histogram of its query slot.
 __device__ __forceinline__ void emit_score(float* scores, uint32_t* hist_l, int64_t row, int64_t sstride,
                                            int64_t N, int64_t key, uint32_t nvis, float v) {
   if (key >= N) return;
   bool vis = key < (int64_t)nvis;
   scores[row * sstride + key] = vis ? v : -INFINITY;
-  if (vis) atomicAdd(&hist_l[score_key(v) >> (32 - kHistBits)], 1u);
+  if (vis) {
+    const uint32_t bin = score_key(v) >> (32 - kHistBits);
+    atomicAdd(&hist_l[bin >> 1], 1u << ((bin & 1u) << 4));
+  }
 }
 
 __device__ __forceinline__ void flush_hist(const uint32_t* hist_l, uint32_t* hist_g, int64_t row) {
-  for (int bin = threadIdx.x; bin < kHistBins; bin += kThreads) {
-    uint32_t c = hist_l[bin];
-    if (c) atomicAdd(&hist_g[row * kHistBins + bin], c);
+  for (int w = threadIdx.x; w < kHistWords; w += kThreads) {
+    const uint32_t c = hist_l[w];
+    if (c & 0xffffu) atomicAdd(&hist_g[row * kHistBins + 2 * w], c & 0xffffu);
+    if (c >> 16) atomicAdd(&hist_g[row * kHistBins + 2 * w + 1], c >> 16);
   }
 }
 
@@ -71,11 +80,11 @@ __global__ __launch_bounds__(kThreads) void index_f32_kernel(
     float* __restrict__ scores, int64_t sstride, uint32_t* __restrict__ hist_g) {
   extern __shared__ uint32_t sm[];
   uint32_t* hist_l = sm;
-  float* qs = reinterpret_cast<float*>(sm + kHistBins);
+  float* qs = reinterpret_cast<float*>(sm + kHistWords);
   float* ws = qs + HI * DI;
   const int64_t row = blockIdx.y;            // b * Q + q
   const int64_t b = row / Q;
-  for (int i = threadIdx.x; i < kHistBins; i += kThreads) hist_l[i] = 0u;
+  for (int i = threadIdx.x; i < kHistWords; i += kThreads) hist_l[i] = 0u;
   for (int i = threadIdx.x; i < HI * DI; i += kThreads) qs[i] = qi[row * HI * DI + i];
   for (int i = threadIdx.x; i < HI; i += kThreads) ws[i] = wi[row * HI + i];
   __syncthreads();
@@ -156,7 +165,9 @@ struct KeyTile<KEY_FP8, DI> {
   __device__ long op(int c) const { return __builtin_bit_cast(long, w[c]); }
 };
 
-template <int KIND, int DI, int HI>
+// QTW query tiles (QTW * 16/HI queries) per workgroup: every key tile loaded is used by
+// all of them (QTW > 1 when there are many queries, e.g. a prefill chunk).
+template <int KIND, int DI, int HI, int QTW>
 __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
     const uint8_t* __restrict__ qi, const float* __restrict__ wi, const uint8_t* __restrict__ ki,
     const uint8_t* __restrict__ ksc, const int32_t* __restrict__ q_pos, int64_t N, int64_t k_bs,
@@ -164,41 +175,54 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
   constexpr int QPT = 16 / HI;          // queries per 16-row MFMA tile
   constexpr int KS = DI / 32;
   constexpr int GPQ = HI / 4;           // lane groups per query slot
-  extern __shared__ uint32_t hist_l[];  // [QPT][kHistBins]
+  extern __shared__ uint32_t hist_l[];  // [QTW * QPT][kHistWords]
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, col = lane & 15;
   const int64_t QT = (Q + QPT - 1) / QPT;
-  const int64_t b = blockIdx.y / QT, qt = blockIdx.y % QT;
-  const int nq = (int)((Q - qt * QPT) < QPT ? (Q - qt * QPT) : QPT);
-
-  for (int i = threadIdx.x; i < nq * kHistBins; i += kThreads) hist_l[i] = 0u;
-
-  // A operand: query rows (row = lane % 16 = qslot * HI + head)
-  const int r = col;
-  const int qs_a = r / HI, h_a = r % HI;
-  const bool qa_ok = qs_a < nq;
-  const int64_t qrow_a = (b * Q + qt * QPT + (qa_ok ? qs_a : 0)) * HI + h_a;
-  uint4 qa16[KS];   // bf16 queries
-  uint2 qa8[KS];    // fp8 queries
-  if constexpr (KIND == KEY_FP8) {
-    const uint2* p = reinterpret_cast<const uint2*>(qi + qrow_a * DI + g * (DI / 4));
+  const int64_t QG = (QT + QTW - 1) / QTW;
+  const int64_t b = blockIdx.y / QG, qt0 = (blockIdx.y % QG) * QTW;
+  int nq[QTW];
+  int nslots = 0;
 #pragma unroll
-    for (int c = 0; c < KS; ++c) qa8[c] = qa_ok ? p[c] : make_uint2(0, 0);
-  } else {
-    const uint4* p = reinterpret_cast<const uint4*>(qi + (qrow_a * DI + g * (DI / 4)) * 2);
-#pragma unroll
-    for (int c = 0; c < KS; ++c) qa16[c] = qa_ok ? p[c] : make_uint4(0, 0, 0, 0);
+  for (int t = 0; t < QTW; ++t) {
+    const int64_t left = Q - (qt0 + t) * QPT;
+    nq[t] = left <= 0 ? 0 : (left < QPT ? (int)left : QPT);
+    nslots += nq[t] > 0 ? QPT : 0;
   }
-  // epilogue weights: accumulator row 4g+i -> (slot (4g+i)/HI, head (4g+i)%HI)
+  for (int i = threadIdx.x; i < nslots * kHistWords; i += kThreads) hist_l[i] = 0u;
+
+  // A operands: query rows (row = lane % 16 = qslot * HI + head) of each query tile
+  const int qs_a = col / HI, h_a = col % HI;
+  uint4 qa16[QTW][KS];   // bf16 queries
+  uint2 qa8[QTW][KS];    // fp8 queries
+  // epilogue: accumulator row 4g+i -> (slot (4g+i)/HI, head (4g+i)%HI)
   const int qs_c = (4 * g) / HI;
-  const bool qc_ok = qs_c < nq;
-  const int64_t row_c = b * Q + qt * QPT + (qc_ok ? qs_c : 0);
-  float wv[4];
+  float wv[QTW][4];
+  uint32_t nvis[QTW];
+  int64_t row_c[QTW];
+  bool owner[QTW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) wv[i] = qc_ok ? wi[row_c * HI + ((4 * g + i) % HI)] : 0.f;
-  const uint32_t nvis = qc_ok ? vis_blocks(q_pos, row_c, m, N) : 0u;
-  const bool owner = qc_ok && (g % GPQ) == 0;
+  for (int t = 0; t < QTW; ++t) {
+    const int64_t qbase = b * Q + (qt0 + t) * QPT;
+    const bool qa_ok = qs_a < nq[t];
+    const int64_t qrow_a = (qa_ok ? qbase + qs_a : b * Q) * HI + h_a;
+    if constexpr (KIND == KEY_FP8) {
+      const uint2* p = reinterpret_cast<const uint2*>(qi + qrow_a * DI + g * (DI / 4));
+#pragma unroll
+      for (int c = 0; c < KS; ++c) qa8[t][c] = qa_ok ? p[c] : make_uint2(0, 0);
+    } else {
+      const uint4* p = reinterpret_cast<const uint4*>(qi + (qrow_a * DI + g * (DI / 4)) * 2);
+#pragma unroll
+      for (int c = 0; c < KS; ++c) qa16[t][c] = qa_ok ? p[c] : make_uint4(0, 0, 0, 0);
+    }
+    const bool qc_ok = qs_c < nq[t];
+    row_c[t] = qc_ok ? qbase + qs_c : b * Q;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[t][i] = qc_ok ? wi[row_c[t] * HI + ((4 * g + i) % HI)] : 0.f;
+    nvis[t] = qc_ok ? vis_blocks(q_pos, row_c[t], m, N) : 0u;
+    owner[t] = qc_ok && (g % GPQ) == 0;
+  }
   __syncthreads();
 
   const uint8_t* kbase;
@@ -213,8 +237,8 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
   // Each wave takes TPW consecutive 16-key tiles per step; the next step's tiles are
   // loaded before this step's are used.  Key indices past the range are clamped to its
   // last key, so loads never branch; only the score write is guarded.
-  constexpr int TPW = tiles_per_step<KIND, DI>();
-  constexpr int KPS = keys_per_step<KIND, DI>();
+  constexpr int TPW = QTW == 1 ? tiles_per_step<KIND, DI>() : (KIND == KEY_FP8 ? 4 : 2);
+  constexpr int KPS = TPW * 16 * 4;
   const int64_t c0 = (int64_t)blockIdx.x * chunk;
   int64_t c1 = c0 + chunk;
   if (c1 > N) c1 = N;
@@ -239,26 +263,33 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
     }
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < KS; ++c) {
-        if constexpr (KIND == KEY_FP8) acc = mfma_fp8(__builtin_bit_cast(long, qa8[c]), cur[u].op(c), acc);
-        else acc = mfma_bf16(bit_cast_to<bf16x8>(qa16[c]), cur[u].op(c), acc);
-      }
-      float v = wv[0] * fmaxf(acc[0], 0.f);
-      v = fmaf(wv[1], fmaxf(acc[1], 0.f), v);
-      v = fmaf(wv[2], fmaxf(acc[2], 0.f), v);
-      v = fmaf(wv[3], fmaxf(acc[3], 0.f), v);
-      if constexpr (GPQ >= 2) v += __shfl_xor(v, 16);
-      if constexpr (GPQ >= 4) v += __shfl_xor(v, 32);
       const int64_t key = base + u * 16 + col;
-      if (owner && key < c1) emit_score(scores, hist_l + qs_c * kHistBins, row_c, sstride, N, key, nvis, v);
+#pragma unroll
+      for (int t = 0; t < QTW; ++t) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < KS; ++c) {
+          if constexpr (KIND == KEY_FP8) acc = mfma_fp8(__builtin_bit_cast(long, qa8[t][c]), cur[u].op(c), acc);
+          else acc = mfma_bf16(bit_cast_to<bf16x8>(qa16[t][c]), cur[u].op(c), acc);
+        }
+        float v = wv[t][0] * fmaxf(acc[0], 0.f);
+        v = fmaf(wv[t][1], fmaxf(acc[1], 0.f), v);
+        v = fmaf(wv[t][2], fmaxf(acc[2], 0.f), v);
+        v = fmaf(wv[t][3], fmaxf(acc[3], 0.f), v);
+        if constexpr (GPQ >= 2) v += __shfl_xor(v, 16);
+        if constexpr (GPQ >= 4) v += __shfl_xor(v, 32);
+        if (owner[t] && key < c1)
+          emit_score(scores, hist_l + (t * QPT + qs_c) * kHistWords, row_c[t], sstride, N, key, nvis[t], v);
+      }
     }
 #pragma unroll
     for (int u = 0; u < TPW; ++u) cur[u] = nxt[u];
   }
   __syncthreads();
-  for (int s = 0; s < nq; ++s) flush_hist(hist_l + s * kHistBins, hist_g, b * Q + qt * QPT + s);
+#pragma unroll
+  for (int t = 0; t < QTW; ++t)
+    for (int s = 0; s < nq[t]; ++s)
+      flush_hist(hist_l + (t * QPT + s) * kHistWords, hist_g, b * Q + (qt0 + t) * QPT + s);
 }
 
 // ------------------------------------------------------------------ selection
@@ -399,6 +430,96 @@ __global__ __launch_bounds__(kScanThreads) void select_scan_kernel(
   if (tid == 0) ccount[row * nch + blockIdx.x] = misc[2];
 }
 
+// The last steps of a row's selection, shared by the two selection paths: radix select
+// (8-bit digits, below the histogram prefix) of the `need` largest composites among the c
+// candidates (cand_at(f) returns candidate f), their bits added to the key bitmap, and
+// compaction of the bitmap into ascending indices followed by -1 padding.  Every thread of
+// the NT-thread workgroup calls it.
+template <int NT, bool kLdsBits, typename CandAt>
+__device__ __forceinline__ void finish_row(uint32_t c, uint32_t need, uint32_t tbin, CandAt cand_at,
+                                           uint32_t* bits, int64_t wn, int k, int32_t* __restrict__ orow,
+                                           float* __restrict__ srow, const float* __restrict__ sc, uint32_t* tmp,
+                                           uint32_t* h256, uint32_t* misc) {
+  const int tid = threadIdx.x;
+#define DSV4_FOR_CAND(body)                          \
+  for (uint32_t f_ = tid; f_ < c; f_ += NT) {        \
+    const uint64_t comp = cand_at(f_);               \
+    body                                             \
+  }
+  uint64_t thr = 0;                                          // select composites >= thr
+  if (need < c) {
+    uint64_t prefix = (uint64_t)tbin << (64 - kHistBits);
+    int hi = 64 - kHistBits;                                 // bits [hi-1 : 0] still open
+    while (true) {
+      const int wd = hi < 8 ? hi : 8;
+      const int sh = hi - wd;
+      if (tid < 256) h256[tid] = 0u;
+      __syncthreads();
+      DSV4_FOR_CAND(if ((comp >> hi) == (prefix >> hi)) atomicAdd(&h256[(comp >> sh) & ((1u << wd) - 1u)], 1u);)
+      __syncthreads();
+      const uint32_t hc = (tid < (1 << wd)) ? h256[tid] : 0u;
+      uint32_t tot;
+      const uint32_t ex = block_scan<NT>(hc, tmp, &tot);
+      const uint32_t gt = tot - ex - hc;                     // candidates with a larger digit
+      if (tid < (1 << wd) && gt < need && need <= gt + hc) {
+        misc[4] = tid;
+        misc[5] = gt;
+        misc[6] = hc;
+      }
+      __syncthreads();
+      need -= misc[5];
+      prefix |= (uint64_t)misc[4] << sh;
+      const bool done = misc[6] == need || sh == 0;
+      hi = sh;
+      if (done) break;
+    }
+    thr = prefix;
+  }
+  DSV4_FOR_CAND(if (comp >= thr) {
+    const uint32_t j = ~(uint32_t)comp;
+    atomicOr(&bits[j >> 5], 1u << (j & 31));
+  })
+#undef DSV4_FOR_CAND
+  __threadfence_block();
+  __syncthreads();
+
+  // compaction: thread t takes 8 consecutive words (256 keys) per round
+  uint32_t base_off = 0;
+  for (int64_t r0 = 0; r0 < wn; r0 += 8 * NT) {
+    const int64_t w0 = r0 + (int64_t)tid * 8;
+    uint32_t wv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (kLdsBits) wv[i] = w0 + i < wn ? bits[w0 + i] : 0u;
+      else wv[i] = w0 + i < wn ? __hip_atomic_load(&bits[w0 + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+    }
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cnt += __popc(wv[i]);
+    uint32_t rtot;
+    uint32_t off = base_off + block_scan<NT>(cnt, tmp, &rtot);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t b_ = wv[i];
+      while (b_) {
+        const int bpos = __ffs(b_) - 1;
+        b_ &= b_ - 1;
+        const int64_t j = (w0 + i) * 32 + bpos;
+        if (off < (uint32_t)k) {
+          orow[off] = (int32_t)j;
+          if (srow) srow[off] = sc[j];
+        }
+        ++off;
+      }
+    }
+    base_off += rtot;
+  }
+  for (int64_t p = (int64_t)base_off + tid; p < k; p += NT) {
+    orow[p] = -1;
+    if (srow) srow[p] = -INFINITY;
+  }
+}
+
 // Selection, pass 2 (one workgroup per row): radix-selects (8-bit digits) the
 // kk - #(bin > b*) largest composites among the candidates, adds their bits to the
 // bitmap and compacts it into ascending indices, then -1 padding.
@@ -491,108 +612,47 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
     }
   }
   __syncthreads();
-#define DSV4_FOR_CAND(body)                                              \
-  for (uint32_t f_ = tid; f_ < c; f_ += NT) {                            \
-    const uint64_t comp = f_ < (uint32_t)kCandCap ? cand_l[f_] : cand_at(f_); \
-    body                                                                 \
-  }
-  uint32_t need = kk - cnt_above;
-  uint64_t thr = 0;                                          // select composites >= thr
-  if (need < c) {
-    uint64_t prefix = (uint64_t)tbin << (64 - kHistBits);
-    int hi = 64 - kHistBits;                                 // bits [hi-1 : 0] still open
-    while (true) {
-      const int wd = hi < 8 ? hi : 8;
-      const int sh = hi - wd;
-      if (tid < 256) h256[tid] = 0u;
-      __syncthreads();
-      DSV4_FOR_CAND(if ((comp >> hi) == (prefix >> hi)) atomicAdd(&h256[(comp >> sh) & ((1u << wd) - 1u)], 1u);)
-      __syncthreads();
-      const uint32_t hc = (tid < (1 << wd)) ? h256[tid] : 0u;
-      uint32_t tot;
-      const uint32_t ex = block_scan<NT>(hc, tmp, &tot);
-      const uint32_t gt = tot - ex - hc;                     // candidates with a larger digit
-      if (tid < (1 << wd) && gt < need && need <= gt + hc) {
-        misc[4] = tid;
-        misc[5] = gt;
-        misc[6] = hc;
-      }
-      __syncthreads();
-      need -= misc[5];
-      prefix |= (uint64_t)misc[4] << sh;
-      const bool done = misc[6] == need || sh == 0;
-      hi = sh;
-      if (done) break;
-    }
-    thr = prefix;
-  }
   uint32_t* bits = kLdsBits ? bits_l : gbits;
-  DSV4_FOR_CAND(if (comp >= thr) {
-    const uint32_t j = ~(uint32_t)comp;
-    atomicOr(&bits[j >> 5], 1u << (j & 31));
-  })
-#undef DSV4_FOR_CAND
-  __threadfence_block();
-  __syncthreads();
+  finish_row<NT, kLdsBits>(c, kk - cnt_above, tbin,
+                           [&](uint32_t f) -> uint64_t { return f < (uint32_t)kCandCap ? cand_l[f] : cand_at(f); },
+                           bits, wn, k, orow, srow, sc, tmp, h256, misc);
+}
 
-  // compaction: thread t takes 8 consecutive words (256 keys) per round
-  uint32_t base_off = 0;
-  for (int64_t r0 = 0; r0 < wn; r0 += 8 * NT) {
-    const int64_t w0 = r0 + (int64_t)tid * 8;
-    uint32_t wv[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if constexpr (kLdsBits) wv[i] = w0 + i < wn ? bits[w0 + i] : 0u;
-      else wv[i] = w0 + i < wn ? __hip_atomic_load(&bits[w0 + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
-    }
-    uint32_t cnt = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) cnt += __popc(wv[i]);
-    uint32_t rtot;
-    uint32_t off = base_off + block_scan<NT>(cnt, tmp, &rtot);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t b_ = wv[i];
-      while (b_) {
-        const int bpos = __ffs(b_) - 1;
-        b_ &= b_ - 1;
-        const int64_t j = (w0 + i) * 32 + bpos;
-        if (off < (uint32_t)k) {
-          orow[off] = (int32_t)j;
-          if (srow) srow[off] = sc[j];
-        }
-        ++off;
-      }
-    }
-    base_off += rtot;
+template <int KIND, int DI, int HI, int QTW>
+hipError_t launch_mfma_q(const IndexArgs& a, float* scores, uint32_t* hist, int64_t chunk, hipStream_t st) {
+  constexpr int QPT = 16 / HI;
+  constexpr int KPS = (QTW == 1 ? tiles_per_step<KIND, DI>() : (KIND == KEY_FP8 ? 4 : 2)) * 16 * 4;
+  const int64_t QT = (a.Q + QPT - 1) / QPT;
+  const int64_t QG = (QT + QTW - 1) / QTW;
+  if (QTW > 1) {                          // about 1024 workgroups over the whole call
+    int64_t chunks = 1024 / (a.B * QG);
+    if (chunks < 1) chunks = 1;
+    chunk = (a.N + chunks - 1) / chunks;
   }
-  for (int64_t p = (int64_t)base_off + tid; p < k; p += NT) {
-    orow[p] = -1;
-    if (srow) srow[p] = -INFINITY;
-  }
+  if (chunk > kMaxIndexChunk) chunk = kMaxIndexChunk;    // 16-bit LDS bin counters
+  chunk = ((chunk + KPS - 1) / KPS) * KPS;
+  if (chunk < KPS) chunk = KPS;
+  dim3 grid((unsigned)((a.N + chunk - 1) / chunk), (unsigned)(a.B * QG));
+  const int64_t slots = (int64_t)QTW * QPT < a.Q ? (int64_t)QTW * QPT : a.Q;
+  size_t smem = (size_t)slots * kHistWords * sizeof(uint32_t);
+  DSV4_LAUNCH_MAIN((index_mfma_kernel<KIND, DI, HI, QTW>), grid, dim3(kThreads), smem, st,
+                   reinterpret_cast<const uint8_t*>(a.qi), a.wi, reinterpret_cast<const uint8_t*>(a.ki), a.ki_scale,
+                   a.q_pos, a.N, a.k_bs, a.Q, a.m, chunk, scores, ((a.N + 63) / 64) * 64, hist);
+  return hipGetLastError();
 }
 
 template <int KIND, int DI>
 hipError_t launch_mfma_di(const IndexArgs& a, float* scores, uint32_t* hist, int64_t chunk, hipStream_t st) {
-  constexpr int KPS = keys_per_step<KIND, DI>();
-  chunk = ((chunk + KPS - 1) / KPS) * KPS;
-  if (chunk < KPS) chunk = KPS;
-  int QPT = 16 / a.HI;
-  int64_t QT = (a.Q + QPT - 1) / QPT;
-  dim3 grid((unsigned)((a.N + chunk - 1) / chunk), (unsigned)(a.B * QT));
-  size_t smem = (size_t)(a.Q < QPT ? a.Q : QPT) * kHistBins * sizeof(uint32_t);
-  const uint8_t* qi = reinterpret_cast<const uint8_t*>(a.qi);
-  const uint8_t* ki = reinterpret_cast<const uint8_t*>(a.ki);
-#define DSV4_IDX_LAUNCH(HIv)                                                                                  \
-  DSV4_LAUNCH_MAIN((index_mfma_kernel<KIND, DI, HIv>), grid, dim3(kThreads), smem, st, qi, a.wi, ki,        \
-                     a.ki_scale, a.q_pos, a.N, a.k_bs, a.Q, a.m, chunk, scores, ((a.N + 63) / 64) * 64, hist)
-  switch (a.HI) {
-    case 4: DSV4_IDX_LAUNCH(4); break;
-    case 8: DSV4_IDX_LAUNCH(8); break;
-    default: DSV4_IDX_LAUNCH(16); break;
+  // many queries (a prefill chunk): 4 query tiles (8 queries) per workgroup at the common
+  // indexer shape; otherwise one query tile
+  if constexpr (DI == 128) {
+    if (a.HI == 8 && a.B * a.Q >= 64) return launch_mfma_q<KIND, DI, 8, 4>(a, scores, hist, chunk, st);
   }
-#undef DSV4_IDX_LAUNCH
-  return hipGetLastError();
+  switch (a.HI) {
+    case 4: return launch_mfma_q<KIND, DI, 4, 1>(a, scores, hist, chunk, st);
+    case 8: return launch_mfma_q<KIND, DI, 8, 1>(a, scores, hist, chunk, st);
+    default: return launch_mfma_q<KIND, DI, 16, 1>(a, scores, hist, chunk, st);
+  }
 }
 
 template <int KIND>
@@ -644,7 +704,7 @@ hipError_t launch_index_topk(const IndexArgs& a, const TopkWorkspace& ws, hipStr
   if (a.N > 0) {
     if (a.kind == KEY_F32) {
       dim3 grid((unsigned)((a.N + kThreads - 1) / kThreads), (unsigned)R);
-      size_t smem = (kHistBins + (size_t)a.HI * a.DI + a.HI) * 4;
+      size_t smem = (kHistWords + (size_t)a.HI * a.DI + a.HI) * 4;
       DSV4_LAUNCH_MAIN(index_f32_kernel, grid, dim3(kThreads), smem, st, reinterpret_cast<const float*>(a.qi),
                          a.wi, reinterpret_cast<const float*>(a.ki), a.q_pos, a.N, a.k_bs, a.Q, a.HI, a.DI, a.m,
                          ws.scores, ((a.N + 63) / 64) * 64, ws.hist);

@@ -244,6 +244,41 @@ def test_index_topk_ties_and_zero_scores():
     check_topk(idx[0, 1], s_ref[0, 1], N, k)
 
 
+@pytest.mark.parametrize("kind", ["bf16", "fp8", "mxfp4"])
+def test_index_topk_many_queries(kind):
+    """Enough queries for the multi-query indexer path (several query tiles share each key
+    tile); a ragged last query group and per-query visibility."""
+    cfg = 260
+    B, Q, HI, DI, N, m, k = 2, 37, 8, 128, 3000, 4, 100
+    q32 = synth.normal(cfg, synth.QI, (B, Q, HI, DI))
+    w = synth.uniform(cfg, synth.WI, (B, Q, HI))
+    k32 = synth.normal(cfg, synth.KI, (B, N, DI))
+    pos = (np.arange(B * Q, dtype=np.int32).reshape(B, Q) * 311) % (4 * N + 50)
+    zero1 = dev(np.zeros(1, np.float32))
+    if kind == "bf16":
+        qd, qb = dev_bf16(q32)
+        kd, kb = dev_bf16(k32)
+        q64, k64 = codecs.decode_bf16(qb), codecs.decode_bf16(kb)
+        idx = L.csa_index_topk(qd, dev(w), kd, dev(pos), m, k)
+    elif kind == "fp8":
+        qc, kc = codecs.encode_e4m3(q32), codecs.encode_e4m3(k32)
+        q64, k64 = codecs.decode_e4m3(qc), codecs.decode_e4m3(kc)
+        idx = L.csa_index_topk(dev(qc).view(torch.float8_e4m3fn), dev(w), dev(kc).view(torch.float8_e4m3fn), dev(pos),
+                               m, k)
+    else:
+        qd, qb = dev_bf16(q32)
+        codes, scales = codecs.encode_mxfp4(k32)
+        q64, k64 = codecs.decode_bf16(qb), codecs.decode_mxfp4(codes, scales)
+        idx = L.csa_index_topk(qd, dev(w), dev(codes), dev(pos), m, k, ki_scale=dev(scales))
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    s_ref = _scores_oracle(q64, w, k64, pos, m)
+    nvis = method.visible_blocks(pos, m, N)
+    for b in range(B):
+        for q in range(Q):
+            assert check_topk(idx[b, q], s_ref[b, q], int(nvis[b, q]), k) <= 2
+
+
 @pytest.mark.parametrize("N", [10000, 300000])
 def test_index_topk_many_candidates(N):
     """All-zero scores put every key into the threshold bin: more candidates than the
