@@ -87,9 +87,11 @@ class Workload:
         self.replicas = replicas
         self.q_pos = torch.full((B, 1), CTX - 1, dtype=torch.int32, device=dev)
         self.win_pos0 = torch.full((B,), CTX - LWIN, dtype=torch.int32, device=dev)
-        # CSA compressed K/V cache (gathered rows only; one copy)
-        self.kc = torch.empty((B, N_CSA, D), dtype=bf, device=dev)
-        self.vc = torch.empty((B, N_CSA, D), dtype=bf, device=dev)
+        # CSA compressed K/V cache (gathered rows only; one copy).  K and V of an entry sit
+        # side by side in one [B, N, 2D] buffer, as do the raw K|V rows of the window, so
+        # that one pooling call compresses both (they share the block's gate weights).
+        self.kvc = torch.empty((B, N_CSA, 2 * D), dtype=bf, device=dev)
+        self.kc, self.vc = self.kvc[..., :D], self.kvc[..., D:]
         for b in range(B):
             self.kc[b] = synth.device_normal((N_CSA, D), seed(CFG_CSA, synth.KC, 0, b), bf)
             self.vc[b] = synth.device_normal((N_CSA, D), seed(CFG_CSA, synth.VC, 0, b), bf)
@@ -107,17 +109,20 @@ class Workload:
                 gz = torch.zeros((1, N_CSA), dtype=torch.float32, device=dev)
                 L.csa_compress(k32, gz, zeros1, 1, L.MXFP4_DTYPE, out=t["ki"][b:b + 1], out_scale=t["ks"][b:b + 1])
                 del k32, gz
-            t["kw"] = synth.device_normal((B, LWIN, D), seed(CFG_CSA, synth.KW, rep), bf)
-            t["vw"] = synth.device_normal((B, LWIN, D), seed(CFG_CSA, synth.VW, rep), bf)
+            t["kvw"] = torch.cat([synth.device_normal((B, LWIN, D), seed(CFG_CSA, synth.KW, rep), bf),
+                                  synth.device_normal((B, LWIN, D), seed(CFG_CSA, synth.VW, rep), bf)], dim=2)
+            t["kw"], t["vw"] = t["kvw"][..., :D], t["kvw"][..., D:]
             t["kiw"] = synth.device_normal((B, LWIN, DI), seed(CFG_CSA, synth.RAW_KI, rep), bf)
             t["gate"] = synth.device_normal((B, LWIN), seed(CFG_CSA, synth.GATE, rep), torch.float32)
             t["bias"] = synth.device_normal((M_CSA,), seed(CFG_CSA, synth.BIAS, rep), torch.float32, std=0.1)
             # HCA layer
             t["hq"] = synth.device_normal((B, 1, H, D), seed(CFG_HCA, synth.Q, rep), bf)
-            t["hkc"] = synth.device_normal((B, N_HCA, D), seed(CFG_HCA, synth.KC, rep), bf)
-            t["hvc"] = synth.device_normal((B, N_HCA, D), seed(CFG_HCA, synth.VC, rep), bf)
-            t["hkw"] = synth.device_normal((B, LWIN, D), seed(CFG_HCA, synth.KW, rep), bf)
-            t["hvw"] = synth.device_normal((B, LWIN, D), seed(CFG_HCA, synth.VW, rep), bf)
+            t["hkvc"] = torch.cat([synth.device_normal((B, N_HCA, D), seed(CFG_HCA, synth.KC, rep), bf),
+                                   synth.device_normal((B, N_HCA, D), seed(CFG_HCA, synth.VC, rep), bf)], dim=2)
+            t["hkc"], t["hvc"] = t["hkvc"][..., :D], t["hkvc"][..., D:]
+            t["hkvw"] = torch.cat([synth.device_normal((B, LWIN, D), seed(CFG_HCA, synth.KW, rep), bf),
+                                   synth.device_normal((B, LWIN, D), seed(CFG_HCA, synth.VW, rep), bf)], dim=2)
+            t["hkw"], t["hvw"] = t["hkvw"][..., :D], t["hkvw"][..., D:]
             t["hgate"] = synth.device_normal((B, LWIN), seed(CFG_HCA, synth.GATE, rep), torch.float32)
             t["hbias"] = synth.device_normal((M_HCA,), seed(CFG_HCA, synth.BIAS, rep), torch.float32, std=0.1)
             # outputs
@@ -140,10 +145,10 @@ def marshal_step(L, torch, wl, rep):
     calls = []
     g4 = t["gate"][:, LWIN - M_CSA:].contiguous()
     t["g4"] = g4
-    # CSA: the newest 4-token block -> entry N_CSA-1 of K, V (bf16) and indexer key (MXFP4)
-    for src, dst in ((t["kw"], wl.kc), (t["vw"], wl.vc)):
-        calls.append((lib.csa_compress, (P(src[:, LWIN - M_CSA:]), L.BF16, P(g4), P(t["bias"]), B, M_CSA, D, M_CSA,
-                                         LWIN, P(dst[:, N_CSA - 1:]), None, L.BF16, N_CSA, st)))
+    # CSA: the newest 4-token block -> entry N_CSA-1 of K|V (bf16, one call over the 2D
+    # channels) and of the indexer key (MXFP4)
+    calls.append((lib.csa_compress, (P(t["kvw"][:, LWIN - M_CSA:]), L.BF16, P(g4), P(t["bias"]), B, M_CSA, 2 * D,
+                                     M_CSA, LWIN, P(wl.kvc[:, N_CSA - 1:]), None, L.BF16, N_CSA, st)))
     calls.append((lib.csa_compress, (P(t["kiw"][:, LWIN - M_CSA:]), L.BF16, P(g4), P(t["bias"]), B, M_CSA, DI, M_CSA,
                                      LWIN, P(t["ki"][:, N_CSA - 1:]), P(t["ks"][:, N_CSA - 1:]), L.MXFP4, N_CSA, st)))
     # CSA: indexer + top-k
@@ -157,18 +162,17 @@ def marshal_step(L, torch, wl, rep):
     timed = {len(calls) - 1: "index_mfma_kernel"}
     # CSA attention
     att = (P(t["q"]), P(wl.kc), P(wl.vc), L.BF16, P(t["idx"]), TOPK, P(t["kw"]), P(t["vw"]), P(wl.win_pos0), LWIN, W,
-           P(wl.q_pos), B, 1, H, D, N_CSA, 0, ctypes.c_float(scale), P(t["o"]), P(t["lse"]))
+           P(wl.q_pos), B, 1, H, D, N_CSA, 0, 2 * D, 2 * D, ctypes.c_float(scale), P(t["o"]), P(t["lse"]))
     assert lib.csa_attend(*att, None, ctypes.byref(n), st) == 0
     t["ws_csa"] = torch.empty(max(n.value, 1), dtype=torch.uint8, device="cuda")
     t["ws_csa_n"] = ctypes.c_size_t(n.value)
     calls.append((lib.csa_attend, att + (P(t["ws_csa"]), ctypes.byref(t["ws_csa_n"]), st)))
     timed[len(calls) - 1] = "attend_bf16_kernel (CSA)"
-    # HCA: the newest 128-token block (the whole window) -> entry N_HCA-1
-    for src, dst in ((t["hkw"], t["hkc"]), (t["hvw"], t["hvc"])):
-        calls.append((lib.csa_compress, (P(src), L.BF16, P(t["hgate"]), P(t["hbias"]), B, M_HCA, D, M_HCA, LWIN,
-                                         P(dst[:, N_HCA - 1:]), None, L.BF16, N_HCA, st)))
+    # HCA: the newest 128-token block (the whole window) -> entry N_HCA-1 of K|V
+    calls.append((lib.csa_compress, (P(t["hkvw"]), L.BF16, P(t["hgate"]), P(t["hbias"]), B, M_HCA, 2 * D, M_HCA, LWIN,
+                                     P(t["hkvc"][:, N_HCA - 1:]), None, L.BF16, N_HCA, st)))
     hatt = (P(t["hq"]), P(t["hkc"]), P(t["hvc"]), L.BF16, M_HCA, P(t["hkw"]), P(t["hvw"]), P(wl.win_pos0), LWIN, W,
-            P(wl.q_pos), B, 1, H, D, N_HCA, 0, ctypes.c_float(scale), P(t["ho"]), P(t["hlse"]))
+            P(wl.q_pos), B, 1, H, D, N_HCA, 0, 2 * D, 2 * D, ctypes.c_float(scale), P(t["ho"]), P(t["hlse"]))
     assert lib.hca_attend(*hatt, None, ctypes.byref(n), st) == 0
     t["ws_hca"] = torch.empty(max(n.value, 1), dtype=torch.uint8, device="cuda")
     t["ws_hca_n"] = ctypes.c_size_t(n.value)

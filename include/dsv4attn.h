@@ -148,9 +148,14 @@ dsv4_status csa_index_topk(const void* qi, int qi_dt, const float* wi,
  *   (multi-query: the H heads share one K/V; a recent token may contribute both through
  *   its compressed entry and through its window row.)
  *
- *   q    [B, Q, H, D];  kc, vc [B, kv_bstride rows, D] (kv_bstride == 0 means N);
+ *   q    [B, Q, H, D];  kc, vc [B, kv_bstride rows, D] (kv_bstride == 0 means N) with
+ *        kv_rstride elements from one row to the next (0 means D);
  *   idx  [B, Q, k] int32 (entries outside [0, N) are skipped);
- *   kw, vw [B, L, D]: row r holds position win_pos0[b] + r;  win_pos0 [B], q_pos [B, Q].
+ *   kw, vw [B, L, D]: row r holds position win_pos0[b] + r, w_rstride elements from one row
+ *        to the next (0 means D);  win_pos0 [B], q_pos [B, Q].
+ *   Row strides larger than D let K and V live side by side in one [.., 2D] buffer (then
+ *   one csa_compress call pools both).  BF16: strides multiples of 8 elements, rows and
+ *   pointers 16-byte aligned.
  *   dt = F32 or BF16 for q, kc, vc, kw, vw and out.  BF16: D in {128, 256, 512} and
  *   H in {16, 32, 48, 64}; F32: D <= 512.  B*Q <= 65535.  out [B, Q, H, D] of dt;  lse [B, Q, H] f32 or NULL.
  *   fp32 accumulation; partial results are merged by log-sum-exp in fp32.
@@ -159,7 +164,7 @@ dsv4_status csa_attend(const void* q, const void* kc, const void* vc, int dt,
                        const int32_t* idx, int32_t k,
                        const void* kw, const void* vw, const int32_t* win_pos0, int64_t L, int32_t W,
                        const int32_t* q_pos, int64_t B, int64_t Q, int32_t H, int32_t D,
-                       int64_t N, int64_t kv_bstride, float scale,
+                       int64_t N, int64_t kv_bstride, int64_t kv_rstride, int64_t w_rstride, float scale,
                        void* out, float* lse, void* workspace, size_t* ws_bytes, hipStream_t stream);
 
 /*
@@ -173,7 +178,7 @@ dsv4_status csa_attend(const void* q, const void* kc, const void* vc, int dt,
 dsv4_status hca_attend(const void* q, const void* kc, const void* vc, int dt, int32_t m,
                        const void* kw, const void* vw, const int32_t* win_pos0, int64_t L, int32_t W,
                        const int32_t* q_pos, int64_t B, int64_t Q, int32_t H, int32_t D,
-                       int64_t N, int64_t kv_bstride, float scale,
+                       int64_t N, int64_t kv_bstride, int64_t kv_rstride, int64_t w_rstride, float scale,
                        void* out, float* lse, void* workspace, size_t* ws_bytes, hipStream_t stream);
 
 /*

@@ -34,9 +34,9 @@ _SIGS = {
     "csa_index_topk": ([_p, ctypes.c_int, _p, _p, _p, ctypes.c_int, _p, _i64, _i64, _i32, _i32, _i64, _i64, _i32,
                         _i32, _p, _p, _p, ctypes.POINTER(ctypes.c_size_t), _p], ctypes.c_int),
     "csa_attend": ([_p, _p, _p, ctypes.c_int, _p, _i32, _p, _p, _p, _i64, _i32, _p, _i64, _i64, _i32, _i32, _i64,
-                    _i64, ctypes.c_float, _p, _p, _p, ctypes.POINTER(ctypes.c_size_t), _p], ctypes.c_int),
+                    _i64, _i64, _i64, ctypes.c_float, _p, _p, _p, ctypes.POINTER(ctypes.c_size_t), _p], ctypes.c_int),
     "hca_attend": ([_p, _p, _p, ctypes.c_int, _i32, _p, _p, _p, _i64, _i32, _p, _i64, _i64, _i32, _i32, _i64, _i64,
-                    ctypes.c_float, _p, _p, _p, ctypes.POINTER(ctypes.c_size_t), _p], ctypes.c_int),
+                    _i64, _i64, ctypes.c_float, _p, _p, _p, ctypes.POINTER(ctypes.c_size_t), _p], ctypes.c_int),
     "lse_merge": ([_p, _p, _i32, _i64, _i32, _p, ctypes.c_int, _p, _p], ctypes.c_int),
 }
 
@@ -105,6 +105,8 @@ def csa_compress(x, gate, pos_bias, m: int, y_dtype=torch.bfloat16, out=None, ou
     (codes [B,T/m,C/2] uint8, scales [B,T/m,C/32] uint8)).  `out` may be a [B, rows, ...] view
     with rows >= T/m (e.g. the tail of a cache); its batch stride is passed through.
     """
+    if not (gate.is_contiguous() and pos_bias.is_contiguous()):
+        raise ValueError("gate [B, T] and pos_bias [m] must be contiguous")
     B, T, C = x.shape
     nb = T // m
     if y_dtype == MXFP4_DTYPE:
@@ -144,23 +146,30 @@ def csa_index_topk(qi, wi, ki, q_pos, m: int, k: int, ki_scale=None, N=None, wit
     return (out_idx, out_score) if with_scores else out_idx
 
 
-def _attend_common(q, kc, kw, win_pos0, q_pos, N):
+def _attend_common(q, kc, vc, kw, vw, win_pos0, q_pos, N):
+    """Sizes and strides of the key/value tensors: rows may be wider than D (e.g. K and V
+    side by side in one [.., 2D] buffer), the last dimension must be contiguous."""
     B, Q, H, D = q.shape
     N = kc.shape[1] if N is None else N
-    kv_bs = kc.stride(0) // kc.stride(1) if B > 0 else 0
+    if kc.stride(-1) != 1 or kw.stride(-1) != 1 or kc.stride() != vc.stride() or kw.stride() != vw.stride():
+        raise ValueError("kc/vc and kw/vw must share strides and have a contiguous last dimension")
+    kv_rs, w_rs = kc.stride(1), kw.stride(1)
+    kv_bs = kc.stride(0) // kv_rs if B > 0 else 0
     L = kw.shape[1]
-    return B, Q, H, D, N, kv_bs, L
+    if B > 1 and kw.stride(0) != L * w_rs:
+        raise ValueError("kw/vw batches must be L rows apart")
+    return B, Q, H, D, N, kv_bs, L, kv_rs, w_rs
 
 
 def csa_attend(q, kc, vc, idx, kw, vw, win_pos0, W: int, q_pos, scale: float, N=None, workspace=None, out=None,
                lse=None):
     """One softmax over the listed compressed entries and the window rows.
     Returns (o [B,Q,H,D] in q's dtype, lse [B,Q,H] f32)."""
-    B, Q, H, D, N, kv_bs, L = _attend_common(q, kc, kw, win_pos0, q_pos, N)
+    B, Q, H, D, N, kv_bs, L, kv_rs, w_rs = _attend_common(q, kc, vc, kw, vw, win_pos0, q_pos, N)
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, Q, H), dtype=torch.float32, device=q.device) if lse is None else lse
     args = (_ptr(q), _ptr(kc), _ptr(vc), _dt(q), _ptr(idx), idx.shape[2], _ptr(kw), _ptr(vw), _ptr(win_pos0), L, W,
-            _ptr(q_pos), B, Q, H, D, N, kv_bs, float(scale), _ptr(out), _ptr(lse))
+            _ptr(q_pos), B, Q, H, D, N, kv_bs, kv_rs, w_rs, float(scale), _ptr(out), _ptr(lse))
     ws, n = _workspace(lambda n: lib().csa_attend(*args, None, ctypes.byref(n), _stream()), workspace)
     _check(lib().csa_attend(*args, _ptr(ws), n, _stream()))
     return out, lse
@@ -169,11 +178,11 @@ def csa_attend(q, kc, vc, idx, kw, vw, win_pos0, W: int, q_pos, scale: float, N=
 def hca_attend(q, kc, vc, m: int, kw, vw, win_pos0, W: int, q_pos, scale: float, N=None, workspace=None, out=None,
                lse=None):
     """One softmax over every visible compressed entry and the window rows."""
-    B, Q, H, D, N, kv_bs, L = _attend_common(q, kc, kw, win_pos0, q_pos, N)
+    B, Q, H, D, N, kv_bs, L, kv_rs, w_rs = _attend_common(q, kc, vc, kw, vw, win_pos0, q_pos, N)
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, Q, H), dtype=torch.float32, device=q.device) if lse is None else lse
     args = (_ptr(q), _ptr(kc), _ptr(vc), _dt(q), m, _ptr(kw), _ptr(vw), _ptr(win_pos0), L, W, _ptr(q_pos), B, Q, H,
-            D, N, kv_bs, float(scale), _ptr(out), _ptr(lse))
+            D, N, kv_bs, kv_rs, w_rs, float(scale), _ptr(out), _ptr(lse))
     ws, n = _workspace(lambda n: lib().hca_attend(*args, None, ctypes.byref(n), _stream()), workspace)
     _check(lib().hca_attend(*args, _ptr(ws), n, _stream()))
     return out, lse

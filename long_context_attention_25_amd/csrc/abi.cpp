@@ -73,7 +73,7 @@ struct AttendCommon {
   int32_t W;
   int64_t B, Q;
   int32_t H, D;
-  int64_t N, kv_bstride;
+  int64_t N, kv_bstride, kv_rstride, w_rstride;
   float scale;
   void* out;
 };
@@ -91,6 +91,12 @@ dsv4_status check_attend(const char* what, const AttendCommon& c) {
   }
   REQUIRE(c.kv_bstride == 0 || c.kv_bstride >= c.N, "%s: kv_bstride (%lld) must be 0 or >= N (%lld)", what,
           (long long)c.kv_bstride, (long long)c.N);
+  REQUIRE(c.kv_rstride == 0 || c.kv_rstride >= c.D, "%s: kv_rstride (%lld) must be 0 or >= D (%d)", what,
+          (long long)c.kv_rstride, c.D);
+  REQUIRE(c.w_rstride == 0 || c.w_rstride >= c.D, "%s: w_rstride (%lld) must be 0 or >= D (%d)", what,
+          (long long)c.w_rstride, c.D);
+  if (c.dt == DSV4_BF16)
+    REQUIRE(c.kv_rstride % 8 == 0 && c.w_rstride % 8 == 0, "%s: bf16 row strides must be multiples of 8", what);
   REQUIRE(c.B * c.Q <= 65535, "%s: B*Q must be <= 65535", what);
   if (c.B * c.Q > 0) {
     REQUIRE(c.q && c.out && c.q_pos && c.win_pos0, "%s: q, out, q_pos and win_pos0 must not be NULL", what);
@@ -109,6 +115,8 @@ dsv4::AttendArgs to_args(const AttendCommon& c, bool csa, const int32_t* idx, in
   a.kw = c.kw; a.vw = c.vw; a.win_pos0 = c.win_pos0; a.L = c.L; a.W = c.W;
   a.q_pos = c.q_pos; a.B = c.B; a.Q = c.Q; a.H = c.H; a.D = c.D;
   a.N = c.N; a.kv_bs = c.kv_bstride ? c.kv_bstride : c.N;
+  a.kv_rs = c.kv_rstride ? c.kv_rstride : c.D;
+  a.w_rs = c.w_rstride ? c.w_rstride : c.D;
   a.scale = c.scale; a.out = c.out; a.lse = lse;
   return a;
 }
@@ -228,10 +236,11 @@ dsv4_status csa_index_topk(const void* qi, int qi_dt, const float* wi, const voi
 dsv4_status csa_attend(const void* q, const void* kc, const void* vc, int dt, const int32_t* idx, int32_t k,
                        const void* kw, const void* vw, const int32_t* win_pos0, int64_t L, int32_t W,
                        const int32_t* q_pos, int64_t B, int64_t Q, int32_t H, int32_t D, int64_t N,
-                       int64_t kv_bstride, float scale, void* out, float* lse, void* workspace, size_t* ws_bytes,
-                       hipStream_t stream) {
+                       int64_t kv_bstride, int64_t kv_rstride, int64_t w_rstride, float scale, void* out, float* lse,
+                       void* workspace, size_t* ws_bytes, hipStream_t stream) {
   const char* what = "csa_attend";
-  AttendCommon c{q, kc, vc, kw, vw, dt, win_pos0, q_pos, L, W, B, Q, H, D, N, kv_bstride, scale, out};
+  AttendCommon c{q, kc, vc, kw, vw, dt, win_pos0, q_pos, L, W, B, Q, H, D, N, kv_bstride, kv_rstride, w_rstride,
+                 scale, out};
   dsv4_status s = check_attend(what, c);
   if (s != DSV4_OK) return s;
   REQUIRE(k >= 0 && k <= 65536, "%s: k must be in [0, 65536]", what);
@@ -241,10 +250,12 @@ dsv4_status csa_attend(const void* q, const void* kc, const void* vc, int dt, co
 
 dsv4_status hca_attend(const void* q, const void* kc, const void* vc, int dt, int32_t m, const void* kw,
                        const void* vw, const int32_t* win_pos0, int64_t L, int32_t W, const int32_t* q_pos,
-                       int64_t B, int64_t Q, int32_t H, int32_t D, int64_t N, int64_t kv_bstride, float scale,
-                       void* out, float* lse, void* workspace, size_t* ws_bytes, hipStream_t stream) {
+                       int64_t B, int64_t Q, int32_t H, int32_t D, int64_t N, int64_t kv_bstride,
+                       int64_t kv_rstride, int64_t w_rstride, float scale, void* out, float* lse, void* workspace,
+                       size_t* ws_bytes, hipStream_t stream) {
   const char* what = "hca_attend";
-  AttendCommon c{q, kc, vc, kw, vw, dt, win_pos0, q_pos, L, W, B, Q, H, D, N, kv_bstride, scale, out};
+  AttendCommon c{q, kc, vc, kw, vw, dt, win_pos0, q_pos, L, W, B, Q, H, D, N, kv_bstride, kv_rstride, w_rstride,
+                 scale, out};
   dsv4_status s = check_attend(what, c);
   if (s != DSV4_OK) return s;
   REQUIRE(m >= 1, "%s: m must be >= 1", what);

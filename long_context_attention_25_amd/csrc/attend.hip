@@ -71,10 +71,10 @@ __device__ __forceinline__ int64_t key_row(const AttendArgs& a, int64_t bq, cons
   if (pos < kr.n_c) {
     int64_t j = a.csa ? (int64_t)a.idx[bq * a.k + pos] : pos;
     if (j < 0 || j >= a.N) return -1;
-    return (b * a.kv_bs + j) * a.D;
+    return (b * a.kv_bs + j) * a.kv_rs;
   }
   *win = true;
-  return (b * a.L + kr.r_lo + (pos - kr.n_c)) * a.D;
+  return (b * a.L + kr.r_lo + (pos - kr.n_c)) * a.w_rs;
 }
 
 // ---------------------------------------------------------------------------- bf16 / MFMA
@@ -174,10 +174,11 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
   if (s1 > kr.n_tot) s1 = kr.n_tot;
   const int ntile = s1 > s0 ? (int)((s1 - s0 + KT - 1) / KT) : 0;
 
-  const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.kc) + b * a.kv_bs * D;
-  const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.vc) + b * a.kv_bs * D;
-  const uint16_t* kw = reinterpret_cast<const uint16_t*>(a.kw) + b * a.L * D;
-  const uint16_t* vw = reinterpret_cast<const uint16_t*>(a.vw) + b * a.L * D;
+  const int64_t krs = a.kv_rs, wrs = a.w_rs;
+  const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.kc) + b * a.kv_bs * krs;
+  const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.vc) + b * a.kv_bs * krs;
+  const uint16_t* kw = reinterpret_cast<const uint16_t*>(a.kw) + b * a.L * wrs;
+  const uint16_t* vw = reinterpret_cast<const uint16_t*>(a.vw) + b * a.L * wrs;
 
   const int hg = wave % 4, dh = wave / 4;  // head group and output slice
   const int head = hg * 16 + col;
@@ -204,14 +205,14 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
         const int64_t j = a.csa ? (int64_t)list[pos - s0] : pos;
         if (j >= 0 && j < a.N) {
           ok = true;
-          kp = kc + j * D;
-          vp = vc + j * D;
+          kp = kc + j * krs;
+          vp = vc + j * krs;
         }
       } else {
         const int64_t r = kr.r_lo + (pos - kr.n_c);
         ok = true;
-        kp = kw + r * D;
-        vp = vw + r * D;
+        kp = kw + r * wrs;
+        vp = vw + r * wrs;
       }
     }
     my_kp = kp;

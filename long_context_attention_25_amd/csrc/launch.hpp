@@ -85,7 +85,8 @@ struct AttendArgs {
   const int32_t* q_pos;
   int64_t B, Q;
   int H, D;
-  int64_t N, kv_bs;
+  int64_t N, kv_bs;       // kv_bs: rows between batches of kc/vc
+  int64_t kv_rs, w_rs;     // elements between rows of kc/vc and of kw/vw
   float scale;
   void* out;
   float* lse;

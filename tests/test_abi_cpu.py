@@ -91,17 +91,17 @@ def test_index_topk_validation_and_workspace_query():
 
 def _attend(csa=True, ws=None, **kw):
     a = dict(q=P, kc=P, vc=P, dt=1, idx=P, k=1024, kw=P, vw=P, wp0=P, L=128, W=128, qpos=P, B=8, Q=1, H=64, D=512,
-             N=262144, kvbs=0, scale=0.044, out=P, lse=P, m=128)
+             N=262144, kvbs=0, kvrs=0, wrs=0, scale=0.044, out=P, lse=P, m=128)
     a.update(kw)
     n = ctypes.c_size_t(0)
     if csa:
         st = L.lib().csa_attend(a["q"], a["kc"], a["vc"], a["dt"], a["idx"], a["k"], a["kw"], a["vw"], a["wp0"],
                                 a["L"], a["W"], a["qpos"], a["B"], a["Q"], a["H"], a["D"], a["N"], a["kvbs"],
-                                a["scale"], a["out"], a["lse"], ws, ctypes.byref(n), None)
+                                a["kvrs"], a["wrs"], a["scale"], a["out"], a["lse"], ws, ctypes.byref(n), None)
     else:
         st = L.lib().hca_attend(a["q"], a["kc"], a["vc"], a["dt"], a["m"], a["kw"], a["vw"], a["wp0"], a["L"],
-                                a["W"], a["qpos"], a["B"], a["Q"], a["H"], a["D"], a["N"], a["kvbs"], a["scale"],
-                                a["out"], a["lse"], ws, ctypes.byref(n), None)
+                                a["W"], a["qpos"], a["B"], a["Q"], a["H"], a["D"], a["N"], a["kvbs"], a["kvrs"],
+                                a["wrs"], a["scale"], a["out"], a["lse"], ws, ctypes.byref(n), None)
     return st, n.value
 
 
@@ -117,6 +117,9 @@ def test_attend_validation_and_workspace_query():
     assert _attend(q=None)[0] == 1
     assert _attend(csa=False, m=0)[0] == 1
     assert _attend(kvbs=7)[0] == 1
+    assert _attend(kvrs=1024, wrs=1024)[0] == 0          # K and V side by side
+    assert _attend(kvrs=100)[0] == 1                     # narrower than D
+    assert _attend(wrs=1028)[0] == 1                     # bf16 rows must stay 16-byte aligned
     assert _attend(scale=float("nan"))[0] == 1
     assert _attend(dt=0, D=128, H=16)[0] == 0           # f32 path needs no workspace
     assert _attend(dt=0, D=1024, H=16)[0] == 2

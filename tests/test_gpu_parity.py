@@ -362,6 +362,49 @@ def test_hca_attend_bf16(H, D, N):
     assert lse_abs_err(host(lse), lse_ref) <= 1e-2
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_attend_with_kv_side_by_side(dt):
+    """K and V rows in one [.., 2D] buffer (caches and window), pooled by one csa_compress
+    call; attention reads them through row strides and matches the separate-tensor call."""
+    cfg = 470
+    B, Q, H, D, N, L_, W, k, m = 2, 2, 16, 128, 900, 140, 128, 64, 4
+    T = 4 * m
+    q, kc, vc, kw, vw = _attn_inputs(cfg, B, Q, H, D, N, L_)
+    idx = synth.sorted_unique_indices(cfg, synth.IDX, B * Q, N, k).reshape(B, Q, k)
+    win_pos0 = np.array([2700, 2000], dtype=np.int32)
+    pos = np.array([[2799, 2750], [2100, 2139]], dtype=np.int32)
+    scale = 1.0 / math.sqrt(D)
+    if dt == "bf16":
+        cv = lambda a: dev_bf16(a)[0]
+    else:
+        cv = dev
+    kvc = torch.cat([cv(kc), cv(vc)], dim=2)          # [B, N, 2D]
+    kvw = torch.cat([cv(kw), cv(vw)], dim=2)          # [B, L, 2D]
+    # the newest block of both K and V pooled in one call into the caches' last entry
+    gate = dev(synth.normal(cfg, synth.GATE, (B, T)))
+    bias = dev(synth.normal(cfg, synth.BIAS, (m,), std=0.1))
+    g_blk = gate[:, :m].contiguous()
+    L.csa_compress(kvw[:, L_ - T:L_ - T + m], g_blk, bias, m, kvc.dtype, out=kvc[:, N - 1:])
+    qd = cv(q)
+    o1, lse1 = L.csa_attend(qd, kvc[..., :D], kvc[..., D:], dev(idx), kvw[..., :D], kvw[..., D:], dev(win_pos0), W,
+                            dev(pos), scale)
+    o2, lse2 = L.csa_attend(qd, kvc[..., :D].contiguous(), kvc[..., D:].contiguous(), dev(idx),
+                            kvw[..., :D].contiguous(), kvw[..., D:].contiguous(), dev(win_pos0), W, dev(pos), scale)
+    h1, hl1 = L.hca_attend(qd, kvc[..., :D], kvc[..., D:], m, kvw[..., :D], kvw[..., D:], dev(win_pos0), W, dev(pos),
+                           scale, N=300)
+    h2, hl2 = L.hca_attend(qd, kvc[..., :D].contiguous(), kvc[..., D:].contiguous(), m, kvw[..., :D].contiguous(),
+                           kvw[..., D:].contiguous(), dev(win_pos0), W, dev(pos), scale, N=300)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(lse1, lse2)
+    assert torch.equal(h1, h2) and torch.equal(hl1, hl2)
+    # the pooled entry: K and V halves each equal the oracle's pooling of their raw rows
+    kv_h = host(kvc)
+    raw = host(kvw)
+    y_r = method.compress(raw[:, L_ - T:L_ - T + m], host(g_blk), host(bias), m)
+    tol = compress_tol(raw[:, L_ - T:L_ - T + m], m, y_r) if dt == "bf16" else 1e-5 * np.abs(y_r).max()
+    assert np.all(np.abs(kv_h[:, N - 1:N] - y_r) <= tol)
+
+
 @pytest.mark.parametrize("D,H", [(128, 16), (64, 4), (512, 2)])
 def test_attend_f32_csa_and_hca(D, H):
     cfg = 450 + D
