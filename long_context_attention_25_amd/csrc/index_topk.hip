@@ -182,6 +182,32 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
   const int64_t QT = (Q + QPT - 1) / QPT;
   const int64_t QG = (QT + QTW - 1) / QTW;
   const int64_t b = blockIdx.y / QG, qt0 = (blockIdx.y % QG) * QTW;
+  // key range of this workgroup; the first step's key tiles are loaded before anything
+  // else so that their latency overlaps the query loads below
+  const uint8_t* kbase;
+  const uint8_t* sbase = nullptr;
+  if constexpr (KIND == KEY_BF16) kbase = ki + b * k_bs * DI * 2;
+  else if constexpr (KIND == KEY_FP8) kbase = ki + b * k_bs * DI;
+  else {
+    kbase = ki + b * k_bs * (DI / 2);
+    sbase = ksc + b * k_bs * (DI / 32);
+  }
+  constexpr int TPW = QTW == 1 ? tiles_per_step<KIND, DI>() : (KIND == KEY_FP8 ? 4 : 2);
+  constexpr int KPS = TPW * 16 * 4;
+  const int64_t c0 = (int64_t)blockIdx.x * chunk;
+  int64_t c1 = c0 + chunk;
+  if (c1 > N) c1 = N;
+  const int64_t klast = c1 - 1;
+  KeyTile<KIND, DI> cur[TPW], nxt[TPW];
+  int64_t base = c0 + wave * (TPW * 16);
+  if (base < c1) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int64_t key = base + u * 16 + col;
+      cur[u].load(kbase, sbase, key < klast ? key : klast, g, true);
+    }
+  }
+
   int nq[QTW];
   int nslots = 0;
 #pragma unroll
@@ -225,33 +251,9 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
   }
   __syncthreads();
 
-  const uint8_t* kbase;
-  const uint8_t* sbase = nullptr;
-  if constexpr (KIND == KEY_BF16) kbase = ki + b * k_bs * DI * 2;
-  else if constexpr (KIND == KEY_FP8) kbase = ki + b * k_bs * DI;
-  else {
-    kbase = ki + b * k_bs * (DI / 2);
-    sbase = ksc + b * k_bs * (DI / 32);
-  }
-
   // Each wave takes TPW consecutive 16-key tiles per step; the next step's tiles are
   // loaded before this step's are used.  Key indices past the range are clamped to its
   // last key, so loads never branch; only the score write is guarded.
-  constexpr int TPW = QTW == 1 ? tiles_per_step<KIND, DI>() : (KIND == KEY_FP8 ? 4 : 2);
-  constexpr int KPS = TPW * 16 * 4;
-  const int64_t c0 = (int64_t)blockIdx.x * chunk;
-  int64_t c1 = c0 + chunk;
-  if (c1 > N) c1 = N;
-  const int64_t klast = c1 - 1;
-  KeyTile<KIND, DI> cur[TPW], nxt[TPW];
-  int64_t base = c0 + wave * (TPW * 16);
-  if (base < c1) {
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      const int64_t key = base + u * 16 + col;
-      cur[u].load(kbase, sbase, key < klast ? key : klast, g, true);
-    }
-  }
   for (; base < c1; base += KPS) {
     const int64_t nb = base + KPS;
     if (nb < c1) {
@@ -363,8 +365,8 @@ constexpr int kCandCap = 4096;                               // candidates stage
 
 __global__ __launch_bounds__(kScanThreads) void select_scan_kernel(
     const float* __restrict__ scores, const uint32_t* __restrict__ hist_g, uint32_t* __restrict__ bitmap_g,
-    uint64_t* __restrict__ cand_g, uint32_t* __restrict__ ccount, const int32_t* __restrict__ q_pos, int64_t N,
-    int64_t sstride, int64_t words, int m, int k) {
+    uint64_t* __restrict__ cand_g, uint32_t* __restrict__ ccount, uint32_t* __restrict__ thr,
+    const int32_t* __restrict__ q_pos, int64_t N, int64_t sstride, int64_t words, int m, int k) {
   __shared__ uint32_t tmp[kScanThreads / kWave];
   __shared__ uint32_t misc[4];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -391,6 +393,10 @@ __global__ __launch_bounds__(kScanThreads) void select_scan_kernel(
   if (tid == 0) misc[2] = 0u;
   threshold_bin<kScanThreads>(hist_g + row * kHistBins, kk, tmp, misc);
   const uint32_t tbin = misc[0];
+  if (blockIdx.x == 0 && tid == 0) {       // recorded once per row for pass 2
+    thr[row * 2] = tbin;
+    thr[row * 2 + 1] = misc[1];
+  }
 
   uint32_t* bm = bitmap_g + row * words + c0 / 32;
   uint64_t* cs = cand_g + row * N + c0;
@@ -526,9 +532,10 @@ __device__ __forceinline__ void finish_row(uint32_t c, uint32_t need, uint32_t t
 // kLdsBits: the row's bitmap is copied into LDS (N <= kLdsBitmapKeys).
 template <bool kLdsBits>
 __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
-    const float* __restrict__ scores, const uint32_t* __restrict__ hist_g, uint32_t* __restrict__ bitmap_g,
-    const uint64_t* __restrict__ cand_g, const uint32_t* __restrict__ ccount, const int32_t* __restrict__ q_pos,
-    int64_t N, int64_t sstride, int64_t words, int m, int k, int nch, int32_t* __restrict__ out_idx,
+    const float* __restrict__ scores, uint32_t* __restrict__ bitmap_g,
+    const uint64_t* __restrict__ cand_g, const uint32_t* __restrict__ ccount, const uint32_t* __restrict__ thr,
+    const int32_t* __restrict__ q_pos, int64_t N, int64_t sstride, int64_t words, int m, int k, int nch,
+    int32_t* __restrict__ out_idx,
     float* __restrict__ out_score) {
   constexpr int NT = kFinThreads;
   __shared__ uint32_t bits_l[kLdsBits ? kLdsBitmapKeys / 32 : 1];
@@ -553,7 +560,9 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
     }
     return;
   }
-  // bitmap copy and candidate counts first (independent loads), then the threshold
+  // threshold bin and #keys above it, as pass 1 found them from the row's histogram
+  const uint2 th = *reinterpret_cast<const uint2*>(thr + row * 2);
+  const uint32_t tbin = th.x, cnt_above = th.y;
   if constexpr (kLdsBits) {
     for (int64_t w = (int64_t)tid * 4; w < wn; w += (int64_t)NT * 4) {
       const uint4 x = *reinterpret_cast<const uint4*>(gbits + w);   // rows are 16-byte padded
@@ -561,8 +570,6 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
     }
   }
   const int nrange = (int)(((int64_t)n + kScanKeys - 1) / kScanKeys);
-  threshold_bin<NT>(hist_g + row * kHistBins, kk, tmp, misc);
-  const uint32_t tbin = misc[0], cnt_above = misc[1];
   // candidate offsets per range (ranges beyond n hold none); more than NT ranges are
   // summed in rounds
   uint32_t run = 0;
@@ -674,7 +681,7 @@ size_t topk_workspace_bytes(int64_t R, int64_t N) {
   const int64_t sstride = ((N + 63) / 64) * 64;
   const int64_t nch = (N + kScanKeys - 1) / kScanKeys;
   return align256((size_t)R * sstride * 4) + align256((size_t)R * kHistBins * 4) + align256((size_t)R * words * 4) +
-         align256((size_t)R * N * 8) + align256((size_t)R * nch * 4);
+         align256((size_t)R * N * 8) + align256((size_t)R * nch * 4) + align256((size_t)R * 2 * 4);
 }
 
 TopkWorkspace topk_workspace_carve(void* base, int64_t R, int64_t N) {
@@ -690,6 +697,8 @@ TopkWorkspace topk_workspace_carve(void* base, int64_t R, int64_t N) {
   w.cand = reinterpret_cast<uint64_t*>(p);
   p += align256((size_t)R * N * 8);
   w.ccount = reinterpret_cast<uint32_t*>(p);
+  p += align256((size_t)R * ((N + kScanKeys - 1) / kScanKeys) * 4);
+  w.thr = reinterpret_cast<uint32_t*>(p);
   return w;
 }
 
@@ -724,8 +733,8 @@ hipError_t launch_index_topk(const IndexArgs& a, const TopkWorkspace& ws, hipStr
   }
   // selection: pass 1 over all rows x key ranges, pass 2 one workgroup per row
   if (a.N == 0) {
-    hipLaunchKernelGGL(select_finish_kernel<true>, dim3((unsigned)R), dim3(kFinThreads), 0, st, ws.scores, ws.hist,
-                       ws.bitmap, ws.cand, ws.ccount, a.q_pos, a.N, (int64_t)0, (int64_t)0, a.m, a.k, 0, a.out_idx,
+    hipLaunchKernelGGL(select_finish_kernel<true>, dim3((unsigned)R), dim3(kFinThreads), 0, st, ws.scores,
+                       ws.bitmap, ws.cand, ws.ccount, ws.thr, a.q_pos, a.N, (int64_t)0, (int64_t)0, a.m, a.k, 0, a.out_idx,
                        a.out_score);
     return hipGetLastError();
   }
@@ -733,16 +742,16 @@ hipError_t launch_index_topk(const IndexArgs& a, const TopkWorkspace& ws, hipStr
   const int64_t sstride = ((a.N + 63) / 64) * 64;
   const int64_t nch = (a.N + kScanKeys - 1) / kScanKeys;
   hipLaunchKernelGGL(select_scan_kernel, dim3((unsigned)nch, (unsigned)R), dim3(kScanThreads), 0, st, ws.scores,
-                     ws.hist, ws.bitmap, ws.cand, ws.ccount, a.q_pos, a.N, sstride, words, a.m, a.k);
+                     ws.hist, ws.bitmap, ws.cand, ws.ccount, ws.thr, a.q_pos, a.N, sstride, words, a.m, a.k);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.N <= kLdsBitmapKeys)
-    hipLaunchKernelGGL(select_finish_kernel<true>, dim3((unsigned)R), dim3(kFinThreads), 0, st, ws.scores, ws.hist,
-                       ws.bitmap, ws.cand, ws.ccount, a.q_pos, a.N, sstride, words, a.m, a.k, (int)nch, a.out_idx,
+    hipLaunchKernelGGL(select_finish_kernel<true>, dim3((unsigned)R), dim3(kFinThreads), 0, st, ws.scores,
+                       ws.bitmap, ws.cand, ws.ccount, ws.thr, a.q_pos, a.N, sstride, words, a.m, a.k, (int)nch, a.out_idx,
                        a.out_score);
   else
-    hipLaunchKernelGGL(select_finish_kernel<false>, dim3((unsigned)R), dim3(kFinThreads), 0, st, ws.scores, ws.hist,
-                       ws.bitmap, ws.cand, ws.ccount, a.q_pos, a.N, sstride, words, a.m, a.k, (int)nch, a.out_idx,
+    hipLaunchKernelGGL(select_finish_kernel<false>, dim3((unsigned)R), dim3(kFinThreads), 0, st, ws.scores,
+                       ws.bitmap, ws.cand, ws.ccount, ws.thr, a.q_pos, a.N, sstride, words, a.m, a.k, (int)nch, a.out_idx,
                        a.out_score);
   return hipGetLastError();
 }

@@ -62,6 +62,7 @@ struct TopkWorkspace {
   uint32_t* bitmap;     // [R][words]
   uint64_t* cand;       // [R][N]: candidate slices of the key ranges
   uint32_t* ccount;     // [R][ranges]: candidates per key range
+  uint32_t* thr;        // [R][2]: threshold bin and #keys above it, per row
 };
 size_t topk_workspace_bytes(int64_t R, int64_t N);
 TopkWorkspace topk_workspace_carve(void* base, int64_t R, int64_t N);
