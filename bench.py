@@ -405,9 +405,12 @@ def run_prefill(L, torch, synth, steps, warmup):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--replicas", type=int, default=3)
+    ap.add_argument("--time-every", type=int, default=10,
+                    help="per-kernel event timing on every n-th timed step (event-timed launches cost "
+                         "a few microseconds each, so timing every step would slow the step itself)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill", action="store_true",
@@ -435,7 +438,8 @@ def main():
     steps = [marshal_step(L, torch, wl, r) for r in range(args.replicas)]
     timed = steps[0][1]
     ev = HipEvents()
-    pairs = [{i: (ev.create(), ev.create()) for i in timed} for _ in range(args.steps)]
+    every = max(1, args.time_every)
+    pairs = [{i: (ev.create(), ev.create()) for i in timed} for _ in range((args.steps + every - 1) // every)]
 
     for i in range(args.warmup):
         run_step(lib, steps[i % args.replicas][0])
@@ -451,7 +455,7 @@ def main():
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(args.steps):
-        run_step(lib, steps[i % args.replicas][0], arm=pairs[i])
+        run_step(lib, steps[i % args.replicas][0], arm=pairs[i // every] if i % every == 0 else None)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
@@ -460,7 +464,7 @@ def main():
     qps = B / (ms / 1e3)
     kernels = {}
     for i, name in timed.items():
-        k_ms = sum(ev.elapsed_ms(*p[i]) for p in pairs) / args.steps
+        k_ms = sum(ev.elapsed_ms(*p[i]) for p in pairs) / len(pairs)
         gbs = KERNEL_BYTES[name] / (k_ms / 1e3) / 1e9
         kernels[name] = {"avg_launch_us": round(k_ms * 1e3, 2), "bytes_per_launch": KERNEL_BYTES[name],
                          "achieved_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
@@ -493,7 +497,8 @@ def main():
         "bytes_per_step": total_bytes,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": k["achieved_gbs"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": k["frac"], "traffic": traffic,
-                     "bytes_per_launch": k["bytes_per_launch"], "avg_launch_us": k["avg_launch_us"]},
+                     "bytes_per_launch": k["bytes_per_launch"], "avg_launch_us": k["avg_launch_us"],
+                     "timed_launches": len(pairs)},
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:

@@ -194,6 +194,7 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
   }
   constexpr int TPW = QTW == 1 ? tiles_per_step<KIND, DI>() : (KIND == KEY_FP8 ? 4 : 2);
   constexpr int KPS = TPW * 16 * 4;
+  constexpr int E = GPQ < TPW ? GPQ : TPW;
   const int64_t c0 = (int64_t)blockIdx.x * chunk;
   int64_t c1 = c0 + chunk;
   if (c1 > N) c1 = N;
@@ -224,6 +225,7 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
   uint2 qa8[QTW][KS];    // fp8 queries
   // epilogue: accumulator row 4g+i -> (slot (4g+i)/HI, head (4g+i)%HI)
   const int qs_c = (4 * g) / HI;
+  const int esel = g % GPQ;              // this lane's tile within a group of E emitted together
   float wv[QTW][4];
   uint32_t nvis[QTW];
   int64_t row_c[QTW];
@@ -247,7 +249,7 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) wv[t][i] = qc_ok ? wi[row_c[t] * HI + ((4 * g + i) % HI)] : 0.f;
     nvis[t] = qc_ok ? vis_blocks(q_pos, row_c[t], m, N) : 0u;
-    owner[t] = qc_ok && (g % GPQ) == 0;
+    owner[t] = qc_ok && esel < E;
   }
   __syncthreads();
 
@@ -263,25 +265,33 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
         nxt[u].load(kbase, sbase, key < klast ? key : klast, g, true);
       }
     }
+    // After the head reduction the GPQ lanes of a query slot hold the same score, so E
+    // consecutive tiles are emitted together: lane group e of the slot writes tile u + e.
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      const int64_t key = base + u * 16 + col;
+    for (int u = 0; u < TPW; u += E) {
 #pragma unroll
       for (int t = 0; t < QTW; ++t) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        float vs = 0.f;
 #pragma unroll
-        for (int c = 0; c < KS; ++c) {
-          if constexpr (KIND == KEY_FP8) acc = mfma_fp8(__builtin_bit_cast(long, qa8[t][c]), cur[u].op(c), acc);
-          else acc = mfma_bf16(bit_cast_to<bf16x8>(qa16[t][c]), cur[u].op(c), acc);
+        for (int j = 0; j < E; ++j) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < KS; ++c) {
+            if constexpr (KIND == KEY_FP8)
+              acc = mfma_fp8(__builtin_bit_cast(long, qa8[t][c]), cur[u + j].op(c), acc);
+            else acc = mfma_bf16(bit_cast_to<bf16x8>(qa16[t][c]), cur[u + j].op(c), acc);
+          }
+          float v = wv[t][0] * fmaxf(acc[0], 0.f);
+          v = fmaf(wv[t][1], fmaxf(acc[1], 0.f), v);
+          v = fmaf(wv[t][2], fmaxf(acc[2], 0.f), v);
+          v = fmaf(wv[t][3], fmaxf(acc[3], 0.f), v);
+          if constexpr (GPQ >= 2) v += __shfl_xor(v, 16);
+          if constexpr (GPQ >= 4) v += __shfl_xor(v, 32);
+          vs = (j == esel) ? v : vs;
         }
-        float v = wv[t][0] * fmaxf(acc[0], 0.f);
-        v = fmaf(wv[t][1], fmaxf(acc[1], 0.f), v);
-        v = fmaf(wv[t][2], fmaxf(acc[2], 0.f), v);
-        v = fmaf(wv[t][3], fmaxf(acc[3], 0.f), v);
-        if constexpr (GPQ >= 2) v += __shfl_xor(v, 16);
-        if constexpr (GPQ >= 4) v += __shfl_xor(v, 32);
+        const int64_t key = base + (u + esel) * 16 + col;
         if (owner[t] && key < c1)
-          emit_score(scores, hist_l + (t * QPT + qs_c) * kHistWords, row_c[t], sstride, N, key, nvis[t], v);
+          emit_score(scores, hist_l + (t * QPT + qs_c) * kHistWords, row_c[t], sstride, N, key, nvis[t], vs);
       }
     }
 #pragma unroll
@@ -358,7 +368,7 @@ __device__ __forceinline__ void threshold_bin(const uint32_t* __restrict__ hr, u
 // the bin are appended to this range's own slice of the candidate buffer as composite
 // keys (score key << 32 | ~index: equal scores order the lower index first).
 constexpr int kScanThreads = 256;
-constexpr int kScanKeys = 8192;                              // 8 float4 loads per thread
+constexpr int kScanKeys = 2048;                              // 2 float4 loads per thread
 constexpr int kFinThreads = 1024;
 constexpr int kLdsBitmapKeys = 1 << 18;                      // bitmap kept in LDS by pass 2
 constexpr int kCandCap = 4096;                               // candidates staged in LDS by pass 2

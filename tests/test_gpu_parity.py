@@ -297,6 +297,25 @@ def test_index_topk_many_candidates(N):
     check_topk(idx[0, 1], s_ref[0, 1], int(method.visible_blocks(pos, m, N)[0, 1]), k)
 
 
+def test_index_topk_very_long_rows():
+    """Rows of more than 2^21 visible blocks: more key ranges in the selection's first pass
+    than the second pass indexes directly, so candidates of the last ranges are found by
+    walking the range counts."""
+    B, Q, HI, DI, N, m, k = 1, 2, 4, 32, 2200000, 4, 2048
+    qi = synth.normal(233, synth.QI, (B, Q, HI, DI))
+    ki = synth.normal(233, synth.KI, (B, N, DI))
+    w = synth.uniform(233, synth.WI, (B, Q, HI))
+    pos = np.array([[4 * N - 1, 4 * 2150000 + 1]], dtype=np.int32)
+    qd, qbits = dev_bf16(qi)
+    kd, kbits = dev_bf16(ki)
+    idx = L.csa_index_topk(qd, dev(w), kd, dev(pos), m, k).cpu().numpy()
+    s_ref = _scores_oracle(codecs.decode_bf16(qbits), w, codecs.decode_bf16(kbits), pos, m)
+    nvis = method.visible_blocks(pos, m, N)
+    for q in range(Q):
+        assert check_topk(idx[0, q], s_ref[0, q], int(nvis[0, q]), k) <= 2
+    assert idx[0, 0].max() >= 2095104                     # the tail ranges contribute
+
+
 def test_index_topk_f32_is_deterministic():
     cfg = 240
     B, Q, HI, DI, N, m, k = 1, 1, 4, 64, 1024, 4, 64
