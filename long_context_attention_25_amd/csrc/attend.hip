@@ -41,9 +41,8 @@ struct KeyRange {
   int64_t n_tot;    // n_c + window rows
 };
 
-__device__ __forceinline__ KeyRange key_range(const AttendArgs& a, int64_t bq) {
-  const int64_t b = bq / a.Q;
-  const int64_t p = a.q_pos[bq];
+// p: position of query bq, wp0: position of window row 0 of its sequence
+__device__ __forceinline__ KeyRange key_range(const AttendArgs& a, int64_t p, int64_t wp0) {
   KeyRange r;
   if (a.csa) {
     r.n_c = a.k;
@@ -51,7 +50,6 @@ __device__ __forceinline__ KeyRange key_range(const AttendArgs& a, int64_t bq) {
     int64_t n = p < 0 ? 0 : (p + 1) / a.m;
     r.n_c = n < a.N ? n : a.N;
   }
-  const int64_t wp0 = a.win_pos0[b];
   int64_t lo = p - a.W + 1 - wp0;
   int64_t hi = p + 1 - wp0;
   if (lo < 0) lo = 0;
@@ -59,6 +57,9 @@ __device__ __forceinline__ KeyRange key_range(const AttendArgs& a, int64_t bq) {
   r.r_lo = lo;
   r.n_tot = r.n_c + (hi > lo ? hi - lo : 0);
   return r;
+}
+__device__ __forceinline__ KeyRange key_range(const AttendArgs& a, int64_t bq) {
+  return key_range(a, a.q_pos[bq], a.win_pos0[bq / a.Q]);
 }
 
 // Row (element offset into kc/vc or kw/vw) of list position `pos`; -1 if the slot is empty.
@@ -162,14 +163,48 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
   constexpr int STB = KTB + VTB;          // one stage: K tile then V tile
   __shared__ __attribute__((aligned(1024))) uint8_t ring[4 * STB];
   __shared__ int32_t list[kMaxCsaChunk];  // the split's index entries
+  __shared__ __attribute__((aligned(16))) uint8_t xchg[DS > 1 ? NT * 16 : 16];   // partial scores
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
   const int64_t bq = blockIdx.y;
   const int64_t b = bq / a.Q;
   const int split = blockIdx.x;
-  const KeyRange kr = key_range(a, bq);
   const int64_t s0 = (int64_t)split * chunk;
+  const int hg = wave % 4, dh = wave / 4;  // head group and output slice
+  const int head = hg * 16 + col;
+  const bool wave_on = hg * 16 < a.H;
+
+  // The loads that do not depend on each other are issued together and waited for once:
+  // the query position, the split's index entries (CSA: list slots s0 .. s0+chunk-1, all
+  // below k <= n_tot), and the workgroup's query rows, copied once into LDS stages 2 and 3
+  // (free until tile 2 is issued).  The copies into LDS are then the only vector-memory
+  // operations in flight in the tile loop.
+  const uint32_t ring_lds = lds_addr(ring);
+  const uint32_t q_lds = ring_lds + 2 * STB;
+  static_assert(kHeads * KSTR <= 2 * STB, "query rows fit in two stages");
+  {
+    const uint16_t* qb = reinterpret_cast<const uint16_t*>(a.q) + bq * a.H * D;
+#pragma unroll
+    for (int i = 0; i < kHeads / NWV; ++i) {
+      const int h = wave + i * NWV;
+      if (h < a.H && lane < LPR) copy16_to_lds(qb + h * D + lane * 8, q_lds + h * KSTR);
+    }
+  }
+  const int32_t qpos = a.q_pos[bq];
+  const int32_t wpos0 = a.win_pos0[b];
+  constexpr int LPT = kMaxCsaChunk / NT;   // index entries per thread
+  int32_t lv[LPT];
+  const int64_t e1 = s0 + chunk < a.k ? s0 + chunk : a.k;
+  if (a.csa) {
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const int64_t p = s0 + tid + u * NT;
+      lv[u] = p < e1 ? a.idx[bq * a.k + p] : -1;
+    }
+  }
+  wait_vmcnt<0>();
+  const KeyRange kr = key_range(a, qpos, wpos0);
   int64_t s1 = s0 + chunk;
   if (s1 > kr.n_tot) s1 = kr.n_tot;
   const int ntile = s1 > s0 ? (int)((s1 - s0 + KT - 1) / KT) : 0;
@@ -180,14 +215,11 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
   const uint16_t* kw = reinterpret_cast<const uint16_t*>(a.kw) + b * a.L * wrs;
   const uint16_t* vw = reinterpret_cast<const uint16_t*>(a.vw) + b * a.L * wrs;
 
-  const int hg = wave % 4, dh = wave / 4;  // head group and output slice
-  const int head = hg * 16 + col;
-  const bool wave_on = hg * 16 < a.H;
-
   // CSA: the split's index entries, once, in LDS (the tile loop issues no other loads)
   if (a.csa) {
-    int64_t e1 = s1 < kr.n_c ? s1 : kr.n_c;
-    for (int64_t p = s0 + tid; p < e1; p += NT) list[p - s0] = a.idx[bq * a.k + p];
+#pragma unroll
+    for (int u = 0; u < LPT; ++u)
+      if (s0 + tid + u * NT < e1) list[tid + u * NT] = lv[u];
   }
   __syncthreads();
 
@@ -221,7 +253,6 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
   };
   // Wave w copies rows w, w+4, ... of the tile; a row is LPR lanes x 16 bytes (the other
   // lanes of a wave are masked off when a row is shorter than a wave).
-  const uint32_t ring_lds = lds_addr(ring);
   auto issue = [&](int stage) {
     const uint32_t kdst = ring_lds + stage * STB;
     const uint32_t vdst = kdst + KTB;
@@ -242,23 +273,26 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
   for (int i = 0; i < NDT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.scale * kLog2e;
-  // per-lane LDS byte offsets: K operand row `col`, chunk g*KS; V^T rows 4g + col/4 at
-  // dims dh*DH + 4(col%4)
-  const int k_off = col * KSTR + g * (D / 4) * 2;
+  // Scores over the head dim are split between the DS waves of a head group: wave slice
+  // dh takes k-steps dh*KSW .. +KSW-1 (dims g*D/4 + 8c .. +7 of lane group g for k-step c)
+  // and the DS partial scores are summed through LDS.
+  constexpr int KSW = KS / DS;
+  // per-lane LDS byte offsets: K operand row `col` at this wave's first k-step; V^T rows
+  // 4g + col/4 at dims dh*DH + 4(col%4)
+  const int k_off = col * KSTR + g * (D / 4) * 2 + dh * KSW * 16;
   const int v_off = (4 * g + (col >> 2)) * VSTR + dh * DH * 2 + (col & 3) * 8;
 
-  uint4 qop[KS];                           // Q^T operands, loaded below
-  auto compute = [&](int stage, uint32_t cur_mask) {
-    if (!wave_on) return;
+  uint4 qop[KSW];                          // Q^T operands, read from LDS below
+  // ---- partial S^T = K . Q^T (16 keys x 16 heads) over this wave's k-steps.  K operands
+  // are read in batches of CB; batch i+1 is issued before the MFMAs of batch i (the
+  // scheduling barriers keep the compiler from pairing each read with its MFMA; two
+  // batches stay within the 15 outstanding LDS reads the counter tracks).  Two
+  // accumulators halve the dependent MFMA chain.
+  auto compute_s = [&](int stage) -> f32x4 {
     const uint8_t* kt_l = ring + stage * STB;
-    const uint8_t* vt_l = kt_l + KTB;
-    // ---- S^T = K . Q^T (16 keys x 16 heads).  K operands are read in batches of CB;
-    // batch i+1 is issued before the MFMAs of batch i (the scheduling barriers keep the
-    // compiler from pairing each read with its MFMA; two batches stay within the 15
-    // outstanding LDS reads the counter tracks).
-    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
-    constexpr int CB = KS < 4 ? KS : 4;
-    constexpr int NB = KS / CB;
+    f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = sa;
+    constexpr int CB = KSW < 4 ? KSW : 4;
+    constexpr int NB = KSW / CB;
     uint4 kv[2][CB];
     auto kread = [&](int buf, int c0) {
 #pragma unroll
@@ -270,11 +304,18 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
       if (bi + 1 < NB) kread((bi + 1) & 1, (bi + 1) * CB);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int c = 0; c < CB; ++c)
-        s = mfma_bf16(bit_cast_to<bf16x8>(kv[bi & 1][c]), bit_cast_to<bf16x8>(qop[bi * CB + c]), s);
+      for (int c = 0; c < CB; ++c) {
+        if ((bi * CB + c) & 1) sb = mfma_bf16(bit_cast_to<bf16x8>(kv[bi & 1][c]), bit_cast_to<bf16x8>(qop[bi * CB + c]), sb);
+        else sa = mfma_bf16(bit_cast_to<bf16x8>(kv[bi & 1][c]), bit_cast_to<bf16x8>(qop[bi * CB + c]), sa);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // ---- softmax (lane holds keys 4g + i of head `head`), lazy rescaling
+    return sa + sb;
+  };
+  // ---- softmax of the full scores (lane holds keys 4g + i of head `head`), lazy
+  // rescaling, then O^T += V^T . P^T
+  auto compute_pv = [&](int stage, uint32_t cur_mask, f32x4 s) {
+    const uint8_t* vt_l = ring + stage * STB + KTB;
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -303,9 +344,9 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
     }
     // P^T operand of the 16x16x16 MFMA: this lane's own keys 4g .. 4g+3 of head `head`
     const v4i16 pb = __builtin_bit_cast(v4i16, make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])));
-    // ---- O^T += V^T . P^T; V^T operands by transposed LDS reads of the row-major tile:
-    // lane p of a 16-lane block addresses key row 4g + p/4 at dims 16dt + 4(p%4) and
-    // receives its own dim (16dt + p) from the four key rows.
+    // V^T operands by transposed LDS reads of the row-major tile: lane p of a 16-lane
+    // block addresses key row 4g + p/4 at dims 16dt + 4(p%4) and receives its own dim
+    // (16dt + p) from the four key rows.
     constexpr int DB = NDT < 4 ? NDT : 4;
     constexpr int ND = NDT / DB;
     v4i16 vt[2][DB];
@@ -327,21 +368,21 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
     }
   };
 
-  // Tile t lives in stage t % 4.  Tiles 0..2 are issued first and this lane's Q^T operands
-  // (head `head`, dims g*D/4 + 8c .. +7 for k-step c) behind them, so that the query
-  // loads overlap the first copies; one wait covers both.  Step t then waits for tile t
-  // (tiles t+1, t+2 stay in flight), passes a barrier (tile t visible to all waves; every
-  // wave is done with tile t-1), issues tile t+3 into the stage of tile t-1 and uses tile t.
+  // Tile t lives in stage t % 4.  Tiles 0 and 1 are issued first; then every wave reads
+  // its Q^T operands (head `head`, dims g*D/4 + 8c .. +7 for k-step c) from stages 2-3,
+  // and after a barrier tile 2 is issued.  Step t then waits for tile t (tiles t+1, t+2
+  // stay in flight), passes a barrier (tile t visible to all waves; every wave is done
+  // with tile t-1), issues tile t+3 into the stage of tile t-1 and uses tile t.
   uint32_t mq0 = 0, mq1 = 0, mq2 = 0;      // masks of tiles t, t+1, t+2
   if (ntile > 0) { tile_ptrs(0); mq0 = vmask; issue(0); }
   if (ntile > 1) { tile_ptrs(1); mq1 = vmask; issue(1); }
-  if (ntile > 2) { tile_ptrs(2); mq2 = vmask; issue(2); }
   {
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + (bq * a.H + (wave_on ? head : 0)) * D + g * (D / 4);
+    const uint8_t* ql = ring + 2 * STB + (wave_on ? head : 0) * KSTR + g * (D / 4) * 2 + dh * KSW * 16;
 #pragma unroll
-    for (int c = 0; c < KS; ++c) qop[c] = gload_u4(qp + 8 * c);
+    for (int c = 0; c < KSW; ++c) qop[c] = *reinterpret_cast<const uint4*>(ql + c * 16);
   }
-  wait_vmcnt<0>();
+  tile_barrier();
+  if (ntile > 2) { tile_ptrs(2); mq2 = vmask; issue(2); }
   for (int t = 0; t < ntile; ++t) {
     if (t + 2 < ntile) wait_vmcnt<2 * NL>();
     else if (t + 1 < ntile) wait_vmcnt<NL>();
@@ -353,7 +394,22 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
       mq3 = vmask;
       issue((t + 3) & 3);
     }
-    compute(t & 3, mq0);
+    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (wave_on) sc = compute_s(t & 3);
+    if constexpr (DS > 1) {
+      // partial scores of the DS slices of a head group (waves hg + 4j), summed in the
+      // same order by every slice so that all of them see identical scores
+      f32x4* xs = reinterpret_cast<f32x4*>(xchg);
+      if (wave_on) xs[wave * kWave + lane] = sc;
+      tile_barrier();
+      if (wave_on) {
+        f32x4 tot = xs[hg * kWave + lane];
+#pragma unroll
+        for (int j = 1; j < DS; ++j) tot += xs[(hg + 4 * j) * kWave + lane];
+        sc = tot;
+      }
+    }
+    if (wave_on) compute_pv(t & 3, mq0, sc);
     mq0 = mq1;
     mq1 = mq2;
     mq2 = mq3;
