@@ -69,12 +69,12 @@ KERNEL_BYTES = {
 # the counter's reading for a 256 MiB device copy (see profiles/).  An entry is used only
 # while the kernel source it was measured on is unchanged (sha256 of the file).
 MEASURED_TRAFFIC = {
-    "index_mfma_kernel": {"bytes_per_launch": 151444422,
-                          "source_sha256": "955917201fd1ffb9090885d6bda532738787cc148dbdb50a96a05b197c0388a8"},
-    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 155904324,
-                                 "source_sha256": "6f80b45ffb6476c4df5cb2543d4ec217da9ed79ea6f29511bd5e0cd90a554ee3"},
-    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32726487,
-                                 "source_sha256": "6f80b45ffb6476c4df5cb2543d4ec217da9ed79ea6f29511bd5e0cd90a554ee3"},
+    "index_mfma_kernel": {"bytes_per_launch": 151636293,
+                          "source_sha256": "374da6ea153d68ec96e0964acf4eb460daf4aaea93d3839b96bfa2e75617675f"},
+    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 155915454,
+                                 "source_sha256": "dea3069f284cfa63a5ab0b38e502bf00607fed8446dca339c6313d97a7be281b"},
+    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32737437,
+                                 "source_sha256": "dea3069f284cfa63a5ab0b38e502bf00607fed8446dca339c6313d97a7be281b"},
 }
 
 
