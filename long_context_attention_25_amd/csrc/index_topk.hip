@@ -305,18 +305,25 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
 }
 
 // ------------------------------------------------------------------ selection
+// Inclusive prefix sum over the 64 lanes of a wave: row shifts within each 16-lane row,
+// then the last lane of a row is broadcast into the following rows.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return v;
+}
+
 // Block-wide exclusive prefix sum for NT threads (NT / 64 waves); `tmp` holds NT / 64
 // words of LDS.  Returns the exclusive prefix and writes the total to *total.
 template <int NT>
 __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
   constexpr int NW = NT / kWave;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t t = __shfl_up(incl, o);
-    if (lane >= o) incl += t;
-  }
+  const uint32_t incl = wave_incl_scan(v);
   if (lane == 63) tmp[wave] = incl;
   __syncthreads();
   uint32_t base = 0, tot = 0;
@@ -366,12 +373,14 @@ __device__ __forceinline__ void threshold_bin(const uint32_t* __restrict__ hr, u
 // Selection, pass 1 (all rows x key ranges of kScanKeys): keys above the threshold bin
 // get their bit in the row's key bitmap (whole 32-bit words, plain stores); keys inside
 // the bin are appended to this range's own slice of the candidate buffer as composite
-// keys (score key << 32 | ~index: equal scores order the lower index first).
+// keys (score key << 32 | ~index: equal scores order the lower index first), and the
+// range's candidate count is stored.
 constexpr int kScanThreads = 256;
 constexpr int kScanKeys = 2048;                              // 2 float4 loads per thread
 constexpr int kFinThreads = 1024;
 constexpr int kLdsBitmapKeys = 1 << 18;                      // bitmap kept in LDS by pass 2
 constexpr int kCandCap = 4096;                               // candidates staged in LDS by pass 2
+constexpr int kRadixBits = 12;                               // digit width of pass 2's radix select
 
 __global__ __launch_bounds__(kScanThreads) void select_scan_kernel(
     const float* __restrict__ scores, const uint32_t* __restrict__ hist_g, uint32_t* __restrict__ bitmap_g,
@@ -446,114 +455,28 @@ __global__ __launch_bounds__(kScanThreads) void select_scan_kernel(
   if (tid == 0) ccount[row * nch + blockIdx.x] = misc[2];
 }
 
-// The last steps of a row's selection, shared by the two selection paths: radix select
-// (8-bit digits, below the histogram prefix) of the `need` largest composites among the c
-// candidates (cand_at(f) returns candidate f), their bits added to the key bitmap, and
-// compaction of the bitmap into ascending indices followed by -1 padding.  Every thread of
-// the NT-thread workgroup calls it.
-template <int NT, bool kLdsBits, typename CandAt>
-__device__ __forceinline__ void finish_row(uint32_t c, uint32_t need, uint32_t tbin, CandAt cand_at,
-                                           uint32_t* bits, int64_t wn, int k, int32_t* __restrict__ orow,
-                                           float* __restrict__ srow, const float* __restrict__ sc, uint32_t* tmp,
-                                           uint32_t* h256, uint32_t* misc) {
-  const int tid = threadIdx.x;
-#define DSV4_FOR_CAND(body)                          \
-  for (uint32_t f_ = tid; f_ < c; f_ += NT) {        \
-    const uint64_t comp = cand_at(f_);               \
-    body                                             \
-  }
-  uint64_t thr = 0;                                          // select composites >= thr
-  if (need < c) {
-    uint64_t prefix = (uint64_t)tbin << (64 - kHistBits);
-    int hi = 64 - kHistBits;                                 // bits [hi-1 : 0] still open
-    while (true) {
-      const int wd = hi < 8 ? hi : 8;
-      const int sh = hi - wd;
-      if (tid < 256) h256[tid] = 0u;
-      __syncthreads();
-      DSV4_FOR_CAND(if ((comp >> hi) == (prefix >> hi)) atomicAdd(&h256[(comp >> sh) & ((1u << wd) - 1u)], 1u);)
-      __syncthreads();
-      const uint32_t hc = (tid < (1 << wd)) ? h256[tid] : 0u;
-      uint32_t tot;
-      const uint32_t ex = block_scan<NT>(hc, tmp, &tot);
-      const uint32_t gt = tot - ex - hc;                     // candidates with a larger digit
-      if (tid < (1 << wd) && gt < need && need <= gt + hc) {
-        misc[4] = tid;
-        misc[5] = gt;
-        misc[6] = hc;
-      }
-      __syncthreads();
-      need -= misc[5];
-      prefix |= (uint64_t)misc[4] << sh;
-      const bool done = misc[6] == need || sh == 0;
-      hi = sh;
-      if (done) break;
-    }
-    thr = prefix;
-  }
-  DSV4_FOR_CAND(if (comp >= thr) {
-    const uint32_t j = ~(uint32_t)comp;
-    atomicOr(&bits[j >> 5], 1u << (j & 31));
-  })
-#undef DSV4_FOR_CAND
-  __threadfence_block();
-  __syncthreads();
-
-  // compaction: thread t takes 8 consecutive words (256 keys) per round
-  uint32_t base_off = 0;
-  for (int64_t r0 = 0; r0 < wn; r0 += 8 * NT) {
-    const int64_t w0 = r0 + (int64_t)tid * 8;
-    uint32_t wv[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if constexpr (kLdsBits) wv[i] = w0 + i < wn ? bits[w0 + i] : 0u;
-      else wv[i] = w0 + i < wn ? __hip_atomic_load(&bits[w0 + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
-    }
-    uint32_t cnt = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) cnt += __popc(wv[i]);
-    uint32_t rtot;
-    uint32_t off = base_off + block_scan<NT>(cnt, tmp, &rtot);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t b_ = wv[i];
-      while (b_) {
-        const int bpos = __ffs(b_) - 1;
-        b_ &= b_ - 1;
-        const int64_t j = (w0 + i) * 32 + bpos;
-        if (off < (uint32_t)k) {
-          orow[off] = (int32_t)j;
-          if (srow) srow[off] = sc[j];
-        }
-        ++off;
-      }
-    }
-    base_off += rtot;
-  }
-  for (int64_t p = (int64_t)base_off + tid; p < k; p += NT) {
-    orow[p] = -1;
-    if (srow) srow[p] = -INFINITY;
-  }
-}
-
-// Selection, pass 2 (one workgroup per row): radix-selects (8-bit digits) the
-// kk - #(bin > b*) largest composites among the candidates, adds their bits to the
-// bitmap and compacts it into ascending indices, then -1 padding.
+// Selection, pass 2 (one workgroup per row): the threshold, the per-range candidate
+// counts and the row's bitmap are loaded in one round, the candidates (gathered from the
+// range slices) in a second; a radix select (kRadixBits-bit digits below the histogram
+// prefix) finds the kk - #(bin > b*) largest candidates, their bits are added to the
+// bitmap, and the bitmap is compacted into ascending indices followed by -1 padding.
 // kLdsBits: the row's bitmap is copied into LDS (N <= kLdsBitmapKeys).
 template <bool kLdsBits>
 __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
-    const float* __restrict__ scores, uint32_t* __restrict__ bitmap_g,
-    const uint64_t* __restrict__ cand_g, const uint32_t* __restrict__ ccount, const uint32_t* __restrict__ thr,
-    const int32_t* __restrict__ q_pos, int64_t N, int64_t sstride, int64_t words, int m, int k, int nch,
-    int32_t* __restrict__ out_idx,
+    const float* __restrict__ scores, uint32_t* __restrict__ bitmap_g, const uint64_t* __restrict__ cand_g,
+    const uint32_t* __restrict__ ccount, const uint32_t* __restrict__ thr, const int32_t* __restrict__ q_pos,
+    int64_t N, int64_t sstride, int64_t words, int m, int k, int nch, int32_t* __restrict__ out_idx,
     float* __restrict__ out_score) {
   constexpr int NT = kFinThreads;
+  constexpr int kBins = 1 << kRadixBits;
+  constexpr int BPT = kBins / NT;
+  static_assert(BPT >= 1 && kBins % NT == 0, "digit bins per thread");
   __shared__ uint32_t bits_l[kLdsBits ? kLdsBitmapKeys / 32 : 1];
   __shared__ uint64_t cand_l[kCandCap];
-  __shared__ uint32_t pre[kFinThreads + 1];                  // candidate offsets of the ranges
+  __shared__ uint32_t pre[NT + 1];                           // candidate offsets of the ranges
+  __shared__ uint32_t hbin[kBins];
   __shared__ uint32_t tmp[NT / kWave];
-  __shared__ uint32_t h256[256];
-  __shared__ uint32_t misc[8];
+  __shared__ uint32_t misc[4];
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
   const uint32_t n = vis_blocks(q_pos, row, m, N);
@@ -570,21 +493,20 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
     }
     return;
   }
-  // threshold bin and #keys above it, as pass 1 found them from the row's histogram
+  // round 1: threshold, range counts (the first NT ranges), bitmap
+  const int nrange = (int)(((int64_t)n + kScanKeys - 1) / kScanKeys);
   const uint2 th = *reinterpret_cast<const uint2*>(thr + row * 2);
-  const uint32_t tbin = th.x, cnt_above = th.y;
+  const uint32_t cnt0 = tid < nrange ? ccount[row * nch + tid] : 0u;
   if constexpr (kLdsBits) {
     for (int64_t w = (int64_t)tid * 4; w < wn; w += (int64_t)NT * 4) {
       const uint4 x = *reinterpret_cast<const uint4*>(gbits + w);   // rows are 16-byte padded
       *reinterpret_cast<uint4*>(bits_l + w) = x;
     }
   }
-  const int nrange = (int)(((int64_t)n + kScanKeys - 1) / kScanKeys);
-  // candidate offsets per range (ranges beyond n hold none); more than NT ranges are
-  // summed in rounds
+  // candidate offsets per range (more than NT ranges are summed in rounds)
   uint32_t run = 0;
   for (int r0 = 0; r0 < nrange; r0 += NT) {
-    const uint32_t cnt = r0 + tid < nrange ? ccount[row * nch + r0 + tid] : 0u;
+    const uint32_t cnt = r0 == 0 ? cnt0 : (r0 + tid < nrange ? ccount[row * nch + r0 + tid] : 0u);
     uint32_t tot;
     const uint32_t ex = block_scan<NT>(cnt, tmp, &tot);
     if (r0 + tid < nrange && r0 + tid < NT) pre[r0 + tid] = run + ex;
@@ -614,6 +536,7 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
     }
     return cand_g[row * N + r * kScanKeys + (f - base)];
   };
+  // round 2: candidates into LDS
   {
     constexpr int kPer = kCandCap / NT;
     uint64_t vals[kPer];
@@ -629,10 +552,110 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
     }
   }
   __syncthreads();
+  auto cand = [&](uint32_t f) -> uint64_t { return f < (uint32_t)kCandCap ? cand_l[f] : cand_at(f); };
+
+  // radix select among the candidates: composites >= tsel are taken
+  uint64_t tsel = 0;
+  uint32_t need = kk - th.y;
+  if (need < c) {
+    uint64_t prefix = (uint64_t)th.x << (64 - kHistBits);
+    int hi = 64 - kHistBits;                                 // bits [hi-1 : 0] still open
+    while (true) {
+      const int wd = hi < kRadixBits ? hi : kRadixBits;
+      const int sh = hi - wd;
+      for (int i = tid; i < kBins; i += NT) hbin[i] = 0u;
+      __syncthreads();
+      for (uint32_t f = tid; f < c; f += NT) {
+        const uint64_t comp = cand(f);
+        if ((comp >> hi) == (prefix >> hi)) atomicAdd(&hbin[(comp >> sh) & ((1u << wd) - 1u)], 1u);
+      }
+      __syncthreads();
+      // thread t holds digits nd-1-(BPT t + i), i = 0 .. BPT-1 (descending), so that the
+      // exclusive prefix counts the candidates with larger digits
+      const int nd = 1 << wd;
+      uint32_t hv[BPT];
+      uint32_t tsum = 0;
+#pragma unroll
+      for (int i = 0; i < BPT; ++i) {
+        const int d = BPT * tid + i;
+        hv[i] = d < nd ? hbin[nd - 1 - d] : 0u;
+        tsum += hv[i];
+      }
+      uint32_t tot;
+      const uint32_t ex = block_scan<NT>(tsum, tmp, &tot);
+      if (ex < need && need <= ex + tsum) {
+        uint32_t acc = ex;
+#pragma unroll
+        for (int i = 0; i < BPT; ++i) {
+          if (acc < need && need <= acc + hv[i]) {
+            misc[0] = (uint32_t)(nd - 1 - (BPT * tid + i));
+            misc[1] = acc;
+            misc[2] = hv[i];
+          }
+          acc += hv[i];
+        }
+      }
+      __syncthreads();
+      need -= misc[1];
+      prefix |= (uint64_t)misc[0] << sh;
+      const bool done = misc[2] == need || sh == 0;
+      hi = sh;
+      if (done) break;
+    }
+    tsel = prefix;
+  }
   uint32_t* bits = kLdsBits ? bits_l : gbits;
-  finish_row<NT, kLdsBits>(c, kk - cnt_above, tbin,
-                           [&](uint32_t f) -> uint64_t { return f < (uint32_t)kCandCap ? cand_l[f] : cand_at(f); },
-                           bits, wn, k, orow, srow, sc, tmp, h256, misc);
+  for (uint32_t f = tid; f < c; f += NT) {
+    const uint64_t comp = cand(f);
+    if (comp >= tsel) {
+      const uint32_t j = ~(uint32_t)comp;
+      atomicOr(&bits[j >> 5], 1u << (j & 31));
+    }
+  }
+  __threadfence_block();
+  __syncthreads();
+
+  // compaction: thread t takes 8 consecutive words (256 keys) per round
+  uint32_t base_off = 0;
+  for (int64_t r0 = 0; r0 < wn; r0 += 8 * NT) {
+    const int64_t w0 = r0 + (int64_t)tid * 8;
+    uint32_t wv[8];
+    if (kLdsBits && w0 + 8 <= wn) {
+      const uint4 x0 = *reinterpret_cast<const uint4*>(bits + w0);
+      const uint4 x1 = *reinterpret_cast<const uint4*>(bits + w0 + 4);
+      wv[0] = x0.x; wv[1] = x0.y; wv[2] = x0.z; wv[3] = x0.w;
+      wv[4] = x1.x; wv[5] = x1.y; wv[6] = x1.z; wv[7] = x1.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if constexpr (kLdsBits) wv[i] = w0 + i < wn ? bits[w0 + i] : 0u;
+        else wv[i] = w0 + i < wn ? __hip_atomic_load(&bits[w0 + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+      }
+    }
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cnt += __popc(wv[i]);
+    uint32_t rtot;
+    uint32_t off = base_off + block_scan<NT>(cnt, tmp, &rtot);
+    for (int i = 0; i < 8; ++i) {
+      uint32_t b_ = wv[i];
+      while (b_) {
+        const int bpos = __ffs(b_) - 1;
+        b_ &= b_ - 1;
+        const int64_t j = (w0 + i) * 32 + bpos;
+        if (off < (uint32_t)k) {
+          orow[off] = (int32_t)j;
+          if (srow) srow[off] = sc[j];
+        }
+        ++off;
+      }
+    }
+    base_off += rtot;
+  }
+  for (int64_t p = (int64_t)base_off + tid; p < k; p += NT) {
+    orow[p] = -1;
+    if (srow) srow[p] = -INFINITY;
+  }
 }
 
 template <int KIND, int DI, int HI, int QTW>
