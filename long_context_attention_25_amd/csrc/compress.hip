@@ -44,121 +44,140 @@ struct XVec<uint16_t> {   // bf16
   }
 };
 
+// Running softmax-weighted sum over some rows of a block: with z_j = gate_j + bias_j,
+// M = max z_j, s = sum exp(z_j - M) and a = sum exp(z_j - M) x_j; the pooled entry is
+// a / s.  Two states of the same block combine exactly (up to rounding) by rescaling
+// both to the larger maximum.
+template <int V>
+struct PoolState {
+  float M, s, a[V];
+  __device__ void init() {
+    M = -INFINITY;
+    s = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) a[v] = 0.f;
+  }
+  __device__ void add_rows(const float* z, const float (*x)[V], int n) {   // n <= 4 rows
+    float mz = M;
+    for (int u = 0; u < n; ++u) mz = fmaxf(mz, z[u]);
+    const float f = M == -INFINITY ? 0.f : expf(M - mz);
+    s *= f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) a[v] *= f;
+    for (int u = 0; u < n; ++u) {
+      const float e = expf(z[u] - mz);
+      s += e;
+#pragma unroll
+      for (int v = 0; v < V; ++v) a[v] = fmaf(e, x[u][v], a[v]);
+    }
+    M = mz;
+  }
+  __device__ void combine(float oM, float os, const float* oa) {
+    const float mz = fmaxf(M, oM);
+    if (mz == -INFINITY) return;                            // both empty
+    const float f = expf(M - mz), g = expf(oM - mz);
+    s = s * f + os * g;
+#pragma unroll
+    for (int v = 0; v < V; ++v) a[v] = a[v] * f + oa[v] * g;
+    M = mz;
+  }
+};
+
 // YDT: 0 f32, 1 bf16, 2 fp8 e4m3, 3 MXFP4
+// Thread = (row slot, channel vector): slot r0 of a block takes rows r0, r0 + spb, ...
+// and keeps a running state; the spb slots of a block are then combined.  When lpr and
+// spb are powers of two the slots of a block sit at lane distances lpr, 2 lpr, ... and are
+// combined by a butterfly within the wave, then (blocks wider than a wave) across waves
+// through LDS; otherwise every state goes through LDS and the writer combines them.
 template <typename TX, int YDT>
 __global__ __launch_bounds__(kThreads) void compress_kernel(
     const TX* __restrict__ x, const float* __restrict__ gate, const float* __restrict__ bias,
     int64_t T, int C, int m, int64_t nb_per_b, int64_t total_blocks, int64_t x_bs, int64_t y_bs,
     void* __restrict__ y, uint8_t* __restrict__ ysc, int lpr, int spb, int bpw, int cs) {
   constexpr int V = XVec<TX>::N;
-  extern __shared__ float smem[];                      // weights [bpw*m] then partials [256*V]
-  float* wts = smem;
-  float* part = smem + bpw * m;
+  constexpr int NW = kThreads / kWave;
+  __shared__ float part[kThreads * (V + 2)];          // states crossing waves (or all states)
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int64_t blk0 = (int64_t)(blockIdx.x / cs) * bpw;   // cs workgroups share a block group,
   const int slice = blockIdx.x % cs;                         // each on lpr of its channel vectors
 
-  // ---- this thread's first rows (up to 4) are loaded before the weights are computed,
-  // so that the two memory round trips overlap
   const int rs_total = kThreads / lpr;
   const int slot = tid / lpr, cv = tid % lpr + slice * lpr;
   const int bi = slot / spb, r0 = slot % spb;
   const bool active = slot < rs_total && bi < bpw && blk0 + bi < total_blocks;
-  const TX* xb = nullptr;
-  float xf[4][V];
+  PoolState<V> st;
+  st.init();
   if (active) {
-    int64_t blk = blk0 + bi;
-    int64_t b = blk / nb_per_b, i = blk % nb_per_b;
-    xb = x + ((b * x_bs + i * m) * (int64_t)C) + (int64_t)cv * V;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (r0 + u * spb < m) XVec<TX>::load(xb + (int64_t)(r0 + u * spb) * C, xf[u]);
-  }
-
-  // ---- softmax weights of each block handled here, one wave per block
-  for (int wi = wave; wi < bpw; wi += kThreads / kWave) {
-    int64_t blk = blk0 + wi;
-    if (blk >= total_blocks) break;
-    int64_t b = blk / nb_per_b, i = blk % nb_per_b;
+    const int64_t blk = blk0 + bi;
+    const int64_t b = blk / nb_per_b, i = blk % nb_per_b;
+    const TX* xb = x + ((b * x_bs + i * m) * (int64_t)C) + (int64_t)cv * V;
     const float* g = gate + b * T + i * m;
-    float mx = -INFINITY;
-    for (int j = lane; j < m; j += kWave) {
-      float z = g[j] + bias[j];
-      wts[wi * m + j] = z;
-      mx = fmaxf(mx, z);
-    }
-    mx = wave_max(mx);
-    float sum = 0.f;
-    for (int j = lane; j < m; j += kWave) {
-      float e = expf(wts[wi * m + j] - mx);
-      wts[wi * m + j] = e;
-      sum += e;
-    }
-    sum = wave_sum(sum);
-    float inv = 1.0f / sum;
-    for (int j = lane; j < m; j += kWave) wts[wi * m + j] *= inv;
-  }
-  __syncthreads();
-
-  // ---- weighted row sums: thread = (row slot, channel vector)
-  float acc[V];
-#pragma unroll
-  for (int v = 0; v < V; ++v) acc[v] = 0.f;
-  if (active) {
-    const float* wb = wts + bi * m;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (r0 + u * spb < m) {
-        const float w = wb[r0 + u * spb];
-#pragma unroll
-        for (int v = 0; v < V; ++v) acc[v] = fmaf(w, xf[u][v], acc[v]);
-      }
-    }
-    int j = r0 + 4 * spb;
-    for (; j + 3 * spb < m; j += 4 * spb) {
+    // rows r0, r0 + spb, ... in groups of up to 4 (row and gate loads of a group together)
+    for (int j = r0; j < m; j += 4 * spb) {
+      float z[4];
       float xv[4][V];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) XVec<TX>::load(xb + (int64_t)(j + u * spb) * C, xv[u]);
+      int n = 0;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        float w = wb[j + u * spb];
-#pragma unroll
-        for (int v = 0; v < V; ++v) acc[v] = fmaf(w, xv[u][v], acc[v]);
+        const int r = j + u * spb;
+        if (r < m) {
+          XVec<TX>::load(xb + (int64_t)r * C, xv[u]);
+          z[u] = g[r] + bias[r];
+          n = u + 1;
+        }
       }
-    }
-    for (; j < m; j += spb) {
-      float xv[V];
-      XVec<TX>::load(xb + (int64_t)j * C, xv);
-      float w = wb[j];
-#pragma unroll
-      for (int v = 0; v < V; ++v) acc[v] = fmaf(w, xv[v], acc[v]);
+      st.add_rows(z, xv, n);
     }
   }
-  if (spb > 1) {
-    // combine the spb row slots of a block: a halving tree when spb is a power of two
+  const bool pow2 = (lpr & (lpr - 1)) == 0 && (spb & (spb - 1)) == 0;
+  if (pow2) {
+    // butterfly over the slot bits inside the wave
+    for (int d = lpr; d < kWave && d < lpr * spb; d <<= 1) {
+      const float oM = __shfl_xor(st.M, d), os = __shfl_xor(st.s, d);
+      float oa[V];
 #pragma unroll
-    for (int v = 0; v < V; ++v) part[tid * V + v] = acc[v];
-    __syncthreads();
-    if ((spb & (spb - 1)) == 0) {
-      for (int h = spb / 2; h >= 1; h >>= 1) {
-        if (active && r0 < h) {
-          const float* p = part + (tid + h * lpr) * V;
+      for (int v = 0; v < V; ++v) oa[v] = __shfl_xor(st.a[v], d);
+      st.combine(oM, os, oa);
+    }
+    if (lpr * spb > kWave) {
+      // blocks span lpr*spb/64 waves: lanes < lpr of each wave hold the wave's state
+      if (lane < lpr) {
+        float* p = part + (wave * kWave + lane) * (V + 2);
+        p[0] = st.M;
+        p[1] = st.s;
 #pragma unroll
-          for (int v = 0; v < V; ++v) acc[v] += p[v];
-#pragma unroll
-          for (int v = 0; v < V; ++v) part[tid * V + v] = acc[v];
-        }
-        __syncthreads();
+        for (int v = 0; v < V; ++v) p[2 + v] = st.a[v];
       }
-    } else if (active && r0 == 0) {
-      for (int r = 1; r < spb; ++r) {
-        const float* p = part + (tid + r * lpr) * V;
-#pragma unroll
-        for (int v = 0; v < V; ++v) acc[v] += p[v];
+      __syncthreads();
+      const int wpb = lpr * spb / kWave;
+      if (active && r0 == 0) {
+        for (int w = 1; w < wpb && wave + w < NW; ++w) {
+          const float* p = part + ((wave + w) * kWave + lane) * (V + 2);
+          st.combine(p[0], p[1], p + 2);
+        }
       }
     }
+  } else {
+    float* p = part + tid * (V + 2);
+    p[0] = st.M;
+    p[1] = st.s;
+#pragma unroll
+    for (int v = 0; v < V; ++v) p[2 + v] = st.a[v];
+    __syncthreads();
+    if (active && r0 == 0) {
+      for (int r = 1; r < spb; ++r) {
+        const float* q = part + (tid + r * lpr) * (V + 2);
+        st.combine(q[0], q[1], q + 2);
+      }
+    }
+  }
+  float acc[V];
+  {
+    const float inv = st.s > 0.f ? 1.f / st.s : 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc[v] = st.a[v] * inv;
   }
   const bool writer = active && r0 == 0;
 
@@ -235,8 +254,7 @@ hipError_t launch_t(const CompressArgs& a, hipStream_t st) {
   const int spb = a.m < rs ? a.m : rs;
   const int bpw = rs / spb;
   const int64_t grid = ((total + bpw - 1) / bpw) * cs;
-  size_t smem = sizeof(float) * ((size_t)bpw * a.m + (size_t)kThreads * V);
-  DSV4_LAUNCH_MAIN((compress_kernel<TX, YDT>), dim3((unsigned)grid), dim3(kThreads), smem, st,
+  DSV4_LAUNCH_MAIN((compress_kernel<TX, YDT>), dim3((unsigned)grid), dim3(kThreads), 0, st,
                    reinterpret_cast<const TX*>(a.x), a.gate, a.bias, a.T, (int)a.C, a.m, nb, total,
                    a.x_bs, a.y_bs, a.y, a.y_scale, lpr, spb, bpw, cs);
   return hipGetLastError();
