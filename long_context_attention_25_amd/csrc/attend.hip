@@ -108,6 +108,11 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds) {
                "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory", "m0");
 }
+// A load through the constant address space: with a uniform address the compiler emits a
+// scalar load, which the vector-memory counter does not track.
+__device__ __forceinline__ int32_t load_uniform(const int32_t* p) {
+  return *reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(reinterpret_cast<uintptr_t>(p));
+}
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p);
 }
@@ -191,29 +196,71 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
       if (h < a.H && lane < LPR) copy16_to_lds(qb + h * D + lane * 8, q_lds + h * KSTR);
     }
   }
-  const int32_t qpos = a.q_pos[bq];
-  const int32_t wpos0 = a.win_pos0[b];
+  const int64_t krs = a.kv_rs, wrs = a.w_rs;
+  const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.kc) + b * a.kv_bs * krs;
+  const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.vc) + b * a.kv_bs * krs;
+  const uint16_t* kw = reinterpret_cast<const uint16_t*>(a.kw) + b * a.L * wrs;
+  const uint16_t* vw = reinterpret_cast<const uint16_t*>(a.vw) + b * a.L * wrs;
+  // Row pointers of a tile for key (lane % 16), set by tile_ptrs / spec_ptrs below.
+  const uint16_t* my_kp;
+  const uint16_t* my_vp;
+  uint32_t vmask = 0;                       // validity of the tile's 16 keys
+  // Wave w copies rows w, w+4, ... of the tile; a row is LPR lanes x 16 bytes (the other
+  // lanes of a wave are masked off when a row is shorter than a wave).
+  auto issue = [&](int stage) {
+    const uint32_t kdst = ring_lds + stage * STB;
+    const uint32_t vdst = kdst + KTB;
+    const int j = lane / LPR;              // 0 unless LPR < 64
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int r = wave + i * NWV;
+      const int off = (lane % LPR) * 8;
+      if (j == 0) {
+        copy16_to_lds(lane_ptr<true>(my_kp, r) + off, kdst + r * KSTR);
+        copy16_to_lds(lane_ptr<true>(my_vp, r) + off, vdst + r * VSTR);
+      }
+    }
+  };
+
+  // HCA: tiles 0 and 1 are issued before the query position is known, as the compressed
+  // rows s0 + ... (the rows they are, unless the split starts near the end of the visible
+  // entries); they are checked below and issued again when wrong.
+  const bool spec = !a.csa && a.N > 0;
+  auto spec_ptrs = [&](int t) {
+    int64_t j = s0 + (int64_t)t * KT + (lane & (KT - 1));
+    if (j > a.N - 1) j = a.N - 1;
+    my_kp = kc + j * krs;
+    my_vp = vc + j * krs;
+  };
+  if (spec) {
+    spec_ptrs(0);
+    issue(0);
+    spec_ptrs(1);
+    issue(1);
+  }
+  const int32_t qpos = load_uniform(a.q_pos + bq);     // scalar loads: not counted by vmcnt
+  const int32_t wpos0 = load_uniform(a.win_pos0 + b);
   constexpr int LPT = kMaxCsaChunk / NT;   // index entries per thread
   int32_t lv[LPT];
   const int64_t e1 = s0 + chunk < a.k ? s0 + chunk : a.k;
+  // (each branch ends with its own wait, so that no load of one branch is seen as pending
+  // in another)
   if (a.csa) {
 #pragma unroll
     for (int u = 0; u < LPT; ++u) {
       const int64_t p = s0 + tid + u * NT;
       lv[u] = p < e1 ? a.idx[bq * a.k + p] : -1;
     }
+    wait_vmcnt<0>();
+  } else if (spec) {
+    wait_vmcnt<2 * NL>();                   // the query rows (issued first) have landed
+  } else {
+    wait_vmcnt<0>();
   }
-  wait_vmcnt<0>();
   const KeyRange kr = key_range(a, qpos, wpos0);
   int64_t s1 = s0 + chunk;
   if (s1 > kr.n_tot) s1 = kr.n_tot;
   const int ntile = s1 > s0 ? (int)((s1 - s0 + KT - 1) / KT) : 0;
-
-  const int64_t krs = a.kv_rs, wrs = a.w_rs;
-  const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.kc) + b * a.kv_bs * krs;
-  const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.vc) + b * a.kv_bs * krs;
-  const uint16_t* kw = reinterpret_cast<const uint16_t*>(a.kw) + b * a.L * wrs;
-  const uint16_t* vw = reinterpret_cast<const uint16_t*>(a.vw) + b * a.L * wrs;
 
   // CSA: the split's index entries, once, in LDS (the tile loop issues no other loads)
   if (a.csa) {
@@ -223,15 +270,16 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
   }
   __syncthreads();
 
-  // Row pointers of tile t for key (lane % 16); invalid slots point at a real row.
-  const uint16_t* my_kp;
-  const uint16_t* my_vp;
-  uint32_t vmask;                           // validity of the tile's 16 keys
+  // Invalid slots point at a row that holds data (the query's first window row, else the
+  // first compressed row), since their zero weights would not cancel a non-finite value.
+  const bool win_rows = kr.n_tot > kr.n_c;
+  const uint16_t* kdef = win_rows ? kw + kr.r_lo * wrs : kc;
+  const uint16_t* vdef = win_rows ? vw + kr.r_lo * wrs : vc;
   auto tile_ptrs = [&](int t) {
     const int64_t pos = s0 + (int64_t)t * KT + (lane & (KT - 1));
     bool ok = false;
-    const uint16_t* kp = a.N > 0 ? kc : kw;
-    const uint16_t* vp = a.N > 0 ? vc : vw;
+    const uint16_t* kp = kdef;
+    const uint16_t* vp = vdef;
     if (pos < s1) {
       if (pos < kr.n_c) {
         const int64_t j = a.csa ? (int64_t)list[pos - s0] : pos;
@@ -250,22 +298,6 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
     my_kp = kp;
     my_vp = vp;
     vmask = (uint32_t)__ballot(ok) & 0xffffu;
-  };
-  // Wave w copies rows w, w+4, ... of the tile; a row is LPR lanes x 16 bytes (the other
-  // lanes of a wave are masked off when a row is shorter than a wave).
-  auto issue = [&](int stage) {
-    const uint32_t kdst = ring_lds + stage * STB;
-    const uint32_t vdst = kdst + KTB;
-    const int j = lane / LPR;              // 0 unless LPR < 64
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const int r = wave + i * NWV;
-      const int off = (lane % LPR) * 8;
-      if (j == 0) {
-        copy16_to_lds(lane_ptr<true>(my_kp, r) + off, kdst + r * KSTR);
-        copy16_to_lds(lane_ptr<true>(my_vp, r) + off, vdst + r * VSTR);
-      }
-    }
   };
 
   f32x4 acc[NDT];                          // O^T dims dh*DH + 16dt + 4g + i, head `head`
@@ -374,8 +406,35 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
   // stay in flight), passes a barrier (tile t visible to all waves; every wave is done
   // with tile t-1), issues tile t+3 into the stage of tile t-1 and uses tile t.
   uint32_t mq0 = 0, mq1 = 0, mq2 = 0;      // masks of tiles t, t+1, t+2
-  if (ntile > 0) { tile_ptrs(0); mq0 = vmask; issue(0); }
-  if (ntile > 1) { tile_ptrs(1); mq1 = vmask; issue(1); }
+  if (spec) {
+    bool same = true;
+    const uint16_t* sk[2];
+    const uint16_t* sv[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      spec_ptrs(t);
+      sk[t] = my_kp;
+      sv[t] = my_vp;
+    }
+    if (ntile > 0) {
+      tile_ptrs(0);
+      mq0 = vmask;
+      same = same && __ballot(my_kp != sk[0] || my_vp != sv[0]) == 0;
+    }
+    if (ntile > 1) {
+      tile_ptrs(1);
+      mq1 = vmask;
+      same = same && __ballot(my_kp != sk[1] || my_vp != sv[1]) == 0;
+    }
+    if (!same) {                             // copies of the right rows replace them
+      wait_vmcnt<0>();
+      if (ntile > 0) { tile_ptrs(0); issue(0); }
+      if (ntile > 1) { tile_ptrs(1); issue(1); }
+    }
+  } else {
+    if (ntile > 0) { tile_ptrs(0); mq0 = vmask; issue(0); }
+    if (ntile > 1) { tile_ptrs(1); mq1 = vmask; issue(1); }
+  }
   {
     const uint8_t* ql = ring + 2 * STB + (wave_on ? head : 0) * KSTR + g * (D / 4) * 2 + dh * KSW * 16;
 #pragma unroll
@@ -414,6 +473,7 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
     mq1 = mq2;
     mq2 = mq3;
   }
+  wait_vmcnt<0>();                           // no copy into LDS outlives the workgroup
 
   if (!wave_on) return;
   l_run += __shfl_xor(l_run, 16);
