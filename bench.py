@@ -69,12 +69,12 @@ KERNEL_BYTES = {
 # the counter's reading for a 256 MiB device copy (see profiles/).  An entry is used only
 # while the kernel source it was measured on is unchanged (sha256 of the file).
 MEASURED_TRAFFIC = {
-    "index_mfma_kernel": {"bytes_per_launch": 151636293,
-                          "source_sha256": "374da6ea153d68ec96e0964acf4eb460daf4aaea93d3839b96bfa2e75617675f"},
-    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 155915454,
-                                 "source_sha256": "dea3069f284cfa63a5ab0b38e502bf00607fed8446dca339c6313d97a7be281b"},
-    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32737437,
-                                 "source_sha256": "dea3069f284cfa63a5ab0b38e502bf00607fed8446dca339c6313d97a7be281b"},
+    "index_mfma_kernel": {"bytes_per_launch": 151622137,
+                          "source_sha256": "c256a9e77bde90a1ff55a4067b23c4eac0b3213c76df8c15acb0fa5838c9abe2"},
+    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 155952514,
+                                 "source_sha256": "d0d37601a00f1260fb161d716d19eaa9c871cea3f43a5da7235b46c9ab394525"},
+    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32767598,
+                                 "source_sha256": "d0d37601a00f1260fb161d716d19eaa9c871cea3f43a5da7235b46c9ab394525"},
 }
 
 
