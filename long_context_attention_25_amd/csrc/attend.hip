@@ -671,6 +671,17 @@ __global__ __launch_bounds__(kThreads) void merge_bf16_parts_kernel(const uint16
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t r = blockIdx.x;
   float* w = wsh[wave];
+  // the first round of part loads goes out before the weights, which do not gate them
+  const int nd8 = D / 8;
+  const bool on = lane < nd8;
+  const uint4* base = reinterpret_cast<const uint4*>(o_parts + r * D) + lane;
+  const int64_t pstride = R * D / 8;     // uint4 stride between parts
+  uint4 v[kMergePPT];
+#pragma unroll
+  for (int u = 0; u < kMergePPT; ++u) {
+    const int p = wave + u * NW;
+    v[u] = (on && p < P) ? base[(int64_t)p * pstride] : make_uint4(0, 0, 0, 0);
+  }
   float mx = -INFINITY;
   for (int p = lane; p < P; p += kWave) mx = fmaxf(mx, lse_parts[(int64_t)p * R + r]);
   mx = wave_max(mx);
@@ -683,19 +694,16 @@ __global__ __launch_bounds__(kThreads) void merge_bf16_parts_kernel(const uint16
   tot = wave_sum(tot);
   __builtin_amdgcn_s_waitcnt(0xc07f);    // lgkmcnt(0): this wave's LDS writes are done
   __builtin_amdgcn_wave_barrier();
-  const int nd8 = D / 8;
-  const bool on = lane < nd8;
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  const uint4* base = reinterpret_cast<const uint4*>(o_parts + r * D) + lane;
-  const int64_t pstride = R * D / 8;     // uint4 stride between parts
   for (int p0 = wave; p0 < P; p0 += NW * kMergePPT) {
-    uint4 v[kMergePPT];
+    if (p0 != wave) {
 #pragma unroll
-    for (int u = 0; u < kMergePPT; ++u) {
-      const int p = p0 + u * NW;
-      v[u] = (on && p < P) ? base[(int64_t)p * pstride] : make_uint4(0, 0, 0, 0);
+      for (int u = 0; u < kMergePPT; ++u) {
+        const int p = p0 + u * NW;
+        v[u] = (on && p < P) ? base[(int64_t)p * pstride] : make_uint4(0, 0, 0, 0);
+      }
     }
 #pragma unroll
     for (int u = 0; u < kMergePPT; ++u) {
