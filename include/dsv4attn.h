@@ -112,6 +112,37 @@ dsv4_status csa_compress(const void* x, int x_dt, const float* gate, const float
                          hipStream_t stream);
 
 /*
+ * kv_cache_append — one decode step of cache maintenance around the path  [KVC], [CSA],
+ * [HCA], [P2 §4] (a window of recent raw tokens next to the compressed entries).
+ *
+ * For every sequence b, the new token at position pos[b] is written into a ring window
+ * of raw rows, and when it completes a block ((pos[b] + 1) % m == 0) the block's m raw
+ * rows are pooled exactly as csa_compress pools them (softmax of gate + pos_bias,
+ * weighted sum, rounding or quantisation to y_dt) into compressed row (pos[b] + 1)/m - 1.
+ *
+ *   x_new     [B, C] of x_dt (F32 | BF16): the new token's raw row (for instance K and V
+ *             side by side, C = 2 D, or the raw indexer key).  gate_new [B] f32.
+ *   pos       [B] int32 (device): absolute position of the new token of each sequence.
+ *   win       [B, L, C] of x_dt, win_gate [B, L] f32: ring window, position p in row
+ *             p mod L.  The rows of the block being completed must be present (the
+ *             caller appended its earlier tokens).  csa_attend / hca_attend read this
+ *             window with win_pos0 == NULL (kw / vw views with w_rstride = C).
+ *   L         ring rows: a multiple of m, and at least the attention window W.
+ *   pos_bias  [m] f32.
+ *   y, y_scale, y_dt, N, y_bstride: the compressed cache, laid out as csa_compress's y
+ *             (N rows per sequence, batch stride y_bstride rows, 0 meaning N).  A block
+ *             whose row would be >= N, and a sequence with pos[b] < 0, are skipped.
+ *   Constraints on C, x_dt and y_dt as for csa_compress.  The window row and the cache
+ *   row are overwritten; inputs must not alias them.
+ *   Errors: invalid sizes or pointers -> DSV4_ERR_INVALID_ARG; unsupported types ->
+ *   DSV4_ERR_UNSUPPORTED; a failed launch -> DSV4_ERR_LAUNCH.  No workspace.
+ */
+dsv4_status kv_cache_append(const void* x_new, int x_dt, const float* gate_new, const int32_t* pos,
+                            int64_t B, int64_t C, void* win, float* win_gate, int64_t L,
+                            const float* pos_bias, int32_t m, void* y, uint8_t* y_scale, int y_dt,
+                            int64_t N, int64_t y_bstride, hipStream_t stream);
+
+/*
  * csa_index_topk — lightning-indexer scores and per-query top-k block selection  [CSA], [P2 §4].
  *
  *   n(p)      = min(N, floor((p + 1) / m))        blocks complete at or before position p
@@ -153,6 +184,9 @@ dsv4_status csa_index_topk(const void* qi, int qi_dt, const float* wi,
  *   idx  [B, Q, k] int32 (entries outside [0, N) are skipped);
  *   kw, vw [B, L, D]: row r holds position win_pos0[b] + r, w_rstride elements from one row
  *        to the next (0 means D);  win_pos0 [B], q_pos [B, Q].
+ *        win_pos0 == NULL selects a ring window: position p lives in row p mod L (the
+ *        layout kv_cache_append maintains), every position in (q_pos - W, q_pos] with
+ *        p >= 0 is taken to be present, and W <= L is required.
  *   Row strides larger than D let K and V live side by side in one [.., 2D] buffer (then
  *   one csa_compress call pools both).  BF16: strides multiples of 8 elements, rows and
  *   pointers 16-byte aligned.

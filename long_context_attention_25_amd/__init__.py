@@ -12,7 +12,8 @@ import os
 
 import torch
 
-__all__ = ["csa_compress", "csa_index_topk", "csa_attend", "hca_attend", "lse_merge", "lib", "LibError",
+__all__ = ["csa_compress", "kv_cache_append", "csa_index_topk", "csa_attend", "hca_attend", "lse_merge", "lib",
+           "LibError",
            "F32", "BF16", "FP8_E4M3", "MXFP4", "MXFP4_DTYPE"]
 
 F32, BF16, FP8_E4M3, MXFP4 = 0, 1, 2, 3
@@ -31,6 +32,8 @@ _SIGS = {
     "dsv4_time_next_kernel": ([_p, _p], ctypes.c_int),
     "csa_compress": ([_p, ctypes.c_int, _p, _p, _i64, _i64, _i64, _i32, _i64, _p, _p, ctypes.c_int, _i64, _p],
                      ctypes.c_int),
+    "kv_cache_append": ([_p, ctypes.c_int, _p, _p, _i64, _i64, _p, _p, _i64, _p, _i32, _p, _p, ctypes.c_int, _i64,
+                         _i64, _p], ctypes.c_int),
     "csa_index_topk": ([_p, ctypes.c_int, _p, _p, _p, ctypes.c_int, _p, _i64, _i64, _i32, _i32, _i64, _i64, _i32,
                         _i32, _p, _p, _p, ctypes.POINTER(ctypes.c_size_t), _p], ctypes.c_int),
     "csa_attend": ([_p, _p, _p, ctypes.c_int, _p, _i32, _p, _p, _p, _i64, _i32, _p, _i64, _i64, _i32, _i32, _i64,
@@ -125,6 +128,28 @@ def csa_compress(x, gate, pos_bias, m: int, y_dtype=torch.bfloat16, out=None, ou
     return (out, out_scale) if ydt == MXFP4 else out
 
 
+def kv_cache_append(x_new, gate_new, pos, win, win_gate, pos_bias, m: int, cache, cache_scale=None):
+    """One decode step of cache maintenance: x_new [B,C] (gate_new [B] f32, pos [B] int32)
+    goes to row pos % L of the ring window win [B,L,C] / win_gate [B,L], and a block that
+    the new token completes is pooled into its row of `cache` ([B,N,C] of f32/bf16/e4m3, or
+    MXFP4 codes [B,N,C/2] uint8 with cache_scale [B,N,C/32]).  Attend over such a window
+    with win_pos0=None.
+    """
+    for t in (x_new, gate_new, pos, win, win_gate, pos_bias):
+        if not t.is_contiguous():
+            raise ValueError("x_new, gate_new, pos, win, win_gate and pos_bias must be contiguous")
+    B, L, C = win.shape
+    if x_new.shape != (B, C) or x_new.dtype != win.dtype:
+        raise ValueError("x_new must be [B, C] with the window's dtype")
+    if cache.stride(-1) != 1 or (cache.dim() == 3 and cache.stride(1) != cache.shape[2]):
+        raise ValueError("cache rows must be contiguous")
+    ydt = MXFP4 if cache_scale is not None else _dt(cache)
+    N = cache.shape[1]
+    y_bs = cache.stride(0) // cache.stride(1) if B > 0 else 0
+    _check(lib().kv_cache_append(_ptr(x_new), _dt(x_new), _ptr(gate_new), _ptr(pos), B, C, _ptr(win), _ptr(win_gate),
+                                 L, _ptr(pos_bias), m, _ptr(cache), _ptr(cache_scale), ydt, N, y_bs, _stream()))
+
+
 def csa_index_topk(qi, wi, ki, q_pos, m: int, k: int, ki_scale=None, N=None, with_scores=False, workspace=None,
                    out_idx=None, out_score=None):
     """Indexer scores + per-query top-k.  qi [B,Q,HI,DI], wi [B,Q,HI] f32, ki [B,rows,DI]
@@ -163,8 +188,8 @@ def _attend_common(q, kc, vc, kw, vw, win_pos0, q_pos, N):
 
 def csa_attend(q, kc, vc, idx, kw, vw, win_pos0, W: int, q_pos, scale: float, N=None, workspace=None, out=None,
                lse=None):
-    """One softmax over the listed compressed entries and the window rows.
-    Returns (o [B,Q,H,D] in q's dtype, lse [B,Q,H] f32)."""
+    """One softmax over the listed compressed entries and the window rows (win_pos0=None:
+    a ring window, position p in row p % L).  Returns (o [B,Q,H,D] in q's dtype, lse [B,Q,H] f32)."""
     B, Q, H, D, N, kv_bs, L, kv_rs, w_rs = _attend_common(q, kc, vc, kw, vw, win_pos0, q_pos, N)
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, Q, H), dtype=torch.float32, device=q.device) if lse is None else lse

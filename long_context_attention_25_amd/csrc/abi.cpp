@@ -99,7 +99,9 @@ dsv4_status check_attend(const char* what, const AttendCommon& c) {
     REQUIRE(c.kv_rstride % 8 == 0 && c.w_rstride % 8 == 0, "%s: bf16 row strides must be multiples of 8", what);
   REQUIRE(c.B * c.Q <= 65535, "%s: B*Q must be <= 65535", what);
   if (c.B * c.Q > 0) {
-    REQUIRE(c.q && c.out && c.q_pos && c.win_pos0, "%s: q, out, q_pos and win_pos0 must not be NULL", what);
+    REQUIRE(c.q && c.out && c.q_pos, "%s: q, out and q_pos must not be NULL", what);
+    REQUIRE(c.win_pos0 || c.W <= c.L, "%s: a ring window (win_pos0 == NULL) needs W (%d) <= L (%lld)", what, c.W,
+            (long long)c.L);
     REQUIRE(c.N == 0 || (c.kc && c.vc), "%s: kc and vc must not be NULL when N > 0", what);
     REQUIRE(c.L == 0 || (c.kw && c.vw), "%s: kw and vw must not be NULL when L > 0", what);
   }
@@ -191,6 +193,35 @@ dsv4_status csa_compress(const void* x, int x_dt, const float* gate, const float
   a.y = y; a.y_scale = y_scale; a.y_dt = y_dt;
   if (a.total_blocks() == 0) return ok();
   return launched(dsv4::launch_compress(a, stream), what);
+}
+
+dsv4_status kv_cache_append(const void* x_new, int x_dt, const float* gate_new, const int32_t* pos, int64_t B,
+                            int64_t C, void* win, float* win_gate, int64_t L, const float* pos_bias, int32_t m,
+                            void* y, uint8_t* y_scale, int y_dt, int64_t N, int64_t y_bstride, hipStream_t stream) {
+  const char* what = "kv_cache_append";
+  REQUIRE(B >= 0 && C > 0 && N >= 0, "%s: need B >= 0, C > 0, N >= 0", what);
+  REQUIRE(m >= 1 && m <= 1024, "%s: m must be in [1, 1024], got %d", what, m);
+  SUPPORT(x_dt == DSV4_F32 || x_dt == DSV4_BF16, "%s: x_dt must be F32 or BF16", what);
+  SUPPORT(y_dt >= DSV4_F32 && y_dt <= DSV4_MXFP4, "%s: unknown y_dt %d", what, y_dt);
+  SUPPORT(C % 8 == 0, "%s: C must be a multiple of 8, got %lld", what, (long long)C);
+  SUPPORT(C <= (x_dt == DSV4_F32 ? 1024 : 2048), "%s: C too large (f32: <= 1024, bf16: <= 2048)", what);
+  if (y_dt == DSV4_MXFP4) SUPPORT(C % 32 == 0, "%s: MXFP4 output needs C %% 32 == 0", what);
+  REQUIRE(L >= m && L % m == 0, "%s: L (%lld) must be a positive multiple of m (%d)", what, (long long)L, m);
+  REQUIRE(y_bstride == 0 || y_bstride >= N, "%s: y_bstride must be 0 or >= N", what);
+  REQUIRE(B <= 65535, "%s: B must be <= 65535", what);
+  if (B > 0) {
+    REQUIRE(x_new && gate_new && pos && win && win_gate && pos_bias,
+            "%s: x_new, gate_new, pos, win, win_gate and pos_bias must not be NULL", what);
+    REQUIRE(N == 0 || y, "%s: y must not be NULL when N > 0", what);
+    if (y_dt == DSV4_MXFP4 && N > 0) REQUIRE(y_scale, "%s: y_scale must not be NULL for MXFP4 output", what);
+  }
+  dsv4::AppendArgs a;
+  a.x_new = x_new; a.x_f32 = x_dt == DSV4_F32; a.gate_new = gate_new; a.pos = pos;
+  a.win = win; a.win_gate = win_gate;
+  a.B = B; a.L = L; a.C = C; a.bias = pos_bias; a.m = m;
+  a.y = y; a.y_scale = y_scale; a.y_dt = y_dt; a.y_bs = y_bstride ? y_bstride : N; a.N = N;
+  if (B == 0) return ok();
+  return launched(dsv4::launch_append(a, stream), what);
 }
 
 dsv4_status csa_index_topk(const void* qi, int qi_dt, const float* wi, const void* ki, const uint8_t* ki_scale,

@@ -41,7 +41,9 @@ struct KeyRange {
   int64_t n_tot;    // n_c + window rows
 };
 
-// p: position of query bq, wp0: position of window row 0 of its sequence
+// p: position of query bq, wp0: position of window row 0 of its sequence.  In ring mode
+// (no win_pos0) wp0 is 0, window "rows" are absolute positions and wrow() maps them to
+// buffer rows (position mod L); the caller keeps the last L >= W positions there.
 __device__ __forceinline__ KeyRange key_range(const AttendArgs& a, int64_t p, int64_t wp0) {
   KeyRange r;
   if (a.csa) {
@@ -53,14 +55,16 @@ __device__ __forceinline__ KeyRange key_range(const AttendArgs& a, int64_t p, in
   int64_t lo = p - a.W + 1 - wp0;
   int64_t hi = p + 1 - wp0;
   if (lo < 0) lo = 0;
-  if (hi > a.L) hi = a.L;
+  if (a.win_pos0 && hi > a.L) hi = a.L;
   r.r_lo = lo;
   r.n_tot = r.n_c + (hi > lo ? hi - lo : 0);
   return r;
 }
 __device__ __forceinline__ KeyRange key_range(const AttendArgs& a, int64_t bq) {
-  return key_range(a, a.q_pos[bq], a.win_pos0[bq / a.Q]);
+  return key_range(a, a.q_pos[bq], a.win_pos0 ? a.win_pos0[bq / a.Q] : 0);
 }
+// Buffer row of window row r.
+__device__ __forceinline__ int64_t wrow(const AttendArgs& a, int64_t r) { return a.win_pos0 ? r : r % a.L; }
 
 // Row (element offset into kc/vc or kw/vw) of list position `pos`; -1 if the slot is empty.
 // Sets *win when the row comes from the window buffer.
@@ -75,7 +79,7 @@ __device__ __forceinline__ int64_t key_row(const AttendArgs& a, int64_t bq, cons
     return (b * a.kv_bs + j) * a.kv_rs;
   }
   *win = true;
-  return (b * a.L + kr.r_lo + (pos - kr.n_c)) * a.w_rs;
+  return (b * a.L + wrow(a, kr.r_lo + (pos - kr.n_c))) * a.w_rs;
 }
 
 // ---------------------------------------------------------------------------- bf16 / MFMA
@@ -239,7 +243,7 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
     issue(1);
   }
   const int32_t qpos = load_uniform(a.q_pos + bq);     // scalar loads: not counted by vmcnt
-  const int32_t wpos0 = load_uniform(a.win_pos0 + b);
+  const int32_t wpos0 = a.win_pos0 ? load_uniform(a.win_pos0 + b) : 0;
   constexpr int LPT = kMaxCsaChunk / NT;   // index entries per thread
   int32_t lv[LPT];
   const int64_t e1 = s0 + chunk < a.k ? s0 + chunk : a.k;
@@ -273,8 +277,8 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
   // Invalid slots point at a row that holds data (the query's first window row, else the
   // first compressed row), since their zero weights would not cancel a non-finite value.
   const bool win_rows = kr.n_tot > kr.n_c;
-  const uint16_t* kdef = win_rows ? kw + kr.r_lo * wrs : kc;
-  const uint16_t* vdef = win_rows ? vw + kr.r_lo * wrs : vc;
+  const uint16_t* kdef = win_rows ? kw + wrow(a, kr.r_lo) * wrs : kc;
+  const uint16_t* vdef = win_rows ? vw + wrow(a, kr.r_lo) * wrs : vc;
   auto tile_ptrs = [&](int t) {
     const int64_t pos = s0 + (int64_t)t * KT + (lane & (KT - 1));
     bool ok = false;
@@ -289,7 +293,7 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
           vp = vc + j * krs;
         }
       } else {
-        const int64_t r = kr.r_lo + (pos - kr.n_c);
+        const int64_t r = wrow(a, kr.r_lo + (pos - kr.n_c));
         ok = true;
         kp = kw + r * wrs;
         vp = vw + r * wrs;

@@ -89,19 +89,19 @@ struct PoolState {
 // spb are powers of two the slots of a block sit at lane distances lpr, 2 lpr, ... and are
 // combined by a butterfly within the wave, then (blocks wider than a wave) across waves
 // through LDS; otherwise every state goes through LDS and the writer combines them.
+// The work of workgroup `wg` (every thread of the workgroup calls it).
 template <typename TX, int YDT>
-__global__ __launch_bounds__(kThreads) void compress_kernel(
+__device__ __forceinline__ void compress_body(
     const TX* __restrict__ x, const float* __restrict__ gate, const float* __restrict__ bias,
     int64_t T, int C, int m, int64_t nb_per_b, int64_t total_blocks, int64_t x_bs, int64_t y_bs,
-    void* __restrict__ y, uint8_t* __restrict__ ysc, int lpr, int spb, int bpw, int cs) {
+    void* __restrict__ y, uint8_t* __restrict__ ysc, int lpr, int spb, int bpw, int cs, int64_t wg) {
   constexpr int V = XVec<TX>::N;
-  constexpr int NW = kThreads / kWave;
   __shared__ float part[kThreads * (V + 2)];          // states crossing waves (or all states)
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int64_t blk0 = (int64_t)(blockIdx.x / cs) * bpw;   // cs workgroups share a block group,
-  const int slice = blockIdx.x % cs;                         // each on lpr of its channel vectors
+  const int64_t blk0 = (wg / cs) * bpw;                // cs workgroups share a block group,
+  const int slice = (int)(wg % cs);                    // each on lpr of its channel vectors
 
   const int rs_total = kThreads / lpr;
   const int slot = tid / lpr, cv = tid % lpr + slice * lpr;
@@ -142,19 +142,21 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
       st.combine(oM, os, oa);
     }
     if (lpr * spb > kWave) {
-      // blocks span lpr*spb/64 waves: lanes < lpr of each wave hold the wave's state
-      if (lane < lpr) {
-        float* p = part + (wave * kWave + lane) * (V + 2);
+      // a block spans several waves: after the butterfly every group of g = 64/lpr slots
+      // inside a wave (one slot when lpr >= 64) holds one state; the first slot of each
+      // group stores it and the writer (slot 0) combines them
+      const int g = lpr < kWave ? kWave / lpr : 1;
+      if (active && r0 % g == 0) {
+        float* p = part + tid * (V + 2);
         p[0] = st.M;
         p[1] = st.s;
 #pragma unroll
         for (int v = 0; v < V; ++v) p[2 + v] = st.a[v];
       }
       __syncthreads();
-      const int wpb = lpr * spb / kWave;
       if (active && r0 == 0) {
-        for (int w = 1; w < wpb && wave + w < NW; ++w) {
-          const float* p = part + ((wave + w) * kWave + lane) * (V + 2);
+        for (int r = g; r < spb; r += g) {
+          const float* p = part + (tid + r * lpr) * (V + 2);
           st.combine(p[0], p[1], p + 2);
         }
       }
@@ -232,6 +234,57 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
 }
 
 template <typename TX, int YDT>
+__global__ __launch_bounds__(kThreads) void compress_kernel(
+    const TX* __restrict__ x, const float* __restrict__ gate, const float* __restrict__ bias,
+    int64_t T, int C, int m, int64_t nb_per_b, int64_t total_blocks, int64_t x_bs, int64_t y_bs,
+    void* __restrict__ y, uint8_t* __restrict__ ysc, int lpr, int spb, int bpw, int cs) {
+  compress_body<TX, YDT>(x, gate, bias, T, C, m, nb_per_b, total_blocks, x_bs, y_bs, y, ysc, lpr, spb, bpw, cs,
+                         blockIdx.x);
+}
+
+// One decode step of cache maintenance; workgroup (slice, b) owns lpr channel vectors of
+// sequence b: it writes its part of the new token's row into ring row pos[b] mod L (and
+// the gate, which every slice writes alike), and when the token completes a block of m
+// it pools its channels of the block's rows (contiguous in the ring, L being a multiple
+// of m) into compressed row (pos[b] + 1) / m - 1.  A workgroup reads only rows written by
+// earlier calls and the part of the new row it wrote itself.
+template <typename TX, int YDT>
+__global__ __launch_bounds__(kThreads) void append_kernel(
+    const TX* __restrict__ x_new, const float* __restrict__ gate_new, const int32_t* __restrict__ pos,
+    TX* __restrict__ win, float* __restrict__ win_gate, int64_t L, int C, const float* __restrict__ bias, int m,
+    void* __restrict__ y, uint8_t* __restrict__ ysc, int64_t y_bs, int64_t N, int lpr, int spb, int bpw, int cs) {
+  const int64_t b = blockIdx.y;
+  const int slice = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t p = pos[b];
+  if (p < 0) return;
+  const int64_t row = p % L;
+  {
+    // one channel vector is 16 bytes for both input types
+    const uint4* src = reinterpret_cast<const uint4*>(x_new + b * C) + (int64_t)slice * lpr;
+    uint4* dst = reinterpret_cast<uint4*>(win + (b * L + row) * C) + (int64_t)slice * lpr;
+    for (int i = tid; i < lpr; i += kThreads) dst[i] = src[i];
+    if (tid == 0) win_gate[b * L + row] = gate_new[b];
+  }
+  __syncthreads();
+  const int64_t blk = (p + 1) / m - 1;
+  if ((p + 1) % m != 0 || blk >= N) return;
+  const int64_t first = (p + 1 - m) % L;
+  const int64_t yrow = b * y_bs + blk;
+  uint8_t* yr = reinterpret_cast<uint8_t*>(y);
+  uint8_t* sr = ysc;
+  if constexpr (YDT == 0) yr += yrow * C * 4;
+  else if constexpr (YDT == 1) yr += yrow * C * 2;
+  else if constexpr (YDT == 2) yr += yrow * C;
+  else {
+    yr += yrow * (C / 2);
+    sr += yrow * (C / 32);
+  }
+  compress_body<TX, YDT>(win + (b * L + first) * C, win_gate + b * L + first, bias, m, C, m, 1, 1, 0, 0, yr, sr, lpr,
+                         spb, bpw, cs, slice);
+}
+
+template <typename TX, int YDT>
 hipError_t launch_t(const CompressArgs& a, hipStream_t st) {
   constexpr int V = XVec<TX>::N;
   const int lpr_full = (int)(a.C / V);
@@ -260,6 +313,38 @@ hipError_t launch_t(const CompressArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Channel split of the pooling: as for csa_compress (one block per sequence here).
+template <typename TX, int YDT>
+void plan_split(int64_t C, int m, int64_t blocks, int* lpr_o, int* spb_o, int* bpw_o, int* cs_o) {
+  constexpr int V = XVec<TX>::N;
+  const int lpr_full = (int)(C / V);
+  const int min_lanes = (YDT == 3) ? 32 / V : 1;
+  int cs = 1;
+  while (true) {
+    int lpr = lpr_full / cs;
+    int rs = kThreads / lpr;
+    int spb = m < rs ? m : rs;
+    int64_t groups = (blocks + rs / spb - 1) / (rs / spb);
+    if (groups * cs >= 256 || lpr % 2 || lpr / 2 < min_lanes || lpr / 2 > kThreads) break;
+    cs *= 2;
+  }
+  *lpr_o = lpr_full / cs;
+  const int rs = kThreads / *lpr_o;
+  *spb_o = m < rs ? m : rs;
+  *bpw_o = rs / *spb_o;
+  *cs_o = cs;
+}
+
+template <typename TX, int YDT>
+hipError_t launch_append_t(const AppendArgs& a, hipStream_t st) {
+  int lpr, spb, bpw, cs;
+  plan_split<TX, YDT>(a.C, a.m, a.B, &lpr, &spb, &bpw, &cs);
+  hipLaunchKernelGGL((append_kernel<TX, YDT>), dim3((unsigned)cs, (unsigned)a.B), dim3(kThreads), 0, st,
+                     reinterpret_cast<const TX*>(a.x_new), a.gate_new, a.pos, reinterpret_cast<TX*>(a.win), a.win_gate,
+                     a.L, (int)a.C, a.bias, a.m, a.y, a.y_scale, a.y_bs, a.N, lpr, spb, bpw, cs);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
@@ -277,6 +362,24 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
     case 1: return launch_t<uint16_t, 1>(a, st);
     case 2: return launch_t<uint16_t, 2>(a, st);
     default: return launch_t<uint16_t, 3>(a, st);
+  }
+}
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
+  if (a.B == 0) return hipSuccess;
+  if (a.x_f32) {
+    switch (a.y_dt) {
+      case 0: return launch_append_t<float, 0>(a, st);
+      case 1: return launch_append_t<float, 1>(a, st);
+      case 2: return launch_append_t<float, 2>(a, st);
+      default: return launch_append_t<float, 3>(a, st);
+    }
+  }
+  switch (a.y_dt) {
+    case 0: return launch_append_t<uint16_t, 0>(a, st);
+    case 1: return launch_append_t<uint16_t, 1>(a, st);
+    case 2: return launch_append_t<uint16_t, 2>(a, st);
+    default: return launch_append_t<uint16_t, 3>(a, st);
   }
 }
 

@@ -37,6 +37,23 @@ struct CompressArgs {
 };
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st);
 
+struct AppendArgs {
+  const void* x_new;
+  bool x_f32;
+  const float* gate_new;
+  const int32_t* pos;
+  void* win;
+  float* win_gate;
+  int64_t B, L, C;
+  const float* bias;
+  int m;
+  void* y;
+  uint8_t* y_scale;
+  int y_dt;             // 0 f32, 1 bf16, 2 fp8 e4m3, 3 MXFP4
+  int64_t y_bs, N;
+};
+hipError_t launch_append(const AppendArgs& a, hipStream_t st);
+
 // ---------------------------------------------------------------- indexer + top-k
 enum KeyKind { KEY_F32 = 0, KEY_BF16 = 1, KEY_FP8 = 2, KEY_MXFP4 = 3 };
 

@@ -62,6 +62,28 @@ def test_compress_validation():
     assert L.lib().dsv4_last_error() == b""
 
 
+def _append(**kw):
+    a = dict(x=P, x_dt=1, g=P, pos=P, B=2, C=1024, win=P, wg=P, L=256, bias=P, m=128, y=P, ysc=None, ydt=1, N=64,
+             ybs=0)
+    a.update(kw)
+    return L.lib().kv_cache_append(a["x"], a["x_dt"], a["g"], a["pos"], a["B"], a["C"], a["win"], a["wg"], a["L"],
+                                   a["bias"], a["m"], a["y"], a["ysc"], a["ydt"], a["N"], a["ybs"], None)
+
+
+def test_cache_append_validation():
+    assert _append(m=0) == 1
+    assert _append(L=200) == 1 and b"multiple of m" in L.lib().dsv4_last_error()
+    assert _append(L=64) == 1
+    assert _append(x_dt=2) == 2
+    assert _append(C=12) == 2
+    assert _append(ydt=3, C=48) == 2
+    assert _append(ydt=3, ysc=None) == 1
+    assert _append(win=None) == 1
+    assert _append(ybs=10) == 1
+    assert _append(y=None, N=0, B=0) == 0             # nothing to do: no launch
+    assert L.lib().dsv4_last_error() == b""
+
+
 def _index(ws=None, n=None, **kw):
     a = dict(qi=P, qdt=1, wi=P, ki=P, ksc=None, kdt=1, qpos=P, B=8, Q=1, HI=8, DI=128, N=262144, kbs=0, m=4, k=1024,
              oi=P, osc=None)
@@ -123,6 +145,8 @@ def test_attend_validation_and_workspace_query():
     assert _attend(scale=float("nan"))[0] == 1
     assert _attend(dt=0, D=128, H=16)[0] == 0           # f32 path needs no workspace
     assert _attend(dt=0, D=1024, H=16)[0] == 2
+    assert _attend(wp0=None)[0] == 0                     # ring window (W <= L)
+    assert _attend(wp0=None, W=256)[0] == 1 and b"ring" in L.lib().dsv4_last_error()
 
 
 def test_lse_merge_validation():

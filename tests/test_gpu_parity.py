@@ -68,7 +68,8 @@ def test_compress_f32_c1_shapes():
     assert row_rel_err(host(y), y_ref) <= 1e-5
 
 
-@pytest.mark.parametrize("m,C,nb,B", [(128, 512, 13, 2), (4, 128, 37, 3), (4, 512, 9, 1), (32, 64, 5, 2)])
+@pytest.mark.parametrize("m,C,nb,B", [(128, 512, 13, 2), (4, 128, 37, 3), (4, 512, 9, 1), (32, 64, 5, 2), (4, 1024, 1024, 1),
+                                      (128, 1024, 3, 2)])
 def test_compress_bf16_within_one_ulp(m, C, nb, B):
     cfg = 102
     T = m * nb
@@ -97,6 +98,110 @@ def test_compress_into_cache_tail_with_batch_stride():
     assert np.all(got[:, :12] == 0)
     y_ref = method.compress(codecs.decode_bf16(xbits), gate, bias, m)
     assert np.all(np.abs(got[:, 12:] - y_ref) <= compress_tol(codecs.decode_bf16(xbits), m, y_ref))
+
+
+@pytest.mark.parametrize("m,C,ydt", [(4, 1024, "bf16"), (128, 1024, "bf16"), (4, 128, "mxfp4"), (4, 64, "f32")])
+def test_cache_append_decode_matches_prefix_compression(m, C, ydt):
+    """Prefix / decode consistency: a prefix compressed in one call, then one token per
+    step through kv_cache_append (the ring wraps twice, blocks complete at different steps
+    per sequence) leaves the ring holding the last L raw rows at row position % L and the
+    cache holding the oracle's pooled blocks of the whole sequence."""
+    cfg = 150 + m
+    B, W = 3, 16
+    Lw = max(m, 40) if m < 128 else 256                     # a multiple of m, >= W
+    T0 = np.array([5 * m, 5 * m + 1, 7 * m - 1])          # prefix lengths (ragged)
+    S = 2 * Lw + 2 * m                                      # decode steps
+    Tt = int(T0.max()) + S
+    N = Tt // m + 2
+    x32 = synth.normal(cfg, synth.RAW_K, (B, Tt, C))
+    gate = synth.normal(cfg, synth.GATE, (B, Tt))
+    bias = synth.normal(cfg, synth.BIAS, (m,), std=0.1)
+    if ydt == "f32":
+        xd = dev(x32)
+        x64 = x32.astype(np.float64)
+    else:
+        xd, xbits = dev_bf16(x32)
+        x64 = codecs.decode_bf16(xbits)
+    if ydt == "mxfp4":
+        cache = torch.zeros((B, N, C // 2), dtype=torch.uint8, device="cuda")
+        cscale = torch.zeros((B, N, C // 32), dtype=torch.uint8, device="cuda")
+    else:
+        cache = torch.zeros((B, N, C), dtype=torch.float32 if ydt == "f32" else torch.bfloat16, device="cuda")
+        cscale = None
+    gd, bd = dev(gate), dev(bias)
+    # prefix: complete blocks compressed in one call per sequence; the ring holds the last L rows
+    win = torch.zeros((B, Lw, C), dtype=xd.dtype, device="cuda")
+    wgate = torch.zeros((B, Lw), dtype=torch.float32, device="cuda")
+    for b in range(B):
+        nb0 = int(T0[b]) // m
+        if nb0:
+            kw = dict(out=cache[b:b + 1, :nb0])
+            if ydt == "mxfp4":
+                kw["out_scale"] = cscale[b:b + 1, :nb0]
+            L.csa_compress(xd[b:b + 1, :nb0 * m], gd[b:b + 1, :nb0 * m].contiguous(), bd, m,
+                           L.MXFP4_DTYPE if ydt == "mxfp4" else cache.dtype, **kw)
+        for q in range(max(0, int(T0[b]) - Lw), int(T0[b])):
+            win[b, q % Lw] = xd[b, q]
+            wgate[b, q % Lw] = gd[b, q]
+    rows = torch.arange(B, device="cuda")
+    for t in range(S):
+        pd = dev((T0 + t).astype(np.int32))
+        pl = pd.long()
+        L.kv_cache_append(xd[rows, pl].contiguous(), gd[rows, pl].contiguous(), pd, win, wgate, bd, m, cache, cscale)
+    torch.cuda.synchronize()
+    # ring: the last L positions at row position % L, bit for bit
+    for b in range(B):
+        last = int(T0[b]) + S - 1
+        qs = torch.arange(last - Lw + 1, last + 1, device="cuda")
+        assert torch.equal(win[b, qs % Lw], xd[b, qs])
+        assert torch.equal(wgate[b, qs % Lw], gd[b, qs])
+    # cache: every completed block equals the oracle's pooling of the whole sequence
+    for b in range(B):
+        nb = (int(T0[b]) + S) // m
+        y_ref = method.compress(x64[b:b + 1, :nb * m], gate[b:b + 1, :nb * m], bias, m)[0]
+        if ydt == "mxfp4":
+            codes, scales = cache[b, :nb].cpu().numpy(), cscale[b, :nb].cpu().numpy()
+            got = codecs.decode_mxfp4(codes, scales)
+            step = np.repeat(np.ldexp(1.0, scales.astype(np.int64) - 127), 32, axis=1)   # 2^X per group
+            assert np.all(np.abs(got - y_ref) <= 2 * step + 1e-6 * np.abs(y_ref))   # e2m1 rounding / saturation
+        else:
+            got = host(cache[b, :nb])
+            if ydt == "f32":
+                assert row_rel_err(got[None], y_ref[None]) <= 1e-5
+            else:
+                assert np.all(np.abs(got - y_ref) <= compress_tol(x64[b:b + 1, :nb * m], m, y_ref[None])[0])
+        assert torch.count_nonzero(cache[b, nb:]) == 0
+
+
+@pytest.mark.parametrize("csa", [True, False])
+def test_attend_over_a_ring_window(csa):
+    """win_pos0 = NULL: the window is a ring (position p in row p % L); the result equals
+    the oracle on the same rows laid out linearly."""
+    cfg = 170
+    B, Q, H, D, N, m, Lw, W, k = 2, 3, 64, 512, 300, (4 if csa else 128), 256, 128, 64
+    pmax = np.array([N * m + 40, N * m - 7])
+    qpos = np.stack([pmax, pmax - 1, pmax - 90], axis=1).astype(np.int32)       # [B, Q]
+    bits = lambda t, shape: synth.bf16_bits(synth.normal(cfg, t, shape))
+    qb, kb, vb = bits(synth.Q, (B, Q, H, D)), bits(synth.KC, (B, N, D)), bits(synth.VC, (B, N, D))
+    kwl, vwl = bits(synth.KW, (B, Lw, D)), bits(synth.VW, (B, Lw, D))       # linear: row r <-> wp0 + r
+    wp0 = (pmax - Lw + 1).astype(np.int32)
+    kwr, vwr = np.empty_like(kwl), np.empty_like(vwl)
+    for b in range(B):
+        rr = (wp0[b] + np.arange(Lw)) % Lw
+        kwr[b, rr], vwr[b, rr] = kwl[b], vwl[b]
+    tb = lambda x: dev(x.view(np.int16)).view(torch.bfloat16)
+    dec = codecs.decode_bf16
+    scale = 1.0 / math.sqrt(D)
+    if csa:
+        idx = synth.sorted_unique_indices(cfg, synth.IDX, B * Q, N, k).reshape(B, Q, k).astype(np.int32)
+        o, lse = L.csa_attend(tb(qb), tb(kb), tb(vb), dev(idx), tb(kwr), tb(vwr), None, W, dev(qpos), scale)
+        o_r, lse_r = method.csa_attend(dec(qb), dec(kb), dec(vb), idx, dec(kwl), dec(vwl), wp0, W, qpos, scale)
+    else:
+        o, lse = L.hca_attend(tb(qb), tb(kb), tb(vb), m, tb(kwr), tb(vwr), None, W, dev(qpos), scale)
+        o_r, lse_r = method.hca_attend(dec(qb), dec(kb), dec(vb), m, dec(kwl), dec(vwl), wp0, W, qpos, scale)
+    torch.cuda.synchronize()
+    assert row_rel_err(host(o), o_r) <= 1e-2
+    assert lse_abs_err(lse.cpu().numpy(), lse_r) <= 1e-3
 
 
 def _quant_inputs():
