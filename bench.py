@@ -181,6 +181,46 @@ def marshal_step(L, torch, wl, rep):
     return calls, timed
 
 
+def time_cache_append(L, torch, wl, steps):
+    """Average GPU time of one decode step of cache maintenance through kv_cache_append:
+    the new token (position CTX-1, the last row of each 128-row window used as a ring)
+    is appended to the CSA K|V, CSA indexer-key (MXFP4) and HCA K|V windows and completes
+    a block of each layer (the worst case), which is pooled into entry N-1 of each cache.
+    Outside the timed decode steps; the decode step pools with csa_compress instead (its
+    cache row chosen on the host, so no kernel waits for a device-side position)."""
+    lib = L.lib()
+    t = wl.r[0]
+    P = lambda x: ctypes.c_void_p(x.data_ptr()) if x is not None else None
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    new = {k: t[w][:, LWIN - 1].contiguous() for k, w in (("kv", "kvw"), ("ki", "kiw"), ("hkv", "hkvw"))}
+    g_new, hg_new = t["gate"][:, LWIN - 1].contiguous(), t["hgate"][:, LWIN - 1].contiguous()
+    calls = [
+        (P(new["kv"]), L.BF16, P(g_new), P(wl.q_pos), B, 2 * D, P(t["kvw"]), P(t["gate"]), LWIN, P(t["bias"]), M_CSA,
+         P(wl.kvc), None, L.BF16, N_CSA, 0, st),
+        (P(new["ki"]), L.BF16, P(g_new), P(wl.q_pos), B, DI, P(t["kiw"]), P(t["gate"]), LWIN, P(t["bias"]), M_CSA,
+         P(t["ki"]), P(t["ks"]), L.MXFP4, N_CSA, 0, st),
+        (P(new["hkv"]), L.BF16, P(hg_new), P(wl.q_pos), B, 2 * D, P(t["hkvw"]), P(t["hgate"]), LWIN, P(t["hbias"]),
+         M_HCA, P(t["hkvc"]), None, L.BF16, N_HCA, 0, st),
+    ]
+
+    def step():
+        for a in calls:
+            st_ = lib.kv_cache_append(*a)
+            if st_ != 0:
+                raise RuntimeError(lib.dsv4_last_error().decode())
+
+    for _ in range(5):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1000.0 / steps
+
+
 class HipEvents:
     """Raw hipEvent_t pairs from the HIP runtime torch already loaded."""
 
@@ -501,6 +541,9 @@ def main():
                      "timed_launches": len(pairs)},
         "kernels": kernels,
     }
+    out["cache_append"] = {"us_per_step": round(time_cache_append(L, torch, wl, 50), 2), "calls_per_step": 3,
+                           "note": "kv_cache_append for CSA K|V, CSA indexer key (MXFP4) and HCA K|V, each new "
+                                   "token completing a block (worst case); measured after the timed steps"}
     if not args.no_cpu_baseline:
         done, el = cpu_baseline(L, torch, synth, wl, args.cpu_seconds)
         out["cpu_baseline"] = {"value": round(done / el, 3), "unit": "queries/s", "cores": 1, "kind": "oracle",

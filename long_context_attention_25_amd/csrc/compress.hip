@@ -94,7 +94,10 @@ template <typename TX, int YDT>
 __device__ __forceinline__ void compress_body(
     const TX* __restrict__ x, const float* __restrict__ gate, const float* __restrict__ bias,
     int64_t T, int C, int m, int64_t nb_per_b, int64_t total_blocks, int64_t x_bs, int64_t y_bs,
-    void* __restrict__ y, uint8_t* __restrict__ ysc, int lpr, int spb, int bpw, int cs, int64_t wg) {
+    void* __restrict__ y, uint8_t* __restrict__ ysc, int lpr, int spb, int bpw, int cs, int64_t wg,
+    const TX* __restrict__ last_row = nullptr, float last_gate = 0.f) {
+  // last_row (one block only): row m-1 of the block and its gate are taken from here
+  // instead of x / gate
   constexpr int V = XVec<TX>::N;
   __shared__ float part[kThreads * (V + 2)];          // states crossing waves (or all states)
 
@@ -123,8 +126,13 @@ __device__ __forceinline__ void compress_body(
       for (int u = 0; u < 4; ++u) {
         const int r = j + u * spb;
         if (r < m) {
-          XVec<TX>::load(xb + (int64_t)r * C, xv[u]);
-          z[u] = g[r] + bias[r];
+          if (last_row && r == m - 1) {
+            XVec<TX>::load(last_row + (int64_t)cv * V, xv[u]);
+            z[u] = last_gate + bias[r];
+          } else {
+            XVec<TX>::load(xb + (int64_t)r * C, xv[u]);
+            z[u] = g[r] + bias[r];
+          }
           n = u + 1;
         }
       }
@@ -246,8 +254,8 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
 // sequence b: it writes its part of the new token's row into ring row pos[b] mod L (and
 // the gate, which every slice writes alike), and when the token completes a block of m
 // it pools its channels of the block's rows (contiguous in the ring, L being a multiple
-// of m) into compressed row (pos[b] + 1) / m - 1.  A workgroup reads only rows written by
-// earlier calls and the part of the new row it wrote itself.
+// of m) into compressed row (pos[b] + 1) / m - 1.  The pooling reads the block's earlier
+// rows from the window (written by earlier calls) and the new row from x_new.
 template <typename TX, int YDT>
 __global__ __launch_bounds__(kThreads) void append_kernel(
     const TX* __restrict__ x_new, const float* __restrict__ gate_new, const int32_t* __restrict__ pos,
@@ -256,17 +264,19 @@ __global__ __launch_bounds__(kThreads) void append_kernel(
   const int64_t b = blockIdx.y;
   const int slice = blockIdx.x;
   const int tid = threadIdx.x;
-  const int64_t p = pos[b];
+  // the position through the scalar path (constant address space, uniform address)
+  const int64_t p = *reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
+      reinterpret_cast<uintptr_t>(pos + b));
   if (p < 0) return;
   const int64_t row = p % L;
+  const float gnew = gate_new[b];
   {
     // one channel vector is 16 bytes for both input types
     const uint4* src = reinterpret_cast<const uint4*>(x_new + b * C) + (int64_t)slice * lpr;
     uint4* dst = reinterpret_cast<uint4*>(win + (b * L + row) * C) + (int64_t)slice * lpr;
     for (int i = tid; i < lpr; i += kThreads) dst[i] = src[i];
-    if (tid == 0) win_gate[b * L + row] = gate_new[b];
+    if (tid == 0) win_gate[b * L + row] = gnew;
   }
-  __syncthreads();
   const int64_t blk = (p + 1) / m - 1;
   if ((p + 1) % m != 0 || blk >= N) return;
   const int64_t first = (p + 1 - m) % L;
@@ -280,8 +290,10 @@ __global__ __launch_bounds__(kThreads) void append_kernel(
     yr += yrow * (C / 2);
     sr += yrow * (C / 32);
   }
+  // the block's last row is the new token: read from x_new, so that the pooling does not
+  // wait for the window write above
   compress_body<TX, YDT>(win + (b * L + first) * C, win_gate + b * L + first, bias, m, C, m, 1, 1, 0, 0, yr, sr, lpr,
-                         spb, bpw, cs, slice);
+                         spb, bpw, cs, slice, x_new + b * C, gnew);
 }
 
 template <typename TX, int YDT>
