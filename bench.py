@@ -221,6 +221,53 @@ def time_cache_append(L, torch, wl, steps):
     return e0.elapsed_time(e1) * 1000.0 / steps
 
 
+# The V4-Pro stack the pages describe: 61 layers, layers 0 and 1 HCA, layers 2 .. 60
+# alternating CSA and HCA (CSA first), then an MTP block with sliding-window attention only.
+SCHEDULE = ["hca", "hca"] + ["csa" if i % 2 == 0 else "hca" for i in range(2, 61)] + ["swa"]
+
+
+def kv_bytes_per_token():
+    """Stored cache bytes per token and layer type at this workload's storage formats (bf16
+    K|V entries, MXFP4 indexer keys); the 128-row raw windows are per sequence, not per token."""
+    csa = (2 * D * 2 + DI // 2 + DI // 32) / M_CSA            # K|V entry + indexer key, per 4 tokens
+    hca = 2 * D * 2 / M_HCA                                   # K|V entry per 128 tokens
+    return {"csa": csa, "hca": hca, "swa": 0.0}
+
+
+def time_schedule(L, torch, marsh, steps):
+    """One decode token for the 8 sequences through the whole layer schedule: the CSA and
+    HCA layers run the decode step's calls (marsh: the marshalled step of each replica;
+    replicas rotate layer by layer), the MTP layer attends over its window only.  Returns
+    (us per token step, per-layer-type us)."""
+    lib = L.lib()
+    parts = [{"csa": c[:4], "hca": c[4:]} for c in marsh]
+    # window-only attention: the HCA call with no compressed entries
+    for r, c in enumerate(marsh):
+        fn, a = c[5]
+        a = list(a)
+        a[15] = 0                                   # N
+        parts[r]["swa"] = [(fn, tuple(a))]
+
+    def run(kinds):
+        for i, kind in enumerate(kinds):
+            for fn, a in parts[i % len(parts)][kind]:
+                if fn(*a) != 0:
+                    raise RuntimeError(lib.dsv4_last_error().decode())
+
+    res = {}
+    for name, kinds in (("schedule", SCHEDULE), ("csa", ["csa"] * 12), ("hca", ["hca"] * 12), ("swa", ["swa"] * 12)):
+        run(kinds)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            run(kinds)
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) * 1000.0 / (steps * len(kinds))
+    return res["schedule"] * len(SCHEDULE), {k: round(res[k], 2) for k in ("csa", "hca", "swa")}
+
+
 class HipEvents:
     """Raw hipEvent_t pairs from the HIP runtime torch already loaded."""
 
@@ -453,6 +500,7 @@ def main():
                          "a few microseconds each, so timing every step would slow the step itself)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-schedule", action="store_true", help="skip the 61-layer schedule timing")
     ap.add_argument("--prefill", action="store_true",
                     help="measure the chunked-prefill stack instead of decode (prints its own line)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -544,6 +592,16 @@ def main():
     out["cache_append"] = {"us_per_step": round(time_cache_append(L, torch, wl, 50), 2), "calls_per_step": 3,
                            "note": "kv_cache_append for CSA K|V, CSA indexer key (MXFP4) and HCA K|V, each new "
                                    "token completing a block (worst case); measured after the timed steps"}
+    if not args.no_schedule:
+        us_tok, per_layer = time_schedule(L, torch, [c for c, _ in steps], 5)
+        kvb = kv_bytes_per_token()
+        counts = {k: SCHEDULE.count(k) for k in ("csa", "hca", "swa")}
+        out["schedule_61"] = {
+            "layers": counts, "us_per_token_step": round(us_tok, 1), "queries_per_s": round(B / (us_tok / 1e6), 1),
+            "per_layer_us": per_layer,
+            "kv_bytes_per_token": round(sum(counts[k] * kvb[k] for k in counts), 1),
+            "note": "layers 0-1 HCA, 2-60 alternating CSA/HCA, MTP block window-only; each layer is one decode "
+                    "step of this workload (new block pooled every step); caches rotate over the replicas"}
     if not args.no_cpu_baseline:
         done, el = cpu_baseline(L, torch, synth, wl, args.cpu_seconds)
         out["cpu_baseline"] = {"value": round(done / el, 3), "unit": "queries/s", "cores": 1, "kind": "oracle",
