@@ -153,8 +153,13 @@ dsv4_status kv_cache_append(const void* x_new, int x_dt, const float* gate_new, 
  *   qi        [B, Q, HI, DI] of qi_dt;  wi [B, Q, HI] f32;  q_pos [B, Q] int32 (device).
  *   ki        [B, ki_bstride rows, DI] of ki_dt, or MXFP4 bytes [B, ki_bstride, DI/2] plus
  *             ki_scale [B, ki_bstride, DI/32]; ki_bstride == 0 means N.
- *   (qi_dt, ki_dt) in {(F32,F32), (BF16,BF16), (BF16,MXFP4), (FP8_E4M3,FP8_E4M3)};
- *   HI in {4,8,16} and DI in {32,64,128,256} (F32 pair: 1 <= HI <= 16, 1 <= DI <= 256);
+ *   (qi_dt, ki_dt) in {(F32,F32), (BF16,BF16), (BF16,MXFP4), (FP8_E4M3,FP8_E4M3),
+ *   (MXFP4,MXFP4)}; HI in {4,8,16} and DI in {32,64,128,256} (F32 pair: 1 <= HI <= 16,
+ *   1 <= DI <= 256; MXFP4 queries: DI in {128,256}).
+ *   MXFP4 queries ([P2 §5]: an FP4 indexer): qi holds the codes [B, Q, HI, DI/2] followed,
+ *   in the same allocation, by the E8M0 scales [B, Q, HI, DI/32] (csa_compress with m = 1
+ *   writes this layout given y = qi and y_scale = qi + B*Q*HI*DI/2); the products run on
+ *   the scaled FP4 MFMA, exact in fp32 for scales within the fp32 range.
  *   1 <= k <= 4096; N < 2^31; B*Q <= 65535.
  *   out_idx   [B, Q, k] int32.   out_score [B, Q, k] f32 (score of each selected index,
  *             -inf on padding) or NULL.

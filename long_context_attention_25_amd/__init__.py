@@ -151,11 +151,18 @@ def kv_cache_append(x_new, gate_new, pos, win, win_gate, pos_bias, m: int, cache
 
 
 def csa_index_topk(qi, wi, ki, q_pos, m: int, k: int, ki_scale=None, N=None, with_scores=False, workspace=None,
-                   out_idx=None, out_score=None):
+                   out_idx=None, out_score=None, qi_scale=None):
     """Indexer scores + per-query top-k.  qi [B,Q,HI,DI], wi [B,Q,HI] f32, ki [B,rows,DI]
     (or MXFP4 codes [B,rows,DI/2] uint8 with ki_scale [B,rows,DI/32]), q_pos [B,Q] int32.
+    MXFP4 queries: qi codes [B,Q,HI,DI/2] uint8 and qi_scale [B,Q,HI,DI/32], stored right
+    after the codes in one allocation.
     Returns idx [B,Q,k] int32 (and scores [B,Q,k] f32 with with_scores)."""
     B, Q, HI, DI = qi.shape
+    if qi.dtype == torch.uint8:
+        DI *= 2
+        if (qi_scale is None or not qi.is_contiguous() or not qi_scale.is_contiguous()
+                or qi_scale.data_ptr() != qi.data_ptr() + qi.numel()):
+            raise ValueError("MXFP4 queries: qi_scale must follow the codes qi in the same allocation")
     rows = ki.shape[1]
     N = rows if N is None else N
     kdt = _dt(ki)

@@ -240,6 +240,7 @@ dsv4_status csa_index_topk(const void* qi, int qi_dt, const float* wi, const voi
   else if (qi_dt == DSV4_BF16 && ki_dt == DSV4_BF16) kind = dsv4::KEY_BF16;
   else if (qi_dt == DSV4_BF16 && ki_dt == DSV4_MXFP4) kind = dsv4::KEY_MXFP4;
   else if (qi_dt == DSV4_FP8_E4M3 && ki_dt == DSV4_FP8_E4M3) kind = dsv4::KEY_FP8;
+  else if (qi_dt == DSV4_MXFP4 && ki_dt == DSV4_MXFP4) kind = dsv4::KEY_MXFP4_Q4;
   else return fail(DSV4_ERR_UNSUPPORTED, "%s: unsupported (qi_dt, ki_dt) = (%d, %d)", what, qi_dt, ki_dt);
   if (kind == dsv4::KEY_F32) {
     SUPPORT(HI >= 1 && HI <= 16, "%s: f32 path supports HI in [1, 16], got %d", what, HI);
@@ -247,18 +248,23 @@ dsv4_status csa_index_topk(const void* qi, int qi_dt, const float* wi, const voi
   } else {
     SUPPORT(HI == 4 || HI == 8 || HI == 16, "%s: HI must be 4, 8 or 16, got %d", what, HI);
     SUPPORT(DI == 32 || DI == 64 || DI == 128 || DI == 256, "%s: DI must be 32, 64, 128 or 256, got %d", what, DI);
+    if (kind == dsv4::KEY_MXFP4_Q4)
+      SUPPORT(DI == 128 || DI == 256, "%s: MXFP4 queries need DI of 128 or 256, got %d", what, DI);
   }
   const int64_t R = B * Q;
   if (R > 0) {
     REQUIRE(qi && wi && q_pos && out_idx, "%s: qi, wi, q_pos and out_idx must not be NULL", what);
     REQUIRE(N == 0 || ki, "%s: ki must not be NULL when N > 0", what);
-    if (kind == dsv4::KEY_MXFP4) REQUIRE(N == 0 || ki_scale, "%s: ki_scale must not be NULL for MXFP4", what);
+    if (kind == dsv4::KEY_MXFP4 || kind == dsv4::KEY_MXFP4_Q4)
+      REQUIRE(N == 0 || ki_scale, "%s: ki_scale must not be NULL for MXFP4", what);
   }
   bool query;
   dsv4_status s = workspace_check(what, workspace, ws_bytes, R > 0 ? dsv4::topk_workspace_bytes(R, N) : 0, &query);
   if (s != DSV4_OK || query || R == 0) return s;
   dsv4::IndexArgs a;
   a.qi = qi; a.wi = wi; a.ki = ki; a.ki_scale = ki_scale; a.kind = kind; a.q_pos = q_pos;
+  // MXFP4 queries: the scale bytes follow the codes in the same allocation
+  a.qi_scale = kind == dsv4::KEY_MXFP4_Q4 ? reinterpret_cast<const uint8_t*>(qi) + R * HI * (DI / 2) : nullptr;
   a.B = B; a.Q = Q; a.HI = HI; a.DI = DI; a.N = N; a.k_bs = ki_bstride ? ki_bstride : N;
   a.m = m; a.k = k; a.out_idx = out_idx; a.out_score = out_score;
   return launched(dsv4::launch_index_topk(a, dsv4::topk_workspace_carve(workspace, R, N), stream), what);

@@ -24,6 +24,8 @@
 
 namespace dsv4 {
 
+typedef int v8i32 __attribute__((ext_vector_type(8)));
+
 namespace {
 
 constexpr int kThreads = 256;
@@ -153,6 +155,11 @@ struct KeyTile<KEY_MXFP4, DI> {
   }
 };
 
+// MXFP4 keys for the FP4 x FP4 product: the raw code words and scale bytes feed the
+// scaled MFMA directly (lane g's 32-element block c is words 4c .. 4c+3, scale byte c).
+template <int DI>
+struct KeyTile<KEY_MXFP4_Q4, DI> : KeyTile<KEY_MXFP4, DI> {};
+
 template <int DI>
 struct KeyTile<KEY_FP8, DI> {
   static constexpr int KS = DI / 32;
@@ -169,9 +176,10 @@ struct KeyTile<KEY_FP8, DI> {
 // all of them (QTW > 1 when there are many queries, e.g. a prefill chunk).
 template <int KIND, int DI, int HI, int QTW>
 __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
-    const uint8_t* __restrict__ qi, const float* __restrict__ wi, const uint8_t* __restrict__ ki,
-    const uint8_t* __restrict__ ksc, const int32_t* __restrict__ q_pos, int64_t N, int64_t k_bs,
-    int64_t Q, int m, int64_t chunk, float* __restrict__ scores, int64_t sstride, uint32_t* __restrict__ hist_g) {
+    const uint8_t* __restrict__ qi, const uint8_t* __restrict__ qsc, const float* __restrict__ wi,
+    const uint8_t* __restrict__ ki, const uint8_t* __restrict__ ksc, const int32_t* __restrict__ q_pos, int64_t N,
+    int64_t k_bs, int64_t Q, int m, int64_t chunk, float* __restrict__ scores, int64_t sstride,
+    uint32_t* __restrict__ hist_g) {
   constexpr int QPT = 16 / HI;          // queries per 16-row MFMA tile
   constexpr int KS = DI / 32;
   constexpr int GPQ = HI / 4;           // lane groups per query slot
@@ -223,6 +231,9 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
   const int qs_a = col / HI, h_a = col % HI;
   uint4 qa16[QTW][KS];   // bf16 queries
   uint2 qa8[QTW][KS];    // fp8 queries
+  constexpr int KS4 = DI / 128 > 0 ? DI / 128 : 1;   // FP4 x FP4: 128-deep MFMA steps
+  uint4 qa4[QTW][KS4];   // MXFP4 query codes (32 per lane and step)
+  uint32_t qs4[QTW];     // their scale bytes (byte c: step c)
   // epilogue: accumulator row 4g+i -> (slot (4g+i)/HI, head (4g+i)%HI)
   const int qs_c = (4 * g) / HI;
   const int esel = g % GPQ;              // this lane's tile within a group of E emitted together
@@ -235,7 +246,16 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
     const int64_t qbase = b * Q + (qt0 + t) * QPT;
     const bool qa_ok = qs_a < nq[t];
     const int64_t qrow_a = (qa_ok ? qbase + qs_a : b * Q) * HI + h_a;
-    if constexpr (KIND == KEY_FP8) {
+    if constexpr (KIND == KEY_MXFP4_Q4) {
+      const uint4* p = reinterpret_cast<const uint4*>(qi + qrow_a * (DI / 2) + g * (DI / 8));
+#pragma unroll
+      for (int c = 0; c < KS4; ++c) qa4[t][c] = qa_ok ? p[c] : make_uint4(0, 0, 0, 0);
+      const uint8_t* sp = qsc + qrow_a * (DI / 32) + g * KS4;
+      uint32_t sv = 0;
+#pragma unroll
+      for (int c = 0; c < KS4; ++c) sv |= (uint32_t)sp[c] << (8 * c);
+      qs4[t] = qa_ok ? sv : 0x7f7f7f7fu;
+    } else if constexpr (KIND == KEY_FP8) {
       const uint2* p = reinterpret_cast<const uint2*>(qi + qrow_a * DI + g * (DI / 4));
 #pragma unroll
       for (int c = 0; c < KS; ++c) qa8[t][c] = qa_ok ? p[c] : make_uint2(0, 0);
@@ -275,11 +295,24 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
 #pragma unroll
         for (int j = 0; j < E; ++j) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (KIND == KEY_MXFP4_Q4) {
 #pragma unroll
-          for (int c = 0; c < KS; ++c) {
-            if constexpr (KIND == KEY_FP8)
-              acc = mfma_fp8(__builtin_bit_cast(long, qa8[t][c]), cur[u + j].op(c), acc);
-            else acc = mfma_bf16(bit_cast_to<bf16x8>(qa16[t][c]), cur[u + j].op(c), acc);
+            for (int c = 0; c < KS4; ++c) {
+              const auto& kt = cur[u + j];
+              const v8i32 av = {(int)qa4[t][c].x, (int)qa4[t][c].y, (int)qa4[t][c].z, (int)qa4[t][c].w, 0, 0, 0, 0};
+              const v8i32 bv = {(int)kt.w[4 * c], (int)kt.w[4 * c + 1], (int)kt.w[4 * c + 2], (int)kt.w[4 * c + 3],
+                                0, 0, 0, 0};
+              acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 4, 4, 0,
+                                                                      (int)((qs4[t] >> (8 * c)) & 0xffu), 0,
+                                                                      (int)((kt.sc >> (8 * c)) & 0xffu));
+            }
+          } else {
+#pragma unroll
+            for (int c = 0; c < KS; ++c) {
+              if constexpr (KIND == KEY_FP8)
+                acc = mfma_fp8(__builtin_bit_cast(long, qa8[t][c]), cur[u + j].op(c), acc);
+              else acc = mfma_bf16(bit_cast_to<bf16x8>(qa16[t][c]), cur[u + j].op(c), acc);
+            }
           }
           float v = wv[t][0] * fmaxf(acc[0], 0.f);
           v = fmaf(wv[t][1], fmaxf(acc[1], 0.f), v);
@@ -676,7 +709,8 @@ hipError_t launch_mfma_q(const IndexArgs& a, float* scores, uint32_t* hist, int6
   const int64_t slots = (int64_t)QTW * QPT < a.Q ? (int64_t)QTW * QPT : a.Q;
   size_t smem = (size_t)slots * kHistWords * sizeof(uint32_t);
   DSV4_LAUNCH_MAIN((index_mfma_kernel<KIND, DI, HI, QTW>), grid, dim3(kThreads), smem, st,
-                   reinterpret_cast<const uint8_t*>(a.qi), a.wi, reinterpret_cast<const uint8_t*>(a.ki), a.ki_scale,
+                   reinterpret_cast<const uint8_t*>(a.qi), a.qi_scale, a.wi, reinterpret_cast<const uint8_t*>(a.ki),
+                   a.ki_scale,
                    a.q_pos, a.N, a.k_bs, a.Q, a.m, chunk, scores, ((a.N + 63) / 64) * 64, hist);
   return hipGetLastError();
 }
@@ -697,6 +731,10 @@ hipError_t launch_mfma_di(const IndexArgs& a, float* scores, uint32_t* hist, int
 
 template <int KIND>
 hipError_t launch_mfma(const IndexArgs& a, float* scores, uint32_t* hist, int64_t chunk, hipStream_t st) {
+  if constexpr (KIND == KEY_MXFP4_Q4) {    // 128-deep FP4 MFMA steps: DI of 128 or 256
+    if (a.DI == 128) return launch_mfma_di<KIND, 128>(a, scores, hist, chunk, st);
+    return launch_mfma_di<KIND, 256>(a, scores, hist, chunk, st);
+  }
   switch (a.DI) {
     case 32: return launch_mfma_di<KIND, 32>(a, scores, hist, chunk, st);
     case 64: return launch_mfma_di<KIND, 64>(a, scores, hist, chunk, st);
@@ -760,6 +798,7 @@ hipError_t launch_index_topk(const IndexArgs& a, const TopkWorkspace& ws, hipStr
       int64_t chunk = per;
       if (a.kind == KEY_BF16) e = launch_mfma<KEY_BF16>(a, ws.scores, ws.hist, chunk, st);
       else if (a.kind == KEY_FP8) e = launch_mfma<KEY_FP8>(a, ws.scores, ws.hist, chunk, st);
+      else if (a.kind == KEY_MXFP4_Q4) e = launch_mfma<KEY_MXFP4_Q4>(a, ws.scores, ws.hist, chunk, st);
       else e = launch_mfma<KEY_MXFP4>(a, ws.scores, ws.hist, chunk, st);
     }
     if (e != hipSuccess) return e;

@@ -55,10 +55,12 @@ struct AppendArgs {
 hipError_t launch_append(const AppendArgs& a, hipStream_t st);
 
 // ---------------------------------------------------------------- indexer + top-k
-enum KeyKind { KEY_F32 = 0, KEY_BF16 = 1, KEY_FP8 = 2, KEY_MXFP4 = 3 };
+// KEY_MXFP4: bf16 queries x MXFP4 keys; KEY_MXFP4_Q4: MXFP4 queries x MXFP4 keys
+enum KeyKind { KEY_F32 = 0, KEY_BF16 = 1, KEY_FP8 = 2, KEY_MXFP4 = 3, KEY_MXFP4_Q4 = 4 };
 
 struct IndexArgs {
   const void* qi;
+  const uint8_t* qi_scale;   // MXFP4 queries: E8M0 scales [B, Q, HI, DI/32]
   const float* wi;
   const void* ki;
   const uint8_t* ki_scale;

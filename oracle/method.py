@@ -33,7 +33,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .codecs import rows
+from .codecs import decode_mxfp4, encode_mxfp4, rows
 
 
 # --------------------------------------------------------------------------- compression
@@ -82,6 +82,17 @@ def index_scores(qi, wi, ki, q_pos, m: int) -> np.ndarray:
             dots = qi[b, q] @ kb[:n].T                       # [HI, n]
             s[b, q, :n] = wi[b, q] @ np.maximum(dots, 0.0)
     return s
+
+
+def index_scores_fp4(qi32, wi, ki, q_pos, m: int):
+    """Indexer scores with FP4 queries as well as FP4 keys  [P2§4] (FP4 lightning indexer),
+    [P2§5]: the queries go through the MXFP4 quantiser (codecs.encode_mxfp4, per 32-element
+    group of each head row) and the scores are then those of index_scores on the decoded
+    values.  Returns (scores, query codes, query scales): the codes and scales are the
+    bytes the quantised queries are stored as.
+    """
+    codes, scales = encode_mxfp4(np.asarray(qi32, dtype=np.float32))
+    return index_scores(decode_mxfp4(codes, scales), wi, ki, q_pos, m), codes, scales
 
 
 def topk(s: np.ndarray, q_pos, m: int, k: int) -> np.ndarray:

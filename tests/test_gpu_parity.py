@@ -311,6 +311,40 @@ def test_index_topk_mxfp4_keys():
         assert check_topk(idx[b, 0], s_ref[b, 0], int(nvis[b, 0]), k) <= 2
 
 
+@pytest.mark.parametrize("DI", [128, 256])
+def test_index_topk_fp4_queries_and_keys(DI):
+    """FP4 x FP4 indexer: queries quantised by the library (bit-equal to the oracle's MXFP4
+    encoder), keys in MXFP4; scores on the scaled FP4 MFMA against the oracle's FP4-query
+    mode."""
+    cfg = 215
+    B, Q, HI, N, m, k = 2, 3, 8, 5000, 4, 256
+    q32 = synth.normal(cfg, synth.QI, (B, Q, HI, DI))
+    w = synth.uniform(cfg, synth.WI, (B, Q, HI))
+    k32 = synth.normal(cfg, synth.KI, (B, N, DI))
+    pos = np.array([[4 * N - 1, 4 * 3000 + 2, 4 * 50], [4 * N - 3, 4 * N - 1, 7]], dtype=np.int32)
+    kp, ks = codecs.encode_mxfp4(k32)
+    R = B * Q * HI
+    qbuf = torch.empty(R * DI // 2 + R * DI // 32, dtype=torch.uint8, device="cuda")
+    qc, qs = qbuf[:R * DI // 2].view(1, R, DI // 2), qbuf[R * DI // 2:].view(1, R, DI // 32)
+    L.csa_compress(dev(q32.reshape(1, R, DI)), dev(np.zeros((1, R), np.float32)), dev(np.zeros(1, np.float32)), 1,
+                   L.MXFP4_DTYPE, out=qc, out_scale=qs)
+    s_ref, qp_ref, qs_ref = method.index_scores_fp4(q32, w, codecs.decode_mxfp4(kp, ks), pos, m)
+    assert np.array_equal(qc.cpu().numpy().reshape(qp_ref.shape), qp_ref)
+    assert np.array_equal(qs.cpu().numpy().reshape(qs_ref.shape), qs_ref)
+    idx, sc = L.csa_index_topk(qc.view(B, Q, HI, DI // 2), dev(w), dev(kp), dev(pos), m, k, ki_scale=dev(ks),
+                               qi_scale=qs.view(B, Q, HI, DI // 32), with_scores=True)
+    torch.cuda.synchronize()
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+    nvis = method.visible_blocks(pos, m, N)
+    for b in range(B):
+        for q in range(Q):
+            n = int(nvis[b, q])
+            check_topk(idx[b, q], s_ref[b, q], n, k)
+            take = min(k, n)
+            ref = s_ref[b, q, idx[b, q, :take]]
+            assert np.all(np.abs(sc[b, q, :take] - ref) <= 1e-5 * np.abs(s_ref[b, q, :n]).max() + 1e-6)
+
+
 def test_index_topk_fp8():
     cfg = 220
     B, Q, HI, DI, N, m, k = 1, 4, 8, 128, 3000, 4, 300

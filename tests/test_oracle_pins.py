@@ -202,6 +202,30 @@ def test_indexer_matches_brute_force():
                     assert s[b, t, j] == -np.inf
 
 
+def test_indexer_fp4_queries_hand_example_and_grid_identity():
+    """FP4-query scores: a hand-quantised query, and queries already on the MXFP4 grid
+    (each group's largest magnitude 4 or 6 times a power of two) pass unchanged."""
+    # 0.3 alone in its group: shared exponent floor(log2 0.3) - 2 = -4, 0.3 / 2^-4 = 4.8 -> 4,
+    # so the query becomes 0.25; key e0, weight 1: score relu(0.25) = 0.25
+    q = np.zeros((1, 1, 1, 32), np.float32)
+    q[0, 0, 0, 0] = 0.3
+    k = np.zeros((1, 3, 32))
+    k[0, :, 0] = [1.0, -2.0, 8.0]
+    s, codes, scales = method.index_scores_fp4(q, np.ones((1, 1, 1)), k, np.array([[11]]), 4)
+    assert np.allclose(s[0, 0], [0.25, 0.0, 2.0], rtol=0, atol=0)
+    assert scales[0, 0, 0, 0] == 127 - 4 and (codes[0, 0, 0, 0] & 0xF) == 0b0110       # e2m1 code of 4.0
+    r = _rng(23)
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    q = grid[r.integers(0, 8, (2, 2, 3, 64))] * np.where(r.random((2, 2, 3, 64)) < 0.5, -1.0, 1.0)
+    q[..., ::32] = np.where(r.random(q[..., ::32].shape) < 0.5, 4.0, 6.0)              # group maxima
+    q = (q * np.exp2(r.integers(-3, 4, (2, 2, 3, 2))).repeat(32, axis=-1)).astype(np.float32)
+    w = r.random((2, 2, 3))
+    k = r.standard_normal((2, 9, 64))
+    pos = np.array([[35, 20], [7, 100]])
+    s4, _, _ = method.index_scores_fp4(q, w, k, pos, 4)
+    assert np.array_equal(s4, method.index_scores(q, w, k, pos, 4))
+
+
 # ============================================================ top-k
 def test_topk_worked_ties():
     g = GOLD["topk_ties"]
