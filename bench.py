@@ -378,7 +378,40 @@ def source_sha(path):
 
 # ------------------------------------------------------------------------------------ prefill
 PF_T, PF_P0, PF_K = 4096, 262144, 512           # chunk tokens, cached raw tokens, top-k
-PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
+
+
+def time_index_kernel(L, torch, call, n):
+    """Average duration (ms) of the indexer kernel of csa_index_topk over n calls, from HIP
+    events attached to that kernel's launch; call(lib) issues one csa_index_topk."""
+    lib = L.lib()
+    ev = HipEvents()
+    call(lib)
+    torch.cuda.synchronize()
+    pairs = [(ev.create(), ev.create()) for _ in range(n)]
+    for p in pairs:
+        lib.dsv4_time_next_kernel(*p)
+        call(lib)
+    torch.cuda.synchronize()
+    return sum(ev.elapsed_ms(*p) for p in pairs) / n
+
+
+def fp4_index_decode(L, torch, wl):
+    """The decode workload's indexer (8 x 262,144 MXFP4 keys) with MXFP4 queries on the
+    scaled FP4 MFMA: main-kernel microseconds, next to the bf16-query figure of the step."""
+    t = wl.r[0]
+    R = B * HI
+    qbuf = torch.empty(R * DI // 2 + R * DI // 32, dtype=torch.uint8, device="cuda")
+    qc, qs = qbuf[:R * DI // 2].view(1, R, DI // 2), qbuf[R * DI // 2:].view(1, R, DI // 32)
+    L.csa_compress(t["qi"].view(1, R, DI).float(), torch.zeros((1, R), device="cuda"),
+                   torch.zeros(1, device="cuda"), 1, L.MXFP4_DTYPE, out=qc, out_scale=qs)
+    idx = torch.empty((B, 1, TOPK), dtype=torch.int32, device="cuda")
+    ws = torch.empty(t["ws_idx"].numel(), dtype=torch.uint8, device="cuda")     # same shapes as the step's call
+
+    def call(lib):
+        L.csa_index_topk(qc.view(B, 1, HI, DI // 2), t["wi"], t["ki"], wl.q_pos, M_CSA, TOPK, ki_scale=t["ks"],
+                         qi_scale=qs.view(B, 1, HI, DI // 32), out_idx=idx, workspace=ws)
+    return time_index_kernel(L, torch, call, 20) * 1e3
 
 
 def prefill_flops():
@@ -474,6 +507,23 @@ def run_prefill(L, torch, synth, steps, warmup):
     ideal_ms = 2 * (f_idx / PEAK_TFLOPS["fp8"] + f_csa / PEAK_TFLOPS["bf16"] + f_hca / PEAK_TFLOPS["bf16"]) / 1e9
     kern = lambda f, kms, pk: {"avg_launch_ms": round(kms, 4), "tflops": round(f / kms / 1e9, 1),
                                "frac_of_peak": round(f / kms / 1e9 / PEAK_TFLOPS[pk], 4), "flops": f}
+    # the CSA indexer again with MXFP4 queries and keys (scaled FP4 MFMA), same shapes
+    t0 = layers[0]
+    n = t0["ki"].shape[1]
+    k4 = torch.empty((1, n, DI // 2), dtype=torch.uint8, device="cuda")
+    k4s = torch.empty((1, n, DI // 32), dtype=torch.uint8, device="cuda")
+    L.csa_compress(synth.device_normal((1, n, DI), seed(7, synth.KI, 0), bf), torch.zeros((1, n), device="cuda"),
+                   torch.zeros(1, device="cuda"), 1, L.MXFP4_DTYPE, out=k4, out_scale=k4s)
+    R = T * HI
+    qbuf = torch.empty(R * DI // 2 + R * DI // 32, dtype=torch.uint8, device="cuda")
+    qc, qs = qbuf[:R * DI // 2].view(1, R, DI // 2), qbuf[R * DI // 2:].view(1, R, DI // 32)
+    L.csa_compress(synth.device_normal((1, R, DI), seed(7, synth.QI, 0), bf), torch.zeros((1, R), device="cuda"),
+                   torch.zeros(1, device="cuda"), 1, L.MXFP4_DTYPE, out=qc, out_scale=qs)
+
+    def fp4_call(lib_):
+        L.csa_index_topk(qc.view(1, T, HI, DI // 2), t0["wi"], k4, qpos, M_CSA, PF_K, ki_scale=k4s,
+                         qi_scale=qs.view(1, T, HI, DI // 32), out_idx=t0["idx"], workspace=ws.get("idx"))
+    k_fp4 = time_index_kernel(L, torch, fp4_call, max(2, steps))
     return {
         "metric": "chunked prefill MFMA utilisation (4-layer CSA/HCA stack, 4096-token chunk, 256K cache)",
         "value": round(ideal_ms / ms, 4), "unit": "fraction of dense MFMA peak", "n_gpus": 1, "steps": steps,
@@ -486,6 +536,8 @@ def run_prefill(L, torch, synth, steps, warmup):
         "kernels": {"index_mfma_kernel (fp8)": kern(f_idx, k_idx, "fp8"),
                     "attend_bf16_kernel (CSA)": kern(f_csa, k_csa, "bf16"),
                     "attend_bf16_kernel (HCA)": kern(f_hca, k_hca, "bf16")},
+        "fp4_indexer": dict(kern(f_idx, k_fp4, "fp4"), note="the CSA layer's indexer with MXFP4 queries and keys "
+                            "on the scaled FP4 MFMA (outside the stack timing)"),
     }
 
 
@@ -589,6 +641,10 @@ def main():
                      "timed_launches": len(pairs)},
         "kernels": kernels,
     }
+    out["fp4_indexer"] = {"avg_launch_us": round(fp4_index_decode(L, torch, wl), 2),
+                          "bf16_query_avg_launch_us": kernels["index_mfma_kernel"]["avg_launch_us"],
+                          "note": "the same 8 x 262144 MXFP4 keys with MXFP4 queries (scaled FP4 MFMA); "
+                                  "main kernel only, measured after the timed steps"}
     out["cache_append"] = {"us_per_step": round(time_cache_append(L, torch, wl, 50), 2), "calls_per_step": 3,
                            "note": "kv_cache_append for CSA K|V, CSA indexer key (MXFP4) and HCA K|V, each new "
                                    "token completing a block (worst case); measured after the timed steps"}
