@@ -69,12 +69,12 @@ KERNEL_BYTES = {
 # the counter's reading for a 256 MiB device copy (see profiles/).  An entry is used only
 # while the kernel source it was measured on is unchanged (sha256 of the file).
 MEASURED_TRAFFIC = {
-    "index_mfma_kernel": {"bytes_per_launch": 151622137,
-                          "source_sha256": "c256a9e77bde90a1ff55a4067b23c4eac0b3213c76df8c15acb0fa5838c9abe2"},
-    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 155952514,
-                                 "source_sha256": "d0d37601a00f1260fb161d716d19eaa9c871cea3f43a5da7235b46c9ab394525"},
-    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32767598,
-                                 "source_sha256": "d0d37601a00f1260fb161d716d19eaa9c871cea3f43a5da7235b46c9ab394525"},
+    "index_mfma_kernel": {"bytes_per_launch": 151634139,
+                          "source_sha256": "42978ac55e131ad1a4b16b8e7d7b0bd2ac9e9e1bc3045c0d21a5f8fdd9368a38"},
+    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 156013708,
+                                 "source_sha256": "e6876c97d029158c70d3c397b6a31282324e802f6e3819760260e27c9991451f"},
+    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32818319,
+                                 "source_sha256": "e6876c97d029158c70d3c397b6a31282324e802f6e3819760260e27c9991451f"},
 }
 
 
