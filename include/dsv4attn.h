@@ -221,6 +221,40 @@ dsv4_status hca_attend(const void* q, const void* kc, const void* vc, int dt, in
                        void* out, float* lse, void* workspace, size_t* ws_bytes, hipStream_t stream);
 
 /*
+ * csa_attend_fp8kv, hca_attend_fp8kv — csa_attend / hca_attend over K/V caches stored in
+ * FP8 with the RoPE dims of K kept in BF16  [P2 §5] (most of each KV entry in FP8, the
+ * RoPE dims in BF16), dequantised inside the attention kernel.
+ *
+ *   K row (kc and kw): D - d_rope E4M3 codes (bytes), then d_rope bf16 values (the RoPE
+ *       dims, the last d_rope dims of the head), i.e. D + d_rope bytes.
+ *   V row (vc and vw): D E4M3 codes.
+ *   Decoded K = [k_scale * e4m3(code) for the code dims, the bf16 values as they are];
+ *   decoded V = v_scale * e4m3(code).  One scale per tensor kind (compressed and window
+ *   rows share it).  The result is the bf16 call's result on the decoded K and V: the
+ *   codes are decoded exactly, k_scale multiplies the fp32 partial scores of the code
+ *   dims and v_scale the fp32 output, so both are applied without an extra rounding.
+ *   q, out: bf16 as in csa_attend; lse f32.  D = 512, d_rope = 64, H in {16, 32, 48, 64}.
+ *   kv_rstride, w_rstride: BYTES from one row to the next, shared by K and V rows (so a K
+ *   row and its V row may sit side by side in one row of D + d_rope + D bytes); 0 means
+ *   D + d_rope for K rows and D for V rows.  Nonzero strides: multiples of 16, >= D +
+ *   d_rope.  kc, vc, kw, vw 16-byte aligned.  k_scale, v_scale finite.
+ *   Every other argument, the workspace protocol and the errors are as for csa_attend /
+ *   hca_attend.
+ */
+dsv4_status csa_attend_fp8kv(const void* q, const void* kc, const void* vc, const int32_t* idx, int32_t k,
+                             const void* kw, const void* vw, const int32_t* win_pos0, int64_t L, int32_t W,
+                             const int32_t* q_pos, int64_t B, int64_t Q, int32_t H, int32_t D, int32_t d_rope,
+                             int64_t N, int64_t kv_bstride, int64_t kv_rstride, int64_t w_rstride, float k_scale,
+                             float v_scale, float scale, void* out, float* lse, void* workspace, size_t* ws_bytes,
+                             hipStream_t stream);
+dsv4_status hca_attend_fp8kv(const void* q, const void* kc, const void* vc, int32_t m, const void* kw,
+                             const void* vw, const int32_t* win_pos0, int64_t L, int32_t W, const int32_t* q_pos,
+                             int64_t B, int64_t Q, int32_t H, int32_t D, int32_t d_rope, int64_t N,
+                             int64_t kv_bstride, int64_t kv_rstride, int64_t w_rstride, float k_scale,
+                             float v_scale, float scale, void* out, float* lse, void* workspace, size_t* ws_bytes,
+                             hipStream_t stream);
+
+/*
  * lse_merge — combine attention results over P disjoint key sets (e.g. the compressed
  * part and the window part, or the shards of a split key range) into the result over
  * their union:

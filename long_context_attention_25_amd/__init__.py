@@ -12,7 +12,8 @@ import os
 
 import torch
 
-__all__ = ["csa_compress", "kv_cache_append", "csa_index_topk", "csa_attend", "hca_attend", "lse_merge", "lib",
+__all__ = ["csa_compress", "kv_cache_append", "csa_index_topk", "csa_attend", "hca_attend", "csa_attend_fp8kv",
+           "hca_attend_fp8kv", "lse_merge", "lib",
            "LibError",
            "F32", "BF16", "FP8_E4M3", "MXFP4", "MXFP4_DTYPE"]
 
@@ -41,6 +42,12 @@ _SIGS = {
     "hca_attend": ([_p, _p, _p, ctypes.c_int, _i32, _p, _p, _p, _i64, _i32, _p, _i64, _i64, _i32, _i32, _i64, _i64,
                     _i64, _i64, ctypes.c_float, _p, _p, _p, ctypes.POINTER(ctypes.c_size_t), _p], ctypes.c_int),
     "lse_merge": ([_p, _p, _i32, _i64, _i32, _p, ctypes.c_int, _p, _p], ctypes.c_int),
+    "csa_attend_fp8kv": ([_p, _p, _p, _p, _i32, _p, _p, _p, _i64, _i32, _p, _i64, _i64, _i32, _i32, _i32, _i64, _i64,
+                          _i64, _i64, ctypes.c_float, ctypes.c_float, ctypes.c_float, _p, _p, _p,
+                          ctypes.POINTER(ctypes.c_size_t), _p], ctypes.c_int),
+    "hca_attend_fp8kv": ([_p, _p, _p, _i32, _p, _p, _p, _i64, _i32, _p, _i64, _i64, _i32, _i32, _i32, _i64, _i64,
+                          _i64, _i64, ctypes.c_float, ctypes.c_float, ctypes.c_float, _p, _p, _p,
+                          ctypes.POINTER(ctypes.c_size_t), _p], ctypes.c_int),
 }
 
 
@@ -217,6 +224,70 @@ def hca_attend(q, kc, vc, m: int, kw, vw, win_pos0, W: int, q_pos, scale: float,
             D, N, kv_bs, kv_rs, w_rs, float(scale), _ptr(out), _ptr(lse))
     ws, n = _workspace(lambda n: lib().hca_attend(*args, None, ctypes.byref(n), _stream()), workspace)
     _check(lib().hca_attend(*args, _ptr(ws), n, _stream()))
+    return out, lse
+
+
+FP8_ROPE_DIMS = 64   # bf16 tail of an FP8 K row
+
+
+def _fp8kv_common(q, kc, vc, kw, vw, N, d_rope):
+    """Byte strides of FP8 K/V rows (uint8 tensors [B, rows, bytes], last dimension
+    contiguous): K rows of D + d_rope bytes, V rows of D bytes, either each in its own
+    tensor (natural strides) or sharing one row stride (e.g. K and V side by side)."""
+    B, Q, H, D = q.shape
+    N = kc.shape[1] if N is None else N
+    for t in (kc, vc, kw, vw):
+        if t.dtype != torch.uint8 or t.stride(-1) != 1:
+            raise ValueError("FP8 K/V rows are uint8 tensors with a contiguous last dimension")
+    if kc.shape[-1] != D + d_rope or vc.shape[-1] != D or kw.shape[-1] != D + d_rope or vw.shape[-1] != D:
+        raise ValueError("K rows must hold D + d_rope bytes and V rows D bytes")
+
+    def rows(k, v):
+        if k.stride(1) == v.stride(1):
+            rs = k.stride(1)
+            if B > 1 and k.stride(0) != v.stride(0):
+                raise ValueError("K and V batches must be equally far apart")
+            return rs, (k.stride(0) // rs if B > 0 else 0)
+        if k.stride(1) != D + d_rope or v.stride(1) != D:
+            raise ValueError("K and V rows must share a row stride or be packed")
+        kb, vb = k.stride(0) // k.stride(1), v.stride(0) // v.stride(1)
+        if B > 1 and kb != vb:
+            raise ValueError("K and V batches must hold the same number of rows")
+        return 0, (kb if B > 0 else 0)
+
+    kv_rs, kv_bs = rows(kc, vc)
+    w_rs, w_bs = rows(kw, vw)
+    L = kw.shape[1]
+    if B > 1 and w_bs != L:
+        raise ValueError("kw/vw batches must be L rows apart")
+    return B, Q, H, D, N, kv_bs, L, kv_rs, w_rs
+
+
+def csa_attend_fp8kv(q, kc, vc, idx, kw, vw, win_pos0, W: int, q_pos, scale: float, k_scale: float = 1.0,
+                     v_scale: float = 1.0, d_rope: int = FP8_ROPE_DIMS, N=None, workspace=None, out=None, lse=None):
+    """csa_attend over FP8 K/V rows (K: D - d_rope E4M3 codes then d_rope bf16 values; V: D
+    E4M3 codes; decoded K codes x k_scale, V codes x v_scale).  q and the output are bf16."""
+    B, Q, H, D, N, kv_bs, L, kv_rs, w_rs = _fp8kv_common(q, kc, vc, kw, vw, N, d_rope)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Q, H), dtype=torch.float32, device=q.device) if lse is None else lse
+    args = (_ptr(q), _ptr(kc), _ptr(vc), _ptr(idx), idx.shape[2], _ptr(kw), _ptr(vw), _ptr(win_pos0), L, W,
+            _ptr(q_pos), B, Q, H, D, d_rope, N, kv_bs, kv_rs, w_rs, float(k_scale), float(v_scale), float(scale),
+            _ptr(out), _ptr(lse))
+    ws, n = _workspace(lambda n: lib().csa_attend_fp8kv(*args, None, ctypes.byref(n), _stream()), workspace)
+    _check(lib().csa_attend_fp8kv(*args, _ptr(ws), n, _stream()))
+    return out, lse
+
+
+def hca_attend_fp8kv(q, kc, vc, m: int, kw, vw, win_pos0, W: int, q_pos, scale: float, k_scale: float = 1.0,
+                     v_scale: float = 1.0, d_rope: int = FP8_ROPE_DIMS, N=None, workspace=None, out=None, lse=None):
+    """hca_attend over FP8 K/V rows (layout as csa_attend_fp8kv)."""
+    B, Q, H, D, N, kv_bs, L, kv_rs, w_rs = _fp8kv_common(q, kc, vc, kw, vw, N, d_rope)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Q, H), dtype=torch.float32, device=q.device) if lse is None else lse
+    args = (_ptr(q), _ptr(kc), _ptr(vc), m, _ptr(kw), _ptr(vw), _ptr(win_pos0), L, W, _ptr(q_pos), B, Q, H, D,
+            d_rope, N, kv_bs, kv_rs, w_rs, float(k_scale), float(v_scale), float(scale), _ptr(out), _ptr(lse))
+    ws, n = _workspace(lambda n: lib().hca_attend_fp8kv(*args, None, ctypes.byref(n), _stream()), workspace)
+    _check(lib().hca_attend_fp8kv(*args, _ptr(ws), n, _stream()))
     return out, lse
 
 

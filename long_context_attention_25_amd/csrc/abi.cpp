@@ -123,6 +123,48 @@ dsv4::AttendArgs to_args(const AttendCommon& c, bool csa, const int32_t* idx, in
   return a;
 }
 
+// FP8 K/V rows (csa_attend_fp8kv / hca_attend_fp8kv): the shared checks with bf16 queries
+// and outputs, then the row format, byte strides, alignment and scales.
+struct Fp8Kv {
+  int32_t d_rope;
+  float k_scale, v_scale;
+};
+dsv4_status check_attend_fp8(const char* what, const AttendCommon& c, const Fp8Kv& f) {
+  AttendCommon e = c;
+  e.dt = DSV4_BF16;
+  e.kv_rstride = 0;   // byte strides, checked below
+  e.w_rstride = 0;
+  dsv4_status s = check_attend(what, e);
+  if (s != DSV4_OK) return s;
+  SUPPORT(c.D == 512, "%s: FP8 K/V rows support D = 512, got %d", what, c.D);
+  SUPPORT(f.d_rope == dsv4::kFp8RopeDims, "%s: FP8 K/V rows support d_rope = %d, got %d", what,
+          dsv4::kFp8RopeDims, f.d_rope);
+  const int64_t kb = c.D + f.d_rope;   // bytes of a K row (codes + bf16 dims)
+  REQUIRE(c.kv_rstride == 0 || (c.kv_rstride >= kb && c.kv_rstride % 16 == 0),
+          "%s: kv_rstride (%lld bytes) must be 0 or a multiple of 16 that is >= %lld", what,
+          (long long)c.kv_rstride, (long long)kb);
+  REQUIRE(c.w_rstride == 0 || (c.w_rstride >= kb && c.w_rstride % 16 == 0),
+          "%s: w_rstride (%lld bytes) must be 0 or a multiple of 16 that is >= %lld", what, (long long)c.w_rstride,
+          (long long)kb);
+  for (const void* p : {c.kc, c.vc, c.kw, c.vw})
+    REQUIRE(((uintptr_t)p & 15) == 0, "%s: kc, vc, kw and vw must be 16-byte aligned", what);
+  REQUIRE(f.k_scale == f.k_scale && f.v_scale == f.v_scale && f.k_scale - f.k_scale == 0.f &&
+              f.v_scale - f.v_scale == 0.f,
+          "%s: k_scale and v_scale must be finite", what);
+  return ok();
+}
+
+void to_args_fp8(dsv4::AttendArgs& a, const AttendCommon& c, const Fp8Kv& f) {
+  a.f8 = true;
+  a.k_scale = f.k_scale;
+  a.v_scale = f.v_scale;
+  const int64_t kb = c.D + f.d_rope;
+  a.kv_rs = c.kv_rstride ? c.kv_rstride : kb;
+  a.v_rs = c.kv_rstride ? c.kv_rstride : c.D;
+  a.w_rs = c.w_rstride ? c.w_rstride : kb;
+  a.wv_rs = c.w_rstride ? c.w_rstride : c.D;
+}
+
 dsv4_status run_attend(const char* what, const dsv4::AttendArgs& a, void* ws, size_t* ws_bytes, hipStream_t st) {
   dsv4::AttendPlan p = dsv4::plan_attend(a);
   bool query;
@@ -297,6 +339,42 @@ dsv4_status hca_attend(const void* q, const void* kc, const void* vc, int dt, in
   if (s != DSV4_OK) return s;
   REQUIRE(m >= 1, "%s: m must be >= 1", what);
   return run_attend(what, to_args(c, false, nullptr, 0, m, lse), workspace, ws_bytes, stream);
+}
+
+dsv4_status csa_attend_fp8kv(const void* q, const void* kc, const void* vc, const int32_t* idx, int32_t k,
+                             const void* kw, const void* vw, const int32_t* win_pos0, int64_t L, int32_t W,
+                             const int32_t* q_pos, int64_t B, int64_t Q, int32_t H, int32_t D, int32_t d_rope,
+                             int64_t N, int64_t kv_bstride, int64_t kv_rstride, int64_t w_rstride, float k_scale,
+                             float v_scale, float scale, void* out, float* lse, void* workspace, size_t* ws_bytes,
+                             hipStream_t stream) {
+  const char* what = "csa_attend_fp8kv";
+  AttendCommon c{q, kc, vc, kw, vw, DSV4_BF16, win_pos0, q_pos, L, W, B, Q, H, D, N, kv_bstride, kv_rstride,
+                 w_rstride, scale, out};
+  const Fp8Kv f{d_rope, k_scale, v_scale};
+  dsv4_status s = check_attend_fp8(what, c, f);
+  if (s != DSV4_OK) return s;
+  REQUIRE(k >= 0 && k <= 65536, "%s: k must be in [0, 65536]", what);
+  if (B * Q > 0 && k > 0) REQUIRE(idx, "%s: idx must not be NULL", what);
+  dsv4::AttendArgs a = to_args(c, true, idx, k, 1, lse);
+  to_args_fp8(a, c, f);
+  return run_attend(what, a, workspace, ws_bytes, stream);
+}
+
+dsv4_status hca_attend_fp8kv(const void* q, const void* kc, const void* vc, int32_t m, const void* kw, const void* vw,
+                             const int32_t* win_pos0, int64_t L, int32_t W, const int32_t* q_pos, int64_t B,
+                             int64_t Q, int32_t H, int32_t D, int32_t d_rope, int64_t N, int64_t kv_bstride,
+                             int64_t kv_rstride, int64_t w_rstride, float k_scale, float v_scale, float scale,
+                             void* out, float* lse, void* workspace, size_t* ws_bytes, hipStream_t stream) {
+  const char* what = "hca_attend_fp8kv";
+  AttendCommon c{q, kc, vc, kw, vw, DSV4_BF16, win_pos0, q_pos, L, W, B, Q, H, D, N, kv_bstride, kv_rstride,
+                 w_rstride, scale, out};
+  const Fp8Kv f{d_rope, k_scale, v_scale};
+  dsv4_status s = check_attend_fp8(what, c, f);
+  if (s != DSV4_OK) return s;
+  REQUIRE(m >= 1, "%s: m must be >= 1", what);
+  dsv4::AttendArgs a = to_args(c, false, nullptr, 0, m, lse);
+  to_args_fp8(a, c, f);
+  return run_attend(what, a, workspace, ws_bytes, stream);
 }
 
 dsv4_status lse_merge(const float* o_parts, const float* lse_parts, int32_t P, int64_t R, int32_t D, void* out,

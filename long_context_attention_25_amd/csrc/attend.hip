@@ -47,7 +47,7 @@ struct KeyRange {
 __device__ __forceinline__ KeyRange key_range(const AttendArgs& a, int64_t p, int64_t wp0) {
   KeyRange r;
   if (a.csa) {
-    r.n_c = a.k;
+    r.n_c = a.N > 0 ? a.k : 0;   // with no compressed entries every list slot is empty
   } else {
     int64_t n = p < 0 ? 0 : (p + 1) / a.m;
     r.n_c = n < a.N ? n : a.N;
@@ -87,8 +87,8 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 // Pointer held by lane `src` (src < 64): a scalar readlane when `src` is the same for the
 // whole wave, a cross-lane shuffle otherwise.
-template <bool kUniform>
-__device__ __forceinline__ const uint16_t* lane_ptr(const uint16_t* p, int src) {
+template <bool kUniform, typename T>
+__device__ __forceinline__ const T* lane_ptr(const T* p, int src) {
   const uint64_t v = reinterpret_cast<uint64_t>(p);
   uint32_t lo, hi;
   if constexpr (kUniform) {
@@ -98,7 +98,7 @@ __device__ __forceinline__ const uint16_t* lane_ptr(const uint16_t* p, int src) 
     lo = (uint32_t)__shfl((int)(uint32_t)v, src);
     hi = (uint32_t)__shfl((int)(uint32_t)(v >> 32), src);
   }
-  return reinterpret_cast<const uint16_t*>(((uint64_t)hi << 32) | lo);
+  return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
 }
 
 // Async copy of 16 bytes per lane from global memory (per-lane address) into LDS at byte
@@ -149,10 +149,18 @@ __device__ __forceinline__ void tile_barrier() {
 // bytes, V: +32 bytes) so that the K operand reads (16 rows, same column) and the
 // transposed V reads (4 rows x 2 chunks per 16 lanes) hit distinct banks while every read
 // of a lane uses one base address plus immediate offsets.
-template <int D, int DS>
-__global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a, int64_t chunk, int splits,
-                                                               uint16_t* __restrict__ o_part,
-                                                               float* __restrict__ lse_part) {
+//
+// F8 (K/V rows stored as e4m3 codes, the last kFp8RopeDims dims of K as bf16): the copies
+// land in a separate four-stage ring of packed fp8 rows, and one tile ahead of its use
+// every tile is decoded (exactly: each e4m3 value is a bf16 value) into one of two bf16
+// tiles of the layout above, which the same MFMA code then reads.  The K scale multiplies
+// the scores of the fp8 dims only, and the V scale the output, so both stay exact.  Here
+// the k-steps take the head dims in natural order (k-step c: dims 32c .. 32c+31) so that
+// the bf16 dims form whole k-steps with their own accumulator.
+template <int D, int DS, bool F8>
+__device__ __forceinline__ void attend_body(const AttendArgs& a, int64_t chunk, int splits,
+                                            uint16_t* __restrict__ o_part, float* __restrict__ lse_part) {
+  using E = typename std::conditional<F8, uint8_t, uint16_t>::type;   // row pointer unit
   constexpr int KT = 16;                   // keys per tile
   constexpr int NT = kThreads * DS;
   constexpr int NWV = NT / kWave;
@@ -167,10 +175,19 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
   constexpr int NL = 2 * RPW;              // copy instructions per wave and tile
   constexpr int KTB = KT * KSTR, VTB = KT * VSTR;
   static_assert(LPR <= kWave && kWave % LPR == 0, "a row is copied by one instruction");
-  static_assert(3 * NL < 64, "vmcnt range");
+  static_assert(3 * NL < 64 && 4 * NL < 64, "vmcnt range");
+  // fp8 rows: K = DN e4m3 bytes + DR bf16 values, V = D e4m3 bytes (packed in the ring)
+  constexpr int DR = F8 ? kFp8RopeDims : 0;
+  constexpr int DN = D - DR;
+  constexpr int K8B = DN + 2 * DR, V8B = D;
+  constexpr int K8T = KT * K8B, ST8 = K8T + KT * V8B;
+  static_assert(!F8 || (K8B % 16 == 0 && K8B / 16 <= kWave && V8B / 16 <= kWave), "fp8 row copies");
+  static_assert(!F8 || (DN % 16 == 0 && DR % 32 == 0), "fp8 dims");
 
   constexpr int STB = KTB + VTB;          // one stage: K tile then V tile
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[4 * STB];
+  // bf16: four stages of bf16 tiles.  F8: two bf16 tiles, then four stages of fp8 tiles.
+  constexpr int RING = F8 ? 2 * STB + 4 * ST8 : 4 * STB;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[RING];
   __shared__ int32_t list[kMaxCsaChunk];  // the split's index entries
   __shared__ __attribute__((aligned(16))) uint8_t xchg[DS > 1 ? NT * 16 : 16];   // partial scores
 
@@ -186,11 +203,13 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
 
   // The loads that do not depend on each other are issued together and waited for once:
   // the query position, the split's index entries (CSA: list slots s0 .. s0+chunk-1, all
-  // below k <= n_tot), and the workgroup's query rows, copied once into LDS stages 2 and 3
-  // (free until tile 2 is issued).  The copies into LDS are then the only vector-memory
-  // operations in flight in the tile loop.
+  // below k <= n_tot), and the workgroup's query rows, copied once into LDS (bf16: stages
+  // 2 and 3, free until tile 2 is issued; F8: the two bf16 tiles, free until tile 0 is
+  // decoded).  The copies into LDS are then the only vector-memory operations in flight in
+  // the tile loop.
   const uint32_t ring_lds = lds_addr(ring);
-  const uint32_t q_lds = ring_lds + 2 * STB;
+  const uint32_t q_lds = F8 ? ring_lds : ring_lds + 2 * STB;
+  const uint32_t f8_lds = ring_lds + 2 * STB;      // F8: first fp8 stage
   static_assert(kHeads * KSTR <= 2 * STB, "query rows fit in two stages");
   {
     const uint16_t* qb = reinterpret_cast<const uint16_t*>(a.q) + bq * a.H * D;
@@ -200,28 +219,43 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
       if (h < a.H && lane < LPR) copy16_to_lds(qb + h * D + lane * 8, q_lds + h * KSTR);
     }
   }
+  // row strides in units of E (bf16: elements; F8: bytes)
   const int64_t krs = a.kv_rs, wrs = a.w_rs;
-  const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.kc) + b * a.kv_bs * krs;
-  const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.vc) + b * a.kv_bs * krs;
-  const uint16_t* kw = reinterpret_cast<const uint16_t*>(a.kw) + b * a.L * wrs;
-  const uint16_t* vw = reinterpret_cast<const uint16_t*>(a.vw) + b * a.L * wrs;
+  const int64_t vrs = F8 ? a.v_rs : a.kv_rs, wvrs = F8 ? a.wv_rs : a.w_rs;
+  const E* kc = reinterpret_cast<const E*>(a.kc) + b * a.kv_bs * krs;
+  const E* vc = reinterpret_cast<const E*>(a.vc) + b * a.kv_bs * vrs;
+  const E* kw = reinterpret_cast<const E*>(a.kw) + b * a.L * wrs;
+  const E* vw = reinterpret_cast<const E*>(a.vw) + b * a.L * wvrs;
   // Row pointers of a tile for key (lane % 16), set by tile_ptrs / spec_ptrs below.
-  const uint16_t* my_kp;
-  const uint16_t* my_vp;
+  const E* my_kp;
+  const E* my_vp;
   uint32_t vmask = 0;                       // validity of the tile's 16 keys
   // Wave w copies rows w, w+4, ... of the tile; a row is LPR lanes x 16 bytes (the other
   // lanes of a wave are masked off when a row is shorter than a wave).
   auto issue = [&](int stage) {
-    const uint32_t kdst = ring_lds + stage * STB;
-    const uint32_t vdst = kdst + KTB;
-    const int j = lane / LPR;              // 0 unless LPR < 64
+    if constexpr (F8) {
+      const uint32_t kdst = f8_lds + stage * ST8;
+      const uint32_t vdst = kdst + K8T;
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const int r = wave + i * NWV;
-      const int off = (lane % LPR) * 8;
-      if (j == 0) {
-        copy16_to_lds(lane_ptr<true>(my_kp, r) + off, kdst + r * KSTR);
-        copy16_to_lds(lane_ptr<true>(my_vp, r) + off, vdst + r * VSTR);
+      for (int i = 0; i < RPW; ++i) {
+        const int r = wave + i * NWV;
+        const E* kp = lane_ptr<true>(my_kp, r);
+        const E* vp = lane_ptr<true>(my_vp, r);
+        if (lane < K8B / 16) copy16_to_lds(kp + lane * 16, kdst + r * K8B);
+        if (lane < V8B / 16) copy16_to_lds(vp + lane * 16, vdst + r * V8B);
+      }
+    } else {
+      const uint32_t kdst = ring_lds + stage * STB;
+      const uint32_t vdst = kdst + KTB;
+      const int j = lane / LPR;              // 0 unless LPR < 64
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        const int r = wave + i * NWV;
+        const int off = (lane % LPR) * 8;
+        if (j == 0) {
+          copy16_to_lds(lane_ptr<true>(my_kp, r) + off, kdst + r * KSTR);
+          copy16_to_lds(lane_ptr<true>(my_vp, r) + off, vdst + r * VSTR);
+        }
       }
     }
   };
@@ -234,7 +268,7 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
     int64_t j = s0 + (int64_t)t * KT + (lane & (KT - 1));
     if (j > a.N - 1) j = a.N - 1;
     my_kp = kc + j * krs;
-    my_vp = vc + j * krs;
+    my_vp = vc + j * vrs;
   };
   if (spec) {
     spec_ptrs(0);
@@ -277,26 +311,26 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
   // Invalid slots point at a row that holds data (the query's first window row, else the
   // first compressed row), since their zero weights would not cancel a non-finite value.
   const bool win_rows = kr.n_tot > kr.n_c;
-  const uint16_t* kdef = win_rows ? kw + wrow(a, kr.r_lo) * wrs : kc;
-  const uint16_t* vdef = win_rows ? vw + wrow(a, kr.r_lo) * wrs : vc;
+  const E* kdef = win_rows ? kw + wrow(a, kr.r_lo) * wrs : kc;
+  const E* vdef = win_rows ? vw + wrow(a, kr.r_lo) * wvrs : vc;
   auto tile_ptrs = [&](int t) {
     const int64_t pos = s0 + (int64_t)t * KT + (lane & (KT - 1));
     bool ok = false;
-    const uint16_t* kp = kdef;
-    const uint16_t* vp = vdef;
+    const E* kp = kdef;
+    const E* vp = vdef;
     if (pos < s1) {
       if (pos < kr.n_c) {
         const int64_t j = a.csa ? (int64_t)list[pos - s0] : pos;
         if (j >= 0 && j < a.N) {
           ok = true;
           kp = kc + j * krs;
-          vp = vc + j * krs;
+          vp = vc + j * vrs;
         }
       } else {
         const int64_t r = wrow(a, kr.r_lo + (pos - kr.n_c));
         ok = true;
         kp = kw + r * wrs;
-        vp = vw + r * wrs;
+        vp = vw + r * wvrs;
       }
     }
     my_kp = kp;
@@ -310,13 +344,18 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.scale * kLog2e;
   // Scores over the head dim are split between the DS waves of a head group: wave slice
-  // dh takes k-steps dh*KSW .. +KSW-1 (dims g*D/4 + 8c .. +7 of lane group g for k-step c)
-  // and the DS partial scores are summed through LDS.
+  // dh takes k-steps dh*KSW .. +KSW-1 (bf16: dims g*D/4 + 8c .. +7 of lane group g for
+  // k-step c; F8: dims 32c + 8g .. +7) and the DS partial scores are summed through LDS.
   constexpr int KSW = KS / DS;
+  constexpr int KSR = DR / 32;             // F8: bf16 k-steps, the last ones of slice DS-1
+  static_assert(KSR <= KSW, "bf16 dims within one slice");
   // per-lane LDS byte offsets: K operand row `col` at this wave's first k-step; V^T rows
   // 4g + col/4 at dims dh*DH + 4(col%4)
-  const int k_off = col * KSTR + g * (D / 4) * 2 + dh * KSW * 16;
+  constexpr int KCS = F8 ? 64 : 16;        // byte step between k-steps of a lane
+  const int k_off = F8 ? col * KSTR + g * 16 + dh * KSW * 64 : col * KSTR + g * (D / 4) * 2 + dh * KSW * 16;
   const int v_off = (4 * g + (col >> 2)) * VSTR + dh * DH * 2 + (col & 3) * 8;
+  // F8: the fp8 k-steps' partial scores are multiplied by k_scale, the bf16 ones are not
+  const float rope_mul = F8 && dh != DS - 1 ? a.k_scale : 1.f;
 
   uint4 qop[KSW];                          // Q^T operands, read from LDS below
   // ---- partial S^T = K . Q^T (16 keys x 16 heads) over this wave's k-steps.  K operands
@@ -324,15 +363,14 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
   // scheduling barriers keep the compiler from pairing each read with its MFMA; two
   // batches stay within the 15 outstanding LDS reads the counter tracks).  Two
   // accumulators halve the dependent MFMA chain.
-  auto compute_s = [&](int stage) -> f32x4 {
-    const uint8_t* kt_l = ring + stage * STB;
-    f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = sa;
+  auto compute_s = [&](const uint8_t* kt_l) -> f32x4 {
+    f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = sa, sr = sa;
     constexpr int CB = KSW < 4 ? KSW : 4;
     constexpr int NB = KSW / CB;
     uint4 kv[2][CB];
     auto kread = [&](int buf, int c0) {
 #pragma unroll
-      for (int c = 0; c < CB; ++c) kv[buf][c] = *reinterpret_cast<const uint4*>(kt_l + k_off + (c0 + c) * 16);
+      for (int c = 0; c < CB; ++c) kv[buf][c] = *reinterpret_cast<const uint4*>(kt_l + k_off + (c0 + c) * KCS);
     };
     kread(0, 0);
 #pragma unroll
@@ -341,17 +379,21 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int c = 0; c < CB; ++c) {
-        if ((bi * CB + c) & 1) sb = mfma_bf16(bit_cast_to<bf16x8>(kv[bi & 1][c]), bit_cast_to<bf16x8>(qop[bi * CB + c]), sb);
-        else sa = mfma_bf16(bit_cast_to<bf16x8>(kv[bi & 1][c]), bit_cast_to<bf16x8>(qop[bi * CB + c]), sa);
+        const int ks = bi * CB + c;
+        const bf16x8 ka = bit_cast_to<bf16x8>(kv[bi & 1][c]);
+        const bf16x8 qb = bit_cast_to<bf16x8>(qop[ks]);
+        if (F8 && ks >= KSW - KSR) sr = mfma_bf16(ka, qb, sr);
+        else if (ks & 1) sb = mfma_bf16(ka, qb, sb);
+        else sa = mfma_bf16(ka, qb, sa);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (F8) return (sa + sb) * a.k_scale + sr * rope_mul;
     return sa + sb;
   };
   // ---- softmax of the full scores (lane holds keys 4g + i of head `head`), lazy
   // rescaling, then O^T += V^T . P^T
-  auto compute_pv = [&](int stage, uint32_t cur_mask, f32x4 s) {
-    const uint8_t* vt_l = ring + stage * STB + KTB;
+  auto compute_pv = [&](const uint8_t* vt_l, uint32_t cur_mask, f32x4 s) {
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -403,17 +445,59 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // ---- F8: decode the fp8 tile of stage `stage` into bf16 tile `buf`.  Units of 16 fp8
+  // bytes (K codes, then V codes) and of 16 bytes of K's bf16 dims, spread over the
+  // threads; the unit counts are multiples of 64, so every branch is uniform in a wave.
+  auto decode = [&](int stage, int buf) {
+    if constexpr (F8) {
+      constexpr int UK = KT * (DN / 16), UV = KT * (D / 16), UR = KT * (DR * 2 / 16);
+      static_assert(UK % kWave == 0 && UV % kWave == 0 && UR % kWave == 0, "uniform units");
+      const uint8_t* src = ring + 2 * STB + stage * ST8;
+      uint8_t* dst = ring + buf * STB;
+#pragma unroll
+      for (int u0 = 0; u0 < UK + UV + UR; u0 += NT) {
+        const int u = u0 + tid;
+        if (u < UK + UV) {
+          const bool is_v = u >= UK;
+          const int w = is_v ? u - UK : u;
+          const int cpr = is_v ? D / 16 : DN / 16;     // units per row
+          const int r = w / cpr, c = w - r * cpr;
+          const uint4 x = *reinterpret_cast<const uint4*>(src + (is_v ? K8T + r * V8B : r * K8B) + c * 16);
+          uint8_t* d = dst + (is_v ? KTB + r * VSTR : r * KSTR) + c * 32;
+          const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+          uint32_t y[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            y[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(xs[i], 1.f, false));
+            y[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(xs[i], 1.f, true));
+          }
+          reinterpret_cast<uint4*>(d)[0] = make_uint4(y[0], y[1], y[2], y[3]);
+          reinterpret_cast<uint4*>(d)[1] = make_uint4(y[4], y[5], y[6], y[7]);
+        } else if (u < UK + UV + UR) {
+          const int w = u - UK - UV;
+          const int r = w / (DR * 2 / 16), c = w - r * (DR * 2 / 16);
+          *reinterpret_cast<uint4*>(dst + r * KSTR + DN * 2 + c * 16) =
+              *reinterpret_cast<const uint4*>(src + r * K8B + DN + c * 16);
+        }
+      }
+    }
+  };
 
-  // Tile t lives in stage t % 4.  Tiles 0 and 1 are issued first; then every wave reads
-  // its Q^T operands (head `head`, dims g*D/4 + 8c .. +7 for k-step c) from stages 2-3,
-  // and after a barrier tile 2 is issued.  Step t then waits for tile t (tiles t+1, t+2
-  // stay in flight), passes a barrier (tile t visible to all waves; every wave is done
-  // with tile t-1), issues tile t+3 into the stage of tile t-1 and uses tile t.
-  uint32_t mq0 = 0, mq1 = 0, mq2 = 0;      // masks of tiles t, t+1, t+2
+  // bf16: tile t lives in stage t % 4.  Tiles 0 and 1 are issued first; then every wave
+  // reads its Q^T operands (head `head`, for each of its k-steps) from stages 2-3, and
+  // after a barrier tile 2 is issued.  Step t then waits for tile t (tiles t+1, t+2 stay
+  // in flight), passes a barrier (tile t visible to all waves; every wave is done with
+  // tile t-1), issues tile t+3 into the stage of tile t-1 and uses tile t.
+  // F8: tile t lives in fp8 stage t % 4 and, decoded, in bf16 tile t % 2.  Tiles 0 .. 3
+  // are issued first, tile 0 is decoded after the Q^T operands are read; step t waits for
+  // tile t+1, passes a barrier (bf16 tile t complete; every wave is done with bf16 tile
+  // t-1 and with fp8 stage t), issues tile t+4 into fp8 stage t % 4, decodes tile t+1 into
+  // bf16 tile (t+1) % 2 and uses bf16 tile t.
+  uint32_t mq0 = 0, mq1 = 0, mq2 = 0, mq3 = 0;   // masks of tiles t, t+1, t+2, t+3
   if (spec) {
     bool same = true;
-    const uint16_t* sk[2];
-    const uint16_t* sv[2];
+    const E* sk[2];
+    const E* sv[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       spec_ptrs(t);
@@ -439,26 +523,54 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
     if (ntile > 0) { tile_ptrs(0); mq0 = vmask; issue(0); }
     if (ntile > 1) { tile_ptrs(1); mq1 = vmask; issue(1); }
   }
-  {
-    const uint8_t* ql = ring + 2 * STB + (wave_on ? head : 0) * KSTR + g * (D / 4) * 2 + dh * KSW * 16;
-#pragma unroll
-    for (int c = 0; c < KSW; ++c) qop[c] = *reinterpret_cast<const uint4*>(ql + c * 16);
+  if constexpr (F8) {
+    if (ntile > 2) { tile_ptrs(2); mq2 = vmask; issue(2); }
+    if (ntile > 3) { tile_ptrs(3); mq3 = vmask; issue(3); }
   }
-  tile_barrier();
-  if (ntile > 2) { tile_ptrs(2); mq2 = vmask; issue(2); }
-  for (int t = 0; t < ntile; ++t) {
-    if (t + 2 < ntile) wait_vmcnt<2 * NL>();
-    else if (t + 1 < ntile) wait_vmcnt<NL>();
+  {
+    const uint8_t* ql = F8 ? ring + (wave_on ? head : 0) * KSTR + g * 16 + dh * KSW * 64
+                           : ring + 2 * STB + (wave_on ? head : 0) * KSTR + g * (D / 4) * 2 + dh * KSW * 16;
+#pragma unroll
+    for (int c = 0; c < KSW; ++c) qop[c] = *reinterpret_cast<const uint4*>(ql + c * KCS);
+  }
+  if constexpr (F8) {
+    if (ntile > 3) wait_vmcnt<3 * NL>();
+    else if (ntile > 2) wait_vmcnt<2 * NL>();
+    else if (ntile > 1) wait_vmcnt<NL>();
     else wait_vmcnt<0>();
+    tile_barrier();                          // tile 0 landed everywhere; Q^T operands read
+    if (ntile > 0) decode(0, 0);
+  } else {
     tile_barrier();
-    uint32_t mq3 = 0;
-    if (t + 3 < ntile) {
-      tile_ptrs(t + 3);
-      mq3 = vmask;
-      issue((t + 3) & 3);
+    if (ntile > 2) { tile_ptrs(2); mq2 = vmask; issue(2); }
+  }
+  for (int t = 0; t < ntile; ++t) {
+    uint32_t mqn = 0;
+    if constexpr (F8) {
+      if (t + 3 < ntile) wait_vmcnt<2 * NL>();
+      else if (t + 2 < ntile) wait_vmcnt<NL>();
+      else wait_vmcnt<0>();
+      tile_barrier();
+      if (t + 4 < ntile) {
+        tile_ptrs(t + 4);
+        mqn = vmask;
+        issue(t & 3);
+      }
+      if (t + 1 < ntile) decode((t + 1) & 3, (t + 1) & 1);
+    } else {
+      if (t + 2 < ntile) wait_vmcnt<2 * NL>();
+      else if (t + 1 < ntile) wait_vmcnt<NL>();
+      else wait_vmcnt<0>();
+      tile_barrier();
+      if (t + 3 < ntile) {
+        tile_ptrs(t + 3);
+        mqn = vmask;
+        issue((t + 3) & 3);
+      }
     }
+    const uint8_t* kt_l = F8 ? ring + (t & 1) * STB : ring + (t & 3) * STB;
     f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (wave_on) sc = compute_s(t & 3);
+    if (wave_on) sc = compute_s(kt_l);
     if constexpr (DS > 1) {
       // partial scores of the DS slices of a head group (waves hg + 4j), summed in the
       // same order by every slice so that all of them see identical scores
@@ -472,17 +584,22 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
         sc = tot;
       }
     }
-    if (wave_on) compute_pv(t & 3, mq0, sc);
+    if (wave_on) compute_pv(kt_l + KTB, mq0, sc);
     mq0 = mq1;
     mq1 = mq2;
-    mq2 = mq3;
+    if constexpr (F8) {
+      mq2 = mq3;
+      mq3 = mqn;
+    } else {
+      mq2 = mqn;
+    }
   }
   wait_vmcnt<0>();                           // no copy into LDS outlives the workgroup
 
   if (!wave_on) return;
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  const float inv = l_run > 0.f ? (F8 ? a.v_scale : 1.f) / l_run : 0.f;
   const float lse = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
   // the output row, or with several splits this split's partial row (bf16 like the
   // output; the merge accumulates in fp32)
@@ -504,6 +621,19 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
       lse_part[(int64_t)split * R + orow] = lse;
     }
   }
+}
+
+template <int D, int DS>
+__global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a, int64_t chunk, int splits,
+                                                               uint16_t* __restrict__ o_part,
+                                                               float* __restrict__ lse_part) {
+  attend_body<D, DS, false>(a, chunk, splits, o_part, lse_part);
+}
+template <int D, int DS>
+__global__ __launch_bounds__(kThreads * DS) void attend_fp8kv_kernel(AttendArgs a, int64_t chunk, int splits,
+                                                                uint16_t* __restrict__ o_part,
+                                                                float* __restrict__ lse_part) {
+  attend_body<D, DS, true>(a, chunk, splits, o_part, lse_part);
 }
 
 // ---------------------------------------------------------------------------- fp32 / VALU
@@ -792,7 +922,10 @@ hipError_t launch_attend(const AttendArgs& a, const AttendPlan& p, void* ws, hip
     lse_part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + align256((size_t)p.splits * R * a.D * 2));
   }
   dim3 grid((unsigned)p.splits, (unsigned)rows);
-  switch (a.D) {
+  if (a.f8) {   // D == 512 (checked by the caller)
+    DSV4_LAUNCH_MAIN((attend_fp8kv_kernel<512, 2>), grid, dim3(kThreads * 2), 0, st, a, (int64_t)p.chunk, p.splits,
+                     o_part, lse_part);
+  } else switch (a.D) {
     case 128: DSV4_LAUNCH_MAIN((attend_bf16_kernel<128, 1>), grid, dim3(kThreads), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part); break;
     case 256: DSV4_LAUNCH_MAIN((attend_bf16_kernel<256, 1>), grid, dim3(kThreads), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part); break;
     default: DSV4_LAUNCH_MAIN((attend_bf16_kernel<512, 2>), grid, dim3(kThreads * 2), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part); break;

@@ -88,6 +88,7 @@ TopkWorkspace topk_workspace_carve(void* base, int64_t R, int64_t N);
 hipError_t launch_index_topk(const IndexArgs& a, const TopkWorkspace& ws, hipStream_t st);
 
 // ---------------------------------------------------------------- attention
+constexpr int kFp8RopeDims = 64;   // bf16 tail of an FP8 K row
 struct AttendArgs {
   const void* q;
   const void* kc;
@@ -106,8 +107,13 @@ struct AttendArgs {
   int64_t B, Q;
   int H, D;
   int64_t N, kv_bs;       // kv_bs: rows between batches of kc/vc
-  int64_t kv_rs, w_rs;     // elements between rows of kc/vc and of kw/vw
+  int64_t kv_rs, w_rs;     // elements between rows of kc/vc and of kw/vw (fp8 rows: bytes, K rows)
   float scale;
+  // FP8 K/V rows: K = (D - kFp8RopeDims) e4m3 codes then kFp8RopeDims bf16 values, V = D
+  // e4m3 codes; decoded value = code * k_scale (K codes) or code * v_scale (V codes).
+  bool f8 = false;
+  int64_t v_rs = 0, wv_rs = 0;   // bytes between V rows of vc and of vw
+  float k_scale = 1.f, v_scale = 1.f;
   void* out;
   float* lse;
 };

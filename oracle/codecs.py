@@ -168,6 +168,43 @@ class Stored:
         return decode(self.bits[key], self.dtype, None if self.scales is None else self.scales[key])
 
 
+# ----------------------------------------------------------------- FP8 K/V rows
+# pogovet.com, 상세 정리 §5: most of each KV entry is stored in FP8 and only the RoPE
+# dimensions in BF16.  Reading of what the page leaves open: the RoPE dims are the last
+# d_rope dims of a K row (V carries none), the FP8 format is OCP E4M3, and one scale per
+# tensor kind maps codes to values (decoded = scale * e4m3(code)).
+def decode_fp8_k_rows(rows_u8: np.ndarray, D: int, d_rope: int, k_scale: float) -> np.ndarray:
+    """K rows of D - d_rope E4M3 code bytes followed by d_rope little-endian bf16 values
+    -> float64 [..., D]: k_scale * code value for the code dims, the bf16 values as they are."""
+    r = np.asarray(rows_u8, dtype=np.uint8)
+    dn = D - d_rope
+    if r.shape[-1] != dn + 2 * d_rope:
+        raise ValueError("a K row holds D - d_rope code bytes and d_rope bf16 values")
+    codes = r[..., :dn]
+    tail = np.ascontiguousarray(r[..., dn:]).view("<u2")
+    return np.concatenate([float(k_scale) * decode_e4m3(codes), decode_bf16(tail)], axis=-1)
+
+
+def decode_fp8_v_rows(rows_u8: np.ndarray, v_scale: float) -> np.ndarray:
+    """V rows of D E4M3 code bytes -> float64 [..., D] = v_scale * code value."""
+    return float(v_scale) * decode_e4m3(np.asarray(rows_u8, dtype=np.uint8))
+
+
+def encode_fp8_k_rows(k: np.ndarray, d_rope: int, k_scale: float) -> np.ndarray:
+    """float32 K [..., D] -> the byte rows decode_fp8_k_rows reads: e4m3(k / k_scale) for
+    the first D - d_rope dims (float32 division, then nearest-even), bf16 of the rest."""
+    k = np.asarray(k, dtype=np.float32)
+    dn = k.shape[-1] - d_rope
+    codes = encode_e4m3(k[..., :dn] / np.float32(k_scale))
+    tail = encode_bf16(k[..., dn:]).astype("<u2").view(np.uint8)
+    return np.concatenate([codes, tail.reshape(k.shape[:-1] + (2 * d_rope,))], axis=-1)
+
+
+def encode_fp8_v_rows(v: np.ndarray, v_scale: float) -> np.ndarray:
+    """float32 V [..., D] -> E4M3 codes of v / v_scale (float32 division, nearest-even)."""
+    return encode_e4m3(np.asarray(v, dtype=np.float32) / np.float32(v_scale))
+
+
 def decode(bits: np.ndarray, dtype: str, scales: np.ndarray | None = None) -> np.ndarray:
     if dtype == F32:
         return np.asarray(bits, dtype=np.float32).astype(np.float64)

@@ -149,6 +149,44 @@ def test_attend_validation_and_workspace_query():
     assert _attend(wp0=None, W=256)[0] == 1 and b"ring" in L.lib().dsv4_last_error()
 
 
+def _attend_fp8(csa=True, **kw):
+    a = dict(q=P, kc=P, vc=P, idx=P, k=512, m=128, kw=P, vw=P, wp0=P, L=256, W=128, qpos=P, B=8, Q=1, H=64, D=512,
+             dr=64, N=262144, kvbs=0, kvrs=0, wrs=0, ks=1.0, vs=1.0, scale=0.04, out=P, lse=P)
+    a.update(kw)
+    n = ctypes.c_size_t(0)
+    lib = L.lib()
+    if csa:
+        st = lib.csa_attend_fp8kv(a["q"], a["kc"], a["vc"], a["idx"], a["k"], a["kw"], a["vw"], a["wp0"], a["L"],
+                                  a["W"], a["qpos"], a["B"], a["Q"], a["H"], a["D"], a["dr"], a["N"], a["kvbs"],
+                                  a["kvrs"], a["wrs"], a["ks"], a["vs"], a["scale"], a["out"], a["lse"], None,
+                                  ctypes.byref(n), None)
+    else:
+        st = lib.hca_attend_fp8kv(a["q"], a["kc"], a["vc"], a["m"], a["kw"], a["vw"], a["wp0"], a["L"], a["W"],
+                                  a["qpos"], a["B"], a["Q"], a["H"], a["D"], a["dr"], a["N"], a["kvbs"], a["kvrs"],
+                                  a["wrs"], a["ks"], a["vs"], a["scale"], a["out"], a["lse"], None, ctypes.byref(n),
+                                  None)
+    return st, n.value
+
+
+def test_attend_fp8kv_validation_and_workspace_query():
+    st, n = _attend_fp8()
+    assert st == 0 and n > 0
+    st, n = _attend_fp8(csa=False, N=8192)
+    assert st == 0 and n > 0
+    assert _attend_fp8(D=256)[0] == 2                       # D = 512 only
+    assert _attend_fp8(dr=32)[0] == 2                       # d_rope = 64 only
+    assert _attend_fp8(H=40)[0] == 2
+    assert _attend_fp8(kvrs=1088, wrs=1088)[0] == 0         # K and V side by side (576 + 512 bytes)
+    assert _attend_fp8(kvrs=512)[0] == 1                    # narrower than a K row
+    assert _attend_fp8(wrs=584)[0] == 1                     # not a multiple of 16 bytes
+    assert _attend_fp8(kc=ctypes.c_void_p(24))[0] == 1      # not 16-byte aligned
+    assert _attend_fp8(ks=float("inf"))[0] == 1
+    assert _attend_fp8(vs=float("nan"))[0] == 1
+    assert _attend_fp8(idx=None)[0] == 1
+    assert _attend_fp8(csa=False, m=0)[0] == 1
+    assert _attend_fp8(wp0=None, W=512)[0] == 1             # ring window needs W <= L
+
+
 def test_lse_merge_validation():
     lib = L.lib()
     assert lib.lse_merge(P, P, 0, 4, 8, P, 0, P, None) == 1

@@ -600,6 +600,138 @@ def test_attend_empty_key_set_and_determinism():
     assert torch.equal(r1[0], r2[0]) and torch.equal(r1[1], r2[1])
 
 
+# ============================================================ FP8 K/V rows
+DR = 64   # RoPE dims of a K row kept in bf16
+
+
+def _fp8_kv(cfg, B, N, L_, D, k_scale, v_scale):
+    """Seeded K/V caches and windows as FP8 byte rows (the oracle's encoder) and their
+    float64 decoding (the oracle's decoder)."""
+    _, kc, vc, kw, vw = _attn_inputs(cfg, B, 1, 1, D, N, L_)
+    rows = [codecs.encode_fp8_k_rows(kc, DR, k_scale), codecs.encode_fp8_v_rows(vc, v_scale),
+            codecs.encode_fp8_k_rows(kw, DR, k_scale), codecs.encode_fp8_v_rows(vw, v_scale)]
+    dec = [codecs.decode_fp8_k_rows(rows[0], D, DR, k_scale), codecs.decode_fp8_v_rows(rows[1], v_scale),
+           codecs.decode_fp8_k_rows(rows[2], D, DR, k_scale), codecs.decode_fp8_v_rows(rows[3], v_scale)]
+    return rows, dec
+
+
+@pytest.mark.parametrize("H,Q", [(64, 2), (32, 3)])
+def test_csa_attend_fp8kv(H, Q):
+    """Selected entries (short list, out-of-range entries) plus a linear window, with
+    non-power-of-two scales; the oracle attends over the decoded rows."""
+    cfg = 700 + H
+    B, D, N, L_, W, k = 2, 512, 3000, 160, 128, 512
+    ks, vs = 0.71, 1.37
+    (kcb, vcb, kwb, vwb), (kcd, vcd, kwd, vwd) = _fp8_kv(cfg, B, N, L_, D, ks, vs)
+    q = synth.normal(cfg, synth.Q, (B, Q, H, D))
+    idx = synth.sorted_unique_indices(cfg, synth.IDX, B * Q, N, k).reshape(B, Q, k)
+    idx[0, 0, -7:] = -1
+    idx[1, 0, 3] = N + 5
+    win_pos0 = np.array([40000, 7], dtype=np.int32)
+    pos = np.array([[40000 + 150, 40000 + 20, 40000 + 159][:Q], [7 + 127, 7 + 300, 3][:Q]], dtype=np.int32)
+    qd, qb = dev_bf16(q)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = L.csa_attend_fp8kv(qd, dev(kcb), dev(vcb), dev(idx), dev(kwb), dev(vwb), dev(win_pos0), W, dev(pos),
+                                scale, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = method.csa_attend(codecs.decode_bf16(qb), kcd, vcd, idx, kwd, vwd, win_pos0, W, pos, scale)
+    assert row_rel_err(host(o), o_ref) <= 1e-2
+    assert lse_abs_err(host(lse), lse_ref) <= 1e-2
+
+
+@pytest.mark.parametrize("N", [1000, 45])
+def test_hca_attend_fp8kv_ring_window(N):
+    """Every visible entry (several splits and a ragged tail, or fewer entries than one
+    tile) plus a ring window (position p in row p % L)."""
+    cfg = 720 + N
+    B, Q, H, D, m, Lw, W = 2, 3, 64, 512, 128, 256, 128
+    ks, vs = 2.0 ** -2, 3.1
+    (kcb, vcb, kwl, vwl), (kcd, vcd, kwd, vwd) = _fp8_kv(cfg, B, N, Lw, D, ks, vs)
+    pmax = np.array([N * m + 40, N * m - 7])
+    qpos = np.stack([pmax, pmax - 1, pmax - 90], axis=1).astype(np.int32)   # windows inside the ring
+    wp0 = (pmax - Lw + 1).astype(np.int32)
+    kwr, vwr = np.empty_like(kwl), np.empty_like(vwl)
+    for b in range(B):
+        rr = (wp0[b] + np.arange(Lw)) % Lw
+        kwr[b, rr], vwr[b, rr] = kwl[b], vwl[b]
+    q = synth.normal(cfg, synth.Q, (B, Q, H, D))
+    qd, qb = dev_bf16(q)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = L.hca_attend_fp8kv(qd, dev(kcb), dev(vcb), m, dev(kwr), dev(vwr), None, W, dev(qpos), scale,
+                                k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = method.hca_attend(codecs.decode_bf16(qb), kcd, vcd, m, kwd, vwd, wp0, W, qpos, scale)
+    assert row_rel_err(host(o), o_ref) <= 1e-2
+    assert lse_abs_err(host(lse), lse_ref) <= 1e-2
+
+
+def test_attend_fp8kv_side_by_side_and_every_code():
+    """K and V rows side by side in one row of 576 + 512 bytes give the same bits as
+    separate tensors; code bytes drawn over every finite E4M3 code (subnormals, zeros,
+    +-448) still match the oracle."""
+    cfg = 760
+    B, Q, H, D, N, L_, W, k, m = 2, 2, 48, 512, 700, 140, 128, 256, 4
+    ks, vs = 2.0 ** -6, 2.0 ** -5
+    r = np.random.default_rng(cfg)
+
+    def draw(shape):                      # any finite code (the two NaN codes become zero)
+        c = r.integers(0, 256, size=shape).astype(np.uint8)
+        c[(c & 0x7F) == 0x7F] = 0
+        return c
+
+    kcb = np.concatenate([draw((B, N, D - DR)), synth.bf16_bits(synth.normal(cfg, synth.KC, (B, N, DR)))
+                          .astype("<u2").view(np.uint8).reshape(B, N, 2 * DR)], axis=2)
+    kwb = np.concatenate([draw((B, L_, D - DR)), synth.bf16_bits(synth.normal(cfg, synth.KW, (B, L_, DR)))
+                          .astype("<u2").view(np.uint8).reshape(B, L_, 2 * DR)], axis=2)
+    vcb, vwb = draw((B, N, D)), draw((B, L_, D))
+    q = synth.normal(cfg, synth.Q, (B, Q, H, D))
+    idx = synth.sorted_unique_indices(cfg, synth.IDX, B * Q, N, k).reshape(B, Q, k)
+    win_pos0 = np.array([2700, 2000], dtype=np.int32)
+    pos = np.array([[2799, 2750], [2100, 2139]], dtype=np.int32)
+    qd, qb = dev_bf16(q)
+    scale = 1.0 / math.sqrt(D)
+    kvc = dev(np.concatenate([kcb, vcb], axis=2))
+    kvw = dev(np.concatenate([kwb, vwb], axis=2))
+    KB = D + DR
+    o1, l1 = L.csa_attend_fp8kv(qd, kvc[..., :KB], kvc[..., KB:], dev(idx), kvw[..., :KB], kvw[..., KB:],
+                                dev(win_pos0), W, dev(pos), scale, k_scale=ks, v_scale=vs)
+    o2, l2 = L.csa_attend_fp8kv(qd, dev(kcb), dev(vcb), dev(idx), dev(kwb), dev(vwb), dev(win_pos0), W, dev(pos),
+                                scale, k_scale=ks, v_scale=vs)
+    h1, hl1 = L.hca_attend_fp8kv(qd, kvc[..., :KB], kvc[..., KB:], m, kvw[..., :KB], kvw[..., KB:], dev(win_pos0), W,
+                                 dev(pos), scale, k_scale=ks, v_scale=vs, N=300)
+    h2, hl2 = L.hca_attend_fp8kv(qd, dev(kcb), dev(vcb), m, dev(kwb), dev(vwb), dev(win_pos0), W, dev(pos), scale,
+                                 k_scale=ks, v_scale=vs, N=300)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(h1, h2) and torch.equal(hl1, hl2)
+    kd, vd = codecs.decode_fp8_k_rows(kcb, D, DR, ks), codecs.decode_fp8_v_rows(vcb, vs)
+    kwd, vwd = codecs.decode_fp8_k_rows(kwb, D, DR, ks), codecs.decode_fp8_v_rows(vwb, vs)
+    o_ref, lse_ref = method.csa_attend(codecs.decode_bf16(qb), kd, vd, idx, kwd, vwd, win_pos0, W, pos, scale)
+    assert row_rel_err(host(o1), o_ref) <= 1e-2
+    assert lse_abs_err(host(l1), lse_ref) <= 1e-2
+    h_ref, hl_ref = method.hca_attend(codecs.decode_bf16(qb), kd[:, :300], vd[:, :300], m, kwd, vwd, win_pos0, W,
+                                      pos, scale)
+    assert row_rel_err(host(h1), h_ref) <= 1e-2
+    assert lse_abs_err(host(hl1), hl_ref) <= 1e-2
+
+
+def test_attend_fp8kv_empty_key_sets():
+    """No compressed entries and no window row in range: o = 0 and lse = -inf (CSA with N = 0
+    and a list of slots, HCA before its first complete block)."""
+    B, Q, H, D, L_ = 1, 2, 64, 512, 32
+    (kcb, vcb, kwb, vwb), _ = _fp8_kv(780, B, 8, L_, D, 1.0, 1.0)
+    q, _ = dev_bf16(synth.normal(780, synth.Q, (B, Q, H, D)))
+    win_pos0 = np.array([10000], dtype=np.int32)
+    pos = np.array([[5, 100]], dtype=np.int32)
+    idx = np.zeros((B, Q, 16), dtype=np.int32)
+    o, lse = L.csa_attend_fp8kv(q, dev(kcb), dev(vcb), dev(idx), dev(kwb), dev(vwb), dev(win_pos0), 16, dev(pos), 0.1,
+                                N=0)
+    h, hl = L.hca_attend_fp8kv(q, dev(kcb), dev(vcb), 128, dev(kwb), dev(vwb), dev(win_pos0), 16, dev(pos), 0.1)
+    torch.cuda.synchronize()
+    assert torch.all(o.float() == 0) and torch.all(torch.isneginf(lse))
+    assert torch.all(h.float() == 0) and torch.all(torch.isneginf(hl))
+
+
 def test_lse_merge():
     r = np.random.default_rng(600)
     P, R, D = 5, 37, 512

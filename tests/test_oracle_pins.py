@@ -100,6 +100,37 @@ def test_mxfp4_is_nearest_grid_point():
                     assert np.sign(dq[i, j]) == np.sign(x[i, j])
 
 
+def test_fp8_kv_rows_worked_example():
+    """A K row of 4 code dims + 2 RoPE dims (D = 6, d_rope = 2) and a V row, decoded by the
+    OCP E4M3 definition (bias 7, three mantissa bits, subnormals m * 2^-9) and the bf16
+    definition: the scale multiplies the code dims only, bytes are little-endian."""
+    k_row = np.array([[0x38, 0xB8, 0x4C, 0x01, 0x80, 0x3F, 0x40, 0xC0]], np.uint8)
+    # 0x38 = +1.0, 0xB8 = -1.0, 0x4C = 2^(9-7) * (1 + 4/8) = 6.0, 0x01 = 2^-9;
+    # bf16 0x3F80 = 1.0, 0xC040 = -3.0
+    got = codecs.decode_fp8_k_rows(k_row, 6, 2, 0.25)
+    assert list(got[0]) == [0.25, -0.25, 1.5, 2.0 ** -11, 1.0, -3.0]
+    v_row = np.array([[0x7E, 0xFE, 0x08, 0x00]], np.uint8)          # +448, -448, 2^-6, 0
+    assert list(codecs.decode_fp8_v_rows(v_row, 3.0)[0]) == [1344.0, -1344.0, 3.0 * 2.0 ** -6, 0.0]
+
+
+def test_fp8_kv_rows_round_trip_and_rounding():
+    """Values on the E4M3 grid (times a power-of-two scale) and bf16 values survive the
+    encoder exactly; off-grid code dims land on a nearest grid point."""
+    r = _rng(55)
+    codes = r.integers(0, 256, size=(40, 448)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3C                             # no NaN codes
+    k = np.concatenate([codecs.decode_e4m3(codes) * 2.0 ** -5,
+                        codecs.decode_bf16(codecs.encode_bf16(r.standard_normal((40, 64))))], axis=1)
+    rows = codecs.encode_fp8_k_rows(k.astype(np.float32), 64, 2.0 ** -5)
+    assert rows.shape == (40, 576)
+    assert np.array_equal(codecs.decode_fp8_k_rows(rows, 512, 64, 2.0 ** -5), k)
+    v = r.standard_normal((40, 512)).astype(np.float32)
+    dv = codecs.decode_fp8_v_rows(codecs.encode_fp8_v_rows(v, 0.5), 0.5)
+    grid = np.unique(np.abs(codecs.decode_e4m3(np.arange(0, 127, dtype=np.uint8)))) * 0.5
+    nearest = np.abs(np.abs(v.astype(np.float64))[..., None] - grid).min(axis=-1)
+    assert np.all(np.abs(np.abs(dv) - np.abs(v)) <= nearest + 1e-12)
+
+
 # ============================================================ compression
 def _raw(seed, B, T, C):
     r = _rng(seed)
