@@ -66,7 +66,8 @@ typedef enum {
   DSV4_F32 = 0,
   DSV4_BF16 = 1,
   DSV4_FP8_E4M3 = 2,
-  DSV4_MXFP4 = 3
+  DSV4_MXFP4 = 3,
+  DSV4_FP8_KV = 4   /* pooling output only: FP8 K|V rows as read by csa_attend_fp8kv */
 } dsv4_dtype;
 
 /* Library version (major * 10000 + minor * 100 + patch). */
@@ -100,6 +101,14 @@ dsv4_status dsv4_time_next_kernel(hipEvent_t start, hipEvent_t stop);
  *   y        [B, y_bstride rows, C] of y_dt (F32 | BF16 | FP8_E4M3), or for MXFP4
  *            [B, y_bstride rows, C/2] bytes plus y_scale [B, y_bstride rows, C/32].
  *            Rows 0..T/m-1 are written.  y_bstride == 0 means T/m.
+ *   y_dt = FP8_KV ([P2 §5]: K/V stored mostly in FP8, RoPE dims in BF16): the C channels are
+ *            K then V (D = C/2 each, e.g. a [.., 2D] K|V window); each pooled row is written
+ *            as one row of C + 64 bytes: K's first D - 64 channels as E4M3 codes, K's last 64
+ *            channels as bf16, V's D channels as E4M3 codes (the layout csa_attend_fp8kv
+ *            reads with kv_rstride = C + 64 and vc = kc + D + 64).  Codes are
+ *            e4m3(y * 2^-e): e = y_scale[0] - 127 for K and y_scale[1] - 127 for V when
+ *            y_scale (two device bytes, E8M0) is given, else 0; then k_scale = 2^e_K and
+ *            v_scale = 2^e_V for the attention call.  Requires C % 16 == 0, C/2 > 64.
  *   Requires T % m == 0, 1 <= m <= 1024, C % 8 == 0, C <= 1024 (F32 x) or 2048 (BF16 x),
  *   C % 32 == 0 for MXFP4.
  *   Arithmetic: softmax and sums in fp32; rounding to y_dt is nearest-even (fp8 and

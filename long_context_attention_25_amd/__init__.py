@@ -15,10 +15,12 @@ import torch
 __all__ = ["csa_compress", "kv_cache_append", "csa_index_topk", "csa_attend", "hca_attend", "csa_attend_fp8kv",
            "hca_attend_fp8kv", "lse_merge", "lib",
            "LibError",
-           "F32", "BF16", "FP8_E4M3", "MXFP4", "MXFP4_DTYPE"]
+           "F32", "BF16", "FP8_E4M3", "MXFP4", "FP8_KV", "MXFP4_DTYPE", "FP8_KV_DTYPE", "FP8_ROPE_DIMS"]
 
-F32, BF16, FP8_E4M3, MXFP4 = 0, 1, 2, 3
+F32, BF16, FP8_E4M3, MXFP4, FP8_KV = 0, 1, 2, 3, 4
 MXFP4_DTYPE = "mxfp4"            # marker for packed MXFP4 (uint8 codes + uint8 E8M0 scales)
+FP8_KV_DTYPE = "fp8_kv"          # marker for FP8 K|V rows (E4M3 codes, bf16 RoPE dims of K)
+FP8_ROPE_DIMS = 64               # bf16 tail of an FP8 K row
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsv4attn.so")
 _lib = None
@@ -112,8 +114,10 @@ def csa_compress(x, gate, pos_bias, m: int, y_dtype=torch.bfloat16, out=None, ou
     """Softmax-gated pooling of disjoint blocks of m tokens: x [B,T,C] -> y [B,T/m,C].
 
     y_dtype: torch.float32 / torch.bfloat16 / torch.float8_e4m3fn, or MXFP4_DTYPE (returns
-    (codes [B,T/m,C/2] uint8, scales [B,T/m,C/32] uint8)).  `out` may be a [B, rows, ...] view
-    with rows >= T/m (e.g. the tail of a cache); its batch stride is passed through.
+    (codes [B,T/m,C/2] uint8, scales [B,T/m,C/32] uint8)), or FP8_KV_DTYPE (x = K|V side by
+    side; returns FP8 K|V rows [B,T/m,C+64] uint8; out_scale: optional 2 device bytes, the
+    E8M0 exponents of the K and V codes).  `out` may be a [B, rows, ...] view with rows >= T/m
+    (e.g. the tail of a cache); its batch stride is passed through.
     """
     if not (gate.is_contiguous() and pos_bias.is_contiguous()):
         raise ValueError("gate [B, T] and pos_bias [m] must be contiguous")
@@ -124,6 +128,12 @@ def csa_compress(x, gate, pos_bias, m: int, y_dtype=torch.bfloat16, out=None, ou
         if out is None:
             out = torch.empty((B, nb, C // 2), dtype=torch.uint8, device=x.device)
             out_scale = torch.empty((B, nb, C // 32), dtype=torch.uint8, device=x.device)
+    elif y_dtype == FP8_KV_DTYPE:
+        ydt = FP8_KV
+        if out is None:
+            out = torch.empty((B, nb, C + FP8_ROPE_DIMS), dtype=torch.uint8, device=x.device)
+        if out.dtype != torch.uint8 or out.stride(-1) != 1 or (out.dim() == 3 and out.stride(1) != C + FP8_ROPE_DIMS):
+            raise ValueError("FP8 K|V rows: out must be uint8 with contiguous rows of C + 64 bytes")
     else:
         ydt = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3}[y_dtype]
         if out is None:
@@ -135,12 +145,14 @@ def csa_compress(x, gate, pos_bias, m: int, y_dtype=torch.bfloat16, out=None, ou
     return (out, out_scale) if ydt == MXFP4 else out
 
 
-def kv_cache_append(x_new, gate_new, pos, win, win_gate, pos_bias, m: int, cache, cache_scale=None):
+def kv_cache_append(x_new, gate_new, pos, win, win_gate, pos_bias, m: int, cache, cache_scale=None,
+                    cache_dtype=None):
     """One decode step of cache maintenance: x_new [B,C] (gate_new [B] f32, pos [B] int32)
     goes to row pos % L of the ring window win [B,L,C] / win_gate [B,L], and a block that
     the new token completes is pooled into its row of `cache` ([B,N,C] of f32/bf16/e4m3, or
-    MXFP4 codes [B,N,C/2] uint8 with cache_scale [B,N,C/32]).  Attend over such a window
-    with win_pos0=None.
+    MXFP4 codes [B,N,C/2] uint8 with cache_scale [B,N,C/32], or with cache_dtype=FP8_KV_DTYPE
+    FP8 K|V rows [B,N,C+64] uint8 with optional cache_scale = 2 E8M0 bytes).  Attend over such
+    a window with win_pos0=None.
     """
     for t in (x_new, gate_new, pos, win, win_gate, pos_bias):
         if not t.is_contiguous():
@@ -150,7 +162,10 @@ def kv_cache_append(x_new, gate_new, pos, win, win_gate, pos_bias, m: int, cache
         raise ValueError("x_new must be [B, C] with the window's dtype")
     if cache.stride(-1) != 1 or (cache.dim() == 3 and cache.stride(1) != cache.shape[2]):
         raise ValueError("cache rows must be contiguous")
-    ydt = MXFP4 if cache_scale is not None else _dt(cache)
+    if cache_dtype == FP8_KV_DTYPE:
+        ydt = FP8_KV
+    else:
+        ydt = MXFP4 if cache_scale is not None else _dt(cache)
     N = cache.shape[1]
     y_bs = cache.stride(0) // cache.stride(1) if B > 0 else 0
     _check(lib().kv_cache_append(_ptr(x_new), _dt(x_new), _ptr(gate_new), _ptr(pos), B, C, _ptr(win), _ptr(win_gate),
@@ -225,9 +240,6 @@ def hca_attend(q, kc, vc, m: int, kw, vw, win_pos0, W: int, q_pos, scale: float,
     ws, n = _workspace(lambda n: lib().hca_attend(*args, None, ctypes.byref(n), _stream()), workspace)
     _check(lib().hca_attend(*args, _ptr(ws), n, _stream()))
     return out, lse
-
-
-FP8_ROPE_DIMS = 64   # bf16 tail of an FP8 K row
 
 
 def _fp8kv_common(q, kc, vc, kw, vw, N, d_rope):

@@ -217,7 +217,10 @@ dsv4_status csa_compress(const void* x, int x_dt, const float* gate, const float
   REQUIRE(m >= 1 && m <= 1024, "%s: m must be in [1, 1024], got %d", what, m);
   REQUIRE(T % m == 0, "%s: T (%lld) must be a multiple of m (%d)", what, (long long)T, m);
   SUPPORT(x_dt == DSV4_F32 || x_dt == DSV4_BF16, "%s: x_dt must be F32 or BF16", what);
-  SUPPORT(y_dt >= DSV4_F32 && y_dt <= DSV4_MXFP4, "%s: unknown y_dt %d", what, y_dt);
+  SUPPORT(y_dt >= DSV4_F32 && y_dt <= DSV4_FP8_KV, "%s: unknown y_dt %d", what, y_dt);
+  if (y_dt == DSV4_FP8_KV)
+    SUPPORT(C % 16 == 0 && C / 2 > dsv4::kFp8RopeDims, "%s: FP8 K|V rows need C %% 16 == 0 and C/2 > %d", what,
+            dsv4::kFp8RopeDims);
   SUPPORT(C % 8 == 0, "%s: C must be a multiple of 8, got %lld", what, (long long)C);
   SUPPORT(C <= (x_dt == DSV4_F32 ? 1024 : 2048), "%s: C too large (f32: <= 1024, bf16: <= 2048)", what);
   if (y_dt == DSV4_MXFP4) SUPPORT(C % 32 == 0, "%s: MXFP4 output needs C %% 32 == 0", what);
@@ -244,7 +247,10 @@ dsv4_status kv_cache_append(const void* x_new, int x_dt, const float* gate_new, 
   REQUIRE(B >= 0 && C > 0 && N >= 0, "%s: need B >= 0, C > 0, N >= 0", what);
   REQUIRE(m >= 1 && m <= 1024, "%s: m must be in [1, 1024], got %d", what, m);
   SUPPORT(x_dt == DSV4_F32 || x_dt == DSV4_BF16, "%s: x_dt must be F32 or BF16", what);
-  SUPPORT(y_dt >= DSV4_F32 && y_dt <= DSV4_MXFP4, "%s: unknown y_dt %d", what, y_dt);
+  SUPPORT(y_dt >= DSV4_F32 && y_dt <= DSV4_FP8_KV, "%s: unknown y_dt %d", what, y_dt);
+  if (y_dt == DSV4_FP8_KV)
+    SUPPORT(C % 16 == 0 && C / 2 > dsv4::kFp8RopeDims, "%s: FP8 K|V rows need C %% 16 == 0 and C/2 > %d", what,
+            dsv4::kFp8RopeDims);
   SUPPORT(C % 8 == 0, "%s: C must be a multiple of 8, got %lld", what, (long long)C);
   SUPPORT(C <= (x_dt == DSV4_F32 ? 1024 : 2048), "%s: C too large (f32: <= 1024, bf16: <= 2048)", what);
   if (y_dt == DSV4_MXFP4) SUPPORT(C % 32 == 0, "%s: MXFP4 output needs C %% 32 == 0", what);

@@ -83,7 +83,10 @@ struct PoolState {
   }
 };
 
-// YDT: 0 f32, 1 bf16, 2 fp8 e4m3, 3 MXFP4
+// YDT: 0 f32, 1 bf16, 2 fp8 e4m3, 3 MXFP4, 4 FP8 K|V rows (the C channels are K then V of
+// D = C/2 dims each; a row is K's first D - kFp8RopeDims channels as E4M3 codes, K's last
+// kFp8RopeDims channels as bf16, then V as E4M3 codes: C + kFp8RopeDims bytes).  Codes
+// are e4m3(y * 2^-e) with e = ysc[0] - 127 for K and ysc[1] - 127 for V (0 without ysc).
 // Thread = (row slot, channel vector): slot r0 of a block takes rows r0, r0 + spb, ...
 // and keeps a running state; the spb slots of a block are then combined.  When lpr and
 // spb are powers of two the slots of a block sit at lane distances lpr, 2 lpr, ... and are
@@ -221,6 +224,31 @@ __device__ __forceinline__ void compress_body(
 #pragma unroll
       for (int v = 0; v < V / 4; ++v) yp[v] = w[v];
     }
+  } else if constexpr (YDT == 4) {
+    if (writer) {
+      const int D = C / 2, DN = D - kFp8RopeDims;
+      const int c0 = cv * V;                     // a vector never straddles a part
+      uint8_t* yr = reinterpret_cast<uint8_t*>(y) + row * (int64_t)(C + kFp8RopeDims);
+      if (c0 >= DN && c0 < D) {
+        uint32_t w[V / 2];
+#pragma unroll
+        for (int v = 0; v < V / 2; ++v) w[v] = pack_bf16x2(acc[2 * v], acc[2 * v + 1]);
+        uint32_t* yp = reinterpret_cast<uint32_t*>(yr + DN + 2 * (c0 - DN));
+#pragma unroll
+        for (int v = 0; v < V / 2; ++v) yp[v] = w[v];
+      } else {
+        const bool is_v = c0 >= D;
+        const int e = ysc ? (int)ysc[is_v ? 1 : 0] - 127 : 0;
+        uint32_t w[V / 4];
+#pragma unroll
+        for (int v = 0; v < V / 4; ++v)
+          w[v] = f32_to_e4m3(ldexpf(acc[4 * v], -e)) | (f32_to_e4m3(ldexpf(acc[4 * v + 1], -e)) << 8) |
+                 (f32_to_e4m3(ldexpf(acc[4 * v + 2], -e)) << 16) | (f32_to_e4m3(ldexpf(acc[4 * v + 3], -e)) << 24);
+        uint32_t* yp = reinterpret_cast<uint32_t*>(yr + (is_v ? c0 + kFp8RopeDims : c0));
+#pragma unroll
+        for (int v = 0; v < V / 4; ++v) yp[v] = w[v];
+      }
+    }
   } else {
     // MXFP4: the 32 channels of a group live in 32/V consecutive lanes.
     float amax = 0.f;
@@ -286,6 +314,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(
   if constexpr (YDT == 0) yr += yrow * C * 4;
   else if constexpr (YDT == 1) yr += yrow * C * 2;
   else if constexpr (YDT == 2) yr += yrow * C;
+  else if constexpr (YDT == 4) yr += yrow * (C + kFp8RopeDims);   // (the scale bytes are per call)
   else {
     yr += yrow * (C / 2);
     sr += yrow * (C / 32);
@@ -366,6 +395,7 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
       case 0: return launch_t<float, 0>(a, st);
       case 1: return launch_t<float, 1>(a, st);
       case 2: return launch_t<float, 2>(a, st);
+      case 4: return launch_t<float, 4>(a, st);
       default: return launch_t<float, 3>(a, st);
     }
   }
@@ -373,6 +403,7 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
     case 0: return launch_t<uint16_t, 0>(a, st);
     case 1: return launch_t<uint16_t, 1>(a, st);
     case 2: return launch_t<uint16_t, 2>(a, st);
+    case 4: return launch_t<uint16_t, 4>(a, st);
     default: return launch_t<uint16_t, 3>(a, st);
   }
 }
@@ -384,6 +415,7 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
       case 0: return launch_append_t<float, 0>(a, st);
       case 1: return launch_append_t<float, 1>(a, st);
       case 2: return launch_append_t<float, 2>(a, st);
+      case 4: return launch_append_t<float, 4>(a, st);
       default: return launch_append_t<float, 3>(a, st);
     }
   }
@@ -391,6 +423,7 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
     case 0: return launch_append_t<uint16_t, 0>(a, st);
     case 1: return launch_append_t<uint16_t, 1>(a, st);
     case 2: return launch_append_t<uint16_t, 2>(a, st);
+    case 4: return launch_append_t<uint16_t, 4>(a, st);
     default: return launch_append_t<uint16_t, 3>(a, st);
   }
 }

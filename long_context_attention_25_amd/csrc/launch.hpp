@@ -32,7 +32,7 @@ struct CompressArgs {
   int64_t x_bs, y_bs;   // batch strides in rows
   void* y;
   uint8_t* y_scale;
-  int y_dt;             // 0 f32, 1 bf16, 2 fp8 e4m3, 3 MXFP4
+  int y_dt;             // 0 f32, 1 bf16, 2 fp8 e4m3, 3 MXFP4, 4 FP8 K|V rows
   int64_t total_blocks() const { return B * (T / m); }
 };
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st);
@@ -49,7 +49,7 @@ struct AppendArgs {
   int m;
   void* y;
   uint8_t* y_scale;
-  int y_dt;             // 0 f32, 1 bf16, 2 fp8 e4m3, 3 MXFP4
+  int y_dt;             // 0 f32, 1 bf16, 2 fp8 e4m3, 3 MXFP4, 4 FP8 K|V rows
   int64_t y_bs, N;
 };
 hipError_t launch_append(const AppendArgs& a, hipStream_t st);

@@ -100,7 +100,8 @@ def test_compress_into_cache_tail_with_batch_stride():
     assert np.all(np.abs(got[:, 12:] - y_ref) <= compress_tol(codecs.decode_bf16(xbits), m, y_ref))
 
 
-@pytest.mark.parametrize("m,C,ydt", [(4, 1024, "bf16"), (128, 1024, "bf16"), (4, 128, "mxfp4"), (4, 64, "f32")])
+@pytest.mark.parametrize("m,C,ydt", [(4, 1024, "bf16"), (128, 1024, "bf16"), (4, 128, "mxfp4"), (4, 64, "f32"),
+                                     (4, 1024, "fp8kv"), (128, 1024, "fp8kv")])
 def test_cache_append_decode_matches_prefix_compression(m, C, ydt):
     """Prefix / decode consistency: a prefix compressed in one call, then one token per
     step through kv_cache_append (the ring wraps twice, blocks complete at different steps
@@ -125,6 +126,9 @@ def test_cache_append_decode_matches_prefix_compression(m, C, ydt):
     if ydt == "mxfp4":
         cache = torch.zeros((B, N, C // 2), dtype=torch.uint8, device="cuda")
         cscale = torch.zeros((B, N, C // 32), dtype=torch.uint8, device="cuda")
+    elif ydt == "fp8kv":
+        cache = torch.zeros((B, N, C + DR), dtype=torch.uint8, device="cuda")
+        cscale = None
     else:
         cache = torch.zeros((B, N, C), dtype=torch.float32 if ydt == "f32" else torch.bfloat16, device="cuda")
         cscale = None
@@ -139,7 +143,7 @@ def test_cache_append_decode_matches_prefix_compression(m, C, ydt):
             if ydt == "mxfp4":
                 kw["out_scale"] = cscale[b:b + 1, :nb0]
             L.csa_compress(xd[b:b + 1, :nb0 * m], gd[b:b + 1, :nb0 * m].contiguous(), bd, m,
-                           L.MXFP4_DTYPE if ydt == "mxfp4" else cache.dtype, **kw)
+                           {"mxfp4": L.MXFP4_DTYPE, "fp8kv": L.FP8_KV_DTYPE}.get(ydt, cache.dtype), **kw)
         for q in range(max(0, int(T0[b]) - Lw), int(T0[b])):
             win[b, q % Lw] = xd[b, q]
             wgate[b, q % Lw] = gd[b, q]
@@ -147,7 +151,8 @@ def test_cache_append_decode_matches_prefix_compression(m, C, ydt):
     for t in range(S):
         pd = dev((T0 + t).astype(np.int32))
         pl = pd.long()
-        L.kv_cache_append(xd[rows, pl].contiguous(), gd[rows, pl].contiguous(), pd, win, wgate, bd, m, cache, cscale)
+        L.kv_cache_append(xd[rows, pl].contiguous(), gd[rows, pl].contiguous(), pd, win, wgate, bd, m, cache, cscale,
+                          cache_dtype=L.FP8_KV_DTYPE if ydt == "fp8kv" else None)
     torch.cuda.synchronize()
     # ring: the last L positions at row position % L, bit for bit
     for b in range(B):
@@ -164,6 +169,9 @@ def test_cache_append_decode_matches_prefix_compression(m, C, ydt):
             got = codecs.decode_mxfp4(codes, scales)
             step = np.repeat(np.ldexp(1.0, scales.astype(np.int64) - 127), 32, axis=1)   # 2^X per group
             assert np.all(np.abs(got - y_ref) <= 2 * step + 1e-6 * np.abs(y_ref))   # e2m1 rounding / saturation
+        elif ydt == "fp8kv":
+            x_b = x64[b:b + 1, :nb * m]
+            _check_fp8kv_rows(cache[b, :nb].cpu().numpy(), y_ref, compress_tol(x_b, m, y_ref[None])[0] - bf16_ulp(y_ref))
         else:
             got = host(cache[b, :nb])
             if ydt == "f32":
@@ -255,6 +263,77 @@ def test_compress_fp8_output_is_a_valid_rounding():
     hi = codecs.encode_e4m3(y32 * np.float32(1 + 1e-6))
     assert np.all(~diff | (got == lo) | (got == hi))
     assert diff.mean() < 1e-3
+
+
+def _check_fp8kv_rows(rows, y_ref, tol, ek=0, ev=0):
+    """rows: FP8 K|V rows [.., C+64] uint8 written by the pooling; y_ref: the oracle's pooled
+    values [.., C]; tol: the fp32 accumulation bound per element.  Code dims must be an
+    E4M3 rounding (nearest-even, saturating) of a value within tol of y_ref * 2^-e; the
+    bf16 dims must lie within tol of y_ref plus one bf16 ulp."""
+    C = y_ref.shape[-1]
+    D, DN = C // 2, C // 2 - DR
+    tol = np.broadcast_to(tol, y_ref.shape)
+
+    def codes_ok(codes, y, t, e):
+        y = y * 2.0 ** -e
+        t = t * 2.0 ** -e
+        lo = codecs.decode_e4m3(codecs.encode_e4m3((y - t).astype(np.float32)))
+        hi = codecs.decode_e4m3(codecs.encode_e4m3((y + t).astype(np.float32)))
+        got = codecs.decode_e4m3(codes)
+        return np.all((got >= lo) & (got <= hi))
+
+    assert codes_ok(rows[..., :DN], y_ref[..., :DN], tol[..., :DN], ek)
+    assert codes_ok(rows[..., D + DR:], y_ref[..., D:], tol[..., D:], ev)
+    tail = np.ascontiguousarray(rows[..., DN:D + DR]).view("<u2")
+    got = codecs.decode_bf16(tail)
+    assert np.all(np.abs(got - y_ref[..., DN:D]) <= tol[..., DN:D] + bf16_ulp(y_ref[..., DN:D]))
+
+
+@pytest.mark.parametrize("m,nb", [(4, 60), (128, 5)])
+def test_compress_fp8kv_rows(m, nb):
+    """Pooling K|V side by side straight into FP8 K|V rows (E4M3 codes with power-of-two
+    scales from two E8M0 bytes, bf16 RoPE dims of K) against the oracle's pooled values."""
+    cfg = 106 + m
+    B, C = 2, 1024
+    x32 = synth.normal(cfg, synth.RAW_K, (B, nb * m, C)) * np.float32(3)
+    gate = synth.normal(cfg, synth.GATE, (B, nb * m))
+    bias = synth.normal(cfg, synth.BIAS, (m,), std=0.1)
+    xd, xbits = dev_bf16(x32)
+    sc = dev(np.array([127 - 2, 127 + 1], dtype=np.uint8))   # K codes of y * 2^2, V codes of y * 2^-1
+    rows = L.csa_compress(xd, dev(gate), dev(bias), m, L.FP8_KV_DTYPE, out_scale=sc)
+    torch.cuda.synchronize()
+    x64 = codecs.decode_bf16(xbits)
+    y_ref = method.compress(x64, gate, bias, m)
+    tol = compress_tol(x64, m, y_ref) - bf16_ulp(y_ref)      # the accumulation part
+    _check_fp8kv_rows(rows.cpu().numpy(), y_ref, tol, ek=-2, ev=1)
+
+
+def test_fp8kv_rows_from_pooling_feed_the_attention():
+    """Stage-wise: HCA attention over an FP8 K|V cache written by the pooling (K|V side by
+    side, row stride C + 64) equals the oracle on the oracle's decoding of those bytes."""
+    cfg = 108
+    B, Q, H, D, m, nb, Lw, W = 2, 2, 64, 512, 128, 40, 128, 128
+    x32 = synth.normal(cfg, synth.RAW_K, (B, nb * m, 2 * D))
+    gate = synth.normal(cfg, synth.GATE, (B, nb * m))
+    bias = synth.normal(cfg, synth.BIAS, (m,), std=0.1)
+    xd, _ = dev_bf16(x32)
+    kv = L.csa_compress(xd, dev(gate), dev(bias), m, L.FP8_KV_DTYPE)        # [B, nb, 1088]
+    (_, _, kwb, vwb), (_, _, kwd, vwd) = _fp8_kv(cfg, B, 1, Lw, D, 1.0, 1.0)
+    q = synth.normal(cfg, synth.Q, (B, Q, H, D))
+    qd, qb = dev_bf16(q)
+    T = nb * m
+    win_pos0 = np.array([T - Lw, T - Lw], dtype=np.int32)
+    pos = np.array([[T - 1, T - 50], [T - 30, T - 100]], dtype=np.int32)
+    KB = D + DR
+    scale = 1.0 / math.sqrt(D)
+    o, lse = L.hca_attend_fp8kv(qd, kv[..., :KB], kv[..., KB:], m, dev(kwb), dev(vwb), dev(win_pos0), W, dev(pos),
+                                scale)
+    torch.cuda.synchronize()
+    rows = kv.cpu().numpy()
+    kd, vd = codecs.decode_fp8_k_rows(rows[..., :KB], D, DR, 1.0), codecs.decode_fp8_v_rows(rows[..., KB:], 1.0)
+    o_ref, lse_ref = method.hca_attend(codecs.decode_bf16(qb), kd, vd, m, kwd, vwd, win_pos0, W, pos, scale)
+    assert row_rel_err(host(o), o_ref) <= 1e-2
+    assert lse_abs_err(host(lse), lse_ref) <= 1e-2
 
 
 # ============================================================ indexer + top-k
