@@ -268,6 +268,110 @@ def time_schedule(L, torch, marsh, steps):
     return res["schedule"] * len(SCHEDULE), {k: round(res[k], 2) for k in ("csa", "hca", "swa")}
 
 
+FP8_ROW = 2 * D + 64               # FP8 K|V row: 448 K codes + 64 bf16 K dims + 512 V codes
+FP8_KERNEL_BYTES = {
+    "attend_fp8kv_kernel (CSA)": B * (TOPK + W) * FP8_ROW + B * H * D * 2 + B * TOPK * 4,
+    "attend_fp8kv_kernel (HCA)": B * (N_HCA + W) * FP8_ROW + B * H * D * 2,
+}
+
+
+def fp8_step_bytes():
+    """Algorithmic bytes of the step with FP8 K|V rows (the bf16 step's, K/V rows at
+    FP8_ROW bytes instead of 4D, pooled rows written at FP8_ROW bytes)."""
+    total, parts = algorithmic_bytes()
+    parts = dict(parts)
+    parts["csa_attend_rows"] = B * (TOPK + W) * FP8_ROW
+    parts["hca_attend_rows"] = B * (N_HCA + W) * FP8_ROW
+    parts["compress"] -= 2 * B * (2 * D * 2 - FP8_ROW)          # the two pooled K|V rows
+    return sum(parts.values()), parts
+
+
+def run_fp8_kv(L, torch, wl, steps, warmup, every=10):
+    """The decode step with the K/V caches and windows stored as FP8 K|V rows (E4M3 codes,
+    bf16 RoPE dims of K): the K|V pooling writes FP8 rows, the attention reads them (the
+    indexer and its MXFP4 keys as in the bf16 step).  The FP8 copies are made once by the
+    library's own pooling with m = 1 (an exact per-row quantisation) before timing."""
+    lib = L.lib()
+    dev = "cuda"
+    P = lambda x: ctypes.c_void_p(x.data_ptr()) if x is not None else None
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def to_fp8(x):                                             # [B, rows, 2D] bf16 -> [B, rows, FP8_ROW]
+        out = torch.empty((x.shape[0], x.shape[1], FP8_ROW), dtype=torch.uint8, device=dev)
+        for b in range(x.shape[0]):
+            g = torch.zeros((1, x.shape[1]), dtype=torch.float32, device=dev)
+            L.csa_compress(x[b:b + 1], g, torch.zeros(1, device=dev), 1, L.FP8_KV_DTYPE, out=out[b:b + 1])
+        return out
+
+    kvc8 = to_fp8(wl.kvc)
+    KB = D + 64
+    scale = 1.0 / math.sqrt(D)
+    steps_calls = []
+    timed = {}
+    n = ctypes.c_size_t(0)
+    for t in wl.r:
+        t8 = {"kvw": to_fp8(t["kvw"]), "hkvc": to_fp8(t["hkvc"]), "hkvw": to_fp8(t["hkvw"])}
+        calls = []
+        calls.append((lib.csa_compress, (P(t["kvw"][:, LWIN - M_CSA:]), L.BF16, P(t["g4"]), P(t["bias"]), B, M_CSA,
+                                         2 * D, M_CSA, LWIN, P(kvc8[:, N_CSA - 1:]), None, L.FP8_KV, N_CSA, st)))
+        calls.append((lib.csa_compress, (P(t["kiw"][:, LWIN - M_CSA:]), L.BF16, P(t["g4"]), P(t["bias"]), B, M_CSA, DI,
+                                         M_CSA, LWIN, P(t["ki"][:, N_CSA - 1:]), P(t["ks"][:, N_CSA - 1:]), L.MXFP4,
+                                         N_CSA, st)))
+        idx_args = (P(t["qi"]), L.BF16, P(t["wi"]), P(t["ki"]), P(t["ks"]), L.MXFP4, P(wl.q_pos), B, 1, HI, DI, N_CSA,
+                    0, M_CSA, TOPK, P(t["idx"]), None)
+        calls.append((lib.csa_index_topk, idx_args + (P(t["ws_idx"]), ctypes.byref(t["ws_idx_n"]), st)))
+        att = (P(t["q"]), P(kvc8), P(kvc8[..., KB:]), P(t["idx"]), TOPK, P(t8["kvw"]), P(t8["kvw"][..., KB:]),
+               P(wl.win_pos0), LWIN, W, P(wl.q_pos), B, 1, H, D, 64, N_CSA, 0, FP8_ROW, FP8_ROW,
+               ctypes.c_float(1.0), ctypes.c_float(1.0), ctypes.c_float(scale), P(t["o"]), P(t["lse"]))
+        assert lib.csa_attend_fp8kv(*att, None, ctypes.byref(n), st) == 0
+        t8["ws_csa"] = torch.empty(max(n.value, 1), dtype=torch.uint8, device=dev)
+        t8["ws_csa_n"] = ctypes.c_size_t(n.value)
+        calls.append((lib.csa_attend_fp8kv, att + (P(t8["ws_csa"]), ctypes.byref(t8["ws_csa_n"]), st)))
+        timed[len(calls) - 1] = "attend_fp8kv_kernel (CSA)"
+        calls.append((lib.csa_compress, (P(t["hkvw"]), L.BF16, P(t["hgate"]), P(t["hbias"]), B, M_HCA, 2 * D, M_HCA,
+                                         LWIN, P(t8["hkvc"][:, N_HCA - 1:]), None, L.FP8_KV, N_HCA, st)))
+        hatt = (P(t["hq"]), P(t8["hkvc"]), P(t8["hkvc"][..., KB:]), M_HCA, P(t8["hkvw"]), P(t8["hkvw"][..., KB:]),
+                P(wl.win_pos0), LWIN, W, P(wl.q_pos), B, 1, H, D, 64, N_HCA, 0, FP8_ROW, FP8_ROW,
+                ctypes.c_float(1.0), ctypes.c_float(1.0), ctypes.c_float(scale), P(t["ho"]), P(t["hlse"]))
+        assert lib.hca_attend_fp8kv(*hatt, None, ctypes.byref(n), st) == 0
+        t8["ws_hca"] = torch.empty(max(n.value, 1), dtype=torch.uint8, device=dev)
+        t8["ws_hca_n"] = ctypes.c_size_t(n.value)
+        calls.append((lib.hca_attend_fp8kv, hatt + (P(t8["ws_hca"]), ctypes.byref(t8["ws_hca_n"]), st)))
+        timed[len(calls) - 1] = "attend_fp8kv_kernel (HCA)"
+        t["fp8"] = t8
+        steps_calls.append(calls)
+    torch.cuda.synchronize()
+    ev = HipEvents()
+    pairs = [{i: (ev.create(), ev.create()) for i in timed} for _ in range((steps + every - 1) // every)]
+    for i in range(warmup):
+        run_step(lib, steps_calls[i % len(steps_calls)])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        run_step(lib, steps_calls[i % len(steps_calls)], arm=pairs[i // every] if i % every == 0 else None)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    kernels = {}
+    for i, name in timed.items():
+        k_ms = sum(ev.elapsed_ms(*p[i]) for p in pairs) / len(pairs)
+        gbs = FP8_KERNEL_BYTES[name] / (k_ms / 1e3) / 1e9
+        kernels[name] = {"avg_launch_us": round(k_ms * 1e3, 2), "bytes_per_launch": FP8_KERNEL_BYTES[name],
+                         "achieved_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    total, _ = fp8_step_bytes()
+    kv_tok = {"csa": (FP8_ROW + DI // 2 + DI // 32) / M_CSA, "hca": FP8_ROW / M_HCA}
+    del kvc8
+    for t in wl.r:
+        t.pop("fp8", None)
+    return {"ms_per_step": round(ms, 5), "queries_per_s": round(B / (ms / 1e3), 1), "bytes_per_step": total,
+            "step_hbm_gbs": round(total / (ms / 1e3) / 1e9, 1), "kernels": kernels,
+            "kv_bytes_per_token": {k: round(v, 2) for k, v in kv_tok.items()},
+            "note": "the same step with K/V caches and windows as FP8 K|V rows (448 E4M3 K codes, 64 bf16 K dims, "
+                    "512 E4M3 V codes per row; scales 1): pooling writes FP8 rows, attention decodes them in its "
+                    "tile loop; measured after the bf16 steps, same replicas and indexer"}
+
+
 class HipEvents:
     """Raw hipEvent_t pairs from the HIP runtime torch already loaded."""
 
@@ -553,6 +657,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-schedule", action="store_true", help="skip the 61-layer schedule timing")
+    ap.add_argument("--no-fp8-kv", action="store_true", help="skip the step with FP8 K|V caches")
     ap.add_argument("--prefill", action="store_true",
                     help="measure the chunked-prefill stack instead of decode (prints its own line)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -645,6 +750,8 @@ def main():
                           "bf16_query_avg_launch_us": kernels["index_mfma_kernel"]["avg_launch_us"],
                           "note": "the same 8 x 262144 MXFP4 keys with MXFP4 queries (scaled FP4 MFMA); "
                                   "main kernel only, measured after the timed steps"}
+    if not args.no_fp8_kv:
+        out["fp8_kv"] = run_fp8_kv(L, torch, wl, args.steps, args.warmup, every)
     out["cache_append"] = {"us_per_step": round(time_cache_append(L, torch, wl, 50), 2), "calls_per_step": 3,
                            "note": "kv_cache_append for CSA K|V, CSA indexer key (MXFP4) and HCA K|V, each new "
                                    "token completing a block (worst case); measured after the timed steps"}

@@ -19,6 +19,8 @@
 //   O^T += V^T.P^T with no data movement.  Online softmax in fp32 (exp2 with the
 //   scale folded in).  Splits write fp32 partial (o, lse) that lse_merge combines.
 // fp32 path: a plain VALU kernel, one workgroup per (query, head).
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -84,6 +86,7 @@ __device__ __forceinline__ int64_t key_row(const AttendArgs& a, int64_t bq, cons
 
 // ---------------------------------------------------------------------------- bf16 / MFMA
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef int v2i32 __attribute__((ext_vector_type(2)));
 
 // Pointer held by lane `src` (src < 64): a scalar readlane when `src` is the same for the
 // whole wave, a cross-lane shuffle otherwise.
@@ -149,18 +152,10 @@ __device__ __forceinline__ void tile_barrier() {
 // bytes, V: +32 bytes) so that the K operand reads (16 rows, same column) and the
 // transposed V reads (4 rows x 2 chunks per 16 lanes) hit distinct banks while every read
 // of a lane uses one base address plus immediate offsets.
-//
-// F8 (K/V rows stored as e4m3 codes, the last kFp8RopeDims dims of K as bf16): the copies
-// land in a separate four-stage ring of packed fp8 rows, and one tile ahead of its use
-// every tile is decoded (exactly: each e4m3 value is a bf16 value) into one of two bf16
-// tiles of the layout above, which the same MFMA code then reads.  The K scale multiplies
-// the scores of the fp8 dims only, and the V scale the output, so both stay exact.  Here
-// the k-steps take the head dims in natural order (k-step c: dims 32c .. 32c+31) so that
-// the bf16 dims form whole k-steps with their own accumulator.
-template <int D, int DS, bool F8>
-__device__ __forceinline__ void attend_body(const AttendArgs& a, int64_t chunk, int splits,
-                                            uint16_t* __restrict__ o_part, float* __restrict__ lse_part) {
-  using E = typename std::conditional<F8, uint8_t, uint16_t>::type;   // row pointer unit
+template <int D, int DS>
+__global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a, int64_t chunk, int splits,
+                                                               uint16_t* __restrict__ o_part,
+                                                               float* __restrict__ lse_part) {
   constexpr int KT = 16;                   // keys per tile
   constexpr int NT = kThreads * DS;
   constexpr int NWV = NT / kWave;
@@ -175,19 +170,10 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, int64_t chunk, 
   constexpr int NL = 2 * RPW;              // copy instructions per wave and tile
   constexpr int KTB = KT * KSTR, VTB = KT * VSTR;
   static_assert(LPR <= kWave && kWave % LPR == 0, "a row is copied by one instruction");
-  static_assert(3 * NL < 64 && 4 * NL < 64, "vmcnt range");
-  // fp8 rows: K = DN e4m3 bytes + DR bf16 values, V = D e4m3 bytes (packed in the ring)
-  constexpr int DR = F8 ? kFp8RopeDims : 0;
-  constexpr int DN = D - DR;
-  constexpr int K8B = DN + 2 * DR, V8B = D;
-  constexpr int K8T = KT * K8B, ST8 = K8T + KT * V8B;
-  static_assert(!F8 || (K8B % 16 == 0 && K8B / 16 <= kWave && V8B / 16 <= kWave), "fp8 row copies");
-  static_assert(!F8 || (DN % 16 == 0 && DR % 32 == 0), "fp8 dims");
+  static_assert(3 * NL < 64, "vmcnt range");
 
   constexpr int STB = KTB + VTB;          // one stage: K tile then V tile
-  // bf16: four stages of bf16 tiles.  F8: two bf16 tiles, then four stages of fp8 tiles.
-  constexpr int RING = F8 ? 2 * STB + 4 * ST8 : 4 * STB;
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[RING];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[4 * STB];
   __shared__ int32_t list[kMaxCsaChunk];  // the split's index entries
   __shared__ __attribute__((aligned(16))) uint8_t xchg[DS > 1 ? NT * 16 : 16];   // partial scores
 
@@ -203,13 +189,11 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, int64_t chunk, 
 
   // The loads that do not depend on each other are issued together and waited for once:
   // the query position, the split's index entries (CSA: list slots s0 .. s0+chunk-1, all
-  // below k <= n_tot), and the workgroup's query rows, copied once into LDS (bf16: stages
-  // 2 and 3, free until tile 2 is issued; F8: the two bf16 tiles, free until tile 0 is
-  // decoded).  The copies into LDS are then the only vector-memory operations in flight in
-  // the tile loop.
+  // below k <= n_tot), and the workgroup's query rows, copied once into LDS stages 2 and 3
+  // (free until tile 2 is issued).  The copies into LDS are then the only vector-memory
+  // operations in flight in the tile loop.
   const uint32_t ring_lds = lds_addr(ring);
-  const uint32_t q_lds = F8 ? ring_lds : ring_lds + 2 * STB;
-  const uint32_t f8_lds = ring_lds + 2 * STB;      // F8: first fp8 stage
+  const uint32_t q_lds = ring_lds + 2 * STB;
   static_assert(kHeads * KSTR <= 2 * STB, "query rows fit in two stages");
   {
     const uint16_t* qb = reinterpret_cast<const uint16_t*>(a.q) + bq * a.H * D;
@@ -219,43 +203,28 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, int64_t chunk, 
       if (h < a.H && lane < LPR) copy16_to_lds(qb + h * D + lane * 8, q_lds + h * KSTR);
     }
   }
-  // row strides in units of E (bf16: elements; F8: bytes)
   const int64_t krs = a.kv_rs, wrs = a.w_rs;
-  const int64_t vrs = F8 ? a.v_rs : a.kv_rs, wvrs = F8 ? a.wv_rs : a.w_rs;
-  const E* kc = reinterpret_cast<const E*>(a.kc) + b * a.kv_bs * krs;
-  const E* vc = reinterpret_cast<const E*>(a.vc) + b * a.kv_bs * vrs;
-  const E* kw = reinterpret_cast<const E*>(a.kw) + b * a.L * wrs;
-  const E* vw = reinterpret_cast<const E*>(a.vw) + b * a.L * wvrs;
+  const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.kc) + b * a.kv_bs * krs;
+  const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.vc) + b * a.kv_bs * krs;
+  const uint16_t* kw = reinterpret_cast<const uint16_t*>(a.kw) + b * a.L * wrs;
+  const uint16_t* vw = reinterpret_cast<const uint16_t*>(a.vw) + b * a.L * wrs;
   // Row pointers of a tile for key (lane % 16), set by tile_ptrs / spec_ptrs below.
-  const E* my_kp;
-  const E* my_vp;
+  const uint16_t* my_kp;
+  const uint16_t* my_vp;
   uint32_t vmask = 0;                       // validity of the tile's 16 keys
   // Wave w copies rows w, w+4, ... of the tile; a row is LPR lanes x 16 bytes (the other
   // lanes of a wave are masked off when a row is shorter than a wave).
   auto issue = [&](int stage) {
-    if constexpr (F8) {
-      const uint32_t kdst = f8_lds + stage * ST8;
-      const uint32_t vdst = kdst + K8T;
+    const uint32_t kdst = ring_lds + stage * STB;
+    const uint32_t vdst = kdst + KTB;
+    const int j = lane / LPR;              // 0 unless LPR < 64
 #pragma unroll
-      for (int i = 0; i < RPW; ++i) {
-        const int r = wave + i * NWV;
-        const E* kp = lane_ptr<true>(my_kp, r);
-        const E* vp = lane_ptr<true>(my_vp, r);
-        if (lane < K8B / 16) copy16_to_lds(kp + lane * 16, kdst + r * K8B);
-        if (lane < V8B / 16) copy16_to_lds(vp + lane * 16, vdst + r * V8B);
-      }
-    } else {
-      const uint32_t kdst = ring_lds + stage * STB;
-      const uint32_t vdst = kdst + KTB;
-      const int j = lane / LPR;              // 0 unless LPR < 64
-#pragma unroll
-      for (int i = 0; i < RPW; ++i) {
-        const int r = wave + i * NWV;
-        const int off = (lane % LPR) * 8;
-        if (j == 0) {
-          copy16_to_lds(lane_ptr<true>(my_kp, r) + off, kdst + r * KSTR);
-          copy16_to_lds(lane_ptr<true>(my_vp, r) + off, vdst + r * VSTR);
-        }
+    for (int i = 0; i < RPW; ++i) {
+      const int r = wave + i * NWV;
+      const int off = (lane % LPR) * 8;
+      if (j == 0) {
+        copy16_to_lds(lane_ptr<true>(my_kp, r) + off, kdst + r * KSTR);
+        copy16_to_lds(lane_ptr<true>(my_vp, r) + off, vdst + r * VSTR);
       }
     }
   };
@@ -268,7 +237,7 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, int64_t chunk, 
     int64_t j = s0 + (int64_t)t * KT + (lane & (KT - 1));
     if (j > a.N - 1) j = a.N - 1;
     my_kp = kc + j * krs;
-    my_vp = vc + j * vrs;
+    my_vp = vc + j * krs;
   };
   if (spec) {
     spec_ptrs(0);
@@ -311,26 +280,26 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, int64_t chunk, 
   // Invalid slots point at a row that holds data (the query's first window row, else the
   // first compressed row), since their zero weights would not cancel a non-finite value.
   const bool win_rows = kr.n_tot > kr.n_c;
-  const E* kdef = win_rows ? kw + wrow(a, kr.r_lo) * wrs : kc;
-  const E* vdef = win_rows ? vw + wrow(a, kr.r_lo) * wvrs : vc;
+  const uint16_t* kdef = win_rows ? kw + wrow(a, kr.r_lo) * wrs : kc;
+  const uint16_t* vdef = win_rows ? vw + wrow(a, kr.r_lo) * wrs : vc;
   auto tile_ptrs = [&](int t) {
     const int64_t pos = s0 + (int64_t)t * KT + (lane & (KT - 1));
     bool ok = false;
-    const E* kp = kdef;
-    const E* vp = vdef;
+    const uint16_t* kp = kdef;
+    const uint16_t* vp = vdef;
     if (pos < s1) {
       if (pos < kr.n_c) {
         const int64_t j = a.csa ? (int64_t)list[pos - s0] : pos;
         if (j >= 0 && j < a.N) {
           ok = true;
           kp = kc + j * krs;
-          vp = vc + j * vrs;
+          vp = vc + j * krs;
         }
       } else {
         const int64_t r = wrow(a, kr.r_lo + (pos - kr.n_c));
         ok = true;
         kp = kw + r * wrs;
-        vp = vw + r * wvrs;
+        vp = vw + r * wrs;
       }
     }
     my_kp = kp;
@@ -344,18 +313,13 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, int64_t chunk, 
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.scale * kLog2e;
   // Scores over the head dim are split between the DS waves of a head group: wave slice
-  // dh takes k-steps dh*KSW .. +KSW-1 (bf16: dims g*D/4 + 8c .. +7 of lane group g for
-  // k-step c; F8: dims 32c + 8g .. +7) and the DS partial scores are summed through LDS.
+  // dh takes k-steps dh*KSW .. +KSW-1 (dims g*D/4 + 8c .. +7 of lane group g for k-step c)
+  // and the DS partial scores are summed through LDS.
   constexpr int KSW = KS / DS;
-  constexpr int KSR = DR / 32;             // F8: bf16 k-steps, the last ones of slice DS-1
-  static_assert(KSR <= KSW, "bf16 dims within one slice");
   // per-lane LDS byte offsets: K operand row `col` at this wave's first k-step; V^T rows
   // 4g + col/4 at dims dh*DH + 4(col%4)
-  constexpr int KCS = F8 ? 64 : 16;        // byte step between k-steps of a lane
-  const int k_off = F8 ? col * KSTR + g * 16 + dh * KSW * 64 : col * KSTR + g * (D / 4) * 2 + dh * KSW * 16;
+  const int k_off = col * KSTR + g * (D / 4) * 2 + dh * KSW * 16;
   const int v_off = (4 * g + (col >> 2)) * VSTR + dh * DH * 2 + (col & 3) * 8;
-  // F8: the fp8 k-steps' partial scores are multiplied by k_scale, the bf16 ones are not
-  const float rope_mul = F8 && dh != DS - 1 ? a.k_scale : 1.f;
 
   uint4 qop[KSW];                          // Q^T operands, read from LDS below
   // ---- partial S^T = K . Q^T (16 keys x 16 heads) over this wave's k-steps.  K operands
@@ -363,14 +327,15 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, int64_t chunk, 
   // scheduling barriers keep the compiler from pairing each read with its MFMA; two
   // batches stay within the 15 outstanding LDS reads the counter tracks).  Two
   // accumulators halve the dependent MFMA chain.
-  auto compute_s = [&](const uint8_t* kt_l) -> f32x4 {
-    f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = sa, sr = sa;
+  auto compute_s = [&](int stage) -> f32x4 {
+    const uint8_t* kt_l = ring + stage * STB;
+    f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = sa;
     constexpr int CB = KSW < 4 ? KSW : 4;
     constexpr int NB = KSW / CB;
     uint4 kv[2][CB];
     auto kread = [&](int buf, int c0) {
 #pragma unroll
-      for (int c = 0; c < CB; ++c) kv[buf][c] = *reinterpret_cast<const uint4*>(kt_l + k_off + (c0 + c) * KCS);
+      for (int c = 0; c < CB; ++c) kv[buf][c] = *reinterpret_cast<const uint4*>(kt_l + k_off + (c0 + c) * 16);
     };
     kread(0, 0);
 #pragma unroll
@@ -379,21 +344,17 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, int64_t chunk, 
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int c = 0; c < CB; ++c) {
-        const int ks = bi * CB + c;
-        const bf16x8 ka = bit_cast_to<bf16x8>(kv[bi & 1][c]);
-        const bf16x8 qb = bit_cast_to<bf16x8>(qop[ks]);
-        if (F8 && ks >= KSW - KSR) sr = mfma_bf16(ka, qb, sr);
-        else if (ks & 1) sb = mfma_bf16(ka, qb, sb);
-        else sa = mfma_bf16(ka, qb, sa);
+        if ((bi * CB + c) & 1) sb = mfma_bf16(bit_cast_to<bf16x8>(kv[bi & 1][c]), bit_cast_to<bf16x8>(qop[bi * CB + c]), sb);
+        else sa = mfma_bf16(bit_cast_to<bf16x8>(kv[bi & 1][c]), bit_cast_to<bf16x8>(qop[bi * CB + c]), sa);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (F8) return (sa + sb) * a.k_scale + sr * rope_mul;
     return sa + sb;
   };
   // ---- softmax of the full scores (lane holds keys 4g + i of head `head`), lazy
   // rescaling, then O^T += V^T . P^T
-  auto compute_pv = [&](const uint8_t* vt_l, uint32_t cur_mask, f32x4 s) {
+  auto compute_pv = [&](int stage, uint32_t cur_mask, f32x4 s) {
+    const uint8_t* vt_l = ring + stage * STB + KTB;
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -445,59 +406,17 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, int64_t chunk, 
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // ---- F8: decode the fp8 tile of stage `stage` into bf16 tile `buf`.  Units of 16 fp8
-  // bytes (K codes, then V codes) and of 16 bytes of K's bf16 dims, spread over the
-  // threads; the unit counts are multiples of 64, so every branch is uniform in a wave.
-  auto decode = [&](int stage, int buf) {
-    if constexpr (F8) {
-      constexpr int UK = KT * (DN / 16), UV = KT * (D / 16), UR = KT * (DR * 2 / 16);
-      static_assert(UK % kWave == 0 && UV % kWave == 0 && UR % kWave == 0, "uniform units");
-      const uint8_t* src = ring + 2 * STB + stage * ST8;
-      uint8_t* dst = ring + buf * STB;
-#pragma unroll
-      for (int u0 = 0; u0 < UK + UV + UR; u0 += NT) {
-        const int u = u0 + tid;
-        if (u < UK + UV) {
-          const bool is_v = u >= UK;
-          const int w = is_v ? u - UK : u;
-          const int cpr = is_v ? D / 16 : DN / 16;     // units per row
-          const int r = w / cpr, c = w - r * cpr;
-          const uint4 x = *reinterpret_cast<const uint4*>(src + (is_v ? K8T + r * V8B : r * K8B) + c * 16);
-          uint8_t* d = dst + (is_v ? KTB + r * VSTR : r * KSTR) + c * 32;
-          const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
-          uint32_t y[8];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            y[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(xs[i], 1.f, false));
-            y[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(xs[i], 1.f, true));
-          }
-          reinterpret_cast<uint4*>(d)[0] = make_uint4(y[0], y[1], y[2], y[3]);
-          reinterpret_cast<uint4*>(d)[1] = make_uint4(y[4], y[5], y[6], y[7]);
-        } else if (u < UK + UV + UR) {
-          const int w = u - UK - UV;
-          const int r = w / (DR * 2 / 16), c = w - r * (DR * 2 / 16);
-          *reinterpret_cast<uint4*>(dst + r * KSTR + DN * 2 + c * 16) =
-              *reinterpret_cast<const uint4*>(src + r * K8B + DN + c * 16);
-        }
-      }
-    }
-  };
 
-  // bf16: tile t lives in stage t % 4.  Tiles 0 and 1 are issued first; then every wave
-  // reads its Q^T operands (head `head`, for each of its k-steps) from stages 2-3, and
-  // after a barrier tile 2 is issued.  Step t then waits for tile t (tiles t+1, t+2 stay
-  // in flight), passes a barrier (tile t visible to all waves; every wave is done with
-  // tile t-1), issues tile t+3 into the stage of tile t-1 and uses tile t.
-  // F8: tile t lives in fp8 stage t % 4 and, decoded, in bf16 tile t % 2.  Tiles 0 .. 3
-  // are issued first, tile 0 is decoded after the Q^T operands are read; step t waits for
-  // tile t+1, passes a barrier (bf16 tile t complete; every wave is done with bf16 tile
-  // t-1 and with fp8 stage t), issues tile t+4 into fp8 stage t % 4, decodes tile t+1 into
-  // bf16 tile (t+1) % 2 and uses bf16 tile t.
-  uint32_t mq0 = 0, mq1 = 0, mq2 = 0, mq3 = 0;   // masks of tiles t, t+1, t+2, t+3
+  // Tile t lives in stage t % 4.  Tiles 0 and 1 are issued first; then every wave reads
+  // its Q^T operands (head `head`, dims g*D/4 + 8c .. +7 for k-step c) from stages 2-3,
+  // and after a barrier tile 2 is issued.  Step t then waits for tile t (tiles t+1, t+2
+  // stay in flight), passes a barrier (tile t visible to all waves; every wave is done
+  // with tile t-1), issues tile t+3 into the stage of tile t-1 and uses tile t.
+  uint32_t mq0 = 0, mq1 = 0, mq2 = 0;      // masks of tiles t, t+1, t+2
   if (spec) {
     bool same = true;
-    const E* sk[2];
-    const E* sv[2];
+    const uint16_t* sk[2];
+    const uint16_t* sv[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       spec_ptrs(t);
@@ -523,54 +442,26 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, int64_t chunk, 
     if (ntile > 0) { tile_ptrs(0); mq0 = vmask; issue(0); }
     if (ntile > 1) { tile_ptrs(1); mq1 = vmask; issue(1); }
   }
-  if constexpr (F8) {
-    if (ntile > 2) { tile_ptrs(2); mq2 = vmask; issue(2); }
-    if (ntile > 3) { tile_ptrs(3); mq3 = vmask; issue(3); }
-  }
   {
-    const uint8_t* ql = F8 ? ring + (wave_on ? head : 0) * KSTR + g * 16 + dh * KSW * 64
-                           : ring + 2 * STB + (wave_on ? head : 0) * KSTR + g * (D / 4) * 2 + dh * KSW * 16;
+    const uint8_t* ql = ring + 2 * STB + (wave_on ? head : 0) * KSTR + g * (D / 4) * 2 + dh * KSW * 16;
 #pragma unroll
-    for (int c = 0; c < KSW; ++c) qop[c] = *reinterpret_cast<const uint4*>(ql + c * KCS);
+    for (int c = 0; c < KSW; ++c) qop[c] = *reinterpret_cast<const uint4*>(ql + c * 16);
   }
-  if constexpr (F8) {
-    if (ntile > 3) wait_vmcnt<3 * NL>();
-    else if (ntile > 2) wait_vmcnt<2 * NL>();
-    else if (ntile > 1) wait_vmcnt<NL>();
-    else wait_vmcnt<0>();
-    tile_barrier();                          // tile 0 landed everywhere; Q^T operands read
-    if (ntile > 0) decode(0, 0);
-  } else {
-    tile_barrier();
-    if (ntile > 2) { tile_ptrs(2); mq2 = vmask; issue(2); }
-  }
+  tile_barrier();
+  if (ntile > 2) { tile_ptrs(2); mq2 = vmask; issue(2); }
   for (int t = 0; t < ntile; ++t) {
-    uint32_t mqn = 0;
-    if constexpr (F8) {
-      if (t + 3 < ntile) wait_vmcnt<2 * NL>();
-      else if (t + 2 < ntile) wait_vmcnt<NL>();
-      else wait_vmcnt<0>();
-      tile_barrier();
-      if (t + 4 < ntile) {
-        tile_ptrs(t + 4);
-        mqn = vmask;
-        issue(t & 3);
-      }
-      if (t + 1 < ntile) decode((t + 1) & 3, (t + 1) & 1);
-    } else {
-      if (t + 2 < ntile) wait_vmcnt<2 * NL>();
-      else if (t + 1 < ntile) wait_vmcnt<NL>();
-      else wait_vmcnt<0>();
-      tile_barrier();
-      if (t + 3 < ntile) {
-        tile_ptrs(t + 3);
-        mqn = vmask;
-        issue((t + 3) & 3);
-      }
+    if (t + 2 < ntile) wait_vmcnt<2 * NL>();
+    else if (t + 1 < ntile) wait_vmcnt<NL>();
+    else wait_vmcnt<0>();
+    tile_barrier();
+    uint32_t mq3 = 0;
+    if (t + 3 < ntile) {
+      tile_ptrs(t + 3);
+      mq3 = vmask;
+      issue((t + 3) & 3);
     }
-    const uint8_t* kt_l = F8 ? ring + (t & 1) * STB : ring + (t & 3) * STB;
     f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (wave_on) sc = compute_s(kt_l);
+    if (wave_on) sc = compute_s(t & 3);
     if constexpr (DS > 1) {
       // partial scores of the DS slices of a head group (waves hg + 4j), summed in the
       // same order by every slice so that all of them see identical scores
@@ -584,22 +475,17 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, int64_t chunk, 
         sc = tot;
       }
     }
-    if (wave_on) compute_pv(kt_l + KTB, mq0, sc);
+    if (wave_on) compute_pv(t & 3, mq0, sc);
     mq0 = mq1;
     mq1 = mq2;
-    if constexpr (F8) {
-      mq2 = mq3;
-      mq3 = mqn;
-    } else {
-      mq2 = mqn;
-    }
+    mq2 = mq3;
   }
   wait_vmcnt<0>();                           // no copy into LDS outlives the workgroup
 
   if (!wave_on) return;
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  const float inv = l_run > 0.f ? (F8 ? a.v_scale : 1.f) / l_run : 0.f;
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
   const float lse = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
   // the output row, or with several splits this split's partial row (bf16 like the
   // output; the merge accumulates in fp32)
@@ -623,17 +509,379 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, int64_t chunk, 
   }
 }
 
-template <int D, int DS>
-__global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a, int64_t chunk, int splits,
-                                                               uint16_t* __restrict__ o_part,
-                                                               float* __restrict__ lse_part) {
-  attend_body<D, DS, false>(a, chunk, splits, o_part, lse_part);
-}
-template <int D, int DS>
-__global__ __launch_bounds__(kThreads * DS) void attend_fp8kv_kernel(AttendArgs a, int64_t chunk, int splits,
+// ---------------------------------------------------------------------------- FP8 K/V rows
+// K rows of DN = D - kFp8RopeDims E4M3 codes followed by kFp8RopeDims bf16 values, V rows
+// of D E4M3 codes.  Same work split as the bf16 kernel (D = 512: 8 waves, wave w owns
+// heads 16(w%4) .. +15 and output dims (w/4)*256 .. +255), with 32-key tiles whose fp8
+// rows are copied straight into a four-stage LDS ring (about 105 KB in flight per CU) and
+// decoded exactly to bf16 in registers as MFMA operands are read:
+//   S^T = K.Q^T per 16-key half: K operand = 8 code bytes of one key (one 8-byte LDS
+//     read, four conversions) or 8 bf16 values for the RoPE dims; the k-steps take the
+//     head dims in natural order (k-step c: dims 32c .. 32c+31) so that the bf16 dims
+//     form whole k-steps, accumulated apart; k_scale multiplies the code dims' scores.
+//   O^T += V^T.P^T with mfma_f32_16x16x32_bf16 over all 32 keys: a transposed 8-bit LDS
+//     read gives a lane one dim of 8 keys (the 8 rows its 16-lane block addresses, two
+//     lanes per row), chosen as the keys whose probabilities the lane already holds from
+//     the two S^T halves (keys 4g..4g+3 and 16+4g..16+4g+3), so P^T needs no exchange.
+//   v_scale multiplies the output.
+// LDS rows are padded (K: +16 bytes, V: +16 bytes and +128 for the second half of a tile)
+// so that the 8-byte K reads of 16 rows hit distinct banks and the two 16-lane blocks of
+// a transposed V read that the LDS serves together (8 rows each) take disjoint halves of
+// the banks.
+constexpr int kListF8 = 512;          // index entries of one CSA split (FP8 kernel)
+
+template <int D>
+__global__ __launch_bounds__(kThreads * 2) void attend_fp8kv_kernel(AttendArgs a, int64_t chunk, int splits,
                                                                 uint16_t* __restrict__ o_part,
                                                                 float* __restrict__ lse_part) {
-  attend_body<D, DS, true>(a, chunk, splits, o_part, lse_part);
+  constexpr int DS = 2;
+  constexpr int KT = 32;                   // keys per tile
+  constexpr int NT = kThreads * DS;
+  constexpr int NWV = NT / kWave;
+  constexpr int KS = D / 32;               // k-steps over the head dim
+  constexpr int KSW = KS / DS;             // k-steps of a wave slice
+  constexpr int DH = D / DS;               // output dims of a wave
+  constexpr int NDT = DH / 16;             // 16-dim output tiles of a wave
+  constexpr int DR = kFp8RopeDims, DN = D - DR;
+  constexpr int KSR = DR / 32;             // bf16 k-steps: the last ones of slice DS-1
+  constexpr int K8B = DN + 2 * DR, V8B = D;   // bytes of a K row and a V row
+  constexpr int K8S = K8B + 16, V8S = V8B + 16;
+  constexpr int VH = 128;                  // extra offset of V rows 16..31
+  constexpr int KTB = KT * K8S, VTB = KT * V8S + VH;
+  constexpr int STB = KTB + VTB;           // one stage: K tile then V tile
+  constexpr int RPW = KT / NWV;            // rows copied per wave and matrix
+  constexpr int NL = 2 * RPW;              // copy instructions per wave and tile
+  constexpr int QSTR = 2 * D + 16;         // query rows in LDS
+  static_assert(DS == 2 && KSR <= KSW && DN % 32 == 0, "slices and bf16 k-steps");
+  static_assert(K8B % 16 == 0 && K8B / 16 <= kWave && V8B / 16 <= kWave, "one row per copy");
+  static_assert(kHeads * QSTR <= 2 * STB, "query rows fit in two stages");
+  static_assert(3 * NL < 64, "vmcnt range");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[4 * STB];
+  __shared__ int32_t list[kListF8];
+  __shared__ __attribute__((aligned(16))) f32x4 xchg[2 * NT];   // partial scores of both halves
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, col = lane & 15;
+  const int64_t bq = blockIdx.y;
+  const int64_t b = bq / a.Q;
+  const int split = blockIdx.x;
+  const int64_t s0 = (int64_t)split * chunk;
+  const int hg = wave % 4, dh = wave / 4;
+  const int head = hg * 16 + col;
+  const bool wave_on = hg * 16 < a.H;
+
+  // query rows into stages 2 and 3 (free until tile 2 is issued), issued first
+  const uint32_t ring_lds = lds_addr(ring);
+  {
+    const uint16_t* qb = reinterpret_cast<const uint16_t*>(a.q) + bq * a.H * D;
+#pragma unroll
+    for (int i = 0; i < kHeads / NWV; ++i) {
+      const int h = wave + i * NWV;
+      if (h < a.H && lane < D * 2 / 16) copy16_to_lds(qb + h * D + lane * 8, ring_lds + 2 * STB + h * QSTR);
+    }
+  }
+  const int64_t krs = a.kv_rs, vrs = a.v_rs, wrs = a.w_rs, wvrs = a.wv_rs;   // bytes
+  const uint8_t* kc = reinterpret_cast<const uint8_t*>(a.kc) + b * a.kv_bs * krs;
+  const uint8_t* vc = reinterpret_cast<const uint8_t*>(a.vc) + b * a.kv_bs * vrs;
+  const uint8_t* kw = reinterpret_cast<const uint8_t*>(a.kw) + b * a.L * wrs;
+  const uint8_t* vw = reinterpret_cast<const uint8_t*>(a.vw) + b * a.L * wvrs;
+  const uint8_t* my_kp;                    // row pointers of key (lane % 32) of a tile
+  const uint8_t* my_vp;
+  uint32_t vmask = 0;
+  // Wave w copies rows w, w+8, w+16, w+24 of K and of V (one row per copy instruction).
+  auto issue = [&](int stage) {
+    const uint32_t kdst = ring_lds + stage * STB;
+    const uint32_t vdst = kdst + KTB;
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int r = wave + i * NWV;
+      const uint8_t* kp = lane_ptr<true>(my_kp, r);
+      const uint8_t* vp = lane_ptr<true>(my_vp, r);
+      if (lane < K8B / 16) copy16_to_lds(kp + lane * 16, kdst + r * K8S);
+      if (lane < V8B / 16) copy16_to_lds(vp + lane * 16, vdst + r * V8S + (r >= 16 ? VH : 0));
+    }
+  };
+  // HCA: tiles 0 and 1 issued before the query position is known (checked below)
+  const bool spec = !a.csa && a.N > 0;
+  auto spec_ptrs = [&](int t) {
+    int64_t j = s0 + (int64_t)t * KT + (lane & (KT - 1));
+    if (j > a.N - 1) j = a.N - 1;
+    my_kp = kc + j * krs;
+    my_vp = vc + j * vrs;
+  };
+  if (spec) {
+    spec_ptrs(0);
+    issue(0);
+    spec_ptrs(1);
+    issue(1);
+  }
+  const int32_t qpos = load_uniform(a.q_pos + bq);
+  const int32_t wpos0 = a.win_pos0 ? load_uniform(a.win_pos0 + b) : 0;
+  static_assert(kListF8 % NT == 0, "list entries per thread");
+  constexpr int LPT = kListF8 / NT;
+  int32_t lv[LPT];
+  const int64_t e1 = s0 + chunk < a.k ? s0 + chunk : a.k;
+  if (a.csa) {
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const int64_t p = s0 + tid + u * NT;
+      lv[u] = p < e1 ? a.idx[bq * a.k + p] : -1;
+    }
+    wait_vmcnt<0>();
+  } else if (spec) {
+    wait_vmcnt<2 * NL>();                   // the query rows (issued first) have landed
+  } else {
+    wait_vmcnt<0>();
+  }
+  const KeyRange kr = key_range(a, qpos, wpos0);
+  int64_t s1 = s0 + chunk;
+  if (s1 > kr.n_tot) s1 = kr.n_tot;
+  const int ntile = s1 > s0 ? (int)((s1 - s0 + KT - 1) / KT) : 0;
+  if (a.csa) {
+#pragma unroll
+    for (int u = 0; u < LPT; ++u)
+      if (s0 + tid + u * NT < e1) list[tid + u * NT] = lv[u];
+  }
+  __syncthreads();
+
+  const bool win_rows = kr.n_tot > kr.n_c;
+  const uint8_t* kdef = win_rows ? kw + wrow(a, kr.r_lo) * wrs : kc;
+  const uint8_t* vdef = win_rows ? vw + wrow(a, kr.r_lo) * wvrs : vc;
+  auto tile_ptrs = [&](int t) {
+    const int64_t pos = s0 + (int64_t)t * KT + (lane & (KT - 1));
+    bool ok = false;
+    const uint8_t* kp = kdef;
+    const uint8_t* vp = vdef;
+    if (pos < s1) {
+      if (pos < kr.n_c) {
+        const int64_t j = a.csa ? (int64_t)list[pos - s0] : pos;
+        if (j >= 0 && j < a.N) {
+          ok = true;
+          kp = kc + j * krs;
+          vp = vc + j * vrs;
+        }
+      } else {
+        const int64_t r = wrow(a, kr.r_lo + (pos - kr.n_c));
+        ok = true;
+        kp = kw + r * wrs;
+        vp = vw + r * wvrs;
+      }
+    }
+    my_kp = kp;
+    my_vp = vp;
+    vmask = (uint32_t)__ballot(ok);         // keys 0..31 (lanes 32..63 repeat them)
+  };
+
+  f32x4 acc[NDT];
+#pragma unroll
+  for (int i = 0; i < NDT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sl2 = a.scale * kLog2e;
+  const float ksc = a.k_scale;
+  uint4 qop[KSW];                          // Q^T operands: head `head`, dims 32(dh*KSW + c) + 8g .. +7
+
+  auto cvt8 = [](uint32_t lo, uint32_t hi) -> bf16x8 {   // 8 E4M3 codes -> 8 bf16 (exact)
+    const uint32_t w[4] = {
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, true)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, true))};
+    return bit_cast_to<bf16x8>(make_uint4(w[0], w[1], w[2], w[3]));
+  };
+  // ---- partial S^T (16 keys x 16 heads) of one 16-key half over this wave's k-steps.
+  // kLast: slice DS-1, whose last KSR k-steps are the bf16 dims.
+  auto compute_s = [&](const uint8_t* kt_l, int half, auto last_tag) -> f32x4 {
+    constexpr bool kLast = decltype(last_tag)::value;
+    constexpr int NC = kLast ? KSW - KSR : KSW;      // code k-steps of this slice
+    const uint8_t* kb = kt_l + (half * 16 + col) * K8S + 8 * g + dh * KSW * 32;
+    uint2 kx[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) kx[c] = *reinterpret_cast<const uint2*>(kb + c * 32);
+    uint4 kr4[KSR];
+    if constexpr (kLast) {
+      const uint8_t* rb = kt_l + (half * 16 + col) * K8S + DN + 16 * g;
+#pragma unroll
+      for (int c = 0; c < KSR; ++c) kr4[c] = *reinterpret_cast<const uint4*>(rb + c * 64);
+    }
+    f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = sa, sr = sa;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const bf16x8 ka = cvt8(kx[c].x, kx[c].y);
+      if (c & 1) sb = mfma_bf16(ka, bit_cast_to<bf16x8>(qop[c]), sb);
+      else sa = mfma_bf16(ka, bit_cast_to<bf16x8>(qop[c]), sa);
+    }
+    if constexpr (kLast) {
+#pragma unroll
+      for (int c = 0; c < KSR; ++c) sr = mfma_bf16(bit_cast_to<bf16x8>(kr4[c]), bit_cast_to<bf16x8>(qop[NC + c]), sr);
+      return (sa + sb) * ksc + sr;
+    }
+    return (sa + sb) * ksc;
+  };
+  // V^T operand rows of this lane: its 16-lane block reads keys 4g .. 4g+3 and
+  // 16+4g .. 16+4g+3 (lane pair (2i, 2i+1) one key row, 8 bytes each)
+  const int vi = col >> 1;
+  const int vrow = vi < 4 ? 4 * g + vi : 16 + 4 * g + (vi - 4);
+  const int v_off = KTB + vrow * V8S + (vrow >= 16 ? VH : 0) + dh * DH + 8 * (col & 1);
+  // ---- softmax over the 32 keys (lane: keys 4g+i and 16+4g+i of head `head`), lazy
+  // rescaling, then O^T += V^T . P^T over the 32 keys
+  auto compute_pv = [&](const uint8_t* st_l, uint32_t mask, f32x4 s0v, f32x4 s1v) {
+    float s[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s[i] = ((mask >> (4 * g + i)) & 1u) ? s0v[i] * sl2 : -INFINITY;
+      s[4 + i] = ((mask >> (16 + 4 * g + i)) & 1u) ? s1v[i] * sl2 : -INFINITY;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mx = fmaxf(mx, s[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    if (m_new > m_run + kLazyRescale) {
+      if (m_run != -INFINITY) {
+        const float alpha = exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < NDT; ++i) acc[i] *= alpha;
+      }
+      m_run = m_new;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    float pv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pv[i] = exp2f(s[i] - m_use);
+      l_run += pv[i];
+    }
+    const bf16x8 pb = bit_cast_to<bf16x8>(make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                                                     pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])));
+    constexpr int DB = 4;
+    constexpr int ND = NDT / DB;
+    v2i32 vt[2][DB];
+    auto vread = [&](int buf, int d0) {
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+        vt[buf][d] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) v2i32*)(st_l + v_off + (d0 + d) * 16));
+    };
+    vread(0, 0);
+#pragma unroll
+    for (int bi = 0; bi < ND; ++bi) {
+      if (bi + 1 < ND) vread((bi + 1) & 1, (bi + 1) * DB);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int d = 0; d < DB; ++d) {
+        const v2i32 x = vt[bi & 1][d];
+        acc[bi * DB + d] = mfma_bf16(cvt8((uint32_t)x.x, (uint32_t)x.y), pb, acc[bi * DB + d]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Tile t lives in stage t % 4; tiles 0 and 1 are issued first, the Q^T operands are read
+  // from stages 2-3, then tile 2 is issued; step t waits for tile t, passes a barrier,
+  // issues tile t+3 into the stage of tile t-1 and uses tile t.
+  uint32_t mq0 = 0, mq1 = 0, mq2 = 0;
+  if (spec) {
+    bool same = true;
+    const uint8_t* sk[2];
+    const uint8_t* sv[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      spec_ptrs(t);
+      sk[t] = my_kp;
+      sv[t] = my_vp;
+    }
+    if (ntile > 0) {
+      tile_ptrs(0);
+      mq0 = vmask;
+      same = same && __ballot(my_kp != sk[0] || my_vp != sv[0]) == 0;
+    }
+    if (ntile > 1) {
+      tile_ptrs(1);
+      mq1 = vmask;
+      same = same && __ballot(my_kp != sk[1] || my_vp != sv[1]) == 0;
+    }
+    if (!same) {
+      wait_vmcnt<0>();
+      if (ntile > 0) { tile_ptrs(0); issue(0); }
+      if (ntile > 1) { tile_ptrs(1); issue(1); }
+    }
+  } else {
+    if (ntile > 0) { tile_ptrs(0); mq0 = vmask; issue(0); }
+    if (ntile > 1) { tile_ptrs(1); mq1 = vmask; issue(1); }
+  }
+  {
+    const uint8_t* ql = ring + 2 * STB + (wave_on ? head : 0) * QSTR + 16 * g + dh * KSW * 64;
+#pragma unroll
+    for (int c = 0; c < KSW; ++c) qop[c] = *reinterpret_cast<const uint4*>(ql + c * 64);
+  }
+  tile_barrier();
+  if (ntile > 2) { tile_ptrs(2); mq2 = vmask; issue(2); }
+  for (int t = 0; t < ntile; ++t) {
+    if (t + 2 < ntile) wait_vmcnt<2 * NL>();
+    else if (t + 1 < ntile) wait_vmcnt<NL>();
+    else wait_vmcnt<0>();
+    tile_barrier();
+    uint32_t mq3 = 0;
+    if (t + 3 < ntile) {
+      tile_ptrs(t + 3);
+      mq3 = vmask;
+      issue((t + 3) & 3);
+    }
+    const uint8_t* st_l = ring + (t & 3) * STB;
+    f32x4 sc0 = f32x4{0.f, 0.f, 0.f, 0.f}, sc1 = sc0;
+    if (wave_on) {
+      if (dh == DS - 1) {
+        sc0 = compute_s(st_l, 0, std::true_type{});
+        sc1 = compute_s(st_l, 1, std::true_type{});
+      } else {
+        sc0 = compute_s(st_l, 0, std::false_type{});
+        sc1 = compute_s(st_l, 1, std::false_type{});
+      }
+    }
+    // partial scores of the two slices of a head group (waves hg and hg + 4), summed in
+    // the same order by both
+    if (wave_on) {
+      xchg[wave * kWave + lane] = sc0;
+      xchg[NT + wave * kWave + lane] = sc1;
+    }
+    tile_barrier();
+    if (wave_on) {
+      sc0 = xchg[hg * kWave + lane] + xchg[(hg + 4) * kWave + lane];
+      sc1 = xchg[NT + hg * kWave + lane] + xchg[NT + (hg + 4) * kWave + lane];
+      compute_pv(st_l, mq0, sc0, sc1);
+    }
+    mq0 = mq1;
+    mq1 = mq2;
+    mq2 = mq3;
+  }
+  wait_vmcnt<0>();
+
+  if (!wave_on) return;
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  const float inv = l_run > 0.f ? a.v_scale / l_run : 0.f;
+  const float lse = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+  const int64_t R = a.B * a.Q * a.H;
+  const int64_t orow = bq * a.H + head;
+  uint16_t* out = (splits == 1 ? reinterpret_cast<uint16_t*>(a.out) + orow * D
+                               : o_part + ((int64_t)split * R + orow) * D) + dh * DH;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    uint2 w;
+    w.x = pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv);
+    w.y = pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv);
+    *reinterpret_cast<uint2*>(out + dt * 16 + 4 * g) = w;
+  }
+  if (g == 0 && dh == 0) {
+    if (splits == 1) {
+      if (a.lse) a.lse[orow] = lse;
+    } else {
+      lse_part[(int64_t)split * R + orow] = lse;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------- fp32 / VALU
@@ -896,6 +1144,7 @@ AttendPlan plan_attend(const AttendArgs& a) {
   int64_t chunk = (n_max + want - 1) / want;
   chunk = ((chunk + kTile - 1) / kTile) * kTile;
   if (a.csa && chunk > kMaxCsaChunk) chunk = kMaxCsaChunk;
+  if (a.f8 && a.csa && chunk > kListF8) chunk = kListF8;
   int64_t splits = (n_max + chunk - 1) / chunk;
   p.splits = (int)splits;
   p.chunk = (int)chunk;
@@ -923,7 +1172,7 @@ hipError_t launch_attend(const AttendArgs& a, const AttendPlan& p, void* ws, hip
   }
   dim3 grid((unsigned)p.splits, (unsigned)rows);
   if (a.f8) {   // D == 512 (checked by the caller)
-    DSV4_LAUNCH_MAIN((attend_fp8kv_kernel<512, 2>), grid, dim3(kThreads * 2), 0, st, a, (int64_t)p.chunk, p.splits,
+    DSV4_LAUNCH_MAIN((attend_fp8kv_kernel<512>), grid, dim3(kThreads * 2), 0, st, a, (int64_t)p.chunk, p.splits,
                      o_part, lse_part);
   } else switch (a.D) {
     case 128: DSV4_LAUNCH_MAIN((attend_bf16_kernel<128, 1>), grid, dim3(kThreads), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part); break;
