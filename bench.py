@@ -69,12 +69,16 @@ KERNEL_BYTES = {
 # the counter's reading for a 256 MiB device copy (see profiles/).  An entry is used only
 # while the kernel source it was measured on is unchanged (sha256 of the file).
 MEASURED_TRAFFIC = {
-    "index_mfma_kernel": {"bytes_per_launch": 151634139,
-                          "source_sha256": "42978ac55e131ad1a4b16b8e7d7b0bd2ac9e9e1bc3045c0d21a5f8fdd9368a38"},
-    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 156013708,
-                                 "source_sha256": "e6876c97d029158c70d3c397b6a31282324e802f6e3819760260e27c9991451f"},
-    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32818319,
-                                 "source_sha256": "e6876c97d029158c70d3c397b6a31282324e802f6e3819760260e27c9991451f"},
+    "index_mfma_kernel": {"bytes_per_launch": 151634956,
+        "source_sha256": "42978ac55e131ad1a4b16b8e7d7b0bd2ac9e9e1bc3045c0d21a5f8fdd9368a38"},
+    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 156016486,
+        "source_sha256": "e0c852e4e76fa0e273d6aa0779f49156814f6c6689f74ed8ba8743a3fd553a92"},
+    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32826687,
+        "source_sha256": "e0c852e4e76fa0e273d6aa0779f49156814f6c6689f74ed8ba8743a3fd553a92"},
+    "attend_fp8kv_kernel (HCA)": {"bytes_per_launch": 92201038,
+        "source_sha256": "e0c852e4e76fa0e273d6aa0779f49156814f6c6689f74ed8ba8743a3fd553a92"},
+    "attend_fp8kv_kernel (CSA)": {"bytes_per_launch": 24557732,
+        "source_sha256": "e0c852e4e76fa0e273d6aa0779f49156814f6c6689f74ed8ba8743a3fd553a92"},
 }
 
 
@@ -357,8 +361,13 @@ def run_fp8_kv(L, torch, wl, steps, warmup, every=10):
     for i, name in timed.items():
         k_ms = sum(ev.elapsed_ms(*p[i]) for p in pairs) / len(pairs)
         gbs = FP8_KERNEL_BYTES[name] / (k_ms / 1e3) / 1e9
+        tr = MEASURED_TRAFFIC.get(name)
+        src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "long_context_attention_25_amd", "csrc",
+                           "attend.hip")
         kernels[name] = {"avg_launch_us": round(k_ms * 1e3, 2), "bytes_per_launch": FP8_KERNEL_BYTES[name],
-                         "achieved_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+                         "achieved_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": tr["bytes_per_launch"] if tr and tr["source_sha256"] == source_sha(src)
+                         else None}
     total, _ = fp8_step_bytes()
     kv_tok = {"csa": (FP8_ROW + DI // 2 + DI // 32) / M_CSA, "hca": FP8_ROW / M_HCA}
     del kvc8
