@@ -411,7 +411,9 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
   // its Q^T operands (head `head`, dims g*D/4 + 8c .. +7 for k-step c) from stages 2-3,
   // and after a barrier tile 2 is issued.  Step t then waits for tile t (tiles t+1, t+2
   // stay in flight), passes a barrier (tile t visible to all waves; every wave is done
-  // with tile t-1), issues tile t+3 into the stage of tile t-1 and uses tile t.
+  // with tile t-1), uses tile t and then issues tile t+3 into the stage of tile t-1 (after
+  // the tile's work, so that a wave held up by a full memory queue while issuing copies
+  // does not hold up the tile's scores and the barrier inside the step).
   uint32_t mq0 = 0, mq1 = 0, mq2 = 0;      // masks of tiles t, t+1, t+2
   if (spec) {
     bool same = true;
@@ -455,11 +457,6 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
     else wait_vmcnt<0>();
     tile_barrier();
     uint32_t mq3 = 0;
-    if (t + 3 < ntile) {
-      tile_ptrs(t + 3);
-      mq3 = vmask;
-      issue((t + 3) & 3);
-    }
     f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
     if (wave_on) sc = compute_s(t & 3);
     if constexpr (DS > 1) {
@@ -476,6 +473,11 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
       }
     }
     if (wave_on) compute_pv(t & 3, mq0, sc);
+    if (t + 3 < ntile) {
+      tile_ptrs(t + 3);
+      mq3 = vmask;
+      issue((t + 3) & 3);
+    }
     mq0 = mq1;
     mq1 = mq2;
     mq2 = mq3;
@@ -781,7 +783,7 @@ __global__ __launch_bounds__(kThreads * 2) void attend_fp8kv_kernel(AttendArgs a
 
   // Tile t lives in stage t % 4; tiles 0 and 1 are issued first, the Q^T operands are read
   // from stages 2-3, then tile 2 is issued; step t waits for tile t, passes a barrier,
-  // issues tile t+3 into the stage of tile t-1 and uses tile t.
+  // uses tile t and then issues tile t+3 into the stage of tile t-1.
   uint32_t mq0 = 0, mq1 = 0, mq2 = 0;
   if (spec) {
     bool same = true;
@@ -825,11 +827,6 @@ __global__ __launch_bounds__(kThreads * 2) void attend_fp8kv_kernel(AttendArgs a
     else wait_vmcnt<0>();
     tile_barrier();
     uint32_t mq3 = 0;
-    if (t + 3 < ntile) {
-      tile_ptrs(t + 3);
-      mq3 = vmask;
-      issue((t + 3) & 3);
-    }
     const uint8_t* st_l = ring + (t & 3) * STB;
     f32x4 sc0 = f32x4{0.f, 0.f, 0.f, 0.f}, sc1 = sc0;
     if (wave_on) {
@@ -852,6 +849,11 @@ __global__ __launch_bounds__(kThreads * 2) void attend_fp8kv_kernel(AttendArgs a
       sc0 = xchg[hg * kWave + lane] + xchg[(hg + 4) * kWave + lane];
       sc1 = xchg[NT + hg * kWave + lane] + xchg[NT + (hg + 4) * kWave + lane];
       compute_pv(st_l, mq0, sc0, sc1);
+    }
+    if (t + 3 < ntile) {
+      tile_ptrs(t + 3);
+      mq3 = vmask;
+      issue((t + 3) & 3);
     }
     mq0 = mq1;
     mq1 = mq2;
