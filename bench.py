@@ -496,35 +496,46 @@ PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
 
 def time_index_kernel(L, torch, call, n):
     """Average duration (ms) of the indexer kernel of csa_index_topk over n calls, from HIP
-    events attached to that kernel's launch; call(lib) issues one csa_index_topk."""
+    events attached to that kernel's launch; call(lib, i) issues the i-th csa_index_topk."""
     lib = L.lib()
     ev = HipEvents()
-    call(lib)
+    for i in range(3):
+        call(lib, i)
     torch.cuda.synchronize()
     pairs = [(ev.create(), ev.create()) for _ in range(n)]
-    for p in pairs:
+    for i, p in enumerate(pairs):
         lib.dsv4_time_next_kernel(*p)
-        call(lib)
+        call(lib, i)
     torch.cuda.synchronize()
     return sum(ev.elapsed_ms(*p) for p in pairs) / n
 
 
 def fp4_index_decode(L, torch, wl):
     """The decode workload's indexer (8 x 262,144 MXFP4 keys) with MXFP4 queries on the
-    scaled FP4 MFMA: main-kernel microseconds, next to the bf16-query figure of the step."""
-    t = wl.r[0]
+    scaled FP4 MFMA and, timed the same way, with the step's bf16 queries: main-kernel
+    microseconds of calls on their own, the replicas' keys rotating as in the step (one
+    replica's 143 MB of keys repeated would be served from the 256 MB Infinity Cache)."""
     R = B * HI
-    qbuf = torch.empty(R * DI // 2 + R * DI // 32, dtype=torch.uint8, device="cuda")
-    qc, qs = qbuf[:R * DI // 2].view(1, R, DI // 2), qbuf[R * DI // 2:].view(1, R, DI // 32)
-    L.csa_compress(t["qi"].view(1, R, DI).float(), torch.zeros((1, R), device="cuda"),
-                   torch.zeros(1, device="cuda"), 1, L.MXFP4_DTYPE, out=qc, out_scale=qs)
+    qs = []
+    for t in wl.r:
+        qbuf = torch.empty(R * DI // 2 + R * DI // 32, dtype=torch.uint8, device="cuda")
+        qc, qsc = qbuf[:R * DI // 2].view(1, R, DI // 2), qbuf[R * DI // 2:].view(1, R, DI // 32)
+        L.csa_compress(t["qi"].view(1, R, DI).float(), torch.zeros((1, R), device="cuda"),
+                       torch.zeros(1, device="cuda"), 1, L.MXFP4_DTYPE, out=qc, out_scale=qsc)
+        qs.append((qbuf, qc.view(B, 1, HI, DI // 2), qsc.view(B, 1, HI, DI // 32)))
     idx = torch.empty((B, 1, TOPK), dtype=torch.int32, device="cuda")
-    ws = torch.empty(t["ws_idx"].numel(), dtype=torch.uint8, device="cuda")     # same shapes as the step's call
+    ws = torch.empty(wl.r[0]["ws_idx"].numel(), dtype=torch.uint8, device="cuda")   # same shapes as the step's call
 
-    def call(lib):
-        L.csa_index_topk(qc.view(B, 1, HI, DI // 2), t["wi"], t["ki"], wl.q_pos, M_CSA, TOPK, ki_scale=t["ks"],
-                         qi_scale=qs.view(B, 1, HI, DI // 32), out_idx=idx, workspace=ws)
-    return time_index_kernel(L, torch, call, 20) * 1e3
+    def fp4(lib, i):
+        t, (_, qc, qsc) = wl.r[i % len(wl.r)], qs[i % len(wl.r)]
+        L.csa_index_topk(qc, t["wi"], t["ki"], wl.q_pos, M_CSA, TOPK, ki_scale=t["ks"], qi_scale=qsc, out_idx=idx,
+                         workspace=ws)
+
+    def bf16(lib, i):
+        t = wl.r[i % len(wl.r)]
+        L.csa_index_topk(t["qi"], t["wi"], t["ki"], wl.q_pos, M_CSA, TOPK, ki_scale=t["ks"], out_idx=idx,
+                         workspace=ws)
+    return time_index_kernel(L, torch, fp4, 30) * 1e3, time_index_kernel(L, torch, bf16, 30) * 1e3
 
 
 def prefill_flops():
@@ -633,7 +644,7 @@ def run_prefill(L, torch, synth, steps, warmup):
     L.csa_compress(synth.device_normal((1, R, DI), seed(7, synth.QI, 0), bf), torch.zeros((1, R), device="cuda"),
                    torch.zeros(1, device="cuda"), 1, L.MXFP4_DTYPE, out=qc, out_scale=qs)
 
-    def fp4_call(lib_):
+    def fp4_call(lib_, i=0):
         L.csa_index_topk(qc.view(1, T, HI, DI // 2), t0["wi"], k4, qpos, M_CSA, PF_K, ki_scale=k4s,
                          qi_scale=qs.view(1, T, HI, DI // 32), out_idx=t0["idx"], workspace=ws.get("idx"))
     k_fp4 = time_index_kernel(L, torch, fp4_call, max(2, steps))
@@ -755,10 +766,11 @@ def main():
                      "timed_launches": len(pairs)},
         "kernels": kernels,
     }
-    out["fp4_indexer"] = {"avg_launch_us": round(fp4_index_decode(L, torch, wl), 2),
-                          "bf16_query_avg_launch_us": kernels["index_mfma_kernel"]["avg_launch_us"],
-                          "note": "the same 8 x 262144 MXFP4 keys with MXFP4 queries (scaled FP4 MFMA); "
-                                  "main kernel only, measured after the timed steps"}
+    us_fp4, us_bf16 = fp4_index_decode(L, torch, wl)
+    out["fp4_indexer"] = {"avg_launch_us": round(us_fp4, 2), "bf16_query_avg_launch_us": round(us_bf16, 2),
+                          "note": "the same 8 x 262144 MXFP4 keys with MXFP4 queries (scaled FP4 MFMA) and, timed "
+                                  "alike, with bf16 queries: csa_index_topk calls on their own after the timed steps, "
+                                  "main kernel only, keys of the three replicas rotating"}
     if not args.no_fp8_kv:
         out["fp8_kv"] = run_fp8_kv(L, torch, wl, args.steps, args.warmup, every)
     out["cache_append"] = {"us_per_step": round(time_cache_append(L, torch, wl, 50), 2), "calls_per_step": 3,
