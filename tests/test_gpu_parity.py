@@ -128,7 +128,7 @@ def test_cache_append_decode_matches_prefix_compression(m, C, ydt):
         cscale = torch.zeros((B, N, C // 32), dtype=torch.uint8, device="cuda")
     elif ydt == "fp8kv":
         cache = torch.zeros((B, N, C + DR), dtype=torch.uint8, device="cuda")
-        cscale = None
+        cscale = dev(np.array([127 - 1, 127 + 2], dtype=np.uint8))   # K codes of y * 2, V codes of y / 4
     else:
         cache = torch.zeros((B, N, C), dtype=torch.float32 if ydt == "f32" else torch.bfloat16, device="cuda")
         cscale = None
@@ -142,6 +142,8 @@ def test_cache_append_decode_matches_prefix_compression(m, C, ydt):
             kw = dict(out=cache[b:b + 1, :nb0])
             if ydt == "mxfp4":
                 kw["out_scale"] = cscale[b:b + 1, :nb0]
+            elif ydt == "fp8kv":
+                kw["out_scale"] = cscale
             L.csa_compress(xd[b:b + 1, :nb0 * m], gd[b:b + 1, :nb0 * m].contiguous(), bd, m,
                            {"mxfp4": L.MXFP4_DTYPE, "fp8kv": L.FP8_KV_DTYPE}.get(ydt, cache.dtype), **kw)
         for q in range(max(0, int(T0[b]) - Lw), int(T0[b])):
@@ -171,7 +173,8 @@ def test_cache_append_decode_matches_prefix_compression(m, C, ydt):
             assert np.all(np.abs(got - y_ref) <= 2 * step + 1e-6 * np.abs(y_ref))   # e2m1 rounding / saturation
         elif ydt == "fp8kv":
             x_b = x64[b:b + 1, :nb * m]
-            _check_fp8kv_rows(cache[b, :nb].cpu().numpy(), y_ref, compress_tol(x_b, m, y_ref[None])[0] - bf16_ulp(y_ref))
+            _check_fp8kv_rows(cache[b, :nb].cpu().numpy(), y_ref, compress_tol(x_b, m, y_ref[None])[0] - bf16_ulp(y_ref),
+                              ek=-1, ev=2)
         else:
             got = host(cache[b, :nb])
             if ydt == "f32":
@@ -792,6 +795,28 @@ def test_attend_fp8kv_side_by_side_and_every_code():
                                       pos, scale)
     assert row_rel_err(host(h1), h_ref) <= 1e-2
     assert lse_abs_err(host(hl1), hl_ref) <= 1e-2
+
+
+def test_csa_attend_fp8kv_many_queries():
+    """Enough queries for one workgroup per query: each query's list of 1024 entries plus
+    its window is cut into splits of at most 512 list slots (the FP8 kernel's index list)."""
+    cfg = 790
+    B, Q, H, D, N, L_, W, k = 1, 260, 16, 512, 5000, 400, 128, 1024
+    ks, vs = 0.5, 1.75
+    (kcb, vcb, kwb, vwb), (kcd, vcd, kwd, vwd) = _fp8_kv(cfg, B, N, L_, D, ks, vs)
+    q = synth.normal(cfg, synth.Q, (B, Q, H, D))
+    idx = synth.sorted_unique_indices(cfg, synth.IDX, B * Q, N, k).reshape(B, Q, k)
+    idx[0, 5, 900:] = -1
+    win_pos0 = np.array([80000], dtype=np.int32)
+    pos = (80000 + 130 + np.arange(Q, dtype=np.int32))[None, :]
+    qd, qb = dev_bf16(q)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = L.csa_attend_fp8kv(qd, dev(kcb), dev(vcb), dev(idx), dev(kwb), dev(vwb), dev(win_pos0), W, dev(pos),
+                                scale, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = method.csa_attend(codecs.decode_bf16(qb), kcd, vcd, idx, kwd, vwd, win_pos0, W, pos, scale)
+    assert row_rel_err(host(o), o_ref) <= 1e-2
+    assert lse_abs_err(host(lse), lse_ref) <= 1e-2
 
 
 def test_attend_fp8kv_empty_key_sets():
