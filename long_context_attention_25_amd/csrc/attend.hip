@@ -17,7 +17,11 @@
 //   A operand, so each lane ends up holding 8 scores of ONE head; those scores,
 //   exponentiated and rounded to bf16, are directly the B operand of
 //   O^T += V^T.P^T with no data movement.  Online softmax in fp32 (exp2 with the
-//   scale folded in).  Splits write fp32 partial (o, lse) that lse_merge combines.
+//   scale folded in; the hardware exp2, whose arguments here are <= 0 or -inf).
+//   Splits write bf16 partial outputs and fp32 lse that a merge kernel combines.
+// bf16 query pairs (dense attention over many queries, e.g. a prefill chunk): two
+//   queries per workgroup share every K/V tile and every operand read.
+// FP8 K/V rows: the same scheme over E4M3 rows decoded in registers.
 // fp32 path: a plain VALU kernel, one workgroup per (query, head).
 #include <type_traits>
 
@@ -378,7 +382,7 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
     float pv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      pv[i] = exp2f(s[i] - m_use);
+      pv[i] = __builtin_amdgcn_exp2f(s[i] - m_use);
       l_run += pv[i];
     }
     // P^T operand of the 16x16x16 MFMA: this lane's own keys 4g .. 4g+3 of head `head`
@@ -753,7 +757,7 @@ __global__ __launch_bounds__(kThreads * 2) void attend_fp8kv_kernel(AttendArgs a
     float pv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      pv[i] = exp2f(s[i] - m_use);
+      pv[i] = __builtin_amdgcn_exp2f(s[i] - m_use);
       l_run += pv[i];
     }
     const bf16x8 pb = bit_cast_to<bf16x8>(make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
@@ -884,6 +888,314 @@ __global__ __launch_bounds__(kThreads * 2) void attend_fp8kv_kernel(AttendArgs a
       lse_part[(int64_t)split * R + orow] = lse;
     }
   }
+}
+
+// ---------------------------------------------------------------------------- query pairs
+// Dense (HCA) attention for many queries: a workgroup takes two queries of one sequence,
+// whose key sets are the same but for at most one compressed entry and the window's
+// ends when their positions are close (consecutive tokens of a prefill chunk), and walks
+// the union of the two key lists once.  The work split is the one-query kernel's (8 waves:
+// head group w%4 owns heads 16(w%4) .. +15, slice w/4 half of the head dim, partial
+// scores summed through LDS), but every wave does it for BOTH queries: each K operand
+// read from LDS feeds the score MFMAs of both queries and each transposed V read feeds
+// both output MFMAs, which halves the LDS bytes per flop that bound the one-query kernel
+// at this shape.  Per-query masks keep each query to its own keys.
+template <int D>
+__global__ __launch_bounds__(kThreads * 2) void attend_bf16_pair_kernel(AttendArgs a, int64_t chunk, int splits,
+                                                                        uint16_t* __restrict__ o_part,
+                                                                        float* __restrict__ lse_part) {
+  constexpr int DS = 2;
+  constexpr int KT = 16;
+  constexpr int NT = kThreads * DS;
+  constexpr int NWV = NT / kWave;          // 8
+  constexpr int KS = D / 32;
+  constexpr int KSW = KS / DS;             // k-steps of a slice
+  constexpr int DH = D / DS;               // output dims of a slice
+  constexpr int NDT = DH / 16;
+  constexpr int RB = D * 2;
+  constexpr int KSTR = RB + 16;
+  constexpr int VSTR = RB + 32;
+  constexpr int LPR = RB / 16;
+  constexpr int RPW = KT / NWV;
+  constexpr int NL = 2 * RPW;
+  constexpr int KTB = KT * KSTR, VTB = KT * VSTR;
+  constexpr int STB = KTB + VTB;
+  static_assert(LPR <= kWave && kWave % LPR == 0, "a row is copied by one instruction");
+  static_assert(3 * NL < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[4 * STB];
+  __shared__ __attribute__((aligned(16))) f32x4 xchg[2 * NT];   // partial scores of both queries
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, col = lane & 15;
+  const int64_t QP = (a.Q + 1) / 2;
+  const int64_t b = blockIdx.y / QP;
+  const int64_t q0 = (blockIdx.y % QP) * 2;
+  const bool has1 = q0 + 1 < a.Q;
+  const int64_t bq0 = b * a.Q + q0, bq1 = has1 ? bq0 + 1 : bq0;
+  const int split = blockIdx.x;
+  const int64_t s0 = (int64_t)split * chunk;
+  const int hg = wave % 4, dh = wave / 4;
+  const int head = hg * 16 + col;
+  const bool wave_on = hg * 16 < a.H;
+
+  // Q^T operands of both queries straight into registers (dims g*D/4 + 8c .. +7 for the
+  // slice's k-steps c), waited for before any copy into LDS is issued
+  uint4 qop0[KSW], qop1[KSW];
+  {
+    const int hh = wave_on ? head : 0;
+    const uint4* p0 = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) + (bq0 * a.H + hh) * D +
+                                                     g * (D / 4) + dh * KSW * 8);
+    const uint4* p1 = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) + (bq1 * a.H + hh) * D +
+                                                     g * (D / 4) + dh * KSW * 8);
+#pragma unroll
+    for (int c = 0; c < KSW; ++c) {
+      qop0[c] = p0[c];
+      qop1[c] = p1[c];
+    }
+  }
+  const int32_t p0 = load_uniform(a.q_pos + bq0);
+  const int32_t p1 = load_uniform(a.q_pos + bq1);
+  const int32_t wpos0 = a.win_pos0 ? load_uniform(a.win_pos0 + b) : 0;
+  wait_vmcnt<0>();
+  // the union of the two key lists: compressed entries 0 .. n_c-1, then query 0's window
+  // rows [lo0, hi0), then query 1's window rows outside that range, [lo1, min(hi1, lo0))
+  // and [max(lo1, hi0), hi1) (window coordinates: buffer rows, or positions in ring
+  // mode).  For neighbouring positions the second part is one row; it never exceeds W.
+  const KeyRange k0 = key_range(a, p0, wpos0);
+  const KeyRange k1 = has1 ? key_range(a, p1, wpos0) : k0;
+  const int64_t lo0 = k0.r_lo, hi0 = k0.r_lo + (k0.n_tot - k0.n_c);
+  const int64_t lo1 = k1.r_lo, hi1 = k1.r_lo + (k1.n_tot - k1.n_c);
+  const int64_t e1a = hi1 < lo0 ? hi1 : lo0;               // end of [lo1, min(hi1, lo0))
+  const int64_t nb1 = e1a > lo1 ? e1a - lo1 : 0;
+  const int64_t s2 = lo1 > hi0 ? lo1 : hi0;                 // start of [max(lo1, hi0), hi1)
+  const int64_t nb2 = hi1 > s2 ? hi1 - s2 : 0;
+  const int64_t w0n = hi0 - lo0;
+  const int64_t n_c = k0.n_c > k1.n_c ? k0.n_c : k1.n_c;
+  const int64_t n_w = w0n + nb1 + nb2;
+  const int64_t n_tot = n_c + n_w;
+  auto wr_at = [&](int64_t pp) -> int64_t {                 // window coordinate of window entry pp
+    return pp < w0n ? lo0 + pp : (pp < w0n + nb1 ? lo1 + (pp - w0n) : s2 + (pp - w0n - nb1));
+  };
+  int64_t s1 = s0 + chunk;
+  if (s1 > n_tot) s1 = n_tot;
+  const int ntile = s1 > s0 ? (int)((s1 - s0 + KT - 1) / KT) : 0;
+
+  const int64_t krs = a.kv_rs, wrs = a.w_rs;
+  const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.kc) + b * a.kv_bs * krs;
+  const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.vc) + b * a.kv_bs * krs;
+  const uint16_t* kw = reinterpret_cast<const uint16_t*>(a.kw) + b * a.L * wrs;
+  const uint16_t* vw = reinterpret_cast<const uint16_t*>(a.vw) + b * a.L * wrs;
+  // slots past the list point at a row that holds data
+  const uint16_t* kdef = n_w > 0 ? kw + wrow(a, wr_at(0)) * wrs : kc;
+  const uint16_t* vdef = n_w > 0 ? vw + wrow(a, wr_at(0)) * wrs : vc;
+  const uint16_t* my_kp;
+  const uint16_t* my_vp;
+  uint32_t vm0 = 0, vm1 = 0;
+  auto tile_ptrs = [&](int t) {
+    const int64_t pos = s0 + (int64_t)t * KT + (lane & (KT - 1));
+    bool ok0 = false, ok1 = false;
+    const uint16_t* kp = kdef;
+    const uint16_t* vp = vdef;
+    if (pos < s1) {
+      if (pos < n_c) {
+        if (pos < a.N) {
+          ok0 = pos < k0.n_c;
+          ok1 = has1 && pos < k1.n_c;
+          kp = kc + pos * krs;
+          vp = vc + pos * krs;
+        }
+      } else {
+        const int64_t r = wr_at(pos - n_c);
+        ok0 = r >= lo0 && r < hi0;
+        ok1 = has1 && r >= lo1 && r < hi1;
+        const int64_t rr = wrow(a, r);
+        kp = kw + rr * wrs;
+        vp = vw + rr * wrs;
+      }
+    }
+    my_kp = kp;
+    my_vp = vp;
+    vm0 = (uint32_t)__ballot(ok0) & 0xffffu;
+    vm1 = (uint32_t)__ballot(ok1) & 0xffffu;
+  };
+  const uint32_t ring_lds = lds_addr(ring);
+  auto issue = [&](int stage) {
+    const uint32_t kdst = ring_lds + stage * STB;
+    const uint32_t vdst = kdst + KTB;
+    const int j = lane / LPR;
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int r = wave + i * NWV;
+      const int off = (lane % LPR) * 8;
+      if (j == 0) {
+        copy16_to_lds(lane_ptr<true>(my_kp, r) + off, kdst + r * KSTR);
+        copy16_to_lds(lane_ptr<true>(my_vp, r) + off, vdst + r * VSTR);
+      }
+    }
+  };
+
+  f32x4 acc0[NDT], acc1[NDT];
+#pragma unroll
+  for (int i = 0; i < NDT; ++i) acc0[i] = acc1[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m0 = -INFINITY, l0 = 0.f, m1 = -INFINITY, l1 = 0.f;
+  const float sl2 = a.scale * kLog2e;
+  const int k_off = col * KSTR + g * (D / 4) * 2 + dh * KSW * 16;
+  const int v_off = (4 * g + (col >> 2)) * VSTR + dh * DH * 2 + (col & 3) * 8;
+
+  // S^T of both queries (16 keys x 16 heads each) from one pass over the K operands
+  auto compute_s = [&](int stage, f32x4& s0v, f32x4& s1v) {
+    const uint8_t* kt_l = ring + stage * STB;
+    constexpr int CB = 2;
+    constexpr int NB = KSW / CB;
+    f32x4 a0 = f32x4{0.f, 0.f, 0.f, 0.f}, b0 = a0, a1 = a0, b1 = a0;
+    uint4 kv[2][CB];
+    auto kread = [&](int buf, int c0) {
+#pragma unroll
+      for (int c = 0; c < CB; ++c) kv[buf][c] = *reinterpret_cast<const uint4*>(kt_l + k_off + (c0 + c) * 16);
+    };
+    kread(0, 0);
+#pragma unroll
+    for (int bi = 0; bi < NB; ++bi) {
+      if (bi + 1 < NB) kread((bi + 1) & 1, (bi + 1) * CB);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int c = 0; c < CB; ++c) {
+        const bf16x8 ka = bit_cast_to<bf16x8>(kv[bi & 1][c]);
+        const int ks = bi * CB + c;
+        if (ks & 1) {
+          b0 = mfma_bf16(ka, bit_cast_to<bf16x8>(qop0[ks]), b0);
+          b1 = mfma_bf16(ka, bit_cast_to<bf16x8>(qop1[ks]), b1);
+        } else {
+          a0 = mfma_bf16(ka, bit_cast_to<bf16x8>(qop0[ks]), a0);
+          a1 = mfma_bf16(ka, bit_cast_to<bf16x8>(qop1[ks]), a1);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    s0v = a0 + b0;
+    s1v = a1 + b1;
+  };
+  // softmax step of one query: returns its P^T operand
+  auto softmax = [&](uint32_t mask, f32x4 s, float& m_run, float& l_run, f32x4* acc) -> v4i16 {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = (mask >> (4 * g + i)) & 1u;
+      s[i] = ok ? s[i] * sl2 : -INFINITY;
+      mx = fmaxf(mx, s[i]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    if (m_new > m_run + kLazyRescale) {
+      if (m_run != -INFINITY) {
+        const float alpha = exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < NDT; ++i) acc[i] *= alpha;
+      }
+      m_run = m_new;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    float pv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pv[i] = __builtin_amdgcn_exp2f(s[i] - m_use);
+      l_run += pv[i];
+    }
+    return __builtin_bit_cast(v4i16, make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])));
+  };
+  // O^T += V^T . P^T for both queries from one pass over the transposed V reads
+  auto compute_pv = [&](int stage, v4i16 pb0, v4i16 pb1) {
+    const uint8_t* vt_l = ring + stage * STB + KTB;
+    constexpr int DB = 2;
+    constexpr int ND = NDT / DB;
+    v4i16 vt[2][DB];
+    auto vread = [&](int buf, int d0) {
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+        vt[buf][d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16*)(vt_l + v_off + (d0 + d) * 32));
+    };
+    vread(0, 0);
+#pragma unroll
+    for (int bi = 0; bi < ND; ++bi) {
+      if (bi + 1 < ND) vread((bi + 1) & 1, (bi + 1) * DB);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int d = 0; d < DB; ++d) {
+        acc0[bi * DB + d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[bi & 1][d], pb0, acc0[bi * DB + d], 0, 0, 0);
+        acc1[bi * DB + d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[bi & 1][d], pb1, acc1[bi * DB + d], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Tile t lives in stage t % 4; tiles 0 .. 2 are issued first; step t waits for tile t,
+  // passes a barrier, uses it and then issues tile t+3 into the stage of tile t-1.
+  uint32_t ma0 = 0, ma1 = 0, ma2 = 0, mb0 = 0, mb1 = 0, mb2 = 0;
+  if (ntile > 0) { tile_ptrs(0); ma0 = vm0; mb0 = vm1; issue(0); }
+  if (ntile > 1) { tile_ptrs(1); ma1 = vm0; mb1 = vm1; issue(1); }
+  if (ntile > 2) { tile_ptrs(2); ma2 = vm0; mb2 = vm1; issue(2); }
+  for (int t = 0; t < ntile; ++t) {
+    if (t + 2 < ntile) wait_vmcnt<2 * NL>();
+    else if (t + 1 < ntile) wait_vmcnt<NL>();
+    else wait_vmcnt<0>();
+    tile_barrier();
+    f32x4 s0v = f32x4{0.f, 0.f, 0.f, 0.f}, s1v = s0v;
+    if (wave_on) {
+      compute_s(t & 3, s0v, s1v);
+      xchg[wave * kWave + lane] = s0v;
+      xchg[NT + wave * kWave + lane] = s1v;
+    }
+    tile_barrier();
+    if (wave_on) {
+      // the two slices' partial scores, summed in the same order by both
+      s0v = xchg[hg * kWave + lane] + xchg[(hg + 4) * kWave + lane];
+      s1v = xchg[NT + hg * kWave + lane] + xchg[NT + (hg + 4) * kWave + lane];
+      const v4i16 pb0 = softmax(ma0, s0v, m0, l0, acc0);
+      const v4i16 pb1 = softmax(mb0, s1v, m1, l1, acc1);
+      compute_pv(t & 3, pb0, pb1);
+    }
+    uint32_t ma3 = 0, mb3 = 0;
+    if (t + 3 < ntile) {
+      tile_ptrs(t + 3);
+      ma3 = vm0;
+      mb3 = vm1;
+      issue((t + 3) & 3);
+    }
+    ma0 = ma1; ma1 = ma2; ma2 = ma3;
+    mb0 = mb1; mb1 = mb2; mb2 = mb3;
+  }
+  wait_vmcnt<0>();
+
+  if (!wave_on) return;
+  const int64_t R = a.B * a.Q * a.H;
+  auto finish = [&](int64_t bq, float m_run, float l_run, const f32x4* acc) {
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    const float lse = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+    const int64_t orow = bq * a.H + head;
+    uint16_t* out = (splits == 1 ? reinterpret_cast<uint16_t*>(a.out) + orow * D
+                                 : o_part + ((int64_t)split * R + orow) * D) + dh * DH;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      uint2 w;
+      w.x = pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv);
+      w.y = pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv);
+      *reinterpret_cast<uint2*>(out + dt * 16 + 4 * g) = w;
+    }
+    if (g == 0 && dh == 0) {
+      if (splits == 1) {
+        if (a.lse) a.lse[orow] = lse;
+      } else {
+        lse_part[(int64_t)split * R + orow] = lse;
+      }
+    }
+  };
+  finish(bq0, m0, l0, acc0);
+  if (has1) finish(bq0 + 1, m1, l1, acc1);
 }
 
 // ---------------------------------------------------------------------------- fp32 / VALU
@@ -1128,17 +1440,24 @@ __global__ __launch_bounds__(kThreads) void merge_bf16_parts_kernel(const uint16
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Dense attention over many queries of a sequence (a prefill chunk) runs two queries per
+// workgroup; decode-sized calls keep one query per workgroup.
+constexpr int64_t kPairMinQ = 16;
+inline bool use_pairs(const AttendArgs& a) { return !a.f32 && !a.f8 && !a.csa && a.D == 512 && a.Q >= kPairMinQ; }
+
 }  // namespace
 
 AttendPlan plan_attend(const AttendArgs& a) {
   AttendPlan p{1, 0, 0};
+  const bool pairs = use_pairs(a);
   const int64_t win = a.W < a.L ? a.W : a.L;
-  const int64_t n_max = (a.csa ? (int64_t)a.k : a.N) + (win > 0 ? win : 0);
+  // key list length bound: with pairs, two windows (the union never exceeds both)
+  const int64_t n_max = (a.csa ? (int64_t)a.k : a.N) + (win > 0 ? (pairs ? 2 * win : win) : 0);
   if (a.f32 || n_max == 0) {
     p.chunk = (int)(n_max > 0 ? n_max : 1);
     return p;
   }
-  const int64_t rows = a.B * a.Q;
+  const int64_t rows = a.B * (pairs ? (a.Q + 1) / 2 : a.Q);
   int64_t want = (kTargetWorkgroups + rows - 1) / rows;   // about one workgroup per CU
   int64_t max_splits = (n_max + kTile - 1) / kTile;
   if (want > max_splits) want = max_splits;
@@ -1171,6 +1490,16 @@ hipError_t launch_attend(const AttendArgs& a, const AttendPlan& p, void* ws, hip
   if (p.splits > 1) {
     o_part = reinterpret_cast<uint16_t*>(ws);
     lse_part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + align256((size_t)p.splits * R * a.D * 2));
+  }
+  if (use_pairs(a)) {
+    dim3 pgrid((unsigned)p.splits, (unsigned)(a.B * ((a.Q + 1) / 2)));
+    DSV4_LAUNCH_MAIN((attend_bf16_pair_kernel<512>), pgrid, dim3(kThreads * 2), 0, st, a, (int64_t)p.chunk,
+                     p.splits, o_part, lse_part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.splits == 1) return e;
+    hipLaunchKernelGGL(merge_bf16_parts_kernel, dim3((unsigned)R), dim3(kThreads), 0, st, o_part, lse_part, p.splits,
+                       R, a.D, reinterpret_cast<uint16_t*>(a.out), a.lse);
+    return hipGetLastError();
   }
   dim3 grid((unsigned)p.splits, (unsigned)rows);
   if (a.f8) {   // D == 512 (checked by the caller)

@@ -602,6 +602,43 @@ def test_hca_attend_bf16(H, D, N):
     assert lse_abs_err(host(lse), lse_ref) <= 1e-2
 
 
+@pytest.mark.parametrize("H,ring", [(64, False), (32, False), (64, True)])
+def test_hca_attend_bf16_many_queries(H, ring):
+    """Many queries per sequence (two per workgroup, their key lists merged): a run of
+    consecutive positions, and positions far apart (disjoint windows, a query that sees no
+    compressed entry, one whose window lies before the buffer); an odd query count."""
+    cfg = 480 + H + ring
+    B, Q, D, N, m, W = 2, 37, 512, 300, 128, 128
+    Lw = 256 if ring else 600
+    q, kc, vc, kwl, vwl = _attn_inputs(cfg, B, Q, H, D, N, Lw)
+    T = N * m
+    pos = np.zeros((B, Q), dtype=np.int32)
+    pos[0] = T - Q + np.arange(Q)                                   # consecutive, the chunk's tail
+    r = np.random.default_rng(cfg)
+    pos[1] = np.sort(r.integers(T - 560, T, size=Q))               # scattered inside the window buffer
+    pos[1, :3] = [5, 100, T - 900]                                  # no visible entry / window elsewhere
+    if ring:
+        pos[1] = T - 1 - np.sort(r.integers(0, 100, size=Q))[::-1]   # every window inside the ring's last L
+    wp0 = np.full(B, T - Lw, dtype=np.int32)
+    if ring:
+        kwr, vwr = np.empty_like(kwl), np.empty_like(vwl)
+        for b in range(B):
+            rr = (wp0[b] + np.arange(Lw)) % Lw
+            kwr[b, rr], vwr[b, rr] = kwl[b], vwl[b]
+    else:
+        kwr, vwr = kwl, vwl
+    t = [dev_bf16(x) for x in (q, kc, vc, kwr, vwr)]
+    (qd, qb), (kcd, kcb), (vcd, vcb), (kwd, _), (vwd, _) = t
+    kwlb, vwlb = synth.bf16_bits(kwl), synth.bf16_bits(vwl)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = L.hca_attend(qd, kcd, vcd, m, kwd, vwd, None if ring else dev(wp0), W, dev(pos), scale)
+    torch.cuda.synchronize()
+    dec = codecs.decode_bf16
+    o_ref, lse_ref = method.hca_attend(dec(qb), dec(kcb), dec(vcb), m, dec(kwlb), dec(vwlb), wp0, W, pos, scale)
+    assert row_rel_err(host(o), o_ref) <= 1e-2
+    assert lse_abs_err(host(lse), lse_ref) <= 1e-2
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_attend_with_kv_side_by_side(dt):
     """K and V rows in one [.., 2D] buffer (caches and window), pooled by one csa_compress
