@@ -69,16 +69,16 @@ KERNEL_BYTES = {
 # the counter's reading for a 256 MiB device copy (see profiles/).  An entry is used only
 # while the kernel source it was measured on is unchanged (sha256 of the file).
 MEASURED_TRAFFIC = {
-    "index_mfma_kernel": {"bytes_per_launch": 151634956,
+    "index_mfma_kernel": {"bytes_per_launch": 151634044,
         "source_sha256": "42978ac55e131ad1a4b16b8e7d7b0bd2ac9e9e1bc3045c0d21a5f8fdd9368a38"},
-    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 156016486,
-        "source_sha256": "e0c852e4e76fa0e273d6aa0779f49156814f6c6689f74ed8ba8743a3fd553a92"},
-    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32826687,
-        "source_sha256": "e0c852e4e76fa0e273d6aa0779f49156814f6c6689f74ed8ba8743a3fd553a92"},
-    "attend_fp8kv_kernel (HCA)": {"bytes_per_launch": 92201038,
-        "source_sha256": "e0c852e4e76fa0e273d6aa0779f49156814f6c6689f74ed8ba8743a3fd553a92"},
-    "attend_fp8kv_kernel (CSA)": {"bytes_per_launch": 24557732,
-        "source_sha256": "e0c852e4e76fa0e273d6aa0779f49156814f6c6689f74ed8ba8743a3fd553a92"},
+    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 156020727,
+        "source_sha256": "b4ccb839c3b08f5e16e10a18984ede0506b45df4e0a24cb88f4f8a6a79bd6792"},
+    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32829632,
+        "source_sha256": "b4ccb839c3b08f5e16e10a18984ede0506b45df4e0a24cb88f4f8a6a79bd6792"},
+    "attend_fp8kv_kernel (HCA)": {"bytes_per_launch": 92170581,
+        "source_sha256": "b4ccb839c3b08f5e16e10a18984ede0506b45df4e0a24cb88f4f8a6a79bd6792"},
+    "attend_fp8kv_kernel (CSA)": {"bytes_per_launch": 24546785,
+        "source_sha256": "b4ccb839c3b08f5e16e10a18984ede0506b45df4e0a24cb88f4f8a6a79bd6792"},
 }
 
 
