@@ -149,12 +149,12 @@ def marshal_step(L, torch, wl, rep):
     calls = []
     g4 = t["gate"][:, LWIN - M_CSA:].contiguous()
     t["g4"] = g4
-    # CSA: the newest 4-token block -> entry N_CSA-1 of K|V (bf16, one call over the 2D
-    # channels) and of the indexer key (MXFP4)
-    calls.append((lib.csa_compress, (P(t["kvw"][:, LWIN - M_CSA:]), L.BF16, P(g4), P(t["bias"]), B, M_CSA, 2 * D,
-                                     M_CSA, LWIN, P(wl.kvc[:, N_CSA - 1:]), None, L.BF16, N_CSA, st)))
-    calls.append((lib.csa_compress, (P(t["kiw"][:, LWIN - M_CSA:]), L.BF16, P(g4), P(t["bias"]), B, M_CSA, DI, M_CSA,
-                                     LWIN, P(t["ki"][:, N_CSA - 1:]), P(t["ks"][:, N_CSA - 1:]), L.MXFP4, N_CSA, st)))
+    # CSA: the newest 4-token block -> entry N_CSA-1 of K|V (bf16, the 2D channels side by
+    # side) and of the indexer key (MXFP4), one launch for both (same gates)
+    calls.append((lib.csa_compress2, (P(t["kvw"][:, LWIN - M_CSA:]), P(t["kiw"][:, LWIN - M_CSA:]), L.BF16, P(g4),
+                                      P(t["bias"]), B, M_CSA, M_CSA, 2 * D, LWIN, P(wl.kvc[:, N_CSA - 1:]), None,
+                                      L.BF16, N_CSA, DI, LWIN, P(t["ki"][:, N_CSA - 1:]), P(t["ks"][:, N_CSA - 1:]),
+                                      L.MXFP4, N_CSA, st)))
     # CSA: indexer + top-k
     n = ctypes.c_size_t(0)
     idx_args = (P(t["qi"]), L.BF16, P(t["wi"]), P(t["ki"]), P(t["ks"]), L.MXFP4, P(wl.q_pos), B, 1, HI, DI, N_CSA, 0,
@@ -244,10 +244,10 @@ def time_schedule(L, torch, marsh, steps):
     replicas rotate layer by layer), the MTP layer attends over its window only.  Returns
     (us per token step, per-layer-type us)."""
     lib = L.lib()
-    parts = [{"csa": c[:4], "hca": c[4:]} for c in marsh]
+    parts = [{"csa": c[:3], "hca": c[3:]} for c in marsh]
     # window-only attention: the HCA call with no compressed entries
     for r, c in enumerate(marsh):
-        fn, a = c[5]
+        fn, a = c[4]
         a = list(a)
         a[15] = 0                                   # N
         parts[r]["swa"] = [(fn, tuple(a))]
@@ -316,11 +316,10 @@ def run_fp8_kv(L, torch, wl, steps, warmup, every=10):
     for t in wl.r:
         t8 = {"kvw": to_fp8(t["kvw"]), "hkvc": to_fp8(t["hkvc"]), "hkvw": to_fp8(t["hkvw"])}
         calls = []
-        calls.append((lib.csa_compress, (P(t["kvw"][:, LWIN - M_CSA:]), L.BF16, P(t["g4"]), P(t["bias"]), B, M_CSA,
-                                         2 * D, M_CSA, LWIN, P(kvc8[:, N_CSA - 1:]), None, L.FP8_KV, N_CSA, st)))
-        calls.append((lib.csa_compress, (P(t["kiw"][:, LWIN - M_CSA:]), L.BF16, P(t["g4"]), P(t["bias"]), B, M_CSA, DI,
-                                         M_CSA, LWIN, P(t["ki"][:, N_CSA - 1:]), P(t["ks"][:, N_CSA - 1:]), L.MXFP4,
-                                         N_CSA, st)))
+        calls.append((lib.csa_compress2, (P(t["kvw"][:, LWIN - M_CSA:]), P(t["kiw"][:, LWIN - M_CSA:]), L.BF16,
+                                          P(t["g4"]), P(t["bias"]), B, M_CSA, M_CSA, 2 * D, LWIN,
+                                          P(kvc8[:, N_CSA - 1:]), None, L.FP8_KV, N_CSA, DI, LWIN,
+                                          P(t["ki"][:, N_CSA - 1:]), P(t["ks"][:, N_CSA - 1:]), L.MXFP4, N_CSA, st)))
         idx_args = (P(t["qi"]), L.BF16, P(t["wi"]), P(t["ki"]), P(t["ks"]), L.MXFP4, P(wl.q_pos), B, 1, HI, DI, N_CSA,
                     0, M_CSA, TOPK, P(t["idx"]), None)
         calls.append((lib.csa_index_topk, idx_args + (P(t["ws_idx"]), ctypes.byref(t["ws_idx_n"]), st)))

@@ -121,6 +121,23 @@ dsv4_status csa_compress(const void* x, int x_dt, const float* gate, const float
                          hipStream_t stream);
 
 /*
+ * csa_compress2 — csa_compress of two tensors over the same raw blocks in one launch  [CSA],
+ * [P2 §4] (a CSA layer pools its K, V and its indexer key with the same gate weights).
+ *
+ *   y  = csa_compress(x,  gate, pos_bias, m)   with x  [B, x_bstride rows, C],  y  of y_dt
+ *   y2 = csa_compress(x2, gate, pos_bias, m)   with x2 [B, x2_bstride rows, C2], y2 of y2_dt
+ *   B, T, m, gate and pos_bias are shared; each output is laid out, rounded or quantised
+ *   exactly as csa_compress writes it (the same kernel body computes both).
+ *   Supported: x_dt = BF16, y_dt in {BF16, FP8_KV}, y2_dt = MXFP4 (y2_scale required);
+ *   other combinations return DSV4_ERR_UNSUPPORTED.  Per-tensor constraints and errors as
+ *   for csa_compress.  No workspace.
+ */
+dsv4_status csa_compress2(const void* x, const void* x2, int x_dt, const float* gate, const float* pos_bias,
+                          int64_t B, int64_t T, int32_t m, int64_t C, int64_t x_bstride, void* y, uint8_t* y_scale,
+                          int y_dt, int64_t y_bstride, int64_t C2, int64_t x2_bstride, void* y2, uint8_t* y2_scale,
+                          int y2_dt, int64_t y2_bstride, hipStream_t stream);
+
+/*
  * kv_cache_append — one decode step of cache maintenance around the path  [KVC], [CSA],
  * [HCA], [P2 §4] (a window of recent raw tokens next to the compressed entries).
  *

@@ -12,7 +12,7 @@ import os
 
 import torch
 
-__all__ = ["csa_compress", "kv_cache_append", "csa_index_topk", "csa_attend", "hca_attend", "csa_attend_fp8kv",
+__all__ = ["csa_compress", "csa_compress2", "kv_cache_append", "csa_index_topk", "csa_attend", "hca_attend", "csa_attend_fp8kv",
            "hca_attend_fp8kv", "lse_merge", "lib",
            "LibError",
            "F32", "BF16", "FP8_E4M3", "MXFP4", "FP8_KV", "MXFP4_DTYPE", "FP8_KV_DTYPE", "FP8_ROPE_DIMS"]
@@ -35,6 +35,8 @@ _SIGS = {
     "dsv4_time_next_kernel": ([_p, _p], ctypes.c_int),
     "csa_compress": ([_p, ctypes.c_int, _p, _p, _i64, _i64, _i64, _i32, _i64, _p, _p, ctypes.c_int, _i64, _p],
                      ctypes.c_int),
+    "csa_compress2": ([_p, _p, ctypes.c_int, _p, _p, _i64, _i64, _i32, _i64, _i64, _p, _p, ctypes.c_int, _i64, _i64,
+                       _i64, _p, _p, ctypes.c_int, _i64, _p], ctypes.c_int),
     "kv_cache_append": ([_p, ctypes.c_int, _p, _p, _i64, _i64, _p, _p, _i64, _p, _i32, _p, _p, ctypes.c_int, _i64,
                          _i64, _p], ctypes.c_int),
     "csa_index_topk": ([_p, ctypes.c_int, _p, _p, _p, ctypes.c_int, _p, _i64, _i64, _i32, _i32, _i64, _i64, _i32,
@@ -143,6 +145,25 @@ def csa_compress(x, gate, pos_bias, m: int, y_dtype=torch.bfloat16, out=None, ou
     _check(lib().csa_compress(_ptr(x), _dt(x), _ptr(gate), _ptr(pos_bias), B, T, C, m, x_bs, _ptr(out),
                               _ptr(out_scale), ydt, y_bs, _stream()))
     return (out, out_scale) if ydt == MXFP4 else out
+
+
+def csa_compress2(x, x2, gate, pos_bias, m: int, out, out2, out2_scale, out_scale=None, fp8_kv=False):
+    """Pool x [B,T,C] (bf16) into `out` (bf16 [B,rows,C], or FP8 K|V rows [B,rows,C+64] uint8
+    with fp8_kv=True and optional 2-byte `out_scale`) and x2 [B,T,C2] (bf16) into MXFP4
+    `out2` [B,rows,C2/2] + `out2_scale` [B,rows,C2/32], with the same gate [B,T] and pos_bias
+    [m], in one launch.  Outputs may be [B, rows, ...] views (e.g. a cache's tail)."""
+    if not (gate.is_contiguous() and pos_bias.is_contiguous()):
+        raise ValueError("gate [B, T] and pos_bias [m] must be contiguous")
+    B, T, C = x.shape
+    C2 = x2.shape[2]
+    if x2.shape[:2] != (B, T) or x.dtype != torch.bfloat16 or x2.dtype != torch.bfloat16:
+        raise ValueError("x and x2 must be bf16 [B, T, .] over the same tokens")
+    bs = lambda t: t.stride(0) // t.stride(1) if B > 0 else 0
+    ydt = FP8_KV if fp8_kv else _dt(out)
+    _check(lib().csa_compress2(_ptr(x), _ptr(x2), BF16, _ptr(gate), _ptr(pos_bias), B, T, m, C, bs(x), _ptr(out),
+                               _ptr(out_scale), ydt, bs(out), C2, bs(x2), _ptr(out2), _ptr(out2_scale), MXFP4,
+                               bs(out2), _stream()))
+    return out, (out2, out2_scale)
 
 
 def kv_cache_append(x_new, gate_new, pos, win, win_gate, pos_bias, m: int, cache, cache_scale=None,

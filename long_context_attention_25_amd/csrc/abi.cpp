@@ -109,6 +109,36 @@ dsv4_status check_attend(const char* what, const AttendCommon& c) {
   return ok();
 }
 
+// csa_compress's checks of one pooling job, and its arguments for the launcher.
+dsv4_status check_compress(const char* what, const void* x, int x_dt, const float* gate, const float* pos_bias,
+                           int64_t B, int64_t T, int64_t C, int32_t m, int64_t x_bstride, void* y, uint8_t* y_scale,
+                           int y_dt, int64_t y_bstride, dsv4::CompressArgs* out) {
+  REQUIRE(B >= 0 && T >= 0 && C > 0, "%s: need B >= 0, T >= 0, C > 0", what);
+  REQUIRE(m >= 1 && m <= 1024, "%s: m must be in [1, 1024], got %d", what, m);
+  REQUIRE(T % m == 0, "%s: T (%lld) must be a multiple of m (%d)", what, (long long)T, m);
+  SUPPORT(x_dt == DSV4_F32 || x_dt == DSV4_BF16, "%s: x_dt must be F32 or BF16", what);
+  SUPPORT(y_dt >= DSV4_F32 && y_dt <= DSV4_FP8_KV, "%s: unknown y_dt %d", what, y_dt);
+  if (y_dt == DSV4_FP8_KV)
+    SUPPORT(C % 16 == 0 && C / 2 > dsv4::kFp8RopeDims, "%s: FP8 K|V rows need C %% 16 == 0 and C/2 > %d", what,
+            dsv4::kFp8RopeDims);
+  SUPPORT(C % 8 == 0, "%s: C must be a multiple of 8, got %lld", what, (long long)C);
+  SUPPORT(C <= (x_dt == DSV4_F32 ? 1024 : 2048), "%s: C too large (f32: <= 1024, bf16: <= 2048)", what);
+  if (y_dt == DSV4_MXFP4) SUPPORT(C % 32 == 0, "%s: MXFP4 output needs C %% 32 == 0", what);
+  REQUIRE(x_bstride == 0 || x_bstride >= T, "%s: x_bstride must be 0 or >= T", what);
+  REQUIRE(y_bstride == 0 || y_bstride >= T / m, "%s: y_bstride must be 0 or >= T/m", what);
+  if (B * T > 0) {
+    REQUIRE(x && gate && pos_bias && y, "%s: x, gate, pos_bias and y must not be NULL", what);
+    if (y_dt == DSV4_MXFP4) REQUIRE(y_scale, "%s: y_scale must not be NULL for MXFP4 output", what);
+  }
+  dsv4::CompressArgs& a = *out;
+  a.x = x; a.x_f32 = x_dt == DSV4_F32; a.gate = gate; a.bias = pos_bias;
+  a.B = B; a.T = T; a.C = C; a.m = m;
+  a.x_bs = x_bstride ? x_bstride : T;
+  a.y_bs = y_bstride ? y_bstride : T / m;
+  a.y = y; a.y_scale = y_scale; a.y_dt = y_dt;
+  return ok();
+}
+
 dsv4::AttendArgs to_args(const AttendCommon& c, bool csa, const int32_t* idx, int k, int m, float* lse) {
   dsv4::AttendArgs a;
   a.csa = csa;
@@ -213,31 +243,27 @@ dsv4_status csa_compress(const void* x, int x_dt, const float* gate, const float
                          int64_t C, int32_t m, int64_t x_bstride, void* y, uint8_t* y_scale, int y_dt,
                          int64_t y_bstride, hipStream_t stream) {
   const char* what = "csa_compress";
-  REQUIRE(B >= 0 && T >= 0 && C > 0, "%s: need B >= 0, T >= 0, C > 0", what);
-  REQUIRE(m >= 1 && m <= 1024, "%s: m must be in [1, 1024], got %d", what, m);
-  REQUIRE(T % m == 0, "%s: T (%lld) must be a multiple of m (%d)", what, (long long)T, m);
-  SUPPORT(x_dt == DSV4_F32 || x_dt == DSV4_BF16, "%s: x_dt must be F32 or BF16", what);
-  SUPPORT(y_dt >= DSV4_F32 && y_dt <= DSV4_FP8_KV, "%s: unknown y_dt %d", what, y_dt);
-  if (y_dt == DSV4_FP8_KV)
-    SUPPORT(C % 16 == 0 && C / 2 > dsv4::kFp8RopeDims, "%s: FP8 K|V rows need C %% 16 == 0 and C/2 > %d", what,
-            dsv4::kFp8RopeDims);
-  SUPPORT(C % 8 == 0, "%s: C must be a multiple of 8, got %lld", what, (long long)C);
-  SUPPORT(C <= (x_dt == DSV4_F32 ? 1024 : 2048), "%s: C too large (f32: <= 1024, bf16: <= 2048)", what);
-  if (y_dt == DSV4_MXFP4) SUPPORT(C % 32 == 0, "%s: MXFP4 output needs C %% 32 == 0", what);
-  REQUIRE(x_bstride == 0 || x_bstride >= T, "%s: x_bstride must be 0 or >= T", what);
-  REQUIRE(y_bstride == 0 || y_bstride >= T / m, "%s: y_bstride must be 0 or >= T/m", what);
-  if (B * T > 0) {
-    REQUIRE(x && gate && pos_bias && y, "%s: x, gate, pos_bias and y must not be NULL", what);
-    if (y_dt == DSV4_MXFP4) REQUIRE(y_scale, "%s: y_scale must not be NULL for MXFP4 output", what);
-  }
   dsv4::CompressArgs a;
-  a.x = x; a.x_f32 = x_dt == DSV4_F32; a.gate = gate; a.bias = pos_bias;
-  a.B = B; a.T = T; a.C = C; a.m = m;
-  a.x_bs = x_bstride ? x_bstride : T;
-  a.y_bs = y_bstride ? y_bstride : T / m;
-  a.y = y; a.y_scale = y_scale; a.y_dt = y_dt;
+  dsv4_status s = check_compress(what, x, x_dt, gate, pos_bias, B, T, C, m, x_bstride, y, y_scale, y_dt, y_bstride, &a);
+  if (s != DSV4_OK) return s;
   if (a.total_blocks() == 0) return ok();
   return launched(dsv4::launch_compress(a, stream), what);
+}
+
+dsv4_status csa_compress2(const void* x, const void* x2, int x_dt, const float* gate, const float* pos_bias,
+                          int64_t B, int64_t T, int32_t m, int64_t C, int64_t x_bstride, void* y, uint8_t* y_scale,
+                          int y_dt, int64_t y_bstride, int64_t C2, int64_t x2_bstride, void* y2, uint8_t* y2_scale,
+                          int y2_dt, int64_t y2_bstride, hipStream_t stream) {
+  const char* what = "csa_compress2";
+  dsv4::CompressArgs a, b;
+  dsv4_status s = check_compress(what, x, x_dt, gate, pos_bias, B, T, C, m, x_bstride, y, y_scale, y_dt, y_bstride, &a);
+  if (s != DSV4_OK) return s;
+  s = check_compress(what, x2, x_dt, gate, pos_bias, B, T, C2, m, x2_bstride, y2, y2_scale, y2_dt, y2_bstride, &b);
+  if (s != DSV4_OK) return s;
+  SUPPORT(x_dt == DSV4_BF16 && (y_dt == DSV4_BF16 || y_dt == DSV4_FP8_KV) && y2_dt == DSV4_MXFP4,
+          "%s: supports bf16 x with (y_dt, y2_dt) = (BF16 or FP8_KV, MXFP4)", what);
+  if (a.total_blocks() == 0) return ok();
+  return launched(dsv4::launch_compress2(a, b, stream), what);
 }
 
 dsv4_status kv_cache_append(const void* x_new, int x_dt, const float* gate_new, const int32_t* pos, int64_t B,

@@ -386,7 +386,60 @@ hipError_t launch_append_t(const AppendArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Two pooling jobs over the same raw blocks (same gates, bias, m and batch) in one launch,
+// e.g. a CSA layer's K|V rows and its indexer key: workgroups [0, grid of job 1) run the
+// first job with its own channel split, the rest the second.
+struct PoolJob {
+  const void* x;
+  void* y;
+  uint8_t* ysc;
+  int64_t x_bs, y_bs;
+  int C, lpr, spb, bpw, cs;
+  int64_t grid;
+};
+
+template <typename TX, int Y1, int Y2>
+__global__ __launch_bounds__(kThreads) void compress2_kernel(PoolJob j1, PoolJob j2, const float* __restrict__ gate,
+                                                             const float* __restrict__ bias, int64_t T, int m,
+                                                             int64_t nb_per_b, int64_t total_blocks) {
+  if ((int64_t)blockIdx.x < j1.grid)
+    compress_body<TX, Y1>(reinterpret_cast<const TX*>(j1.x), gate, bias, T, j1.C, m, nb_per_b, total_blocks, j1.x_bs,
+                          j1.y_bs, j1.y, j1.ysc, j1.lpr, j1.spb, j1.bpw, j1.cs, blockIdx.x);
+  else
+    compress_body<TX, Y2>(reinterpret_cast<const TX*>(j2.x), gate, bias, T, j2.C, m, nb_per_b, total_blocks, j2.x_bs,
+                          j2.y_bs, j2.y, j2.ysc, j2.lpr, j2.spb, j2.bpw, j2.cs, (int64_t)blockIdx.x - j1.grid);
+}
+
+template <typename TX, int YDT>
+PoolJob pool_job(const CompressArgs& a) {
+  PoolJob j;
+  j.x = a.x;
+  j.y = a.y;
+  j.ysc = a.y_scale;
+  j.x_bs = a.x_bs;
+  j.y_bs = a.y_bs;
+  j.C = (int)a.C;
+  plan_split<TX, YDT>(a.C, a.m, a.total_blocks(), &j.lpr, &j.spb, &j.bpw, &j.cs);
+  j.grid = ((a.total_blocks() + j.bpw - 1) / j.bpw) * j.cs;
+  return j;
+}
+
+template <typename TX, int Y1, int Y2>
+hipError_t launch2_t(const CompressArgs& a, const CompressArgs& b, hipStream_t st) {
+  const PoolJob j1 = pool_job<TX, Y1>(a), j2 = pool_job<TX, Y2>(b);
+  DSV4_LAUNCH_MAIN((compress2_kernel<TX, Y1, Y2>), dim3((unsigned)(j1.grid + j2.grid)), dim3(kThreads), 0, st, j1,
+                   j2, a.gate, a.bias, a.T, a.m, a.T / a.m, a.total_blocks());
+  return hipGetLastError();
+}
+
 }  // namespace
+
+// (bf16 x) K|V rows as bf16 or FP8 K|V rows, indexer key as MXFP4; checked by the caller
+hipError_t launch_compress2(const CompressArgs& a, const CompressArgs& b, hipStream_t st) {
+  if (a.total_blocks() == 0) return hipSuccess;
+  if (a.y_dt == 4) return launch2_t<uint16_t, 4, 3>(a, b, st);
+  return launch2_t<uint16_t, 1, 3>(a, b, st);
+}
 
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
   if (a.total_blocks() == 0) return hipSuccess;

@@ -36,6 +36,9 @@ struct CompressArgs {
   int64_t total_blocks() const { return B * (T / m); }
 };
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st);
+// two jobs with the same gate, bias, B, T and m in one launch; bf16 x, (y_dt, y2_dt) in
+// {(BF16, MXFP4), (FP8_KV, MXFP4)}
+hipError_t launch_compress2(const CompressArgs& a, const CompressArgs& b, hipStream_t st);
 
 struct AppendArgs {
   const void* x_new;

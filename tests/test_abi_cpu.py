@@ -70,6 +70,26 @@ def _append(**kw):
                                    a["bias"], a["m"], a["y"], a["ysc"], a["ydt"], a["N"], a["ybs"], None)
 
 
+def _compress2(**kw):
+    a = dict(x=P, x2=P, x_dt=1, gate=P, bias=P, B=1, T=16, m=4, C=1024, xbs=0, y=P, ysc=None, ydt=1, ybs=0,
+             C2=128, x2bs=0, y2=P, y2sc=P, y2dt=3, y2bs=0)
+    a.update(kw)
+    return L.lib().csa_compress2(a["x"], a["x2"], a["x_dt"], a["gate"], a["bias"], a["B"], a["T"], a["m"], a["C"],
+                                 a["xbs"], a["y"], a["ysc"], a["ydt"], a["ybs"], a["C2"], a["x2bs"], a["y2"],
+                                 a["y2sc"], a["y2dt"], a["y2bs"], None)
+
+
+def test_compress2_validation():
+    assert _compress2(B=0) == 0                              # nothing to pool: no launch
+    assert _compress2(ydt=0) == 2                            # f32 K|V output: unsupported here
+    assert _compress2(y2dt=1) == 2                           # the second job must be MXFP4
+    assert _compress2(x_dt=0) == 2
+    assert _compress2(y2sc=None) == 1                        # MXFP4 needs its scales
+    assert _compress2(T=18) == 1
+    assert _compress2(C2=48) == 2                            # MXFP4 groups of 32
+    assert _compress2(x2=None) == 1
+
+
 def test_cache_append_validation():
     assert _append(m=0) == 1
     assert _append(L=200) == 1 and b"multiple of m" in L.lib().dsv4_last_error()

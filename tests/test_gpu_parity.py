@@ -311,6 +311,32 @@ def test_compress_fp8kv_rows(m, nb):
     _check_fp8kv_rows(rows.cpu().numpy(), y_ref, tol, ek=-2, ev=1)
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_compress2_equals_two_compress_calls(fp8):
+    """K|V rows and the indexer key pooled in one launch write the same bytes as two
+    csa_compress calls (into the tail of caches with a batch stride)."""
+    cfg = 109 + fp8
+    B, m, nb, C, C2, N = 3, 4, 20, 1024, 128, 50
+    T = nb * m
+    x, _ = dev_bf16(synth.normal(cfg, synth.RAW_K, (B, T, C)))
+    x2, _ = dev_bf16(synth.normal(cfg, synth.RAW_KI, (B, T, C2)))
+    gate = dev(synth.normal(cfg, synth.GATE, (B, T)))
+    bias = dev(synth.normal(cfg, synth.BIAS, (m,), std=0.1))
+    width = C + DR if fp8 else C
+    ydt = torch.uint8 if fp8 else torch.bfloat16
+    y_a, y_b = torch.zeros((B, N, width), dtype=ydt, device="cuda"), torch.zeros((B, N, width), dtype=ydt, device="cuda")
+    k_a, k_b = (torch.zeros((B, N, C2 // 2), dtype=torch.uint8, device="cuda") for _ in range(2))
+    s_a, s_b = (torch.zeros((B, N, C2 // 32), dtype=torch.uint8, device="cuda") for _ in range(2))
+    sc = dev(np.array([127 - 1, 127 + 1], dtype=np.uint8)) if fp8 else None
+    L.csa_compress2(x, x2, gate, bias, m, y_a[:, N - nb:], k_a[:, N - nb:], s_a[:, N - nb:], out_scale=sc, fp8_kv=fp8)
+    L.csa_compress(x, gate, bias, m, L.FP8_KV_DTYPE if fp8 else torch.bfloat16, out=y_b[:, N - nb:],
+                   out_scale=sc)
+    L.csa_compress(x2, gate, bias, m, L.MXFP4_DTYPE, out=k_b[:, N - nb:], out_scale=s_b[:, N - nb:])
+    torch.cuda.synchronize()
+    assert torch.equal(y_a, y_b) and torch.equal(k_a, k_b) and torch.equal(s_a, s_b)
+    assert torch.count_nonzero(y_a[:, :N - nb]) == 0 and torch.count_nonzero(y_a[:, N - nb:]) > 0
+
+
 def test_fp8kv_rows_from_pooling_feed_the_attention():
     """Stage-wise: HCA attention over an FP8 K|V cache written by the pooling (K|V side by
     side, row stride C + 64) equals the oracle on the oracle's decoding of those bytes."""
