@@ -69,15 +69,15 @@ KERNEL_BYTES = {
 # the counter's reading for a 256 MiB device copy (see profiles/).  An entry is used only
 # while the kernel source it was measured on is unchanged (sha256 of the file).
 MEASURED_TRAFFIC = {
-    "index_mfma_kernel": {"bytes_per_launch": 151634044,
+    "index_mfma_kernel": {"bytes_per_launch": 151635354,
         "source_sha256": "42978ac55e131ad1a4b16b8e7d7b0bd2ac9e9e1bc3045c0d21a5f8fdd9368a38"},
-    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 156020727,
+    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 156022004,
         "source_sha256": "b4ccb839c3b08f5e16e10a18984ede0506b45df4e0a24cb88f4f8a6a79bd6792"},
-    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32829632,
+    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32829845,
         "source_sha256": "b4ccb839c3b08f5e16e10a18984ede0506b45df4e0a24cb88f4f8a6a79bd6792"},
-    "attend_fp8kv_kernel (HCA)": {"bytes_per_launch": 92170581,
+    "attend_fp8kv_kernel (HCA)": {"bytes_per_launch": 92169255,
         "source_sha256": "b4ccb839c3b08f5e16e10a18984ede0506b45df4e0a24cb88f4f8a6a79bd6792"},
-    "attend_fp8kv_kernel (CSA)": {"bytes_per_launch": 24546785,
+    "attend_fp8kv_kernel (CSA)": {"bytes_per_launch": 24546845,
         "source_sha256": "b4ccb839c3b08f5e16e10a18984ede0506b45df4e0a24cb88f4f8a6a79bd6792"},
 }
 
