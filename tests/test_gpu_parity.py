@@ -338,15 +338,23 @@ def test_compress2_equals_two_compress_calls(fp8):
 
 
 def test_fp8kv_rows_from_pooling_feed_the_attention():
-    """Stage-wise: HCA attention over an FP8 K|V cache written by the pooling (K|V side by
-    side, row stride C + 64) equals the oracle on the oracle's decoding of those bytes."""
+    """Pooling into FP8 K|V rows (K|V side by side, row stride C + 64) and HCA attention over
+    such a cache.  Parity: the GPU attends over the oracle's own pooled-and-encoded rows and
+    matches the oracle on them.  Layout: the GPU's pooled rows equal those bytes but for
+    rare rounding midpoints, and attending over them gives the same result (GPU vs GPU)."""
     cfg = 108
     B, Q, H, D, m, nb, Lw, W = 2, 2, 64, 512, 128, 40, 128, 128
     x32 = synth.normal(cfg, synth.RAW_K, (B, nb * m, 2 * D))
     gate = synth.normal(cfg, synth.GATE, (B, nb * m))
     bias = synth.normal(cfg, synth.BIAS, (m,), std=0.1)
-    xd, _ = dev_bf16(x32)
-    kv = L.csa_compress(xd, dev(gate), dev(bias), m, L.FP8_KV_DTYPE)        # [B, nb, 1088]
+    xd, xbits = dev_bf16(x32)
+    kv_gpu = L.csa_compress(xd, dev(gate), dev(bias), m, L.FP8_KV_DTYPE)        # [B, nb, 1088]
+    y_ref = method.compress(codecs.decode_bf16(xbits), gate, bias, m).astype(np.float32)
+    rows = np.concatenate([codecs.encode_fp8_k_rows(y_ref[..., :D], DR, 1.0),
+                           codecs.encode_fp8_v_rows(y_ref[..., D:], 1.0)], axis=-1)     # the oracle's rows
+    torch.cuda.synchronize()
+    gpu_rows = kv_gpu.cpu().numpy()
+    assert (gpu_rows != rows).mean() < 1e-3                    # only rounding midpoints differ
     (_, _, kwb, vwb), (_, _, kwd, vwd) = _fp8_kv(cfg, B, 1, Lw, D, 1.0, 1.0)
     q = synth.normal(cfg, synth.Q, (B, Q, H, D))
     qd, qb = dev_bf16(q)
@@ -355,14 +363,18 @@ def test_fp8kv_rows_from_pooling_feed_the_attention():
     pos = np.array([[T - 1, T - 50], [T - 30, T - 100]], dtype=np.int32)
     KB = D + DR
     scale = 1.0 / math.sqrt(D)
-    o, lse = L.hca_attend_fp8kv(qd, kv[..., :KB], kv[..., KB:], m, dev(kwb), dev(vwb), dev(win_pos0), W, dev(pos),
-                                scale)
+    kv_ref = dev(rows)
+    o, lse = L.hca_attend_fp8kv(qd, kv_ref[..., :KB], kv_ref[..., KB:], m, dev(kwb), dev(vwb), dev(win_pos0), W,
+                                dev(pos), scale)
+    o2, lse2 = L.hca_attend_fp8kv(qd, kv_gpu[..., :KB], kv_gpu[..., KB:], m, dev(kwb), dev(vwb), dev(win_pos0), W,
+                                  dev(pos), scale)
     torch.cuda.synchronize()
-    rows = kv.cpu().numpy()
     kd, vd = codecs.decode_fp8_k_rows(rows[..., :KB], D, DR, 1.0), codecs.decode_fp8_v_rows(rows[..., KB:], 1.0)
-    o_ref, lse_ref = method.hca_attend(codecs.decode_bf16(qb), kd, vd, m, kwd, vwd, win_pos0, W, pos, scale)
-    assert row_rel_err(host(o), o_ref) <= 1e-2
-    assert lse_abs_err(host(lse), lse_ref) <= 1e-2
+    o_r, lse_r = method.hca_attend(codecs.decode_bf16(qb), kd, vd, m, kwd, vwd, win_pos0, W, pos, scale)
+    assert row_rel_err(host(o), o_r) <= 1e-2
+    assert lse_abs_err(host(lse), lse_r) <= 1e-2
+    assert row_rel_err(host(o2), host(o)) <= 1e-2
+    assert lse_abs_err(host(lse2), host(lse)) <= 1e-2
 
 
 # ============================================================ indexer + top-k
