@@ -69,16 +69,16 @@ KERNEL_BYTES = {
 # the counter's reading for a 256 MiB device copy (see profiles/).  An entry is used only
 # while the kernel source it was measured on is unchanged (sha256 of the file).
 MEASURED_TRAFFIC = {
-    "index_mfma_kernel": {"bytes_per_launch": 151635354,
-        "source_sha256": "42978ac55e131ad1a4b16b8e7d7b0bd2ac9e9e1bc3045c0d21a5f8fdd9368a38"},
-    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 156022004,
-        "source_sha256": "b4ccb839c3b08f5e16e10a18984ede0506b45df4e0a24cb88f4f8a6a79bd6792"},
-    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32829845,
-        "source_sha256": "b4ccb839c3b08f5e16e10a18984ede0506b45df4e0a24cb88f4f8a6a79bd6792"},
-    "attend_fp8kv_kernel (HCA)": {"bytes_per_launch": 92169255,
-        "source_sha256": "b4ccb839c3b08f5e16e10a18984ede0506b45df4e0a24cb88f4f8a6a79bd6792"},
-    "attend_fp8kv_kernel (CSA)": {"bytes_per_launch": 24546845,
-        "source_sha256": "b4ccb839c3b08f5e16e10a18984ede0506b45df4e0a24cb88f4f8a6a79bd6792"},
+    "index_mfma_kernel": {"bytes_per_launch": 151656688,
+        "source_sha256": "7522fc641e82460a790e10a7a6610b0ee80a90978bcd7cdd70d295a74b6d1a5f"},
+    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 156021062,
+        "source_sha256": "495eabb8887fb193194551e9e012c5877bcee5dc19acd9afba5177dbf8206ec1"},
+    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32829691,
+        "source_sha256": "495eabb8887fb193194551e9e012c5877bcee5dc19acd9afba5177dbf8206ec1"},
+    "attend_fp8kv_kernel (HCA)": {"bytes_per_launch": 92170809,
+        "source_sha256": "495eabb8887fb193194551e9e012c5877bcee5dc19acd9afba5177dbf8206ec1"},
+    "attend_fp8kv_kernel (CSA)": {"bytes_per_launch": 24546975,
+        "source_sha256": "495eabb8887fb193194551e9e012c5877bcee5dc19acd9afba5177dbf8206ec1"},
 }
 
 

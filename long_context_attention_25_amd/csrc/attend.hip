@@ -113,9 +113,10 @@ __device__ __forceinline__ const T* lane_ptr(const T* p, int src) {
 // the compiler does not track it: it would otherwise make LDS reads wait for copies into
 // other buffers.  The copy has no register result; completion is waited for explicitly
 // with wait_vmcnt (it counts as a vector-memory operation until its data is in LDS).
-// s_nop 3 covers the m0 write before the copy reads it.
+// s_nop 3 covers the m0 write before the copy reads it.  The copies stream K/V rows a
+// call reads once, so they carry the non-temporal hint (nt), as the streaming loads do.
 __device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 3\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src),
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 3\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src),
                "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory", "m0");
 }

@@ -122,7 +122,7 @@ struct KeyTile<KEY_BF16, DI> {
   __device__ void load(const uint8_t* kbase, const uint8_t*, int64_t key, int g, bool ok) {
     const uint4* p = reinterpret_cast<const uint4*>(kbase + key * (DI * 2) + g * (DI / 2));
 #pragma unroll
-    for (int c = 0; c < KS; ++c) w[c] = ok ? p[c] : make_uint4(0, 0, 0, 0);
+    for (int c = 0; c < KS; ++c) w[c] = ok ? load_stream(p + c) : make_uint4(0, 0, 0, 0);
   }
   __device__ bf16x8 op(int c) const { return bit_cast_to<bf16x8>(w[c]); }
 };
@@ -134,11 +134,19 @@ struct KeyTile<KEY_MXFP4, DI> {
   uint32_t sc;   // up to 2 scale bytes for this lane's dims
   __device__ void load(const uint8_t* kbase, const uint8_t* sbase, int64_t key, int g, bool ok) {
     const uint32_t* p = reinterpret_cast<const uint32_t*>(kbase + key * (DI / 2) + g * (DI / 8));
+    if constexpr (KS % 4 == 0) {          // 16-byte aligned: whole dwordx4 loads
 #pragma unroll
-    for (int c = 0; c < KS; ++c) w[c] = ok ? p[c] : 0u;
+      for (int c = 0; c < KS; c += 4) {
+        const uint4 v = ok ? load_stream(reinterpret_cast<const uint4*>(p + c)) : make_uint4(0, 0, 0, 0);
+        w[c] = v.x; w[c + 1] = v.y; w[c + 2] = v.z; w[c + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < KS; ++c) w[c] = ok ? load_stream(p + c) : 0u;
+    }
     const uint8_t* s = sbase + key * (DI / 32) + (g * (DI / 4)) / 32;
-    if constexpr (DI == 256) sc = ok ? (uint32_t)s[0] | ((uint32_t)s[1] << 8) : 0x7f7fu;
-    else sc = ok ? (uint32_t)s[0] : 0x7fu;
+    if constexpr (DI == 256) sc = ok ? load_stream(s) | (load_stream(s + 1) << 8) : 0x7f7fu;
+    else sc = ok ? load_stream(s) : 0x7fu;
   }
   __device__ bf16x8 op(int c) const {
     // scale byte of k-step c: dims g*DI/4 + 8c lie in group (g*DI/4 + 8c)/32
@@ -167,7 +175,7 @@ struct KeyTile<KEY_FP8, DI> {
   __device__ void load(const uint8_t* kbase, const uint8_t*, int64_t key, int g, bool ok) {
     const uint2* p = reinterpret_cast<const uint2*>(kbase + key * DI + g * (DI / 4));
 #pragma unroll
-    for (int c = 0; c < KS; ++c) w[c] = ok ? p[c] : make_uint2(0, 0);
+    for (int c = 0; c < KS; ++c) w[c] = ok ? load_stream(p + c) : make_uint2(0, 0);
   }
   __device__ long op(int c) const { return __builtin_bit_cast(long, w[c]); }
 };
