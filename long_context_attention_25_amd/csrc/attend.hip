@@ -113,12 +113,21 @@ __device__ __forceinline__ const T* lane_ptr(const T* p, int src) {
 // the compiler does not track it: it would otherwise make LDS reads wait for copies into
 // other buffers.  The copy has no register result; completion is waited for explicitly
 // with wait_vmcnt (it counts as a vector-memory operation until its data is in LDS).
-// s_nop 3 covers the m0 write before the copy reads it.  The copies stream K/V rows a
-// call reads once, so they carry the non-temporal hint (nt), as the streaming loads do.
+// s_nop 3 covers the m0 write before the copy reads it.  kNT adds the non-temporal hint
+// (nt), used for K/V rows that one workgroup of the call reads once (one query per
+// sequence): such streams are faster with it and leave the caches to reused data.  It is
+// a template parameter of the kernels: a branch per copy on a run-time flag cost ~2 us
+// per decode launch.
+template <bool kNT = false>
 __device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 3\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src),
-               "s"(__builtin_amdgcn_readfirstlane(lds))
-               : "memory", "m0");
+  if constexpr (kNT)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 3\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src),
+                 "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 3\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src),
+                 "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory", "m0");
 }
 // A load through the constant address space: with a uniform address the compiler emits a
 // scalar load, which the vector-memory counter does not track.
@@ -157,7 +166,7 @@ __device__ __forceinline__ void tile_barrier() {
 // bytes, V: +32 bytes) so that the K operand reads (16 rows, same column) and the
 // transposed V reads (4 rows x 2 chunks per 16 lanes) hit distinct banks while every read
 // of a lane uses one base address plus immediate offsets.
-template <int D, int DS>
+template <int D, int DS, bool kNT>
 __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a, int64_t chunk, int splits,
                                                                uint16_t* __restrict__ o_part,
                                                                float* __restrict__ lse_part) {
@@ -228,8 +237,8 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
       const int r = wave + i * NWV;
       const int off = (lane % LPR) * 8;
       if (j == 0) {
-        copy16_to_lds(lane_ptr<true>(my_kp, r) + off, kdst + r * KSTR);
-        copy16_to_lds(lane_ptr<true>(my_vp, r) + off, vdst + r * VSTR);
+        copy16_to_lds<kNT>(lane_ptr<true>(my_kp, r) + off, kdst + r * KSTR);
+        copy16_to_lds<kNT>(lane_ptr<true>(my_vp, r) + off, vdst + r * VSTR);
       }
     }
   };
@@ -537,7 +546,7 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
 // the banks.
 constexpr int kListF8 = 512;          // index entries of one CSA split (FP8 kernel)
 
-template <int D>
+template <int D, bool kNT>
 __global__ __launch_bounds__(kThreads * 2) void attend_fp8kv_kernel(AttendArgs a, int64_t chunk, int splits,
                                                                 uint16_t* __restrict__ o_part,
                                                                 float* __restrict__ lse_part) {
@@ -605,8 +614,8 @@ __global__ __launch_bounds__(kThreads * 2) void attend_fp8kv_kernel(AttendArgs a
       const int r = wave + i * NWV;
       const uint8_t* kp = lane_ptr<true>(my_kp, r);
       const uint8_t* vp = lane_ptr<true>(my_vp, r);
-      if (lane < K8B / 16) copy16_to_lds(kp + lane * 16, kdst + r * K8S);
-      if (lane < V8B / 16) copy16_to_lds(vp + lane * 16, vdst + r * V8S + (r >= 16 ? VH : 0));
+      if (lane < K8B / 16) copy16_to_lds<kNT>(kp + lane * 16, kdst + r * K8S);
+      if (lane < V8B / 16) copy16_to_lds<kNT>(vp + lane * 16, vdst + r * V8S + (r >= 16 ? VH : 0));
     }
   };
   // HCA: tiles 0 and 1 issued before the query position is known (checked below)
@@ -1477,6 +1486,20 @@ AttendPlan plan_attend(const AttendArgs& a) {
   return p;
 }
 
+template <bool kNT>
+hipError_t launch_split_kernel(const AttendArgs& a, const AttendPlan& p, dim3 grid, uint16_t* o_part,
+                               float* lse_part, hipStream_t st) {
+  if (a.f8) {   // D == 512 (checked by the caller)
+    DSV4_LAUNCH_MAIN((attend_fp8kv_kernel<512, kNT>), grid, dim3(kThreads * 2), 0, st, a, (int64_t)p.chunk, p.splits,
+                     o_part, lse_part);
+  } else switch (a.D) {
+    case 128: DSV4_LAUNCH_MAIN((attend_bf16_kernel<128, 1, kNT>), grid, dim3(kThreads), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part); break;
+    case 256: DSV4_LAUNCH_MAIN((attend_bf16_kernel<256, 1, kNT>), grid, dim3(kThreads), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part); break;
+    default: DSV4_LAUNCH_MAIN((attend_bf16_kernel<512, 2, kNT>), grid, dim3(kThreads * 2), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part); break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_attend(const AttendArgs& a, const AttendPlan& p, void* ws, hipStream_t st) {
   const int64_t rows = a.B * a.Q;
   if (rows == 0) return hipSuccess;
@@ -1502,16 +1525,10 @@ hipError_t launch_attend(const AttendArgs& a, const AttendPlan& p, void* ws, hip
                        R, a.D, reinterpret_cast<uint16_t*>(a.out), a.lse);
     return hipGetLastError();
   }
-  dim3 grid((unsigned)p.splits, (unsigned)rows);
-  if (a.f8) {   // D == 512 (checked by the caller)
-    DSV4_LAUNCH_MAIN((attend_fp8kv_kernel<512>), grid, dim3(kThreads * 2), 0, st, a, (int64_t)p.chunk, p.splits,
-                     o_part, lse_part);
-  } else switch (a.D) {
-    case 128: DSV4_LAUNCH_MAIN((attend_bf16_kernel<128, 1>), grid, dim3(kThreads), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part); break;
-    case 256: DSV4_LAUNCH_MAIN((attend_bf16_kernel<256, 1>), grid, dim3(kThreads), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part); break;
-    default: DSV4_LAUNCH_MAIN((attend_bf16_kernel<512, 2>), grid, dim3(kThreads * 2), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part); break;
-  }
-  hipError_t e = hipGetLastError();
+  // one query per sequence: each K/V row is read by one workgroup of the call (streamed)
+  const dim3 grid((unsigned)p.splits, (unsigned)rows);
+  hipError_t e = a.Q == 1 ? launch_split_kernel<true>(a, p, grid, o_part, lse_part, st)
+                          : launch_split_kernel<false>(a, p, grid, o_part, lse_part, st);
   if (e != hipSuccess || p.splits == 1) return e;
   hipLaunchKernelGGL(merge_bf16_parts_kernel, dim3((unsigned)R), dim3(kThreads), 0, st, o_part, lse_part, p.splits, R,
                      a.D, reinterpret_cast<uint16_t*>(a.out), a.lse);   // D <= 512: 8 dims per lane

@@ -43,10 +43,12 @@ __device__ __forceinline__ uint32_t gload_u32(const void* p) {
   return *(const __attribute__((address_space(1))) uint32_t*)(p);
 }
 
-// Streaming loads for data a call reads exactly once (cache rows, indexer keys): the
-// non-temporal hint keeps the stream from displacing reused data in L2 and the Infinity
-// Cache, and on MI355X plain streaming reads run ~10-15 % faster with it (2 GiB read:
-// ~6.9-7.0 TB/s against ~6.0-6.3 TB/s with ordinary loads).
+// Streaming loads for data a call reads exactly once (cache rows, indexer keys, when one
+// workgroup per sequence reads them): the non-temporal hint keeps the stream from
+// displacing reused data in L2 and the Infinity Cache, and on MI355X plain streaming
+// reads run ~10-15 % faster with it (2 GiB read: ~6.9-7.0 TB/s against ~6.0-6.3 TB/s
+// with ordinary loads).  Data that several workgroups of a call read (many queries per
+// sequence) is loaded the ordinary way: there the caches serve the repeats.
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint4 load_stream(const uint4* p) {
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
@@ -58,6 +60,18 @@ __device__ __forceinline__ uint2 load_stream(const uint2* p) {
 }
 __device__ __forceinline__ uint32_t load_stream(const uint32_t* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ uint32_t load_stream(const uint8_t* p) { return __builtin_nontemporal_load(p); }
+template <bool kNT> __device__ __forceinline__ uint4 load_key(const uint4* p) {
+  if constexpr (kNT) return load_stream(p); else return *p;
+}
+template <bool kNT> __device__ __forceinline__ uint2 load_key(const uint2* p) {
+  if constexpr (kNT) return load_stream(p); else return *p;
+}
+template <bool kNT> __device__ __forceinline__ uint32_t load_key(const uint32_t* p) {
+  if constexpr (kNT) return load_stream(p); else return *p;
+}
+template <bool kNT> __device__ __forceinline__ uint32_t load_key(const uint8_t* p) {
+  if constexpr (kNT) return load_stream(p); else return *p;
+}
 
 // ------------------------------------------------------------------ OCP fp8 e4m3
 // Nearest-even on the 3-bit mantissa, saturating to +-448 (0x7e), NaN -> 0x7f.

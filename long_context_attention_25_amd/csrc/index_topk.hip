@@ -119,10 +119,11 @@ template <int DI>
 struct KeyTile<KEY_BF16, DI> {
   static constexpr int KS = DI / 32;
   uint4 w[KS];
+  template <bool kNT>
   __device__ void load(const uint8_t* kbase, const uint8_t*, int64_t key, int g, bool ok) {
     const uint4* p = reinterpret_cast<const uint4*>(kbase + key * (DI * 2) + g * (DI / 2));
 #pragma unroll
-    for (int c = 0; c < KS; ++c) w[c] = ok ? load_stream(p + c) : make_uint4(0, 0, 0, 0);
+    for (int c = 0; c < KS; ++c) w[c] = ok ? load_key<kNT>(p + c) : make_uint4(0, 0, 0, 0);
   }
   __device__ bf16x8 op(int c) const { return bit_cast_to<bf16x8>(w[c]); }
 };
@@ -132,21 +133,22 @@ struct KeyTile<KEY_MXFP4, DI> {
   static constexpr int KS = DI / 32;
   uint32_t w[KS];
   uint32_t sc;   // up to 2 scale bytes for this lane's dims
+  template <bool kNT>
   __device__ void load(const uint8_t* kbase, const uint8_t* sbase, int64_t key, int g, bool ok) {
     const uint32_t* p = reinterpret_cast<const uint32_t*>(kbase + key * (DI / 2) + g * (DI / 8));
     if constexpr (KS % 4 == 0) {          // 16-byte aligned: whole dwordx4 loads
 #pragma unroll
       for (int c = 0; c < KS; c += 4) {
-        const uint4 v = ok ? load_stream(reinterpret_cast<const uint4*>(p + c)) : make_uint4(0, 0, 0, 0);
+        const uint4 v = ok ? load_key<kNT>(reinterpret_cast<const uint4*>(p + c)) : make_uint4(0, 0, 0, 0);
         w[c] = v.x; w[c + 1] = v.y; w[c + 2] = v.z; w[c + 3] = v.w;
       }
     } else {
 #pragma unroll
-      for (int c = 0; c < KS; ++c) w[c] = ok ? load_stream(p + c) : 0u;
+      for (int c = 0; c < KS; ++c) w[c] = ok ? load_key<kNT>(p + c) : 0u;
     }
     const uint8_t* s = sbase + key * (DI / 32) + (g * (DI / 4)) / 32;
-    if constexpr (DI == 256) sc = ok ? load_stream(s) | (load_stream(s + 1) << 8) : 0x7f7fu;
-    else sc = ok ? load_stream(s) : 0x7fu;
+    if constexpr (DI == 256) sc = ok ? load_key<kNT>(s) | (load_key<kNT>(s + 1) << 8) : 0x7f7fu;
+    else sc = ok ? load_key<kNT>(s) : 0x7fu;
   }
   __device__ bf16x8 op(int c) const {
     // scale byte of k-step c: dims g*DI/4 + 8c lie in group (g*DI/4 + 8c)/32
@@ -172,17 +174,18 @@ template <int DI>
 struct KeyTile<KEY_FP8, DI> {
   static constexpr int KS = DI / 32;
   uint2 w[KS];
+  template <bool kNT>
   __device__ void load(const uint8_t* kbase, const uint8_t*, int64_t key, int g, bool ok) {
     const uint2* p = reinterpret_cast<const uint2*>(kbase + key * DI + g * (DI / 4));
 #pragma unroll
-    for (int c = 0; c < KS; ++c) w[c] = ok ? load_stream(p + c) : make_uint2(0, 0);
+    for (int c = 0; c < KS; ++c) w[c] = ok ? load_key<kNT>(p + c) : make_uint2(0, 0);
   }
   __device__ long op(int c) const { return __builtin_bit_cast(long, w[c]); }
 };
 
 // QTW query tiles (QTW * 16/HI queries) per workgroup: every key tile loaded is used by
 // all of them (QTW > 1 when there are many queries, e.g. a prefill chunk).
-template <int KIND, int DI, int HI, int QTW>
+template <int KIND, int DI, int HI, int QTW, bool kNT>
 __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
     const uint8_t* __restrict__ qi, const uint8_t* __restrict__ qsc, const float* __restrict__ wi,
     const uint8_t* __restrict__ ki, const uint8_t* __restrict__ ksc, const int32_t* __restrict__ q_pos, int64_t N,
@@ -221,7 +224,7 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       const int64_t key = base + u * 16 + col;
-      cur[u].load(kbase, sbase, key < klast ? key : klast, g, true);
+      cur[u].template load<kNT>(kbase, sbase, key < klast ? key : klast, g, true);
     }
   }
 
@@ -290,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
 #pragma unroll
       for (int u = 0; u < TPW; ++u) {
         const int64_t key = nb + u * 16 + col;
-        nxt[u].load(kbase, sbase, key < klast ? key : klast, g, true);
+        nxt[u].template load<kNT>(kbase, sbase, key < klast ? key : klast, g, true);
       }
     }
     // After the head reduction the GPQ lanes of a query slot hold the same score, so E
@@ -716,10 +719,17 @@ hipError_t launch_mfma_q(const IndexArgs& a, float* scores, uint32_t* hist, int6
   dim3 grid((unsigned)((a.N + chunk - 1) / chunk), (unsigned)(a.B * QG));
   const int64_t slots = (int64_t)QTW * QPT < a.Q ? (int64_t)QTW * QPT : a.Q;
   size_t smem = (size_t)slots * kHistWords * sizeof(uint32_t);
-  DSV4_LAUNCH_MAIN((index_mfma_kernel<KIND, DI, HI, QTW>), grid, dim3(kThreads), smem, st,
-                   reinterpret_cast<const uint8_t*>(a.qi), a.qi_scale, a.wi, reinterpret_cast<const uint8_t*>(a.ki),
-                   a.ki_scale,
-                   a.q_pos, a.N, a.k_bs, a.Q, a.m, chunk, scores, ((a.N + 63) / 64) * 64, hist);
+  // one query group per sequence: every key is read by one workgroup of the call, so the
+  // keys are streamed with the non-temporal hint; with several groups the caches serve the
+  // repeated reads (multi-query calls always run with QTW > 1 or several groups)
+  if (QTW == 1 && QG == 1)
+    DSV4_LAUNCH_MAIN((index_mfma_kernel<KIND, DI, HI, QTW, (QTW == 1)>), grid, dim3(kThreads), smem, st,
+                     reinterpret_cast<const uint8_t*>(a.qi), a.qi_scale, a.wi, reinterpret_cast<const uint8_t*>(a.ki),
+                     a.ki_scale, a.q_pos, a.N, a.k_bs, a.Q, a.m, chunk, scores, ((a.N + 63) / 64) * 64, hist);
+  else
+    DSV4_LAUNCH_MAIN((index_mfma_kernel<KIND, DI, HI, QTW, false>), grid, dim3(kThreads), smem, st,
+                     reinterpret_cast<const uint8_t*>(a.qi), a.qi_scale, a.wi, reinterpret_cast<const uint8_t*>(a.ki),
+                     a.ki_scale, a.q_pos, a.N, a.k_bs, a.Q, a.m, chunk, scores, ((a.N + 63) / 64) * 64, hist);
   return hipGetLastError();
 }
 
