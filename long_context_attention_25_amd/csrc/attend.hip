@@ -8,17 +8,18 @@
 // 강하게 압축하고, 압축된 전체를 보기": every compressed entry, no selection;
 // pogovet.com 상세 정리 §4).
 //
-// bf16 path (MQA, H <= 64 heads share one K/V):
-//   grid = (key-range splits, B*Q); 4 waves, wave w owns heads 16w..16w+15.
-//   Per 32-key sub-tile the K rows (gathered by index, or contiguous) are staged in
-//   LDS as-is and the V rows are staged transposed (dims x keys, via byte
-//   permutes of dword loads), while the next sub-tile's rows are already in flight
-//   in registers.  S^T = K.Q^T comes from mfma_f32_16x16x32_bf16 with K as the
-//   A operand, so each lane ends up holding 8 scores of ONE head; those scores,
-//   exponentiated and rounded to bf16, are directly the B operand of
-//   O^T += V^T.P^T with no data movement.  Online softmax in fp32 (exp2 with the
-//   scale folded in; the hardware exp2, whose arguments here are <= 0 or -inf).
-//   Splits write bf16 partial outputs and fp32 lse that a merge kernel combines.
+// bf16 path (MQA: up to 64 query heads share one K/V row per key):
+//   grid = (key-range splits, B*Q); one workgroup takes all heads of one query over one
+//   key range, so each K/V byte crosses HBM once and is reused from LDS by every head.
+//   The range is walked in 16-key tiles: K and V rows are copied straight into a
+//   four-stage LDS ring (global_load_lds, three tiles in flight, rows padded so that
+//   both operand read patterns are bank-conflict free).  S^T = K.Q^T comes from
+//   mfma_f32_16x16x32_bf16 with K as the A operand, so each lane holds scores of one
+//   head; exponentiated and rounded to bf16 they are directly the B operand of
+//   O^T += V^T.P^T (mfma_f32_16x16x16_bf16, V^T read with transposing LDS reads).
+//   Online softmax in fp32 (exp2 with the scale folded in; the hardware exp2, whose
+//   arguments here are <= 0 or -inf) with lazy rescaling.  Splits write bf16 partial
+//   outputs and fp32 lse that a merge kernel combines.
 // bf16 query pairs (dense attention over many queries, e.g. a prefill chunk): two
 //   queries per workgroup share every K/V tile and every operand read.
 // FP8 K/V rows: the same scheme over E4M3 rows decoded in registers.
@@ -33,13 +34,13 @@ namespace dsv4 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTile = 32;            // keys per sub-tile (split granularity)
+constexpr int kTile = 32;            // split granularity: key ranges are multiples of 32 keys
 constexpr int kMaxCsaChunk = 2048;   // index entries of one CSA split (staged in LDS)
 constexpr int kTargetWorkgroups = 256;   // gfx950: 256 CUs, one attention workgroup each
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazyRescale = 8.0f;  // log2 units: rescale O only when the max grows by > 2^8
-constexpr int kHeads = 64;            // query heads handled by one workgroup (4 waves x 16)
+constexpr int kHeads = 64;            // query heads handled by one workgroup (4 head groups x 16)
 
 struct KeyRange {
   int64_t n_c;      // compressed part length (CSA: k list slots, HCA: visible blocks)

@@ -8,6 +8,8 @@ largest configurations in a test, but each sampled output is computed exactly).
   against compressed-only + window-only partials combined by lse_merge; the 128x
   compression pre-pass over the full 2^20-token raw stream on sampled blocks.
 * 64K-context CSA decode: B = 4, 16,384 entries, bf16 indexer keys, top-512, every row.
+* FP8 K|V rows: the 1M-context HCA decode and a 64K-context CSA decode over rows of 448
+  E4M3 K codes + 64 bf16 RoPE dims and 512 E4M3 V codes, every row.
 """
 import math
 
@@ -207,6 +209,64 @@ def test_csa_decode_64k_bf16_all_rows():
     torch.cuda.synchronize()
     o_r, lse_r = method.csa_attend(dec(q_bits), dec(kc_bits), dec(vc_bits), idx_r, dec(kw_bits), dec(vw_bits),
                                    win_pos0, W, pos, scale)
+    assert row_rel_err(host_bf16(o), o_r) <= 1e-2
+    assert lse_abs_err(lse.cpu().numpy(), lse_r) <= 1e-2
+
+
+# ------------------------------------------------------------------- FP8 K|V rows (NEXT 2)
+DR = 64      # bf16 RoPE dims at the end of an FP8 K row
+
+
+def _fp8_rows(cfg, B, N, Lw, D, ks, vs):
+    """K/V caches and windows as FP8 K|V byte rows made by the oracle's encoder, with the
+    oracle's float64 decoding of those bytes."""
+    kc = synth.normal(cfg, synth.KC, (B, N, D))
+    vc = synth.normal(cfg, synth.VC, (B, N, D))
+    kw = synth.normal(cfg, synth.KW, (B, Lw, D))
+    vw = synth.normal(cfg, synth.VW, (B, Lw, D))
+    rows = [codecs.encode_fp8_k_rows(kc, DR, ks), codecs.encode_fp8_v_rows(vc, vs),
+            codecs.encode_fp8_k_rows(kw, DR, ks), codecs.encode_fp8_v_rows(vw, vs)]
+    dec = [codecs.decode_fp8_k_rows(rows[0], D, DR, ks), codecs.decode_fp8_v_rows(rows[1], vs),
+           codecs.decode_fp8_k_rows(rows[2], D, DR, ks), codecs.decode_fp8_v_rows(rows[3], vs)]
+    return rows, dec
+
+
+def test_hca_decode_1m_fp8kv_all_rows():
+    """The bench's FP8 HCA decode: B = 8, 8,192 entries of 1,088-byte FP8 K|V rows plus a
+    128-row FP8 window, 64 heads x 512, non-power-of-two scales; every row against the
+    oracle attending over its decoding of the same bytes."""
+    B, N, H, D, Lw, W, m = 8, 8192, 64, 512, 128, 128, 128
+    ks, vs = 0.37, 1.9
+    p = (1 << 20) - 1
+    (kcb, vcb, kwb, vwb), (kcd, vcd, kwd, vwd) = _fp8_rows(31, B, N, Lw, D, ks, vs)
+    q, q_bits = bf16_dev(synth.normal(31, synth.Q, (B, 1, H, D)))
+    pos = np.full((B, 1), p, np.int32)
+    win_pos0 = np.full((B,), p + 1 - Lw, np.int32)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = L.hca_attend_fp8kv(q, dev(kcb), dev(vcb), m, dev(kwb), dev(vwb), dev(win_pos0), W, dev(pos), scale,
+                                k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    o_r, lse_r = method.hca_attend(codecs.decode_bf16(q_bits), kcd, vcd, m, kwd, vwd, win_pos0, W, pos, scale)
+    assert row_rel_err(host_bf16(o), o_r) <= 1e-2
+    assert lse_abs_err(lse.cpu().numpy(), lse_r) <= 1e-2
+
+
+def test_csa_decode_64k_fp8kv_all_rows():
+    """CSA decode over FP8 K|V rows: B = 4, 16,384 entries, 512 selected per query (a
+    seeded index set), 128-row FP8 window; every row against the oracle."""
+    B, N, k, H, D, Lw, W = 4, 16384, 512, 64, 512, 128, 128
+    ks, vs = 1.0, 0.55
+    p = 65535
+    (kcb, vcb, kwb, vwb), (kcd, vcd, kwd, vwd) = _fp8_rows(32, B, N, Lw, D, ks, vs)
+    idx = synth.sorted_unique_indices(32, synth.IDX, B, N, k).reshape(B, 1, k)
+    q, q_bits = bf16_dev(synth.normal(32, synth.Q, (B, 1, H, D)))
+    pos = np.full((B, 1), p, np.int32)
+    win_pos0 = np.full((B,), p + 1 - Lw, np.int32)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = L.csa_attend_fp8kv(q, dev(kcb), dev(vcb), dev(idx), dev(kwb), dev(vwb), dev(win_pos0), W, dev(pos),
+                                scale, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    o_r, lse_r = method.csa_attend(codecs.decode_bf16(q_bits), kcd, vcd, idx, kwd, vwd, win_pos0, W, pos, scale)
     assert row_rel_err(host_bf16(o), o_r) <= 1e-2
     assert lse_abs_err(lse.cpu().numpy(), lse_r) <= 1e-2
 
