@@ -69,16 +69,16 @@ KERNEL_BYTES = {
 # the counter's reading for a 256 MiB device copy (see profiles/).  An entry is used only
 # while the kernel source it was measured on is unchanged (sha256 of the file).
 MEASURED_TRAFFIC = {
-    "index_mfma_kernel": {"bytes_per_launch": 151655421,
+    "index_mfma_kernel": {"bytes_per_launch": 151656603,
         "source_sha256": "bb85e2553e8b40aaee74daba5d82dd63ef6f672a75d971535226ddb3d765f9e0"},
-    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 156009233,
-        "source_sha256": "bc335d945f2ccca9542a97fd0e8947c72eae5a994103d1bf9be308ee7d8e3ca4"},
-    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32819510,
-        "source_sha256": "bc335d945f2ccca9542a97fd0e8947c72eae5a994103d1bf9be308ee7d8e3ca4"},
-    "attend_fp8kv_kernel (HCA)": {"bytes_per_launch": 92188056,
-        "source_sha256": "bc335d945f2ccca9542a97fd0e8947c72eae5a994103d1bf9be308ee7d8e3ca4"},
-    "attend_fp8kv_kernel (CSA)": {"bytes_per_launch": 24548996,
-        "source_sha256": "bc335d945f2ccca9542a97fd0e8947c72eae5a994103d1bf9be308ee7d8e3ca4"},
+    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 156010948,
+        "source_sha256": "70f6f82cf977443e032eb622f9438877dd10b730a66cecdaba18dc3213cd70a5"},
+    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32821502,
+        "source_sha256": "70f6f82cf977443e032eb622f9438877dd10b730a66cecdaba18dc3213cd70a5"},
+    "attend_fp8kv_kernel (HCA)": {"bytes_per_launch": 92184807,
+        "source_sha256": "70f6f82cf977443e032eb622f9438877dd10b730a66cecdaba18dc3213cd70a5"},
+    "attend_fp8kv_kernel (CSA)": {"bytes_per_launch": 24549011,
+        "source_sha256": "70f6f82cf977443e032eb622f9438877dd10b730a66cecdaba18dc3213cd70a5"},
 }
 
 

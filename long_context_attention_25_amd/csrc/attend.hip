@@ -190,7 +190,7 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
   constexpr int STB = KTB + VTB;          // one stage: K tile then V tile
   __shared__ __attribute__((aligned(1024))) uint8_t ring[4 * STB];
   __shared__ int32_t list[kMaxCsaChunk];  // the split's index entries
-  __shared__ __attribute__((aligned(16))) uint8_t xchg[DS > 1 ? NT * 16 : 16];   // partial scores
+  __shared__ __attribute__((aligned(16))) uint8_t xchg[DS > 1 ? 2 * NT * 16 : 16];   // partial scores, 2 buffers
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
@@ -424,11 +424,13 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
 
   // Tile t lives in stage t % 4.  Tiles 0 and 1 are issued first; then every wave reads
   // its Q^T operands (head `head`, dims g*D/4 + 8c .. +7 for k-step c) from stages 2-3,
-  // and after a barrier tile 2 is issued.  Step t then waits for tile t (tiles t+1, t+2
-  // stay in flight), passes a barrier (tile t visible to all waves; every wave is done
-  // with tile t-1), uses tile t and then issues tile t+3 into the stage of tile t-1 (after
-  // the tile's work, so that a wave held up by a full memory queue while issuing copies
-  // does not hold up the tile's scores and the barrier inside the step).
+  // and after a barrier tile 2 is issued.  The scores of tile 0 are computed before the
+  // loop; step t then waits for tile t+1 (tile t+2 stays in flight), passes one barrier
+  // (tile t+1 visible to all waves; tile t's partial scores written; every wave done with
+  // tile t-1), issues tile t+3 into the stage of tile t-1, sums tile t's partial scores,
+  // computes the partial scores of tile t+1 and accumulates tile t's outputs: two
+  // independent MFMA chains per step.  The partial scores alternate between two
+  // exchange buffers (tile t in buffer t % 2).
   uint32_t mq0 = 0, mq1 = 0, mq2 = 0;      // masks of tiles t, t+1, t+2
   if (spec) {
     bool same = true;
@@ -466,33 +468,43 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
   }
   tile_barrier();
   if (ntile > 2) { tile_ptrs(2); mq2 = vmask; issue(2); }
-  for (int t = 0; t < ntile; ++t) {
-    if (t + 2 < ntile) wait_vmcnt<2 * NL>();
-    else if (t + 1 < ntile) wait_vmcnt<NL>();
+  f32x4* xs = reinterpret_cast<f32x4*>(xchg);
+  f32x4 sc_next = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (ntile > 0) {
+    if (ntile > 2) wait_vmcnt<2 * NL>();
+    else if (ntile > 1) wait_vmcnt<NL>();
     else wait_vmcnt<0>();
     tile_barrier();
-    uint32_t mq3 = 0;
-    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (wave_on) sc = compute_s(t & 3);
-    if constexpr (DS > 1) {
-      // partial scores of the DS slices of a head group (waves hg + 4j), summed in the
-      // same order by every slice so that all of them see identical scores
-      f32x4* xs = reinterpret_cast<f32x4*>(xchg);
-      if (wave_on) xs[wave * kWave + lane] = sc;
-      tile_barrier();
-      if (wave_on) {
-        f32x4 tot = xs[hg * kWave + lane];
-#pragma unroll
-        for (int j = 1; j < DS; ++j) tot += xs[(hg + 4 * j) * kWave + lane];
-        sc = tot;
-      }
+    if (wave_on) {
+      sc_next = compute_s(0);
+      if constexpr (DS > 1) xs[wave * kWave + lane] = sc_next;
     }
-    if (wave_on) compute_pv(t & 3, mq0, sc);
+  }
+  for (int t = 0; t < ntile; ++t) {
+    if (t + 2 < ntile) wait_vmcnt<NL>();     // tile t+1 has landed (t+2 may be in flight)
+    else wait_vmcnt<0>();
+    tile_barrier();    // tile t+1 visible; tile t's partial scores written; tile t-1 done
+    uint32_t mq3 = 0;
     if (t + 3 < ntile) {
       tile_ptrs(t + 3);
       mq3 = vmask;
       issue((t + 3) & 3);
     }
+    f32x4 sc = sc_next;
+    if constexpr (DS > 1) {
+      if (wave_on) {
+        const f32x4* xb = xs + (t & 1) * NT;
+        f32x4 tot = xb[hg * kWave + lane];
+#pragma unroll
+        for (int j = 1; j < DS; ++j) tot += xb[(hg + 4 * j) * kWave + lane];
+        sc = tot;
+      }
+    }
+    if (wave_on && t + 1 < ntile) {
+      sc_next = compute_s((t + 1) & 3);
+      if constexpr (DS > 1) xs[((t + 1) & 1) * NT + wave * kWave + lane] = sc_next;
+    }
+    if (wave_on) compute_pv(t & 3, mq0, sc);
     mq0 = mq1;
     mq1 = mq2;
     mq2 = mq3;
