@@ -399,6 +399,48 @@ class HipEvents:
         return ms.value
 
 
+def measured_ceilings(torch):
+    """Rates this GPU reaches on kernels that do nothing else (libdsv4probe.so): a 2 GiB
+    streaming read with non-temporal loads (GB/s) and back-to-back dense MFMAs (TFLOP/s)
+    for bf16, fp8 (16x16x32 and the scaled 16x16x128 form) and fp4.  Context for the
+    roofline, whose peaks stay the published ones; None when the library is not built."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "long_context_attention_25_amd",
+                        "libdsv4probe.so")
+    if not os.path.exists(path):
+        return None
+    p = ctypes.CDLL(path)
+    p.dsv4probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    p.dsv4probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def timed(fn, reps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps / 1e3          # seconds per call
+
+    nbytes, blocks = 2 << 30, 512
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(1024 * 256, dtype=torch.float32, device="cuda")
+    s_read = timed(lambda: p.dsv4probe_read(ctypes.c_void_p(buf.data_ptr()), nbytes,
+                                            ctypes.c_void_p(sink.data_ptr()), blocks, st), 10)
+    del buf
+    res = {"hbm_read_gbs": round(nbytes / s_read / 1e9, 1), "mfma_tflops": {}}
+    iters, mblocks = 4000, 1024
+    for kind, name, flops in ((0, "bf16", 16 * 16 * 32 * 2), (1, "fp8 16x16x32", 16 * 16 * 32 * 2),
+                              (2, "fp8 16x16x128", 16 * 16 * 128 * 2), (3, "fp4 16x16x128", 16 * 16 * 128 * 2)):
+        sec = timed(lambda: p.dsv4probe_mfma(kind, iters, ctypes.c_void_p(sink.data_ptr()), mblocks, st), 10)
+        res["mfma_tflops"][name] = round(mblocks * 4 * iters * 8 * flops / sec / 1e12, 1)
+    torch.cuda.synchronize()
+    return res
+
+
 def run_step(lib, calls, arm=None):
     """One step; arm maps a call index to the (start, stop) events of its main kernel."""
     for i, (fn, args) in enumerate(calls):
@@ -647,6 +689,16 @@ def run_prefill(L, torch, synth, steps, warmup):
         L.csa_index_topk(qc.view(1, T, HI, DI // 2), t0["wi"], k4, qpos, M_CSA, PF_K, ki_scale=k4s,
                          qi_scale=qs.view(1, T, HI, DI // 32), out_idx=t0["idx"], workspace=ws.get("idx"))
     k_fp4 = time_index_kernel(L, torch, fp4_call, max(2, steps))
+    ceil = measured_ceilings(torch)
+    extra = {}
+    if ceil is not None:
+        mt = ceil["mfma_tflops"]
+        # the stack at the measured MFMA rates of the instructions it uses (fp8 16x16x32, bf16)
+        ideal_meas = 2 * (f_idx / mt["fp8 16x16x32"] + (f_csa + f_hca) / mt["bf16"]) / 1e9
+        extra["measured_ceilings"] = {"mfma_tflops": mt, "ideal_ms_at_measured": round(ideal_meas, 4),
+                                      "value_vs_measured": round(ideal_meas / ms, 4),
+                                      "note": "back-to-back MFMAs on this GPU; context only, value uses the "
+                                              "published peaks"}
     return {
         "metric": "chunked prefill MFMA utilisation (4-layer CSA/HCA stack, 4096-token chunk, 256K cache)",
         "value": round(ideal_ms / ms, 4), "unit": "fraction of dense MFMA peak", "n_gpus": 1, "steps": steps,
@@ -661,6 +713,7 @@ def run_prefill(L, torch, synth, steps, warmup):
                     "attend_bf16_kernel (HCA)": kern(f_hca, k_hca, "bf16")},
         "fp4_indexer": dict(kern(f_idx, k_fp4, "fp4"), note="the CSA layer's indexer with MXFP4 queries and keys "
                             "on the scaled FP4 MFMA (outside the stack timing)"),
+        **extra,
     }
 
 
@@ -785,6 +838,11 @@ def main():
             "kv_bytes_per_token": round(sum(counts[k] * kvb[k] for k in counts), 1),
             "note": "layers 0-1 HCA, 2-60 alternating CSA/HCA, MTP block window-only; each layer is one decode "
                     "step of this workload (new block pooled every step); caches rotate over the replicas"}
+    ceil = measured_ceilings(torch)
+    if ceil is not None:
+        out["measured_ceilings"] = dict(ceil, roofline_frac_of_read=round(k["achieved_gbs"] / ceil["hbm_read_gbs"], 4),
+                                        note="2 GiB streaming read (non-temporal loads) and back-to-back MFMAs on "
+                                             "this GPU; context only, the roofline uses the published peaks")
     if not args.no_cpu_baseline:
         done, el = cpu_baseline(L, torch, synth, wl, args.cpu_seconds)
         out["cpu_baseline"] = {"value": round(done / el, 3), "unit": "queries/s", "cores": 1, "kind": "oracle",

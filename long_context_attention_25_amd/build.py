@@ -14,6 +14,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsv4attn.so")
+# measurement helpers for bench.py (HBM streaming and MFMA throughput), a library of their own
+PROBE_SRC = os.path.join(HERE, "probe", "ceilings.hip")
+PROBE_LIB = os.path.join(HERE, "libdsv4probe.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -35,7 +38,7 @@ def _hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [os.path.join(CSRC, "abi.cpp")]
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [os.path.join(CSRC, "abi.cpp"), PROBE_SRC]
     objs = []
     build_dir = os.path.join(HERE, "_build")
     os.makedirs(build_dir, exist_ok=True)
@@ -60,10 +63,12 @@ def build(verbose: bool = False) -> str:
         for s, t in failed:
             sys.stderr.write(f"--- {s}\n{t}\n")
         raise RuntimeError(f"hipcc failed for {[os.path.basename(s) for s, _ in failed]}")
-    tmp = LIB + ".tmp"
-    cmd = [_hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    probe_obj = objs.pop()                   # the last source is the probe library's
+    for lib, parts in ((LIB, objs), (PROBE_LIB, [probe_obj])):
+        tmp = lib + ".tmp"
+        cmd = [_hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *parts]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, lib)
     return LIB
 
 
