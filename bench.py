@@ -69,15 +69,15 @@ KERNEL_BYTES = {
 # the counter's reading for a 256 MiB device copy (see profiles/).  An entry is used only
 # while the kernel source it was measured on is unchanged (sha256 of the file).
 MEASURED_TRAFFIC = {
-    "index_mfma_kernel": {"bytes_per_launch": 151656603,
-        "source_sha256": "bb85e2553e8b40aaee74daba5d82dd63ef6f672a75d971535226ddb3d765f9e0"},
-    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 156010948,
+    "index_mfma_kernel": {"bytes_per_launch": 151658877,
+        "source_sha256": "a9e2d06f1a8e4a01072e6b60e0ad35ffaa8cd0676b38c02896618181bb9162a6"},
+    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 156011080,
         "source_sha256": "70f6f82cf977443e032eb622f9438877dd10b730a66cecdaba18dc3213cd70a5"},
-    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32821502,
+    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32821525,
         "source_sha256": "70f6f82cf977443e032eb622f9438877dd10b730a66cecdaba18dc3213cd70a5"},
-    "attend_fp8kv_kernel (HCA)": {"bytes_per_launch": 92184807,
+    "attend_fp8kv_kernel (HCA)": {"bytes_per_launch": 92184880,
         "source_sha256": "70f6f82cf977443e032eb622f9438877dd10b730a66cecdaba18dc3213cd70a5"},
-    "attend_fp8kv_kernel (CSA)": {"bytes_per_launch": 24549011,
+    "attend_fp8kv_kernel (CSA)": {"bytes_per_launch": 24548974,
         "source_sha256": "70f6f82cf977443e032eb622f9438877dd10b730a66cecdaba18dc3213cd70a5"},
 }
 
@@ -693,8 +693,9 @@ def run_prefill(L, torch, synth, steps, warmup):
     extra = {}
     if ceil is not None:
         mt = ceil["mfma_tflops"]
-        # the stack at the measured MFMA rates of the instructions it uses (fp8 16x16x32, bf16)
-        ideal_meas = 2 * (f_idx / mt["fp8 16x16x32"] + (f_csa + f_hca) / mt["bf16"]) / 1e9
+        # the stack at the measured MFMA rates of the instructions it uses (the indexer's fp8
+        # keys on the scaled 16x16x128 form, attention on bf16 16x16x32 / 16x16x16)
+        ideal_meas = 2 * (f_idx / mt["fp8 16x16x128"] + (f_csa + f_hca) / mt["bf16"]) / 1e9
         extra["measured_ceilings"] = {"mfma_tflops": mt, "ideal_ms_at_measured": round(ideal_meas, 4),
                                       "value_vs_measured": round(ideal_meas / ms, 4),
                                       "note": "back-to-back MFMAs on this GPU; context only, value uses the "

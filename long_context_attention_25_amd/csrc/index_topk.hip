@@ -9,7 +9,8 @@
 // Decode path (few query rows, very long rows):
 //   1. index kernel: streams the keys once (bf16, fp8 e4m3 or MXFP4 decoded to bf16
 //      in registers) and computes the [heads x keys] dot products with MFMA
-//      (16 rows = QPT queries x HI heads, 16 keys per tile, K = 32 per step).  The
+//      (16 rows = QPT queries x HI heads, 16 keys per tile, K = 32 per step; fp8 keys
+//      with DI >= 128 and MXFP4 queries: the scaled MFMA, K = 128 per step).  The
 //      epilogue applies ReLU, the head weights and the head sum, writes the fp32
 //      scores and adds the top 12 bits of each score's order-preserving key into a
 //      per-row histogram (LDS histogram, then one global atomic per non-empty bin).
@@ -316,6 +317,22 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
               acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 4, 4, 0,
                                                                       (int)((qs4[t] >> (8 * c)) & 0xffu), 0,
                                                                       (int)((kt.sc >> (8 * c)) & 0xffu));
+            }
+          } else if constexpr (KIND == KEY_FP8 && DI >= 128) {
+            // fp8 x fp8 on the scaled 16x16x128 MFMA with unit scales (E8M0 127): the fp8
+            // 16x16x32 form runs at the bf16 rate on gfx950, this one at the fp8 rate.  A
+            // lane's 32 codes of 128-dim block c are its k-step words 4c .. 4c+3 (the same
+            // dims for the query and the key operand).
+#pragma unroll
+            for (int c = 0; c < DI / 128; ++c) {
+              const auto& kt = cur[u + j];
+              const uint2* qw = qa8[t] + 4 * c;
+              const v8i32 av = {(int)qw[0].x, (int)qw[0].y, (int)qw[1].x, (int)qw[1].y,
+                                (int)qw[2].x, (int)qw[2].y, (int)qw[3].x, (int)qw[3].y};
+              const v8i32 bv = {(int)kt.w[4 * c].x, (int)kt.w[4 * c].y, (int)kt.w[4 * c + 1].x,
+                                (int)kt.w[4 * c + 1].y, (int)kt.w[4 * c + 2].x, (int)kt.w[4 * c + 2].y,
+                                (int)kt.w[4 * c + 3].x, (int)kt.w[4 * c + 3].y};
+              acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 0, 0, 0, 127, 0, 127);
             }
           } else {
 #pragma unroll

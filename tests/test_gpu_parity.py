@@ -465,20 +465,26 @@ def test_index_topk_fp4_queries_and_keys(DI):
             assert np.all(np.abs(sc[b, q, :take] - ref) <= 1e-5 * np.abs(s_ref[b, q, :n]).max() + 1e-6)
 
 
-def test_index_topk_fp8():
-    cfg = 220
-    B, Q, HI, DI, N, m, k = 1, 4, 8, 128, 3000, 4, 300
+@pytest.mark.parametrize("HI,DI", [(8, 128), (16, 256), (4, 64)])
+def test_index_topk_fp8(HI, DI):
+    """fp8 queries and keys: DI >= 128 runs on the scaled 16x16x128 MFMA, DI = 64 on the
+    16x16x32 one.  Both sides read the oracle's e4m3 codes; the library's quantiser is
+    checked against the oracle's encoder separately."""
+    cfg = 220 + DI
+    B, Q, N, m, k = 1, 4, 3000, 4, 300
     q32 = synth.normal(cfg, synth.QI, (B, Q, HI, DI)) * np.float32(4)
     w = synth.uniform(cfg, synth.WI, (B, Q, HI))
     k32 = synth.normal(cfg, synth.KI, (B, N, DI)) * np.float32(4)
     pos = np.array([[4 * N - 1, 4 * N - 2, 5000, 40]], dtype=np.int32)
     zero1 = dev(np.zeros(1, np.float32))
+    qc, kc = codecs.encode_e4m3(q32), codecs.encode_e4m3(k32)
     q8 = L.csa_compress(dev(q32.reshape(1, -1, DI)), dev(np.zeros((1, B * Q * HI), np.float32)), zero1, 1,
                         torch.float8_e4m3fn).view(B, Q, HI, DI)
     k8 = L.csa_compress(dev(k32), dev(np.zeros((B, N), np.float32)), zero1, 1, torch.float8_e4m3fn)
-    qc, kc = codecs.encode_e4m3(q32), codecs.encode_e4m3(k32)
     assert np.array_equal(q8.view(torch.uint8).cpu().numpy(), qc)
-    idx = L.csa_index_topk(q8, dev(w), k8, dev(pos), m, k)
+    assert np.array_equal(k8.view(torch.uint8).cpu().numpy(), kc)
+    idx = L.csa_index_topk(dev(qc).view(torch.float8_e4m3fn), dev(w), dev(kc).view(torch.float8_e4m3fn), dev(pos),
+                           m, k)
     torch.cuda.synchronize()
     idx = idx.cpu().numpy()
     s_ref = _scores_oracle(codecs.decode_e4m3(qc), w, codecs.decode_e4m3(kc), pos, m)
