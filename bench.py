@@ -69,15 +69,15 @@ KERNEL_BYTES = {
 # the counter's reading for a 256 MiB device copy (see profiles/).  An entry is used only
 # while the kernel source it was measured on is unchanged (sha256 of the file).
 MEASURED_TRAFFIC = {
-    "index_mfma_kernel": {"bytes_per_launch": 151658877,
-        "source_sha256": "a9e2d06f1a8e4a01072e6b60e0ad35ffaa8cd0676b38c02896618181bb9162a6"},
-    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 156011080,
+    "index_mfma_kernel": {"bytes_per_launch": 151659132,
+        "source_sha256": "606dbfa84c58c10329103529516aaca6e87a1c3c89263a8d7e27e995ea466a2a"},
+    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 156011549,
         "source_sha256": "70f6f82cf977443e032eb622f9438877dd10b730a66cecdaba18dc3213cd70a5"},
-    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32821525,
+    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32821626,
         "source_sha256": "70f6f82cf977443e032eb622f9438877dd10b730a66cecdaba18dc3213cd70a5"},
-    "attend_fp8kv_kernel (HCA)": {"bytes_per_launch": 92184880,
+    "attend_fp8kv_kernel (HCA)": {"bytes_per_launch": 92185495,
         "source_sha256": "70f6f82cf977443e032eb622f9438877dd10b730a66cecdaba18dc3213cd70a5"},
-    "attend_fp8kv_kernel (CSA)": {"bytes_per_launch": 24548974,
+    "attend_fp8kv_kernel (CSA)": {"bytes_per_launch": 24548922,
         "source_sha256": "70f6f82cf977443e032eb622f9438877dd10b730a66cecdaba18dc3213cd70a5"},
 }
 

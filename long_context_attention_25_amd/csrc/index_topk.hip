@@ -431,18 +431,25 @@ __device__ __forceinline__ void threshold_bin(const uint32_t* __restrict__ hr, u
   __syncthreads();
 }
 
-// Selection, pass 1 (all rows x key ranges of kScanKeys): keys above the threshold bin
+// Selection, pass 1 (all rows x key ranges of KEYS keys): keys above the threshold bin
 // get their bit in the row's key bitmap (whole 32-bit words, plain stores); keys inside
 // the bin are appended to this range's own slice of the candidate buffer as composite
 // keys (score key << 32 | ~index: equal scores order the lower index first), and the
 // range's candidate count is stored.
 constexpr int kScanThreads = 256;
-constexpr int kScanKeys = 2048;                              // 2 float4 loads per thread
+constexpr int kScanKeys = 2048;                              // range of few-row calls: 2 float4 per thread
+constexpr int kScanKeysMany = 8192;                          // range of calls with >= kManyRows rows
+constexpr int64_t kManyRows = 256;
+// Many rows (a prefill chunk) fill the GPU with long ranges, which read the row's histogram
+// for the threshold 4x less often per key; few long rows need the shorter ranges to have
+// enough workgroups.
+inline int64_t scan_keys(int64_t rows) { return rows >= kManyRows ? kScanKeysMany : kScanKeys; }
 constexpr int kFinThreads = 1024;
 constexpr int kLdsBitmapKeys = 1 << 18;                      // bitmap kept in LDS by pass 2
 constexpr int kCandCap = 4096;                               // candidates staged in LDS by pass 2
 constexpr int kRadixBits = 12;                               // digit width of pass 2's radix select
 
+template <int KEYS>
 __global__ __launch_bounds__(kScanThreads) void select_scan_kernel(
     const float* __restrict__ scores, const uint32_t* __restrict__ hist_g, uint32_t* __restrict__ bitmap_g,
     uint64_t* __restrict__ cand_g, uint32_t* __restrict__ ccount, uint32_t* __restrict__ thr,
@@ -453,7 +460,7 @@ __global__ __launch_bounds__(kScanThreads) void select_scan_kernel(
   const int64_t row = blockIdx.y;
   const uint32_t n = vis_blocks(q_pos, row, m, N);
   const uint32_t kk = (uint32_t)k < n ? (uint32_t)k : n;
-  const int64_t c0 = (int64_t)blockIdx.x * kScanKeys;
+  const int64_t c0 = (int64_t)blockIdx.x * KEYS;
   const int64_t nch = gridDim.x;
   if (kk == 0 || c0 >= (int64_t)n) {
     if (tid == 0) ccount[row * nch + blockIdx.x] = 0u;
@@ -461,8 +468,8 @@ __global__ __launch_bounds__(kScanThreads) void select_scan_kernel(
   }
   // issue the score loads first; the threshold is computed while they are in flight
   const float* sc = scores + row * sstride + c0;
-  const int64_t c1 = (c0 + kScanKeys < (int64_t)n ? c0 + kScanKeys : (int64_t)n) - c0;   // keys in range
-  constexpr int IT = kScanKeys / (4 * kScanThreads);
+  const int64_t c1 = (c0 + KEYS < (int64_t)n ? c0 + KEYS : (int64_t)n) - c0;   // keys in range
+  constexpr int IT = KEYS / (4 * kScanThreads);
   float4 v[IT];
 #pragma unroll
   for (int u = 0; u < IT; ++u) {
@@ -526,7 +533,7 @@ template <bool kLdsBits>
 __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
     const float* __restrict__ scores, uint32_t* __restrict__ bitmap_g, const uint64_t* __restrict__ cand_g,
     const uint32_t* __restrict__ ccount, const uint32_t* __restrict__ thr, const int32_t* __restrict__ q_pos,
-    int64_t N, int64_t sstride, int64_t words, int m, int k, int nch, int32_t* __restrict__ out_idx,
+    int64_t N, int64_t sstride, int64_t words, int m, int k, int nch, int64_t rkeys, int32_t* __restrict__ out_idx,
     float* __restrict__ out_score) {
   constexpr int NT = kFinThreads;
   constexpr int kBins = 1 << kRadixBits;
@@ -555,7 +562,7 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
     return;
   }
   // round 1: threshold, range counts (the first NT ranges), bitmap
-  const int nrange = (int)(((int64_t)n + kScanKeys - 1) / kScanKeys);
+  const int nrange = (int)(((int64_t)n + rkeys - 1) / rkeys);
   const uint2 th = *reinterpret_cast<const uint2*>(thr + row * 2);
   const uint32_t cnt0 = tid < nrange ? ccount[row * nch + tid] : 0u;
   if constexpr (kLdsBits) {
@@ -595,7 +602,7 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
         cnt = ccount[row * nch + r];
       }
     }
-    return cand_g[row * N + r * kScanKeys + (f - base)];
+    return cand_g[row * N + r * rkeys + (f - base)];
   };
   // round 2: candidates into LDS
   {
@@ -841,25 +848,30 @@ hipError_t launch_index_topk(const IndexArgs& a, const TopkWorkspace& ws, hipStr
   // selection: pass 1 over all rows x key ranges, pass 2 one workgroup per row
   if (a.N == 0) {
     hipLaunchKernelGGL(select_finish_kernel<true>, dim3((unsigned)R), dim3(kFinThreads), 0, st, ws.scores,
-                       ws.bitmap, ws.cand, ws.ccount, ws.thr, a.q_pos, a.N, (int64_t)0, (int64_t)0, a.m, a.k, 0, a.out_idx,
-                       a.out_score);
+                       ws.bitmap, ws.cand, ws.ccount, ws.thr, a.q_pos, a.N, (int64_t)0, (int64_t)0, a.m, a.k, 0,
+                       (int64_t)kScanKeys, a.out_idx, a.out_score);
     return hipGetLastError();
   }
   const int64_t words = ((a.N + 127) / 128) * 4;
   const int64_t sstride = ((a.N + 63) / 64) * 64;
-  const int64_t nch = (a.N + kScanKeys - 1) / kScanKeys;
-  hipLaunchKernelGGL(select_scan_kernel, dim3((unsigned)nch, (unsigned)R), dim3(kScanThreads), 0, st, ws.scores,
-                     ws.hist, ws.bitmap, ws.cand, ws.ccount, ws.thr, a.q_pos, a.N, sstride, words, a.m, a.k);
+  const int64_t rk = scan_keys(R);        // keys per range (the workspace holds counts for kScanKeys)
+  const int64_t nch = (a.N + rk - 1) / rk;
+  if (rk == kScanKeysMany)
+    hipLaunchKernelGGL(select_scan_kernel<kScanKeysMany>, dim3((unsigned)nch, (unsigned)R), dim3(kScanThreads), 0, st,
+                       ws.scores, ws.hist, ws.bitmap, ws.cand, ws.ccount, ws.thr, a.q_pos, a.N, sstride, words, a.m, a.k);
+  else
+    hipLaunchKernelGGL(select_scan_kernel<kScanKeys>, dim3((unsigned)nch, (unsigned)R), dim3(kScanThreads), 0, st,
+                       ws.scores, ws.hist, ws.bitmap, ws.cand, ws.ccount, ws.thr, a.q_pos, a.N, sstride, words, a.m, a.k);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.N <= kLdsBitmapKeys)
     hipLaunchKernelGGL(select_finish_kernel<true>, dim3((unsigned)R), dim3(kFinThreads), 0, st, ws.scores,
-                       ws.bitmap, ws.cand, ws.ccount, ws.thr, a.q_pos, a.N, sstride, words, a.m, a.k, (int)nch, a.out_idx,
-                       a.out_score);
+                       ws.bitmap, ws.cand, ws.ccount, ws.thr, a.q_pos, a.N, sstride, words, a.m, a.k, (int)nch, rk,
+                       a.out_idx, a.out_score);
   else
     hipLaunchKernelGGL(select_finish_kernel<false>, dim3((unsigned)R), dim3(kFinThreads), 0, st, ws.scores,
-                       ws.bitmap, ws.cand, ws.ccount, ws.thr, a.q_pos, a.N, sstride, words, a.m, a.k, (int)nch, a.out_idx,
-                       a.out_score);
+                       ws.bitmap, ws.cand, ws.ccount, ws.thr, a.q_pos, a.N, sstride, words, a.m, a.k, (int)nch, rk,
+                       a.out_idx, a.out_score);
   return hipGetLastError();
 }
 

@@ -544,6 +544,27 @@ def test_index_topk_many_queries(kind):
             assert check_topk(idx[b, q], s_ref[b, q], int(nvis[b, q]), k) <= 2
 
 
+def test_index_topk_many_rows_long_ranges():
+    """300 query rows (a prefill-sized call): the selection scans 8192-key ranges instead of
+    2048; ragged last range, per-query visibility, every row against the oracle."""
+    cfg = 265
+    B, Q, HI, DI, N, m, k = 1, 300, 4, 64, 20000, 4, 256
+    q32 = synth.normal(cfg, synth.QI, (B, Q, HI, DI))
+    w = synth.uniform(cfg, synth.WI, (B, Q, HI))
+    k32 = synth.normal(cfg, synth.KI, (B, N, DI))
+    pos = (np.arange(Q, dtype=np.int32).reshape(B, Q) * 263 + 4 * N - 300 * 263) % (4 * N + 9)
+    qd, qb = dev_bf16(q32)
+    kd, kb = dev_bf16(k32)
+    idx = L.csa_index_topk(qd, dev(w), kd, dev(pos), m, k)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    s_ref = _scores_oracle(codecs.decode_bf16(qb), w, codecs.decode_bf16(kb), pos, m)
+    nvis = method.visible_blocks(pos, m, N)
+    assert nvis.max() > 16384                                # rows with more than two long ranges
+    for q in range(Q):
+        assert check_topk(idx[0, q], s_ref[0, q], int(nvis[0, q]), k) <= 2
+
+
 @pytest.mark.parametrize("N", [10000, 300000])
 def test_index_topk_many_candidates(N):
     """All-zero scores put every key into the threshold bin: more candidates than the
