@@ -69,16 +69,16 @@ KERNEL_BYTES = {
 # the counter's reading for a 256 MiB device copy (see profiles/).  An entry is used only
 # while the kernel source it was measured on is unchanged (sha256 of the file).
 MEASURED_TRAFFIC = {
-    "index_mfma_kernel": {"bytes_per_launch": 151659132,
-        "source_sha256": "606dbfa84c58c10329103529516aaca6e87a1c3c89263a8d7e27e995ea466a2a"},
-    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 156011549,
-        "source_sha256": "70f6f82cf977443e032eb622f9438877dd10b730a66cecdaba18dc3213cd70a5"},
-    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32821626,
-        "source_sha256": "70f6f82cf977443e032eb622f9438877dd10b730a66cecdaba18dc3213cd70a5"},
-    "attend_fp8kv_kernel (HCA)": {"bytes_per_launch": 92185495,
-        "source_sha256": "70f6f82cf977443e032eb622f9438877dd10b730a66cecdaba18dc3213cd70a5"},
-    "attend_fp8kv_kernel (CSA)": {"bytes_per_launch": 24548922,
-        "source_sha256": "70f6f82cf977443e032eb622f9438877dd10b730a66cecdaba18dc3213cd70a5"},
+    "index_mfma_kernel": {"bytes_per_launch": 151664529,
+        "source_sha256": "160c654eb902a5e6f1a43413f3e8bc75d70185df51c1e1227fec438324c4f3da"},
+    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 156014907,
+        "source_sha256": "e8faa5bea47fbc91d42ca5dd2c1ae3b4a62bcfe17750be5d6e5053a89dc7efc6"},
+    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32825577,
+        "source_sha256": "e8faa5bea47fbc91d42ca5dd2c1ae3b4a62bcfe17750be5d6e5053a89dc7efc6"},
+    "attend_fp8kv_kernel (HCA)": {"bytes_per_launch": 92169836,
+        "source_sha256": "e8faa5bea47fbc91d42ca5dd2c1ae3b4a62bcfe17750be5d6e5053a89dc7efc6"},
+    "attend_fp8kv_kernel (CSA)": {"bytes_per_launch": 24546821,
+        "source_sha256": "e8faa5bea47fbc91d42ca5dd2c1ae3b4a62bcfe17750be5d6e5053a89dc7efc6"},
 }
 
 

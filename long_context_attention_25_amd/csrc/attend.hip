@@ -377,8 +377,8 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
       s[i] = ok ? s[i] * sl2 : -INFINITY;
       mx = fmaxf(mx, s[i]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor16(mx);
+    mx = max_xor32(mx);
     const float m_new = fmaxf(m_run, mx);
     if (m_new > m_run + kLazyRescale) {
       if (m_run != -INFINITY) {
@@ -512,8 +512,8 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
   wait_vmcnt<0>();                           // no copy into LDS outlives the workgroup
 
   if (!wave_on) return;
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = add_xor16(l_run);
+  l_run = add_xor32(l_run);
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
   const float lse = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
   // the output row, or with several splits this split's partial row (bf16 like the
@@ -764,8 +764,8 @@ __global__ __launch_bounds__(kThreads * 2) void attend_fp8kv_kernel(AttendArgs a
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) mx = fmaxf(mx, s[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor16(mx);
+    mx = max_xor32(mx);
     const float m_new = fmaxf(m_run, mx);
     if (m_new > m_run + kLazyRescale) {
       if (m_run != -INFINITY) {
@@ -889,8 +889,8 @@ __global__ __launch_bounds__(kThreads * 2) void attend_fp8kv_kernel(AttendArgs a
   wait_vmcnt<0>();
 
   if (!wave_on) return;
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = add_xor16(l_run);
+  l_run = add_xor32(l_run);
   const float inv = l_run > 0.f ? a.v_scale / l_run : 0.f;
   const float lse = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
   const int64_t R = a.B * a.Q * a.H;
@@ -1107,8 +1107,8 @@ __global__ __launch_bounds__(kThreads * 2) void attend_bf16_pair_kernel(AttendAr
       s[i] = ok ? s[i] * sl2 : -INFINITY;
       mx = fmaxf(mx, s[i]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor16(mx);
+    mx = max_xor32(mx);
     const float m_new = fmaxf(m_run, mx);
     if (m_new > m_run + kLazyRescale) {
       if (m_run != -INFINITY) {
@@ -1195,8 +1195,8 @@ __global__ __launch_bounds__(kThreads * 2) void attend_bf16_pair_kernel(AttendAr
   if (!wave_on) return;
   const int64_t R = a.B * a.Q * a.H;
   auto finish = [&](int64_t bq, float m_run, float l_run, const f32x4* acc) {
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
+    l_run = add_xor16(l_run);
+    l_run = add_xor32(l_run);
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     const float lse = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
     const int64_t orow = bq * a.H + head;

@@ -60,6 +60,27 @@ __device__ __forceinline__ uint2 load_stream(const uint2* p) {
 }
 __device__ __forceinline__ uint32_t load_stream(const uint32_t* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ uint32_t load_stream(const uint8_t* p) { return __builtin_nontemporal_load(p); }
+// Butterfly steps across the 16-lane rows of a wave: the values of lanes l and l ^ 16
+// (l ^ 32) are exchanged by the gfx950 permlane swaps, a VALU operation, instead of a
+// shuffle routed through the LDS crossbar.  The swap returns the two values of a lane
+// pair in a lane-dependent order; their max or sum is the same in both lanes.
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <bool kNT> __device__ __forceinline__ uint4 load_key(const uint4* p) {
   if constexpr (kNT) return load_stream(p); else return *p;
 }

@@ -346,8 +346,8 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
           v = fmaf(wv[t][1], fmaxf(acc[1], 0.f), v);
           v = fmaf(wv[t][2], fmaxf(acc[2], 0.f), v);
           v = fmaf(wv[t][3], fmaxf(acc[3], 0.f), v);
-          if constexpr (GPQ >= 2) v += __shfl_xor(v, 16);
-          if constexpr (GPQ >= 4) v += __shfl_xor(v, 32);
+          if constexpr (GPQ >= 2) v = add_xor16(v);
+          if constexpr (GPQ >= 4) v = add_xor32(v);
           vs = (j == esel) ? v : vs;
         }
         const int64_t key = base + (u + esel) * 16 + col;
