@@ -504,7 +504,7 @@ __global__ __launch_bounds__(kScanThreads) void select_scan_kernel(
         const int leader = __ffsll((unsigned long long)mask) - 1;
         uint32_t base = 0;
         if (lane == leader) base = atomicAdd(&misc[2], (uint32_t)__popcll(mask));
-        base = __shfl(base, leader);
+        base = __builtin_amdgcn_readlane(base, leader);          // leader is the same in every lane
         if (isc) {
           const uint32_t f = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
@@ -512,11 +512,12 @@ __global__ __launch_bounds__(kScanThreads) void select_scan_kernel(
         }
       }
     }
-    // a bitmap word is the nibbles of 8 consecutive lanes
+    // a bitmap word is the nibbles of 8 consecutive lanes, OR-ed by DPP moves: lane ^ 1 and
+    // lane ^ 2 (quad permutes), then the mirrored lane of the other quad (row_half_mirror)
     uint32_t wv = nib << (4 * (lane & 7));
-    wv |= __shfl_xor(wv, 1);
-    wv |= __shfl_xor(wv, 2);
-    wv |= __shfl_xor(wv, 4);
+    wv |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)wv, 0xB1, 0xf, 0xf, false);    // quad_perm [1,0,3,2]
+    wv |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)wv, 0x4E, 0xf, 0xf, false);    // quad_perm [2,3,0,1]
+    wv |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)wv, 0x141, 0xf, 0xf, false);   // row_half_mirror
     if ((lane & 7) == 0 && kb < c1) bm[kb / 32] = wv;
   }
   __syncthreads();
