@@ -157,15 +157,27 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // ------------------------------------------------------------------ wave helpers
+// Wave-wide max / sum, the result in every lane: DPP moves inside each 16-lane row (lane ^ 1
+// and lane ^ 2 by quad permutes, then the mirrored lane of the other quad and of the other
+// half row), then the permlane swaps across rows; no step goes through the LDS crossbar.
+// Every step combines a lane pair symmetrically, so all lanes end with the same value.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = fmaxf(v, dpp_move<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_move<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_move<0x141>(v));   // row_half_mirror
+  v = fmaxf(v, dpp_move<0x140>(v));   // row_mirror
+  return max_xor32(max_xor16(v));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp_move<0xB1>(v);
+  v += dpp_move<0x4E>(v);
+  v += dpp_move<0x141>(v);
+  v += dpp_move<0x140>(v);
+  return add_xor32(add_xor16(v));
 }
 
 __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
