@@ -69,15 +69,15 @@ KERNEL_BYTES = {
 # the counter's reading for a 256 MiB device copy (see profiles/).  An entry is used only
 # while the kernel source it was measured on is unchanged (sha256 of the file).
 MEASURED_TRAFFIC = {
-    "index_mfma_kernel": {"bytes_per_launch": 151664572,
+    "index_mfma_kernel": {"bytes_per_launch": 151663851,
         "source_sha256": "55d724a43380e692b8fdd09166fe964408e73df3df2e6f959fe9b18a52c0fdc1"},
-    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 156015511,
+    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 156023635,
         "source_sha256": "e8faa5bea47fbc91d42ca5dd2c1ae3b4a62bcfe17750be5d6e5053a89dc7efc6"},
-    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32825674,
+    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32833858,
         "source_sha256": "e8faa5bea47fbc91d42ca5dd2c1ae3b4a62bcfe17750be5d6e5053a89dc7efc6"},
-    "attend_fp8kv_kernel (HCA)": {"bytes_per_launch": 92171203,
+    "attend_fp8kv_kernel (HCA)": {"bytes_per_launch": 92170360,
         "source_sha256": "e8faa5bea47fbc91d42ca5dd2c1ae3b4a62bcfe17750be5d6e5053a89dc7efc6"},
-    "attend_fp8kv_kernel (CSA)": {"bytes_per_launch": 24547142,
+    "attend_fp8kv_kernel (CSA)": {"bytes_per_launch": 24536691,
         "source_sha256": "e8faa5bea47fbc91d42ca5dd2c1ae3b4a62bcfe17750be5d6e5053a89dc7efc6"},
 }
 
