@@ -213,3 +213,14 @@ def test_lse_merge_validation():
     assert lib.lse_merge(P, P, 2, 4, 6, P, 0, P, None) == 1
     assert lib.lse_merge(P, P, 2, 4, 8, P, 2, P, None) == 2
     assert lib.lse_merge(P, P, 2, 0, 8, P, 0, P, None) == 0
+
+
+def test_ceiling_probe_library_exports():
+    """The benchmark's measurement helpers (HBM-read and MFMA-throughput kernels) build into a
+    library of their own that exports its two entry points; nothing is launched here."""
+    path = os.path.join(os.path.dirname(L.LIB_PATH), "libdsv4probe.so")
+    if not os.path.exists(path):
+        pytest.skip("probe library not built")
+    probe = ctypes.CDLL(path)
+    for name in ("dsv4probe_read", "dsv4probe_mfma"):
+        assert hasattr(probe, name), name
