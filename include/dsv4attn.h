@@ -283,7 +283,12 @@ dsv4_status hca_attend_fp8kv(const void* q, const void* kc, const void* vc, int3
 /*
  * lse_merge — combine attention results over P disjoint key sets (e.g. the compressed
  * part and the window part, or the shards of a split key range) into the result over
- * their union:
+ * their union.  Source: the pages describe no merge step; they only say that the
+ * compressed memory and the recent raw window are used together ([CSA], [P2 §4]).  The
+ * merge comes from the workload definition instead (the 1M-context HCA decode combines
+ * its compressed branch and its window branch with it), and it is exact: one softmax over
+ * the union of the key sets equals the log-sum-exp merge of the softmaxes over its parts.
+ *
  *   M = max_p lse_p;  lse = M + log sum_p exp(lse_p - M);  o = sum_p exp(lse_p - lse) o_p
  *   (a part with lse = -inf is empty; all parts empty -> o = 0, lse = -inf).
  *

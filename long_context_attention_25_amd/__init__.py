@@ -88,6 +88,13 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+def _contig(**tensors) -> None:
+    """The kernels read these tensors as packed row-major arrays."""
+    for name, t in tensors.items():
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
 def _dt(t) -> int:
     if t.dtype == torch.float32:
         return F32
@@ -206,6 +213,14 @@ def csa_index_topk(qi, wi, ki, q_pos, m: int, k: int, ki_scale=None, N=None, wit
         if (qi_scale is None or not qi.is_contiguous() or not qi_scale.is_contiguous()
                 or qi_scale.data_ptr() != qi.data_ptr() + qi.numel()):
             raise ValueError("MXFP4 queries: qi_scale must follow the codes qi in the same allocation")
+    _contig(qi=qi, wi=wi, q_pos=q_pos, qi_scale=qi_scale, out_idx=out_idx, out_score=out_score)
+    packed = {torch.float32: DI, torch.bfloat16: DI, torch.float8_e4m3fn: DI, torch.uint8: DI // 2}.get(ki.dtype)
+    if ki.dim() != 3 or ki.stride(2) != 1 or ki.stride(1) != packed:
+        raise ValueError("ki rows must be packed: [B, rows, DI] (MXFP4: [B, rows, DI/2] bytes) with unit strides "
+                         "inside a row")
+    if ki_scale is not None and (ki_scale.stride(2) != 1 or ki_scale.stride(1) != DI // 32
+                                 or ki_scale.stride(0) // ki_scale.stride(1) != ki.stride(0) // ki.stride(1)):
+        raise ValueError("ki_scale rows must be packed [B, rows, DI/32] with the batch stride of ki")
     rows = ki.shape[1]
     N = rows if N is None else N
     kdt = _dt(ki)
@@ -226,6 +241,7 @@ def _attend_common(q, kc, vc, kw, vw, win_pos0, q_pos, N):
     side by side in one [.., 2D] buffer), the last dimension must be contiguous."""
     B, Q, H, D = q.shape
     N = kc.shape[1] if N is None else N
+    _contig(q=q, q_pos=q_pos, win_pos0=win_pos0)
     if kc.stride(-1) != 1 or kw.stride(-1) != 1 or kc.stride() != vc.stride() or kw.stride() != vw.stride():
         raise ValueError("kc/vc and kw/vw must share strides and have a contiguous last dimension")
     kv_rs, w_rs = kc.stride(1), kw.stride(1)
@@ -243,6 +259,7 @@ def csa_attend(q, kc, vc, idx, kw, vw, win_pos0, W: int, q_pos, scale: float, N=
     B, Q, H, D, N, kv_bs, L, kv_rs, w_rs = _attend_common(q, kc, vc, kw, vw, win_pos0, q_pos, N)
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, Q, H), dtype=torch.float32, device=q.device) if lse is None else lse
+    _contig(idx=idx, out=out, lse=lse)
     args = (_ptr(q), _ptr(kc), _ptr(vc), _dt(q), _ptr(idx), idx.shape[2], _ptr(kw), _ptr(vw), _ptr(win_pos0), L, W,
             _ptr(q_pos), B, Q, H, D, N, kv_bs, kv_rs, w_rs, float(scale), _ptr(out), _ptr(lse))
     ws, n = _workspace(lambda n: lib().csa_attend(*args, None, ctypes.byref(n), _stream()), workspace)
@@ -256,6 +273,7 @@ def hca_attend(q, kc, vc, m: int, kw, vw, win_pos0, W: int, q_pos, scale: float,
     B, Q, H, D, N, kv_bs, L, kv_rs, w_rs = _attend_common(q, kc, vc, kw, vw, win_pos0, q_pos, N)
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, Q, H), dtype=torch.float32, device=q.device) if lse is None else lse
+    _contig(out=out, lse=lse)
     args = (_ptr(q), _ptr(kc), _ptr(vc), _dt(q), m, _ptr(kw), _ptr(vw), _ptr(win_pos0), L, W, _ptr(q_pos), B, Q, H,
             D, N, kv_bs, kv_rs, w_rs, float(scale), _ptr(out), _ptr(lse))
     ws, n = _workspace(lambda n: lib().hca_attend(*args, None, ctypes.byref(n), _stream()), workspace)
@@ -269,6 +287,7 @@ def _fp8kv_common(q, kc, vc, kw, vw, N, d_rope):
     tensor (natural strides) or sharing one row stride (e.g. K and V side by side)."""
     B, Q, H, D = q.shape
     N = kc.shape[1] if N is None else N
+    _contig(q=q)
     for t in (kc, vc, kw, vw):
         if t.dtype != torch.uint8 or t.stride(-1) != 1:
             raise ValueError("FP8 K/V rows are uint8 tensors with a contiguous last dimension")
@@ -303,6 +322,7 @@ def csa_attend_fp8kv(q, kc, vc, idx, kw, vw, win_pos0, W: int, q_pos, scale: flo
     B, Q, H, D, N, kv_bs, L, kv_rs, w_rs = _fp8kv_common(q, kc, vc, kw, vw, N, d_rope)
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, Q, H), dtype=torch.float32, device=q.device) if lse is None else lse
+    _contig(idx=idx, q_pos=q_pos, win_pos0=win_pos0, out=out, lse=lse)
     args = (_ptr(q), _ptr(kc), _ptr(vc), _ptr(idx), idx.shape[2], _ptr(kw), _ptr(vw), _ptr(win_pos0), L, W,
             _ptr(q_pos), B, Q, H, D, d_rope, N, kv_bs, kv_rs, w_rs, float(k_scale), float(v_scale), float(scale),
             _ptr(out), _ptr(lse))
@@ -317,6 +337,7 @@ def hca_attend_fp8kv(q, kc, vc, m: int, kw, vw, win_pos0, W: int, q_pos, scale: 
     B, Q, H, D, N, kv_bs, L, kv_rs, w_rs = _fp8kv_common(q, kc, vc, kw, vw, N, d_rope)
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, Q, H), dtype=torch.float32, device=q.device) if lse is None else lse
+    _contig(q_pos=q_pos, win_pos0=win_pos0, out=out, lse=lse)
     args = (_ptr(q), _ptr(kc), _ptr(vc), m, _ptr(kw), _ptr(vw), _ptr(win_pos0), L, W, _ptr(q_pos), B, Q, H, D,
             d_rope, N, kv_bs, kv_rs, w_rs, float(k_scale), float(v_scale), float(scale), _ptr(out), _ptr(lse))
     ws, n = _workspace(lambda n: lib().hca_attend_fp8kv(*args, None, ctypes.byref(n), _stream()), workspace)
@@ -329,5 +350,6 @@ def lse_merge(o_parts, lse_parts, out_dtype=torch.float32, out=None, lse_out=Non
     P, R, D = o_parts.shape
     out = torch.empty((R, D), dtype=out_dtype, device=o_parts.device) if out is None else out
     lse_out = torch.empty((R,), dtype=torch.float32, device=o_parts.device) if lse_out is None else lse_out
+    _contig(o_parts=o_parts, lse_parts=lse_parts, out=out, lse_out=lse_out)
     _check(lib().lse_merge(_ptr(o_parts), _ptr(lse_parts), P, R, D, _ptr(out), _dt(out), _ptr(lse_out), _stream()))
     return out, lse_out

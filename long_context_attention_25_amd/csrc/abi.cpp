@@ -197,6 +197,9 @@ void to_args_fp8(dsv4::AttendArgs& a, const AttendCommon& c, const Fp8Kv& f) {
 
 dsv4_status run_attend(const char* what, const dsv4::AttendArgs& a, void* ws, size_t* ws_bytes, hipStream_t st) {
   dsv4::AttendPlan p = dsv4::plan_attend(a);
+  if (!p.supported)
+    return fail(DSV4_ERR_UNSUPPORTED, "%s: the key list (k or N plus the window) needs more than 1024 splits "
+                "of the longest supported chunk; use a smaller window W", what);
   bool query;
   dsv4_status s = workspace_check(what, ws, ws_bytes, p.ws_bytes, &query);
   if (s != DSV4_OK || query) return s;

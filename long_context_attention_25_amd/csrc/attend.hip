@@ -36,6 +36,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTile = 32;            // split granularity: key ranges are multiples of 32 keys
 constexpr int kMaxCsaChunk = 2048;   // index entries of one CSA split (staged in LDS)
+constexpr int64_t kMaxSplits = 1024;  // key-range splits per query (part weights held by the merge)
 constexpr int kTargetWorkgroups = 256;   // gfx950: 256 CUs, one attention workgroup each
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -1490,6 +1491,15 @@ AttendPlan plan_attend(const AttendArgs& a) {
   if (a.csa && chunk > kMaxCsaChunk) chunk = kMaxCsaChunk;
   if (a.f8 && a.csa && chunk > kListF8) chunk = kListF8;
   int64_t splits = (n_max + chunk - 1) / chunk;
+  if (splits > kMaxSplits) {              // the merge holds at most kMaxSplits part weights
+    chunk = ((n_max + kMaxSplits - 1) / kMaxSplits + kTile - 1) / kTile * kTile;
+    const int64_t cap = a.csa ? (a.f8 ? kListF8 : kMaxCsaChunk) : ((int64_t)1 << 30);
+    if (chunk > cap) {
+      p.supported = false;
+      return p;
+    }
+    splits = (n_max + chunk - 1) / chunk;
+  }
   p.splits = (int)splits;
   p.chunk = (int)chunk;
   if (splits > 1) {

@@ -562,10 +562,20 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
     }
     return;
   }
-  // round 1: threshold, range counts (the first NT ranges), bitmap
+  // round 1: threshold, range counts (the first NT ranges), bitmap.  Every value read back
+  // from the workspace is clamped to what pass 1 can have written (a range holds at most
+  // its own keys; the count above the threshold bin is below kk), so that a wrong value
+  // can only give a wrong selection, never an access outside the row's slices.
   const int nrange = (int)(((int64_t)n + rkeys - 1) / rkeys);
-  const uint2 th = *reinterpret_cast<const uint2*>(thr + row * 2);
-  const uint32_t cnt0 = tid < nrange ? ccount[row * nch + tid] : 0u;
+  auto range_count = [&](int64_t r) -> uint32_t {
+    const uint32_t c_ = ccount[row * nch + r];
+    const int64_t keys = (int64_t)n - r * rkeys < rkeys ? (int64_t)n - r * rkeys : rkeys;
+    return c_ < (uint64_t)keys ? c_ : (uint32_t)keys;
+  };
+  uint2 th = *reinterpret_cast<const uint2*>(thr + row * 2);
+  th.x &= kHistBins - 1;
+  if (th.y > kk) th.y = kk;
+  const uint32_t cnt0 = tid < nrange ? range_count(tid) : 0u;
   if constexpr (kLdsBits) {
     for (int64_t w = (int64_t)tid * 4; w < wn; w += (int64_t)NT * 4) {
       const uint4 x = *reinterpret_cast<const uint4*>(gbits + w);   // rows are 16-byte padded
@@ -575,7 +585,7 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
   // candidate offsets per range (more than NT ranges are summed in rounds)
   uint32_t run = 0;
   for (int r0 = 0; r0 < nrange; r0 += NT) {
-    const uint32_t cnt = r0 == 0 ? cnt0 : (r0 + tid < nrange ? ccount[row * nch + r0 + tid] : 0u);
+    const uint32_t cnt = r0 == 0 ? cnt0 : (r0 + tid < nrange ? range_count(r0 + tid) : 0u);
     uint32_t tot;
     const uint32_t ex = block_scan<NT>(cnt, tmp, &tot);
     if (r0 + tid < nrange && r0 + tid < NT) pre[r0 + tid] = run + ex;
@@ -596,13 +606,14 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
     uint32_t base = pre[lo];
     int64_t r = lo;
     if (r == NT - 1 && nrange > NT) {                         // rare: very long rows
-      uint32_t cnt = ccount[row * nch + r];
-      while (f >= base + cnt) {
+      uint32_t cnt = range_count(r);
+      while (f >= base + cnt && r + 1 < nrange) {
         base += cnt;
         ++r;
-        cnt = ccount[row * nch + r];
+        cnt = range_count(r);
       }
     }
+    // f < c = the sum of the clamped counts, so f - base lies inside range r's slice
     return cand_g[row * N + r * rkeys + (f - base)];
   };
   // round 2: candidates into LDS
@@ -676,10 +687,8 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
   uint32_t* bits = kLdsBits ? bits_l : gbits;
   for (uint32_t f = tid; f < c; f += NT) {
     const uint64_t comp = cand(f);
-    if (comp >= tsel) {
-      const uint32_t j = ~(uint32_t)comp;
-      atomicOr(&bits[j >> 5], 1u << (j & 31));
-    }
+    const uint32_t j = ~(uint32_t)comp;
+    if (comp >= tsel && j < n) atomicOr(&bits[j >> 5], 1u << (j & 31));
   }
   __threadfence_block();
   __syncthreads();
@@ -742,8 +751,9 @@ hipError_t launch_mfma_q(const IndexArgs& a, float* scores, uint32_t* hist, int6
   chunk = ((chunk + KPS - 1) / KPS) * KPS;
   if (chunk < KPS) chunk = KPS;
   dim3 grid((unsigned)((a.N + chunk - 1) / chunk), (unsigned)(a.B * QG));
-  const int64_t slots = (int64_t)QTW * QPT < a.Q ? (int64_t)QTW * QPT : a.Q;
-  size_t smem = (size_t)slots * kHistWords * sizeof(uint32_t);
+  // the kernel clears and uses QPT histogram slots for each of its non-empty query tiles
+  const int64_t tiles = QTW < QT ? QTW : QT;
+  const size_t smem = (size_t)(tiles * QPT) * kHistWords * sizeof(uint32_t);
   // one query group per sequence: every key is read by one workgroup of the call, so the
   // keys are streamed with the non-temporal hint; with several groups the caches serve the
   // repeated reads (multi-query calls always run with QTW > 1 or several groups)
@@ -760,10 +770,12 @@ hipError_t launch_mfma_q(const IndexArgs& a, float* scores, uint32_t* hist, int6
 
 template <int KIND, int DI>
 hipError_t launch_mfma_di(const IndexArgs& a, float* scores, uint32_t* hist, int64_t chunk, hipStream_t st) {
-  // many queries (a prefill chunk): 4 query tiles (8 queries) per workgroup at the common
-  // indexer shape; otherwise one query tile
+  // many queries per sequence (a prefill chunk): 4 query tiles (8 queries of one sequence)
+  // per workgroup at the common indexer shape, so that every key tile feeds 4 MFMA row
+  // blocks; a decode call (few queries per sequence, any batch) keeps one query tile and
+  // streams its keys once
   if constexpr (DI == 128) {
-    if (a.HI == 8 && a.B * a.Q >= 64) return launch_mfma_q<KIND, DI, 8, 4>(a, scores, hist, chunk, st);
+    if (a.HI == 8 && a.Q >= 8 && a.B * a.Q >= 64) return launch_mfma_q<KIND, DI, 8, 4>(a, scores, hist, chunk, st);
   }
   switch (a.HI) {
     case 4: return launch_mfma_q<KIND, DI, 4, 1>(a, scores, hist, chunk, st);

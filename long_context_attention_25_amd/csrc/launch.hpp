@@ -124,6 +124,7 @@ struct AttendPlan {
   int splits;           // key-range splits per (b, q)
   int chunk;            // keys per split (multiple of the key tile)
   size_t ws_bytes;
+  bool supported = true;   // false: the key list is too long for the split limits
 };
 AttendPlan plan_attend(const AttendArgs& a);
 hipError_t launch_attend(const AttendArgs& a, const AttendPlan& p, void* ws, hipStream_t st);

@@ -169,6 +169,18 @@ def test_attend_validation_and_workspace_query():
     assert _attend(wp0=None, W=256)[0] == 1 and b"ring" in L.lib().dsv4_last_error()
 
 
+def test_attend_split_count_stays_within_the_merge_limit():
+    """The split-K merge holds at most 1024 part weights: a key list longer than 1024 splits
+    of the longest CSA chunk is rejected before any launch; a dense (HCA) list of any length
+    is planned with longer splits instead."""
+    win = 3_000_000
+    st, _ = _attend(W=win, L=win)                                   # bf16 CSA: 2048-entry chunks
+    assert st == 2 and b"1024 splits" in L.lib().dsv4_last_error()
+    assert _attend_fp8(W=600_000, L=600_000)[0] == 2               # FP8 CSA: 512-entry chunks
+    st, n = _attend(csa=False, N=40_000_000, W=128, L=256)          # HCA: longer splits, accepted
+    assert st == 0 and n > 0
+    assert _attend(W=1_000_000, L=1_000_000)[0] == 0                 # within 1024 x 2048
+
 def _attend_fp8(csa=True, **kw):
     a = dict(q=P, kc=P, vc=P, idx=P, k=512, m=128, kw=P, vw=P, wp0=P, L=256, W=128, qpos=P, B=8, Q=1, H=64, D=512,
              dr=64, N=262144, kvbs=0, kvrs=0, wrs=0, ks=1.0, vs=1.0, scale=0.04, out=P, lse=P)
@@ -224,3 +236,34 @@ def test_ceiling_probe_library_exports():
     probe = ctypes.CDLL(path)
     for name in ("dsv4probe_read", "dsv4probe_mfma"):
         assert hasattr(probe, name), name
+
+
+def test_binding_rejects_strided_operands_before_any_call():
+    """The kernels read packed row-major arrays: the binding raises ValueError for views whose
+    rows are not packed (checked on host tensors, before the library is called)."""
+    B, Q, HI, DI, N = 2, 1, 8, 128, 64
+    qi = torch.zeros((B, Q, HI, DI), dtype=torch.bfloat16)
+    wi = torch.zeros((B, Q, HI))
+    qpos = torch.zeros((B, Q), dtype=torch.int32)
+    ki = torch.zeros((B, N, 2 * DI), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="ki rows"):
+        L.csa_index_topk(qi, wi, ki[..., :DI], qpos, 4, 16)          # column slice: rows not packed
+    with pytest.raises(ValueError, match="qi must be contiguous"):
+        L.csa_index_topk(torch.zeros((B, Q, HI, 2 * DI), dtype=torch.bfloat16)[..., :DI], wi,
+                         ki[..., :DI].contiguous(), qpos, 4, 16)
+    H, D, k = 16, 128, 8
+    q = torch.zeros((B, Q, H, D), dtype=torch.bfloat16)
+    kc = torch.zeros((B, N, D), dtype=torch.bfloat16)
+    kw = torch.zeros((B, 16, D), dtype=torch.bfloat16)
+    wp0 = torch.zeros(B, dtype=torch.int32)
+    idx = torch.zeros((B, Q, 2 * k), dtype=torch.int32)[..., ::2]
+    with pytest.raises(ValueError, match="idx must be contiguous"):
+        L.csa_attend(q, kc, kc, idx, kw, kw, wp0, 16, qpos, 0.1)
+    with pytest.raises(ValueError, match="q must be contiguous"):
+        L.hca_attend(torch.zeros((B, Q, H, 2 * D), dtype=torch.bfloat16)[..., :D], kc, kc, 4, kw, kw, wp0, 16,
+                     qpos, 0.1)
+    with pytest.raises(ValueError, match="out must be contiguous"):
+        L.hca_attend(q, kc, kc, 4, kw, kw, wp0, 16, qpos, 0.1, out=torch.zeros((B, Q, H, 2 * D),
+                                                                                dtype=torch.bfloat16)[..., :D])
+    with pytest.raises(ValueError, match="o_parts must be contiguous"):
+        L.lse_merge(torch.zeros((2, 8, 32))[..., :16], torch.zeros((2, 8)))
