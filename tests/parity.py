@@ -13,6 +13,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from oracle import codecs
+
 
 def row_rel_err(o, o_ref) -> float:
     o = np.asarray(o, dtype=np.float64)
@@ -52,3 +54,36 @@ def check_topk(idx_gpu: np.ndarray, s_ref: np.ndarray, n: int, k: int, tau_rel: 
     assert np.all(s[sel] >= s_star - tau), "a block clearly below the k-th score was chosen"
     ref = np.sort(order[:take])
     return int(np.sum(~np.isin(sel, ref)))   # tie-zone swaps (allowed)
+
+
+def check_mxfp4_rounding(codes, scales, y_ref, tol) -> None:
+    """MXFP4 codes [.., C/2] and E8M0 scales [.., C/32] written by a GPU quantiser, against
+    the oracle's values y_ref [.., C] and an error bound tol (per element, e.g. the fp32
+    accumulation bound of a pooling): each group's shared exponent must be the OCP MX rule's
+    exponent (floor(log2 amax) - 2, clamped to [-127, 127]; 0 for an all-zero group) of some
+    group maximum within tol of the oracle's, and each element an E2M1 rounding (nearest-even,
+    saturating at 6) at that exponent of some value within tol of y_ref.  With tol = 0 only
+    the oracle's own encoding passes."""
+    y = np.asarray(y_ref, np.float64)
+    C = y.shape[-1]
+    g = y.reshape(y.shape[:-1] + (C // 32, 32))
+    t = np.broadcast_to(np.asarray(tol, np.float64), y.shape).reshape(g.shape)
+    X = np.asarray(scales).astype(np.int64) - 127
+
+    def rule(amax):
+        with np.errstate(divide="ignore"):
+            e = np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2
+        return np.where(amax > 0, np.clip(e, -127, 127), 0).astype(np.int64)
+
+    a_lo = np.maximum(np.abs(g) - t, 0.0).max(axis=-1)
+    a_hi = (np.abs(g) + t).max(axis=-1)
+    lo = np.where(a_lo > 0, rule(a_lo), -127)
+    ok = ((X >= lo) & (X <= rule(a_hi))) | ((a_lo == 0) & (X == 0))
+    assert np.all(ok), "shared exponent outside the range the values allow"
+    step = np.ldexp(1.0, X)[..., None]
+
+    def q(v):                                   # E2M1 rounding at the group's exponent, as values
+        return codecs.decode_e2m1(codecs._e2m1_code(v / step)) * step
+
+    got = codecs.decode_mxfp4(codes, scales).reshape(g.shape)
+    assert np.all((got >= q(g - t)) & (got <= q(g + t))), "an element is not a rounding of its value"

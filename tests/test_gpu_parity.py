@@ -8,7 +8,7 @@ import torch
 
 import synth
 from oracle import codecs, method
-from tests.parity import check_topk, lse_abs_err, row_rel_err
+from tests.parity import check_mxfp4_rounding, check_topk, lse_abs_err, row_rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -337,6 +337,45 @@ def test_compress2_equals_two_compress_calls(fp8):
     assert torch.count_nonzero(y_a[:, :N - nb]) == 0 and torch.count_nonzero(y_a[:, N - nb:]) > 0
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_compress2_against_the_oracle(fp8):
+    """csa_compress2 (a CSA layer's K|V rows and indexer key pooled in one launch, the decode
+    step's pooling call) against the oracle's pooling of the same bytes: bf16 K|V within one
+    ulp plus the fp32 accumulation bound, FP8 K|V rows as valid E4M3 roundings with bf16 RoPE
+    dims, MXFP4 keys as valid roundings group by group; rows outside the written range stay
+    untouched."""
+    cfg = 111 + fp8
+    B, m, nb, C, C2, N = 3, 4, 24, 1024, 128, 60
+    T = nb * m
+    x32 = synth.normal(cfg, synth.RAW_K, (B, T, C)) * np.float32(2)
+    x2_32 = synth.normal(cfg, synth.RAW_KI, (B, T, C2)) * np.exp(synth.normal(cfg + 50, synth.RAW_KI, (B, T, 1)))
+    gate = synth.normal(cfg, synth.GATE, (B, T))
+    bias = synth.normal(cfg, synth.BIAS, (m,), std=0.1)
+    x, xbits = dev_bf16(x32)
+    x2, x2bits = dev_bf16(x2_32)
+    width = C + DR if fp8 else C
+    ydt = torch.uint8 if fp8 else torch.bfloat16
+    y = torch.zeros((B, N, width), dtype=ydt, device="cuda")
+    kc = torch.zeros((B, N, C2 // 2), dtype=torch.uint8, device="cuda")
+    ks = torch.zeros((B, N, C2 // 32), dtype=torch.uint8, device="cuda")
+    sc = dev(np.array([127 - 1, 127 + 1], dtype=np.uint8)) if fp8 else None
+    L.csa_compress2(x, x2, dev(gate), dev(bias), m, y[:, N - nb:], kc[:, N - nb:], ks[:, N - nb:], out_scale=sc,
+                    fp8_kv=fp8)
+    torch.cuda.synchronize()
+    x64, x2_64 = codecs.decode_bf16(xbits), codecs.decode_bf16(x2bits)
+    y_ref = method.compress(x64, gate, bias, m)
+    k_ref = method.compress(x2_64, gate, bias, m)
+    acc = compress_tol(x64, m, y_ref) - bf16_ulp(y_ref)            # the fp32 accumulation part
+    if fp8:
+        _check_fp8kv_rows(y[:, N - nb:].cpu().numpy(), y_ref, acc, ek=-1, ev=1)
+    else:
+        assert np.all(np.abs(host(y[:, N - nb:]) - y_ref) <= compress_tol(x64, m, y_ref))
+    acc2 = compress_tol(x2_64, m, k_ref) - bf16_ulp(k_ref)
+    check_mxfp4_rounding(kc[:, N - nb:].cpu().numpy(), ks[:, N - nb:].cpu().numpy(), k_ref, acc2)
+    for t in (y, kc, ks):
+        assert torch.count_nonzero(t[:, :N - nb]) == 0
+
+
 def test_fp8kv_rows_from_pooling_feed_the_attention():
     """Pooling into FP8 K|V rows (K|V side by side, row stride C + 64) and HCA attention over
     such a cache.  Parity: the GPU attends over the oracle's own pooled-and-encoded rows and
@@ -354,7 +393,9 @@ def test_fp8kv_rows_from_pooling_feed_the_attention():
                            codecs.encode_fp8_v_rows(y_ref[..., D:], 1.0)], axis=-1)     # the oracle's rows
     torch.cuda.synchronize()
     gpu_rows = kv_gpu.cpu().numpy()
-    assert (gpu_rows != rows).mean() < 1e-3                    # only rounding midpoints differ
+    x64 = codecs.decode_bf16(xbits)
+    y64 = method.compress(x64, gate, bias, m)
+    _check_fp8kv_rows(gpu_rows, y64, compress_tol(x64, m, y64) - bf16_ulp(y64))   # every code a valid rounding
     (_, _, kwb, vwb), (_, _, kwd, vwd) = _fp8_kv(cfg, B, 1, Lw, D, 1.0, 1.0)
     q = synth.normal(cfg, synth.Q, (B, Q, H, D))
     qd, qb = dev_bf16(q)
@@ -373,8 +414,10 @@ def test_fp8kv_rows_from_pooling_feed_the_attention():
     o_r, lse_r = method.hca_attend(codecs.decode_bf16(qb), kd, vd, m, kwd, vwd, win_pos0, W, pos, scale)
     assert row_rel_err(host(o), o_r) <= 1e-2
     assert lse_abs_err(host(lse), lse_r) <= 1e-2
-    assert row_rel_err(host(o2), host(o)) <= 1e-2
-    assert lse_abs_err(host(lse2), host(lse)) <= 1e-2
+    # end to end: the GPU's own pooled rows through the GPU attention, against the oracle's
+    # pooling, encoding and attention
+    assert row_rel_err(host(o2), o_r) <= 1e-2
+    assert lse_abs_err(host(lse2), lse_r) <= 1e-2
 
 
 # ============================================================ indexer + top-k
@@ -745,6 +788,17 @@ def test_attend_with_kv_side_by_side(dt):
     y_r = method.compress(raw[:, L_ - T:L_ - T + m], host(g_blk), host(bias), m)
     tol = compress_tol(raw[:, L_ - T:L_ - T + m], m, y_r) if dt == "bf16" else 1e-5 * np.abs(y_r).max()
     assert np.all(np.abs(kv_h[:, N - 1:N] - y_r) <= tol)
+    # the strided attention against the oracle over the same rows, with the oracle's own
+    # pooled entry in row N-1
+    kc_r, vc_r = kv_h[..., :D].copy(), kv_h[..., D:].copy()
+    kc_r[:, N - 1], vc_r[:, N - 1] = y_r[:, 0, :D], y_r[:, 0, D:]
+    kw_r, vw_r = raw[..., :D], raw[..., D:]
+    q_r = host(qd)
+    o_r, lse_r = method.csa_attend(q_r, kc_r, vc_r, idx, kw_r, vw_r, win_pos0, W, pos, scale)
+    h_r, hl_r = method.hca_attend(q_r, kc_r[:, :300], vc_r[:, :300], m, kw_r, vw_r, win_pos0, W, pos, scale)
+    tol_o = 1e-2 if dt == "bf16" else 1e-4
+    assert row_rel_err(host(o1), o_r) <= tol_o and lse_abs_err(host(lse1), lse_r) <= tol_o
+    assert row_rel_err(host(h1), h_r) <= tol_o and lse_abs_err(host(hl1), hl_r) <= tol_o
 
 
 @pytest.mark.parametrize("D,H", [(128, 16), (64, 4), (512, 2)])
