@@ -200,6 +200,22 @@ dsv4_status csa_index_topk(const void* qi, int qi_dt, const float* wi,
                            void* workspace, size_t* ws_bytes, hipStream_t stream);
 
 /*
+ * csa_index_topk_noalloc — csa_index_topk for callers that cannot allocate device memory
+ * or pass a workspace (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Arguments, results and errors are those of csa_index_topk, without
+ * the workspace pair.  The call allocates nothing: its scratch is a 48 MiB array owned by
+ * the library, one per device, held until the process ends and shared by every call on
+ * that device.  A call whose scratch need (the size csa_index_topk's workspace query
+ * reports) exceeds 48 MiB returns DSV4_ERR_UNSUPPORTED before any launch (the 1M-context
+ * decode, B = 8, N = 262,144, needs about 25 MiB).  Calls that overlap in time on one
+ * device race on the array: issue them on one stream, or order them.
+ */
+dsv4_status csa_index_topk_noalloc(const void* qi, int qi_dt, const float* wi, const void* ki,
+                                   const uint8_t* ki_scale, int ki_dt, const int32_t* q_pos, int64_t B, int64_t Q,
+                                   int32_t HI, int32_t DI, int64_t N, int64_t ki_bstride, int32_t m, int32_t k,
+                                   int32_t* out_idx, float* out_score, hipStream_t stream);
+
+/*
  * csa_attend — attention over the selected compressed entries plus the sliding
  * window, as ONE softmax over the union  [CSA], [P2 §4].
  *

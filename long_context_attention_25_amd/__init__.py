@@ -41,6 +41,8 @@ _SIGS = {
                          _i64, _p], ctypes.c_int),
     "csa_index_topk": ([_p, ctypes.c_int, _p, _p, _p, ctypes.c_int, _p, _i64, _i64, _i32, _i32, _i64, _i64, _i32,
                         _i32, _p, _p, _p, ctypes.POINTER(ctypes.c_size_t), _p], ctypes.c_int),
+    "csa_index_topk_noalloc": ([_p, ctypes.c_int, _p, _p, _p, ctypes.c_int, _p, _i64, _i64, _i32, _i32, _i64, _i64,
+                                _i32, _i32, _p, _p, _p], ctypes.c_int),
     "csa_attend": ([_p, _p, _p, ctypes.c_int, _p, _i32, _p, _p, _p, _i64, _i32, _p, _i64, _i64, _i32, _i32, _i64,
                     _i64, _i64, _i64, ctypes.c_float, _p, _p, _p, ctypes.POINTER(ctypes.c_size_t), _p], ctypes.c_int),
     "hca_attend": ([_p, _p, _p, ctypes.c_int, _i32, _p, _p, _p, _i64, _i32, _p, _i64, _i64, _i32, _i32, _i64, _i64,

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "dsv4attn.h"
 #include "launch.hpp"
@@ -13,6 +14,15 @@ namespace {
 
 thread_local char g_err[512] = "";
 thread_local hipEvent_t g_time_start = nullptr, g_time_stop = nullptr;
+
+// Scratch of csa_index_topk_noalloc: one array per device, held until the process ends.
+// In host code `scratch` is only a stand-in for the symbol; its device address comes from
+// hipGetSymbolAddress (per device, on the first call made with that device current).
+constexpr size_t kScratchBytes = (size_t)48 << 20;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
 
 dsv4_status fail(dsv4_status s, const char* fmt, ...) {
   va_list ap;
@@ -24,6 +34,25 @@ dsv4_status fail(dsv4_status s, const char* fmt, ...) {
 
 dsv4_status ok() {
   g_err[0] = '\0';
+  return DSV4_OK;
+}
+
+// Device address of this device's scratch array (looked up once per device).
+dsv4_status scratch_ptr(const char* what, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DSV4_ERR_LAUNCH, "%s: hipGetDevice failed: %s", what, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(DSV4_ERR_UNSUPPORTED, "%s: device %d out of range", what, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(DSV4_ERR_LAUNCH, "%s: hipGetSymbolAddress of the scratch array failed: %s", what,
+                  hipGetErrorString(e));
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
   return DSV4_OK;
 }
 
@@ -301,11 +330,17 @@ dsv4_status kv_cache_append(const void* x_new, int x_dt, const float* gate_new, 
   return launched(dsv4::launch_append(a, stream), what);
 }
 
-dsv4_status csa_index_topk(const void* qi, int qi_dt, const float* wi, const void* ki, const uint8_t* ki_scale,
-                           int ki_dt, const int32_t* q_pos, int64_t B, int64_t Q, int32_t HI, int32_t DI, int64_t N,
-                           int64_t ki_bstride, int32_t m, int32_t k, int32_t* out_idx, float* out_score,
-                           void* workspace, size_t* ws_bytes, hipStream_t stream) {
-  const char* what = "csa_index_topk";
+}  // extern "C"
+
+namespace {
+
+// csa_index_topk and its allocation-free variant.  noalloc: the workspace is the
+// library's static scratch array of this device (workspace and ws_bytes are ignored).
+dsv4_status index_topk_impl(const char* what, const void* qi, int qi_dt, const float* wi, const void* ki,
+                            const uint8_t* ki_scale, int ki_dt, const int32_t* q_pos, int64_t B, int64_t Q,
+                            int32_t HI, int32_t DI, int64_t N, int64_t ki_bstride, int32_t m, int32_t k,
+                            int32_t* out_idx, float* out_score, void* workspace, size_t* ws_bytes,
+                            hipStream_t stream, bool noalloc) {
   REQUIRE(B >= 0 && Q >= 0 && N >= 0, "%s: sizes must be non-negative", what);
   REQUIRE(m >= 1, "%s: m must be >= 1", what);
   REQUIRE(k >= 1 && k <= 4096, "%s: k must be in [1, 4096], got %d", what, k);
@@ -335,8 +370,20 @@ dsv4_status csa_index_topk(const void* qi, int qi_dt, const float* wi, const voi
     if (kind == dsv4::KEY_MXFP4 || kind == dsv4::KEY_MXFP4_Q4)
       REQUIRE(N == 0 || ki_scale, "%s: ki_scale must not be NULL for MXFP4", what);
   }
+  const size_t need = R > 0 ? dsv4::topk_workspace_bytes(R, N) : 0;
+  size_t scratch_size = 0;
+  if (noalloc) {
+    if (need > kScratchBytes)
+      return fail(DSV4_ERR_UNSUPPORTED, "%s: this call needs %zu bytes of scratch, more than the %zu bytes of the "
+                  "static scratch array; use csa_index_topk with a workspace", what, need, kScratchBytes);
+    if (R == 0) return ok();
+    dsv4_status st = scratch_ptr(what, &workspace);
+    if (st != DSV4_OK) return st;
+    scratch_size = kScratchBytes;
+    ws_bytes = &scratch_size;
+  }
   bool query;
-  dsv4_status s = workspace_check(what, workspace, ws_bytes, R > 0 ? dsv4::topk_workspace_bytes(R, N) : 0, &query);
+  dsv4_status s = workspace_check(what, workspace, ws_bytes, need, &query);
   if (s != DSV4_OK || query || R == 0) return s;
   dsv4::IndexArgs a;
   a.qi = qi; a.wi = wi; a.ki = ki; a.ki_scale = ki_scale; a.kind = kind; a.q_pos = q_pos;
@@ -345,6 +392,26 @@ dsv4_status csa_index_topk(const void* qi, int qi_dt, const float* wi, const voi
   a.B = B; a.Q = Q; a.HI = HI; a.DI = DI; a.N = N; a.k_bs = ki_bstride ? ki_bstride : N;
   a.m = m; a.k = k; a.out_idx = out_idx; a.out_score = out_score;
   return launched(dsv4::launch_index_topk(a, dsv4::topk_workspace_carve(workspace, R, N), stream), what);
+}
+
+}  // namespace
+
+extern "C" {
+
+dsv4_status csa_index_topk(const void* qi, int qi_dt, const float* wi, const void* ki, const uint8_t* ki_scale,
+                           int ki_dt, const int32_t* q_pos, int64_t B, int64_t Q, int32_t HI, int32_t DI, int64_t N,
+                           int64_t ki_bstride, int32_t m, int32_t k, int32_t* out_idx, float* out_score,
+                           void* workspace, size_t* ws_bytes, hipStream_t stream) {
+  return index_topk_impl("csa_index_topk", qi, qi_dt, wi, ki, ki_scale, ki_dt, q_pos, B, Q, HI, DI, N, ki_bstride, m,
+                         k, out_idx, out_score, workspace, ws_bytes, stream, false);
+}
+
+dsv4_status csa_index_topk_noalloc(const void* qi, int qi_dt, const float* wi, const void* ki,
+                                   const uint8_t* ki_scale, int ki_dt, const int32_t* q_pos, int64_t B, int64_t Q,
+                                   int32_t HI, int32_t DI, int64_t N, int64_t ki_bstride, int32_t m, int32_t k,
+                                   int32_t* out_idx, float* out_score, hipStream_t stream) {
+  return index_topk_impl("csa_index_topk_noalloc", qi, qi_dt, wi, ki, ki_scale, ki_dt, q_pos, B, Q, HI, DI, N,
+                         ki_bstride, m, k, out_idx, out_score, nullptr, nullptr, stream, true);
 }
 
 dsv4_status csa_attend(const void* q, const void* kc, const void* vc, int dt, const int32_t* idx, int32_t k,

@@ -267,3 +267,12 @@ def test_binding_rejects_strided_operands_before_any_call():
                                                                                 dtype=torch.bfloat16)[..., :D])
     with pytest.raises(ValueError, match="o_parts must be contiguous"):
         L.lse_merge(torch.zeros((2, 8, 32))[..., :16], torch.zeros((2, 8)))
+
+
+def test_noalloc_index_rejects_a_call_larger_than_its_scratch():
+    """csa_index_topk_noalloc refuses, before touching the device, a call whose scratch need
+    exceeds the library's 48 MiB array (here 2^28 keys of one query)."""
+    lib = L.lib()
+    st = lib.csa_index_topk_noalloc(P, 1, P, P, P, 3, P, 1, 1, 8, 128, 1 << 28, 0, 4, 64, P, None, None)
+    assert st == 2 and b"static scratch" in lib.dsv4_last_error()
+    assert lib.csa_index_topk_noalloc(P, 1, P, P, P, 3, P, 1, 1, 8, 128, 1000, 0, 4, 0, P, None, None) == 1
