@@ -207,7 +207,7 @@ dsv4_status csa_index_topk(const void* qi, int qi_dt, const float* wi,
  * the library, one per device, held until the process ends and shared by every call on
  * that device.  A call whose scratch need (the size csa_index_topk's workspace query
  * reports) exceeds 48 MiB returns DSV4_ERR_UNSUPPORTED before any launch (the 1M-context
- * decode, B = 8, N = 262,144, needs about 25 MiB).  Calls that overlap in time on one
+ * decode, B = 8, N = 262,144, needs about 9 MiB).  Calls that overlap in time on one
  * device race on the array: issue them on one stream, or order them.
  */
 dsv4_status csa_index_topk_noalloc(const void* qi, int qi_dt, const float* wi, const void* ki,

@@ -370,7 +370,13 @@ dsv4_status index_topk_impl(const char* what, const void* qi, int qi_dt, const f
     if (kind == dsv4::KEY_MXFP4 || kind == dsv4::KEY_MXFP4_Q4)
       REQUIRE(N == 0 || ki_scale, "%s: ki_scale must not be NULL for MXFP4", what);
   }
-  const size_t need = R > 0 ? dsv4::topk_workspace_bytes(R, N) : 0;
+  dsv4::IndexArgs a;
+  a.qi = qi; a.wi = wi; a.ki = ki; a.ki_scale = ki_scale; a.kind = kind; a.q_pos = q_pos;
+  // MXFP4 queries: the scale bytes follow the codes in the same allocation
+  a.qi_scale = kind == dsv4::KEY_MXFP4_Q4 ? reinterpret_cast<const uint8_t*>(qi) + R * HI * (DI / 2) : nullptr;
+  a.B = B; a.Q = Q; a.HI = HI; a.DI = DI; a.N = N; a.k_bs = ki_bstride ? ki_bstride : N;
+  a.m = m; a.k = k; a.out_idx = out_idx; a.out_score = out_score;
+  const size_t need = dsv4::topk_workspace_bytes(a);
   size_t scratch_size = 0;
   if (noalloc) {
     if (need > kScratchBytes)
@@ -385,13 +391,7 @@ dsv4_status index_topk_impl(const char* what, const void* qi, int qi_dt, const f
   bool query;
   dsv4_status s = workspace_check(what, workspace, ws_bytes, need, &query);
   if (s != DSV4_OK || query || R == 0) return s;
-  dsv4::IndexArgs a;
-  a.qi = qi; a.wi = wi; a.ki = ki; a.ki_scale = ki_scale; a.kind = kind; a.q_pos = q_pos;
-  // MXFP4 queries: the scale bytes follow the codes in the same allocation
-  a.qi_scale = kind == dsv4::KEY_MXFP4_Q4 ? reinterpret_cast<const uint8_t*>(qi) + R * HI * (DI / 2) : nullptr;
-  a.B = B; a.Q = Q; a.HI = HI; a.DI = DI; a.N = N; a.k_bs = ki_bstride ? ki_bstride : N;
-  a.m = m; a.k = k; a.out_idx = out_idx; a.out_score = out_score;
-  return launched(dsv4::launch_index_topk(a, dsv4::topk_workspace_carve(workspace, R, N), stream), what);
+  return launched(dsv4::launch_index_topk(a, workspace, stream), what);
 }
 
 }  // namespace

@@ -6,20 +6,25 @@
 // indexer picks the top-k compressed blocks per query).  Score of block j:
 //     s_j = sum_h w_h * max(0, q_h . k_j)            (j < floor((p+1)/m) only)
 //
-// Decode path (few query rows, very long rows):
-//   1. index kernel: streams the keys once (bf16, fp8 e4m3 or MXFP4 decoded to bf16
-//      in registers) and computes the [heads x keys] dot products with MFMA
-//      (16 rows = QPT queries x HI heads, 16 keys per tile, K = 32 per step; fp8 keys
-//      with DI >= 128 and MXFP4 queries: the scaled MFMA, K = 128 per step).  The
-//      epilogue applies ReLU, the head weights and the head sum, writes the fp32
-//      scores and adds the top 12 bits of each score's order-preserving key into a
-//      per-row histogram (LDS histogram, then one global atomic per non-empty bin).
-//   2. select kernel, one workgroup per row: finds the threshold bin of the row from the
-//      histogram, reads the row's scores once, marks the keys above the bin in an LDS
-//      bitmap and collects the keys inside the bin as candidates, radix-selects the
-//      remaining candidates by (score, lower index first), and compacts the bitmap into
-//      ascending indices.
-// The result is exact on the fp32 scores and independent of scheduling.
+// Index kernel (every call): streams the keys once (bf16, fp8 e4m3 or MXFP4 decoded to
+// bf16 in registers) and computes the [heads x keys] dot products with MFMA (16 rows =
+// QPT queries x HI heads, 16 keys per tile, K = 32 per step; fp8 keys with DI >= 128 and
+// MXFP4 queries: the scaled MFMA, K = 128 per step).  Its epilogue applies ReLU, the head
+// weights and the head sum, and counts the top 12 bits of each score's order-preserving
+// key in an LDS histogram.
+// Decode-shaped calls (one query tile per workgroup, N <= 2^18): two launches.
+//   1. the index kernel keeps its chunk's scores in LDS and ends with a local selection:
+//      the whole histogram bins holding the chunk's best keys (at most klocal of them)
+//      become the chunk's candidates; the scores go to the workspace;
+//   2. one workgroup per row selects the top-k among the chunks' candidates, widening the
+//      rare chunk that could hide more winners than it kept (select_local_kernel).
+// Other calls (many queries per sequence, fp32 keys, longer rows): four launches.
+//   0. the row histograms are cleared; 1. the index kernel adds its LDS histogram to them
+//   and writes the scores; 2. a chip-wide scan pass (rows x key ranges) marks the keys
+//   above each row's threshold bin in a bitmap and collects the keys inside it;
+//   3. one workgroup per row radix-selects those candidates and compacts the bitmap.
+// Either way the result is exact on the fp32 scores (ties to the lower index) and
+// independent of scheduling.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -57,11 +62,13 @@ constexpr int kHistWords = kHistBins / 2;
 constexpr int64_t kMaxIndexChunk = 32768;
 
 // Writes one score and counts it in the LDS histogram of its query slot.
+// kStore: the score goes to the global row here (else the caller stores it later).
+template <bool kStore = true>
 __device__ __forceinline__ void emit_score(float* scores, uint32_t* hist_l, int64_t row, int64_t sstride,
                                            int64_t N, int64_t key, uint32_t nvis, float v) {
   if (key >= N) return;
   bool vis = key < (int64_t)nvis;
-  scores[row * sstride + key] = vis ? v : -INFINITY;
+  if constexpr (kStore) scores[row * sstride + key] = vis ? v : -INFINITY;
   if (vis) {
     const uint32_t bin = score_key(v) >> (32 - kHistBits);
     atomicAdd(&hist_l[bin >> 1], 1u << ((bin & 1u) << 4));
@@ -73,6 +80,285 @@ __device__ __forceinline__ void flush_hist(const uint32_t* hist_l, uint32_t* his
     const uint32_t c = hist_l[w];
     if (c & 0xffffu) atomicAdd(&hist_g[row * kHistBins + 2 * w], c & 0xffffu);
     if (c >> 16) atomicAdd(&hist_g[row * kHistBins + 2 * w + 1], c >> 16);
+  }
+}
+
+// ------------------------------------------------------------------ block-wide helpers
+// Inclusive prefix sum over the 64 lanes of a wave: row shifts within each 16-lane row,
+// then the last lane of a row is broadcast into the following rows.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return v;
+}
+
+// Block-wide exclusive prefix sum for NT threads (NT / 64 waves); `tmp` holds NT / 64
+// words of LDS.  Returns the exclusive prefix and writes the total to *total.
+template <int NT>
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_incl_scan(v);
+  if (lane == 63) tmp[wave] = incl;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t x = tmp[w];
+    base += (w < wave) ? x : 0u;
+    tot += x;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + incl - v;
+}
+
+// Minimum of a 64-bit value over an NT-thread workgroup (tmp: 2 * NT / 64 words of LDS).
+template <int NT>
+__device__ __forceinline__ uint64_t block_min_u64(uint64_t v, uint32_t* tmp) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint64_t w = __shfl_xor(v, o);
+    v = w < v ? w : v;
+  }
+  if (lane == 0) {
+    tmp[2 * wave] = (uint32_t)v;
+    tmp[2 * wave + 1] = (uint32_t)(v >> 32);
+  }
+  __syncthreads();
+  uint64_t r = ~0ull;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint64_t x = ((uint64_t)tmp[2 * w + 1] << 32) | tmp[2 * w];
+    r = x < r ? x : r;
+  }
+  __syncthreads();
+  return r;
+}
+
+// Minimum and maximum of 64-bit values over an NT-thread workgroup in one exchange
+// (tmp: 4 * NT / 64 words of LDS).
+template <int NT>
+__device__ __forceinline__ void block_minmax_u64(uint64_t& mn, uint64_t& mx, uint32_t* tmp) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint64_t a = __shfl_xor(mn, o), b = __shfl_xor(mx, o);
+    mn = a < mn ? a : mn;
+    mx = b > mx ? b : mx;
+  }
+  if (lane == 0) {
+    tmp[4 * wave] = (uint32_t)mn;
+    tmp[4 * wave + 1] = (uint32_t)(mn >> 32);
+    tmp[4 * wave + 2] = (uint32_t)mx;
+    tmp[4 * wave + 3] = (uint32_t)(mx >> 32);
+  }
+  __syncthreads();
+  mn = ~0ull;
+  mx = 0ull;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint64_t a = ((uint64_t)tmp[4 * w + 1] << 32) | tmp[4 * w];
+    const uint64_t b = ((uint64_t)tmp[4 * w + 3] << 32) | tmp[4 * w + 2];
+    mn = a < mn ? a : mn;
+    mx = b > mx ? b : mx;
+  }
+  __syncthreads();
+}
+
+// Composite selection key: the score key in the high half and the complemented block
+// index in the low half, so that a larger composite is a larger score or, for equal
+// scores, a lower index; the composites of different blocks are distinct, and no real
+// score gives the composite 0 (which marks an empty slot).
+__device__ __forceinline__ uint64_t comp_key(float s, uint32_t j) {
+  return ((uint64_t)score_key(s) << 32) | (uint64_t)(~j);
+}
+
+constexpr int kRadixBits = 12;                               // digit width of the radix selections
+
+// The need-th largest of c distinct composites get(0) .. get(c-1) (1 <= need <= the number
+// of nonzero ones): radix selection from the top bit down, kRadixBits per round, over an LDS
+// histogram (hbin: 1 << kRadixBits words; tmp: 2 NT / 64 words; misc: 3 words).  Exactly
+// `need` composites are >= the result.  Rounds stop as soon as the digit bin holding the
+// boundary is taken whole.  Every thread returns the same value.
+template <int NT, class Get>
+__device__ __forceinline__ uint64_t kth_largest(Get get, uint32_t c, uint32_t need, uint32_t* hbin, uint32_t* tmp, uint32_t* misc) {
+  constexpr int kBins = 1 << kRadixBits;
+  constexpr int BPT = kBins / NT;
+  static_assert(BPT >= 1 && kBins % NT == 0, "digit bins per thread");
+  const int tid = threadIdx.x;
+  // The top bits that every nonzero composite shares need no round: the rounds start below
+  // the highest bit in which the smallest and the largest differ (so that the first
+  // round's digits spread over the histogram instead of piling onto a few bins).
+  uint64_t mn = ~0ull, mx = 0ull;
+  for (uint32_t f = tid; f < c; f += NT) {
+    const uint64_t v = get(f);
+    if (v != 0ull) {
+      mn = v < mn ? v : mn;
+      mx = v > mx ? v : mx;
+    }
+  }
+  mn = block_min_u64<NT>(mn, tmp);
+  mx = ~block_min_u64<NT>(~mx, tmp);
+  const uint64_t diff = mn ^ mx;
+  int hi = diff ? 64 - __clzll((long long)diff) : 0;         // bits [hi-1 : 0] still open
+  uint64_t prefix = hi == 64 ? 0ull : (mx >> hi) << hi;
+  while (true) {
+    const int wd = hi < kRadixBits ? hi : kRadixBits;
+    const int sh = hi - wd;
+    const int nd = 1 << wd;
+    for (int i = tid; i < kBins; i += NT) hbin[i] = 0u;
+    __syncthreads();
+    for (uint32_t f = tid; f < c; f += NT) {
+      const uint64_t v = get(f);
+      if (hi == 64 || (v >> hi) == (prefix >> hi)) atomicAdd(&hbin[(uint32_t)(v >> sh) & (uint32_t)(nd - 1)], 1u);
+    }
+    __syncthreads();
+    // thread t holds digits nd-1-(BPT t + i), i = 0 .. BPT-1 (descending), so that the
+    // exclusive prefix counts the composites with larger digits
+    uint32_t hv[BPT];
+    uint32_t tsum = 0;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      const int d = BPT * tid + i;
+      hv[i] = d < nd ? hbin[nd - 1 - d] : 0u;
+      tsum += hv[i];
+    }
+    uint32_t tot;
+    const uint32_t ex = block_scan<NT>(tsum, tmp, &tot);
+    if (ex < need && need <= ex + tsum) {
+      uint32_t acc = ex;
+#pragma unroll
+      for (int i = 0; i < BPT; ++i) {
+        if (acc < need && need <= acc + hv[i]) {
+          misc[0] = (uint32_t)(nd - 1 - (BPT * tid + i));
+          misc[1] = acc;
+          misc[2] = hv[i];
+        }
+        acc += hv[i];
+      }
+    }
+    __syncthreads();
+    need -= misc[1];
+    prefix |= (uint64_t)misc[0] << sh;
+    const bool done = misc[2] == need || sh == 0;
+    hi = sh;
+    __syncthreads();                                         // misc is rewritten next round
+    if (done) break;
+  }
+  return prefix;
+}
+
+// Local selection at the end of an index workgroup (decode-shaped calls), from the chunk's
+// visible scores sc[0 .. nv) and their 12-bit histogram hist16 (two 16-bit counters per
+// word), both built in LDS as the scores were emitted.  The workgroup keeps whole histogram
+// bins: every key in the bins from the one holding its KL-th largest score upward, or, when
+// that would be more than KL keys, from the next bin up (then fewer than KL).  The kept keys
+// are written as composites (in no particular order) to out[0 .. count) and *meta receives
+// {count, nv, floor (low, high words)}: every kept composite is >= floor and every omitted
+// one is below it.  With nv <= KL every visible key is kept (floor 0).
+// key0: index of the chunk's first key; hb: 1 << kRadixBits words of LDS (staging);
+// tmp: 2 NT / 64 words; misc: 4 words.
+constexpr int kLocalChunk = 4096;                            // keys per index workgroup (local selection)
+template <int NT>
+__device__ __forceinline__ void local_select(const float* sc, uint32_t nv, const uint32_t* hist16, uint32_t KL, uint32_t key0,
+                             uint64_t* __restrict__ out, uint4* __restrict__ meta, uint32_t* hb, uint32_t* tmp,
+                             uint32_t* misc) {
+  const int tid = threadIdx.x;
+  if (nv <= KL) {
+    for (uint32_t i = tid; i < nv; i += NT) out[i] = comp_key(sc[i], key0 + i);
+    if (tid == 0) *meta = make_uint4(nv, nv, 0u, 0u);
+    return;
+  }
+  // 1. the bin holding the KL-th largest score, the count above it and its own count
+  constexpr int BPT = kHistBins / NT;
+  static_assert(BPT % 2 == 0, "whole histogram words per thread");
+  uint32_t cnt[BPT];
+  uint32_t tsum = 0;
+  static_assert((BPT / 2) % 4 == 0, "16-byte reads of the packed histogram");
+#pragma unroll
+  for (int i = 0; i < BPT / 2; i += 4) {
+    const uint4 x = *reinterpret_cast<const uint4*>(hist16 + tid * (BPT / 2) + i);
+    const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      cnt[2 * (i + j)] = w4[j] & 0xffffu;
+      cnt[2 * (i + j) + 1] = w4[j] >> 16;
+      tsum += cnt[2 * (i + j)] + cnt[2 * (i + j) + 1];
+    }
+  }
+  uint32_t total;
+  const uint32_t excl = block_scan<NT>(tsum, tmp, &total);
+  const uint32_t above = total - excl - tsum;               // keys in higher threads' bins
+  if (tid == 0) misc[3] = 0u;                                // staging counter
+  if (above < KL && KL <= above + tsum) {
+    uint32_t acc = above;
+#pragma unroll
+    for (int i = BPT - 1; i >= 0; --i) {                      // (no early exit: cnt stays in registers)
+      if (acc < KL && KL <= acc + cnt[i]) {
+        misc[0] = tid * BPT + i;
+        misc[1] = acc;
+        misc[2] = cnt[i];
+      }
+      acc += cnt[i];
+    }
+  }
+  __syncthreads();
+  const uint32_t keep_bin = misc[1] + misc[2] <= KL ? misc[0] : misc[0] + 1;
+  // 2. one pass: wave w takes keys [KPW w, KPW (w+1)), 64 consecutive keys per step (conflict-
+  //    free LDS reads, all issued before they are used); kept keys are staged in LDS
+  constexpr int NW = NT / kWave;
+  constexpr int KPW = kLocalChunk / NW;
+  constexpr int STEPS = KPW / kWave;
+  const int lane = tid & 63, wave = tid >> 6;
+  const uint32_t w0 = (uint32_t)wave * KPW;
+  uint64_t* stage = reinterpret_cast<uint64_t*>(hb);         // KL <= (1 << kRadixBits) / 2 entries
+  float v[STEPS];
+#pragma unroll
+  for (int u = 0; u < STEPS; ++u) {                          // (keys past nv are ignored below)
+    const uint32_t i = w0 + u * kWave + lane;
+    v[u] = sc[i < nv ? i : nv - 1];
+  }
+  uint64_t masks[STEPS];
+  uint32_t wtot = 0;
+  if (w0 + KPW <= nv) {                                      // the wave's keys are all visible
+#pragma unroll
+    for (int u = 0; u < STEPS; ++u) {
+      masks[u] = __ballot((score_key(v[u]) >> (32 - kHistBits)) >= keep_bin);
+      wtot += (uint32_t)__popcll(masks[u]);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < STEPS; ++u) {
+      const uint32_t i = w0 + u * kWave + lane;
+      masks[u] = __ballot(i < nv && (score_key(v[u]) >> (32 - kHistBits)) >= keep_bin);
+      wtot += (uint32_t)__popcll(masks[u]);
+    }
+  }
+  uint32_t base = 0;                                         // one staging reservation per wave
+  if (lane == 0 && wtot) base = atomicAdd(&misc[3], wtot);
+  base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+  for (int u = 0; u < STEPS; ++u) {
+    const uint64_t mask = masks[u];
+    const uint32_t pos = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+    if (((mask >> lane) & 1ull) && pos < KL) stage[pos] = comp_key(v[u], key0 + w0 + u * kWave + lane);
+    base += (uint32_t)__popcll(mask);
+  }
+  __syncthreads();
+  const uint32_t count = misc[3] < KL ? misc[3] : KL;
+  for (uint32_t j = tid; j < count; j += NT) out[j] = stage[j];
+  if (tid == 0) {
+    const uint64_t floor = keep_bin >= (uint32_t)kHistBins ? ~0ull : (uint64_t)(keep_bin << (32 - kHistBits)) << 32;
+    *meta = make_uint4(count, nv, (uint32_t)floor, (uint32_t)(floor >> 32));
   }
 }
 
@@ -186,16 +472,26 @@ struct KeyTile<KEY_FP8, DI> {
 
 // QTW query tiles (QTW * 16/HI queries) per workgroup: every key tile loaded is used by
 // all of them (QTW > 1 when there are many queries, e.g. a prefill chunk).
-template <int KIND, int DI, int HI, int QTW, bool kNT>
+// kLocal (decode-shaped calls, QTW = 1, chunk <= kLocalChunk): the workgroup also keeps its
+// chunk's scores in LDS and ends with a local selection of each query's klocal best keys
+// (cand_loc [rows][nch][klocal] composites, meta_loc [rows][nch]); the row histogram in
+// hist_g is not used.
+template <int KIND, int DI, int HI, int QTW, bool kNT, bool kLocal>
 __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
     const uint8_t* __restrict__ qi, const uint8_t* __restrict__ qsc, const float* __restrict__ wi,
     const uint8_t* __restrict__ ki, const uint8_t* __restrict__ ksc, const int32_t* __restrict__ q_pos, int64_t N,
     int64_t k_bs, int64_t Q, int m, int64_t chunk, float* __restrict__ scores, int64_t sstride,
-    uint32_t* __restrict__ hist_g) {
+    uint32_t* __restrict__ hist_g, uint64_t* __restrict__ cand_loc, uint4* __restrict__ meta_loc, int klocal,
+    int nch) {
   constexpr int QPT = 16 / HI;          // queries per 16-row MFMA tile
   constexpr int KS = DI / 32;
   constexpr int GPQ = HI / 4;           // lane groups per query slot
-  extern __shared__ uint32_t hist_l[];  // [QTW * QPT][kHistWords]
+  static_assert(!kLocal || QTW == 1, "local selection: one query tile per workgroup");
+  // LDS: [QTW * QPT][kHistWords] histograms; with kLocal then the scores [min(Q, QPT)][chunk]
+  // and the selection's scratch
+  extern __shared__ uint32_t hist_l[];
+  float* const sc_l = reinterpret_cast<float*>(hist_l + QTW * QPT * kHistWords);
+  uint32_t* const selb = reinterpret_cast<uint32_t*>(sc_l + (kLocal ? (Q < QPT ? Q : QPT) * chunk : 0));
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, col = lane & 15;
@@ -351,54 +647,47 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
           vs = (j == esel) ? v : vs;
         }
         const int64_t key = base + (u + esel) * 16 + col;
-        if (owner[t] && key < c1)
-          emit_score(scores, hist_l + (t * QPT + qs_c) * kHistWords, row_c[t], sstride, N, key, nvis[t], vs);
+        if (owner[t] && key < c1) {
+          emit_score<!kLocal>(scores, hist_l + (t * QPT + qs_c) * kHistWords, row_c[t], sstride, N, key, nvis[t],
+                              vs);
+          if constexpr (kLocal) sc_l[qs_c * chunk + (key - c0)] = key < (int64_t)nvis[t] ? vs : -INFINITY;
+        }
       }
     }
 #pragma unroll
     for (int u = 0; u < TPW; ++u) cur[u] = nxt[u];
   }
   __syncthreads();
+  if constexpr (kLocal) {
+    // each query's klocal best keys of this chunk; then its scores go to the global row in
+    // 16-byte stores (they are read back only to widen a chunk, or for out_score)
+    for (int s = 0; s < nq[0]; ++s) {
+      const int64_t row = b * Q + qt0 * QPT + s;
+      const int64_t nvis_s = vis_blocks(q_pos, row, m, N);
+      int64_t nv = nvis_s - c0;
+      nv = nv < 0 ? 0 : (nv > c1 - c0 ? c1 - c0 : nv);
+      const int64_t slot = row * nch + blockIdx.x;
+      local_select<kThreads>(sc_l + s * chunk, (uint32_t)nv, hist_l + s * kHistWords, (uint32_t)klocal, (uint32_t)c0,
+                             cand_loc + slot * klocal, meta_loc + slot, selb, selb + (1 << kRadixBits),
+                             selb + (1 << kRadixBits) + 2 * kThreads / kWave);
+      const float* src = sc_l + s * chunk;
+      float* dst = scores + row * sstride + c0;
+      const int64_t nk = c1 - c0;                            // c0 and the row stride are multiples of 64
+      for (int64_t i = (int64_t)threadIdx.x * 4; i < nk; i += kThreads * 4) {
+        if (i + 4 <= nk) *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(src + i);
+        else for (int64_t j = i; j < nk; ++j) dst[j] = src[j];
+      }
+      __syncthreads();
+    }
+  } else {
 #pragma unroll
-  for (int t = 0; t < QTW; ++t)
-    for (int s = 0; s < nq[t]; ++s)
-      flush_hist(hist_l + (t * QPT + s) * kHistWords, hist_g, b * Q + (qt0 + t) * QPT + s);
+    for (int t = 0; t < QTW; ++t)
+      for (int s = 0; s < nq[t]; ++s)
+        flush_hist(hist_l + (t * QPT + s) * kHistWords, hist_g, b * Q + (qt0 + t) * QPT + s);
+  }
 }
 
 // ------------------------------------------------------------------ selection
-// Inclusive prefix sum over the 64 lanes of a wave: row shifts within each 16-lane row,
-// then the last lane of a row is broadcast into the following rows.
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);   // row_shr:1
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);   // row_shr:2
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);   // row_shr:4
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);   // row_shr:8
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);   // row_bcast:15
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);   // row_bcast:31
-  return v;
-}
-
-// Block-wide exclusive prefix sum for NT threads (NT / 64 waves); `tmp` holds NT / 64
-// words of LDS.  Returns the exclusive prefix and writes the total to *total.
-template <int NT>
-__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* tmp, uint32_t* total) {
-  constexpr int NW = NT / kWave;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t incl = wave_incl_scan(v);
-  if (lane == 63) tmp[wave] = incl;
-  __syncthreads();
-  uint32_t base = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const uint32_t x = tmp[w];
-    base += (w < wave) ? x : 0u;
-    tot += x;
-  }
-  __syncthreads();
-  *total = tot;
-  return base + incl - v;
-}
-
 // Threshold bin of a row: the bin b* with #(bin > b*) < kk <= #(bin >= b*).  Every thread
 // of an NT-thread workgroup takes kHistBins / NT consecutive bins; the result goes to
 // misc[0] (bin) and misc[1] (#keys above it).
@@ -447,7 +736,6 @@ inline int64_t scan_keys(int64_t rows) { return rows >= kManyRows ? kScanKeysMan
 constexpr int kFinThreads = 1024;
 constexpr int kLdsBitmapKeys = 1 << 18;                      // bitmap kept in LDS by pass 2
 constexpr int kCandCap = 4096;                               // candidates staged in LDS by pass 2
-constexpr int kRadixBits = 12;                               // digit width of pass 2's radix select
 
 template <int KEYS>
 __global__ __launch_bounds__(kScanThreads) void select_scan_kernel(
@@ -736,155 +1024,486 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
   }
 }
 
-template <int KIND, int DI, int HI, int QTW>
-hipError_t launch_mfma_q(const IndexArgs& a, float* scores, uint32_t* hist, int64_t chunk, hipStream_t st) {
-  constexpr int QPT = 16 / HI;
-  constexpr int KPS = (QTW == 1 ? tiles_per_step<KIND, DI>() : (KIND == KEY_FP8 ? 4 : 2)) * 16 * 4;
-  const int64_t QT = (a.Q + QPT - 1) / QPT;
-  const int64_t QG = (QT + QTW - 1) / QTW;
-  if (QTW > 1) {                          // about 1024 workgroups over the whole call
-    int64_t chunks = 1024 / (a.B * QG);
-    if (chunks < 1) chunks = 1;
-    chunk = (a.N + chunks - 1) / chunks;
+// ---------------------------------------------------------------- local-candidate selection
+// Pass 2 of decode-shaped calls, one workgroup per row (N <= kLdsBitmapKeys).  Every chunk
+// kept whole histogram bins of its scores (all keys at or above its floor composite); the
+// kept composites are loaded (eight slots per thread, held in registers) and the kk-th
+// largest of them is found by radix selection.  A chunk that omitted keys can hide further
+// winners only if its floor lies above that threshold; the omitted keys of such a chunk that
+// lie above the threshold are added from the stored scores and the threshold is taken again
+// (it can only rise, so no other chunk is affected).  If they do not fit in LDS, the whole
+// row is selected from the stored scores instead.  The selection is marked in an LDS bitmap
+// and compacted into ascending indices: the exact top-kk of the fp32 scores.
+constexpr int kLocalCap = 8192;          // staged candidate slots per row (nch * klocal)
+constexpr int kExpCap = 4096;            // candidates added from chunks with hidden keys
+constexpr int kLocalKeep = 64;           // most candidates a chunk keeps
+constexpr int kMaxLocalChunks = 512;     // chunks per row on the local path
+// threads of a finish workgroup (measured: 1024 threads 14.6 us per decode call, 512 17.1,
+// 256 26.5; the work per thread, not the barriers, dominates)
+constexpr int kLocalFinThreads = 1024;
+// digit width of the finish's selection (4 bins per thread: one 16-byte LDS read)
+constexpr int kLocalRadixBits = 12;
+
+// kth_largest over values held in registers plus a list in LDS: thread t holds v[u] (0 for an
+// empty slot) and the composites ext[0 .. next) are read from LDS.  Same contract and result
+// as kth_largest.
+template <int NT, int SPT, int RB>
+__device__ __forceinline__ uint64_t kth_largest_regs(const uint64_t (&v)[SPT], const uint64_t* ext, uint32_t next,
+                                                     uint32_t need, uint32_t* hbin, uint32_t* tmp, uint32_t* misc) {
+  constexpr int kBins = 1 << RB;
+  constexpr int BPT = kBins / NT;
+  const int tid = threadIdx.x;
+  uint64_t mn = ~0ull, mx = 0ull;
+#pragma unroll
+  for (int u = 0; u < SPT; ++u) {
+    if (v[u] != 0ull) {
+      mn = v[u] < mn ? v[u] : mn;
+      mx = v[u] > mx ? v[u] : mx;
+    }
   }
-  if (chunk > kMaxIndexChunk) chunk = kMaxIndexChunk;    // 16-bit LDS bin counters
-  chunk = ((chunk + KPS - 1) / KPS) * KPS;
-  if (chunk < KPS) chunk = KPS;
-  dim3 grid((unsigned)((a.N + chunk - 1) / chunk), (unsigned)(a.B * QG));
-  // the kernel clears and uses QPT histogram slots for each of its non-empty query tiles
-  const int64_t tiles = QTW < QT ? QTW : QT;
-  const size_t smem = (size_t)(tiles * QPT) * kHistWords * sizeof(uint32_t);
-  // one query group per sequence: every key is read by one workgroup of the call, so the
-  // keys are streamed with the non-temporal hint; with several groups the caches serve the
-  // repeated reads (multi-query calls always run with QTW > 1 or several groups)
-  if (QTW == 1 && QG == 1)
-    DSV4_LAUNCH_MAIN((index_mfma_kernel<KIND, DI, HI, QTW, (QTW == 1)>), grid, dim3(kThreads), smem, st,
-                     reinterpret_cast<const uint8_t*>(a.qi), a.qi_scale, a.wi, reinterpret_cast<const uint8_t*>(a.ki),
-                     a.ki_scale, a.q_pos, a.N, a.k_bs, a.Q, a.m, chunk, scores, ((a.N + 63) / 64) * 64, hist);
-  else
-    DSV4_LAUNCH_MAIN((index_mfma_kernel<KIND, DI, HI, QTW, false>), grid, dim3(kThreads), smem, st,
-                     reinterpret_cast<const uint8_t*>(a.qi), a.qi_scale, a.wi, reinterpret_cast<const uint8_t*>(a.ki),
-                     a.ki_scale, a.q_pos, a.N, a.k_bs, a.Q, a.m, chunk, scores, ((a.N + 63) / 64) * 64, hist);
-  return hipGetLastError();
+  for (uint32_t f = tid; f < next; f += NT) {
+    const uint64_t x = ext[f];
+    mn = x < mn ? x : mn;
+    mx = x > mx ? x : mx;
+  }
+  block_minmax_u64<NT>(mn, mx, tmp);
+  const uint64_t diff = mn ^ mx;
+  int hi = diff ? 64 - __clzll((long long)diff) : 0;         // bits [hi-1 : 0] still open
+  uint64_t prefix = hi == 64 ? 0ull : (mx >> hi) << hi;
+  while (true) {
+    const int wd = hi < RB ? hi : RB;
+    const int sh = hi - wd;
+    const int nd = 1 << wd;
+    for (int i = tid; i < kBins; i += NT) hbin[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < SPT; ++u)
+      if (v[u] != 0ull && (hi == 64 || (v[u] >> hi) == (prefix >> hi)))
+        atomicAdd(&hbin[(uint32_t)(v[u] >> sh) & (uint32_t)(nd - 1)], 1u);
+    for (uint32_t f = tid; f < next; f += NT) {
+      const uint64_t x = ext[f];
+      if (hi == 64 || (x >> hi) == (prefix >> hi)) atomicAdd(&hbin[(uint32_t)(x >> sh) & (uint32_t)(nd - 1)], 1u);
+    }
+    __syncthreads();
+    uint32_t hv[BPT];
+    uint32_t tsum = 0;
+    if constexpr (BPT == 4) {
+      // thread t holds digits nd-1-4t .. nd-4-4t: one 16-byte read of 4 adjacent bins
+      const int d0 = nd - 4 - 4 * tid;
+      if (d0 >= 0) {
+        const uint4 x = *reinterpret_cast<const uint4*>(hbin + d0);
+        hv[0] = x.w; hv[1] = x.z; hv[2] = x.y; hv[3] = x.x;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hv[i] = nd - 1 - 4 * tid - i >= 0 ? hbin[nd - 1 - 4 * tid - i] : 0u;
+      }
+      tsum = hv[0] + hv[1] + hv[2] + hv[3];
+    } else {
+#pragma unroll
+      for (int i = 0; i < BPT; ++i) {
+        const int d = BPT * tid + i;
+        hv[i] = d < nd ? hbin[nd - 1 - d] : 0u;
+        tsum += hv[i];
+      }
+    }
+    uint32_t tot;
+    const uint32_t ex = block_scan<NT>(tsum, tmp, &tot);
+    if (ex < need && need <= ex + tsum) {
+      uint32_t acc = ex;
+#pragma unroll
+      for (int i = 0; i < BPT; ++i) {
+        if (acc < need && need <= acc + hv[i]) {
+          misc[0] = (uint32_t)(nd - 1 - (BPT * tid + i));
+          misc[1] = acc;
+          misc[2] = hv[i];
+        }
+        acc += hv[i];
+      }
+    }
+    __syncthreads();
+    need -= misc[1];
+    prefix |= (uint64_t)misc[0] << sh;
+    const bool done = misc[2] == need || sh == 0;
+    hi = sh;
+    __syncthreads();
+    if (done) break;
+  }
+  return prefix;
 }
 
-template <int KIND, int DI>
-hipError_t launch_mfma_di(const IndexArgs& a, float* scores, uint32_t* hist, int64_t chunk, hipStream_t st) {
-  // many queries per sequence (a prefill chunk): 4 query tiles (8 queries of one sequence)
-  // per workgroup at the common indexer shape, so that every key tile feeds 4 MFMA row
-  // blocks; a decode call (few queries per sequence, any batch) keeps one query tile and
-  // streams its keys once
-  if constexpr (DI == 128) {
-    if (a.HI == 8 && a.Q >= 8 && a.B * a.Q >= 64) return launch_mfma_q<KIND, DI, 8, 4>(a, scores, hist, chunk, st);
+template <int FT>
+__global__ __launch_bounds__(FT) void select_local_kernel(
+    const float* __restrict__ scores, const uint64_t* __restrict__ cand_g, const uint4* __restrict__ meta_g,
+    const int32_t* __restrict__ q_pos, int64_t N, int64_t sstride, int m, int k, int nch, int klocal, int64_t chunk,
+    int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
+  constexpr int NT = FT;
+  constexpr int SPT = kLocalCap / NT;                         // staged slots per thread
+  __shared__ uint64_t cand_l[kExpCap];                       // candidates added by expansion
+  __shared__ uint32_t bits_l[kLdsBitmapKeys / 32];           // also kth_largest's histogram
+  __shared__ uint32_t hbin_l[1 << kLocalRadixBits];          // kth_largest_regs' histogram
+  __shared__ uint32_t mcnt[kMaxLocalChunks];
+  __shared__ uint32_t mnv[kMaxLocalChunks];
+  __shared__ uint64_t mfloor[kMaxLocalChunks];
+  __shared__ uint32_t tmp[4 * NT / kWave];
+  __shared__ uint32_t misc[8];
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const uint32_t n = vis_blocks(q_pos, row, m, N);
+  const uint32_t kk = (uint32_t)k < n ? (uint32_t)k : n;
+  int32_t* orow = out_idx + row * k;
+  float* srow = out_score ? out_score + row * k : nullptr;
+  const float* sc = scores + row * sstride;
+  if (kk == 0) {
+    for (int p = tid; p < k; p += NT) {
+      orow[p] = -1;
+      if (srow) srow[p] = -INFINITY;
+    }
+    return;
   }
-  switch (a.HI) {
-    case 4: return launch_mfma_q<KIND, DI, 4, 1>(a, scores, hist, chunk, st);
-    case 8: return launch_mfma_q<KIND, DI, 8, 1>(a, scores, hist, chunk, st);
-    default: return launch_mfma_q<KIND, DI, 16, 1>(a, scores, hist, chunk, st);
+  // 1. the chunks' lists and their counts in one load round; slots past a chunk's count
+  //    become 0 (below every real composite).  Counts are clamped to what the index
+  //    workgroups can have written.
+  const uint32_t nslot = (uint32_t)nch * (uint32_t)klocal;
+  const uint64_t* cg = cand_g + row * (int64_t)nslot;
+  uint64_t v[SPT];
+#pragma unroll
+  for (int u = 0; u < SPT; ++u) {
+    const uint32_t f = tid + u * NT;
+    v[u] = f < nslot ? cg[f] : 0ull;
   }
-}
-
-template <int KIND>
-hipError_t launch_mfma(const IndexArgs& a, float* scores, uint32_t* hist, int64_t chunk, hipStream_t st) {
-  if constexpr (KIND == KEY_MXFP4_Q4) {    // 128-deep FP4 MFMA steps: DI of 128 or 256
-    if (a.DI == 128) return launch_mfma_di<KIND, 128>(a, scores, hist, chunk, st);
-    return launch_mfma_di<KIND, 256>(a, scores, hist, chunk, st);
+  for (int c = tid; c < nch; c += NT) {
+    const uint4 mm = meta_g[row * nch + c];
+    const int64_t keys = N - (int64_t)c * chunk < chunk ? N - (int64_t)c * chunk : chunk;
+    const uint32_t nvc = (int64_t)mm.y < keys ? mm.y : (uint32_t)keys;
+    const uint32_t kept = mm.x < (uint32_t)klocal ? mm.x : (uint32_t)klocal;
+    mnv[c] = nvc;
+    mcnt[c] = kept < nvc ? kept : nvc;
+    mfloor[c] = ((uint64_t)mm.w << 32) | mm.z;
   }
-  switch (a.DI) {
-    case 32: return launch_mfma_di<KIND, 32>(a, scores, hist, chunk, st);
-    case 64: return launch_mfma_di<KIND, 64>(a, scores, hist, chunk, st);
-    case 128: return launch_mfma_di<KIND, 128>(a, scores, hist, chunk, st);
-    default: return launch_mfma_di<KIND, 256>(a, scores, hist, chunk, st);
+  __syncthreads();
+  uint32_t nval = 0;
+#pragma unroll
+  for (int u = 0; u < SPT; ++u) {
+    const uint32_t f = tid + u * NT;
+    const uint32_t c = f / (uint32_t)klocal;
+    const bool ok = f < nslot && f - c * (uint32_t)klocal < mcnt[c < (uint32_t)nch ? c : 0];
+    v[u] = ok ? v[u] : 0ull;
+    nval += ok ? 1u : 0u;
+  }
+  uint32_t valid;
+  block_scan<NT>(nval, tmp, &valid);
+  // 2. the threshold among the kept candidates (none if they are fewer than kk: then every
+  //    chunk with omitted keys is expanded whole)
+  uint64_t T = 0;
+  if (valid >= kk) T = kth_largest_regs<NT, SPT, kLocalRadixBits>(v, cand_l, 0u, kk, hbin_l, tmp, misc);
+  // 3. chunks that may hide keys above the threshold (checked in parallel; usually none)
+  bool hidden = false;
+  for (int c = tid; c < nch; c += NT) hidden |= mnv[c] > mcnt[c] && (valid < kk || mfloor[c] > T);
+  const bool any_hidden = __syncthreads_or(hidden);
+  bool fallback = false;
+  uint32_t nexp = 0;
+  if (any_hidden) {
+    if (tid == 0) misc[4] = 0u;
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+      if (!(mnv[c] > mcnt[c] && (valid < kk || mfloor[c] > T))) continue;
+      const int64_t k0 = (int64_t)c * chunk;
+      for (uint32_t i = tid; i < mnv[c]; i += NT) {
+        const uint64_t x = comp_key(sc[k0 + i], (uint32_t)(k0 + i));
+        if (x > T && x < mfloor[c]) {
+          const uint32_t at = atomicAdd(&misc[4], 1u);
+          if (at < (uint32_t)kExpCap) cand_l[at] = x;
+        }
+      }
+    }
+    __syncthreads();
+    nexp = misc[4];
+    fallback = nexp > (uint32_t)kExpCap;
+    if (fallback) {   // rare: the whole row from the stored scores
+      T = kth_largest<NT>([&](uint32_t f) -> uint64_t { return comp_key(sc[f], f); }, n, kk, bits_l, tmp, misc);
+    } else {
+      T = kth_largest_regs<NT, SPT, kLocalRadixBits>(v, cand_l, nexp, kk, hbin_l, tmp, misc);
+    }
+  }
+  // 4. mark the selection in the bitmap
+  const int64_t wn = ((int64_t)n + 31) / 32;
+  for (int64_t w = tid; w < wn; w += NT) bits_l[w] = 0u;
+  __syncthreads();
+  if (!fallback) {
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+      const uint32_t j = ~(uint32_t)v[u];
+      if (v[u] != 0ull && v[u] >= T && j < n) atomicOr(&bits_l[j >> 5], 1u << (j & 31));
+    }
+    for (uint32_t f = tid; f < nexp; f += NT) {
+      const uint64_t x = cand_l[f];
+      const uint32_t j = ~(uint32_t)x;
+      if (x >= T && j < n) atomicOr(&bits_l[j >> 5], 1u << (j & 31));
+    }
+  } else {
+    for (uint32_t j = tid; j < n; j += NT)
+      if (comp_key(sc[j], j) >= T) atomicOr(&bits_l[j >> 5], 1u << (j & 31));
+  }
+  __syncthreads();
+  // 5. compaction: thread t takes WPT consecutive words per round
+  constexpr int WPT = (kLdsBitmapKeys / 32) / NT;
+  uint32_t base_off = 0;
+  for (int64_t r0 = 0; r0 < wn; r0 += WPT * NT) {
+    const int64_t w0 = r0 + (int64_t)tid * WPT;
+    uint32_t wv[WPT];
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) wv[i] = w0 + i < wn ? bits_l[w0 + i] : 0u;
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) cnt += __popc(wv[i]);
+    uint32_t rtot;
+    uint32_t off = base_off + block_scan<NT>(cnt, tmp, &rtot);
+    for (int i = 0; i < WPT; ++i) {
+      uint32_t b_ = wv[i];
+      while (b_) {
+        const int bpos = __ffs(b_) - 1;
+        b_ &= b_ - 1;
+        const int64_t j = (w0 + i) * 32 + bpos;
+        if (off < (uint32_t)k) {
+          orow[off] = (int32_t)j;
+          if (srow) srow[off] = sc[j];
+        }
+        ++off;
+      }
+    }
+    base_off += rtot;
+  }
+  for (int64_t p = (int64_t)base_off + tid; p < k; p += NT) {
+    orow[p] = -1;
+    if (srow) srow[p] = -INFINITY;
   }
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Launch plan of one csa_index_topk call, shared by the workspace query and the launch.
+struct TopkPlan {
+  bool local = false;      // local candidates + one finish pass (else histogram, scan, finish)
+  int qtw = 1;             // query tiles per index workgroup
+  int64_t chunk = 0;       // keys per index workgroup (MFMA kernels)
+  int64_t nch = 0;         // index workgroups (key chunks) per query group
+  int klocal = 0;          // candidates a chunk keeps (local path)
+  size_t scores = 0, hist = 0, bitmap = 0, cand = 0, ccount = 0, thr = 0, cloc = 0, meta = 0, total = 0;
+};
+
+inline int64_t tiles_per_step_host(int kind, int DI) {
+  return kind == KEY_BF16 ? (DI >= 256 ? 2 : 4) : (kind == KEY_FP8 && DI >= 256 ? 4 : 8);
+}
+
+TopkPlan plan_topk(const IndexArgs& a) {
+  TopkPlan p;
+  const int64_t R = a.B * a.Q, N = a.N;
+  if (a.kind != KEY_F32 && N > 0) {
+    const int64_t QPT = 16 / a.HI;
+    // many queries per sequence (a prefill chunk): 4 query tiles (8 queries of one sequence)
+    // per workgroup at the common indexer shape, so that every key tile feeds 4 MFMA row
+    // blocks; a decode call (few queries per sequence, any batch) keeps one query tile and
+    // streams its keys once
+    p.qtw = (a.DI == 128 && a.HI == 8 && a.Q >= 8 && R >= 64) ? 4 : 1;
+    const int64_t tpw = p.qtw == 1 ? tiles_per_step_host(a.kind, a.DI) : (a.kind == KEY_FP8 ? 4 : 2);
+    const int64_t KPS = tpw * 16 * 4;
+    const int64_t QT = (a.Q + QPT - 1) / QPT, QG = (QT + p.qtw - 1) / p.qtw;
+    int64_t chunk;
+    if (p.qtw > 1) {                     // about 1024 workgroups over the whole call
+      int64_t chunks = 1024 / (a.B * QG);
+      if (chunks < 1) chunks = 1;
+      chunk = (N + chunks - 1) / chunks;
+    } else {                             // about two workgroups per CU over the whole call
+      chunk = (N * (a.B * QT) + 511) / 512;
+    }
+    if (chunk > kMaxIndexChunk) chunk = kMaxIndexChunk;    // 16-bit LDS bin counters
+    chunk = ((chunk + KPS - 1) / KPS) * KPS;
+    if (chunk < KPS) chunk = KPS;
+    if (p.qtw == 1 && N <= kLdsBitmapKeys) {
+      const int64_t lc = chunk < kLocalChunk ? chunk : kLocalChunk;   // both multiples of KPS
+      const int64_t nch = (N + lc - 1) / lc;
+      if (nch <= kMaxLocalChunks) {
+        int64_t kl = kLocalCap / nch;
+        if (kl > kLocalKeep) kl = kLocalKeep;
+        if (kl > a.k) kl = a.k;
+        p.local = true;
+        chunk = lc;
+        p.klocal = (int)kl;
+      }
+    }
+    p.chunk = chunk;
+    p.nch = (N + chunk - 1) / chunk;
+  }
+  // workspace regions
+  const int64_t sstride = ((N + 63) / 64) * 64;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  p.scores = take((size_t)R * sstride * 4);
+  if (p.local) {
+    p.cloc = take((size_t)R * p.nch * p.klocal * 8);
+    p.meta = take((size_t)R * p.nch * 16);
+  } else {
+    const int64_t words = ((N + 127) / 128) * 4;             // bitmap rows of 16-byte multiples
+    p.hist = take((size_t)R * kHistBins * 4);
+    p.bitmap = take((size_t)R * words * 4);
+    p.cand = take((size_t)R * N * 8);
+    p.ccount = take((size_t)R * ((N + kScanKeys - 1) / kScanKeys) * 4);
+    p.thr = take((size_t)R * 2 * 4);
+  }
+  p.total = off;
+  return p;
+}
+
+struct IndexBufs {
+  float* scores;
+  uint32_t* hist;
+  uint64_t* cloc;
+  uint4* meta;
+};
+
+template <int KIND, int DI, int HI, int QTW, bool kLocal>
+hipError_t launch_mfma_q(const IndexArgs& a, const TopkPlan& p, const IndexBufs& w, hipStream_t st) {
+  constexpr int QPT = 16 / HI;
+  const int64_t QT = (a.Q + QPT - 1) / QPT;
+  const int64_t QG = (QT + QTW - 1) / QTW;
+  dim3 grid((unsigned)p.nch, (unsigned)(a.B * QG));
+  // the kernel clears and uses QPT histogram slots for each of its non-empty query tiles;
+  // the local selection adds the chunk's scores of each query and its own scratch
+  const int64_t tiles = QTW < QT ? QTW : QT;
+  size_t smem = (size_t)(tiles * QPT) * kHistWords * sizeof(uint32_t);
+  if (kLocal)
+    smem += (size_t)(a.Q < QPT ? a.Q : QPT) * p.chunk * sizeof(float) +
+            (size_t)((1 << kRadixBits) + 2 * kThreads / kWave + 8) * sizeof(uint32_t);
+  const int64_t sstride = ((a.N + 63) / 64) * 64;
+  // one query group per sequence: every key is read by one workgroup of the call, so the
+  // keys are streamed with the non-temporal hint; with several groups the caches serve the
+  // repeated reads (multi-query calls always run with QTW > 1 or several groups)
+  auto go = [&](auto kern) {
+    if (smem > 65536) hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    DSV4_LAUNCH_MAIN(kern, grid, dim3(kThreads), smem, st, reinterpret_cast<const uint8_t*>(a.qi), a.qi_scale, a.wi,
+                     reinterpret_cast<const uint8_t*>(a.ki), a.ki_scale, a.q_pos, a.N, a.k_bs, a.Q, a.m, p.chunk,
+                     w.scores, sstride, w.hist, w.cloc, w.meta, p.klocal, (int)p.nch);
+  };
+  if (QTW == 1 && QG == 1) go(index_mfma_kernel<KIND, DI, HI, QTW, (QTW == 1), kLocal>);
+  else go(index_mfma_kernel<KIND, DI, HI, QTW, false, kLocal>);
+  return hipGetLastError();
+}
+
+template <int KIND, int DI>
+hipError_t launch_mfma_di(const IndexArgs& a, const TopkPlan& p, const IndexBufs& w, hipStream_t st) {
+  if constexpr (DI == 128) {
+    if (p.qtw == 4) return launch_mfma_q<KIND, DI, 8, 4, false>(a, p, w, st);
+  }
+  if (p.local) {
+    switch (a.HI) {
+      case 4: return launch_mfma_q<KIND, DI, 4, 1, true>(a, p, w, st);
+      case 8: return launch_mfma_q<KIND, DI, 8, 1, true>(a, p, w, st);
+      default: return launch_mfma_q<KIND, DI, 16, 1, true>(a, p, w, st);
+    }
+  }
+  switch (a.HI) {
+    case 4: return launch_mfma_q<KIND, DI, 4, 1, false>(a, p, w, st);
+    case 8: return launch_mfma_q<KIND, DI, 8, 1, false>(a, p, w, st);
+    default: return launch_mfma_q<KIND, DI, 16, 1, false>(a, p, w, st);
+  }
+}
+
+template <int KIND>
+hipError_t launch_mfma(const IndexArgs& a, const TopkPlan& p, const IndexBufs& w, hipStream_t st) {
+  if constexpr (KIND == KEY_MXFP4_Q4) {    // 128-deep FP4 MFMA steps: DI of 128 or 256
+    if (a.DI == 128) return launch_mfma_di<KIND, 128>(a, p, w, st);
+    return launch_mfma_di<KIND, 256>(a, p, w, st);
+  }
+  switch (a.DI) {
+    case 32: return launch_mfma_di<KIND, 32>(a, p, w, st);
+    case 64: return launch_mfma_di<KIND, 64>(a, p, w, st);
+    case 128: return launch_mfma_di<KIND, 128>(a, p, w, st);
+    default: return launch_mfma_di<KIND, 256>(a, p, w, st);
+  }
+}
+
 }  // namespace
 
-size_t topk_workspace_bytes(int64_t R, int64_t N) {
-  int64_t words = ((N + 127) / 128) * 4;   // rows of 16-byte multiples
-  const int64_t sstride = ((N + 63) / 64) * 64;
-  const int64_t nch = (N + kScanKeys - 1) / kScanKeys;
-  return align256((size_t)R * sstride * 4) + align256((size_t)R * kHistBins * 4) + align256((size_t)R * words * 4) +
-         align256((size_t)R * N * 8) + align256((size_t)R * nch * 4) + align256((size_t)R * 2 * 4);
-}
+size_t topk_workspace_bytes(const IndexArgs& a) { return a.B * a.Q > 0 ? plan_topk(a).total : 0; }
 
-TopkWorkspace topk_workspace_carve(void* base, int64_t R, int64_t N) {
-  int64_t words = ((N + 127) / 128) * 4;   // rows of 16-byte multiples
-  uint8_t* p = reinterpret_cast<uint8_t*>(base);
-  TopkWorkspace w;
-  w.scores = reinterpret_cast<float*>(p);
-  p += align256((size_t)R * (((N + 63) / 64) * 64) * 4);
-  w.hist = reinterpret_cast<uint32_t*>(p);
-  p += align256((size_t)R * kHistBins * 4);
-  w.bitmap = reinterpret_cast<uint32_t*>(p);
-  p += align256((size_t)R * words * 4);
-  w.cand = reinterpret_cast<uint64_t*>(p);
-  p += align256((size_t)R * N * 8);
-  w.ccount = reinterpret_cast<uint32_t*>(p);
-  p += align256((size_t)R * ((N + kScanKeys - 1) / kScanKeys) * 4);
-  w.thr = reinterpret_cast<uint32_t*>(p);
-  return w;
-}
-
-hipError_t launch_index_topk(const IndexArgs& a, const TopkWorkspace& ws, hipStream_t st) {
+hipError_t launch_index_topk(const IndexArgs& a, void* ws, hipStream_t st) {
   const int64_t R = a.B * a.Q;
   if (R == 0) return hipSuccess;
+  const TopkPlan p = plan_topk(a);
+  uint8_t* base = reinterpret_cast<uint8_t*>(ws);
+  IndexBufs w;
+  w.scores = reinterpret_cast<float*>(base + p.scores);
+  w.hist = p.local ? nullptr : reinterpret_cast<uint32_t*>(base + p.hist);
+  w.cloc = p.local ? reinterpret_cast<uint64_t*>(base + p.cloc) : nullptr;
+  w.meta = p.local ? reinterpret_cast<uint4*>(base + p.meta) : nullptr;
+  const int64_t sstride = ((a.N + 63) / 64) * 64;
+  hipError_t e;
+  if (p.local) {
+    // pass 1: scores, each chunk's local candidates; pass 2: one workgroup per row
+    if (a.kind == KEY_BF16) e = launch_mfma<KEY_BF16>(a, p, w, st);
+    else if (a.kind == KEY_FP8) e = launch_mfma<KEY_FP8>(a, p, w, st);
+    else if (a.kind == KEY_MXFP4_Q4) e = launch_mfma<KEY_MXFP4_Q4>(a, p, w, st);
+    else e = launch_mfma<KEY_MXFP4>(a, p, w, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(select_local_kernel<kLocalFinThreads>, dim3((unsigned)R), dim3(kLocalFinThreads), 0, st,
+                       w.scores, w.cloc, w.meta, a.q_pos, a.N, sstride, a.m, a.k, (int)p.nch, p.klocal, p.chunk,
+                       a.out_idx, a.out_score);
+    return hipGetLastError();
+  }
+  uint32_t* bitmap = reinterpret_cast<uint32_t*>(base + p.bitmap);
+  uint64_t* cand = reinterpret_cast<uint64_t*>(base + p.cand);
+  uint32_t* ccount = reinterpret_cast<uint32_t*>(base + p.ccount);
+  uint32_t* thr = reinterpret_cast<uint32_t*>(base + p.thr);
   const int64_t nclear = R * kHistBins;
   hipLaunchKernelGGL(clear_kernel, dim3((unsigned)((nclear + 1023) / 1024 < 256 ? (nclear + 1023) / 1024 : 256)),
-                     dim3(1024), 0, st, ws.hist, nclear);
-  hipError_t e = hipGetLastError();
+                     dim3(1024), 0, st, w.hist, nclear);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.N > 0) {
     if (a.kind == KEY_F32) {
       dim3 grid((unsigned)((a.N + kThreads - 1) / kThreads), (unsigned)R);
       size_t smem = (kHistWords + (size_t)a.HI * a.DI + a.HI) * 4;
       DSV4_LAUNCH_MAIN(index_f32_kernel, grid, dim3(kThreads), smem, st, reinterpret_cast<const float*>(a.qi),
-                         a.wi, reinterpret_cast<const float*>(a.ki), a.q_pos, a.N, a.k_bs, a.Q, a.HI, a.DI, a.m,
-                         ws.scores, ((a.N + 63) / 64) * 64, ws.hist);
+                       a.wi, reinterpret_cast<const float*>(a.ki), a.q_pos, a.N, a.k_bs, a.Q, a.HI, a.DI, a.m,
+                       w.scores, sstride, w.hist);
       e = hipGetLastError();
-    } else {
-      // about two workgroups per CU over the whole call
-      int QPT = 16 / a.HI;
-      int64_t rows = a.B * ((a.Q + QPT - 1) / QPT);
-      int64_t per = (a.N * rows + 511) / 512;
-      // (rounded to whole steps of the kernel inside launch_mfma_di)
-      int64_t chunk = per;
-      if (a.kind == KEY_BF16) e = launch_mfma<KEY_BF16>(a, ws.scores, ws.hist, chunk, st);
-      else if (a.kind == KEY_FP8) e = launch_mfma<KEY_FP8>(a, ws.scores, ws.hist, chunk, st);
-      else if (a.kind == KEY_MXFP4_Q4) e = launch_mfma<KEY_MXFP4_Q4>(a, ws.scores, ws.hist, chunk, st);
-      else e = launch_mfma<KEY_MXFP4>(a, ws.scores, ws.hist, chunk, st);
-    }
+    } else if (a.kind == KEY_BF16) e = launch_mfma<KEY_BF16>(a, p, w, st);
+    else if (a.kind == KEY_FP8) e = launch_mfma<KEY_FP8>(a, p, w, st);
+    else if (a.kind == KEY_MXFP4_Q4) e = launch_mfma<KEY_MXFP4_Q4>(a, p, w, st);
+    else e = launch_mfma<KEY_MXFP4>(a, p, w, st);
     if (e != hipSuccess) return e;
   }
   // selection: pass 1 over all rows x key ranges, pass 2 one workgroup per row
   if (a.N == 0) {
-    hipLaunchKernelGGL(select_finish_kernel<true>, dim3((unsigned)R), dim3(kFinThreads), 0, st, ws.scores,
-                       ws.bitmap, ws.cand, ws.ccount, ws.thr, a.q_pos, a.N, (int64_t)0, (int64_t)0, a.m, a.k, 0,
-                       (int64_t)kScanKeys, a.out_idx, a.out_score);
+    hipLaunchKernelGGL(select_finish_kernel<true>, dim3((unsigned)R), dim3(kFinThreads), 0, st, w.scores, bitmap,
+                       cand, ccount, thr, a.q_pos, a.N, (int64_t)0, (int64_t)0, a.m, a.k, 0, (int64_t)kScanKeys,
+                       a.out_idx, a.out_score);
     return hipGetLastError();
   }
   const int64_t words = ((a.N + 127) / 128) * 4;
-  const int64_t sstride = ((a.N + 63) / 64) * 64;
   const int64_t rk = scan_keys(R);        // keys per range (the workspace holds counts for kScanKeys)
-  const int64_t nch = (a.N + rk - 1) / rk;
+  const int64_t nrg = (a.N + rk - 1) / rk;
   if (rk == kScanKeysMany)
-    hipLaunchKernelGGL(select_scan_kernel<kScanKeysMany>, dim3((unsigned)nch, (unsigned)R), dim3(kScanThreads), 0, st,
-                       ws.scores, ws.hist, ws.bitmap, ws.cand, ws.ccount, ws.thr, a.q_pos, a.N, sstride, words, a.m, a.k);
+    hipLaunchKernelGGL(select_scan_kernel<kScanKeysMany>, dim3((unsigned)nrg, (unsigned)R), dim3(kScanThreads), 0, st,
+                       w.scores, w.hist, bitmap, cand, ccount, thr, a.q_pos, a.N, sstride, words, a.m, a.k);
   else
-    hipLaunchKernelGGL(select_scan_kernel<kScanKeys>, dim3((unsigned)nch, (unsigned)R), dim3(kScanThreads), 0, st,
-                       ws.scores, ws.hist, ws.bitmap, ws.cand, ws.ccount, ws.thr, a.q_pos, a.N, sstride, words, a.m, a.k);
+    hipLaunchKernelGGL(select_scan_kernel<kScanKeys>, dim3((unsigned)nrg, (unsigned)R), dim3(kScanThreads), 0, st,
+                       w.scores, w.hist, bitmap, cand, ccount, thr, a.q_pos, a.N, sstride, words, a.m, a.k);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.N <= kLdsBitmapKeys)
-    hipLaunchKernelGGL(select_finish_kernel<true>, dim3((unsigned)R), dim3(kFinThreads), 0, st, ws.scores,
-                       ws.bitmap, ws.cand, ws.ccount, ws.thr, a.q_pos, a.N, sstride, words, a.m, a.k, (int)nch, rk,
-                       a.out_idx, a.out_score);
+    hipLaunchKernelGGL(select_finish_kernel<true>, dim3((unsigned)R), dim3(kFinThreads), 0, st, w.scores, bitmap,
+                       cand, ccount, thr, a.q_pos, a.N, sstride, words, a.m, a.k, (int)nrg, rk, a.out_idx,
+                       a.out_score);
   else
-    hipLaunchKernelGGL(select_finish_kernel<false>, dim3((unsigned)R), dim3(kFinThreads), 0, st, ws.scores,
-                       ws.bitmap, ws.cand, ws.ccount, ws.thr, a.q_pos, a.N, sstride, words, a.m, a.k, (int)nch, rk,
-                       a.out_idx, a.out_score);
+    hipLaunchKernelGGL(select_finish_kernel<false>, dim3((unsigned)R), dim3(kFinThreads), 0, st, w.scores, bitmap,
+                       cand, ccount, thr, a.q_pos, a.N, sstride, words, a.m, a.k, (int)nrg, rk, a.out_idx,
+                       a.out_score);
   return hipGetLastError();
 }
 

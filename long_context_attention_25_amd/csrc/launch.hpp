@@ -77,18 +77,9 @@ struct IndexArgs {
   float* out_score;
 };
 
-// Workspace layout of the decode selection path (rows R = B*Q).
-struct TopkWorkspace {
-  float* scores;        // [R][N]
-  uint32_t* hist;       // [R][kHistBins]
-  uint32_t* bitmap;     // [R][words]
-  uint64_t* cand;       // [R][N]: candidate slices of the key ranges
-  uint32_t* ccount;     // [R][ranges]: candidates per key range
-  uint32_t* thr;        // [R][2]: threshold bin and #keys above it, per row
-};
-size_t topk_workspace_bytes(int64_t R, int64_t N);
-TopkWorkspace topk_workspace_carve(void* base, int64_t R, int64_t N);
-hipError_t launch_index_topk(const IndexArgs& a, const TopkWorkspace& ws, hipStream_t st);
+// Workspace bytes of a call (the layout depends on the selection path the call takes).
+size_t topk_workspace_bytes(const IndexArgs& a);
+hipError_t launch_index_topk(const IndexArgs& a, void* workspace, hipStream_t st);
 
 // ---------------------------------------------------------------- attention
 constexpr int kFp8RopeDims = 64;   // bf16 tail of an FP8 K row

@@ -117,7 +117,12 @@ def _index(ws=None, n=None, **kw):
 
 def test_index_topk_validation_and_workspace_query():
     st, n = _index()
-    assert st == 0 and n >= 8 * 262144 * 12            # scores + candidates at least
+    # a decode-shaped call: fp32 scores, then each 4096-key chunk's 128 best as candidates
+    # (64 chunks per row) and one 16-byte record per chunk
+    assert st == 0 and n == 8 * 262144 * 4 + 8 * 64 * 128 * 8 + 8 * 64 * 16
+    # many queries per sequence: scores, row histograms, bitmaps and a candidate slot per key
+    st, n = _index(B=1, Q=4096, N=65536)
+    assert st == 0 and n >= 4096 * 65536 * 12
     assert _index(k=0)[0] == 1
     assert _index(k=5000)[0] == 1
     assert _index(HI=6)[0] == 2

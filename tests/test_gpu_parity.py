@@ -626,6 +626,38 @@ def test_index_topk_many_candidates(N):
     check_topk(idx[0, 1], s_ref[0, 1], int(method.visible_blocks(pos, m, N)[0, 1]), k)
 
 
+def test_index_topk_concentrated_winners():
+    """Rows whose winners crowd into a few key chunks.  With 256 chunks of 256 keys each chunk
+    keeps only its 32 best as candidates.  Sequence 0: five chunks of keys scaled by 5 hold
+    more than 32 winners each, so those chunks are widened from the stored scores.
+    Sequence 1: every score is 0 (negated queries, positive keys), so the winners are the
+    4096 lowest indices, packed 256 to a chunk: widening them would exceed the on-chip room
+    and the whole row is selected from the stored scores.  Both against the oracle."""
+    cfg = 236
+    B, Q, HI, DI, N, m, k = 2, 1, 8, 128, 65536, 4, 4096
+    qi = synth.normal(cfg, synth.QI, (B, Q, HI, DI))
+    w = synth.uniform(cfg, synth.WI, (B, Q, HI))
+    ki = synth.normal(cfg, synth.KI, (B, N, DI))
+    boosted = (3, 100, 101, 102, 103)
+    for c in boosted:
+        ki[0, c * 256:(c + 1) * 256] *= np.float32(5)
+    qi[1] = -np.abs(qi[1])
+    ki[1] = np.abs(ki[1])
+    pos = np.array([[4 * N - 1], [4 * N - 2]], dtype=np.int32)
+    qd, qbits = dev_bf16(qi)
+    kd, kbits = dev_bf16(ki)
+    idx, sc = L.csa_index_topk(qd, dev(w), kd, dev(pos), m, k, with_scores=True)
+    torch.cuda.synchronize()
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+    s_ref = _scores_oracle(codecs.decode_bf16(qbits), w, codecs.decode_bf16(kbits), pos, m)
+    assert check_topk(idx[0, 0], s_ref[0, 0], N, k) <= 2
+    assert np.all(np.abs(sc[0, 0] - s_ref[0, 0, idx[0, 0]]) <= 1e-5 * np.abs(s_ref[0, 0]).max())
+    per_chunk = np.bincount(idx[0, 0] // 256, minlength=N // 256)
+    assert per_chunk[list(boosted)].min() > 32                  # those chunks had to be widened
+    assert np.all(s_ref[1, 0, :N - 1] == 0) and list(idx[1, 0]) == list(range(k))   # (the last block is not visible)
+    assert np.all(sc[1, 0] == 0)
+
+
 def test_index_topk_very_long_rows():
     """Rows of more than 2^21 visible blocks: more key ranges in the selection's first pass
     than the second pass indexes directly, so candidates of the last ranges are found by
