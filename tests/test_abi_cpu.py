@@ -117,9 +117,9 @@ def _index(ws=None, n=None, **kw):
 
 def test_index_topk_validation_and_workspace_query():
     st, n = _index()
-    # a decode-shaped call: fp32 scores, then each 4096-key chunk's 128 best as candidates
+    # a decode-shaped call: fp32 scores, then up to 64 candidates of each 4096-key chunk
     # (64 chunks per row) and one 16-byte record per chunk
-    assert st == 0 and n == 8 * 262144 * 4 + 8 * 64 * 128 * 8 + 8 * 64 * 16
+    assert st == 0 and n == 8 * 262144 * 4 + 8 * 64 * 64 * 8 + 8 * 64 * 16
     # many queries per sequence: scores, row histograms, bitmaps and a candidate slot per key
     st, n = _index(B=1, Q=4096, N=65536)
     assert st == 0 and n >= 4096 * 65536 * 12
