@@ -451,13 +451,60 @@ def run_step(lib, calls, arm=None):
             raise RuntimeError(f"{fn.__name__}: {lib.dsv4_last_error().decode()}")
 
 
+def time_graph_replay(L, torch, wl, replicas, steps):
+    """The decode step captured once per replica into a HIP graph (on a side stream, with
+    the calls marshalled for that stream) and replayed with the replicas rotating: ms per
+    step.  The outputs of the last replay of each replica are compared with an eager run
+    of the same step (bitwise)."""
+    lib = L.lib()
+    s = torch.cuda.Stream()
+    graphs, outs = [], []
+    with torch.cuda.stream(s):
+        marsh = [marshal_step(L, torch, wl, r)[0] for r in range(replicas)]
+        for r in range(replicas):
+            run_step(lib, marsh[r])
+        torch.cuda.synchronize()
+        for r in range(replicas):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                run_step(lib, marsh[r])
+            graphs.append(g)
+    torch.cuda.synchronize()
+    for r in range(replicas):                                  # eager reference outputs
+        run_step(lib, marsh[r])
+        torch.cuda.synchronize()
+        t = wl.r[r]
+        outs.append([t[k].clone() for k in ("idx", "o", "lse", "ho", "hlse")])
+    with torch.cuda.stream(s):                                 # replays and events on one stream
+        for i in range(3 * replicas):
+            graphs[i % replicas].replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            graphs[i % replicas].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        same = True
+        for r in range(replicas):
+            graphs[r].replay()
+            torch.cuda.synchronize()
+            t = wl.r[r]
+            same = same and all(torch.equal(t[k], o) for k, o in zip(("idx", "o", "lse", "ho", "hlse"), outs[r]))
+    del graphs
+    return ms, same
+
+
 # ------------------------------------------------------------------------------------ oracle leg
-def cpu_baseline(L, torch, synth, wl, budget_s):
-    """The float64 oracle on one host thread: whole decode steps of the sequences of
-    replica 0 (both layers), cycling over the 8 sequences until ~budget_s of timed work.
-    Inputs are generated and decoded beforehand (untimed); the library is not used."""
+def cpu_baseline(L, torch, synth, wl, budget_s, threads=1):
+    """The float64 oracle on `threads` host threads (None: all of them; NumPy's BLAS runs the
+    indexer's products on them, the rest of the oracle is single-threaded NumPy): whole
+    decode steps of the sequences of replica 0 (both layers), cycling over the 8 sequences
+    until ~budget_s of timed work.  Inputs are generated and decoded beforehand (untimed);
+    the library is not used.  Returns (steps, seconds, BLAS threads used)."""
     import numpy as np
-    from threadpoolctl import threadpool_limits
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import codecs, method
 
@@ -486,7 +533,8 @@ def cpu_baseline(L, torch, synth, wl, budget_s):
     done, elapsed = 0, 0.0
     scale = 1.0 / math.sqrt(D)
     pos = np.array([[CTX - 1]])
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=threads):
+        used = max([1] + [int(i.get("num_threads", 1)) for i in threadpool_info()])
         while elapsed < budget_s:
             sq = seqs[done % B]
             t0 = time.perf_counter()
@@ -520,7 +568,7 @@ def cpu_baseline(L, torch, synth, wl, budget_s):
             method.hca_attend(sq["hq"], hk, hv, M_HCA, sq["hkw"], sq["hvw"], np.array([CTX - LWIN]), W, pos, scale)
             elapsed += time.perf_counter() - t0 - t_gather
             done += 1
-    return done, elapsed
+    return done, elapsed, used
 
 
 def source_sha(path):
@@ -727,12 +775,14 @@ def main():
     ap.add_argument("--time-every", type=int, default=10,
                     help="per-kernel event timing on every n-th timed step (event-timed launches cost "
                          "a few microseconds each, so timing every step would slow the step itself)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-schedule", action="store_true", help="skip the 61-layer schedule timing")
     ap.add_argument("--no-fp8-kv", action="store_true", help="skip the step with FP8 K|V caches")
     ap.add_argument("--prefill", action="store_true",
                     help="measure the chunked-prefill stack instead of decode (prints its own line)")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill sub-object of the decode line")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing of the step")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device copy of this size after warm-up (reference for traffic counters)")
     args = ap.parse_args()
@@ -819,6 +869,12 @@ def main():
                      "timed_launches": len(pairs)},
         "kernels": kernels,
     }
+    if not args.no_graph:
+        g_ms, g_same = time_graph_replay(L, torch, wl, args.replicas, max(20, args.steps // 2))
+        out["graph_replay"] = {"ms_per_step": round(g_ms, 5), "eager_ms_per_step": round(ms, 5),
+                               "queries_per_s": round(B / (g_ms / 1e3), 1), "outputs_equal_eager": g_same,
+                               "note": "the same step captured once per replica into a HIP graph and replayed "
+                                       "(replicas rotating); value stays the eager rate"}
     us_fp4, us_bf16 = fp4_index_decode(L, torch, wl)
     out["fp4_indexer"] = {"avg_launch_us": round(us_fp4, 2), "bf16_query_avg_launch_us": round(us_bf16, 2),
                           "note": "the same 8 x 262144 MXFP4 keys with MXFP4 queries (scaled FP4 MFMA) and, timed "
@@ -844,12 +900,20 @@ def main():
         out["measured_ceilings"] = dict(ceil, roofline_frac_of_read=round(k["achieved_gbs"] / ceil["hbm_read_gbs"], 4),
                                         note="2 GiB streaming read (non-temporal loads) and back-to-back MFMAs on "
                                              "this GPU; context only, the roofline uses the published peaks")
+    if not args.no_prefill:
+        pf = run_prefill(L, torch, synth, max(1, args.steps // 10), max(1, args.warmup // 5))
+        out["prefill"] = {k: pf[k] for k in ("metric", "value", "unit", "ms_per_step", "ideal_ms_at_peak", "kernels",
+                                              "fp4_indexer", "config") if k in pf}
     if not args.no_cpu_baseline:
-        done, el = cpu_baseline(L, torch, synth, wl, args.cpu_seconds)
-        out["cpu_baseline"] = {"value": round(done / el, 3), "unit": "queries/s", "cores": 1, "kind": "oracle",
-                               "sample": f"{done} decode steps of single sequences (both layers; cycling over "
-                                         f"the {B} sequences of replica 0), {el:.1f} s on 1 host thread "
-                                         f"(float64 NumPy oracle)"}
+        done, el, used = cpu_baseline(L, torch, synth, wl, args.cpu_seconds, threads=None)
+        done1, el1, _ = cpu_baseline(L, torch, synth, wl, args.cpu_seconds, threads=1)
+        sample = (f"decode steps of single sequences (both layers; cycling over the {B} sequences of replica 0), "
+                  f"float64 NumPy oracle")
+        out["cpu_baseline"] = {"value": round(done / el, 3), "unit": "queries/s", "cores": used, "kind": "oracle",
+                               "host_cpus": os.cpu_count(),
+                               "sample": f"{done} {sample}, {el:.1f} s, BLAS on {used} threads"}
+        out["cpu_baseline_1_thread"] = {"value": round(done1 / el1, 3), "unit": "queries/s", "cores": 1,
+                                        "kind": "oracle", "sample": f"{done1} {sample}, {el1:.1f} s on 1 thread"}
     print(json.dumps(out), flush=True)
 
 

@@ -328,10 +328,16 @@ __device__ __forceinline__ void local_select(const float* sc, uint32_t nv, const
   }
   uint64_t masks[STEPS];
   uint32_t wtot = 0;
-  if (w0 + KPW <= nv) {                                      // the wave's keys are all visible
+  if (w0 + KPW <= nv && keep_bin > 0) {                      // the wave's keys are all visible
+    // score_key is monotone, so "key >= the bin's first key" is one float compare against
+    // the smallest score of bin keep_bin (nothing is kept past the last bin)
+    const uint32_t kf = keep_bin << (32 - kHistBits);
+    const float thr = keep_bin >= (uint32_t)kHistBins ? INFINITY
+                                                       : __uint_as_float(kf & 0x80000000u ? kf & 0x7fffffffu : ~kf);
+    const bool none = keep_bin >= (uint32_t)kHistBins;
 #pragma unroll
     for (int u = 0; u < STEPS; ++u) {
-      masks[u] = __ballot((score_key(v[u]) >> (32 - kHistBits)) >= keep_bin);
+      masks[u] = __ballot(!none && v[u] >= thr);
       wtot += (uint32_t)__popcll(masks[u]);
     }
   } else {

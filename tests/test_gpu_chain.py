@@ -298,3 +298,57 @@ def test_fp8kv_attention_is_bitwise_deterministic():
     torch.cuda.synchronize()
     for x, y in zip(*res):
         assert torch.equal(x, y)
+
+
+def test_decode_calls_replayed_from_a_hip_graph():
+    """The decode calls (pooling, indexer + top-k, CSA and HCA attention) captured into one
+    HIP graph: several replays, with eager work and synchronisations between them, each give
+    the eager result bit for bit (the calls record kernels only, no memset nodes)."""
+    B, N, NH, H, D, HI, DI, k, W, LW = 4, 65536, 2048, 64, 512, 8, 128, 512, 128, 128
+    p = 4 * N - 1
+    kvc = synth.device_normal((B, N, 2 * D), 9600, torch.bfloat16)
+    hkvc = synth.device_normal((B, NH, 2 * D), 9601, torch.bfloat16)
+    ki = torch.empty((B, N, DI // 2), dtype=torch.uint8, device="cuda")
+    ks = torch.empty((B, N, DI // 32), dtype=torch.uint8, device="cuda")
+    L.csa_compress(synth.device_normal((B, N, DI), 9602, torch.float32), torch.zeros((B, N), device="cuda"),
+                   torch.zeros(1, device="cuda"), 1, L.MXFP4_DTYPE, out=ki, out_scale=ks)
+    kvw = synth.device_normal((B, LW, 2 * D), 9603, torch.bfloat16)
+    kiw = synth.device_normal((B, LW, DI), 9604, torch.bfloat16)
+    gate = synth.device_normal((B, LW), 9605, torch.float32)
+    bias4, bias128 = synth.device_normal((4,), 9606, torch.float32), synth.device_normal((128,), 9607, torch.float32)
+    q, hq = synth.device_normal((B, 1, H, D), 9608, torch.bfloat16), synth.device_normal((B, 1, H, D), 9609, torch.bfloat16)
+    qi, wi = synth.device_normal((B, 1, HI, DI), 9610, torch.bfloat16), synth.device_uniform((B, 1, HI), 9611)
+    qpos = torch.full((B, 1), p, dtype=torch.int32, device="cuda")
+    wp0 = torch.full((B,), p + 1 - LW, dtype=torch.int32, device="cuda")
+    g4 = gate[:, LW - 4:].contiguous()
+    scale = 1.0 / math.sqrt(D)
+    idx = torch.empty((B, 1, k), dtype=torch.int32, device="cuda")
+    o, lse = torch.empty_like(q), torch.empty((B, 1, H), device="cuda")
+    ho, hlse = torch.empty_like(hq), torch.empty((B, 1, H), device="cuda")
+    ws = {n: torch.empty(64 << 20, dtype=torch.uint8, device="cuda") for n in ("i", "c", "h")}
+
+    def step():
+        L.csa_compress2(kvw[:, LW - 4:], kiw[:, LW - 4:], g4, bias4, 4, kvc[:, N - 1:], ki[:, N - 1:], ks[:, N - 1:])
+        L.csa_index_topk(qi, wi, ki, qpos, 4, k, ki_scale=ks, out_idx=idx, workspace=ws["i"])
+        L.csa_attend(q, kvc[..., :D], kvc[..., D:], idx, kvw[..., :D], kvw[..., D:], wp0, W, qpos, scale, out=o, lse=lse,
+                     workspace=ws["c"])
+        L.csa_compress(kvw, gate, bias128, 128, torch.bfloat16, out=hkvc[:, NH - 1:])
+        L.hca_attend(hq, hkvc[..., :D], hkvc[..., D:], 128, kvw[..., :D], kvw[..., D:], wp0, W, qpos, scale, out=ho,
+                     lse=hlse, workspace=ws["h"])
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        step()
+        torch.cuda.synchronize()
+        ref = [t.clone() for t in (idx, o, lse, ho, hlse)]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            step()
+    for rep in range(3):
+        for t in (idx, o, lse, ho, hlse):
+            t.zero_()                                              # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, r in zip((idx, o, lse, ho, hlse), ref):
+            assert torch.equal(a, r), f"replay {rep} differs from the eager step"
