@@ -32,6 +32,8 @@
  *     one workspace must not run concurrently.
  *   - The caller owns every buffer.  Inputs are read-only; outputs are fully
  *     overwritten; inputs, outputs and workspace must not overlap.
+ *   - Size, count and stride arguments must lie in [0, 2^40] (products of two of them
+ *     that the calls bound, such as B*Q, are checked without overflow).
  *   - All arguments are validated on the host before anything is launched; a bad
  *     argument returns DSV4_ERR_INVALID_ARG, an unsupported combination
  *     DSV4_ERR_UNSUPPORTED, a too-small workspace DSV4_ERR_WORKSPACE, a failed launch

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 
 #include "dsv4attn.h"
@@ -63,6 +64,22 @@ dsv4_status launched(hipError_t e, const char* what) {
 
 bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 
+// Every size, count and stride argument is at most kMaxExtent, so that the products the
+// validation and the launch plans form stay far inside int64_t; size_mul forms the ones
+// that involve two caller-given sizes.
+constexpr int64_t kMaxExtent = (int64_t)1 << 40;
+bool extent_ok(std::initializer_list<int64_t> v) {
+  for (int64_t x : v)
+    if (x < 0 || x > kMaxExtent) return false;
+  return true;
+}
+// a * b for non-negative sizes, or -1 when the product would exceed 2^62
+int64_t size_mul(int64_t a, int64_t b) {
+  if (a < 0 || b < 0) return -1;
+  if (a != 0 && b > ((int64_t)1 << 62) / a) return -1;
+  return a * b;
+}
+
 #define REQUIRE(cond, ...)                                  \
   do {                                                      \
     if (!(cond)) return fail(DSV4_ERR_INVALID_ARG, __VA_ARGS__); \
@@ -109,6 +126,8 @@ struct AttendCommon {
 
 dsv4_status check_attend(const char* what, const AttendCommon& c) {
   REQUIRE(c.B >= 0 && c.Q >= 0 && c.N >= 0 && c.L >= 0 && c.W >= 0, "%s: sizes must be non-negative", what);
+  REQUIRE(extent_ok({c.B, c.Q, c.N, c.L, c.kv_bstride, c.kv_rstride, c.w_rstride}),
+          "%s: sizes and strides must lie in [0, 2^40]", what);
   REQUIRE(c.H > 0 && c.D > 0, "%s: H and D must be positive", what);
   SUPPORT(c.dt == DSV4_F32 || c.dt == DSV4_BF16, "%s: dt must be DSV4_F32 or DSV4_BF16", what);
   if (c.dt == DSV4_BF16) {
@@ -126,8 +145,9 @@ dsv4_status check_attend(const char* what, const AttendCommon& c) {
           (long long)c.w_rstride, c.D);
   if (c.dt == DSV4_BF16)
     REQUIRE(c.kv_rstride % 8 == 0 && c.w_rstride % 8 == 0, "%s: bf16 row strides must be multiples of 8", what);
-  REQUIRE(c.B * c.Q <= 65535, "%s: B*Q must be <= 65535", what);
-  if (c.B * c.Q > 0) {
+  const int64_t BQ = size_mul(c.B, c.Q);
+  REQUIRE(BQ >= 0 && BQ <= 65535, "%s: B*Q must be <= 65535", what);
+  if (BQ > 0) {
     REQUIRE(c.q && c.out && c.q_pos, "%s: q, out and q_pos must not be NULL", what);
     REQUIRE(c.win_pos0 || c.W <= c.L, "%s: a ring window (win_pos0 == NULL) needs W (%d) <= L (%lld)", what, c.W,
             (long long)c.L);
@@ -143,6 +163,8 @@ dsv4_status check_compress(const char* what, const void* x, int x_dt, const floa
                            int64_t B, int64_t T, int64_t C, int32_t m, int64_t x_bstride, void* y, uint8_t* y_scale,
                            int y_dt, int64_t y_bstride, dsv4::CompressArgs* out) {
   REQUIRE(B >= 0 && T >= 0 && C > 0, "%s: need B >= 0, T >= 0, C > 0", what);
+  REQUIRE(extent_ok({B, T, C, x_bstride, y_bstride}), "%s: sizes and strides must lie in [0, 2^40]", what);
+  REQUIRE(size_mul(B, T) >= 0 && size_mul(B, T) <= kMaxExtent, "%s: B*T must be <= 2^40", what);
   REQUIRE(m >= 1 && m <= 1024, "%s: m must be in [1, 1024], got %d", what, m);
   REQUIRE(T % m == 0, "%s: T (%lld) must be a multiple of m (%d)", what, (long long)T, m);
   SUPPORT(x_dt == DSV4_F32 || x_dt == DSV4_BF16, "%s: x_dt must be F32 or BF16", what);
@@ -303,6 +325,7 @@ dsv4_status kv_cache_append(const void* x_new, int x_dt, const float* gate_new, 
                             void* y, uint8_t* y_scale, int y_dt, int64_t N, int64_t y_bstride, hipStream_t stream) {
   const char* what = "kv_cache_append";
   REQUIRE(B >= 0 && C > 0 && N >= 0, "%s: need B >= 0, C > 0, N >= 0", what);
+  REQUIRE(extent_ok({B, C, N, L, y_bstride}), "%s: sizes and strides must lie in [0, 2^40]", what);
   REQUIRE(m >= 1 && m <= 1024, "%s: m must be in [1, 1024], got %d", what, m);
   SUPPORT(x_dt == DSV4_F32 || x_dt == DSV4_BF16, "%s: x_dt must be F32 or BF16", what);
   SUPPORT(y_dt >= DSV4_F32 && y_dt <= DSV4_FP8_KV, "%s: unknown y_dt %d", what, y_dt);
@@ -342,11 +365,12 @@ dsv4_status index_topk_impl(const char* what, const void* qi, int qi_dt, const f
                             int32_t* out_idx, float* out_score, void* workspace, size_t* ws_bytes,
                             hipStream_t stream, bool noalloc) {
   REQUIRE(B >= 0 && Q >= 0 && N >= 0, "%s: sizes must be non-negative", what);
+  REQUIRE(extent_ok({B, Q, N, ki_bstride}), "%s: sizes and strides must lie in [0, 2^40]", what);
   REQUIRE(m >= 1, "%s: m must be >= 1", what);
   REQUIRE(k >= 1 && k <= 4096, "%s: k must be in [1, 4096], got %d", what, k);
   REQUIRE(N < (int64_t)1 << 31, "%s: N must be < 2^31", what);
   REQUIRE(ki_bstride == 0 || ki_bstride >= N, "%s: ki_bstride must be 0 or >= N", what);
-  REQUIRE(B * Q <= 65535, "%s: B*Q must be <= 65535", what);
+  REQUIRE(size_mul(B, Q) >= 0 && size_mul(B, Q) <= 65535, "%s: B*Q must be <= 65535", what);
   int kind;
   if (qi_dt == DSV4_F32 && ki_dt == DSV4_F32) kind = dsv4::KEY_F32;
   else if (qi_dt == DSV4_BF16 && ki_dt == DSV4_BF16) kind = dsv4::KEY_BF16;

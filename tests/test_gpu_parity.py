@@ -854,6 +854,55 @@ def test_attend_f32_csa_and_hca(D, H):
     assert row_rel_err(host(oh), o_ref) <= 1e-4 and lse_abs_err(host(lseh), lse_ref) <= 1e-4
 
 
+@pytest.mark.parametrize("csa,B,Q,H", [(True, 8, 1, 64), (False, 8, 1, 64), (True, 16, 1, 32), (False, 4, 2, 64),
+                                       (True, 32, 1, 64), (False, 11, 1, 48)])
+def test_attend_decode_batches(csa, B, Q, H):
+    """Decode batches of 4 to 32 sequences (key ranges split over the CUs, parts merged):
+    against the oracle, with a sequence whose key set is empty and one with a short list; a
+    second call on other inputs right after the first; the first call again, bitwise."""
+    cfg = 520 + 7 * B + H + csa
+    D, L_, W, m = 512, 160, 128, 128
+    N = 3000 if csa else 1000
+    k = 512
+    scale = 1.0 / math.sqrt(D)
+    dec = codecs.decode_bf16
+
+    def inputs(c):
+        q, kc, vc, kw, vw = _attn_inputs(c, B, Q, H, D, N, L_)
+        T = N * (4 if csa else m)
+        win_pos0 = np.full(B, T - L_, dtype=np.int32)
+        pos = (T - 1 - np.arange(B * Q, dtype=np.int32) % 23).reshape(B, Q)
+        win_pos0[0] = 10 ** 6                                   # sequence 0: window ahead of the query
+        pos[0, :] = 5 if not csa else pos[0, :]                 # HCA: no visible entry either
+        idx = synth.sorted_unique_indices(c, synth.IDX, B * Q, N, k).reshape(B, Q, k)
+        if csa:
+            idx[0] = -1                                         # CSA: empty list for sequence 0
+            idx[B - 1, 0, 100:] = -1                            # a short list
+        return (q, kc, vc, kw, vw), idx, win_pos0, pos
+
+    def run(c):
+        (q, kc, vc, kw, vw), idx, win_pos0, pos = inputs(c)
+        t = [dev_bf16(a) for a in (q, kc, vc, kw, vw)]
+        (qd, qb), (kcd, kcb), (vcd, vcb), (kwd, kwb), (vwd, vwb) = t
+        if csa:
+            o, lse = L.csa_attend(qd, kcd, vcd, dev(idx), kwd, vwd, dev(win_pos0), W, dev(pos), scale)
+            ref = method.csa_attend(dec(qb), dec(kcb), dec(vcb), idx, dec(kwb), dec(vwb), win_pos0, W, pos, scale)
+        else:
+            o, lse = L.hca_attend(qd, kcd, vcd, m, kwd, vwd, dev(win_pos0), W, dev(pos), scale)
+            ref = method.hca_attend(dec(qb), dec(kcb), dec(vcb), m, dec(kwb), dec(vwb), win_pos0, W, pos, scale)
+        return o, lse, ref
+
+    o1, lse1, ref1 = run(cfg)
+    o2, lse2, ref2 = run(cfg + 1)
+    o3, lse3, _ = run(cfg)
+    torch.cuda.synchronize()
+    for o, lse, (o_ref, lse_ref) in ((o1, lse1, ref1), (o2, lse2, ref2)):
+        assert torch.all(o[0].float() == 0) and torch.all(torch.isneginf(lse[0]))
+        assert row_rel_err(host(o), o_ref) <= 1e-2
+        assert lse_abs_err(host(lse), lse_ref) <= 1e-2
+    assert torch.equal(o1, o3) and torch.equal(lse1, lse3)
+
+
 def test_attend_empty_key_set_and_determinism():
     B, Q, H, D, N, L_ = 1, 2, 64, 512, 64, 32
     q, kc, vc, kw, vw = _attn_inputs(500, B, Q, H, D, N, L_)
