@@ -90,6 +90,23 @@ const char* dsv4_last_error(void);
 dsv4_status dsv4_time_next_kernel(hipEvent_t start, hipEvent_t stop);
 
 /*
+ * Debug builds (libdsv4attn_debug.so, compiled with -DDSV4_DEBUG): the kernels also check
+ * facts that the release build only enforces by clamping, and record each failed check as
+ * a bit (results are the release build's):
+ *   1   a top-k scan range's candidate count read back above the keys the range holds
+ *   2   the threshold bin, or the count of keys above it, out of range
+ *   4   a selected candidate's key index at or past the visible keys
+ *   8   a chunk's kept or visible count read back above what the chunk can hold
+ *   16  more keys at or above a chunk's kept bin than the chunk keeps
+ *   32  an index entry of csa_attend outside [0, N) other than -1 (skipped, as documented)
+ *   64  a negative query position (its key set is empty)
+ * *flags receives the bits recorded on the current device since the last call, which
+ * clears them (0xffffffff if they could not be read).  The call synchronises the device.
+ * Release builds set *flags = 0 and return DSV4_ERR_UNSUPPORTED.
+ */
+dsv4_status dsv4_debug_flags(uint32_t* flags);
+
+/*
  * csa_compress — softmax-gated pooling of disjoint blocks of m raw tokens  [CSA], [HCA], [P2 §4].
  *
  *   y[b,i,:] = sum_{j<m} a_j * x[b, i*m + j, :],

@@ -23,6 +23,8 @@ FP8_KV_DTYPE = "fp8_kv"          # marker for FP8 K|V rows (E4M3 codes, bf16 RoP
 FP8_ROPE_DIMS = 64               # bf16 tail of an FP8 K row
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsv4attn.so")
+# the same library built with -DDSV4_DEBUG (kernel-side checks, see dsv4_debug_flags)
+DEBUG_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsv4attn_debug.so")
 _lib = None
 
 _p = ctypes.c_void_p
@@ -33,6 +35,7 @@ _SIGS = {
     "dsv4_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "dsv4_last_error": ([], ctypes.c_char_p),
     "dsv4_time_next_kernel": ([_p, _p], ctypes.c_int),
+    "dsv4_debug_flags": ([ctypes.POINTER(ctypes.c_uint32)], ctypes.c_int),
     "csa_compress": ([_p, ctypes.c_int, _p, _p, _i64, _i64, _i64, _i32, _i64, _p, _p, ctypes.c_int, _i64, _p],
                      ctypes.c_int),
     "csa_compress2": ([_p, _p, ctypes.c_int, _p, _p, _i64, _i64, _i32, _i64, _i64, _p, _p, ctypes.c_int, _i64, _i64,
@@ -63,18 +66,49 @@ class LibError(RuntimeError):
         self.status = status
 
 
+def load_library(path: str) -> ctypes.CDLL:
+    """Load a build of the C library and declare its entry points."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m long_context_attention_25_amd.build`")
+    cdll = ctypes.CDLL(path)
+    for name, (args, res) in _SIGS.items():
+        fn = getattr(cdll, name)
+        fn.argtypes = args
+        fn.restype = res
+    return cdll
+
+
 def lib() -> ctypes.CDLL:
     """The loaded C library (torch is imported first so that one HIP runtime is shared)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m long_context_attention_25_amd.build`")
-        _lib = ctypes.CDLL(LIB_PATH)
-        for name, (args, res) in _SIGS.items():
-            fn = getattr(_lib, name)
-            fn.argtypes = args
-            fn.restype = res
+        _lib = load_library(LIB_PATH)
     return _lib
+
+
+class use_library:
+    """Route the binding's calls through another build (e.g. DEBUG_LIB_PATH) inside a with block."""
+
+    def __init__(self, path: str):
+        self.cdll = load_library(path)
+
+    def __enter__(self):
+        global _lib
+        self.saved = lib()
+        _lib = self.cdll
+        return self.cdll
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
+
+
+def debug_flags() -> int:
+    """Kernel-side check bits recorded since the last read (debug build loaded; see use_library)."""
+    v = ctypes.c_uint32(0)
+    _check(lib().dsv4_debug_flags(ctypes.byref(v)))
+    return v.value
 
 
 def _check(status: int) -> None:

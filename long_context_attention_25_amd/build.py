@@ -1,11 +1,14 @@
-"""Build libdsv4attn.so (all HIP kernels + the C ABI) for gfx950 with hipcc.
+"""Build libdsv4attn.so (all HIP kernels + the C ABI) for gfx950 with hipcc, its debug
+build libdsv4attn_debug.so (-DDSV4_DEBUG: kernel-side checks, read with dsv4_debug_flags)
+and the measurement probes libdsv4probe.so.
 
     python -m long_context_attention_25_amd.build
 
-The library is built in-tree next to this file.  Every call recompiles.
+The libraries are built in-tree next to this file.  Every call recompiles.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import glob
 import os
 import subprocess
@@ -37,16 +40,30 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+DEBUG_LIB = os.path.join(HERE, "libdsv4attn_debug.so")
+
+
 def build(verbose: bool = False) -> str:
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [os.path.join(CSRC, "abi.cpp"), PROBE_SRC]
+    """The release library, its debug build (kernel-side checks) and the probe library."""
+    with concurrent.futures.ThreadPoolExecutor(2) as ex:   # the two builds' compiles run side by side
+        for f in [ex.submit(_build, verbose, d) for d in (False, True)]:
+            f.result()
+    return LIB
+
+
+def _build(verbose: bool, debug: bool) -> None:
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [os.path.join(CSRC, "abi.cpp")]
+    if not debug:
+        srcs.append(PROBE_SRC)
     objs = []
-    build_dir = os.path.join(HERE, "_build")
+    build_dir = os.path.join(HERE, "_build", "debug" if debug else "release")
     os.makedirs(build_dir, exist_ok=True)
     procs = []
     for s in srcs:
         o = os.path.join(build_dir, os.path.basename(s) + ".o")
         lang = ["-x", "hip"] if s.endswith(".cpp") else []
-        cmd = [_hipcc(), *HIPCC_FLAGS, *lang, "-I", os.path.join(HERE, "..", "include"), "-c", s, "-o", o]
+        cmd = [_hipcc(), *HIPCC_FLAGS, *(["-DDSV4_DEBUG"] if debug else []), *lang, "-I",
+               os.path.join(HERE, "..", "include"), "-c", s, "-o", o]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((s, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
@@ -63,13 +80,16 @@ def build(verbose: bool = False) -> str:
         for s, t in failed:
             sys.stderr.write(f"--- {s}\n{t}\n")
         raise RuntimeError(f"hipcc failed for {[os.path.basename(s) for s, _ in failed]}")
-    probe_obj = objs.pop()                   # the last source is the probe library's
-    for lib, parts in ((LIB, objs), (PROBE_LIB, [probe_obj])):
+    if debug:
+        targets = ((DEBUG_LIB, objs),)
+    else:
+        probe_obj = objs.pop()               # the last source is the probe library's
+        targets = ((LIB, objs), (PROBE_LIB, [probe_obj]))
+    for lib, parts in targets:
         tmp = lib + ".tmp"
         cmd = [_hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *parts]
         subprocess.run(cmd, check=True)
         os.replace(tmp, lib)
-    return LIB
 
 
 if __name__ == "__main__":

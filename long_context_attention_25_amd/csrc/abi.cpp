@@ -280,6 +280,17 @@ dsv4_status dsv4_time_next_kernel(hipEvent_t start, hipEvent_t stop) {
 
 int dsv4_version(void) { return 100; }
 
+dsv4_status dsv4_debug_flags(uint32_t* flags) {
+  REQUIRE(flags != nullptr, "dsv4_debug_flags: flags must not be NULL");
+  *flags = 0;
+#ifdef DSV4_DEBUG
+  *flags = dsv4::debug_flags_attend() | dsv4::debug_flags_index() | dsv4::debug_flags_compress();
+  return ok();
+#else
+  return fail(DSV4_ERR_UNSUPPORTED, "dsv4_debug_flags: this library was built without DSV4_DEBUG");
+#endif
+}
+
 const char* dsv4_status_string(int s) {
   switch (s) {
     case DSV4_OK: return "DSV4_OK";

@@ -53,6 +53,7 @@ struct KeyRange {
 // (no win_pos0) wp0 is 0, window "rows" are absolute positions and wrow() maps them to
 // buffer rows (position mod L); the caller keeps the last L >= W positions there.
 __device__ __forceinline__ KeyRange key_range(const AttendArgs& a, int64_t p, int64_t wp0) {
+  DSV4_DCHECK(p >= 0, kDbgQueryPos);
   KeyRange r;
   if (a.csa) {
     r.n_c = a.N > 0 ? a.k : 0;   // with no compressed entries every list slot is empty
@@ -306,6 +307,7 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
     if (pos < s1) {
       if (pos < kr.n_c) {
         const int64_t j = a.csa ? (int64_t)list[pos - s0] : pos;
+        DSV4_DCHECK(j == -1 || (j >= 0 && j < a.N), kDbgIdxEntry);
         if (j >= 0 && j < a.N) {
           ok = true;
           kp = kc + j * krs;
@@ -686,6 +688,7 @@ __global__ __launch_bounds__(kThreads * 2) void attend_fp8kv_kernel(AttendArgs a
     if (pos < s1) {
       if (pos < kr.n_c) {
         const int64_t j = a.csa ? (int64_t)list[pos - s0] : pos;
+        DSV4_DCHECK(j == -1 || (j >= 0 && j < a.N), kDbgIdxEntry);
         if (j >= 0 && j < a.N) {
           ok = true;
           kp = kc + j * krs;
@@ -1574,5 +1577,7 @@ hipError_t launch_lse_merge(const float* o_parts, const float* lse_parts, int P,
 #undef DSV4_MERGE
   return hipGetLastError();
 }
+
+DSV4_DEBUG_READER(debug_flags_attend)
 
 }  // namespace dsv4

@@ -192,4 +192,44 @@ __device__ __forceinline__ T bit_cast_to(const uint4& v) {
   return __builtin_bit_cast(T, v);
 }
 
+// ------------------------------------------------------------------ debug builds
+// Built with -DDSV4_DEBUG, the kernels also check facts that the release build only
+// enforces by clamping (counts and indices read back from the workspace, the local
+// selection's staging) and caller inputs that it tolerates (index entries other than -1
+// outside [0, N), negative query positions).  A failed check sets its bit in the flag word
+// of its source file and the kernel goes on exactly as the release build does.
+enum DebugBit : uint32_t {
+  kDbgRangeCount = 1u << 0,   // a scan range's candidate count above its key count
+  kDbgThreshold = 1u << 1,    // the threshold bin, or the count above it, out of range
+  kDbgCandIndex = 1u << 2,    // a candidate's key index at or past the visible keys
+  kDbgLocalMeta = 1u << 3,    // a chunk's kept or visible count above what it can hold
+  kDbgLocalStage = 1u << 4,   // more keys at or above the kept bin than the chunk keeps
+  kDbgIdxEntry = 1u << 5,     // an index entry outside [0, N) other than -1
+  kDbgQueryPos = 1u << 6,     // a negative query position
+};
+#ifdef DSV4_DEBUG
+namespace {
+__device__ uint32_t g_debug_flags;
+}
+#define DSV4_DCHECK(cond, bit)                                            \
+  do {                                                                    \
+    if (!(cond)) atomicOr(&::dsv4::g_debug_flags, (uint32_t)(bit));       \
+  } while (0)
+// host: this source file's flags since the last read, cleared (all ones if unreadable)
+#define DSV4_DEBUG_READER(fn)                                                            \
+  uint32_t fn() {                                                                        \
+    uint32_t v = 0, z = 0;                                                               \
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_debug_flags), sizeof(v)) != hipSuccess ||   \
+        hipMemcpyToSymbol(HIP_SYMBOL(g_debug_flags), &z, sizeof(z)) != hipSuccess)       \
+      return 0xffffffffu;                                                                \
+    return v;                                                                            \
+  }
+#else
+#define DSV4_DCHECK(cond, bit) \
+  do {                         \
+  } while (0)
+#define DSV4_DEBUG_READER(fn) \
+  uint32_t fn() { return 0u; }
+#endif
+
 }  // namespace dsv4

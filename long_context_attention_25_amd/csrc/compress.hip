@@ -481,4 +481,6 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
   }
 }
 
+DSV4_DEBUG_READER(debug_flags_compress)
+
 }  // namespace dsv4

@@ -46,6 +46,7 @@ constexpr int keys_per_step() { return tiles_per_step<KIND, DI>() * 16 * 4; }   
 
 __device__ __forceinline__ uint32_t vis_blocks(const int32_t* q_pos, int64_t row, int m, int64_t N) {
   int64_t p = q_pos[row];
+  DSV4_DCHECK(p >= 0, kDbgQueryPos);
   int64_t n = (p + 1) / m;
   if (p < 0) n = 0;
   return (uint32_t)(n < N ? n : N);
@@ -360,6 +361,7 @@ __device__ __forceinline__ void local_select(const float* sc, uint32_t nv, const
     base += (uint32_t)__popcll(mask);
   }
   __syncthreads();
+  DSV4_DCHECK(misc[3] <= KL, kDbgLocalStage);
   const uint32_t count = misc[3] < KL ? misc[3] : KL;
   for (uint32_t j = tid; j < count; j += NT) out[j] = stage[j];
   if (tid == 0) {
@@ -864,9 +866,11 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
   auto range_count = [&](int64_t r) -> uint32_t {
     const uint32_t c_ = ccount[row * nch + r];
     const int64_t keys = (int64_t)n - r * rkeys < rkeys ? (int64_t)n - r * rkeys : rkeys;
+    DSV4_DCHECK((int64_t)c_ <= keys, kDbgRangeCount);
     return c_ < (uint64_t)keys ? c_ : (uint32_t)keys;
   };
   uint2 th = *reinterpret_cast<const uint2*>(thr + row * 2);
+  DSV4_DCHECK(th.x < (uint32_t)kHistBins && th.y < kk, kDbgThreshold);
   th.x &= kHistBins - 1;
   if (th.y > kk) th.y = kk;
   const uint32_t cnt0 = tid < nrange ? range_count(tid) : 0u;
@@ -982,6 +986,7 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
   for (uint32_t f = tid; f < c; f += NT) {
     const uint64_t comp = cand(f);
     const uint32_t j = ~(uint32_t)comp;
+    DSV4_DCHECK(comp < tsel || j < n, kDbgCandIndex);
     if (comp >= tsel && j < n) atomicOr(&bits[j >> 5], 1u << (j & 31));
   }
   __threadfence_block();
@@ -1180,6 +1185,7 @@ __global__ __launch_bounds__(FT) void select_local_kernel(
   for (int c = tid; c < nch; c += NT) {
     const uint4 mm = meta_g[row * nch + c];
     const int64_t keys = N - (int64_t)c * chunk < chunk ? N - (int64_t)c * chunk : chunk;
+    DSV4_DCHECK((int64_t)mm.y <= keys && mm.x <= (uint32_t)klocal && mm.x <= mm.y, kDbgLocalMeta);
     const uint32_t nvc = (int64_t)mm.y < keys ? mm.y : (uint32_t)keys;
     const uint32_t kept = mm.x < (uint32_t)klocal ? mm.x : (uint32_t)klocal;
     mnv[c] = nvc;
@@ -1239,11 +1245,13 @@ __global__ __launch_bounds__(FT) void select_local_kernel(
 #pragma unroll
     for (int u = 0; u < SPT; ++u) {
       const uint32_t j = ~(uint32_t)v[u];
+      DSV4_DCHECK(v[u] == 0ull || v[u] < T || j < n, kDbgCandIndex);
       if (v[u] != 0ull && v[u] >= T && j < n) atomicOr(&bits_l[j >> 5], 1u << (j & 31));
     }
     for (uint32_t f = tid; f < nexp; f += NT) {
       const uint64_t x = cand_l[f];
       const uint32_t j = ~(uint32_t)x;
+      DSV4_DCHECK(x < T || j < n, kDbgCandIndex);
       if (x >= T && j < n) atomicOr(&bits_l[j >> 5], 1u << (j & 31));
     }
   } else {
@@ -1512,5 +1520,7 @@ hipError_t launch_index_topk(const IndexArgs& a, void* ws, hipStream_t st) {
                        a.out_score);
   return hipGetLastError();
 }
+
+DSV4_DEBUG_READER(debug_flags_index)
 
 }  // namespace dsv4

@@ -120,6 +120,12 @@ struct AttendPlan {
 AttendPlan plan_attend(const AttendArgs& a);
 hipError_t launch_attend(const AttendArgs& a, const AttendPlan& p, void* ws, hipStream_t st);
 
+// Debug builds: the flags each source file's kernels recorded since the last read
+// (cleared by the read); release builds return 0.
+uint32_t debug_flags_attend();
+uint32_t debug_flags_index();
+uint32_t debug_flags_compress();
+
 hipError_t launch_lse_merge(const float* o_parts, const float* lse_parts, int P, int64_t R, int D,
                             void* out, bool out_f32, float* lse_out, hipStream_t st);
 

@@ -30,6 +30,18 @@ def test_every_declared_symbol_is_exported():
         assert hasattr(lib, n), n
 
 
+def test_debug_flags_release_and_debug_builds():
+    """The release build answers dsv4_debug_flags with DSV4_ERR_UNSUPPORTED; the debug build
+    exports every declared entry point too."""
+    v = ctypes.c_uint32(7)
+    assert L.lib().dsv4_debug_flags(ctypes.byref(v)) == 2 and v.value == 0
+    assert L.lib().dsv4_debug_flags(None) == 1
+    if os.path.exists(L.DEBUG_LIB_PATH):
+        dbg = ctypes.CDLL(L.DEBUG_LIB_PATH)
+        for n in declared_functions():
+            assert hasattr(dbg, n), n
+
+
 def test_version_and_status_strings():
     lib = L.lib()
     assert lib.dsv4_version() >= 100
