@@ -542,6 +542,12 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
     nslots += nq[t] > 0 ? QPT : 0;
   }
   for (int i = threadIdx.x; i < nslots * kHistWords; i += kThreads) hist_l[i] = 0u;
+  // kLocal: the visible keys of each query of the tile, for the epilogue (loaded here, where
+  // the latency is hidden behind the first key loads)
+  __shared__ uint32_t nvis_ep[kLocal ? QPT : 1];
+  if constexpr (kLocal) {
+    if ((int)threadIdx.x < nq[0]) nvis_ep[threadIdx.x] = vis_blocks(q_pos, b * Q + qt0 * QPT + threadIdx.x, m, N);
+  }
 
   // A operands: query rows (row = lane % 16 = qslot * HI + head) of each query tile
   const int qs_a = col / HI, h_a = col % HI;
@@ -671,8 +677,7 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
     // 16-byte stores (they are read back only to widen a chunk, or for out_score)
     for (int s = 0; s < nq[0]; ++s) {
       const int64_t row = b * Q + qt0 * QPT + s;
-      const int64_t nvis_s = vis_blocks(q_pos, row, m, N);
-      int64_t nv = nvis_s - c0;
+      int64_t nv = (int64_t)nvis_ep[s] - c0;
       nv = nv < 0 ? 0 : (nv > c1 - c0 ? c1 - c0 : nv);
       const int64_t slot = row * nch + blockIdx.x;
       local_select<kThreads>(sc_l + s * chunk, (uint32_t)nv, hist_l + s * kHistWords, (uint32_t)klocal, (uint32_t)c0,
@@ -1057,13 +1062,18 @@ constexpr int kLocalRadixBits = 12;
 
 // kth_largest over values held in registers plus a list in LDS: thread t holds v[u] (0 for an
 // empty slot) and the composites ext[0 .. next) are read from LDS.  Same contract and result
-// as kth_largest.
+// as kth_largest.  Each round takes three barriers: the digit histogram (4 bins per thread,
+// one 16-byte read) is scanned within each wave, the waves' totals are added from LDS by
+// every thread, and the histogram of the next round is a second buffer cleared meanwhile.
+// hbin2: 2 << RB words; tmp: 4 NT / 64 words; misc: 3 words.
 template <int NT, int SPT, int RB>
 __device__ __forceinline__ uint64_t kth_largest_regs(const uint64_t (&v)[SPT], const uint64_t* ext, uint32_t next,
-                                                     uint32_t need, uint32_t* hbin, uint32_t* tmp, uint32_t* misc) {
+                                                     uint32_t need, uint32_t* hbin2, uint32_t* tmp, uint32_t* misc) {
   constexpr int kBins = 1 << RB;
-  constexpr int BPT = kBins / NT;
-  const int tid = threadIdx.x;
+  constexpr int NW = NT / kWave;
+  static_assert(kBins == 4 * NT, "four digit bins per thread");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  *reinterpret_cast<uint4*>(hbin2 + 4 * tid) = make_uint4(0u, 0u, 0u, 0u);   // round 0's histogram
   uint64_t mn = ~0ull, mx = 0ull;
 #pragma unroll
   for (int u = 0; u < SPT; ++u) {
@@ -1077,54 +1087,42 @@ __device__ __forceinline__ uint64_t kth_largest_regs(const uint64_t (&v)[SPT], c
     mn = x < mn ? x : mn;
     mx = x > mx ? x : mx;
   }
-  block_minmax_u64<NT>(mn, mx, tmp);
+  block_minmax_u64<NT>(mn, mx, tmp);                         // (its barriers order the clear)
   const uint64_t diff = mn ^ mx;
   int hi = diff ? 64 - __clzll((long long)diff) : 0;         // bits [hi-1 : 0] still open
   uint64_t prefix = hi == 64 ? 0ull : (mx >> hi) << hi;
+  int buf = 0;
   while (true) {
+    uint32_t* hb = hbin2 + buf * kBins;
     const int wd = hi < RB ? hi : RB;
     const int sh = hi - wd;
-    const int nd = 1 << wd;
-    for (int i = tid; i < kBins; i += NT) hbin[i] = 0u;
-    __syncthreads();
+    const uint32_t dmask = (1u << wd) - 1u;
 #pragma unroll
     for (int u = 0; u < SPT; ++u)
       if (v[u] != 0ull && (hi == 64 || (v[u] >> hi) == (prefix >> hi)))
-        atomicAdd(&hbin[(uint32_t)(v[u] >> sh) & (uint32_t)(nd - 1)], 1u);
+        atomicAdd(&hb[(uint32_t)(v[u] >> sh) & dmask], 1u);
     for (uint32_t f = tid; f < next; f += NT) {
       const uint64_t x = ext[f];
-      if (hi == 64 || (x >> hi) == (prefix >> hi)) atomicAdd(&hbin[(uint32_t)(x >> sh) & (uint32_t)(nd - 1)], 1u);
+      if (hi == 64 || (x >> hi) == (prefix >> hi)) atomicAdd(&hb[(uint32_t)(x >> sh) & dmask], 1u);
     }
     __syncthreads();
-    uint32_t hv[BPT];
-    uint32_t tsum = 0;
-    if constexpr (BPT == 4) {
-      // thread t holds digits nd-1-4t .. nd-4-4t: one 16-byte read of 4 adjacent bins
-      const int d0 = nd - 4 - 4 * tid;
-      if (d0 >= 0) {
-        const uint4 x = *reinterpret_cast<const uint4*>(hbin + d0);
-        hv[0] = x.w; hv[1] = x.z; hv[2] = x.y; hv[3] = x.x;
-      } else {
+    // thread t holds digits kBins-1-4t .. kBins-4-4t (descending; digits >= 2^wd are empty)
+    const uint4 x = *reinterpret_cast<const uint4*>(hb + kBins - 4 - 4 * tid);
+    *reinterpret_cast<uint4*>(hbin2 + (buf ^ 1) * kBins + 4 * tid) = make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t hv[4] = {x.w, x.z, x.y, x.x};
+    const uint32_t tsum = hv[0] + hv[1] + hv[2] + hv[3];
+    const uint32_t incl = wave_incl_scan(tsum);
+    if (lane == 63) tmp[wave] = incl;
+    __syncthreads();
+    uint32_t ex = incl - tsum;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) hv[i] = nd - 1 - 4 * tid - i >= 0 ? hbin[nd - 1 - 4 * tid - i] : 0u;
-      }
-      tsum = hv[0] + hv[1] + hv[2] + hv[3];
-    } else {
-#pragma unroll
-      for (int i = 0; i < BPT; ++i) {
-        const int d = BPT * tid + i;
-        hv[i] = d < nd ? hbin[nd - 1 - d] : 0u;
-        tsum += hv[i];
-      }
-    }
-    uint32_t tot;
-    const uint32_t ex = block_scan<NT>(tsum, tmp, &tot);
+    for (int w = 0; w < NW; ++w) ex += w < wave ? tmp[w] : 0u;
     if (ex < need && need <= ex + tsum) {
       uint32_t acc = ex;
 #pragma unroll
-      for (int i = 0; i < BPT; ++i) {
+      for (int i = 0; i < 4; ++i) {
         if (acc < need && need <= acc + hv[i]) {
-          misc[0] = (uint32_t)(nd - 1 - (BPT * tid + i));
+          misc[0] = (uint32_t)(kBins - 1 - (4 * tid + i));
           misc[1] = acc;
           misc[2] = hv[i];
         }
@@ -1136,7 +1134,7 @@ __device__ __forceinline__ uint64_t kth_largest_regs(const uint64_t (&v)[SPT], c
     prefix |= (uint64_t)misc[0] << sh;
     const bool done = misc[2] == need || sh == 0;
     hi = sh;
-    __syncthreads();
+    buf ^= 1;
     if (done) break;
   }
   return prefix;
@@ -1151,7 +1149,7 @@ __global__ __launch_bounds__(FT) void select_local_kernel(
   constexpr int SPT = kLocalCap / NT;                         // staged slots per thread
   __shared__ uint64_t cand_l[kExpCap];                       // candidates added by expansion
   __shared__ uint32_t bits_l[kLdsBitmapKeys / 32];           // also kth_largest's histogram
-  __shared__ uint32_t hbin_l[1 << kLocalRadixBits];          // kth_largest_regs' histogram
+  __shared__ __attribute__((aligned(16))) uint32_t hbin_l[2 << kLocalRadixBits];   // kth_largest_regs' histograms
   __shared__ uint32_t mcnt[kMaxLocalChunks];
   __shared__ uint32_t mnv[kMaxLocalChunks];
   __shared__ uint64_t mfloor[kMaxLocalChunks];
