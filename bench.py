@@ -57,8 +57,10 @@ def algorithmic_bytes():
 # Algorithmic bytes per launch of the three big kernels (what each must read once; the
 # split-K partials, scores and histograms are excluded).
 KERNEL_BYTES = {
-    # MXFP4 key codes + E8M0 scales of every visible block, indexer queries, head weights
-    "index_mfma_kernel": B * N_CSA * (DI // 2 + DI // 32) + B * HI * DI * 2 + B * HI * 4,
+    # MXFP4 key codes + E8M0 scales of every visible block, indexer queries, head weights,
+    # and the pooling of the newest block done in the same launch (raw rows in, pooled rows out)
+    "index_mfma_kernel": B * N_CSA * (DI // 2 + DI // 32) + B * HI * DI * 2 + B * HI * 4
+    + B * (M_CSA * (2 * D + DI) * 2 + M_CSA * 4 + 2 * D * 2 + (DI // 2 + DI // 32)),
     # the selected K/V rows + window rows, q, the index list
     "attend_bf16_kernel (CSA)": B * (TOPK + W) * 2 * D * 2 + B * H * D * 2 + B * TOPK * 4,
     # every visible K/V entry + window rows, q
@@ -150,19 +152,16 @@ def marshal_step(L, torch, wl, rep):
     g4 = t["gate"][:, LWIN - M_CSA:].contiguous()
     t["g4"] = g4
     # CSA: the newest 4-token block -> entry N_CSA-1 of K|V (bf16, the 2D channels side by
-    # side) and of the indexer key (MXFP4), one launch for both (same gates)
-    calls.append((lib.csa_compress2, (P(t["kvw"][:, LWIN - M_CSA:]), P(t["kiw"][:, LWIN - M_CSA:]), L.BF16, P(g4),
-                                      P(t["bias"]), B, M_CSA, M_CSA, 2 * D, LWIN, P(wl.kvc[:, N_CSA - 1:]), None,
-                                      L.BF16, N_CSA, DI, LWIN, P(t["ki"][:, N_CSA - 1:]), P(t["ks"][:, N_CSA - 1:]),
-                                      L.MXFP4, N_CSA, st)))
-    # CSA: indexer + top-k
+    # side) and of the indexer key (MXFP4), pooled in the indexer launch, then indexer + top-k
+    t["pool"] = L.BlockPool(P(t["kvw"][:, LWIN - M_CSA:]), P(t["kiw"][:, LWIN - M_CSA:]), P(g4), P(t["bias"]), 2 * D,
+                            LWIN, LWIN, P(wl.kvc[:, N_CSA - 1]), None, L.BF16, N_CSA, N_CSA - 1)
     n = ctypes.c_size_t(0)
-    idx_args = (P(t["qi"]), L.BF16, P(t["wi"]), P(t["ki"]), P(t["ks"]), L.MXFP4, P(wl.q_pos), B, 1, HI, DI, N_CSA, 0,
-                M_CSA, TOPK, P(t["idx"]), None)
-    assert lib.csa_index_topk(*idx_args, None, ctypes.byref(n), st) == 0
+    idx_args = (ctypes.byref(t["pool"]), P(t["qi"]), L.BF16, P(t["wi"]), P(t["ki"]), P(t["ks"]), L.MXFP4,
+                P(wl.q_pos), B, 1, HI, DI, N_CSA, 0, M_CSA, TOPK, P(t["idx"]), None)
+    assert lib.csa_pool_index_topk(*idx_args, None, ctypes.byref(n), st) == 0
     t["ws_idx"] = torch.empty(n.value, dtype=torch.uint8, device="cuda")
     t["ws_idx_n"] = ctypes.c_size_t(n.value)
-    calls.append((lib.csa_index_topk, idx_args + (P(t["ws_idx"]), ctypes.byref(t["ws_idx_n"]), st)))
+    calls.append((lib.csa_pool_index_topk, idx_args + (P(t["ws_idx"]), ctypes.byref(t["ws_idx_n"]), st)))
     timed = {len(calls) - 1: "index_mfma_kernel"}
     # CSA attention
     att = (P(t["q"]), P(wl.kc), P(wl.vc), L.BF16, P(t["idx"]), TOPK, P(t["kw"]), P(t["vw"]), P(wl.win_pos0), LWIN, W,
@@ -316,13 +315,13 @@ def run_fp8_kv(L, torch, wl, steps, warmup, every=10):
     for t in wl.r:
         t8 = {"kvw": to_fp8(t["kvw"]), "hkvc": to_fp8(t["hkvc"]), "hkvw": to_fp8(t["hkvw"])}
         calls = []
-        calls.append((lib.csa_compress2, (P(t["kvw"][:, LWIN - M_CSA:]), P(t["kiw"][:, LWIN - M_CSA:]), L.BF16,
-                                          P(t["g4"]), P(t["bias"]), B, M_CSA, M_CSA, 2 * D, LWIN,
-                                          P(kvc8[:, N_CSA - 1:]), None, L.FP8_KV, N_CSA, DI, LWIN,
-                                          P(t["ki"][:, N_CSA - 1:]), P(t["ks"][:, N_CSA - 1:]), L.MXFP4, N_CSA, st)))
-        idx_args = (P(t["qi"]), L.BF16, P(t["wi"]), P(t["ki"]), P(t["ks"]), L.MXFP4, P(wl.q_pos), B, 1, HI, DI, N_CSA,
-                    0, M_CSA, TOPK, P(t["idx"]), None)
-        calls.append((lib.csa_index_topk, idx_args + (P(t["ws_idx"]), ctypes.byref(t["ws_idx_n"]), st)))
+        # the newest block pooled into FP8 K|V row N_CSA-1 (and the MXFP4 key) in the indexer launch
+        t8["pool"] = L.BlockPool(P(t["kvw"][:, LWIN - M_CSA:]), P(t["kiw"][:, LWIN - M_CSA:]), P(t["g4"]),
+                                 P(t["bias"]), 2 * D, LWIN, LWIN, P(kvc8[:, N_CSA - 1]), None, L.FP8_KV, N_CSA,
+                                 N_CSA - 1)
+        idx_args = (ctypes.byref(t8["pool"]), P(t["qi"]), L.BF16, P(t["wi"]), P(t["ki"]), P(t["ks"]), L.MXFP4,
+                    P(wl.q_pos), B, 1, HI, DI, N_CSA, 0, M_CSA, TOPK, P(t["idx"]), None)
+        calls.append((lib.csa_pool_index_topk, idx_args + (P(t["ws_idx"]), ctypes.byref(t["ws_idx_n"]), st)))
         att = (P(t["q"]), P(kvc8), P(kvc8[..., KB:]), P(t["idx"]), TOPK, P(t8["kvw"]), P(t8["kvw"][..., KB:]),
                P(wl.win_pos0), LWIN, W, P(wl.q_pos), B, 1, H, D, 64, N_CSA, 0, FP8_ROW, FP8_ROW,
                ctypes.c_float(1.0), ctypes.c_float(1.0), ctypes.c_float(scale), P(t["o"]), P(t["lse"]))

@@ -219,6 +219,49 @@ dsv4_status csa_index_topk(const void* qi, int qi_dt, const float* wi,
                            void* workspace, size_t* ws_bytes, hipStream_t stream);
 
 /*
+ * csa_pool_index_topk — a CSA decode step's pooling and selection in one launch  [CSA],
+ * [P2 §4] (the newest block of m raw tokens becomes a compressed entry of both the K|V
+ * cache and the indexer-key cache, then every visible entry is scored and the top-k kept).
+ *
+ *   The result equals  csa_compress2(pool->x, pool->x2, DSV4_BF16, pool->gate,
+ *   pool->pos_bias, B, m, m, pool->C, pool->x_bstride, pool->y, pool->y_scale, pool->y_dt,
+ *   pool->y_bstride, DI, pool->x2_bstride, ki at row pool->row, ki_scale at row pool->row,
+ *   DSV4_MXFP4, ki_bstride or N)  followed by  csa_index_topk(qi, ..., ki, ki_scale, ...)
+ *   with the remaining arguments, bit for bit: one block per sequence, pooled with the same
+ *   gates into row pool->row (< N) of both caches.  The K|V rows are pooled by extra
+ *   workgroups of the indexer launch and the indexer key by the wave that scores it.
+ *
+ *   pool->x   bf16 raw K|V rows [B, x_bstride rows, C], the block's m rows first (x_bstride
+ *             0 means m); pool->x2 the raw indexer-key rows [B, x2_bstride rows, DI].
+ *   pool->gate [B, m] f32, pool->pos_bias [m] f32.
+ *   pool->y   K|V cache row pool->row of sequence 0 (bf16 [.., C] or FP8 K|V rows of
+ *             C + 64 bytes with pool->y_scale as for csa_compress), pool->y_bstride rows
+ *             between sequences (0 means N).
+ *   ki, ki_scale: MXFP4 indexer keys as for csa_index_topk; row pool->row is written.
+ *   qi_dt BF16 or MXFP4; ki_dt MXFP4; m * DI <= 512 (m = 4 with DI = 128).  Every other
+ *   argument, the workspace protocol and the errors are those of csa_index_topk.
+ */
+typedef struct dsv4_block_pool {
+  const void* x;
+  const void* x2;
+  const float* gate;
+  const float* pos_bias;
+  int64_t C;
+  int64_t x_bstride, x2_bstride;
+  void* y;
+  uint8_t* y_scale;
+  int y_dt;
+  int64_t y_bstride;
+  int64_t row;
+} dsv4_block_pool;
+
+dsv4_status csa_pool_index_topk(const dsv4_block_pool* pool, const void* qi, int qi_dt, const float* wi, void* ki,
+                                uint8_t* ki_scale, int ki_dt, const int32_t* q_pos, int64_t B, int64_t Q,
+                                int32_t HI, int32_t DI, int64_t N, int64_t ki_bstride, int32_t m, int32_t k,
+                                int32_t* out_idx, float* out_score, void* workspace, size_t* ws_bytes,
+                                hipStream_t stream);
+
+/*
  * csa_index_topk_noalloc — csa_index_topk for callers that cannot allocate device memory
  * or pass a workspace (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc).  Arguments, results and errors are those of csa_index_topk, without

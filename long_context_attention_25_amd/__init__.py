@@ -60,6 +60,18 @@ _SIGS = {
 }
 
 
+class BlockPool(ctypes.Structure):
+    """dsv4_block_pool: the newest block pooled by csa_pool_index_topk."""
+    _fields_ = [("x", _p), ("x2", _p), ("gate", _p), ("pos_bias", _p), ("C", _i64), ("x_bstride", _i64),
+                ("x2_bstride", _i64), ("y", _p), ("y_scale", _p), ("y_dt", ctypes.c_int), ("y_bstride", _i64),
+                ("row", _i64)]
+
+
+_SIGS["csa_pool_index_topk"] = ([ctypes.POINTER(BlockPool), _p, ctypes.c_int, _p, _p, _p, ctypes.c_int, _p, _i64,
+                                 _i64, _i32, _i32, _i64, _i64, _i32, _i32, _p, _p, _p,
+                                 ctypes.POINTER(ctypes.c_size_t), _p], ctypes.c_int)
+
+
 class LibError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"{msg} (status {status})")
@@ -236,13 +248,8 @@ def kv_cache_append(x_new, gate_new, pos, win, win_gate, pos_bias, m: int, cache
                                  L, _ptr(pos_bias), m, _ptr(cache), _ptr(cache_scale), ydt, N, y_bs, _stream()))
 
 
-def csa_index_topk(qi, wi, ki, q_pos, m: int, k: int, ki_scale=None, N=None, with_scores=False, workspace=None,
-                   out_idx=None, out_score=None, qi_scale=None):
-    """Indexer scores + per-query top-k.  qi [B,Q,HI,DI], wi [B,Q,HI] f32, ki [B,rows,DI]
-    (or MXFP4 codes [B,rows,DI/2] uint8 with ki_scale [B,rows,DI/32]), q_pos [B,Q] int32.
-    MXFP4 queries: qi codes [B,Q,HI,DI/2] uint8 and qi_scale [B,Q,HI,DI/32], stored right
-    after the codes in one allocation.
-    Returns idx [B,Q,k] int32 (and scores [B,Q,k] f32 with with_scores)."""
+def _index_args(qi, wi, ki, q_pos, m, k, ki_scale, N, with_scores, out_idx, out_score, qi_scale):
+    """Checked arguments of csa_index_topk (and of csa_pool_index_topk after its pool)."""
     B, Q, HI, DI = qi.shape
     if qi.dtype == torch.uint8:
         DI *= 2
@@ -267,8 +274,50 @@ def csa_index_topk(qi, wi, ki, q_pos, m: int, k: int, ki_scale=None, N=None, wit
         out_score = torch.empty((B, Q, k), dtype=torch.float32, device=qi.device)
     args = (_ptr(qi), _dt(qi), _ptr(wi), _ptr(ki), _ptr(ki_scale), kdt, _ptr(q_pos), B, Q, HI, DI, N, k_bs, m, k,
             _ptr(out_idx), _ptr(out_score))
+    return args, out_idx, out_score
+
+
+def csa_index_topk(qi, wi, ki, q_pos, m: int, k: int, ki_scale=None, N=None, with_scores=False, workspace=None,
+                   out_idx=None, out_score=None, qi_scale=None):
+    """Indexer scores + per-query top-k.  qi [B,Q,HI,DI], wi [B,Q,HI] f32, ki [B,rows,DI]
+    (or MXFP4 codes [B,rows,DI/2] uint8 with ki_scale [B,rows,DI/32]), q_pos [B,Q] int32.
+    MXFP4 queries: qi codes [B,Q,HI,DI/2] uint8 and qi_scale [B,Q,HI,DI/32], stored right
+    after the codes in one allocation.
+    Returns idx [B,Q,k] int32 (and scores [B,Q,k] f32 with with_scores)."""
+    args, out_idx, out_score = _index_args(qi, wi, ki, q_pos, m, k, ki_scale, N, with_scores, out_idx, out_score,
+                                           qi_scale)
     ws, n = _workspace(lambda n: lib().csa_index_topk(*args, None, ctypes.byref(n), _stream()), workspace)
     _check(lib().csa_index_topk(*args, _ptr(ws), n, _stream()))
+    return (out_idx, out_score) if with_scores else out_idx
+
+
+def csa_pool_index_topk(x, x2, gate, pos_bias, row: int, kv_cache, qi, wi, ki, q_pos, m: int, k: int, ki_scale,
+                        kv_cache_scale=None, fp8_kv=False, N=None, with_scores=False, workspace=None, out_idx=None,
+                        out_score=None, qi_scale=None):
+    """csa_compress2 of each sequence's newest block followed by csa_index_topk, in one launch:
+    x [B,m,C] raw K|V rows and x2 [B,m,DI] raw indexer-key rows (bf16, views of larger
+    buffers allowed), gate [B,m], pos_bias [m]; the pooled entry goes to row `row` of
+    kv_cache ([B,rows,C] bf16, or FP8 K|V rows [B,rows,C+64] uint8 with fp8_kv=True and
+    kv_cache_scale) and of the MXFP4 key cache ki / ki_scale, which is then scored as by
+    csa_index_topk (same arguments and results)."""
+    if not (gate.is_contiguous() and pos_bias.is_contiguous()):
+        raise ValueError("gate [B, m] and pos_bias [m] must be contiguous")
+    B, T, C = x.shape
+    if T != m or x2.shape[:2] != (B, m) or x.dtype != torch.bfloat16 or x2.dtype != torch.bfloat16:
+        raise ValueError("x and x2 must be bf16 [B, m, .]: the newest block of each sequence")
+    if x.stride(2) != 1 or x.stride(1) != C or x2.stride(2) != 1 or x2.stride(1) != x2.shape[2]:
+        raise ValueError("x and x2 rows must be packed")
+    if kv_cache.dim() != 3 or kv_cache.stride(2) != 1 or kv_cache.stride(1) != kv_cache.shape[2]:
+        raise ValueError("kv_cache rows must be packed")
+    args, out_idx, out_score = _index_args(qi, wi, ki, q_pos, m, k, ki_scale, N, with_scores, out_idx, out_score,
+                                           qi_scale)
+    bs = lambda t: t.stride(0) // t.stride(1) if B > 0 else 0
+    pool = BlockPool(_ptr(x), _ptr(x2), _ptr(gate), _ptr(pos_bias), C, bs(x), bs(x2),
+                     ctypes.c_void_p(kv_cache[:, row].data_ptr()) if B > 0 else None, _ptr(kv_cache_scale),
+                     FP8_KV if fp8_kv else _dt(kv_cache), bs(kv_cache), row)
+    ws, n = _workspace(lambda n: lib().csa_pool_index_topk(ctypes.byref(pool), *args, None, ctypes.byref(n),
+                                                           _stream()), workspace)
+    _check(lib().csa_pool_index_topk(ctypes.byref(pool), *args, _ptr(ws), n, _stream()))
     return (out_idx, out_score) if with_scores else out_idx
 
 

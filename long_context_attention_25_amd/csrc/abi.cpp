@@ -374,7 +374,7 @@ dsv4_status index_topk_impl(const char* what, const void* qi, int qi_dt, const f
                             const uint8_t* ki_scale, int ki_dt, const int32_t* q_pos, int64_t B, int64_t Q,
                             int32_t HI, int32_t DI, int64_t N, int64_t ki_bstride, int32_t m, int32_t k,
                             int32_t* out_idx, float* out_score, void* workspace, size_t* ws_bytes,
-                            hipStream_t stream, bool noalloc) {
+                            hipStream_t stream, bool noalloc, const dsv4_block_pool* pool = nullptr) {
   REQUIRE(B >= 0 && Q >= 0 && N >= 0, "%s: sizes must be non-negative", what);
   REQUIRE(extent_ok({B, Q, N, ki_bstride}), "%s: sizes and strides must lie in [0, 2^40]", what);
   REQUIRE(m >= 1, "%s: m must be >= 1", what);
@@ -411,6 +411,31 @@ dsv4_status index_topk_impl(const char* what, const void* qi, int qi_dt, const f
   a.qi_scale = kind == dsv4::KEY_MXFP4_Q4 ? reinterpret_cast<const uint8_t*>(qi) + R * HI * (DI / 2) : nullptr;
   a.B = B; a.Q = Q; a.HI = HI; a.DI = DI; a.N = N; a.k_bs = ki_bstride ? ki_bstride : N;
   a.m = m; a.k = k; a.out_idx = out_idx; a.out_score = out_score;
+  if (pool) {
+    // the newest block of each sequence, pooled as csa_compress2 would into row pool->row
+    SUPPORT(ki_dt == DSV4_MXFP4, "%s: the pooled indexer keys are MXFP4 (ki_dt must be DSV4_MXFP4)", what);
+    SUPPORT((int64_t)m * DI <= 512, "%s: m * DI must be <= 512 (the key is pooled by one wave)", what);
+    REQUIRE(pool->row >= 0 && pool->row < N, "%s: pool->row (%lld) must lie in [0, N)", what, (long long)pool->row);
+    SUPPORT(pool->y_dt == DSV4_BF16 || pool->y_dt == DSV4_FP8_KV, "%s: pool->y_dt must be DSV4_BF16 or DSV4_FP8_KV",
+            what);
+    REQUIRE(pool->y_bstride == 0 || pool->y_bstride > pool->row,
+            "%s: pool->y_bstride must be 0 or more than pool->row", what);
+    dsv4::CompressArgs ca, cb;
+    const int64_t y_bs = pool->y_bstride ? pool->y_bstride : N;
+    dsv4_status ps = check_compress(what, pool->x, DSV4_BF16, pool->gate, pool->pos_bias, B, m, pool->C, m,
+                                    pool->x_bstride, pool->y, pool->y_scale, pool->y_dt, y_bs, &ca);
+    if (ps != DSV4_OK) return ps;
+    uint8_t* krow = ki ? const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(ki)) + pool->row * (DI / 2) : nullptr;
+    uint8_t* srow = ki_scale ? const_cast<uint8_t*>(ki_scale) + pool->row * (DI / 32) : nullptr;
+    ps = check_compress(what, pool->x2, DSV4_BF16, pool->gate, pool->pos_bias, B, m, DI, m, pool->x2_bstride, krow,
+                        srow, DSV4_MXFP4, a.k_bs, &cb);
+    if (ps != DSV4_OK) return ps;
+    dsv4::IndexPool& ip = a.pool;
+    ip.on = B > 0;
+    ip.x = pool->x; ip.x2 = pool->x2; ip.gate = pool->gate; ip.bias = pool->pos_bias;
+    ip.x_bs = ca.x_bs; ip.x2_bs = cb.x_bs; ip.C = pool->C;
+    ip.y = pool->y; ip.y_scale = pool->y_scale; ip.y_dt = pool->y_dt; ip.y_bs = y_bs; ip.row = pool->row;
+  }
   const size_t need = dsv4::topk_workspace_bytes(a);
   size_t scratch_size = 0;
   if (noalloc) {
@@ -439,6 +464,16 @@ dsv4_status csa_index_topk(const void* qi, int qi_dt, const float* wi, const voi
                            void* workspace, size_t* ws_bytes, hipStream_t stream) {
   return index_topk_impl("csa_index_topk", qi, qi_dt, wi, ki, ki_scale, ki_dt, q_pos, B, Q, HI, DI, N, ki_bstride, m,
                          k, out_idx, out_score, workspace, ws_bytes, stream, false);
+}
+
+dsv4_status csa_pool_index_topk(const dsv4_block_pool* pool, const void* qi, int qi_dt, const float* wi, void* ki,
+                                uint8_t* ki_scale, int ki_dt, const int32_t* q_pos, int64_t B, int64_t Q,
+                                int32_t HI, int32_t DI, int64_t N, int64_t ki_bstride, int32_t m, int32_t k,
+                                int32_t* out_idx, float* out_score, void* workspace, size_t* ws_bytes,
+                                hipStream_t stream) {
+  REQUIRE(pool != nullptr, "csa_pool_index_topk: pool must not be NULL");
+  return index_topk_impl("csa_pool_index_topk", qi, qi_dt, wi, ki, ki_scale, ki_dt, q_pos, B, Q, HI, DI, N,
+                         ki_bstride, m, k, out_idx, out_score, workspace, ws_bytes, stream, false, pool);
 }
 
 dsv4_status csa_index_topk_noalloc(const void* qi, int qi_dt, const float* wi, const void* ki,

@@ -187,6 +187,9 @@ __device__ __forceinline__ f32x4 mfma_fp8(long a, long b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
 }
 
+// Wait until every vector-memory operation of this wave (loads and stores) has completed.
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xf << 8)); }
+
 template <typename T>
 __device__ __forceinline__ T bit_cast_to(const uint4& v) {
   return __builtin_bit_cast(T, v);

@@ -27,6 +27,7 @@
 // independent of scheduling.
 #include "common.hpp"
 #include "launch.hpp"
+#include "pool.hpp"
 
 namespace dsv4 {
 
@@ -478,6 +479,25 @@ struct KeyTile<KEY_FP8, DI> {
   __device__ long op(int c) const { return __builtin_bit_cast(long, w[c]); }
 };
 
+// The pooling of a decode step's newest block inside the indexer launch (see IndexPool).
+// Grid rows at and past index_rows run the K|V rows' job; in the index grid, the wave
+// whose keys include the pooled row pools that sequence's indexer key on its own (a wave
+// of lanes, lpr2 * spb2 <= 64: no workgroup barrier) and stores it before any load of it.
+struct PoolDev {
+  int on;
+  int index_rows;
+  int kv_fp8;
+  int m;
+  int64_t nblk;                  // sequences (one block each)
+  const uint16_t* x2;
+  int64_t x2_bs;                 // elements between sequences of x2
+  const float* gate;
+  const float* bias;
+  int64_t row;
+  int lpr2, spb2;
+  pool::Job kv;
+};
+
 // QTW query tiles (QTW * 16/HI queries) per workgroup: every key tile loaded is used by
 // all of them (QTW > 1 when there are many queries, e.g. a prefill chunk).
 // kLocal (decode-shaped calls, QTW = 1, chunk <= kLocalChunk): the workgroup also keeps its
@@ -487,10 +507,11 @@ struct KeyTile<KEY_FP8, DI> {
 template <int KIND, int DI, int HI, int QTW, bool kNT, bool kLocal>
 __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
     const uint8_t* __restrict__ qi, const uint8_t* __restrict__ qsc, const float* __restrict__ wi,
-    const uint8_t* __restrict__ ki, const uint8_t* __restrict__ ksc, const int32_t* __restrict__ q_pos, int64_t N,
+    const uint8_t* ki, const uint8_t* ksc, const int32_t* __restrict__ q_pos, int64_t N,
     int64_t k_bs, int64_t Q, int m, int64_t chunk, float* __restrict__ scores, int64_t sstride,
     uint32_t* __restrict__ hist_g, uint64_t* __restrict__ cand_loc, uint4* __restrict__ meta_loc, int klocal,
-    int nch) {
+    int nch, PoolDev pd) {
+  // (ki and ksc carry no restrict: with pooling, a row of them is written below)
   constexpr int QPT = 16 / HI;          // queries per 16-row MFMA tile
   constexpr int KS = DI / 32;
   constexpr int GPQ = HI / 4;           // lane groups per query slot
@@ -503,6 +524,20 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, col = lane & 15;
+  if (pd.on && (int)blockIdx.y >= pd.index_rows) {          // the K|V rows' pooling job
+    const int64_t wg = (int64_t)(blockIdx.y - pd.index_rows) * gridDim.x + blockIdx.x;
+    if (wg < pd.kv.grid) {
+      if (pd.kv_fp8)
+        pool::compress_body<uint16_t, 4>(reinterpret_cast<const uint16_t*>(pd.kv.x), pd.gate, pd.bias, pd.m, pd.kv.C,
+                                         pd.m, 1, pd.nblk, pd.kv.x_bs, pd.kv.y_bs, pd.kv.y, pd.kv.ysc, pd.kv.lpr,
+                                         pd.kv.spb, pd.kv.bpw, pd.kv.cs, wg);
+      else
+        pool::compress_body<uint16_t, 1>(reinterpret_cast<const uint16_t*>(pd.kv.x), pd.gate, pd.bias, pd.m, pd.kv.C,
+                                         pd.m, 1, pd.nblk, pd.kv.x_bs, pd.kv.y_bs, pd.kv.y, pd.kv.ysc, pd.kv.lpr,
+                                         pd.kv.spb, pd.kv.bpw, pd.kv.cs, wg);
+    }
+    return;
+  }
   const int64_t QT = (Q + QPT - 1) / QPT;
   const int64_t QG = (QT + QTW - 1) / QTW;
   const int64_t b = blockIdx.y / QG, qt0 = (blockIdx.y % QG) * QTW;
@@ -523,6 +558,17 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
   int64_t c1 = c0 + chunk;
   if (c1 > N) c1 = N;
   const int64_t klast = c1 - 1;
+  if constexpr (KIND == KEY_MXFP4 || KIND == KEY_MXFP4_Q4) {
+    // the pooled indexer key of this sequence, by the wave that loads it, before its loads
+    if (pd.on && pd.row >= c0 && pd.row < c1 && wave == (int)(((pd.row - c0) % KPS) / (TPW * 16))) {
+      pool::compress_body<uint16_t, 3>(pd.x2 + b * pd.x2_bs, pd.gate + b * pd.m, pd.bias, pd.m, DI, pd.m, 1, 1, 0, 0,
+                                       const_cast<uint8_t*>(kbase) + pd.row * (DI / 2),
+                                       const_cast<uint8_t*>(sbase) + pd.row * (DI / 32), pd.lpr2, pd.spb2, 1, 1, 0,
+                                       nullptr, 0.f, lane);
+      wait_vmcnt0();
+    }
+    asm volatile("" ::: "memory");
+  }
   KeyTile<KIND, DI> cur[TPW], nxt[TPW];
   int64_t base = c0 + wave * (TPW * 16);
   if (base < c1) {
@@ -1382,10 +1428,33 @@ hipError_t launch_mfma_q(const IndexArgs& a, const TopkPlan& p, const IndexBufs&
   constexpr int QPT = 16 / HI;
   const int64_t QT = (a.Q + QPT - 1) / QPT;
   const int64_t QG = (QT + QTW - 1) / QTW;
-  dim3 grid((unsigned)p.nch, (unsigned)(a.B * QG));
   // the kernel clears and uses QPT histogram slots for each of its non-empty query tiles;
   // the local selection adds the chunk's scores of each query and its own scratch
   const int64_t tiles = QTW < QT ? QTW : QT;
+  // pooling of the newest block (csa_pool_index_topk): the K|V rows' job on extra grid rows
+  PoolDev pd{};
+  int kv_rows = 0;
+  if (a.pool.on) {
+    pd.on = 1;
+    pd.index_rows = (int)(a.B * QG);
+    pd.kv_fp8 = a.pool.y_dt == 4;
+    pd.m = a.m;
+    pd.nblk = a.B;
+    pd.x2 = reinterpret_cast<const uint16_t*>(a.pool.x2);
+    pd.x2_bs = a.pool.x2_bs * DI;
+    pd.gate = a.pool.gate;
+    pd.bias = a.pool.bias;
+    pd.row = a.pool.row;
+    pd.lpr2 = DI / 8;                                          // bf16: 8 channels per lane
+    pd.spb2 = a.m < kWave / pd.lpr2 ? a.m : kWave / pd.lpr2;
+    CompressArgs ca;
+    ca.x = a.pool.x; ca.x_f32 = false; ca.gate = a.pool.gate; ca.bias = a.pool.bias;
+    ca.B = a.B; ca.T = a.m; ca.C = a.pool.C; ca.m = a.m;
+    ca.x_bs = a.pool.x_bs; ca.y_bs = a.pool.y_bs; ca.y = a.pool.y; ca.y_scale = a.pool.y_scale; ca.y_dt = a.pool.y_dt;
+    pd.kv = a.pool.y_dt == 4 ? pool::make_job<uint16_t, 4>(ca) : pool::make_job<uint16_t, 1>(ca);
+    kv_rows = (int)((pd.kv.grid + p.nch - 1) / p.nch);
+  }
+  dim3 grid((unsigned)p.nch, (unsigned)(a.B * QG + kv_rows));
   size_t smem = (size_t)(tiles * QPT) * kHistWords * sizeof(uint32_t);
   if (kLocal)
     smem += (size_t)(a.Q < QPT ? a.Q : QPT) * p.chunk * sizeof(float) +
@@ -1399,7 +1468,7 @@ hipError_t launch_mfma_q(const IndexArgs& a, const TopkPlan& p, const IndexBufs&
                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     DSV4_LAUNCH_MAIN(kern, grid, dim3(kThreads), smem, st, reinterpret_cast<const uint8_t*>(a.qi), a.qi_scale, a.wi,
                      reinterpret_cast<const uint8_t*>(a.ki), a.ki_scale, a.q_pos, a.N, a.k_bs, a.Q, a.m, p.chunk,
-                     w.scores, sstride, w.hist, w.cloc, w.meta, p.klocal, (int)p.nch);
+                     w.scores, sstride, w.hist, w.cloc, w.meta, p.klocal, (int)p.nch, pd);
   };
   if (QTW == 1 && QG == 1) go(index_mfma_kernel<KIND, DI, HI, QTW, (QTW == 1), kLocal>);
   else go(index_mfma_kernel<KIND, DI, HI, QTW, false, kLocal>);

@@ -61,7 +61,25 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t st);
 // KEY_MXFP4: bf16 queries x MXFP4 keys; KEY_MXFP4_Q4: MXFP4 queries x MXFP4 keys
 enum KeyKind { KEY_F32 = 0, KEY_BF16 = 1, KEY_FP8 = 2, KEY_MXFP4 = 3, KEY_MXFP4_Q4 = 4 };
 
+// A decode step's newest block pooled in the indexer launch (csa_pool_index_topk): one
+// block of m raw tokens per sequence, pooled with the same gates into row `row` of the K|V
+// cache (bf16 or FP8 K|V rows) and of the MXFP4 indexer-key cache the call then scores.
+struct IndexPool {
+  bool on = false;
+  const void* x = nullptr;       // raw K|V rows of the block (bf16), x_bs rows between sequences
+  const void* x2 = nullptr;      // raw indexer-key rows (bf16, DI channels), x2_bs rows apart
+  const float* gate = nullptr;   // [B, m]
+  const float* bias = nullptr;   // [m]
+  int64_t x_bs = 0, x2_bs = 0, C = 0;
+  void* y = nullptr;             // K|V cache row `row` of sequence 0, y_bs rows between sequences
+  uint8_t* y_scale = nullptr;
+  int y_dt = 1;                  // 1 bf16, 4 FP8 K|V rows
+  int64_t y_bs = 0;
+  int64_t row = 0;
+};
+
 struct IndexArgs {
+  IndexPool pool;
   const void* qi;
   const uint8_t* qi_scale;   // MXFP4 queries: E8M0 scales [B, Q, HI, DI/32]
   const float* wi;

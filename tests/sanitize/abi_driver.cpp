@@ -117,6 +117,38 @@ int main() {
                                                      65536, 0, 4, 2048, (int32_t*)P, nullptr, nullptr),
          {DSV4_ERR_UNSUPPORTED, DSV4_ERR_LAUNCH, DSV4_ERR_INVALID_ARG});
 
+  // ---- pooling + indexer in one launch: size queries and invalid pools
+  {
+    dsv4_block_pool pl = {P, P, (float*)P, (float*)P, 1024, 128, 128, P, nullptr, BF16, 0, 0};
+    for (int64_t N : Ns)
+      for (int64_t row : {(int64_t)0, N - 1, N, (int64_t)-1})
+        for (int32_t DI : {64, 128, 256}) {
+          pl.row = row;
+          size_t n1 = 0, n2 = 0;
+          int s1 = csa_pool_index_topk(&pl, P, BF16, (float*)P, P, (uint8_t*)P, MX, (int32_t*)P, 8, 1, 8, DI, N, 0, 4, 1024,
+                                       (int32_t*)P, nullptr, nullptr, &n1, nullptr);
+          int s2 = csa_pool_index_topk(&pl, P, BF16, (float*)P, P, (uint8_t*)P, MX, (int32_t*)P, 8, 1, 8, DI, N, 0, 4, 1024,
+                                       (int32_t*)P, nullptr, nullptr, &n2, nullptr);
+          query("pool_index_topk query", s1, n1, s2, n2);
+          if (row < 0 || row >= N) expect("pool row outside [0, N)", s1, {DSV4_ERR_INVALID_ARG, DSV4_ERR_UNSUPPORTED});
+        }
+    expect("pool NULL", csa_pool_index_topk(nullptr, P, BF16, (float*)P, P, (uint8_t*)P, MX, (int32_t*)P, 8, 1, 8, 128,
+                                            4096, 0, 4, 64, (int32_t*)P, nullptr, nullptr, nullptr, nullptr),
+           {DSV4_ERR_INVALID_ARG});
+    pl.row = 5;
+    pl.y_dt = E4M3;
+    expect("pool y_dt", csa_pool_index_topk(&pl, P, BF16, (float*)P, P, (uint8_t*)P, MX, (int32_t*)P, 8, 1, 8, 128, 4096,
+                                            0, 4, 64, (int32_t*)P, nullptr, nullptr, nullptr, nullptr),
+           {DSV4_ERR_UNSUPPORTED});
+    pl.y_dt = BF16;
+    expect("pool bf16 keys", csa_pool_index_topk(&pl, P, BF16, (float*)P, P, nullptr, BF16, (int32_t*)P, 8, 1, 8, 128,
+                                                 4096, 0, 4, 64, (int32_t*)P, nullptr, nullptr, nullptr, nullptr),
+           {DSV4_ERR_UNSUPPORTED});
+    expect("pool m*DI", csa_pool_index_topk(&pl, P, BF16, (float*)P, P, (uint8_t*)P, MX, (int32_t*)P, 8, 1, 8, 256, 4096,
+                                            0, 4, 64, (int32_t*)P, nullptr, nullptr, nullptr, nullptr),
+           {DSV4_ERR_UNSUPPORTED});
+  }
+
   // ---- attention: size queries over a sweep (bf16, f32, FP8 rows), then invalid arguments
   const int32_t Hs[] = {16, 64, 48, 17};
   const int32_t Ds[] = {128, 512, 256, 100};

@@ -112,22 +112,31 @@ def test_decode_step_end_to_end_1m_sampled_sequences():
     kc, vc = kvc[..., :D], kvc[..., D:]
     hkc, hvc = hkvc[..., :D], hkvc[..., D:]
 
-    def step():
-        L.csa_compress2(kvw[:, LW - 4:], kiw[:, LW - 4:], g4, bias_d, 4, kvc[:, NC - 1:], ki[:, NC - 1:],
-                        ks[:, NC - 1:])
-        idx, sc = L.csa_index_topk(qi, wi_d, ki, qpos_d, 4, k, ki_scale=ks, with_scores=True)
+    def step(fused):
+        if fused:   # the pooling inside the indexer launch (the rows it writes are cleared first)
+            kvc[:, NC - 1] = 0
+            ki[:, NC - 1] = 0
+            ks[:, NC - 1] = 0
+            idx, sc = L.csa_pool_index_topk(kvw[:, LW - 4:], kiw[:, LW - 4:], g4, bias_d, NC - 1, kvc, qi, wi_d, ki,
+                                            qpos_d, 4, k, ks, with_scores=True)
+        else:
+            L.csa_compress2(kvw[:, LW - 4:], kiw[:, LW - 4:], g4, bias_d, 4, kvc[:, NC - 1:], ki[:, NC - 1:],
+                            ks[:, NC - 1:])
+            idx, sc = L.csa_index_topk(qi, wi_d, ki, qpos_d, 4, k, ki_scale=ks, with_scores=True)
         o, lse = L.csa_attend(q, kc, vc, idx, kvw[..., :D], kvw[..., D:], wpos0_d, W, qpos_d, scale)
         L.csa_compress(hkvw, hg, hbias_d, 128, torch.bfloat16, out=hkvc[:, NH - 1:])
         ho, hlse = L.hca_attend(hq, hkc, hvc, 128, hkvw[..., :D], hkvw[..., D:], wpos0_d, W, qpos_d, scale)
         return [t.clone() for t in (idx, sc, o, lse, ho, hlse, kvc[:, NC - 1], ki[:, NC - 1], ks[:, NC - 1],
                                     hkvc[:, NH - 1])]
 
-    r1 = step()
-    r2 = step()
+    r1 = step(False)
+    r2 = step(False)
+    r3 = step(True)
     torch.cuda.synchronize()
     names = ("idx", "scores", "csa o", "csa lse", "hca o", "hca lse", "kv row", "key codes", "key scales", "hca row")
-    for n, a, b_ in zip(names, r1, r2):
+    for n, a, b_, c_ in zip(names, r1, r2, r3):
         assert torch.equal(a, b_), f"decode step not bitwise repeatable: {n}"
+        assert torch.equal(a, c_), f"pooling inside the indexer launch differs from csa_compress2: {n}"
     idx_g, _, o, lse, ho, hlse = r1[:6]
     idx_g = idx_g.cpu().numpy()
     for b in sampled:

@@ -658,6 +658,53 @@ def test_index_topk_concentrated_winners():
     assert np.all(sc[1, 0] == 0)
 
 
+@pytest.mark.parametrize("case", ["decode", "many_queries", "fp4_queries", "fp8_rows"])
+def test_pool_index_topk_equals_compress2_then_index_topk(case):
+    """csa_pool_index_topk (the newest block pooled inside the indexer launch) against
+    csa_compress2 followed by csa_index_topk on copies of the same caches: the pooled K|V
+    and key rows and the selection bit for bit; the pooled row anywhere in a chunk (here not
+    the last row), several query groups per sequence, MXFP4 queries, FP8 K|V rows."""
+    cfg = 250 + len(case)
+    HI, DI, m = 8, 128, 4
+    B, Q, N, k, row = {"decode": (8, 1, 20000, 512, 19999), "many_queries": (2, 37, 3000, 100, 1234),
+                       "fp4_queries": (3, 1, 9000, 256, 5000), "fp8_rows": (2, 1, 6000, 128, 5999)}[case]
+    C, LW = 1024, 16
+    fp8 = case == "fp8_rows"
+    k32 = synth.normal(cfg, synth.KI, (B, N, DI))
+    codes, scales = codecs.encode_mxfp4(k32)
+    ki0, ks0 = dev(codes), dev(scales)
+    if fp8:
+        kv0 = dev(np.random.default_rng(cfg).integers(0, 120, (B, N, C + 64), dtype=np.uint8))
+    else:
+        kv0 = dev_bf16(synth.normal(cfg, synth.KC, (B, N, C)))[0]
+    xw = dev_bf16(synth.normal(cfg, synth.KW, (B, LW, C)))[0]
+    x2w = dev_bf16(synth.normal(cfg, synth.RAW_KI, (B, LW, DI)))[0]
+    gate = dev(synth.normal(cfg, synth.GATE, (B, m)))
+    bias = dev(synth.normal(cfg, synth.BIAS, (m,), std=0.1))
+    wi = dev(synth.uniform(cfg, synth.WI, (B, Q, HI)))
+    pos = dev((4 * N - 1 - (np.arange(B * Q, dtype=np.int32).reshape(B, Q) * 97) % (4 * N // 3)).astype(np.int32))
+    sc8 = dev(np.array([125, 126], np.uint8)) if fp8 else None
+    if case == "fp4_queries":
+        qc, qs = codecs.encode_mxfp4(synth.normal(cfg, synth.QI, (B, Q, HI, DI)))
+        qbuf = dev(np.concatenate([qc.reshape(-1), qs.reshape(-1)]))
+        qi, q_scale = qbuf[:qc.size].view(qc.shape), qbuf[qc.size:].view(qs.shape)
+    else:
+        qi, q_scale = dev_bf16(synth.normal(cfg, synth.QI, (B, Q, HI, DI)))[0], None
+    xs, x2s = xw[:, LW - m:], x2w[:, LW - m:]
+    kv_a, ki_a, ks_a = kv0.clone(), ki0.clone(), ks0.clone()
+    L.csa_compress2(xs, x2s, gate, bias, m, kv_a[:, row:row + 1], ki_a[:, row:row + 1], ks_a[:, row:row + 1],
+                    out_scale=sc8, fp8_kv=fp8)
+    ia, sa = L.csa_index_topk(qi, wi, ki_a, pos, m, k, ki_scale=ks_a, with_scores=True, qi_scale=q_scale)
+    kv_b, ki_b, ks_b = kv0.clone(), ki0.clone(), ks0.clone()
+    ib, sb = L.csa_pool_index_topk(xs, x2s, gate, bias, row, kv_b, qi, wi, ki_b, pos, m, k, ks_b,
+                                   kv_cache_scale=sc8, fp8_kv=fp8, with_scores=True, qi_scale=q_scale)
+    torch.cuda.synchronize()
+    assert not torch.equal(kv_a, kv0) and not torch.equal(ki_a, ki0)       # the row was rewritten
+    for name, a, b_ in (("kv", kv_a, kv_b), ("key codes", ki_a, ki_b), ("key scales", ks_a, ks_b), ("idx", ia, ib),
+                        ("scores", sa, sb)):
+        assert torch.equal(a, b_), name
+
+
 def test_index_topk_very_long_rows():
     """Rows of more than 2^21 visible blocks: more key ranges in the selection's first pass
     than the second pass indexes directly, so candidates of the last ranges are found by
