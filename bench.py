@@ -63,8 +63,11 @@ KERNEL_BYTES = {
     + B * (M_CSA * (2 * D + DI) * 2 + M_CSA * 4 + 2 * D * 2 + (DI // 2 + DI // 32)),
     # the selected K/V rows + window rows, q, the index list
     "attend_bf16_kernel (CSA)": B * (TOPK + W) * 2 * D * 2 + B * H * D * 2 + B * TOPK * 4,
-    # every visible K/V entry + window rows, q
-    "attend_bf16_kernel (HCA)": B * (N_HCA + W) * 2 * D * 2 + B * H * D * 2,
+    # every visible K/V entry + window rows, q, and the pooling of the newest block done in
+    # the same launch (its 128 raw rows are the window rows, read a second time; gates; the
+    # pooled row out)
+    "attend_bf16_kernel (HCA)": B * (N_HCA + W) * 2 * D * 2 + B * H * D * 2
+    + B * (M_HCA * 2 * D * 2 + M_HCA * 4 + 2 * D * 2),
 }
 
 # HBM traffic per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs, each scaled by
@@ -171,15 +174,15 @@ def marshal_step(L, torch, wl, rep):
     t["ws_csa_n"] = ctypes.c_size_t(n.value)
     calls.append((lib.csa_attend, att + (P(t["ws_csa"]), ctypes.byref(t["ws_csa_n"]), st)))
     timed[len(calls) - 1] = "attend_bf16_kernel (CSA)"
-    # HCA: the newest 128-token block (the whole window) -> entry N_HCA-1 of K|V
-    calls.append((lib.csa_compress, (P(t["hkvw"]), L.BF16, P(t["hgate"]), P(t["hbias"]), B, M_HCA, 2 * D, M_HCA, LWIN,
-                                     P(t["hkvc"][:, N_HCA - 1:]), None, L.BF16, N_HCA, st)))
-    hatt = (P(t["hq"]), P(t["hkc"]), P(t["hvc"]), L.BF16, M_HCA, P(t["hkw"]), P(t["hvw"]), P(wl.win_pos0), LWIN, W,
-            P(wl.q_pos), B, 1, H, D, N_HCA, 0, 2 * D, 2 * D, ctypes.c_float(scale), P(t["ho"]), P(t["hlse"]))
-    assert lib.hca_attend(*hatt, None, ctypes.byref(n), st) == 0
+    # HCA: the newest 128-token block (the whole window) -> entry N_HCA-1 of K|V, pooled in
+    # the attention launch, then dense attention over every entry and the window
+    hatt = (P(t["hkvw"]), P(t["hgate"]), P(t["hbias"]), LWIN, P(t["hq"]), P(t["hkc"]), P(t["hvc"]), L.BF16, M_HCA,
+            P(t["hkw"]), P(t["hvw"]), P(wl.win_pos0), LWIN, W, P(wl.q_pos), B, 1, H, D, N_HCA, 0, 2 * D, 2 * D,
+            ctypes.c_float(scale), P(t["ho"]), P(t["hlse"]))
+    assert lib.hca_pool_attend(*hatt, None, ctypes.byref(n), st) == 0
     t["ws_hca"] = torch.empty(max(n.value, 1), dtype=torch.uint8, device="cuda")
     t["ws_hca_n"] = ctypes.c_size_t(n.value)
-    calls.append((lib.hca_attend, hatt + (P(t["ws_hca"]), ctypes.byref(t["ws_hca_n"]), st)))
+    calls.append((lib.hca_pool_attend, hatt + (P(t["ws_hca"]), ctypes.byref(t["ws_hca_n"]), st)))
     timed[len(calls) - 1] = "attend_bf16_kernel (HCA)"
     return calls, timed
 

@@ -325,6 +325,33 @@ dsv4_status hca_attend(const void* q, const void* kc, const void* vc, int dt, in
                        void* out, float* lse, void* workspace, size_t* ws_bytes, hipStream_t stream);
 
 /*
+ * hca_pool_attend — an HCA decode step's pooling and attention in one launch  [HCA],
+ * [P2 §4] (the newest block of m raw tokens becomes the last compressed entry, then every
+ * visible entry and the window are attended).
+ *
+ *   The result equals  csa_compress(x, DSV4_BF16, gate, pos_bias, B, m, 2D, m, x_bstride,
+ *   kc row N - 1, NULL, DSV4_BF16, kv_bstride or N)  followed by  hca_attend(...) with the
+ *   remaining arguments, up to rounding order: the pooled entry (written to row N - 1 of
+ *   the K|V cache) enters the softmax as a part of its own, merged by log-sum-exp with the
+ *   key ranges over entries [0, N - 1) and the window.  The pooling runs on workgroups of
+ *   the attention launch that the key ranges leave free.
+ *
+ *   x         bf16 raw K|V rows [B, x_bstride rows, 2D], the block's m rows first (K then V
+ *             channels, as the cache rows; x_bstride 0 means m);  gate [B, m], pos_bias [m].
+ *   kc, vc    one buffer of K|V rows: vc = kc + D elements, kv_rstride >= 2D.
+ *   dt = DSV4_BF16, D = 512, Q < 16, N >= 1.  Every other argument, the workspace protocol
+ *   and the errors are those of hca_attend.  The call keeps one arrival counter per
+ *   sequence in a library-owned array per device (65,536 counters, taken in turn): calls
+ *   in flight at once on one device may hold at most that many sequences together.
+ */
+dsv4_status hca_pool_attend(const void* x, const float* gate, const float* pos_bias, int64_t x_bstride,
+                            const void* q, const void* kc, const void* vc, int dt, int32_t m, const void* kw,
+                            const void* vw, const int32_t* win_pos0, int64_t L, int32_t W, const int32_t* q_pos,
+                            int64_t B, int64_t Q, int32_t H, int32_t D, int64_t N, int64_t kv_bstride,
+                            int64_t kv_rstride, int64_t w_rstride, float scale, void* out, float* lse, void* workspace,
+                            size_t* ws_bytes, hipStream_t stream);
+
+/*
  * csa_attend_fp8kv, hca_attend_fp8kv — csa_attend / hca_attend over K/V caches stored in
  * FP8 with the RoPE dims of K kept in BF16  [P2 §5] (most of each KV entry in FP8, the
  * RoPE dims in BF16), dequantised inside the attention kernel.

@@ -67,6 +67,9 @@ class BlockPool(ctypes.Structure):
                 ("row", _i64)]
 
 
+_SIGS["hca_pool_attend"] = ([_p, _p, _p, _i64, _p, _p, _p, ctypes.c_int, _i32, _p, _p, _p, _i64, _i32, _p, _i64, _i64,
+                             _i32, _i32, _i64, _i64, _i64, _i64, ctypes.c_float, _p, _p, _p,
+                             ctypes.POINTER(ctypes.c_size_t), _p], ctypes.c_int)
 _SIGS["csa_pool_index_topk"] = ([ctypes.POINTER(BlockPool), _p, ctypes.c_int, _p, _p, _p, ctypes.c_int, _p, _i64,
                                  _i64, _i32, _i32, _i64, _i64, _i32, _i32, _p, _p, _p,
                                  ctypes.POINTER(ctypes.c_size_t), _p], ctypes.c_int)
@@ -363,6 +366,29 @@ def hca_attend(q, kc, vc, m: int, kw, vw, win_pos0, W: int, q_pos, scale: float,
             D, N, kv_bs, kv_rs, w_rs, float(scale), _ptr(out), _ptr(lse))
     ws, n = _workspace(lambda n: lib().hca_attend(*args, None, ctypes.byref(n), _stream()), workspace)
     _check(lib().hca_attend(*args, _ptr(ws), n, _stream()))
+    return out, lse
+
+
+def hca_pool_attend(x, gate, pos_bias, q, kc, vc, m: int, kw, vw, win_pos0, W: int, q_pos, scale: float, N=None,
+                    workspace=None, out=None, lse=None):
+    """csa_compress of each sequence's newest block followed by hca_attend, in one launch:
+    x [B,m,2D] raw K|V rows (bf16, a view of a larger buffer allowed), gate [B,m], pos_bias
+    [m]; the pooled entry goes to row N-1 of the cache whose K and V halves are kc and vc
+    (views of one [B,rows,2D] buffer), then every visible entry and the window are attended."""
+    if not (gate.is_contiguous() and pos_bias.is_contiguous()):
+        raise ValueError("gate [B, m] and pos_bias [m] must be contiguous")
+    B, T, C2 = x.shape
+    if T != m or x.dtype != torch.bfloat16 or x.stride(2) != 1 or x.stride(1) != C2:
+        raise ValueError("x must be packed bf16 rows [B, m, 2D]: the newest block of each sequence")
+    B_, Q, H, D, N, kv_bs, L, kv_rs, w_rs = _attend_common(q, kc, vc, kw, vw, win_pos0, q_pos, N)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B_, Q, H), dtype=torch.float32, device=q.device) if lse is None else lse
+    _contig(out=out, lse=lse)
+    args = (_ptr(x), _ptr(gate), _ptr(pos_bias), x.stride(0) // x.stride(1) if B > 0 else 0, _ptr(q), _ptr(kc),
+            _ptr(vc), _dt(q), m, _ptr(kw), _ptr(vw), _ptr(win_pos0), L, W, _ptr(q_pos), B_, Q, H, D, N, kv_bs, kv_rs,
+            w_rs, float(scale), _ptr(out), _ptr(lse))
+    ws, n = _workspace(lambda n: lib().hca_pool_attend(*args, None, ctypes.byref(n), _stream()), workspace)
+    _check(lib().hca_pool_attend(*args, _ptr(ws), n, _stream()))
     return out, lse
 
 

@@ -513,6 +513,40 @@ dsv4_status hca_attend(const void* q, const void* kc, const void* vc, int dt, in
   return run_attend(what, to_args(c, false, nullptr, 0, m, lse), workspace, ws_bytes, stream);
 }
 
+dsv4_status hca_pool_attend(const void* x, const float* gate, const float* pos_bias, int64_t x_bstride,
+                            const void* q, const void* kc, const void* vc, int dt, int32_t m, const void* kw,
+                            const void* vw, const int32_t* win_pos0, int64_t L, int32_t W, const int32_t* q_pos,
+                            int64_t B, int64_t Q, int32_t H, int32_t D, int64_t N, int64_t kv_bstride,
+                            int64_t kv_rstride, int64_t w_rstride, float scale, void* out, float* lse, void* workspace,
+                            size_t* ws_bytes, hipStream_t stream) {
+  const char* what = "hca_pool_attend";
+  AttendCommon c{q, kc, vc, kw, vw, dt, win_pos0, q_pos, L, W, B, Q, H, D, N, kv_bstride, kv_rstride, w_rstride,
+                 scale, out};
+  dsv4_status s = check_attend(what, c);
+  if (s != DSV4_OK) return s;
+  REQUIRE(m >= 1 && m <= 1024, "%s: m must be in [1, 1024], got %d", what, m);
+  SUPPORT(dt == DSV4_BF16 && D == 512, "%s: supports bf16 with D = 512", what);
+  SUPPORT(Q < 16, "%s: supports fewer than 16 queries per sequence (decode)", what);
+  REQUIRE(N >= 1, "%s: N must be >= 1 (the pooled block becomes entry N - 1)", what);
+  const int64_t rs = kv_rstride ? kv_rstride : D;
+  REQUIRE(B == 0 || (kc && vc && reinterpret_cast<const uint16_t*>(vc) == reinterpret_cast<const uint16_t*>(kc) + D &&
+                     rs >= 2 * D),
+          "%s: K and V rows must sit side by side in one buffer (vc = kc + D, kv_rstride >= 2D)", what);
+  REQUIRE(extent_ok({x_bstride}) && (x_bstride == 0 || x_bstride >= m), "%s: x_bstride must be 0 or >= m", what);
+  if (B * Q > 0) REQUIRE(x && gate && pos_bias, "%s: x, gate and pos_bias must not be NULL", what);
+  AttendCommon cn = c;
+  cn.N = N - 1;                                    // the splits stop before the pooled entry
+  cn.kv_bstride = kv_bstride ? kv_bstride : N;
+  dsv4::AttendArgs a = to_args(cn, false, nullptr, 0, m, lse);
+  a.pool.on = B * Q > 0;
+  a.pool.x = x;
+  a.pool.gate = gate;
+  a.pool.bias = pos_bias;
+  a.pool.x_bs = x_bstride ? x_bstride : m;
+  a.pool.row = N - 1;
+  return run_attend(what, a, workspace, ws_bytes, stream);
+}
+
 dsv4_status csa_attend_fp8kv(const void* q, const void* kc, const void* vc, const int32_t* idx, int32_t k,
                              const void* kw, const void* vw, const int32_t* win_pos0, int64_t L, int32_t W,
                              const int32_t* q_pos, int64_t B, int64_t Q, int32_t H, int32_t D, int32_t d_rope,

@@ -24,10 +24,12 @@
 //   queries per workgroup share every K/V tile and every operand read.
 // FP8 K/V rows: the same scheme over E4M3 rows decoded in registers.
 // fp32 path: a plain VALU kernel, one workgroup per (query, head).
+#include <mutex>
 #include <type_traits>
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "pool.hpp"
 
 namespace dsv4 {
 
@@ -161,6 +163,69 @@ __device__ __forceinline__ void tile_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Launch shape of the HCA block pooling inside the attention launch (hca_pool_attend):
+// grid rows at and past `rows` hold `grid` pooling workgroups, two per sequence (the K and
+// the V half of the pooled entry), placed after the key-range workgroups so that they run
+// on the CUs those leave free.
+struct PoolLaunch {
+  int64_t grid = 0;
+  int rows = 0;
+};
+
+// One pooling workgroup: half `wg % 2` (K or V channels) of sequence b's pooled entry,
+// rounded to bf16 into the cache row.  The K half then scores the entry for each of the
+// sequence's queries and writes it as the last part of the split merge: lse = scale * q.k
+// (-inf where the entry is not visible); the part's output, the entry's V row, is read by
+// the merge from the cache row.  The pooling takes all NT threads: 64 lanes of 8 channels
+// per row and NT / 64 row slots.
+template <int D, int NT>
+__device__ __forceinline__ void hca_pool_block(const AttendArgs& a, const PoolLaunch& pl, int part_ix,
+                                               float* __restrict__ lse_part, float* lds) {
+  const int64_t wg = (int64_t)(blockIdx.y - pl.rows) * gridDim.x + blockIdx.x;
+  if (wg >= pl.grid) return;                                 // (whole workgroup)
+  const int64_t b = wg / 2;
+  const int half = (int)(wg % 2);
+  constexpr int LPR = D / 8;                                 // lanes per row of one half
+  constexpr int SPB = NT / LPR;
+  static_assert(NT % LPR == 0 && (D / 8) * (SPB < 128 ? SPB : 128) <= NT, "pooling layout");
+  uint16_t* yrow = reinterpret_cast<uint16_t*>(const_cast<void*>(a.kc)) + (b * a.kv_bs + a.pool.row) * a.kv_rs;
+  float* krow = lds + NT * (pool::XVec<uint16_t>::N + 2);    // the rounded K half (D floats)
+  pool::compress_body<uint16_t, 1, NT>(reinterpret_cast<const uint16_t*>(a.pool.x) + b * a.pool.x_bs * (2 * D),
+                                       a.pool.gate + b * a.m, a.pool.bias, a.m, 2 * D, a.m, 1, 1, 0, 0, yrow, nullptr,
+                                       LPR, a.m < SPB ? a.m : SPB, 1, 2, half, lds, nullptr, 0.f, -1,
+                                       half == 0 ? krow : nullptr);
+  if (half != 0) return;
+  __syncthreads();
+  const int64_t R = a.B * a.Q * a.H;
+  constexpr int TPH = NT / 64;                               // threads per head (up to 64 heads)
+  constexpr int DPT = D / TPH;                               // dims per thread
+  const int h = threadIdx.x / TPH, j = threadIdx.x % TPH;
+  for (int64_t qq = 0; qq < a.Q; ++qq) {
+    const int64_t bq = b * a.Q + qq;
+    const int64_t p = a.q_pos[bq];
+    const int64_t nvis = p < 0 ? 0 : (p + 1) / a.m;
+    float s = 0.f;
+    if (h < a.H) {
+      const uint4* qv = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) + (bq * a.H + h) * D +
+                                                       j * DPT);
+      const float* kr = krow + j * DPT;
+#pragma unroll
+      for (int i = 0; i < DPT / 8; ++i) {
+        const uint4 x = qv[i];
+        const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s = fmaf(__uint_as_float(xw[e] << 16), kr[8 * i + 2 * e], s);
+          s = fmaf(__uint_as_float(xw[e] & 0xffff0000u), kr[8 * i + 2 * e + 1], s);
+        }
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < TPH; o <<= 1) s += __shfl_xor(s, o);
+    if (h < a.H && j == 0) lse_part[(int64_t)part_ix * R + bq * a.H + h] = a.pool.row < nvis ? s * a.scale : -INFINITY;
+  }
+}
+
 // One workgroup = 4 x DS waves: wave w owns heads 16(w%4) .. +15 and the slice w/4 of
 // the head dim for the output (each of the DS waves of a head group computes the same
 // scores over the full head dim; this keeps the accumulators in ordinary VGPRs).  The key list of the split is walked in 16-key tiles
@@ -172,7 +237,7 @@ __device__ __forceinline__ void tile_barrier() {
 template <int D, int DS, bool kNT>
 __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a, int64_t chunk, int splits,
                                                                uint16_t* __restrict__ o_part,
-                                                               float* __restrict__ lse_part) {
+                                                               float* __restrict__ lse_part, PoolLaunch pl) {
   constexpr int KT = 16;                   // keys per tile
   constexpr int NT = kThreads * DS;
   constexpr int NWV = NT / kWave;
@@ -194,6 +259,10 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
   __shared__ int32_t list[kMaxCsaChunk];  // the split's index entries
   __shared__ __attribute__((aligned(16))) uint8_t xchg[DS > 1 ? 2 * NT * 16 : 16];   // partial scores, 2 buffers
 
+  if (pl.grid > 0 && (int)blockIdx.y >= pl.rows) {          // the HCA block pooling workgroups
+    if constexpr (D == 512) hca_pool_block<D, NT>(a, pl, splits, lse_part, reinterpret_cast<float*>(ring));
+    return;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
   const int64_t bq = blockIdx.y;
@@ -203,6 +272,7 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
   const int hg = wave % 4, dh = wave / 4;  // head group and output slice
   const int head = hg * 16 + col;
   const bool wave_on = hg * 16 < a.H;
+  const bool direct = splits == 1 && pl.grid == 0;   // no merge: the output rows directly
 
   // The loads that do not depend on each other are issued together and waited for once:
   // the query position, the split's index entries (CSA: list slots s0 .. s0+chunk-1, all
@@ -523,8 +593,8 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
   // output; the merge accumulates in fp32)
   const int64_t R = a.B * a.Q * a.H;
   const int64_t orow = bq * a.H + head;
-  uint16_t* out = (splits == 1 ? reinterpret_cast<uint16_t*>(a.out) + orow * D
-                               : o_part + ((int64_t)split * R + orow) * D) + dh * DH;
+  uint16_t* out = (direct ? reinterpret_cast<uint16_t*>(a.out) + orow * D
+                          : o_part + ((int64_t)split * R + orow) * D) + dh * DH;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
     uint2 w;
@@ -533,7 +603,7 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
     *reinterpret_cast<uint2*>(out + dt * 16 + 4 * g) = w;
   }
   if (g == 0 && dh == 0) {
-    if (splits == 1) {
+    if (direct) {
       if (a.lse) a.lse[orow] = lse;
     } else {
       lse_part[(int64_t)split * R + orow] = lse;
@@ -1384,10 +1454,14 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(const float* __rest
 // into its own LDS slice; wave w then accumulates parts w, w+4, ... for 8 dims per lane
 // with up to 8 loads in flight, and the four partial sums are added through LDS.
 constexpr int kMergePPT = 8;              // parts per lane and round
+// extra_v (HCA pooling in the attention launch): part P-1 is a single entry whose output
+// row is its V row, extra_v + (r / rows_per_seq) * extra_bs for output row r.
 __global__ __launch_bounds__(kThreads) void merge_bf16_parts_kernel(const uint16_t* __restrict__ o_parts,
                                                                     const float* __restrict__ lse_parts, int P,
                                                                     int64_t R, int D, uint16_t* __restrict__ out,
-                                                                    float* __restrict__ lse_out) {
+                                                                    float* __restrict__ lse_out,
+                                                                    const uint16_t* __restrict__ extra_v,
+                                                                    int64_t extra_bs, int64_t rows_per_seq) {
   constexpr int NW = kThreads / kWave;
   __shared__ float wsh[NW][1024];
   __shared__ float red[NW - 1][kWave * 8];
@@ -1399,12 +1473,15 @@ __global__ __launch_bounds__(kThreads) void merge_bf16_parts_kernel(const uint16
   const bool on = lane < nd8;
   const uint4* base = reinterpret_cast<const uint4*>(o_parts + r * D) + lane;
   const int64_t pstride = R * D / 8;     // uint4 stride between parts
+  const uint4* xrow = extra_v ? reinterpret_cast<const uint4*>(extra_v + (r / rows_per_seq) * extra_bs) + lane : nullptr;
+  auto part_at = [&](int p) -> uint4 {
+    if (!on || p >= P) return make_uint4(0, 0, 0, 0);
+    if (xrow && p == P - 1) return *xrow;
+    return base[(int64_t)p * pstride];
+  };
   uint4 v[kMergePPT];
 #pragma unroll
-  for (int u = 0; u < kMergePPT; ++u) {
-    const int p = wave + u * NW;
-    v[u] = (on && p < P) ? base[(int64_t)p * pstride] : make_uint4(0, 0, 0, 0);
-  }
+  for (int u = 0; u < kMergePPT; ++u) v[u] = part_at(wave + u * NW);
   float mx = -INFINITY;
   for (int p = lane; p < P; p += kWave) mx = fmaxf(mx, lse_parts[(int64_t)p * R + r]);
   mx = wave_max(mx);
@@ -1423,10 +1500,7 @@ __global__ __launch_bounds__(kThreads) void merge_bf16_parts_kernel(const uint16
   for (int p0 = wave; p0 < P; p0 += NW * kMergePPT) {
     if (p0 != wave) {
 #pragma unroll
-      for (int u = 0; u < kMergePPT; ++u) {
-        const int p = p0 + u * NW;
-        v[u] = (on && p < P) ? base[(int64_t)p * pstride] : make_uint4(0, 0, 0, 0);
-      }
+      for (int u = 0; u < kMergePPT; ++u) v[u] = part_at(p0 + u * NW);
     }
 #pragma unroll
     for (int u = 0; u < kMergePPT; ++u) {
@@ -1482,6 +1556,11 @@ AttendPlan plan_attend(const AttendArgs& a) {
   const int64_t n_max = (a.csa ? (int64_t)a.k : a.N) + (win > 0 ? (pairs ? 2 * win : win) : 0);
   if (a.f32 || n_max == 0) {
     p.chunk = (int)(n_max > 0 ? n_max : 1);
+    if (a.pool.on) {                      // one (empty) key range and the pooled entry's part
+      p.chunk = kTile;
+      const int64_t R = a.B * a.Q * a.H;
+      p.ws_bytes = align256((size_t)2 * R * a.D * 2) + align256((size_t)2 * R * 4);
+    }
     return p;
   }
   const int64_t rows = a.B * (pairs ? (a.Q + 1) / 2 : a.Q);
@@ -1494,8 +1573,9 @@ AttendPlan plan_attend(const AttendArgs& a) {
   if (a.csa && chunk > kMaxCsaChunk) chunk = kMaxCsaChunk;
   if (a.f8 && a.csa && chunk > kListF8) chunk = kListF8;
   int64_t splits = (n_max + chunk - 1) / chunk;
-  if (splits > kMaxSplits) {              // the merge holds at most kMaxSplits part weights
-    chunk = ((n_max + kMaxSplits - 1) / kMaxSplits + kTile - 1) / kTile * kTile;
+  const int64_t max_splits_m = kMaxSplits - (a.pool.on ? 1 : 0);   // (the pooled HCA entry is a part)
+  if (splits > max_splits_m) {            // the merge holds at most kMaxSplits part weights
+    chunk = ((n_max + max_splits_m - 1) / max_splits_m + kTile - 1) / kTile * kTile;
     const int64_t cap = a.csa ? (a.f8 ? kListF8 : kMaxCsaChunk) : ((int64_t)1 << 30);
     if (chunk > cap) {
       p.supported = false;
@@ -1505,23 +1585,24 @@ AttendPlan plan_attend(const AttendArgs& a) {
   }
   p.splits = (int)splits;
   p.chunk = (int)chunk;
-  if (splits > 1) {
+  const int64_t parts = splits + (a.pool.on ? 1 : 0);         // the pooled HCA entry is one more part
+  if (parts > 1) {
     const int64_t R = a.B * a.Q * a.H;
-    p.ws_bytes = align256((size_t)splits * R * a.D * 2) + align256((size_t)splits * R * 4);   // bf16 parts
+    p.ws_bytes = align256((size_t)parts * R * a.D * 2) + align256((size_t)parts * R * 4);   // bf16 parts
   }
   return p;
 }
 
 template <bool kNT>
 hipError_t launch_split_kernel(const AttendArgs& a, const AttendPlan& p, dim3 grid, uint16_t* o_part,
-                               float* lse_part, hipStream_t st) {
+                               float* lse_part, hipStream_t st, const PoolLaunch& pl) {
   if (a.f8) {   // D == 512 (checked by the caller)
     DSV4_LAUNCH_MAIN((attend_fp8kv_kernel<512, kNT>), grid, dim3(kThreads * 2), 0, st, a, (int64_t)p.chunk, p.splits,
                      o_part, lse_part);
   } else switch (a.D) {
-    case 128: DSV4_LAUNCH_MAIN((attend_bf16_kernel<128, 1, kNT>), grid, dim3(kThreads), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part); break;
-    case 256: DSV4_LAUNCH_MAIN((attend_bf16_kernel<256, 1, kNT>), grid, dim3(kThreads), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part); break;
-    default: DSV4_LAUNCH_MAIN((attend_bf16_kernel<512, 2, kNT>), grid, dim3(kThreads * 2), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part); break;
+    case 128: DSV4_LAUNCH_MAIN((attend_bf16_kernel<128, 1, kNT>), grid, dim3(kThreads), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part, pl); break;
+    case 256: DSV4_LAUNCH_MAIN((attend_bf16_kernel<256, 1, kNT>), grid, dim3(kThreads), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part, pl); break;
+    default: DSV4_LAUNCH_MAIN((attend_bf16_kernel<512, 2, kNT>), grid, dim3(kThreads * 2), 0, st, a, (int64_t)p.chunk, p.splits, o_part, lse_part, pl); break;
   }
   return hipGetLastError();
 }
@@ -1537,9 +1618,10 @@ hipError_t launch_attend(const AttendArgs& a, const AttendPlan& p, void* ws, hip
   uint16_t* o_part = nullptr;
   float* lse_part = nullptr;
   const int64_t R = rows * a.H;
-  if (p.splits > 1) {
+  const int parts = p.splits + (a.pool.on ? 1 : 0);
+  if (parts > 1) {
     o_part = reinterpret_cast<uint16_t*>(ws);
-    lse_part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + align256((size_t)p.splits * R * a.D * 2));
+    lse_part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + align256((size_t)parts * R * a.D * 2));
   }
   if (use_pairs(a)) {
     dim3 pgrid((unsigned)p.splits, (unsigned)(a.B * ((a.Q + 1) / 2)));
@@ -1548,16 +1630,26 @@ hipError_t launch_attend(const AttendArgs& a, const AttendPlan& p, void* ws, hip
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
     hipLaunchKernelGGL(merge_bf16_parts_kernel, dim3((unsigned)R), dim3(kThreads), 0, st, o_part, lse_part, p.splits,
-                       R, a.D, reinterpret_cast<uint16_t*>(a.out), a.lse);
+                       R, a.D, reinterpret_cast<uint16_t*>(a.out), a.lse, nullptr, (int64_t)0, (int64_t)1);
     return hipGetLastError();
   }
+  // HCA block pooling in the same launch (bf16, D = 512, K|V rows side by side; checked by
+  // the caller): cs workgroups per sequence after the attention rows
+  PoolLaunch pl;
+  if (a.pool.on) {
+    pl.grid = a.B * 2;
+    pl.rows = (int)rows;
+  }
   // one query per sequence: each K/V row is read by one workgroup of the call (streamed)
-  const dim3 grid((unsigned)p.splits, (unsigned)rows);
-  hipError_t e = a.Q == 1 ? launch_split_kernel<true>(a, p, grid, o_part, lse_part, st)
-                          : launch_split_kernel<false>(a, p, grid, o_part, lse_part, st);
-  if (e != hipSuccess || p.splits == 1) return e;
-  hipLaunchKernelGGL(merge_bf16_parts_kernel, dim3((unsigned)R), dim3(kThreads), 0, st, o_part, lse_part, p.splits, R,
-                     a.D, reinterpret_cast<uint16_t*>(a.out), a.lse);   // D <= 512: 8 dims per lane
+  const dim3 grid((unsigned)p.splits, (unsigned)(rows + (pl.grid + p.splits - 1) / p.splits));
+  hipError_t e = a.Q == 1 ? launch_split_kernel<true>(a, p, grid, o_part, lse_part, st, pl)
+                          : launch_split_kernel<false>(a, p, grid, o_part, lse_part, st, pl);
+  if (e != hipSuccess || parts == 1) return e;
+  // the pooled entry's part: its output is the entry's V row in the cache
+  const uint16_t* extra_v = a.pool.on ? reinterpret_cast<const uint16_t*>(a.kc) + a.pool.row * a.kv_rs + a.D : nullptr;
+  hipLaunchKernelGGL(merge_bf16_parts_kernel, dim3((unsigned)R), dim3(kThreads), 0, st, o_part, lse_part, parts, R,
+                     a.D, reinterpret_cast<uint16_t*>(a.out), a.lse, extra_v, a.kv_bs * a.kv_rs,
+                     a.Q * (int64_t)a.H);   // D <= 512: 8 dims per lane
   return hipGetLastError();
 }
 

@@ -29,8 +29,9 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
     const TX* __restrict__ x, const float* __restrict__ gate, const float* __restrict__ bias,
     int64_t T, int C, int m, int64_t nb_per_b, int64_t total_blocks, int64_t x_bs, int64_t y_bs,
     void* __restrict__ y, uint8_t* __restrict__ ysc, int lpr, int spb, int bpw, int cs) {
+  __shared__ float part[kThreads * (XVec<TX>::N + 2)];
   compress_body<TX, YDT>(x, gate, bias, T, C, m, nb_per_b, total_blocks, x_bs, y_bs, y, ysc, lpr, spb, bpw, cs,
-                         blockIdx.x);
+                         blockIdx.x, part);
 }
 
 // One decode step of cache maintenance; workgroup (slice, b) owns lpr channel vectors of
@@ -76,8 +77,9 @@ __global__ __launch_bounds__(kThreads) void append_kernel(
   }
   // the block's last row is the new token: read from x_new, so that the pooling does not
   // wait for the window write above
+  __shared__ float part[kThreads * (XVec<TX>::N + 2)];
   compress_body<TX, YDT>(win + (b * L + first) * C, win_gate + b * L + first, bias, m, C, m, 1, 1, 0, 0, yr, sr, lpr,
-                         spb, bpw, cs, slice, x_new + b * C, gnew);
+                         spb, bpw, cs, slice, part, x_new + b * C, gnew);
 }
 
 template <typename TX, int YDT>
@@ -131,12 +133,13 @@ template <typename TX, int Y1, int Y2>
 __global__ __launch_bounds__(kThreads) void compress2_kernel(PoolJob j1, PoolJob j2, const float* __restrict__ gate,
                                                              const float* __restrict__ bias, int64_t T, int m,
                                                              int64_t nb_per_b, int64_t total_blocks) {
+  __shared__ float part[kThreads * (XVec<TX>::N + 2)];
   if ((int64_t)blockIdx.x < j1.grid)
     compress_body<TX, Y1>(reinterpret_cast<const TX*>(j1.x), gate, bias, T, j1.C, m, nb_per_b, total_blocks, j1.x_bs,
-                          j1.y_bs, j1.y, j1.ysc, j1.lpr, j1.spb, j1.bpw, j1.cs, blockIdx.x);
+                          j1.y_bs, j1.y, j1.ysc, j1.lpr, j1.spb, j1.bpw, j1.cs, blockIdx.x, part);
   else
     compress_body<TX, Y2>(reinterpret_cast<const TX*>(j2.x), gate, bias, T, j2.C, m, nb_per_b, total_blocks, j2.x_bs,
-                          j2.y_bs, j2.y, j2.ysc, j2.lpr, j2.spb, j2.bpw, j2.cs, (int64_t)blockIdx.x - j1.grid);
+                          j2.y_bs, j2.y, j2.ysc, j2.lpr, j2.spb, j2.bpw, j2.cs, (int64_t)blockIdx.x - j1.grid, part);
 }
 
 template <typename TX, int Y1, int Y2>

@@ -524,17 +524,18 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, col = lane & 15;
+  __shared__ float pool_part[pool::kThreads * (pool::XVec<uint16_t>::N + 2)];
   if (pd.on && (int)blockIdx.y >= pd.index_rows) {          // the K|V rows' pooling job
     const int64_t wg = (int64_t)(blockIdx.y - pd.index_rows) * gridDim.x + blockIdx.x;
     if (wg < pd.kv.grid) {
       if (pd.kv_fp8)
         pool::compress_body<uint16_t, 4>(reinterpret_cast<const uint16_t*>(pd.kv.x), pd.gate, pd.bias, pd.m, pd.kv.C,
                                          pd.m, 1, pd.nblk, pd.kv.x_bs, pd.kv.y_bs, pd.kv.y, pd.kv.ysc, pd.kv.lpr,
-                                         pd.kv.spb, pd.kv.bpw, pd.kv.cs, wg);
+                                         pd.kv.spb, pd.kv.bpw, pd.kv.cs, wg, pool_part);
       else
         pool::compress_body<uint16_t, 1>(reinterpret_cast<const uint16_t*>(pd.kv.x), pd.gate, pd.bias, pd.m, pd.kv.C,
                                          pd.m, 1, pd.nblk, pd.kv.x_bs, pd.kv.y_bs, pd.kv.y, pd.kv.ysc, pd.kv.lpr,
-                                         pd.kv.spb, pd.kv.bpw, pd.kv.cs, wg);
+                                         pd.kv.spb, pd.kv.bpw, pd.kv.cs, wg, pool_part);
     }
     return;
   }
@@ -564,7 +565,7 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
       pool::compress_body<uint16_t, 3>(pd.x2 + b * pd.x2_bs, pd.gate + b * pd.m, pd.bias, pd.m, DI, pd.m, 1, 1, 0, 0,
                                        const_cast<uint8_t*>(kbase) + pd.row * (DI / 2),
                                        const_cast<uint8_t*>(sbase) + pd.row * (DI / 32), pd.lpr2, pd.spb2, 1, 1, 0,
-                                       nullptr, 0.f, lane);
+                                       pool_part, nullptr, 0.f, lane);
       wait_vmcnt0();
     }
     asm volatile("" ::: "memory");

@@ -101,7 +101,22 @@ hipError_t launch_index_topk(const IndexArgs& a, void* workspace, hipStream_t st
 
 // ---------------------------------------------------------------- attention
 constexpr int kFp8RopeDims = 64;   // bf16 tail of an FP8 K row
+// An HCA decode step's newest block pooled inside the attention launch (hca_pool_attend):
+// extra workgroups pool each sequence's block of m raw K|V rows into cache entry `row`, the
+// last visible entry; the last of them for a sequence adds that entry's contribution (its
+// score and its V row) as one more part of the split merge, and the key-range splits stop
+// before the entry (the call's N is then the cache's N - 1).
+struct AttendPool {
+  bool on = false;
+  const void* x = nullptr;       // raw K|V rows of the block (bf16, 2D channels), x_bs rows apart
+  const float* gate = nullptr;   // [B, m]
+  const float* bias = nullptr;   // [m]
+  int64_t x_bs = 0;
+  int64_t row = 0;
+};
+
 struct AttendArgs {
+  AttendPool pool;
   const void* q;
   const void* kc;
   const void* vc;

@@ -84,25 +84,28 @@ struct PoolState {
 // combined by a butterfly within the wave, then (blocks wider than a wave) across waves
 // through LDS; otherwise every state goes through LDS and the writer combines them.
 // The work of workgroup `wg` (every thread of the workgroup calls it).
-template <typename TX, int YDT>
+template <typename TX, int YDT, int NT = kThreads>
 __device__ __forceinline__ void compress_body(
     const TX* __restrict__ x, const float* __restrict__ gate, const float* __restrict__ bias,
     int64_t T, int C, int m, int64_t nb_per_b, int64_t total_blocks, int64_t x_bs, int64_t y_bs,
     void* __restrict__ y, uint8_t* __restrict__ ysc, int lpr, int spb, int bpw, int cs, int64_t wg,
-    const TX* __restrict__ last_row = nullptr, float last_gate = 0.f, int tid = -1) {
-  // last_row (one block only): row m-1 of the block and its gate are taken from here
-  // instead of x / gate.  tid: the thread's index in the pooling (default threadIdx.x); a
-  // single wave may pool on its own (tid = lane) when lpr * spb <= 64, which takes no
-  // workgroup barrier.
+    float* part, const TX* __restrict__ last_row = nullptr, float last_gate = 0.f, int tid = -1,
+    float* y_lds = nullptr) {
+  // NT: threads that pool.  part: LDS for the states that cross waves (NT * (V + 2) floats;
+  // not touched when lpr * spb <= 64).  last_row (one block only): row m-1 of the block and
+  // its gate are taken from here instead of x / gate.  tid: the thread's index in the
+  // pooling (default threadIdx.x); threads at NT and above take part in the barriers only,
+  // and a single wave may pool on its own (tid = lane) when lpr * spb <= 64 (no barrier
+  // then).  y_lds (bf16 output, one block): the rounded values also go to LDS, at their
+  // channel index, for a consumer in the same workgroup.
   constexpr int V = XVec<TX>::N;
-  __shared__ float part[kThreads * (V + 2)];          // states crossing waves (or all states)
 
   if (tid < 0) tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int64_t blk0 = (wg / cs) * bpw;                // cs workgroups share a block group,
   const int slice = (int)(wg % cs);                    // each on lpr of its channel vectors
 
-  const int rs_total = kThreads / lpr;
+  const int rs_total = NT / lpr;
   const int slot = tid / lpr, cv = tid % lpr + slice * lpr;
   const int bi = slot / spb, r0 = slot % spb;
   const bool active = slot < rs_total && bi < bpw && blk0 + bi < total_blocks;
@@ -166,11 +169,13 @@ __device__ __forceinline__ void compress_body(
       }
     }
   } else {
-    float* p = part + tid * (V + 2);
-    p[0] = st.M;
-    p[1] = st.s;
+    if (tid < NT) {
+      float* p = part + tid * (V + 2);
+      p[0] = st.M;
+      p[1] = st.s;
 #pragma unroll
-    for (int v = 0; v < V; ++v) p[2 + v] = st.a[v];
+      for (int v = 0; v < V; ++v) p[2 + v] = st.a[v];
+    }
     __syncthreads();
     if (active && r0 == 0) {
       for (int r = 1; r < spb; ++r) {
@@ -205,6 +210,13 @@ __device__ __forceinline__ void compress_body(
       uint32_t* yp = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(y) + row * C + (int64_t)cv * V);
 #pragma unroll
       for (int v = 0; v < V / 2; ++v) yp[v] = w[v];
+      if (y_lds) {
+#pragma unroll
+        for (int v = 0; v < V / 2; ++v) {
+          y_lds[cv * V + 2 * v] = __uint_as_float(w[v] << 16);
+          y_lds[cv * V + 2 * v + 1] = __uint_as_float(w[v] & 0xffff0000u);
+        }
+      }
     }
   } else if constexpr (YDT == 2) {
     if (writer) {

@@ -124,20 +124,28 @@ def test_decode_step_end_to_end_1m_sampled_sequences():
                             ks[:, NC - 1:])
             idx, sc = L.csa_index_topk(qi, wi_d, ki, qpos_d, 4, k, ki_scale=ks, with_scores=True)
         o, lse = L.csa_attend(q, kc, vc, idx, kvw[..., :D], kvw[..., D:], wpos0_d, W, qpos_d, scale)
-        L.csa_compress(hkvw, hg, hbias_d, 128, torch.bfloat16, out=hkvc[:, NH - 1:])
-        ho, hlse = L.hca_attend(hq, hkc, hvc, 128, hkvw[..., :D], hkvw[..., D:], wpos0_d, W, qpos_d, scale)
+        if fused:   # the HCA pooling inside the attention launch (its row cleared first)
+            hkvc[:, NH - 1] = 0
+            ho, hlse = L.hca_pool_attend(hkvw, hg, hbias_d, hq, hkc, hvc, 128, hkvw[..., :D], hkvw[..., D:], wpos0_d,
+                                         W, qpos_d, scale)
+        else:
+            L.csa_compress(hkvw, hg, hbias_d, 128, torch.bfloat16, out=hkvc[:, NH - 1:])
+            ho, hlse = L.hca_attend(hq, hkc, hvc, 128, hkvw[..., :D], hkvw[..., D:], wpos0_d, W, qpos_d, scale)
         return [t.clone() for t in (idx, sc, o, lse, ho, hlse, kvc[:, NC - 1], ki[:, NC - 1], ks[:, NC - 1],
                                     hkvc[:, NH - 1])]
 
     r1 = step(False)
     r2 = step(False)
     r3 = step(True)
+    r4 = step(True)
     torch.cuda.synchronize()
     names = ("idx", "scores", "csa o", "csa lse", "hca o", "hca lse", "kv row", "key codes", "key scales", "hca row")
-    for n, a, b_, c_ in zip(names, r1, r2, r3):
-        assert torch.equal(a, b_), f"decode step not bitwise repeatable: {n}"
-        assert torch.equal(a, c_), f"pooling inside the indexer launch differs from csa_compress2: {n}"
+    for i, (n, a, b_, c_, d_) in enumerate(zip(names, r1, r2, r3, r4)):
+        assert torch.equal(a, b_) and torch.equal(c_, d_), f"decode step not bitwise repeatable: {n}"
+        if n not in ("hca o", "hca lse", "hca row"):   # (the HCA pooling in the attention launch: to the oracle)
+            assert torch.equal(a, c_), f"pooling inside the indexer launch differs from csa_compress2: {n}"
     idx_g, _, o, lse, ho, hlse = r1[:6]
+    ho3, hlse3, hrow3 = r3[4], r3[5], r3[9]
     idx_g = idx_g.cpu().numpy()
     for b in sampled:
         # CSA: the oracle pools the newest block (K|V and the indexer key), encodes its key
@@ -171,6 +179,16 @@ def test_decode_step_end_to_end_1m_sampled_sequences():
                                          hw[..., D:], wpos0[b:b + 1], W, pos[b:b + 1], scale)
         assert row_rel_err(host_bf16(ho[b:b + 1]), ho_r) <= 1e-2
         assert lse_abs_err(hlse[b:b + 1].cpu().numpy(), hlse_r) <= 1e-2
+        # the same with the pooling inside the attention launch (its own pooled row)
+        row3 = host_bf16(hrow3[b:b + 1])[0]
+        tol = np.abs(new_h) * 2.0 ** -7 + 128 * 2.0 ** -21 * np.abs(dec(hkvw_bits[b])).max()
+        assert np.all(np.abs(row3 - new_h) <= tol)
+        hrows3 = hrows.copy()
+        hrows3[0, NH - 1] = row3
+        ho_r3, hlse_r3 = method.hca_attend(dec(hq_bits[b:b + 1]), hrows3[..., :D], hrows3[..., D:], 128, hw[..., :D],
+                                           hw[..., D:], wpos0[b:b + 1], W, pos[b:b + 1], scale)
+        assert row_rel_err(host_bf16(ho3[b:b + 1]), ho_r3) <= 1e-2
+        assert lse_abs_err(hlse3[b:b + 1].cpu().numpy(), hlse_r3) <= 1e-2
     del kvc, ki, ks, hkvc
 
 

@@ -950,6 +950,45 @@ def test_attend_decode_batches(csa, B, Q, H):
     assert torch.equal(o1, o3) and torch.equal(lse1, lse3)
 
 
+@pytest.mark.parametrize("B,Q,H,N", [(8, 1, 64, 1000), (3, 2, 48, 301), (2, 1, 16, 1)])
+def test_hca_pool_attend_against_the_oracle(B, Q, H, N):
+    """hca_pool_attend (the newest 128-token block pooled on free workgroups of the attention
+    launch, its entry merged as a part of its own): the pooled cache row and the attention
+    against the oracle (pooling, then dense attention over every visible entry and the
+    window); a query that does not see the new entry; the call twice in a row, bitwise."""
+    cfg = 560 + B + N
+    D, m, Lw, W = 512, 128, 128, 128
+    T = N * m
+    q = synth.normal(cfg, synth.Q, (B, Q, H, D))
+    kv = synth.normal(cfg, synth.KC, (B, N, 2 * D))
+    win = synth.normal(cfg, synth.KW, (B, Lw, 2 * D))                  # the newest Lw raw tokens (K|V)
+    gate = synth.normal(cfg, synth.GATE, (B, m))
+    bias = synth.normal(cfg, synth.BIAS, (m,), std=0.1)
+    wpos0 = np.full(B, T - Lw, np.int32)
+    pos = np.tile((T - 1 - np.arange(Q, dtype=np.int32) * 3)[None], (B, 1))
+    pos[B - 1, 0] = T - 2                                               # sees entries [0, N - 1) only
+    (qd, qb), (kvd, kvb), (wd, wb) = dev_bf16(q), dev_bf16(kv), dev_bf16(win)
+    scale = 1.0 / math.sqrt(D)
+    outs = []
+    for _ in range(2):
+        o, lse = L.hca_pool_attend(wd[:, Lw - m:], dev(gate), dev(bias), qd, kvd[..., :D], kvd[..., D:], m, wd[..., :D],
+                                   wd[..., D:], dev(wpos0), W, dev(pos), scale)
+        outs.append((o.clone(), lse.clone(), kvd[:, N - 1].clone()))
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b_) for a, b_ in zip(outs[0], outs[1]))
+    dec = codecs.decode_bf16
+    new = method.compress(dec(wb[:, Lw - m:]), gate, bias, m)[:, 0]       # [B, 2D] exact pooled entry
+    row = host(outs[0][2])
+    assert np.all(np.abs(row - new) <= compress_tol(dec(wb[:, Lw - m:]), m, new[:, None])[:, 0])
+    rows = dec(kvb).copy()
+    rows[:, N - 1] = row                                                # the cache as the call left it
+    wr = dec(wb)
+    o_ref, lse_ref = method.hca_attend(dec(qb), rows[..., :D], rows[..., D:], m, wr[..., :D], wr[..., D:], wpos0, W,
+                                       pos, scale)
+    assert row_rel_err(host(outs[0][0]), o_ref) <= 1e-2
+    assert lse_abs_err(host(outs[0][1]), lse_ref) <= 1e-2
+
+
 def test_attend_empty_key_set_and_determinism():
     B, Q, H, D, N, L_ = 1, 2, 64, 512, 64, 32
     q, kc, vc, kw, vw = _attn_inputs(500, B, Q, H, D, N, L_)
