@@ -200,6 +200,35 @@ int main() {
                                       0, 0.1f, P, nullptr, nullptr, nullptr, nullptr),
          {DSV4_ERR_INVALID_ARG});
 
+  // ---- HCA pooling + attention in one launch: size queries and invalid arguments
+  {
+    const int32_t QP[] = {1, 2, 15, 16};
+    for (int64_t N : Ns)
+      for (int32_t Q : QP)
+        for (int32_t H : {16, 64}) {
+          size_t n1 = 0, n2 = 0;
+          uint16_t* kc = (uint16_t*)P;
+          int s1 = hca_pool_attend(P, (float*)P, (float*)P, 0, P, kc, kc + 512, BF16, 128, P, P, (int32_t*)P, 128, 128,
+                                   (int32_t*)P, 8, Q, H, 512, N, 0, 1024, 0, 0.1f, P, nullptr, nullptr, &n1, nullptr);
+          int s2 = hca_pool_attend(P, (float*)P, (float*)P, 0, P, kc, kc + 512, BF16, 128, P, P, (int32_t*)P, 128, 128,
+                                   (int32_t*)P, 8, Q, H, 512, N, 0, 1024, 0, 0.1f, P, nullptr, nullptr, &n2, nullptr);
+          query("hca_pool_attend query", s1, n1, s2, n2);
+        }
+    uint16_t* kc = (uint16_t*)P;
+    expect("hca_pool_attend split K/V", hca_pool_attend(P, (float*)P, (float*)P, 0, P, kc, kc + 4096, BF16, 128, P, P,
+                                                        (int32_t*)P, 128, 128, (int32_t*)P, 8, 1, 64, 512, 1000, 0, 1024,
+                                                        0, 0.1f, P, nullptr, nullptr, nullptr, nullptr),
+           {DSV4_ERR_INVALID_ARG});
+    expect("hca_pool_attend D", hca_pool_attend(P, (float*)P, (float*)P, 0, P, kc, kc + 256, BF16, 128, P, P,
+                                                (int32_t*)P, 128, 128, (int32_t*)P, 8, 1, 64, 256, 1000, 0, 512, 0,
+                                                0.1f, P, nullptr, nullptr, nullptr, nullptr),
+           {DSV4_ERR_UNSUPPORTED});
+    expect("hca_pool_attend N=0", hca_pool_attend(P, (float*)P, (float*)P, 0, P, kc, kc + 512, BF16, 128, P, P,
+                                                  (int32_t*)P, 128, 128, (int32_t*)P, 8, 1, 64, 512, 0, 0, 1024, 0,
+                                                  0.1f, P, nullptr, nullptr, nullptr, nullptr),
+           {DSV4_ERR_INVALID_ARG});
+  }
+
   // ---- merge: invalid arguments only
   for (int64_t v : big) {
     expect("lse_merge R", lse_merge((float*)P, (float*)P, 2, v, 64, P, F32, nullptr, nullptr),
