@@ -246,13 +246,16 @@ def time_schedule(L, torch, marsh, steps):
     replicas rotate layer by layer), the MTP layer attends over its window only.  Returns
     (us per token step, per-layer-type us)."""
     lib = L.lib()
-    parts = [{"csa": c[:3], "hca": c[3:]} for c in marsh]
-    # window-only attention: the HCA call with no compressed entries
+    parts = [{"csa": c[:2], "hca": c[2:]} for c in marsh]
+    # window-only attention: hca_attend with no compressed entries (the pooled HCA call's
+    # arguments from q on, N = 0)
+    lib_ = L.lib()
     for r, c in enumerate(marsh):
-        fn, a = c[4]
-        a = list(a)
+        fn, a = c[2]
+        assert fn.__name__ == "hca_pool_attend"
+        a = list(a[4:])
         a[15] = 0                                   # N
-        parts[r]["swa"] = [(fn, tuple(a))]
+        parts[r]["swa"] = [(lib_.hca_attend, tuple(a))]
 
     def run(kinds):
         for i, kind in enumerate(kinds):
