@@ -74,16 +74,12 @@ KERNEL_BYTES = {
 # the counter's reading for a 256 MiB device copy (see profiles/).  An entry is used only
 # while the kernel source it was measured on is unchanged (sha256 of the file).
 MEASURED_TRAFFIC = {
-    "index_mfma_kernel": {"bytes_per_launch": 151663851,
-        "source_sha256": "55d724a43380e692b8fdd09166fe964408e73df3df2e6f959fe9b18a52c0fdc1"},
-    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 156023635,
-        "source_sha256": "e8faa5bea47fbc91d42ca5dd2c1ae3b4a62bcfe17750be5d6e5053a89dc7efc6"},
-    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32833858,
-        "source_sha256": "e8faa5bea47fbc91d42ca5dd2c1ae3b4a62bcfe17750be5d6e5053a89dc7efc6"},
-    "attend_fp8kv_kernel (HCA)": {"bytes_per_launch": 92170360,
-        "source_sha256": "e8faa5bea47fbc91d42ca5dd2c1ae3b4a62bcfe17750be5d6e5053a89dc7efc6"},
-    "attend_fp8kv_kernel (CSA)": {"bytes_per_launch": 24536691,
-        "source_sha256": "e8faa5bea47fbc91d42ca5dd2c1ae3b4a62bcfe17750be5d6e5053a89dc7efc6"},
+    "index_mfma_kernel": {"bytes_per_launch": 152316977,
+        "source_sha256": "223a00383fb6762a35e258d4191b15f93791fc24f75f4297a0ff0a6f03346a29"},
+    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 157970600,
+        "source_sha256": "d12398dbab0c66643745546dfce9450aab71500becbcc08b3a457389b9fd025c"},
+    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32840335,
+        "source_sha256": "d12398dbab0c66643745546dfce9450aab71500becbcc08b3a457389b9fd025c"},
 }
 
 
