@@ -340,9 +340,11 @@ dsv4_status hca_attend(const void* q, const void* kc, const void* vc, int dt, in
  *             channels, as the cache rows; x_bstride 0 means m);  gate [B, m], pos_bias [m].
  *   kc, vc    one buffer of K|V rows: vc = kc + D elements, kv_rstride >= 2D.
  *   dt = DSV4_BF16, D = 512, Q < 16, N >= 1.  Every other argument, the workspace protocol
- *   and the errors are those of hca_attend.  The call keeps one arrival counter per
- *   sequence in a library-owned array per device (65,536 counters, taken in turn): calls
- *   in flight at once on one device may hold at most that many sequences together.
+ *   and the errors are those of hca_attend (the workspace also holds the pooled entry's
+ *   per-query scores).  Row N - 1 is written by this call and read back by the merge
+ *   launch that ends it; the attention workgroups never read it, so no ordering between
+ *   workgroups of one launch is needed.  x may be the window's rows (both are only read),
+ *   but not row N - 1 of the cache.
  */
 dsv4_status hca_pool_attend(const void* x, const float* gate, const float* pos_bias, int64_t x_bstride,
                             const void* q, const void* kc, const void* vc, int dt, int32_t m, const void* kw,
