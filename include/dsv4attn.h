@@ -238,8 +238,9 @@ dsv4_status csa_index_topk(const void* qi, int qi_dt, const float* wi,
  *             C + 64 bytes with pool->y_scale as for csa_compress), pool->y_bstride rows
  *             between sequences (0 means N).
  *   ki, ki_scale: MXFP4 indexer keys as for csa_index_topk; row pool->row is written.
- *   qi_dt BF16 or MXFP4; ki_dt MXFP4; m * DI <= 512 (m = 4 with DI = 128).  Every other
- *   argument, the workspace protocol and the errors are those of csa_index_topk.
+ *   qi_dt BF16 or MXFP4; ki_dt MXFP4; m a power of two with m * DI <= 512 (m = 4 with
+ *   DI = 128; other m: DSV4_ERR_UNSUPPORTED).  Every other argument, the workspace protocol
+ *   and the errors are those of csa_index_topk.
  */
 typedef struct dsv4_block_pool {
   const void* x;

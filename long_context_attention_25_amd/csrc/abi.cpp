@@ -415,6 +415,8 @@ dsv4_status index_topk_impl(const char* what, const void* qi, int qi_dt, const f
     // the newest block of each sequence, pooled as csa_compress2 would into row pool->row
     SUPPORT(ki_dt == DSV4_MXFP4, "%s: the pooled indexer keys are MXFP4 (ki_dt must be DSV4_MXFP4)", what);
     SUPPORT((int64_t)m * DI <= 512, "%s: m * DI must be <= 512 (the key is pooled by one wave)", what);
+    SUPPORT(m >= 1 && (m & (m - 1)) == 0,
+            "%s: m must be a power of two (the key's rows combine inside one wave), got %d", what, m);
     REQUIRE(pool->row >= 0 && pool->row < N, "%s: pool->row (%lld) must lie in [0, N)", what, (long long)pool->row);
     SUPPORT(pool->y_dt == DSV4_BF16 || pool->y_dt == DSV4_FP8_KV, "%s: pool->y_dt must be DSV4_BF16 or DSV4_FP8_KV",
             what);

@@ -263,12 +263,13 @@ __device__ __forceinline__ uint64_t kth_largest(Get get, uint32_t c, uint32_t ne
 // word), both built in LDS as the scores were emitted.  The workgroup keeps whole histogram
 // bins: every key in the bins from the one holding its KL-th largest score upward, or, when
 // that would be more than KL keys, from the next bin up (then fewer than KL).  The kept keys
-// are written as composites (in no particular order) to out[0 .. count) and *meta receives
+// are written as composites, in ascending key order, to out[0 .. count) and *meta receives
 // {count, nv, floor (low, high words)}: every kept composite is >= floor and every omitted
 // one is below it.  With nv <= KL every visible key is kept (floor 0).
 // key0: index of the chunk's first key; hb: 1 << kRadixBits words of LDS (staging);
 // tmp: 2 NT / 64 words; misc: 4 words.
 constexpr int kLocalChunk = 4096;                            // keys per index workgroup (local selection)
+constexpr size_t kMinLocalLds = 56 * 1024;                   // LDS of a local-path index workgroup
 template <int NT>
 __device__ __forceinline__ void local_select(const float* sc, uint32_t nv, const uint32_t* hist16, uint32_t KL, uint32_t key0,
                              uint64_t* __restrict__ out, uint4* __restrict__ meta, uint32_t* hb, uint32_t* tmp,
@@ -299,7 +300,6 @@ __device__ __forceinline__ void local_select(const float* sc, uint32_t nv, const
   uint32_t total;
   const uint32_t excl = block_scan<NT>(tsum, tmp, &total);
   const uint32_t above = total - excl - tsum;               // keys in higher threads' bins
-  if (tid == 0) misc[3] = 0u;                                // staging counter
   if (above < KL && KL <= above + tsum) {
     uint32_t acc = above;
 #pragma unroll
@@ -350,9 +350,17 @@ __device__ __forceinline__ void local_select(const float* sc, uint32_t nv, const
       wtot += (uint32_t)__popcll(masks[u]);
     }
   }
-  uint32_t base = 0;                                         // one staging reservation per wave
-  if (lane == 0 && wtot) base = atomicAdd(&misc[3], wtot);
-  base = __builtin_amdgcn_readfirstlane(base);
+  // staging offsets in wave order, so that the list is in ascending key order (the row
+  // selection relies on it to compact its result without a key bitmap)
+  if (lane == 0) tmp[wave] = wtot;
+  __syncthreads();
+  uint32_t base = 0, staged = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t x = tmp[w];
+    base += w < wave ? x : 0u;
+    staged += x;
+  }
 #pragma unroll
   for (int u = 0; u < STEPS; ++u) {
     const uint64_t mask = masks[u];
@@ -362,8 +370,8 @@ __device__ __forceinline__ void local_select(const float* sc, uint32_t nv, const
     base += (uint32_t)__popcll(mask);
   }
   __syncthreads();
-  DSV4_DCHECK(misc[3] <= KL, kDbgLocalStage);
-  const uint32_t count = misc[3] < KL ? misc[3] : KL;
+  DSV4_DCHECK(staged <= KL, kDbgLocalStage);
+  const uint32_t count = staged < KL ? staged : KL;
   for (uint32_t j = tid; j < count; j += NT) out[j] = stage[j];
   if (tid == 0) {
     const uint64_t floor = keep_bin >= (uint32_t)kHistBins ? ~0ull : (uint64_t)(keep_bin << (32 - kHistBits)) << 32;
@@ -516,17 +524,18 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
   constexpr int KS = DI / 32;
   constexpr int GPQ = HI / 4;           // lane groups per query slot
   static_assert(!kLocal || QTW == 1, "local selection: one query tile per workgroup");
-  // LDS: [QTW * QPT][kHistWords] histograms; with kLocal then the scores [min(Q, QPT)][chunk]
-  // and the selection's scratch
+  // LDS: [QTW * QPT][kHistWords] histograms (kLocal: [min(Q, QPT)]), with kLocal then the
+  // scores [min(Q, QPT)][chunk] and the selection's scratch.  A pooling workgroup uses the
+  // start of the same space for its states (the launch sizes it for both).
   extern __shared__ uint32_t hist_l[];
-  float* const sc_l = reinterpret_cast<float*>(hist_l + QTW * QPT * kHistWords);
+  float* const sc_l = reinterpret_cast<float*>(hist_l + (kLocal ? (Q < QPT ? Q : QPT) : QTW * QPT) * kHistWords);
   uint32_t* const selb = reinterpret_cast<uint32_t*>(sc_l + (kLocal ? (Q < QPT ? Q : QPT) * chunk : 0));
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, col = lane & 15;
-  __shared__ float pool_part[pool::kThreads * (pool::XVec<uint16_t>::N + 2)];
   if (pd.on && (int)blockIdx.y >= pd.index_rows) {          // the K|V rows' pooling job
     const int64_t wg = (int64_t)(blockIdx.y - pd.index_rows) * gridDim.x + blockIdx.x;
+    float* const pool_part = reinterpret_cast<float*>(hist_l);
     if (wg < pd.kv.grid) {
       if (pd.kv_fp8)
         pool::compress_body<uint16_t, 4>(reinterpret_cast<const uint16_t*>(pd.kv.x), pd.gate, pd.bias, pd.m, pd.kv.C,
@@ -561,11 +570,13 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
   const int64_t klast = c1 - 1;
   if constexpr (KIND == KEY_MXFP4 || KIND == KEY_MXFP4_Q4) {
     // the pooled indexer key of this sequence, by the wave that loads it, before its loads
+    // (lpr2 * spb2 <= 64, both powers of two: the states combine inside the wave, without
+    // LDS or a barrier)
     if (pd.on && pd.row >= c0 && pd.row < c1 && wave == (int)(((pd.row - c0) % KPS) / (TPW * 16))) {
       pool::compress_body<uint16_t, 3>(pd.x2 + b * pd.x2_bs, pd.gate + b * pd.m, pd.bias, pd.m, DI, pd.m, 1, 1, 0, 0,
                                        const_cast<uint8_t*>(kbase) + pd.row * (DI / 2),
                                        const_cast<uint8_t*>(sbase) + pd.row * (DI / 32), pd.lpr2, pd.spb2, 1, 1, 0,
-                                       pool_part, nullptr, 0.f, lane);
+                                       nullptr, nullptr, 0.f, lane);
       wait_vmcnt0();
     }
     asm volatile("" ::: "memory");
@@ -586,7 +597,7 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
   for (int t = 0; t < QTW; ++t) {
     const int64_t left = Q - (qt0 + t) * QPT;
     nq[t] = left <= 0 ? 0 : (left < QPT ? (int)left : QPT);
-    nslots += nq[t] > 0 ? QPT : 0;
+    nslots += kLocal ? nq[t] : (nq[t] > 0 ? QPT : 0);
   }
   for (int i = threadIdx.x; i < nslots * kHistWords; i += kThreads) hist_l[i] = 0u;
   // kLocal: the visible keys of each query of the tile, for the epilogue (loaded here, where
@@ -1095,8 +1106,9 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
 // winners only if its floor lies above that threshold; the omitted keys of such a chunk that
 // lie above the threshold are added from the stored scores and the threshold is taken again
 // (it can only rise, so no other chunk is affected).  If they do not fit in LDS, the whole
-// row is selected from the stored scores instead.  The selection is marked in an LDS bitmap
-// and compacted into ascending indices: the exact top-kk of the fp32 scores.
+// row is selected from the stored scores instead.  The result, ascending indices of the exact
+// top-kk of the fp32 scores, is compacted straight from the slots when no chunk was widened
+// (the chunks' lists are in ascending key order), else through an LDS key bitmap.
 constexpr int kLocalCap = 8192;          // staged candidate slots per row (nch * klocal)
 constexpr int kExpCap = 4096;            // candidates added from chunks with hidden keys
 constexpr int kLocalKeep = 64;           // most candidates a chunk keeps
@@ -1282,7 +1294,64 @@ __global__ __launch_bounds__(FT) void select_local_kernel(
       T = kth_largest_regs<NT, SPT, kLocalRadixBits>(v, cand_l, nexp, kk, hbin_l, tmp, misc);
     }
   }
-  // 4. mark the selection in the bitmap
+  // 4. no chunk widened (the usual case): every chunk's list is in ascending key order and
+  //    the chunks follow each other in slot order (slot f = u NT + tid), so the selected
+  //    slots are compacted in slot order by one block scan of 16-bit counters, two slots
+  //    per word
+  if (!any_hidden) {
+    constexpr int NW = NT / kWave;
+    constexpr int NWD = (SPT + 1) / 2;
+    static_assert(NW * NWD <= 4 * NT / kWave, "scan words fit in tmp");
+    const int lane = tid & 63, wave = tid >> 6;
+    uint32_t cw[NWD], inc[NWD];
+#pragma unroll
+    for (int j = 0; j < NWD; ++j) {
+      uint32_t f2 = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int u = 2 * j + h;
+        if (u < SPT) {
+          const uint32_t key = ~(uint32_t)v[u];
+          DSV4_DCHECK(v[u] == 0ull || v[u] < T || key < n, kDbgCandIndex);
+          f2 |= (v[u] != 0ull && v[u] >= T && key < n ? 1u : 0u) << (16 * h);
+        }
+      }
+      cw[j] = f2;
+      inc[j] = wave_incl_scan(f2);
+      if (lane == 63) tmp[wave * NWD + j] = inc[j];
+    }
+    __syncthreads();
+    uint32_t before[NWD], tot[NWD];
+#pragma unroll
+    for (int j = 0; j < NWD; ++j) before[j] = tot[j] = 0u;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+#pragma unroll
+      for (int j = 0; j < NWD; ++j) {
+        const uint32_t x = tmp[w * NWD + j];
+        before[j] += w < wave ? x : 0u;
+        tot[j] += x;
+      }
+    }
+    uint32_t acc = 0;                                        // selected slots of earlier u
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+      const int j = u >> 1, sh = (u & 1) * 16;
+      const uint32_t pos = acc + (((before[j] + inc[j] - cw[j]) >> sh) & 0xffffu);
+      if (((cw[j] >> sh) & 1u) && pos < (uint32_t)k) {
+        const uint32_t key = ~(uint32_t)v[u];
+        orow[pos] = (int32_t)key;
+        if (srow) srow[pos] = sc[key];
+      }
+      acc += (tot[j] >> sh) & 0xffffu;
+    }
+    for (int64_t p = (int64_t)acc + tid; p < k; p += NT) {
+      orow[p] = -1;
+      if (srow) srow[p] = -INFINITY;
+    }
+    return;
+  }
+  // 5. otherwise mark the selection in the bitmap
   const int64_t wn = ((int64_t)n + 31) / 32;
   for (int64_t w = tid; w < wn; w += NT) bits_l[w] = 0u;
   __syncthreads();
@@ -1304,7 +1373,7 @@ __global__ __launch_bounds__(FT) void select_local_kernel(
       if (comp_key(sc[j], j) >= T) atomicOr(&bits_l[j >> 5], 1u << (j & 31));
   }
   __syncthreads();
-  // 5. compaction: thread t takes WPT consecutive words per round
+  // 6. compaction: thread t takes WPT consecutive words per round
   constexpr int WPT = (kLdsBitmapKeys / 32) / NT;
   uint32_t base_off = 0;
   for (int64_t r0 = 0; r0 < wn; r0 += WPT * NT) {
@@ -1429,8 +1498,9 @@ hipError_t launch_mfma_q(const IndexArgs& a, const TopkPlan& p, const IndexBufs&
   constexpr int QPT = 16 / HI;
   const int64_t QT = (a.Q + QPT - 1) / QPT;
   const int64_t QG = (QT + QTW - 1) / QTW;
-  // the kernel clears and uses QPT histogram slots for each of its non-empty query tiles;
-  // the local selection adds the chunk's scores of each query and its own scratch
+  // the kernel clears and uses QPT histogram slots for each of its non-empty query tiles
+  // (kLocal: one per query of its tile); the local selection adds the chunk's scores of
+  // each query and its own scratch
   const int64_t tiles = QTW < QT ? QTW : QT;
   // pooling of the newest block (csa_pool_index_topk): the K|V rows' job on extra grid rows
   PoolDev pd{};
@@ -1447,19 +1517,28 @@ hipError_t launch_mfma_q(const IndexArgs& a, const TopkPlan& p, const IndexBufs&
     pd.bias = a.pool.bias;
     pd.row = a.pool.row;
     pd.lpr2 = DI / 8;                                          // bf16: 8 channels per lane
-    pd.spb2 = a.m < kWave / pd.lpr2 ? a.m : kWave / pd.lpr2;
+    pd.spb2 = 1;                                               // a power of two, lpr2 * spb2 <= 64
+    while (2 * pd.spb2 <= a.m && 2 * pd.spb2 * pd.lpr2 <= kWave) pd.spb2 *= 2;
     CompressArgs ca;
     ca.x = a.pool.x; ca.x_f32 = false; ca.gate = a.pool.gate; ca.bias = a.pool.bias;
     ca.B = a.B; ca.T = a.m; ca.C = a.pool.C; ca.m = a.m;
     ca.x_bs = a.pool.x_bs; ca.y_bs = a.pool.y_bs; ca.y = a.pool.y; ca.y_scale = a.pool.y_scale; ca.y_dt = a.pool.y_dt;
-    pd.kv = a.pool.y_dt == 4 ? pool::make_job<uint16_t, 4>(ca) : pool::make_job<uint16_t, 1>(ca);
+    pd.kv = a.pool.y_dt == 4 ? pool::make_job_packed<uint16_t, 4>(ca) : pool::make_job_packed<uint16_t, 1>(ca);
     kv_rows = (int)((pd.kv.grid + p.nch - 1) / p.nch);
   }
   dim3 grid((unsigned)p.nch, (unsigned)(a.B * QG + kv_rows));
-  size_t smem = (size_t)(tiles * QPT) * kHistWords * sizeof(uint32_t);
+  size_t smem = (size_t)(kLocal ? (a.Q < QPT ? a.Q : QPT) : tiles * QPT) * kHistWords * sizeof(uint32_t);
   if (kLocal)
     smem += (size_t)(a.Q < QPT ? a.Q : QPT) * p.chunk * sizeof(float) +
             (size_t)((1 << kRadixBits) + 2 * kThreads / kWave + 8) * sizeof(uint32_t);
+  if (a.pool.on) {                                           // a pooling workgroup's states
+    const size_t part = (size_t)pool::kThreads * (pool::XVec<uint16_t>::N + 2) * sizeof(float);
+    smem = smem > part ? smem : part;
+  }
+  // at most two decode workgroups per CU: with three the dispatcher fills some CUs before
+  // others, and at the per-CU read rate the fullest CUs set the kernel's end (measured:
+  // 37.5 us instead of 34.8 us for the 1M-context decode call)
+  if (kLocal && smem < kMinLocalLds) smem = kMinLocalLds;
   const int64_t sstride = ((a.N + 63) / 64) * 64;
   // one query group per sequence: every key is read by one workgroup of the call, so the
   // keys are streamed with the non-temporal hint; with several groups the caches serve the

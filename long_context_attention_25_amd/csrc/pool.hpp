@@ -321,6 +321,25 @@ inline Job make_job(const CompressArgs& a) {
   return j;
 }
 
+// The same job on as few workgroups as its results allow: when the planned split combines
+// each block's slots inside one wave (power-of-two lpr and spb, lpr * spb <= 64), every
+// such split with the same spb adds and combines the same values in the same order, so
+// lpr = 64 / spb (one wave per block) gives the planned job's results bit for bit.  For
+// a pooling that shares a launch with other work, where each workgroup waits for a slot.
+template <typename TX, int YDT>
+inline Job make_job_packed(const CompressArgs& a) {
+  Job j = make_job<TX, YDT>(a);
+  const int lpr_full = (int)(a.C / XVec<TX>::N);
+  const int lpr = kWave / j.spb;
+  const bool pow2 = (j.spb & (j.spb - 1)) == 0 && (j.lpr & (j.lpr - 1)) == 0;
+  if (!pow2 || j.lpr * j.spb > kWave || lpr <= j.lpr || lpr > lpr_full || lpr_full % lpr != 0) return j;
+  j.lpr = lpr;
+  j.cs = lpr_full / lpr;
+  j.bpw = (kThreads / lpr) / j.spb;
+  j.grid = ((a.total_blocks() + j.bpw - 1) / j.bpw) * j.cs;
+  return j;
+}
+
 }  // namespace pool
 }  // namespace dsv4
 

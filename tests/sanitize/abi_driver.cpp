@@ -147,6 +147,10 @@ int main() {
     expect("pool m*DI", csa_pool_index_topk(&pl, P, BF16, (float*)P, P, (uint8_t*)P, MX, (int32_t*)P, 8, 1, 8, 256, 4096,
                                             0, 4, 64, (int32_t*)P, nullptr, nullptr, nullptr, nullptr),
            {DSV4_ERR_UNSUPPORTED});
+    expect("pool m not a power of two", csa_pool_index_topk(&pl, P, BF16, (float*)P, P, (uint8_t*)P, MX, (int32_t*)P, 8,
+                                                            1, 8, 128, 4096, 0, 3, 64, (int32_t*)P, nullptr, nullptr,
+                                                            nullptr, nullptr),
+           {DSV4_ERR_UNSUPPORTED});
   }
 
   // ---- attention: size queries over a sweep (bf16, f32, FP8 rows), then invalid arguments
