@@ -658,16 +658,18 @@ def test_index_topk_concentrated_winners():
     assert np.all(sc[1, 0] == 0)
 
 
-@pytest.mark.parametrize("case", ["decode", "many_queries", "fp4_queries", "fp8_rows"])
+@pytest.mark.parametrize("case", ["decode", "many_queries", "fp4_queries", "fp8_rows", "batch40", "batch256"])
 def test_pool_index_topk_equals_compress2_then_index_topk(case):
     """csa_pool_index_topk (the newest block pooled inside the indexer launch) against
     csa_compress2 followed by csa_index_topk on copies of the same caches: the pooled K|V
     and key rows and the selection bit for bit; the pooled row anywhere in a chunk (here not
-    the last row), several query groups per sequence, MXFP4 queries, FP8 K|V rows."""
+    the last row), several query groups per sequence, MXFP4 queries, FP8 K|V rows, and
+    batches whose planned K|V split is packed into fewer workgroups (40) or kept (256)."""
     cfg = 250 + len(case)
     HI, DI, m = 8, 128, 4
     B, Q, N, k, row = {"decode": (8, 1, 20000, 512, 19999), "many_queries": (2, 37, 3000, 100, 1234),
-                       "fp4_queries": (3, 1, 9000, 256, 5000), "fp8_rows": (2, 1, 6000, 128, 5999)}[case]
+                       "fp4_queries": (3, 1, 9000, 256, 5000), "fp8_rows": (2, 1, 6000, 128, 5999),
+                       "batch40": (40, 1, 3000, 64, 2999), "batch256": (256, 1, 300, 32, 299)}[case]
     C, LW = 1024, 16
     fp8 = case == "fp8_rows"
     k32 = synth.normal(cfg, synth.KI, (B, N, DI))
