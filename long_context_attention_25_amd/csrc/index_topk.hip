@@ -655,14 +655,15 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
 
   // Each wave takes TPW consecutive 16-key tiles per step; the next step's tiles are
   // loaded before this step's are used.  Key indices past the range are clamped to its
-  // last key, so loads never branch; only the score write is guarded.
-  for (; base < c1; base += KPS) {
+  // last key, so loads never branch; only the score write is guarded.  Two steps per
+  // iteration with the tile buffers' roles swapped, so that no buffer is copied.
+  auto step = [&](KeyTile<KIND, DI>(&cu)[TPW], KeyTile<KIND, DI>(&nx)[TPW], const int64_t base) {
     const int64_t nb = base + KPS;
     if (nb < c1) {
 #pragma unroll
       for (int u = 0; u < TPW; ++u) {
         const int64_t key = nb + u * 16 + col;
-        nxt[u].template load<kNT>(kbase, sbase, key < klast ? key : klast, g, true);
+        nx[u].template load<kNT>(kbase, sbase, key < klast ? key : klast, g, true);
       }
     }
     // After the head reduction the GPQ lanes of a query slot hold the same score, so E
@@ -678,7 +679,7 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
           if constexpr (KIND == KEY_MXFP4_Q4) {
 #pragma unroll
             for (int c = 0; c < KS4; ++c) {
-              const auto& kt = cur[u + j];
+              const auto& kt = cu[u + j];
               const v8i32 av = {(int)qa4[t][c].x, (int)qa4[t][c].y, (int)qa4[t][c].z, (int)qa4[t][c].w, 0, 0, 0, 0};
               const v8i32 bv = {(int)kt.w[4 * c], (int)kt.w[4 * c + 1], (int)kt.w[4 * c + 2], (int)kt.w[4 * c + 3],
                                 0, 0, 0, 0};
@@ -693,7 +694,7 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
             // dims for the query and the key operand).
 #pragma unroll
             for (int c = 0; c < DI / 128; ++c) {
-              const auto& kt = cur[u + j];
+              const auto& kt = cu[u + j];
               const uint2* qw = qa8[t] + 4 * c;
               const v8i32 av = {(int)qw[0].x, (int)qw[0].y, (int)qw[1].x, (int)qw[1].y,
                                 (int)qw[2].x, (int)qw[2].y, (int)qw[3].x, (int)qw[3].y};
@@ -706,8 +707,8 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
 #pragma unroll
             for (int c = 0; c < KS; ++c) {
               if constexpr (KIND == KEY_FP8)
-                acc = mfma_fp8(__builtin_bit_cast(long, qa8[t][c]), cur[u + j].op(c), acc);
-              else acc = mfma_bf16(bit_cast_to<bf16x8>(qa16[t][c]), cur[u + j].op(c), acc);
+                acc = mfma_fp8(__builtin_bit_cast(long, qa8[t][c]), cu[u + j].op(c), acc);
+              else acc = mfma_bf16(bit_cast_to<bf16x8>(qa16[t][c]), cu[u + j].op(c), acc);
             }
           }
           float v = wv[t][0] * fmaxf(acc[0], 0.f);
@@ -726,8 +727,10 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
         }
       }
     }
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) cur[u] = nxt[u];
+  };
+  for (; base < c1; base += 2 * KPS) {
+    step(cur, nxt, base);
+    if (base + KPS < c1) step(nxt, cur, base + KPS);
   }
   __syncthreads();
   if constexpr (kLocal) {
