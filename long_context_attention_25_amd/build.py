@@ -33,6 +33,14 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-source additions: the indexer keeps its MFMA results in ordinary VGPRs (with AGPR
+# results every score took an extra copy into a VGPR before its epilogue, ~7 % of the
+# decode index loop's VALU instructions).
+EXTRA_FLAGS = {
+    "index_topk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", "hipcc"):
         if c and (os.path.isabs(c) and os.path.exists(c) or not os.path.isabs(c)):
@@ -62,7 +70,8 @@ def _build(verbose: bool, debug: bool) -> None:
     for s in srcs:
         o = os.path.join(build_dir, os.path.basename(s) + ".o")
         lang = ["-x", "hip"] if s.endswith(".cpp") else []
-        cmd = [_hipcc(), *HIPCC_FLAGS, *(["-DDSV4_DEBUG"] if debug else []), *lang, "-I",
+        cmd = [_hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(os.path.basename(s), []),
+               *(["-DDSV4_DEBUG"] if debug else []), *lang, "-I",
                os.path.join(HERE, "..", "include"), "-c", s, "-o", o]
         if verbose:
             print(" ".join(cmd), flush=True)
