@@ -74,11 +74,11 @@ KERNEL_BYTES = {
 # the counter's reading for a 256 MiB device copy (see profiles/).  An entry is used only
 # while the kernel source it was measured on is unchanged (sha256 of the file).
 MEASURED_TRAFFIC = {
-    "index_mfma_kernel": {"bytes_per_launch": 152316977,
-        "source_sha256": "223a00383fb6762a35e258d4191b15f93791fc24f75f4297a0ff0a6f03346a29"},
-    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 157970600,
+    "index_mfma_kernel": {"bytes_per_launch": 151903076,
+        "source_sha256": "0d4292e54e0bf3214e050c93e9185e98936ba441a58531e1e165e1a80cc17328"},
+    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 157980424,
         "source_sha256": "d12398dbab0c66643745546dfce9450aab71500becbcc08b3a457389b9fd025c"},
-    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32840335,
+    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32841932,
         "source_sha256": "d12398dbab0c66643745546dfce9450aab71500becbcc08b3a457389b9fd025c"},
 }
 
