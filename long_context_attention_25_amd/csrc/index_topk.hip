@@ -18,11 +18,12 @@
 //      become the chunk's candidates; the scores go to the workspace;
 //   2. one workgroup per row selects the top-k among the chunks' candidates, widening the
 //      rare chunk that could hide more winners than it kept (select_local_kernel).
-// Other calls (many queries per sequence, fp32 keys, longer rows): four launches.
+// Other calls (many queries per sequence, fp32 keys, longer rows): five launches.
 //   0. the row histograms are cleared; 1. the index kernel adds its LDS histogram to them
-//   and writes the scores; 2. a chip-wide scan pass (rows x key ranges) marks the keys
-//   above each row's threshold bin in a bitmap and collects the keys inside it;
-//   3. one workgroup per row radix-selects those candidates and compacts the bitmap.
+//   and writes the scores; 2. one workgroup per row finds the row's threshold bin; 3. a
+//   chip-wide scan pass (rows x key ranges) marks the keys above it in a bitmap and
+//   collects the keys inside it; 4. one workgroup per row radix-selects those candidates
+//   and compacts the bitmap.
 // Either way the result is exact on the fp32 scores (ties to the lower index) and
 // independent of scheduling.
 #include "common.hpp"
@@ -811,12 +812,31 @@ constexpr int kFinThreads = 1024;
 constexpr int kLdsBitmapKeys = 1 << 18;                      // bitmap kept in LDS by pass 2
 constexpr int kCandCap = 4096;                               // candidates staged in LDS by pass 2
 
+// Selection, pass 0 (one workgroup per row): the row's threshold bin and the count of keys
+// above it, from its histogram, recorded for the scan ranges and the finish pass (each scan
+// range then reads two words instead of the 16 KB histogram).
+__global__ __launch_bounds__(kScanThreads) void select_threshold_kernel(const uint32_t* __restrict__ hist_g,
+                                                                        uint32_t* __restrict__ thr,
+                                                                        const int32_t* __restrict__ q_pos, int64_t N,
+                                                                        int m, int k) {
+  __shared__ uint32_t tmp[kScanThreads / kWave];
+  __shared__ uint32_t misc[4];
+  const int64_t row = blockIdx.x;
+  const uint32_t n = vis_blocks(q_pos, row, m, N);
+  const uint32_t kk = (uint32_t)k < n ? (uint32_t)k : n;
+  if (kk == 0) return;                     // (the passes below return before reading it)
+  threshold_bin<kScanThreads>(hist_g + row * kHistBins, kk, tmp, misc);
+  if (threadIdx.x == 0) {
+    thr[row * 2] = misc[0];
+    thr[row * 2 + 1] = misc[1];
+  }
+}
+
 template <int KEYS>
 __global__ __launch_bounds__(kScanThreads) void select_scan_kernel(
-    const float* __restrict__ scores, const uint32_t* __restrict__ hist_g, uint32_t* __restrict__ bitmap_g,
-    uint64_t* __restrict__ cand_g, uint32_t* __restrict__ ccount, uint32_t* __restrict__ thr,
-    const int32_t* __restrict__ q_pos, int64_t N, int64_t sstride, int64_t words, int m, int k) {
-  __shared__ uint32_t tmp[kScanThreads / kWave];
+    const float* __restrict__ scores, uint32_t* __restrict__ bitmap_g, uint64_t* __restrict__ cand_g,
+    uint32_t* __restrict__ ccount, const uint32_t* __restrict__ thr, const int32_t* __restrict__ q_pos, int64_t N,
+    int64_t sstride, int64_t words, int m, int k) {
   __shared__ uint32_t misc[4];
   const int tid = threadIdx.x, lane = tid & 63;
   const int64_t row = blockIdx.y;
@@ -828,7 +848,7 @@ __global__ __launch_bounds__(kScanThreads) void select_scan_kernel(
     if (tid == 0) ccount[row * nch + blockIdx.x] = 0u;
     return;
   }
-  // issue the score loads first; the threshold is computed while they are in flight
+  // issue the score loads first; the threshold is read while they are in flight
   const float* sc = scores + row * sstride + c0;
   const int64_t c1 = (c0 + KEYS < (int64_t)n ? c0 + KEYS : (int64_t)n) - c0;   // keys in range
   constexpr int IT = KEYS / (4 * kScanThreads);
@@ -840,12 +860,10 @@ __global__ __launch_bounds__(kScanThreads) void select_scan_kernel(
                    : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
   }
   if (tid == 0) misc[2] = 0u;
-  threshold_bin<kScanThreads>(hist_g + row * kHistBins, kk, tmp, misc);
-  const uint32_t tbin = misc[0];
-  if (blockIdx.x == 0 && tid == 0) {       // recorded once per row for pass 2
-    thr[row * 2] = tbin;
-    thr[row * 2 + 1] = misc[1];
-  }
+  // the row's threshold bin, recorded by select_threshold_kernel (a uniform load)
+  const uint32_t tbin = *reinterpret_cast<const __attribute__((address_space(4))) uint32_t*>(
+      reinterpret_cast<uintptr_t>(thr + row * 2));
+  __syncthreads();                         // (misc[2] is cleared before any range count)
 
   uint32_t* bm = bitmap_g + row * words + c0 / 32;
   uint64_t* cs = cand_g + row * N + c0;
@@ -1652,12 +1670,14 @@ hipError_t launch_index_topk(const IndexArgs& a, void* ws, hipStream_t st) {
   const int64_t words = ((a.N + 127) / 128) * 4;
   const int64_t rk = scan_keys(R);        // keys per range (the workspace holds counts for kScanKeys)
   const int64_t nrg = (a.N + rk - 1) / rk;
+  hipLaunchKernelGGL(select_threshold_kernel, dim3((unsigned)R), dim3(kScanThreads), 0, st, w.hist, thr, a.q_pos, a.N,
+                     a.m, a.k);
   if (rk == kScanKeysMany)
     hipLaunchKernelGGL(select_scan_kernel<kScanKeysMany>, dim3((unsigned)nrg, (unsigned)R), dim3(kScanThreads), 0, st,
-                       w.scores, w.hist, bitmap, cand, ccount, thr, a.q_pos, a.N, sstride, words, a.m, a.k);
+                       w.scores, bitmap, cand, ccount, thr, a.q_pos, a.N, sstride, words, a.m, a.k);
   else
     hipLaunchKernelGGL(select_scan_kernel<kScanKeys>, dim3((unsigned)nrg, (unsigned)R), dim3(kScanThreads), 0, st,
-                       w.scores, w.hist, bitmap, cand, ccount, thr, a.q_pos, a.N, sstride, words, a.m, a.k);
+                       w.scores, bitmap, cand, ccount, thr, a.q_pos, a.N, sstride, words, a.m, a.k);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.N <= kLdsBitmapKeys)
