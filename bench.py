@@ -435,7 +435,8 @@ def measured_ceilings(torch):
     res = {"hbm_read_gbs": round(nbytes / s_read / 1e9, 1), "mfma_tflops": {}}
     iters, mblocks = 4000, 1024
     for kind, name, flops in ((0, "bf16", 16 * 16 * 32 * 2), (1, "fp8 16x16x32", 16 * 16 * 32 * 2),
-                              (2, "fp8 16x16x128", 16 * 16 * 128 * 2), (3, "fp4 16x16x128", 16 * 16 * 128 * 2)):
+                              (2, "fp8 16x16x128", 16 * 16 * 128 * 2), (3, "fp4 16x16x128", 16 * 16 * 128 * 2),
+                              (4, "bf16 16x16x16", 16 * 16 * 16 * 2)):
         sec = timed(lambda: p.dsv4probe_mfma(kind, iters, ctypes.c_void_p(sink.data_ptr()), mblocks, st), 10)
         res["mfma_tflops"][name] = round(mblocks * 4 * iters * 8 * flops / sec / 1e12, 1)
     torch.cuda.synchronize()

@@ -994,12 +994,14 @@ __global__ __launch_bounds__(kThreads * 2) void attend_fp8kv_kernel(AttendArgs a
 // ends when their positions are close (consecutive tokens of a prefill chunk), and walks
 // the union of the two key lists once: every K/V tile is copied into LDS once for both.
 // Wave w takes head group w%4 of query w/4 over the full head dim (Q^T operands 64 VGPRs,
-// O^T accumulators 128), so no partial scores cross waves: one barrier per tile, no score
-// exchange, each softmax computed once.  Per-query masks keep each query to its own keys.
+// O^T accumulators 128), so no partial scores cross waves: no score exchange, each softmax
+// computed once.  Per-query masks keep each query to its own keys.  The loop steps over
+// 32 keys (two 16-key ring stages) per barrier so that P.V runs on the 16x16x32 MFMA.
 // (Splitting the head dim between two waves instead, each wave serving both queries from
 // one operand read, halves the LDS reads per flop but needs a score exchange and a second
 // barrier per tile and computes every softmax twice: 2.2-2.3 ms against 1.74 ms for the
-// 4096-query prefill layer.)
+// 4096-query prefill layer.  One wave per SIMD serving 16 heads of both queries does not
+// fit the register file: both queries' accumulators and Q^T operands spill.)
 template <int D>
 __global__ __launch_bounds__(kThreads * 2) void attend_bf16_pair_kernel(AttendArgs a, int64_t chunk, int splits,
                                                                         uint16_t* __restrict__ o_part,
@@ -1134,41 +1136,47 @@ __global__ __launch_bounds__(kThreads * 2) void attend_bf16_pair_kernel(AttendAr
   const int k_off = col * KSTR + g * (D / 4) * 2;
   const int v_off = (4 * g + (col >> 2)) * VSTR + (col & 3) * 8;
 
-  // S^T of this wave's query (16 keys x 16 heads) over the full head dim
-  auto compute_s = [&](int stage) -> f32x4 {
-    const uint8_t* kt_l = ring + stage * STB;
-    constexpr int CB = 2;
-    constexpr int NB = KS / CB;
-    f32x4 a0 = f32x4{0.f, 0.f, 0.f, 0.f}, b0 = a0;
-    uint4 kv[2][CB];
-    auto kread = [&](int buf, int c0) {
-#pragma unroll
-      for (int c = 0; c < CB; ++c) kv[buf][c] = *reinterpret_cast<const uint4*>(kt_l + k_off + (c0 + c) * 16);
+  // S^T of this wave's query over the full head dim for the two 16-key tiles of a step
+  // (stages st and st + 1): 16 keys x 16 heads each, the two tiles' MFMAs interleaved so
+  // that four accumulators carry the dependent chains
+  auto compute_s2 = [&](int st, f32x4& s0, f32x4& s1) {
+    const uint8_t* k0 = ring + st * STB + k_off;
+    const uint8_t* k1 = k0 + STB;
+    f32x4 a0 = f32x4{0.f, 0.f, 0.f, 0.f}, b0 = a0, a1 = a0, b1 = a0;
+    uint4 kv[2][2];
+    auto kread = [&](int buf, int c) {
+      kv[buf][0] = *reinterpret_cast<const uint4*>(k0 + c * 16);
+      kv[buf][1] = *reinterpret_cast<const uint4*>(k1 + c * 16);
     };
     kread(0, 0);
 #pragma unroll
-    for (int bi = 0; bi < NB; ++bi) {
-      if (bi + 1 < NB) kread((bi + 1) & 1, (bi + 1) * CB);
+    for (int c = 0; c < KS; ++c) {
+      if (c + 1 < KS) kread((c + 1) & 1, c + 1);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int c = 0; c < CB; ++c) {
-        const bf16x8 ka = bit_cast_to<bf16x8>(kv[bi & 1][c]);
-        const int ks = bi * CB + c;
-        if (ks & 1) b0 = mfma_bf16(ka, bit_cast_to<bf16x8>(qop[ks]), b0);
-        else a0 = mfma_bf16(ka, bit_cast_to<bf16x8>(qop[ks]), a0);
+      const bf16x8 qb = bit_cast_to<bf16x8>(qop[c]);
+      if (c & 1) {
+        b0 = mfma_bf16(bit_cast_to<bf16x8>(kv[c & 1][0]), qb, b0);
+        b1 = mfma_bf16(bit_cast_to<bf16x8>(kv[c & 1][1]), qb, b1);
+      } else {
+        a0 = mfma_bf16(bit_cast_to<bf16x8>(kv[c & 1][0]), qb, a0);
+        a1 = mfma_bf16(bit_cast_to<bf16x8>(kv[c & 1][1]), qb, a1);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    return a0 + b0;
+    s0 = a0 + b0;
+    s1 = a1 + b1;
   };
-  // softmax step of one query: returns its P^T operand
-  auto softmax = [&](uint32_t mask, f32x4 s, float& m_run, float& l_run, f32x4* acc) -> v4i16 {
+  // softmax step of one query over a step's 32 keys: returns its P^T operand for the
+  // 16x16x32 MFMA, k-slots 8g .. 8g+3 = keys 4g .. 4g+3 of the first tile and 8g+4 .. 8g+7
+  // the same keys of the second (the rows a lane holds of each S^T tile)
+  auto softmax2 = [&](uint32_t mk0, uint32_t mk1, f32x4 s0, f32x4 s1, float& m_run, float& l_run,
+                      f32x4* acc) -> bf16x8 {
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool ok = (mask >> (4 * g + i)) & 1u;
-      s[i] = ok ? s[i] * sl2 : -INFINITY;
-      mx = fmaxf(mx, s[i]);
+      s0[i] = ((mk0 >> (4 * g + i)) & 1u) ? s0[i] * sl2 : -INFINITY;
+      s1[i] = ((mk1 >> (4 * g + i)) & 1u) ? s1[i] * sl2 : -INFINITY;
+      mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
     }
     mx = max_xor16(mx);
     mx = max_xor32(mx);
@@ -1183,25 +1191,33 @@ __global__ __launch_bounds__(kThreads * 2) void attend_bf16_pair_kernel(AttendAr
       m_run = m_new;
     }
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    float pv[4];
+    float p0[4], p1[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      pv[i] = __builtin_amdgcn_exp2f(s[i] - m_use);
-      l_run += pv[i];
+      p0[i] = __builtin_amdgcn_exp2f(s0[i] - m_use);
+      p1[i] = __builtin_amdgcn_exp2f(s1[i] - m_use);
+      l_run += p0[i] + p1[i];
     }
-    return __builtin_bit_cast(v4i16, make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])));
+    return bit_cast_to<bf16x8>(make_uint4(pack_bf16x2(p0[0], p0[1]), pack_bf16x2(p0[2], p0[3]),
+                                          pack_bf16x2(p1[0], p1[1]), pack_bf16x2(p1[2], p1[3])));
   };
-  // O^T += V^T . P^T over the full head dim
-  auto compute_pv = [&](int stage, v4i16 pb) {
-    const uint8_t* vt_l = ring + stage * STB + KTB;
+  // O^T += V^T . P^T over the full head dim and a step's 32 keys on the 16x16x32 MFMA (the
+  // 16x16x16 form runs at half its rate on gfx950): a lane's V^T operand is the transposed
+  // read of its 4 keys from each of the two tiles, in the k-slot order of P^T
+  auto compute_pv2 = [&](int st, bf16x8 pb) {
+    const uint8_t* v0 = ring + st * STB + KTB + v_off;
+    const uint8_t* v1 = v0 + STB;
     constexpr int DB = 2;
     constexpr int ND = NDT / DB;
-    v4i16 vt[2][DB];
+    v4i16 vt[2][DB][2];
     auto vread = [&](int buf, int d0) {
 #pragma unroll
-      for (int d = 0; d < DB; ++d)
-        vt[buf][d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16*)(vt_l + v_off + (d0 + d) * 32));
+      for (int d = 0; d < DB; ++d) {
+        vt[buf][d][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16*)(v0 + (d0 + d) * 32));
+        vt[buf][d][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16*)(v1 + (d0 + d) * 32));
+      }
     };
     vread(0, 0);
 #pragma unroll
@@ -1210,37 +1226,41 @@ __global__ __launch_bounds__(kThreads * 2) void attend_bf16_pair_kernel(AttendAr
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int d = 0; d < DB; ++d) {
-        acc[bi * DB + d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[bi & 1][d], pb, acc[bi * DB + d], 0, 0, 0);
+        const uint2 lo = __builtin_bit_cast(uint2, vt[bi & 1][d][0]);
+        const uint2 hi = __builtin_bit_cast(uint2, vt[bi & 1][d][1]);
+        acc[bi * DB + d] = mfma_bf16(bit_cast_to<bf16x8>(make_uint4(lo.x, lo.y, hi.x, hi.y)), pb, acc[bi * DB + d]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // Tile t lives in stage t % 4; tiles 0 .. 2 are issued first; step t waits for tile t,
-  // passes a barrier, uses it and then issues tile t+3 into the stage of tile t-1.
-  uint32_t ma0 = 0, ma1 = 0, ma2 = 0, mb0 = 0, mb1 = 0, mb2 = 0;
-  if (ntile > 0) { tile_ptrs(0); ma0 = vm0; mb0 = vm1; issue(0); }
-  if (ntile > 1) { tile_ptrs(1); ma1 = vm0; mb1 = vm1; issue(1); }
-  if (ntile > 2) { tile_ptrs(2); ma2 = vm0; mb2 = vm1; issue(2); }
-  for (int t = 0; t < ntile; ++t) {
-    if (t + 2 < ntile) wait_vmcnt<2 * NL>();
-    else if (t + 1 < ntile) wait_vmcnt<NL>();
-    else wait_vmcnt<0>();
+  // Steps of 32 keys: step u takes tiles 2u and 2u + 1, in stages 2(u % 2) and 2(u % 2) + 1.
+  // Step u waits for its own two tiles and passes a barrier, after which every wave is done
+  // with step u - 1, so step u + 1's tiles go into that step's stages before step u computes.
+  const int nstep = (ntile + 1) / 2;
+  uint32_t ca0 = 0, ca1 = 0, cb0 = 0, cb1 = 0;   // key masks of the current step's tiles (a: query 0, b: query 1)
+  if (nstep > 0) {
+    tile_ptrs(0); ca0 = vm0; cb0 = vm1; issue(0);
+    tile_ptrs(1); ca1 = vm0; cb1 = vm1; issue(1);
+  }
+  for (int u = 0; u < nstep; ++u) {
+    wait_vmcnt<0>();
     tile_barrier();
+    uint32_t na0 = 0, na1 = 0, nb0 = 0, nb1 = 0;
+    if (u + 1 < nstep) {
+      const int st = ((u + 1) & 1) * 2;
+      tile_ptrs(2 * u + 2); na0 = vm0; nb0 = vm1; issue(st);
+      tile_ptrs(2 * u + 3); na1 = vm0; nb1 = vm1; issue(st + 1);
+    }
     if (wave_on) {
-      const f32x4 sv = compute_s(t & 3);
-      const v4i16 pb = softmax(qi == 0 ? ma0 : mb0, sv, m_run, l_run, acc);
-      compute_pv(t & 3, pb);
+      const int st = (u & 1) * 2;
+      f32x4 sv0, sv1;
+      compute_s2(st, sv0, sv1);
+      const bf16x8 pb = softmax2(qi == 0 ? ca0 : cb0, qi == 0 ? ca1 : cb1, sv0, sv1, m_run, l_run, acc);
+      compute_pv2(st, pb);
     }
-    uint32_t ma3 = 0, mb3 = 0;
-    if (t + 3 < ntile) {
-      tile_ptrs(t + 3);
-      ma3 = vm0;
-      mb3 = vm1;
-      issue((t + 3) & 3);
-    }
-    ma0 = ma1; ma1 = ma2; ma2 = ma3;
-    mb0 = mb1; mb1 = mb2; mb2 = mb3;
+    ca0 = na0; ca1 = na1;
+    cb0 = nb0; cb1 = nb1;
   }
   wait_vmcnt<0>();
 

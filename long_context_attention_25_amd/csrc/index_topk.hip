@@ -63,6 +63,7 @@ __global__ void clear_kernel(uint32_t* p, int64_t n) {
 // 2^16 keys per query: kMaxIndexChunk); the flush adds them to the 32-bit row histogram.
 constexpr int kHistWords = kHistBins / 2;
 constexpr int64_t kMaxIndexChunk = 32768;
+constexpr int64_t kXcds = 8;            // gfx950: XCDs, each with its own L2
 
 // Writes one score and counts it in the LDS histogram of its query slot.
 // kStore: the score goes to the global row here (else the caller stores it later).
@@ -810,6 +811,7 @@ constexpr int64_t kManyRows = 256;
 inline int64_t scan_keys(int64_t rows) { return rows >= kManyRows ? kScanKeysMany : kScanKeys; }
 constexpr int kFinThreads = 1024;
 constexpr int kLdsBitmapKeys = 1 << 18;                      // bitmap kept in LDS by pass 2
+constexpr int kLdsBitmapKeysSmall = 1 << 17;                 // ... in a workgroup that fits twice on a CU
 constexpr int kCandCap = 4096;                               // candidates staged in LDS by pass 2
 
 // Selection, pass 0 (one workgroup per row): the row's threshold bin and the count of keys
@@ -856,8 +858,12 @@ __global__ __launch_bounds__(kScanThreads) void select_scan_kernel(
 #pragma unroll
   for (int u = 0; u < IT; ++u) {
     const int64_t kb = (int64_t)(u * kScanThreads + tid) * 4;
-    v[u] = kb < c1 ? reinterpret_cast<const float4*>(sc)[u * kScanThreads + tid]
-                   : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    if (kb < c1) {
+      const uint4 x = load_stream(reinterpret_cast<const uint4*>(sc) + u * kScanThreads + tid);   // read once
+      v[u] = make_float4(__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w));
+    } else {
+      v[u] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    }
   }
   if (tid == 0) misc[2] = 0u;
   // the row's threshold bin, recorded by select_threshold_kernel (a uniform load)
@@ -909,9 +915,10 @@ __global__ __launch_bounds__(kScanThreads) void select_scan_kernel(
 // range slices) in a second; a radix select (kRadixBits-bit digits below the histogram
 // prefix) finds the kk - #(bin > b*) largest candidates, their bits are added to the
 // bitmap, and the bitmap is compacted into ascending indices followed by -1 padding.
-// kLdsBits: the row's bitmap is copied into LDS (N <= kLdsBitmapKeys).
-template <bool kLdsBits>
-__global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
+// LK > 0: the row's bitmap is copied into LDS (N <= LK keys; LK = 2^17 keeps the LDS under
+// 80 KB, so that two rows' workgroups share a CU); LK = 0: it stays in the workspace.
+template <int LK>
+__global__ __launch_bounds__(kFinThreads) __attribute__((amdgpu_waves_per_eu(8))) void select_finish_kernel(
     const float* __restrict__ scores, uint32_t* __restrict__ bitmap_g, const uint64_t* __restrict__ cand_g,
     const uint32_t* __restrict__ ccount, const uint32_t* __restrict__ thr, const int32_t* __restrict__ q_pos,
     int64_t N, int64_t sstride, int64_t words, int m, int k, int nch, int64_t rkeys, int32_t* __restrict__ out_idx,
@@ -920,7 +927,8 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(
   constexpr int kBins = 1 << kRadixBits;
   constexpr int BPT = kBins / NT;
   static_assert(BPT >= 1 && kBins % NT == 0, "digit bins per thread");
-  __shared__ uint32_t bits_l[kLdsBits ? kLdsBitmapKeys / 32 : 1];
+  constexpr bool kLdsBits = LK > 0;
+  __shared__ uint32_t bits_l[kLdsBits ? LK / 32 : 1];
   __shared__ uint64_t cand_l[kCandCap];
   __shared__ uint32_t pre[NT + 1];                           // candidate offsets of the ranges
   __shared__ uint32_t hbin[kBins];
@@ -1458,9 +1466,14 @@ TopkPlan plan_topk(const IndexArgs& a) {
     const int64_t KPS = tpw * 16 * 4;
     const int64_t QT = (a.Q + QPT - 1) / QPT, QG = (QT + p.qtw - 1) / p.qtw;
     int64_t chunk;
-    if (p.qtw > 1) {                     // about 1024 workgroups over the whole call
+    if (p.qtw > 1) {                     // at least about 1024 workgroups over the whole call
       int64_t chunks = 1024 / (a.B * QG);
       if (chunks < 1) chunks = 1;
+      // a multiple of the 8 XCDs: workgroup i runs on XCD i % 8, so with the key ranges as
+      // the grid's fastest dimension each XCD reads one range of every sequence and its L2
+      // keeps that range for all the query groups (one 66K-key prefill row: 1 MB of fp8
+      // keys per XCD, against 4 MB per range with three ranges)
+      chunks = (chunks + kXcds - 1) / kXcds * kXcds;
       chunk = (N + chunks - 1) / chunks;
     } else {                             // about two workgroups per CU over the whole call
       chunk = (N * (a.B * QT) + 511) / 512;
@@ -1662,9 +1675,9 @@ hipError_t launch_index_topk(const IndexArgs& a, void* ws, hipStream_t st) {
   }
   // selection: pass 1 over all rows x key ranges, pass 2 one workgroup per row
   if (a.N == 0) {
-    hipLaunchKernelGGL(select_finish_kernel<true>, dim3((unsigned)R), dim3(kFinThreads), 0, st, w.scores, bitmap,
-                       cand, ccount, thr, a.q_pos, a.N, (int64_t)0, (int64_t)0, a.m, a.k, 0, (int64_t)kScanKeys,
-                       a.out_idx, a.out_score);
+    hipLaunchKernelGGL(select_finish_kernel<kLdsBitmapKeysSmall>, dim3((unsigned)R), dim3(kFinThreads), 0, st,
+                       w.scores, bitmap, cand, ccount, thr, a.q_pos, a.N, (int64_t)0, (int64_t)0, a.m, a.k, 0,
+                       (int64_t)kScanKeys, a.out_idx, a.out_score);
     return hipGetLastError();
   }
   const int64_t words = ((a.N + 127) / 128) * 4;
@@ -1680,12 +1693,16 @@ hipError_t launch_index_topk(const IndexArgs& a, void* ws, hipStream_t st) {
                        w.scores, bitmap, cand, ccount, thr, a.q_pos, a.N, sstride, words, a.m, a.k);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.N <= kLdsBitmapKeys)
-    hipLaunchKernelGGL(select_finish_kernel<true>, dim3((unsigned)R), dim3(kFinThreads), 0, st, w.scores, bitmap,
-                       cand, ccount, thr, a.q_pos, a.N, sstride, words, a.m, a.k, (int)nrg, rk, a.out_idx,
+  if (a.N <= kLdsBitmapKeysSmall)
+    hipLaunchKernelGGL(select_finish_kernel<kLdsBitmapKeysSmall>, dim3((unsigned)R), dim3(kFinThreads), 0, st,
+                       w.scores, bitmap, cand, ccount, thr, a.q_pos, a.N, sstride, words, a.m, a.k, (int)nrg, rk,
+                       a.out_idx, a.out_score);
+  else if (a.N <= kLdsBitmapKeys)
+    hipLaunchKernelGGL(select_finish_kernel<kLdsBitmapKeys>, dim3((unsigned)R), dim3(kFinThreads), 0, st, w.scores,
+                       bitmap, cand, ccount, thr, a.q_pos, a.N, sstride, words, a.m, a.k, (int)nrg, rk, a.out_idx,
                        a.out_score);
   else
-    hipLaunchKernelGGL(select_finish_kernel<false>, dim3((unsigned)R), dim3(kFinThreads), 0, st, w.scores, bitmap,
+    hipLaunchKernelGGL(select_finish_kernel<0>, dim3((unsigned)R), dim3(kFinThreads), 0, st, w.scores, bitmap,
                        cand, ccount, thr, a.q_pos, a.N, sstride, words, a.m, a.k, (int)nrg, rk, a.out_idx,
                        a.out_score);
   return hipGetLastError();

@@ -37,7 +37,7 @@ __global__ __launch_bounds__(kThreads) void read_kernel(const u32x4* __restrict_
 // One MFMA of the given kind accumulating into c (a VGPR quad):
 //   0: v_mfma_f32_16x16x32_bf16            1: v_mfma_f32_16x16x32_fp8_fp8
 //   2: v_mfma_scale_f32_16x16x128_f8f6f4 with fp8 (e4m3) operands
-//   3: the same with fp4 (e2m1) operands
+//   3: the same with fp4 (e2m1) operands        4: v_mfma_f32_16x16x16_bf16
 // Issued from asm so that the accumulators stay in place: compiled from the builtins, the
 // loop below moved one of them through AGPR copies and padding every iteration, which
 // halved the measured rate.
@@ -51,9 +51,12 @@ __device__ __forceinline__ void mfma_op(f32x4& c, const u32x4& a4, const i32x8& 
   } else if constexpr (KIND == 2) {
     asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %1, %0, %2, %2 op_sel_hi:[0,0,0]"
                  : "+v"(c) : "v"(a8), "v"(sc));
-  } else {
+  } else if constexpr (KIND == 3) {
     asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %1, %0, %2, %2 op_sel_hi:[0,0,0] cbsz:4 blgp:4"
                  : "+v"(c) : "v"(a4), "v"(sc));
+  } else {
+    const uint64_t a2 = ((uint64_t)a4[1] << 32) | a4[0];
+    asm volatile("v_mfma_f32_16x16x16_bf16 %0, %1, %1, %0" : "+v"(c) : "v"(a2));
   }
 }
 
@@ -95,8 +98,9 @@ int dsv4probe_read(const void* buf, int64_t bytes, uint32_t* out, int blocks, hi
   return (int)hipGetLastError();
 }
 
-// Issues blocks * 4 waves * iters * 8 MFMAs of the given kind (0..3, see mfma_op); `out`
-// holds blocks * 256 floats.  Flops per MFMA: 16*16*32*2 (kinds 0, 1), 16*16*128*2 (2, 3).
+// Issues blocks * 4 waves * iters * 8 MFMAs of the given kind (0..4, see mfma_op); `out`
+// holds blocks * 256 floats.  Flops per MFMA: 16*16*32*2 (kinds 0, 1), 16*16*128*2 (2, 3),
+// 16*16*16*2 (4).
 int dsv4probe_mfma(int kind, int64_t iters, float* out, int blocks, hipStream_t stream) {
   if (!out || iters <= 0 || blocks <= 0) return (int)hipErrorInvalidValue;
   switch (kind) {
@@ -104,6 +108,7 @@ int dsv4probe_mfma(int kind, int64_t iters, float* out, int blocks, hipStream_t 
     case 1: hipLaunchKernelGGL(mfma_kernel<1>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, iters, out); break;
     case 2: hipLaunchKernelGGL(mfma_kernel<2>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, iters, out); break;
     case 3: hipLaunchKernelGGL(mfma_kernel<3>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, iters, out); break;
+    case 4: hipLaunchKernelGGL(mfma_kernel<4>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, iters, out); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();

@@ -608,6 +608,33 @@ def test_index_topk_many_rows_long_ranges():
         assert check_topk(idx[0, q], s_ref[0, q], int(nvis[0, q]), k) <= 2
 
 
+def test_index_topk_many_queries_rows_past_2e17_keys():
+    """A many-query call (several query tiles per workgroup) whose rows see 131,073 to
+    262,144 keys: the row selection keeps its key bitmap on chip in the larger of its two
+    layouts (rows of at most 2^17 keys take the smaller one, two workgroups to a CU).
+    Sampled rows, including the shortest and the longest, against the oracle."""
+    cfg = 266
+    B, Q, HI, DI, N, m, k = 2, 32, 8, 128, 150000, 4, 512
+    q32 = synth.normal(cfg, synth.QI, (B, Q, HI, DI))
+    w = synth.uniform(cfg, synth.WI, (B, Q, HI))
+    k32 = synth.normal(cfg, synth.KI, (B, N, DI))
+    pos = (4 * N - 1 - 4 * 600 * np.arange(Q, dtype=np.int32)[::-1]).reshape(1, Q).repeat(B, 0).astype(np.int32)
+    qd, qb = dev_bf16(q32)
+    kd, kb = dev_bf16(k32)
+    print("index_topk many queries: N=150000 B=2 Q=32", flush=True)
+    idx = L.csa_index_topk(qd, dev(w), kd, dev(pos), m, k)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    nvis = method.visible_blocks(pos, m, N)
+    assert nvis.min() > 1 << 17
+    sel = [0, 13, Q - 1]
+    q64, k64 = codecs.decode_bf16(qb), codecs.decode_bf16(kb)
+    s_ref = _scores_oracle(q64[:, sel], w[:, sel], k64, pos[:, sel], m)
+    for b in range(B):
+        for j, q in enumerate(sel):
+            assert check_topk(idx[b, q], s_ref[b, j], int(nvis[b, q]), k) <= 2
+
+
 @pytest.mark.parametrize("N", [10000, 300000])
 def test_index_topk_many_candidates(N):
     """All-zero scores put every key into the threshold bin: more candidates than the
