@@ -584,31 +584,45 @@ __global__ __launch_bounds__(kThreads * DS) void attend_bf16_kernel(AttendArgs a
     mq2 = mq3;
   }
   wait_vmcnt<0>();                           // no copy into LDS outlives the workgroup
+  __syncthreads();                           // every wave is done with the ring
 
-  if (!wave_on) return;
-  l_run = add_xor16(l_run);
-  l_run = add_xor32(l_run);
-  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-  const float lse = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
-  // the output row, or with several splits this split's partial row (bf16 like the
-  // output; the merge accumulates in fp32)
+  // the output rows, or with several splits this split's partial rows (bf16 like the
+  // output; the merge accumulates in fp32): staged in LDS as [head][dim] rows, then
+  // written with one 16-byte store per lane, a whole row per wave instruction (a lane's
+  // accumulators hold 4 dims of one head: stored directly they make 32-byte pieces)
+  constexpr int OSTR = RB + 16;              // staging row stride: the lanes' 8-byte writes hit distinct banks
+  static_assert(kHeads * OSTR <= 4 * STB, "staged output rows fit in the ring");
   const int64_t R = a.B * a.Q * a.H;
-  const int64_t orow = bq * a.H + head;
-  uint16_t* out = (direct ? reinterpret_cast<uint16_t*>(a.out) + orow * D
-                          : o_part + ((int64_t)split * R + orow) * D) + dh * DH;
+  if (wave_on) {
+    l_run = add_xor16(l_run);
+    l_run = add_xor32(l_run);
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    const float lse = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+    uint8_t* srow = ring + head * OSTR + (dh * DH + 4 * g) * 2;
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-    uint2 w;
-    w.x = pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv);
-    w.y = pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv);
-    *reinterpret_cast<uint2*>(out + dt * 16 + 4 * g) = w;
-  }
-  if (g == 0 && dh == 0) {
-    if (direct) {
-      if (a.lse) a.lse[orow] = lse;
-    } else {
-      lse_part[(int64_t)split * R + orow] = lse;
+    for (int dt = 0; dt < NDT; ++dt) {
+      uint2 w;
+      w.x = pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv);
+      w.y = pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv);
+      *reinterpret_cast<uint2*>(srow + dt * 32) = w;
     }
+    if (g == 0 && dh == 0) {
+      const int64_t orow = bq * a.H + head;
+      if (direct) {
+        if (a.lse) a.lse[orow] = lse;
+      } else {
+        lse_part[(int64_t)split * R + orow] = lse;
+      }
+    }
+  }
+  __syncthreads();
+  uint16_t* out = direct ? reinterpret_cast<uint16_t*>(a.out) + bq * a.H * D
+                         : o_part + ((int64_t)split * R + bq * a.H) * D;
+  const int nchunk = a.H * LPR;              // 16-byte chunks of the workgroup's rows
+  for (int c = tid; c < nchunk; c += NT) {
+    const int r = c / LPR, off = c % LPR;
+    const uint4 v = *reinterpret_cast<const uint4*>(ring + r * OSTR + off * 16);
+    *reinterpret_cast<uint4*>(out + (int64_t)r * D + off * 8) = v;
   }
 }
 
@@ -962,29 +976,42 @@ __global__ __launch_bounds__(kThreads * 2) void attend_fp8kv_kernel(AttendArgs a
     mq2 = mq3;
   }
   wait_vmcnt<0>();
+  __syncthreads();                           // every wave is done with the ring
 
-  if (!wave_on) return;
-  l_run = add_xor16(l_run);
-  l_run = add_xor32(l_run);
-  const float inv = l_run > 0.f ? a.v_scale / l_run : 0.f;
-  const float lse = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+  // output rows staged in LDS as [head][dim] bf16 rows, then one 16-byte store per lane
+  constexpr int ORB = D * 2, OLPR = ORB / 16, OSTR = ORB + 16;
+  static_assert(kHeads * OSTR <= 4 * STB, "staged output rows fit in the ring");
   const int64_t R = a.B * a.Q * a.H;
-  const int64_t orow = bq * a.H + head;
-  uint16_t* out = (splits == 1 ? reinterpret_cast<uint16_t*>(a.out) + orow * D
-                               : o_part + ((int64_t)split * R + orow) * D) + dh * DH;
+  if (wave_on) {
+    l_run = add_xor16(l_run);
+    l_run = add_xor32(l_run);
+    const float inv = l_run > 0.f ? a.v_scale / l_run : 0.f;
+    const float lse = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+    uint8_t* srow = ring + head * OSTR + (dh * DH + 4 * g) * 2;
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-    uint2 w;
-    w.x = pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv);
-    w.y = pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv);
-    *reinterpret_cast<uint2*>(out + dt * 16 + 4 * g) = w;
-  }
-  if (g == 0 && dh == 0) {
-    if (splits == 1) {
-      if (a.lse) a.lse[orow] = lse;
-    } else {
-      lse_part[(int64_t)split * R + orow] = lse;
+    for (int dt = 0; dt < NDT; ++dt) {
+      uint2 w;
+      w.x = pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv);
+      w.y = pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv);
+      *reinterpret_cast<uint2*>(srow + dt * 32) = w;
     }
+    if (g == 0 && dh == 0) {
+      const int64_t orow = bq * a.H + head;
+      if (splits == 1) {
+        if (a.lse) a.lse[orow] = lse;
+      } else {
+        lse_part[(int64_t)split * R + orow] = lse;
+      }
+    }
+  }
+  __syncthreads();
+  uint16_t* out = splits == 1 ? reinterpret_cast<uint16_t*>(a.out) + bq * a.H * D
+                              : o_part + ((int64_t)split * R + bq * a.H) * D;
+  const int nchunk = a.H * OLPR;
+  for (int c = tid; c < nchunk; c += NT) {
+    const int r = c / OLPR, off = c % OLPR;
+    const uint4 v = *reinterpret_cast<const uint4*>(ring + r * OSTR + off * 16);
+    *reinterpret_cast<uint4*>(out + (int64_t)r * D + off * 8) = v;
   }
 }
 
@@ -1263,33 +1290,44 @@ __global__ __launch_bounds__(kThreads * 2) void attend_bf16_pair_kernel(AttendAr
     cb0 = nb0; cb1 = nb1;
   }
   wait_vmcnt<0>();
+  __syncthreads();                           // every wave is done with the ring
 
-  if (!wave_on) return;
+  // both queries' output rows staged in LDS as [query][head][dim] bf16 rows, then one
+  // 16-byte store per lane (the two rows of a head are consecutive in the output)
+  constexpr int OSTR = RB + 16;
+  static_assert(2 * kHeads * OSTR <= 4 * STB, "staged output rows fit in the ring");
   const int64_t R = a.B * a.Q * a.H;
-  auto finish = [&](int64_t bq, float m_run, float l_run, const f32x4* acc) {
+  if (wave_on) {
     l_run = add_xor16(l_run);
     l_run = add_xor32(l_run);
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     const float lse = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
-    const int64_t orow = bq * a.H + head;
-    uint16_t* out = splits == 1 ? reinterpret_cast<uint16_t*>(a.out) + orow * D
-                                : o_part + ((int64_t)split * R + orow) * D;
+    uint8_t* srow = ring + (qi * a.H + head) * OSTR + 4 * g * 2;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       uint2 w;
       w.x = pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv);
       w.y = pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv);
-      *reinterpret_cast<uint2*>(out + dt * 16 + 4 * g) = w;
+      *reinterpret_cast<uint2*>(srow + dt * 32) = w;
     }
-    if (g == 0) {
+    if (g == 0 && (qi == 0 || has1)) {
+      const int64_t orow = (bq0 + qi) * a.H + head;
       if (splits == 1) {
         if (a.lse) a.lse[orow] = lse;
       } else {
         lse_part[(int64_t)split * R + orow] = lse;
       }
     }
-  };
-  finish(qi == 0 ? bq0 : bq0 + 1, m_run, l_run, acc);
+  }
+  __syncthreads();
+  uint16_t* out = splits == 1 ? reinterpret_cast<uint16_t*>(a.out) + bq0 * a.H * D
+                              : o_part + ((int64_t)split * R + bq0 * a.H) * D;
+  const int nchunk = (has1 ? 2 : 1) * a.H * LPR;   // rows of query 0, then of query 1
+  for (int c = tid; c < nchunk; c += NT) {
+    const int r = c / LPR, off = c % LPR;
+    const uint4 v = *reinterpret_cast<const uint4*>(ring + r * OSTR + off * 16);
+    *reinterpret_cast<uint4*>(out + (int64_t)r * D + off * 8) = v;
+  }
 }
 
 // ---------------------------------------------------------------------------- fp32 / VALU
