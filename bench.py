@@ -74,12 +74,12 @@ KERNEL_BYTES = {
 # the counter's reading for a 256 MiB device copy (see profiles/).  An entry is used only
 # while the kernel source it was measured on is unchanged (sha256 of the file).
 MEASURED_TRAFFIC = {
-    "index_mfma_kernel": {"bytes_per_launch": 151912323,
-        "source_sha256": "639976391756e6e2df9440479e3f6cc7b94613c4af450263861f0c92964a415b"},
-    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 157988331,
-        "source_sha256": "a970b1131079bcd5d2fc63e13a8bd077f152e7d443cd7eaa39ccae9e8766587e"},
-    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32837771,
-        "source_sha256": "a970b1131079bcd5d2fc63e13a8bd077f152e7d443cd7eaa39ccae9e8766587e"},
+    "index_mfma_kernel": {"bytes_per_launch": 151853344,
+        "source_sha256": "77b0f0a05c8ea3f8bdfd648cf64de3cc377f489e1d161b1a403bf23b77016426"},
+    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 157989691,
+        "source_sha256": "d06b252d9fbb7db53c5156c03001dd0ebdbaea00a299f956ba8f58a9c8c628ae"},
+    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32835050,
+        "source_sha256": "d06b252d9fbb7db53c5156c03001dd0ebdbaea00a299f956ba8f58a9c8c628ae"},
 }
 
 
