@@ -79,8 +79,9 @@ __device__ __forceinline__ void emit_score(float* scores, uint32_t* hist_l, int6
   }
 }
 
+template <int NT = kThreads>
 __device__ __forceinline__ void flush_hist(const uint32_t* hist_l, uint32_t* hist_g, int64_t row) {
-  for (int w = threadIdx.x; w < kHistWords; w += kThreads) {
+  for (int w = threadIdx.x; w < kHistWords; w += NT) {
     const uint32_t c = hist_l[w];
     if (c & 0xffffu) atomicAdd(&hist_g[row * kHistBins + 2 * w], c & 0xffffu);
     if (c >> 16) atomicAdd(&hist_g[row * kHistBins + 2 * w + 1], c >> 16);
@@ -514,8 +515,8 @@ struct PoolDev {
 // chunk's scores in LDS and ends with a local selection of each query's klocal best keys
 // (cand_loc [rows][nch][klocal] composites, meta_loc [rows][nch]); the row histogram in
 // hist_g is not used.
-template <int KIND, int DI, int HI, int QTW, bool kNT, bool kLocal>
-__global__ __launch_bounds__(kThreads) void index_mfma_kernel(
+template <int KIND, int DI, int HI, int QTW, bool kNT, bool kLocal, int NW = 4>
+__global__ __launch_bounds__(NW * kWave) void index_mfma_kernel(
     const uint8_t* __restrict__ qi, const uint8_t* __restrict__ qsc, const float* __restrict__ wi,
     const uint8_t* ki, const uint8_t* ksc, const int32_t* __restrict__ q_pos, int64_t N,
     int64_t k_bs, int64_t Q, int m, int64_t chunk, float* __restrict__ scores, int64_t sstride,
@@ -525,7 +526,9 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
   constexpr int QPT = 16 / HI;          // queries per 16-row MFMA tile
   constexpr int KS = DI / 32;
   constexpr int GPQ = HI / 4;           // lane groups per query slot
+  constexpr int NTH = NW * kWave;       // threads (8 waves only for many-query calls without pooling)
   static_assert(!kLocal || QTW == 1, "local selection: one query tile per workgroup");
+  static_assert(NW == 4 || (NW == 8 && QTW > 1 && !kLocal), "eight waves: many-query calls");
   // LDS: [QTW * QPT][kHistWords] histograms (kLocal: [min(Q, QPT)]), with kLocal then the
   // scores [min(Q, QPT)][chunk] and the selection's scratch.  A pooling workgroup uses the
   // start of the same space for its states (the launch sizes it for both).
@@ -563,8 +566,8 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
     kbase = ki + b * k_bs * (DI / 2);
     sbase = ksc + b * k_bs * (DI / 32);
   }
-  constexpr int TPW = QTW == 1 ? tiles_per_step<KIND, DI>() : (KIND == KEY_FP8 ? 4 : 2);
-  constexpr int KPS = TPW * 16 * 4;
+  constexpr int TPW = QTW == 1 ? tiles_per_step<KIND, DI>() : (KIND == KEY_FP8 && NW == 4 ? 4 : 2);
+  constexpr int KPS = TPW * 16 * NW;
   constexpr int E = GPQ < TPW ? GPQ : TPW;
   const int64_t c0 = (int64_t)blockIdx.x * chunk;
   int64_t c1 = c0 + chunk;
@@ -601,7 +604,7 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
     nq[t] = left <= 0 ? 0 : (left < QPT ? (int)left : QPT);
     nslots += kLocal ? nq[t] : (nq[t] > 0 ? QPT : 0);
   }
-  for (int i = threadIdx.x; i < nslots * kHistWords; i += kThreads) hist_l[i] = 0u;
+  for (int i = threadIdx.x; i < nslots * kHistWords; i += NTH) hist_l[i] = 0u;
   // kLocal: the visible keys of each query of the tile, for the epilogue (loaded here, where
   // the latency is hidden behind the first key loads)
   __shared__ uint32_t nvis_ep[kLocal ? QPT : 1];
@@ -759,7 +762,7 @@ __global__ __launch_bounds__(kThreads) void index_mfma_kernel(
 #pragma unroll
     for (int t = 0; t < QTW; ++t)
       for (int s = 0; s < nq[t]; ++s)
-        flush_hist(hist_l + (t * QPT + s) * kHistWords, hist_g, b * Q + (qt0 + t) * QPT + s);
+        flush_hist<NTH>(hist_l + (t * QPT + s) * kHistWords, hist_g, b * Q + (qt0 + t) * QPT + s);
   }
 }
 
@@ -1462,8 +1465,9 @@ TopkPlan plan_topk(const IndexArgs& a) {
     // blocks; a decode call (few queries per sequence, any batch) keeps one query tile and
     // streams its keys once
     p.qtw = (a.DI == 128 && a.HI == 8 && a.Q >= 8 && R >= 64) ? 4 : 1;
-    const int64_t tpw = p.qtw == 1 ? tiles_per_step_host(a.kind, a.DI) : (a.kind == KEY_FP8 ? 4 : 2);
-    const int64_t KPS = tpw * 16 * 4;
+    const int64_t nw = (p.qtw > 1 && !a.pool.on) ? 8 : 4;   // waves per index workgroup
+    const int64_t tpw = p.qtw == 1 ? tiles_per_step_host(a.kind, a.DI) : (a.kind == KEY_FP8 && nw == 4 ? 4 : 2);
+    const int64_t KPS = tpw * 16 * nw;
     const int64_t QT = (a.Q + QPT - 1) / QPT, QG = (QT + p.qtw - 1) / p.qtw;
     int64_t chunk;
     if (p.qtw > 1) {                     // at least about 1024 workgroups over the whole call
@@ -1527,7 +1531,7 @@ struct IndexBufs {
   uint4* meta;
 };
 
-template <int KIND, int DI, int HI, int QTW, bool kLocal>
+template <int KIND, int DI, int HI, int QTW, bool kLocal, int NW = 4>
 hipError_t launch_mfma_q(const IndexArgs& a, const TopkPlan& p, const IndexBufs& w, hipStream_t st) {
   constexpr int QPT = 16 / HI;
   const int64_t QT = (a.Q + QPT - 1) / QPT;
@@ -1580,19 +1584,27 @@ hipError_t launch_mfma_q(const IndexArgs& a, const TopkPlan& p, const IndexBufs&
   auto go = [&](auto kern) {
     if (smem > 65536) hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    DSV4_LAUNCH_MAIN(kern, grid, dim3(kThreads), smem, st, reinterpret_cast<const uint8_t*>(a.qi), a.qi_scale, a.wi,
+    DSV4_LAUNCH_MAIN(kern, grid, dim3(NW * kWave), smem, st, reinterpret_cast<const uint8_t*>(a.qi), a.qi_scale, a.wi,
                      reinterpret_cast<const uint8_t*>(a.ki), a.ki_scale, a.q_pos, a.N, a.k_bs, a.Q, a.m, p.chunk,
                      w.scores, sstride, w.hist, w.cloc, w.meta, p.klocal, (int)p.nch, pd);
   };
-  if (QTW == 1 && QG == 1) go(index_mfma_kernel<KIND, DI, HI, QTW, (QTW == 1), kLocal>);
-  else go(index_mfma_kernel<KIND, DI, HI, QTW, false, kLocal>);
+  if constexpr (NW == 4) {
+    if (QTW == 1 && QG == 1) go(index_mfma_kernel<KIND, DI, HI, QTW, (QTW == 1), kLocal>);
+    else go(index_mfma_kernel<KIND, DI, HI, QTW, false, kLocal>);
+  } else {
+    go(index_mfma_kernel<KIND, DI, HI, QTW, false, kLocal, NW>);
+  }
   return hipGetLastError();
 }
 
 template <int KIND, int DI>
 hipError_t launch_mfma_di(const IndexArgs& a, const TopkPlan& p, const IndexBufs& w, hipStream_t st) {
   if constexpr (DI == 128) {
-    if (p.qtw == 4) return launch_mfma_q<KIND, DI, 8, 4, false>(a, p, w, st);
+    // many queries: eight waves per workgroup (two workgroups and 16 waves per CU with the
+    // same 64 KB of histograms), four when the call also pools a block (its pooling body
+    // runs on 256 threads)
+    if (p.qtw == 4) return a.pool.on ? launch_mfma_q<KIND, DI, 8, 4, false>(a, p, w, st)
+                                     : launch_mfma_q<KIND, DI, 8, 4, false, 8>(a, p, w, st);
   }
   if (p.local) {
     switch (a.HI) {
