@@ -74,11 +74,11 @@ KERNEL_BYTES = {
 # the counter's reading for a 256 MiB device copy (see profiles/).  An entry is used only
 # while the kernel source it was measured on is unchanged (sha256 of the file).
 MEASURED_TRAFFIC = {
-    "index_mfma_kernel": {"bytes_per_launch": 151899321,
-        "source_sha256": "a450466471b0e4024d0a7b5f98964777cd79e3f939fae183f8f9806720bbbca6"},
-    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 157989314,
+    "index_mfma_kernel": {"bytes_per_launch": 151870796,
+        "source_sha256": "bc3130e1f1eb6f0db2c6dc3ad925ae4439b373c456f0e70ef8a43d11749ae99f"},
+    "attend_bf16_kernel (HCA)": {"bytes_per_launch": 157989339,
         "source_sha256": "d06b252d9fbb7db53c5156c03001dd0ebdbaea00a299f956ba8f58a9c8c628ae"},
-    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32834968,
+    "attend_bf16_kernel (CSA)": {"bytes_per_launch": 32835048,
         "source_sha256": "d06b252d9fbb7db53c5156c03001dd0ebdbaea00a299f956ba8f58a9c8c628ae"},
 }
 

@@ -273,6 +273,7 @@ __device__ __forceinline__ uint64_t kth_largest(Get get, uint32_t c, uint32_t ne
 // tmp: 2 NT / 64 words; misc: 4 words.
 constexpr int kLocalChunk = 4096;                            // keys per index workgroup (local selection)
 constexpr size_t kMinLocalLds = 56 * 1024;                   // LDS of a local-path index workgroup
+constexpr int kLocalWaves = 8;                               // waves of a local-path index workgroup
 template <int NT>
 __device__ __forceinline__ void local_select(const float* sc, uint32_t nv, const uint32_t* hist16, uint32_t KL, uint32_t key0,
                              uint64_t* __restrict__ out, uint4* __restrict__ meta, uint32_t* hb, uint32_t* tmp,
@@ -526,9 +527,9 @@ __global__ __launch_bounds__(NW * kWave) void index_mfma_kernel(
   constexpr int QPT = 16 / HI;          // queries per 16-row MFMA tile
   constexpr int KS = DI / 32;
   constexpr int GPQ = HI / 4;           // lane groups per query slot
-  constexpr int NTH = NW * kWave;       // threads (8 waves only for many-query calls without pooling)
+  constexpr int NTH = NW * kWave;       // threads
   static_assert(!kLocal || QTW == 1, "local selection: one query tile per workgroup");
-  static_assert(NW == 4 || (NW == 8 && QTW > 1 && !kLocal), "eight waves: many-query calls");
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
   // LDS: [QTW * QPT][kHistWords] histograms (kLocal: [min(Q, QPT)]), with kLocal then the
   // scores [min(Q, QPT)][chunk] and the selection's scratch.  A pooling workgroup uses the
   // start of the same space for its states (the launch sizes it for both).
@@ -566,7 +567,10 @@ __global__ __launch_bounds__(NW * kWave) void index_mfma_kernel(
     kbase = ki + b * k_bs * (DI / 2);
     sbase = ksc + b * k_bs * (DI / 32);
   }
-  constexpr int TPW = QTW == 1 ? tiles_per_step<KIND, DI>() : (KIND == KEY_FP8 && NW == 4 ? 4 : 2);
+  // (eight waves take half the tiles per step, so that a step covers the same keys)
+  constexpr int TPW = QTW == 1 ? (NW == 8 && tiles_per_step<KIND, DI>() > 1 ? tiles_per_step<KIND, DI>() / 2
+                                                                            : tiles_per_step<KIND, DI>())
+                               : (KIND == KEY_FP8 && NW == 4 ? 4 : 2);
   constexpr int KPS = TPW * 16 * NW;
   constexpr int E = GPQ < TPW ? GPQ : TPW;
   const int64_t c0 = (int64_t)blockIdx.x * chunk;
@@ -746,13 +750,13 @@ __global__ __launch_bounds__(NW * kWave) void index_mfma_kernel(
       int64_t nv = (int64_t)nvis_ep[s] - c0;
       nv = nv < 0 ? 0 : (nv > c1 - c0 ? c1 - c0 : nv);
       const int64_t slot = row * nch + blockIdx.x;
-      local_select<kThreads>(sc_l + s * chunk, (uint32_t)nv, hist_l + s * kHistWords, (uint32_t)klocal, (uint32_t)c0,
+      local_select<NTH>(sc_l + s * chunk, (uint32_t)nv, hist_l + s * kHistWords, (uint32_t)klocal, (uint32_t)c0,
                              cand_loc + slot * klocal, meta_loc + slot, selb, selb + (1 << kRadixBits),
-                             selb + (1 << kRadixBits) + 2 * kThreads / kWave);
+                             selb + (1 << kRadixBits) + 2 * NTH / kWave);
       const float* src = sc_l + s * chunk;
       float* dst = scores + row * sstride + c0;
       const int64_t nk = c1 - c0;                            // c0 and the row stride are multiples of 64
-      for (int64_t i = (int64_t)threadIdx.x * 4; i < nk; i += kThreads * 4) {
+      for (int64_t i = (int64_t)threadIdx.x * 4; i < nk; i += NTH * 4) {
         if (i + 4 <= nk) *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(src + i);
         else for (int64_t j = i; j < nk; ++j) dst[j] = src[j];
       }
@@ -1568,7 +1572,7 @@ hipError_t launch_mfma_q(const IndexArgs& a, const TopkPlan& p, const IndexBufs&
   size_t smem = (size_t)(kLocal ? (a.Q < QPT ? a.Q : QPT) : tiles * QPT) * kHistWords * sizeof(uint32_t);
   if (kLocal)
     smem += (size_t)(a.Q < QPT ? a.Q : QPT) * p.chunk * sizeof(float) +
-            (size_t)((1 << kRadixBits) + 2 * kThreads / kWave + 8) * sizeof(uint32_t);
+            (size_t)((1 << kRadixBits) + 2 * NW + 8) * sizeof(uint32_t);
   if (a.pool.on) {                                           // a pooling workgroup's states
     const size_t part = (size_t)pool::kThreads * (pool::XVec<uint16_t>::N + 2) * sizeof(float);
     smem = smem > part ? smem : part;
@@ -1592,7 +1596,8 @@ hipError_t launch_mfma_q(const IndexArgs& a, const TopkPlan& p, const IndexBufs&
     if (QTW == 1 && QG == 1) go(index_mfma_kernel<KIND, DI, HI, QTW, (QTW == 1), kLocal>);
     else go(index_mfma_kernel<KIND, DI, HI, QTW, false, kLocal>);
   } else {
-    go(index_mfma_kernel<KIND, DI, HI, QTW, false, kLocal, NW>);
+    if (QTW == 1 && QG == 1) go(index_mfma_kernel<KIND, DI, HI, QTW, (QTW == 1), kLocal, NW>);
+    else go(index_mfma_kernel<KIND, DI, HI, QTW, false, kLocal, NW>);
   }
   return hipGetLastError();
 }
@@ -1608,9 +1613,9 @@ hipError_t launch_mfma_di(const IndexArgs& a, const TopkPlan& p, const IndexBufs
   }
   if (p.local) {
     switch (a.HI) {
-      case 4: return launch_mfma_q<KIND, DI, 4, 1, true>(a, p, w, st);
-      case 8: return launch_mfma_q<KIND, DI, 8, 1, true>(a, p, w, st);
-      default: return launch_mfma_q<KIND, DI, 16, 1, true>(a, p, w, st);
+      case 4: return launch_mfma_q<KIND, DI, 4, 1, true, kLocalWaves>(a, p, w, st);
+      case 8: return launch_mfma_q<KIND, DI, 8, 1, true, kLocalWaves>(a, p, w, st);
+      default: return launch_mfma_q<KIND, DI, 16, 1, true, kLocalWaves>(a, p, w, st);
     }
   }
   switch (a.HI) {
